@@ -1,0 +1,345 @@
+"""Plain CPU oracle of the MSA (MiniMax Sparse Attention) forward path.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module. The product path (the HIP
+library and its binding) never calls it and has no CPU fallback.
+
+Everything here is the definition written out, in float64, one query row at a
+time, with numpy matmuls as the only library step. It shares no code with the
+HIP path.
+
+Sources (web pages; cited by title and section):
+  [P1] "Flash-MSA" kernel article on tech.kuratif.com (Indonesian), paragraphs
+       on block-wise sparsity and on the proxy/main forward.
+  [P2] "MiniMax Sparse Attention (MSA): una atención dispersa en bloques de dos
+       ramas ..." on 7minutos.es, sections "¿Qué es MSA?", "Cómo funcionan las
+       dos ramas", "Cómo se entrena MSA", "El codiseño del kernel".
+  [P3] "Accelerating Million-Token Training with Sparse Attention Kernels"
+       (DeepHorus blog).
+
+Notation: B batch, N tokens (queries = keys), Hkv groups (= KV heads = index
+query heads), G query heads per group, Hq = Hkv*G, D head dim, Di index dim,
+Bk block size, k blocks kept per (query, group). For query position i the local
+block is L = i // Bk; blocks j < L are fully visible and compete; the local
+block is always kept.
+
+Readings of points the pages leave open (each listed in the design notes):
+  * index score = raw dot product q_idx . k_idx (no scale; a positive scale
+    cannot change the selection);
+  * ties in the block ranking go to the lower block id;
+  * the kept ids are emitted in ascending order, padded with -1 to length k;
+  * with fewer than k-1 competing blocks, all of them are kept;
+  * token t is visible to query i iff t <= i;
+  * query head h belongs to group h // G;
+  * LSE is the natural-log log-sum-exp of the scaled logits;
+  * KL is KL(teacher || student) summed over the row's selected tokens, with
+    the teacher the group-mean of the G heads' main-branch probabilities and the
+    student the softmax of index_scale * index score over the same tokens.
+
+Parity: every function here is pinned by tests that do not re-use its code
+(brute force, closed forms, torch's dense SDPA, scipy's entropy, invariants).
+"""
+import math
+
+import numpy as np
+
+__all__ = [
+    "local_block", "visible_block_scores", "select_blocks", "index_topk_rows",
+    "index_topk", "token_set", "token_count", "attention_rows", "sparse_attention",
+    "kl_rows", "kl_align", "map_positions",
+]
+
+
+def _arr(x):
+    """Tensor or array -> numpy array without a copy where possible (bf16 tensors
+    widen exactly to float32; everything is cast to float64 where it is used)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu")
+            if x.dtype == torch.bfloat16 or x.dtype == torch.float16:
+                x = x.float()
+            return x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x)
+
+
+def local_block(i, Bk):
+    """The block holding query i; [P2] "Cómo funcionan las dos ramas": the block
+    that contains the query is always included."""
+    return i // Bk
+
+
+def visible_block_scores(q_idx_row, k_idx_b, i, Bk):
+    """Max-pooled index scores of the competing blocks of query i.
+
+    [P2] "Cómo funcionan las dos ramas": the index branch scores the visible key
+    tokens with one index-query head per group against one shared index-key head,
+    then max-pools the scores to the block level; [P1] paragraph on block-wise
+    sparsity: blocks of 128 chosen by max-pooling the proxy scores.
+
+    Only blocks j < L = i // Bk compete (fully visible, the local block is forced
+    in). Returns a float64 array of length L with m_j = max_{t in block j}
+    <q_idx_row, k_idx_b[t]>.
+    """
+    L = local_block(i, Bk)
+    if L == 0:
+        return np.zeros(0, dtype=np.float64)
+    keys = np.asarray(_arr(k_idx_b)[: L * Bk], dtype=np.float64)   # [L*Bk, Di]
+    s = keys @ np.asarray(_arr(q_idx_row), dtype=np.float64)       # one per token
+    return s.reshape(L, Bk).max(axis=1)
+
+
+def select_blocks(m, L, k):
+    """Forced-local, exp-free top-k of one (query, group) row.
+
+    [P2] "El codiseño del kernel": softmax keeps the order of the scores, so the
+    ranking runs on the raw max-pooled scores; [P2] "Cómo funcionan las dos ramas":
+    top-k per query and group, the local block always present; [P1] paragraph on
+    the proxy forward: local scores are set to +inf so the window stays open.
+
+    Ranking key: score descending, then block id ascending (lower id wins ties).
+    Returns the kept ids as an ascending int list of length min(k, L + 1); the
+    last entry is always L.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    assert m.shape == (L,)
+    ids = np.arange(L)
+    order = np.lexsort((ids, -m))               # primary: -m, secondary: id
+    kept = [int(j) for j in order[: min(k - 1, L)]] + [L]
+    return sorted(kept)
+
+
+def _pad(ids, k):
+    return list(ids) + [-1] * (k - len(ids))
+
+
+def index_topk_rows(q_idx, k_idx, positions, Bk, k, key_chunk=16384):
+    """Block indices at the given (b, i) positions.
+
+    q_idx [B, N, Hkv, Di], k_idx [B, N, Di]; positions int [M, 2].
+    Returns int32 [M, Hkv, k] (ascending ids, -1 padded).
+
+    Same definition as ``visible_block_scores`` + ``select_blocks`` per row; the
+    scores of all requested rows of a batch entry are obtained from one matrix
+    product per key chunk (a chunk holds whole blocks), then max-pooled per block.
+    """
+    qa = _arr(q_idx)
+    ka = _arr(k_idx)
+    Hkv = qa.shape[2]
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    out = np.full((len(positions), Hkv, k), -1, dtype=np.int32)
+    key_chunk = max(Bk, key_chunk // Bk * Bk)
+    for b in np.unique(positions[:, 0]):
+        sel = np.nonzero(positions[:, 0] == b)[0]
+        pos_i = positions[sel, 1]
+        Lmax = int(pos_i.max()) // Bk
+        qrows = np.asarray(qa[b, pos_i], dtype=np.float64).reshape(-1, qa.shape[3])  # [P*Hkv, Di]
+        m = np.empty((Lmax, qrows.shape[0]))
+        for t0 in range(0, Lmax * Bk, key_chunk):
+            t1 = min(Lmax * Bk, t0 + key_chunk)
+            s = np.asarray(ka[b, t0:t1], dtype=np.float64) @ qrows.T       # [tokens, P*Hkv]
+            m[t0 // Bk:t1 // Bk] = s.reshape((t1 - t0) // Bk, Bk, -1).max(axis=1)
+        for p, (r, i) in enumerate(zip(sel, pos_i)):
+            L = local_block(int(i), Bk)
+            for g in range(Hkv):
+                out[r, g] = _pad(select_blocks(m[:L, p * Hkv + g], L, k), k)
+    return out
+
+
+def index_topk(q_idx, k_idx, Bk, k):
+    """Block indices for every position: int32 [B, Hkv, N, k]."""
+    q_idx = _arr(q_idx)
+    B, N, Hkv, _ = q_idx.shape
+    pos = np.array([(b, i) for b in range(B) for i in range(N)], dtype=np.int64).reshape(-1, 2)
+    rows = index_topk_rows(q_idx, k_idx, pos, Bk, k)     # [B*N, Hkv, k]
+    return rows.reshape(B, N, Hkv, k).transpose(0, 2, 1, 3).copy()
+
+
+def token_set(ids, i, Bk):
+    """Causally visible tokens of the kept blocks of query i.
+
+    [P2] "Cómo funcionan las dos ramas": the main branch gathers the causally
+    visible tokens of the selected blocks. Block j contributes tokens
+    j*Bk .. min((j+1)*Bk - 1, i). ``ids`` may contain -1 padding.
+    """
+    parts = []
+    for j in ids:
+        j = int(j)
+        if j < 0:
+            continue
+        lo = j * Bk
+        hi = min((j + 1) * Bk - 1, i)
+        if hi >= lo:
+            parts.append(np.arange(lo, hi + 1, dtype=np.int64))
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def token_count(i, Bk, k):
+    """Closed form of |T_i| for a well-formed selection: (min(k, L+1) - 1) full
+    blocks plus the i mod Bk + 1 causal tokens of the local block ([P2] "¿Qué es
+    MSA?": budget k*Bk tokens per query)."""
+    L = i // Bk
+    return (min(k, L + 1) - 1) * Bk + (i % Bk) + 1
+
+
+def _softmax_stats(z):
+    """Natural-log LSE and normalised probabilities of each row of z."""
+    mx = z.max(axis=-1, keepdims=True)
+    e = np.exp(z - mx)
+    s = e.sum(axis=-1, keepdims=True)
+    lse = (mx + np.log(s))[..., 0]
+    return lse, e / s
+
+
+def attention_rows(q, k, v, block_idx_rows, positions, Bk, scale=None):
+    """Main-branch output at the given (b, i) positions.
+
+    [P2] "Cómo funcionan las dos ramas": exact scaled-dot-product softmax over
+    the gathered tokens; each query head uses its own query and the block set of
+    its group. [P1] paragraph on the forward: the output goes on and the LSE is
+    kept for the backward.
+
+    q [B,N,Hq,D], k/v [B,N,Hkv,D], block_idx_rows int [M, Hkv, k] for the M
+    positions. Returns (O [M, Hq, D], LSE [M, Hq]) in float64, where
+    z_t = scale * <q, k_t>, LSE = ln sum_t exp z_t, O = sum_t exp(z_t - LSE) v_t.
+    """
+    q = _arr(q)
+    kk = _arr(k)
+    vv = _arr(v)
+    Hq, D = q.shape[2], q.shape[3]
+    Hkv = kk.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    M = len(positions)
+    O = np.zeros((M, Hq, D))
+    LSE = np.zeros((M, Hq))
+    for b in np.unique(positions[:, 0]):
+        rows = np.nonzero(positions[:, 0] == b)[0]
+        for g in range(Hkv):
+            kg = np.ascontiguousarray(kk[b, :, g], dtype=np.float64)        # [N, D]
+            vg = np.ascontiguousarray(vv[b, :, g], dtype=np.float64)
+            for r in rows:
+                i = int(positions[r, 1])
+                T = token_set(block_idx_rows[r, g], i, Bk)
+                qh = np.asarray(q[b, i, g * G:(g + 1) * G], dtype=np.float64)   # [G, D]
+                z = scale * (qh @ kg[T].T)                                      # [G, |T|]
+                lse, p = _softmax_stats(z)
+                LSE[r, g * G:(g + 1) * G] = lse
+                O[r, g * G:(g + 1) * G] = p @ vg[T]
+    return O, LSE
+
+
+def sparse_attention(q, k, v, block_idx, Bk, scale=None):
+    """Full main-branch forward: O [B,N,Hq,D] and LSE [B,Hq,N] in float64."""
+    q = _arr(q)
+    B, N, Hq, D = q.shape
+    pos = np.array([(b, i) for b in range(B) for i in range(N)], dtype=np.int64).reshape(-1, 2)
+    bi = np.asarray(block_idx)
+    rows = bi.transpose(0, 2, 1, 3).reshape(B * N, bi.shape[1], bi.shape[3])
+    O, LSE = attention_rows(q, k, v, rows, pos, Bk, scale)
+    return O.reshape(B, N, Hq, D), LSE.reshape(B, N, Hq).transpose(0, 2, 1).copy()
+
+
+def kl_rows(q, k, q_idx, k_idx, block_idx_rows, positions, Bk, scale=None,
+            index_scale=None):
+    """KL-alignment loss per (position, group) at the given positions.
+
+    [P2] "Cómo se entrena MSA": a KL alignment loss matches the index branch's
+    distribution to the main branch's attention pattern; the teacher is the main
+    distribution averaged over the group, over the selected tokens. [P1]
+    paragraph on the backward: computed without materialising the full
+    distributions.
+
+    Teacher p_t = mean_h softmax_t(scale <q_h, k_t>); student
+    s_t = softmax_t(index_scale <q_idx, k_idx_t>); both over the row's selected
+    tokens T_i. Returns float64 [M, Hkv] with sum_t p_t (ln p_t - ln s_t)
+    (terms with p_t = 0 contribute 0).
+    """
+    q = _arr(q)
+    kk = _arr(k)
+    qi = _arr(q_idx)
+    ki = _arr(k_idx)
+    Hq, D = q.shape[2], q.shape[3]
+    Hkv, Di = kk.shape[2], qi.shape[3]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    index_scale = (1.0 / math.sqrt(Di) if index_scale is None or index_scale <= 0
+                   else float(index_scale))
+    out = np.zeros((len(positions), Hkv))
+    for r, (b, i) in enumerate(np.asarray(positions)):
+        for g in range(Hkv):
+            T = token_set(block_idx_rows[r, g], int(i), Bk)
+            qh = np.asarray(q[b, i, g * G:(g + 1) * G], dtype=np.float64)
+            kt = np.asarray(kk[b, T, g], dtype=np.float64)
+            z = scale * (qh @ kt.T)
+            _, ph = _softmax_stats(z)
+            p = ph.mean(axis=0)
+            u = index_scale * (np.asarray(ki[b, T], dtype=np.float64)
+                               @ np.asarray(qi[b, i, g], dtype=np.float64))
+            lse_u, _ = _softmax_stats(u[None, :])
+            log_s = u - lse_u[0]
+            nz = p > 0
+            out[r, g] = float(np.sum(p[nz] * (np.log(p[nz]) - log_s[nz])))
+    return out
+
+
+def kl_align(q, k, q_idx, k_idx, block_idx, Bk, scale=None, index_scale=None):
+    """Full KL forward: (kl_rows [B, Hkv, N], kl_sum) in float64; kl_sum is the
+    plain sum over all rows."""
+    q = _arr(q)
+    B, N = q.shape[:2]
+    pos = np.array([(b, i) for b in range(B) for i in range(N)], dtype=np.int64).reshape(-1, 2)
+    bi = np.asarray(block_idx)
+    rows = bi.transpose(0, 2, 1, 3).reshape(B * N, bi.shape[1], bi.shape[3])
+    kl = kl_rows(q, k, q_idx, k_idx, rows, pos, Bk, scale, index_scale)
+    kl = kl.reshape(B, N, -1).transpose(0, 2, 1).copy()
+    return kl, float(kl.sum())
+
+
+def map_positions(fn, positions, row_arrays=(), workers=1, chunk=256):
+    """Run a row-wise oracle function over position chunks in worker processes.
+
+    ``fn(positions_chunk, *row_array_chunks)`` must return an array (or tuple of
+    arrays) whose first axis follows the chunk's rows; ``row_arrays`` are split
+    along their first axis like ``positions``. Rows are independent, so the
+    result equals one call over all positions; this only spreads the rows over
+    ``workers`` forked processes (the children run numpy only).
+    """
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    spans = [(s, min(len(positions), s + chunk)) for s in range(0, len(positions), chunk)]
+    jobs = [(positions[s:e],) + tuple(a[s:e] for a in row_arrays) for s, e in spans]
+    if workers <= 1 or len(jobs) <= 1:
+        parts = [fn(*j) for j in jobs]
+    else:
+        import multiprocessing as mp
+        global _MAP_FN
+        _MAP_FN = fn
+        try:
+            with mp.get_context("fork").Pool(workers, initializer=_single_thread_blas) as pool:
+                parts = pool.map(_map_worker, jobs)
+        finally:
+            _MAP_FN = None
+    if not parts:
+        return None
+    if isinstance(parts[0], tuple):
+        return tuple(np.concatenate([p[t] for p in parts]) for t in range(len(parts[0])))
+    return np.concatenate(parts)
+
+
+_MAP_FN = None
+
+
+def _single_thread_blas():
+    """Workers each run one BLAS thread (the parallelism is across rows)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
+def _map_worker(job):
+    return _MAP_FN(*job)

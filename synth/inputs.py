@@ -1,0 +1,95 @@
+"""Seeded input generation (no method arithmetic here)."""
+import math
+
+import numpy as np
+import torch
+
+from .configs import Workload
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+_CHUNK = 1 << 26  # elements drawn per call, bounds the fp32/int64 temporaries
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return _TORCH_DTYPE[name]
+
+
+def _randint(shape, gen, device, dtype):
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), _CHUNK):
+        e = min(flat.numel(), s + _CHUNK)
+        flat[s:e] = torch.randint(-4, 5, (e - s,), generator=gen, device=device).to(dtype)
+    return out
+
+
+def _randn(shape, gen, device, dtype):
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), _CHUNK):
+        e = min(flat.numel(), s + _CHUNK)
+        flat[s:e] = torch.randn((e - s,), generator=gen, device=device,
+                                dtype=torch.float32).to(dtype)
+    return out
+
+
+def stripe_blocks(w: Workload, gen: torch.Generator, device) -> torch.Tensor:
+    n = int(round(w.stripe_frac * w.nblocks))
+    if n <= 0:
+        return torch.empty(0, dtype=torch.long)
+    perm = torch.randperm(w.nblocks, generator=gen, device=device)
+    return perm[:n].sort().values.cpu()
+
+
+def make_inputs(w: Workload, device="cpu", seed=None, kinds=("q_idx", "k_idx", "q", "k", "v")):
+    """Draw the workload's inputs on ``device`` from one seeded generator.
+
+    Returns a dict with q_idx [B,N,Hkv,Di], k_idx [B,N,Di], q [B,N,Hq,D],
+    k/v [B,N,Hkv,D] (all in the workload dtype) and 'stripes' (block ids that got
+    the k_idx bias). Tensors not listed in ``kinds`` are still drawn (to keep the
+    random stream aligned) but dropped.
+    """
+    seed = w.seed if seed is None else seed
+    dt = torch_dtype(w.dtype)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    B, N, Hkv, G, D, Di, Bk = (w.batch, w.seqlen, w.kv_heads, w.group_size,
+                               w.head_dim, w.index_dim, w.block_size)
+    out = {}
+    out["q_idx"] = _randint((B, N, Hkv, Di), gen, device, dt)
+    k_idx = _randint((B, N, Di), gen, device, dt)
+    stripes = stripe_blocks(w, gen, device)
+    for j in stripes.tolist():
+        k_idx[:, j * Bk:min(N, (j + 1) * Bk), :] += w.stripe_bias
+    out["k_idx"] = k_idx
+    out["stripes"] = stripes
+    out["q"] = _randn((B, N, Hkv * G, D), gen, device, dt)
+    out["k"] = _randn((B, N, Hkv, D), gen, device, dt)
+    out["v"] = _randn((B, N, Hkv, D), gen, device, dt)
+    for name in ("q_idx", "k_idx", "q", "k", "v"):
+        if name not in kinds:
+            del out[name]
+    return out
+
+
+def edge_positions(w: Workload):
+    """Query positions at the block and budget edges: 0, Bk-1, Bk, k*Bk-1, k*Bk, N-1."""
+    Bk, k, N = w.block_size, w.topk, w.seqlen
+    cand = [0, Bk - 1, Bk, k * Bk - 1, k * Bk, N - 1]
+    return sorted({p for p in cand if 0 <= p < N})
+
+
+def sample_rows(w: Workload, n=None, seed=1):
+    """(b, i) query positions checked on large workloads: ``n`` drawn without
+    replacement over all B*N positions plus the edge positions in every batch.
+    Returns an int64 array of shape [M, 2], sorted."""
+    n = w.sampled_rows if n is None else n
+    total = w.batch * w.seqlen
+    rng = np.random.default_rng(seed)
+    if n <= 0 or n >= total:
+        flat = np.arange(total, dtype=np.int64)
+    else:
+        flat = rng.choice(total, size=n, replace=False).astype(np.int64)
+    edges = [b * w.seqlen + p for b in range(w.batch) for p in edge_positions(w)]
+    flat = np.unique(np.concatenate([flat, np.asarray(edges, dtype=np.int64)]))
+    return np.stack([flat // w.seqlen, flat % w.seqlen], axis=1)

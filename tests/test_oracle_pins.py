@@ -1,0 +1,330 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-worked values, brute force, closed forms, torch's dense attention and
+scipy's relative entropy. CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden():
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- selection --
+
+def test_hand_worked_selection():
+    g = _golden()["selection"]
+    Bk, k = g["block_size"], g["topk"]
+    k_idx = np.asarray(g["k_idx"], dtype=np.float64)[None]          # [1, N, Di]
+    N, Di = k_idx.shape[1:]
+    for row in g["rows"]:
+        q_idx = np.zeros((1, N, 1, Di))
+        q_idx[0, row["i"], 0] = row["q_idx"]
+        got = O.index_topk_rows(q_idx, k_idx, np.array([[0, row["i"]]]), Bk, k)
+        assert got[0, 0].tolist() == row["expect"], row["why"]
+
+
+def _brute_force_row(q_row, k_idx_b, i, Bk, k):
+    """Token scores by explicit loops, block max by loops, and the kept set as the
+    unique subset whose members all outrank every non-member under
+    (score desc, id asc), found by enumerating every subset."""
+    L = i // Bk
+    m = []
+    for j in range(L):
+        best = None
+        for t in range(j * Bk, (j + 1) * Bk):
+            s = 0.0
+            for d in range(len(q_row)):
+                s += float(q_row[d]) * float(k_idx_b[t][d])
+            best = s if best is None or s > best else best
+        m.append(best)
+
+    def outranks(a, b):
+        return m[a] > m[b] or (m[a] == m[b] and a < b)
+
+    size = min(k - 1, L)
+    found = []
+    for subset in itertools.combinations(range(L), size):
+        rest = [j for j in range(L) if j not in subset]
+        if all(outranks(a, b) for a in subset for b in rest):
+            found.append(subset)
+    assert len(found) == 1
+    ids = sorted(list(found[0]) + [L])
+    return ids + [-1] * (k - len(ids))
+
+
+@pytest.mark.parametrize("seed,N,Bk,k,Di,Hkv", [
+    (0, 32, 4, 4, 3, 2),     # many ties (values in -2..2, Di = 3)
+    (1, 29, 4, 3, 2, 1),     # ragged tail: N % Bk != 0
+    (2, 24, 3, 6, 4, 2),     # k - 1 >= candidates for most rows
+    (3, 40, 5, 1, 3, 1),     # k = 1: only the local block
+])
+def test_selection_matches_brute_force(seed, N, Bk, k, Di, Hkv):
+    rng = np.random.default_rng(seed)
+    q_idx = rng.integers(-2, 3, size=(1, N, Hkv, Di)).astype(np.float64)
+    k_idx = rng.integers(-2, 3, size=(1, N, Di)).astype(np.float64)
+    got = O.index_topk(q_idx, k_idx, Bk, k)
+    for g in range(Hkv):
+        for i in range(N):
+            want = _brute_force_row(q_idx[0, i, g], k_idx[0], i, Bk, k)
+            assert got[0, g, i].tolist() == want, (g, i)
+
+
+def test_selection_invariants_tiny_workload():
+    from synth import get_workload, make_inputs
+    w = get_workload("tiny")
+    x = make_inputs(w)
+    bi = O.index_topk(x["q_idx"], x["k_idx"], w.block_size, w.topk)
+    Bk, k = w.block_size, w.topk
+    for i in range(w.seqlen):
+        L = i // Bk
+        row = bi[0, 0, i].tolist()
+        valid = [j for j in row if j >= 0]
+        assert len(valid) == min(k, L + 1)                       # count
+        assert valid == sorted(set(valid))                       # distinct, ascending
+        assert valid[-1] == L                                    # local block present, last
+        assert all(0 <= j <= L for j in valid)
+        assert row[len(valid):] == [-1] * (k - len(valid))       # padding
+        assert len(O.token_set(row, i, Bk)) == O.token_count(i, Bk, k)
+
+
+def test_exp_free_equivalence():
+    """Ranking by softmax probabilities (max-pooled per block) keeps exactly the
+    same blocks as ranking the raw scores: softmax preserves order."""
+    rng = np.random.default_rng(7)
+    Bk, k, N, Di, Hkv = 8, 4, 96, 6, 2
+    q_idx = rng.integers(-4, 5, size=(1, N, Hkv, Di)).astype(np.float64)
+    k_idx = rng.integers(-4, 5, size=(1, N, Di)).astype(np.float64)
+    raw = O.index_topk(q_idx, k_idx, Bk, k)
+    for g in range(Hkv):
+        for i in range(N):
+            L = i // Bk
+            if L == 0:
+                continue
+            s = k_idx[0, :L * Bk] @ q_idx[0, i, g]
+            logp = s - (s.max() + math.log(np.exp(s - s.max()).sum()))   # log-softmax
+            mp = logp.reshape(L, Bk).max(axis=1)
+            ids = O.select_blocks(mp, L, k)
+            assert ids + [-1] * (k - len(ids)) == raw[0, g, i].tolist()
+
+
+def test_batched_scores_match_single_row():
+    rng = np.random.default_rng(11)
+    Bk, k, N, Di, Hkv = 4, 3, 64, 5, 3
+    q_idx = rng.integers(-4, 5, size=(2, N, Hkv, Di)).astype(np.float64)
+    k_idx = rng.integers(-4, 5, size=(2, N, Di)).astype(np.float64)
+    pos = np.array([(b, i) for b in range(2) for i in range(0, N, 3)])
+    got = O.index_topk_rows(q_idx, k_idx, pos, Bk, k, key_chunk=8)
+    for r, (b, i) in enumerate(pos):
+        for g in range(Hkv):
+            m = O.visible_block_scores(q_idx[b, i, g], k_idx[b], i, Bk)
+            ids = O.select_blocks(m, i // Bk, k)
+            assert got[r, g].tolist() == ids + [-1] * (k - len(ids))
+
+
+# ---------------------------------------------------------------- attention --
+
+def test_hand_worked_attention():
+    g = _golden()["attention"]
+    Bk = g["block_size"]
+    kk = np.asarray(g["k"])[None, :, None, None]
+    vv = np.asarray(g["v"])[None, :, None, None]
+    N = kk.shape[1]
+    for row in g["rows"]:
+        q = np.zeros((1, N, 1, 1))
+        q[0, row["i"], 0, 0] = g["q"]
+        bi = np.array([[row["blocks"]]])
+        o, lse = O.attention_rows(q, kk, vv, bi, np.array([[0, row["i"]]]), Bk, scale=g["scale"])
+        assert o[0, 0, 0] == pytest.approx(row["o"], abs=1e-14), row["why"]
+        assert lse[0, 0] == pytest.approx(row["lse_value"], abs=1e-14), row["why"]
+
+
+def _rand_case(seed, B=1, N=96, Hkv=2, G=3, D=16, Di=8, Bk=8, k=4):
+    rng = np.random.default_rng(seed)
+    q_idx = rng.integers(-4, 5, size=(B, N, Hkv, Di)).astype(np.float64)
+    k_idx = rng.integers(-4, 5, size=(B, N, Di)).astype(np.float64)
+    q = rng.standard_normal((B, N, Hkv * G, D))
+    kk = rng.standard_normal((B, N, Hkv, D))
+    vv = rng.standard_normal((B, N, Hkv, D))
+    return q_idx, k_idx, q, kk, vv
+
+
+@pytest.mark.parametrize("N,Bk", [(96, 8), (90, 8), (7, 8)])
+def test_warmup_reduces_to_dense_causal_gqa(N, Bk):
+    """With k >= number of blocks every block is kept: the sparse output must
+    equal dense causal GQA attention (the indexer warm-up of section 'Como se
+    entrena MSA'), here torch's SDPA in float64."""
+    Hkv, G, D = 2, 3, 16
+    q_idx, k_idx, q, kk, vv = _rand_case(5, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    k = -(-N // Bk) + 2
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    o, lse = O.sparse_attention(q, kk, vv, bi, Bk)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)          # [B, Hq, N, D]
+    kt = torch.from_numpy(kk).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(vv).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                           enable_gqa=True)
+    np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
+    scores = (qt @ kt.repeat_interleave(G, dim=1).transpose(-1, -2)) / math.sqrt(D)
+    mask = torch.ones(N, N, dtype=torch.bool).tril()
+    ref_lse = torch.logsumexp(scores.masked_fill(~mask, float("-inf")), dim=-1)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), atol=1e-12, rtol=0)
+
+
+def test_zero_query_gives_uniform_average():
+    """Q = 0 makes every logit 0: LSE = ln|T_i| and O = mean of V over T_i, with
+    T_i enumerated here by explicit loops over the kept blocks."""
+    Bk, k = 8, 4
+    q_idx, k_idx, q, kk, vv = _rand_case(9, N=100, Bk=Bk, k=k)
+    q[:] = 0.0
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    o, lse = O.sparse_attention(q, kk, vv, bi, Bk)
+    G = q.shape[2] // kk.shape[2]
+    for g in range(kk.shape[2]):
+        for i in range(q.shape[1]):
+            toks = []
+            for j in bi[0, g, i]:
+                if j >= 0:
+                    for t in range(j * Bk, j * Bk + Bk):
+                        if t <= i:
+                            toks.append(t)
+            assert len(toks) == O.token_count(i, Bk, k)
+            mean_v = sum(vv[0, t, g] for t in toks) / len(toks)
+            for h in range(g * G, (g + 1) * G):
+                assert lse[0, h, i] == pytest.approx(math.log(len(toks)), abs=1e-12)
+                np.testing.assert_allclose(o[0, i, h], mean_v, atol=1e-12)
+
+
+def test_constant_values_give_constant_output():
+    Bk, k = 8, 3
+    q_idx, k_idx, q, kk, vv = _rand_case(13, N=64, Bk=Bk, k=k)
+    vv[:] = 0.375
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    o, _ = O.sparse_attention(q, kk, vv, bi, Bk)
+    np.testing.assert_allclose(o, 0.375, atol=1e-13)
+
+
+def test_scale_enters_logits():
+    """An explicit scale equal to 1/sqrt(D) matches the default; doubling the
+    scale equals doubling Q."""
+    Bk, k = 8, 3
+    q_idx, k_idx, q, kk, vv = _rand_case(17, N=48, Bk=Bk, k=k)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    D = q.shape[-1]
+    o0, l0 = O.sparse_attention(q, kk, vv, bi, Bk)
+    o1, l1 = O.sparse_attention(q, kk, vv, bi, Bk, scale=1 / math.sqrt(D))
+    o2, l2 = O.sparse_attention(2 * q, kk, vv, bi, Bk)
+    o3, l3 = O.sparse_attention(q, kk, vv, bi, Bk, scale=2 / math.sqrt(D))
+    np.testing.assert_allclose(o0, o1, atol=1e-14)
+    np.testing.assert_allclose(o2, o3, atol=1e-12)
+    np.testing.assert_allclose(l2, l3, atol=1e-12)
+
+
+# ----------------------------------------------------------------------- KL --
+
+def test_hand_worked_kl():
+    g = _golden()["kl"]
+    Bk, i = g["block_size"], g["i"]
+    N = len(g["k"])
+    H = len(g["q_heads"])
+    q = np.zeros((1, N, H, 1))
+    q[0, i, :, 0] = g["q_heads"]
+    kk = np.asarray(g["k"])[None, :, None, None]
+    q_idx = np.zeros((1, N, 1, 1))
+    q_idx[0, i, 0, 0] = g["q_idx"]
+    k_idx = np.asarray(g["k_idx"])[None, :, None]
+    bi = np.array([[g["blocks"]]])
+    kl = O.kl_rows(q, kk, q_idx, k_idx, bi, np.array([[0, i]]), Bk,
+                   scale=g["scale"], index_scale=g["index_scale"])
+    assert kl[0, 0] == pytest.approx(g["expect"], abs=1e-14), g["why"]
+
+
+def test_kl_dense_matches_scipy_entropy():
+    """Warm-up case (all blocks kept): teacher and student are dense causal
+    softmaxes built with torch, the KL is scipy's relative entropy."""
+    from scipy.stats import entropy
+    Bk, N, Hkv, G, D, Di = 8, 40, 2, 3, 16, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(21, N=N, Hkv=Hkv, G=G, D=D, Di=Di, Bk=Bk)
+    k = -(-N // Bk) + 1
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    kl, total = O.kl_align(q, kk, q_idx, k_idx, bi, Bk, index_scale=0.25)
+    mask = torch.ones(N, N, dtype=torch.bool).tril()
+    for g in range(Hkv):
+        qh = torch.from_numpy(q[0, :, g * G:(g + 1) * G]).permute(1, 0, 2)       # [G, N, D]
+        s = (qh @ torch.from_numpy(kk[0, :, g]).T) / math.sqrt(D)
+        teacher = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1).mean(0)
+        u = 0.25 * (torch.from_numpy(q_idx[0, :, g]) @ torch.from_numpy(k_idx[0]).T)
+        student = torch.softmax(u.masked_fill(~mask, float("-inf")), dim=-1)
+        for i in range(N):
+            ref = entropy(teacher[i, :i + 1].numpy(), student[i, :i + 1].numpy())
+            assert kl[0, g, i] == pytest.approx(ref, abs=1e-10)
+    assert total == pytest.approx(kl.sum(), abs=1e-9)
+
+
+def test_kl_nonnegative_and_identity_is_zero():
+    Bk, N, D = 8, 64, 16
+    q_idx, k_idx, q, kk, vv = _rand_case(23, N=N, Hkv=1, G=1, D=D, Di=D, Bk=Bk)
+    bi = O.index_topk(q_idx, k_idx, Bk, 3)
+    kl, _ = O.kl_align(q, kk, q_idx, k_idx, bi, Bk)
+    assert (kl >= -1e-12).all()
+    # identity: index branch = main branch (G = 1, same vectors, same scale)
+    kl0, s0 = O.kl_align(q, kk, q, kk[:, :, 0, :], bi, Bk, scale=0.3, index_scale=0.3)
+    np.testing.assert_allclose(kl0, 0.0, atol=1e-12)
+
+
+def test_kl_teacher_of_identical_heads_is_that_head():
+    Bk, N, D = 8, 48, 16
+    q_idx, k_idx, q1, kk, vv = _rand_case(29, N=N, Hkv=1, G=1, D=D, Bk=Bk)
+    bi = O.index_topk(q_idx, k_idx, Bk, 3)
+    q4 = np.repeat(q1, 4, axis=2)
+    a, _ = O.kl_align(q1, kk, q_idx, k_idx, bi, Bk)
+    b, _ = O.kl_align(q4, kk, q_idx, k_idx, bi, Bk)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+# --------------------------------------------------------------- mutations --
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    """Each planted mistake in the oracle makes one of the pins above fail."""
+    rng = np.random.default_rng(0)
+    q_idx = rng.integers(-2, 3, size=(1, 32, 1, 3)).astype(np.float64)
+    k_idx = rng.integers(-2, 3, size=(1, 32, 3)).astype(np.float64)
+
+    def selection_ok():
+        got = O.index_topk(q_idx, k_idx, 4, 4)
+        return all(got[0, 0, i].tolist() == _brute_force_row(q_idx[0, i, 0], k_idx[0], i, 4, 4)
+                   for i in range(32))
+
+    assert selection_ok()
+    real_select = O.select_blocks
+
+    def wrong_tiebreak(m, L, k):   # higher id wins ties
+        order = np.lexsort((-np.arange(L), -np.asarray(m)))
+        return sorted([int(j) for j in order[:min(k - 1, L)]] + [L])
+
+    monkeypatch.setattr(O, "select_blocks", wrong_tiebreak)
+    assert not selection_ok()
+    monkeypatch.setattr(O, "select_blocks", real_select)
+
+    real_scores = O.visible_block_scores
+
+    def mean_pool(q_row, k_b, i, Bk):   # mean instead of max pooling
+        L = i // Bk
+        return (np.asarray(k_b[:L * Bk]) @ q_row).reshape(L, Bk).mean(axis=1)
+
+    monkeypatch.setattr(O, "visible_block_scores", mean_pool)
+    monkeypatch.setattr(O, "index_topk_rows",
+                        lambda qi, ki, pos, Bk, k: np.array(
+                            [[O._pad(real_select(mean_pool(qi[b, i, g], ki[b], i, Bk), i // Bk, k), k)
+                              for g in range(qi.shape[2])] for b, i in pos], dtype=np.int32))
+    assert not selection_ok()
