@@ -1,0 +1,195 @@
+"""Benchmark of the MSA forward hot path on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident
+in HBM: msa_index_topk (index scores, block max-pool, forced-local exp-free
+top-k) followed by msa_sparse_attn_fwd (block-sparse GQA attention with LSE),
+on one HIP stream. Default workload: N = 128K tokens, Hkv = 8, G = 8,
+D = Di = 128, Bk = 128, k = 16, bf16, with long-range stripes.
+
+Prints one JSON line: tokens/s (value), TFLOP/s and the fraction of the bf16
+MFMA peak for the step, a roofline entry for the dominant kernel (the fused
+index kernel, timed with HIP events on its stream), and the CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload n128k] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_gqa_index_amd as msa  # noqa: E402
+from synth import CONFIGS, make_inputs, sample_rows  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and MFMA)
+INDEX_KERNEL = "index_topk_kernel"
+INDEX_SOURCE = os.path.join(ROOT, "block_sparse_gqa_index_amd", "csrc", "index_topk.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_topk_n128k_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops(w):
+    """Algorithmic work: competing blocks only for the index GEMM; causally
+    visible tokens of the kept blocks for the attention (QK^T and PV)."""
+    B, N, Hkv, G, D, Di, Bk, k = (w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim,
+                                  w.index_dim, w.block_size, w.topk)
+    nb_full = N // Bk
+    f_idx = 2.0 * Di * B * Hkv * Bk * Bk * nb_full * (nb_full - 1) / 2
+    i = np.arange(N, dtype=np.int64)
+    L = i // Bk
+    tokens = (np.minimum(k, L + 1) - 1) * Bk + (i % Bk) + 1
+    f_main = 4.0 * D * B * Hkv * G * float(tokens.sum())
+    return f_idx, f_main
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_entry():
+    """HBM bytes per launch of the index kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_digest(INDEX_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, seconds_target=15.0):
+    """The oracle as it stands on a bounded sample of rows of this workload."""
+    from oracle import msa_oracle as O
+    workers = max(1, min(16, os.cpu_count() or 1))
+    n = 64
+    kih = x["k_idx"].cpu()
+    kh, vh = x["k"].cpu(), x["v"].cpu()
+    spent = 0.0
+    rows = 0
+    while True:
+        pos = sample_rows(w, n=n, seed=2 + rows)
+        b = torch.as_tensor(pos[:, 0], device=x["q"].device)
+        i = torch.as_tensor(pos[:, 1], device=x["q"].device)
+        qi_rows, q_rows = x["q_idx"][b, i].cpu(), x["q"][b, i].cpu()
+        t0 = time.perf_counter()
+        bi = O.index_topk_rows(None, kih, pos, w.block_size, w.topk, q_rows=qi_rows)
+        O.map_positions(lambda c, br, qr: O.attention_rows(None, kh, vh, br, c, w.block_size, q_rows=qr),
+                        pos, (bi, q_rows), workers=workers)
+        spent += time.perf_counter() - t0
+        rows += len(pos)
+        if spent >= seconds_target * 0.5 or n >= 4096:
+            break
+        n *= 2
+    return {"value": rows / spent, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{rows} query positions (all {w.kv_heads} groups, {w.q_heads} heads) drawn "
+                      f"from the {w.name} workload; index selection + attention, float64 oracle; "
+                      f"{spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="n128k", choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the MSA forward path here runs on a single MI355X "
+              "(multi-GPU sharding by (batch, group) is a design note, not built). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    msa.load_library()
+    log(f"[bench] workload {w.name}: generating inputs on {dev}")
+    x = make_inputs(w, device=dev)
+    B, N, Hkv, G, D = w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim
+    block_idx = torch.empty((B, Hkv, N, w.topk), dtype=torch.int32, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, Hkv * G, N), dtype=torch.float32, device=dev)
+    dims = msa.make_dims(B, N, Hkv, G, D, w.index_dim, w.topk, x["q"].dtype)
+    ws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_ATTN)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        msa.index_topk(x["q_idx"], x["k_idx"], w.topk, block_idx=block_idx)
+        if ev is not None:
+            ev[1].record(stream)
+        msa.sparse_attn_fwd(x["q"], x["k"], x["v"], block_idx, o=o, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    idx_ms = [e[0].elapsed_time(e[1]) for e in events]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_step = wall * 1e3 / args.steps
+
+    f_idx, f_main = flops(w)
+    tokens = B * N
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_idx = float(np.mean(idx_ms)) * 1e-3
+    achieved = f_idx / t_idx / 1e12
+    out = {
+        "metric": "MSA fwd tokens/s and TFLOP/s (% bf16 MFMA peak) at N=128K, k=16, Bk=128",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B} N={N} Hkv={Hkv} G={G} D={D} Di={w.index_dim} "
+                               f"Bk={w.block_size} k={w.topk} {w.dtype}"
+                               + (f", {int(round(w.stripe_frac * w.nblocks))} stripe blocks +{w.stripe_bias:g}"
+                                  if w.stripe_frac else ""),
+                   "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+        "tflops": (f_idx + f_main) / (ms_step * 1e-3) / 1e12,
+        "frac_of_peak": (f_idx + f_main) / (ms_step * 1e-3) / 1e12 / peak,
+        "algorithmic_tflop": {"index": f_idx / 1e12, "attention": f_main / 1e12},
+        "kernel_ms": {"msa_index_topk": float(np.mean(idx_ms)), "msa_sparse_attn_fwd": float(np.mean(attn_ms))},
+        "roofline": {"kernel": INDEX_KERNEL, "bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic_entry()},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

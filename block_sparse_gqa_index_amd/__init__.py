@@ -1,0 +1,196 @@
+"""MSA (MiniMax Sparse Attention) forward hot path on AMD Instinct MI355X.
+
+Thin ctypes binding over ``libmsa.so`` (the C ABI declared in include/msa.h).
+This module only marshals arguments: shapes and pointers of torch device
+tensors, the current HIP stream, and workspace buffers allocated through
+torch. Every step of the computation runs in the library's HIP kernels; if
+the library is missing, every call raises.
+
+Entry points (same names as the C ABI, without the ``msa_`` prefix):
+  index_topk(q_idx, k_idx, topk)                   -> block_idx int32 [B, Hkv, N, k]
+  sparse_attn_fwd(q, k, v, block_idx, scale)       -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])
+  kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse) -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])
+  workspace_bytes(dims, op)
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_BF16, MSA_F32 = 0, 1
+MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL = 0, 1, 2
+STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
+          4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
+EXPORTS = ("msa_index_topk", "msa_sparse_attn_fwd", "msa_kl_align_fwd", "msa_workspace_bytes",
+           "msa_strerror", "msa_abi_version")
+
+
+class MsaDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("kv_heads", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32)]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmsa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_gqa_index_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    dp = ctypes.POINTER(MsaDims)
+    lib.msa_index_topk.argtypes = [dp, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_fwd.argtypes = [dp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.msa_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+                                     vp, vp, vp, sz, vp]
+    lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
+    lib.msa_workspace_bytes.restype = ctypes.c_size_t
+    lib.msa_strerror.argtypes = [ctypes.c_int]
+    lib.msa_strerror.restype = ctypes.c_char_p
+    lib.msa_abi_version.restype = ctypes.c_int
+    for f in (lib.msa_index_topk, lib.msa_sparse_attn_fwd, lib.msa_kl_align_fwd):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise MsaError(status, load_library().msa_strerror(status).decode())
+
+
+def make_dims(batch, seqlen, kv_heads, group_size, head_dim, index_dim, topk, dtype,
+              block_size=128, causal=1) -> MsaDims:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.bfloat16: MSA_BF16, torch.float32: MSA_F32}.get(dtype, -1)
+    return MsaDims(batch, seqlen, kv_heads, group_size, head_dim, index_dim, block_size, topk,
+                   dtype, causal)
+
+
+def workspace_bytes(dims: MsaDims, op: int) -> int:
+    return int(load_library().msa_workspace_bytes(ctypes.byref(dims), op))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None or ws.numel() * ws.element_size() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def _req(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def index_topk(q_idx, k_idx, topk, block_idx=None, block_size=128):
+    """Block selection. q_idx [B,N,Hkv,Di], k_idx [B,N,Di] -> int32 [B,Hkv,N,topk]."""
+    lib = load_library()
+    _req(q_idx, "q_idx", ndim=4)
+    _req(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)
+    B, N, Hkv, Di = q_idx.shape
+    if tuple(k_idx.shape) != (B, N, Di):
+        raise ValueError(f"k_idx shape {tuple(k_idx.shape)} != {(B, N, Di)}")
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, N, topk), dtype=torch.int32, device=q_idx.device)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    dims = make_dims(B, N, Hkv, 1, 64, Di, topk, q_idx.dtype, block_size)
+    _check(lib.msa_index_topk(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                              None, 0, _stream(q_idx.device)))
+    return block_idx
+
+
+def sparse_attn_fwd(q, k, v, block_idx, softmax_scale=0.0, o=None, lse=None, workspace=None,
+                    block_size=128):
+    """Block-sparse GQA attention. q [B,N,Hq,D], k/v [B,N,Hkv,D], block_idx int32
+    [B,Hkv,N,topk] -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])."""
+    lib = load_library()
+    _req(q, "q", ndim=4)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(v, "v", dtype=q.dtype, ndim=4)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D) or Hq % Hkv:
+        raise ValueError("k/v must be [B, N, Hkv, D] with Hq a multiple of Hkv")
+    topk = block_idx.shape[3]
+    if tuple(block_idx.shape) != (B, Hkv, N, topk):
+        raise ValueError("block_idx must be [B, Hkv, N, topk]")
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, 64, topk, q.dtype, block_size)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _req(o, "o", dtype=q.dtype, ndim=4)
+    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_ATTN), q.device, workspace)
+    _check(lib.msa_sparse_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
+                                   float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), nws,
+                                   _stream(q.device)))
+    return o, lse
+
+
+def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_scale=0.0,
+                 kl_rows=None, kl_sum=None, workspace=None, block_size=128):
+    """KL(group-mean main softmax || index softmax) over the selected tokens,
+    per row -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])."""
+    lib = load_library()
+    _req(q, "q", ndim=4)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(q_idx, "q_idx", dtype=q.dtype, ndim=4)
+    _req(k_idx, "k_idx", dtype=q.dtype, ndim=3)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    B, N, Hq, D = q.shape
+    Hkv, Di = q_idx.shape[2], q_idx.shape[3]
+    topk = block_idx.shape[3]
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
+    if kl_rows is None:
+        kl_rows = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
+    if kl_sum is None:
+        kl_sum = torch.empty((1,), dtype=torch.float32, device=q.device)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_KL), q.device, workspace)
+    _check(lib.msa_kl_align_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
+                                _ptr(block_idx), _ptr(lse), float(softmax_scale), float(index_scale),
+                                _ptr(kl_rows), _ptr(kl_sum), _ptr(ws), nws, _stream(q.device)))
+    return kl_rows, kl_sum
+
+
+def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0):
+    """The whole hot path on one stream: selection, then sparse attention."""
+    block_idx = index_topk(q_idx, k_idx, topk)
+    o, lse = sparse_attn_fwd(q, k, v, block_idx, softmax_scale)
+    return block_idx, o, lse

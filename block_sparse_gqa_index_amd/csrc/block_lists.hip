@@ -1,0 +1,145 @@
+// Inversion of the block selection: for every (batch, group, key block) the
+// list of query rows that kept that block as a non-local block, cut into work
+// items of at most kSeg rows. Used by the attention and KL kernels that iterate
+// over key blocks.
+#include "msa_common.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+// ---------------------------------------------------------------- inversion --
+
+__global__ void fill_i32_kernel(int32_t* p, size_t n, int32_t v) {
+    for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n; x += (size_t)gridDim.x * blockDim.x)
+        p[x] = v;
+}
+
+// One thread per (b, g, i) row: count the row's non-local blocks.
+__global__ void count_kernel(const int32_t* __restrict__ block_idx, int32_t* __restrict__ counts,
+                             int64_t rows, int N, int k, int nb) {
+    const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const int i = (int)(r % N);
+    const int64_t bg = r / N;
+    const int L = i / kBlock;
+    const int32_t* row = block_idx + r * k;
+    for (int s = 0; s + 1 < k; ++s) {   // a non-local block never sits in the last slot
+        const int j = row[s];
+        if (j >= 0 && j < L) atomicAdd(&counts[bg * nb + j], 1);
+    }
+}
+
+// Single work-group exclusive scan over the (b, g, j) keys: list offsets and
+// work-item offsets; also clears the scatter cursors.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ item_offsets,
+                                                    int32_t* __restrict__ cursor,
+                                                    int32_t* __restrict__ total_items, int n_keys) {
+    __shared__ int64_t s_sum[1024];
+    __shared__ int64_t s_items[1024];
+    const int t = threadIdx.x;
+    const int per = (n_keys + 1023) / 1024;
+    const int lo = min(n_keys, t * per), hi = min(n_keys, lo + per);
+    int64_t a = 0, it = 0;
+    for (int x = lo; x < hi; ++x) {
+        a += counts[x];
+        it += (counts[x] + kSeg - 1) / kSeg;
+    }
+    s_sum[t] = a;
+    s_items[t] = it;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {   // inclusive Hillis-Steele scan
+        int64_t va = 0, vi = 0;
+        if (t >= off) { va = s_sum[t - off]; vi = s_items[t - off]; }
+        __syncthreads();
+        s_sum[t] += va;
+        s_items[t] += vi;
+        __syncthreads();
+    }
+    int64_t run = s_sum[t] - a, run_it = s_items[t] - it;
+    for (int x = lo; x < hi; ++x) {
+        offsets[x] = (int32_t)run;
+        item_offsets[x] = (int32_t)run_it;
+        cursor[x] = 0;
+        run += counts[x];
+        run_it += (counts[x] + kSeg - 1) / kSeg;
+    }
+    if (t == 1023) total_items[0] = (int32_t)s_items[1023];
+}
+
+// One thread per row: append (i << 5 | slot) to the list of every non-local block.
+__global__ void scatter_kernel(const int32_t* __restrict__ block_idx, const int32_t* __restrict__ offsets,
+                               int32_t* __restrict__ cursor, int32_t* __restrict__ list, int64_t rows,
+                               int N, int k, int nb) {
+    const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const int i = (int)(r % N);
+    const int64_t bg = r / N;
+    const int L = i / kBlock;
+    const int32_t* row = block_idx + r * k;
+    for (int s = 0; s + 1 < k; ++s) {
+        const int j = row[s];
+        if (j >= 0 && j < L) {
+            const int64_t key = bg * nb + j;
+            const int at = offsets[key] + atomicAdd(&cursor[key], 1);
+            list[at] = (i << 5) | s;
+        }
+    }
+}
+
+// One thread per key: its work items (key, first list entry, entry count).
+__global__ void items_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                             const int32_t* __restrict__ item_offsets, int4* __restrict__ items, int n_keys) {
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n_keys) return;
+    const int c = counts[x];
+    int at = item_offsets[x];
+    for (int u = 0; u * kSeg < c; ++u) items[at++] = make_int4(x, offsets[x] + u * kSeg, min(kSeg, c - u * kSeg), 0);
+}
+
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+ListLayout list_layout(const LaunchDims& d, size_t base) {
+    ListLayout w{};
+    const size_t n_keys = (size_t)d.B * d.Hkv * d.nb;
+    const size_t kp = d.k > 1 ? (size_t)(d.k - 1) : 0;
+    w.max_entries = (size_t)d.B * d.Hkv * d.N * kp;
+    w.n_keys = n_keys;
+    w.max_items = (w.max_entries + kSeg - 1) / kSeg + n_keys;
+    size_t off = align_up(base);
+    w.counts = off;        off = align_up(off + n_keys * 4);
+    w.offsets = off;       off = align_up(off + n_keys * 4);
+    w.item_offsets = off;  off = align_up(off + n_keys * 4);
+    w.cursor = off;        off = align_up(off + n_keys * 4);
+    w.total = off;         off = align_up(off + 4);
+    w.items = off;         off = align_up(off + w.max_items * 16);
+    w.list = off;          off = align_up(off + w.max_entries * 4);
+    w.end = off;
+    w.has_nonlocal = kp > 0 && d.nb > 1;
+    return w;
+}
+
+void launch_build_lists(const LaunchDims& d, const int32_t* block_idx, unsigned char* ws, const ListLayout& L,
+                        hipStream_t st) {
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* item_offsets = reinterpret_cast<int32_t*>(ws + L.item_offsets);
+    int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.cursor);
+    int32_t* total = reinterpret_cast<int32_t*>(ws + L.total);
+    int4* items = reinterpret_cast<int4*>(ws + L.items);
+    int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
+    const int64_t rows = (int64_t)d.B * d.Hkv * d.N;
+    const int nk = (int)L.n_keys;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, (size_t)nk, 0);
+    hipLaunchKernelGGL(count_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, counts,
+                       rows, d.N, d.k, d.nb);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, item_offsets, cursor, total, nk);
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, offsets,
+                       cursor, list, rows, d.N, d.k, d.nb);
+    hipLaunchKernelGGL(items_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, offsets, item_offsets, items,
+                       nk);
+}
+
+}  // namespace msa

@@ -1,0 +1,232 @@
+// Index branch of MSA: causal index scores -> block max-pool -> forced-local,
+// exp-free top-k, fused in one kernel (gfx950).
+//
+// Method: MiniMax Sparse Attention (MSA) article on 7minutos.es, section "Cómo
+// funcionan las dos ramas" (one index-query head per group against one shared
+// index-key head, block max-pooling, top-k per query and group with the local
+// block always kept) and section "El codiseño del kernel" (softmax keeps the
+// order, so the ranking runs on raw scores: no max/exp/sum before selection).
+// The Flash-MSA article (tech.kuratif.com) describes the proxy pass as a
+// stream over keys that keeps running top-k candidates and accumulates no
+// output; this kernel does the same with a CDNA4 layout:
+//
+//  * A work-group owns 128*NT (query, group) rows of one query block. Rows of a
+//    query block share one candidate range (blocks j < L), so no causal mask is
+//    needed anywhere: the local block is forced in and never scored.
+//  * The rows' index queries stay in VGPRs as the B operand of
+//    v_mfma_f32_32x32x16_bf16 for the whole kernel; each key block of k_idx
+//    (128 keys x Di) is staged once per work-group in LDS (double-buffered,
+//    16-byte padded rows) and read as the A operand, so the product is S^T:
+//    every lane's 16 accumulators belong to ONE query row. The 128-key block max
+//    is then 4 x 16 in-lane maxima plus one half-wave swap (v_permlane32_swap).
+//  * Each lane keeps the running top-(k-1) of its rows in registers, sorted by
+//    score; blocks arrive in ascending id order, so "strictly greater" is the
+//    whole tie-break (an equal score never displaces a lower id).
+//  * Work-groups are numbered heaviest query block first (longest-processing-
+//    time order over the triangular load).
+#include "msa_common.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+template <int SLOTS>
+__device__ __forceinline__ void topk_insert(float (&sc)[SLOTS], int (&id)[SLOTS], float x, int j) {
+    if (!(x > sc[SLOTS - 1])) return;
+    float cs = x;
+    int ci = j;
+    bool ins = false;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+        const bool take = ins | (cs > sc[s]);
+        const float ts = sc[s];
+        const int ti = id[s];
+        sc[s] = take ? cs : ts;
+        id[s] = take ? ci : ti;
+        cs = take ? ts : cs;
+        ci = take ? ti : ci;
+        ins = take;
+    }
+}
+
+template <int SLOTS>
+__device__ __forceinline__ void sort_ascending(int (&v)[SLOTS]) {
+#pragma unroll
+    for (int p = 0; p < SLOTS; ++p) {
+#pragma unroll
+        for (int i = (p & 1); i + 1 < SLOTS; i += 2) {
+            const int a = v[i], b = v[i + 1];
+            v[i] = min(a, b);
+            v[i + 1] = max(a, b);
+        }
+    }
+}
+
+template <typename T, int DI, int NT, int SLOTS>
+__global__ __launch_bounds__(256, 1) void index_topk_kernel(
+    const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
+    int B, int N, int Hkv, int k, int nb, int chunks) {
+    constexpr int ES = sizeof(T);
+    constexpr int ROWB = DI * ES + 16;       // padded LDS row, bytes
+    constexpr int KS = DI / 16;              // 16-deep slices of the contraction
+    constexpr int CPR = DI * ES / 16;        // 16-byte chunks per key row
+    constexpr int CPT = kBlock * CPR / 256;  // chunks per thread per key block
+    constexpr int NO = NT >= 2 ? NT / 2 : 1; // rows each lane keeps a top-k list for
+    __shared__ __align__(16) unsigned char lds[2][kBlock * ROWB];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int per_qb = B * chunks;
+    const int qb = nb - 1 - (int)(blockIdx.x / per_qb);
+    const int b = (int)(blockIdx.x % per_qb) / chunks;
+    const int c = (int)(blockIdx.x % chunks);
+    const int r0 = c * (kBlock * NT) + w * (32 * NT);
+    const size_t qrow0 = ((size_t)b * N + (size_t)qb * kBlock) * Hkv;
+
+    // Index queries of this wave's rows: B operand, resident for the whole kernel.
+    Op8<T> bq[NT][KS];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int R = r0 + 32 * t + col;
+        const bool valid = qb * kBlock + R / Hkv < N;
+        const T* src = q_idx + (qrow0 + R) * DI + 8 * half;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (valid) bq[t][s].load(src + 16 * s);
+            else bq[t][s].zero();
+        }
+    }
+
+    float sc[NO][SLOTS];
+    int id[NO][SLOTS];
+    const int nslots = k - 1;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const bool dummy = s < SLOTS - nslots;   // unused slots sit above every score
+            sc[o][s] = dummy ? __builtin_inff() : -__builtin_inff();
+            id[o][s] = dummy ? -2 : -1;
+        }
+    }
+
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
+    uint4 stage[CPT];
+    auto fetch = [&](int j) {
+        const unsigned char* src = kbase + (size_t)j * kBlock * DI * ES;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + 256 * u;
+            stage[u] = *reinterpret_cast<const uint4*>(src + (size_t)ch * 16);
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + 256 * u;
+            const int key = ch / CPR, cc = ch % CPR;
+            *reinterpret_cast<uint4*>(&lds[buf][key * ROWB + cc * 16]) = stage[u];
+        }
+    };
+
+    if (qb > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < qb; ++j) {
+        const int cur = j & 1;
+        if (j + 1 < qb) fetch(j + 1);
+        float bm[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bm[t] = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < kBlock / 32; ++kt) {
+            floatx16 acc[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = zero16();
+            const unsigned char* arow = &lds[cur][(kt * 32 + col) * ROWB + 8 * half * ES];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                Op8<T> a;
+                a.load(arow + 16 * s * ES);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) mma16(acc[t], a, bq[t][s]);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], max16(acc[t]));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], swap_halves(bm[t]));
+#pragma unroll
+        for (int o = 0; o < NO; ++o) {
+            const float x = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
+            topk_insert<SLOTS>(sc[o], id[o], x, j);
+        }
+        if (j + 1 < qb) commit(cur ^ 1);
+        __syncthreads();
+    }
+
+    const int nvalid = min(nslots, qb);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+        const int t = NT >= 2 ? 2 * o + half : 0;
+        const int R = r0 + 32 * t + col;
+        const int pos = qb * kBlock + R / Hkv;
+        const int g = R % Hkv;
+        const bool writer = pos < N && (NT >= 2 || half == 0);
+        int v[SLOTS];
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) v[s] = id[o][s] < 0 ? 0x7fffffff : id[o][s];
+        sort_ascending<SLOTS>(v);
+        if (writer) {
+            int32_t* dst = block_idx + (((size_t)b * Hkv + g) * N + pos) * k;
+#pragma unroll
+            for (int s = 0; s <= SLOTS; ++s) {
+                if (s < k) dst[s] = s < nvalid ? v[s < SLOTS ? s : SLOTS - 1] : (s == nvalid ? qb : -1);
+            }
+        }
+    }
+}
+
+template <typename T, int DI, int NT>
+static hipError_t launch_nt(const LaunchDims& d, const void* q_idx, const void* k_idx,
+                            int32_t* out, hipStream_t st) {
+    const int chunks = d.Hkv / NT;
+    const dim3 grid((unsigned)(d.nb * d.B * chunks));
+    const T* q = static_cast<const T*>(q_idx);
+    const T* kk = static_cast<const T*>(k_idx);
+    if (d.k <= 8)
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, 7>), grid, dim3(256), 0, st, q, kk, out,
+                           d.B, d.N, d.Hkv, d.k, d.nb, chunks);
+    else if (d.k <= 16)
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, 15>), grid, dim3(256), 0, st, q, kk, out,
+                           d.B, d.N, d.Hkv, d.k, d.nb, chunks);
+    else
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, 31>), grid, dim3(256), 0, st, q, kk, out,
+                           d.B, d.N, d.Hkv, d.k, d.nb, chunks);
+    return hipGetLastError();
+}
+
+template <typename T, int DI>
+static hipError_t launch_di(const LaunchDims& d, const void* q_idx, const void* k_idx,
+                            int32_t* out, hipStream_t st) {
+    if constexpr (sizeof(T) == 2) {   // fp32 operands would not fit NT > 1 in VGPRs
+        if (d.Hkv % 4 == 0) return launch_nt<T, DI, 4>(d, q_idx, k_idx, out, st);
+        if (d.Hkv % 2 == 0) return launch_nt<T, DI, 2>(d, q_idx, k_idx, out, st);
+    }
+    return launch_nt<T, DI, 1>(d, q_idx, k_idx, out, st);
+}
+
+hipError_t launch_index_topk(const LaunchDims& d, const void* q_idx, const void* k_idx,
+                             int32_t* block_idx, hipStream_t st) {
+    if (d.B == 0 || d.N == 0) return hipSuccess;
+    if (d.dtype == 0) {
+        return d.Di == 128 ? launch_di<bf16_t, 128>(d, q_idx, k_idx, block_idx, st)
+                           : launch_di<bf16_t, 64>(d, q_idx, k_idx, block_idx, st);
+    }
+    return d.Di == 128 ? launch_di<float, 128>(d, q_idx, k_idx, block_idx, st)
+                       : launch_di<float, 64>(d, q_idx, k_idx, block_idx, st);
+}
+
+}  // namespace msa

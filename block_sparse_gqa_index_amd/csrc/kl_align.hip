@@ -1,0 +1,311 @@
+// KL alignment loss forward of MSA (gfx950).
+//
+// Method: MiniMax Sparse Attention (MSA) article on 7minutos.es, section "Cómo
+// se entrena MSA": the index branch is trained with a KL loss whose teacher is
+// the main-branch distribution averaged over the group's heads, restricted to
+// the selected tokens; the Flash-MSA article (tech.kuratif.com) computes it
+// without materialising either distribution.
+//
+// For a row (b, g, i) with selected tokens T_i:
+//   p_t = (1/G) sum_h exp(z_{h,t} - LSE_h)          (teacher; LSE_h from the main pass)
+//   u_t = index_scale * <q_idx[b,i,g], k_idx[b,t]>    (student logits)
+//   KL  = sum_t p_t (ln p_t - u_t + LSE_u),  LSE_u = ln sum_t exp(u_t)
+// Every term is a sum over tokens, so each kept block contributes five
+// numbers (sum p ln p, sum p u, sum p, max u, sum exp(u - max u)) that merge
+// exactly. Non-local blocks are processed key-block-outer from the same
+// inverted selection as the attention; the local block and the merge run per
+// (batch, query block, group); kl_sum is a fixed-order two-stage reduction.
+#include "msa_common.h"
+#include "msa_internal.h"
+#include "msa_tiles.h"
+
+namespace msa {
+
+constexpr int kKlPart = 8;          // floats per (row, slot) partial record
+constexpr int kRedThreads = 256;
+
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+struct KlAcc {
+    float A, Bs, P, mu, lu;
+};
+
+// Partial sums of one 32-row tile over one 128-key block. With MASK, keys past
+// `p_limit` (the query's offset in its block) are not visible.
+template <int G, bool MASK>
+__device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], floatx16 (&u)[4], float scale_log2, float lse2,
+                                         float iscale, int p_limit, int half) {
+    constexpr float kLn2 = 0.69314718055994531f;
+    KlAcc a{0.f, 0.f, 0.f, -__builtin_inff(), 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+            const bool vis = !MASK || key <= p_limit;
+            const float ph = vis ? exp2f(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
+            const float p = group_sum<G>(ph) * (1.0f / G);
+            const float uu = u[kt][r] * iscale;
+            u[kt][r] = vis ? uu : -__builtin_inff();
+            if (vis) {
+                if (p > 0.f) a.A += p * (__log2f(p) * kLn2);
+                a.Bs += p * uu;
+                a.P += p;
+                a.mu = fmaxf(a.mu, uu);
+            }
+        }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a.lu += __expf(u[kt][r] - a.mu);   // exp(-inf) = 0 for masked keys
+    }
+    if (a.mu == -__builtin_inff()) a.lu = 0.f;
+    a.A += swap_halves(a.A);
+    a.Bs += swap_halves(a.Bs);
+    a.P += swap_halves(a.P);
+    const float omu = swap_halves(a.mu), olu = swap_halves(a.lu);
+    const float m = fmaxf(a.mu, omu);
+    a.lu = (a.mu == -__builtin_inff() ? 0.f : a.lu * __expf(a.mu - m)) +
+           (omu == -__builtin_inff() ? 0.f : olu * __expf(omu - m));
+    a.mu = m;
+    return a;
+}
+
+template <typename T, int D, int DI, int G>
+__global__ __launch_bounds__(256, 1) void kl_nonlocal_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
+    const float* __restrict__ lse, const int32_t* __restrict__ list, const int4* __restrict__ items,
+    const int32_t* __restrict__ total_items, float* __restrict__ part, int N, int Hkv, int nb, int KP,
+    float scale_log2, float iscale) {
+    constexpr int ES = sizeof(T);
+    constexpr int KROWB = D * ES + 16;
+    constexpr int PPT = 32 / G;
+    __shared__ __align__(16) unsigned char lds[kBlock * KROWB + kBlock * (DI * ES + 16)];
+    unsigned char* lds_i = lds + kBlock * KROWB;
+
+    const int total = total_items[0];
+    const int per_xcd = (total + 7) / 8;
+    const int slot_in_xcd = blockIdx.x / 8;
+    if (slot_in_xcd >= per_xcd) return;
+    const int item_id = (blockIdx.x % 8) * per_xcd + slot_in_xcd;
+    if (item_id >= total) return;
+    const int4 it = items[item_id];
+    const int key = it.x, start = it.y, count = it.z;
+    const int j = key % nb;
+    const int g = (key / nb) % Hkv;
+    const int b = key / (nb * Hkv);
+    const int Hq = Hkv * G;
+
+    stage_rows<T, D>(lds, k + ((size_t)b * N + (size_t)j * kBlock) * Hkv * D + (size_t)g * D, (size_t)Hkv * D,
+                     kBlock);
+    stage_rows<T, DI>(lds_i, k_idx + ((size_t)b * N + (size_t)j * kBlock) * DI, DI, kBlock);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int hh = col % G;
+    constexpr float kLog2e = 1.4426950408889634f;
+    for (int base = w * PPT; base < count; base += 4 * PPT) {
+        const int e = base + col / G;
+        const bool valid = e < count;
+        const int packed = list[start + (valid ? e : 0)];
+        const int i = packed >> 5, slot = packed & 31;
+        Op8<T> bq[D / 16];
+        load_q_op<T, D>(bq, q + ((size_t)b * N + i) * Hq * D + (size_t)(g * G + hh) * D, valid, half);
+        Op8<T> bi[DI / 16];
+        load_q_op<T, DI>(bi, q_idx + (((size_t)b * N + i) * Hkv + g) * DI, valid, half);
+        floatx16 s[4], u[4];
+        tile_scores<T, D>(s, bq, lds, col, half);
+        tile_scores<T, DI>(u, bi, lds_i, col, half);
+        const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
+        const KlAcc a = tile_kl<G, false>(s, u, scale_log2, lse2, iscale, 0, half);
+        if (valid && hh == 0 && half == 0) {
+            float* dst = part + ((((size_t)b * Hkv + g) * N + i) * KP + slot) * kKlPart;
+            *reinterpret_cast<float4*>(dst) = make_float4(a.A, a.Bs, a.P, a.mu);
+            dst[4] = a.lu;
+        }
+    }
+}
+
+template <typename T, int D, int DI, int G>
+__global__ __launch_bounds__(256, 1) void kl_local_combine_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
+    const float* __restrict__ lse, const float* __restrict__ part, float* __restrict__ kl_rows, int B, int N,
+    int Hkv, int nb, int topk, int KP, float scale_log2, float iscale) {
+    constexpr int ES = sizeof(T);
+    constexpr int KROWB = D * ES + 16;
+    __shared__ __align__(16) unsigned char lds[kBlock * KROWB + kBlock * (DI * ES + 16)];
+    unsigned char* lds_i = lds + kBlock * KROWB;
+    const int g = blockIdx.x % Hkv;
+    const int b = (blockIdx.x / Hkv) % B;
+    const int qb = blockIdx.x / (Hkv * B);
+    const int Hq = Hkv * G;
+    const int q0 = qb * kBlock;
+    const int valid_keys = min(kBlock, N - q0);
+
+    stage_rows<T, D>(lds, k + ((size_t)b * N + q0) * Hkv * D + (size_t)g * D, (size_t)Hkv * D, valid_keys);
+    stage_rows<T, DI>(lds_i, k_idx + ((size_t)b * N + q0) * DI, DI, valid_keys);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int hh = col % G;
+    const int nnl = min(topk - 1, qb);
+    constexpr float kLog2e = 1.4426950408889634f;
+    for (int tile = w; tile < kBlock * G / 32; tile += 4) {
+        const int p = (tile * 32 + col) / G;
+        const int i = q0 + p;
+        const bool valid = i < N;
+        const int ii = valid ? i : q0;
+        Op8<T> bq[D / 16];
+        load_q_op<T, D>(bq, q + ((size_t)b * N + ii) * Hq * D + (size_t)(g * G + hh) * D, valid, half);
+        Op8<T> bi[DI / 16];
+        load_q_op<T, DI>(bi, q_idx + (((size_t)b * N + ii) * Hkv + g) * DI, valid, half);
+        floatx16 s[4], u[4];
+        tile_scores<T, D>(s, bq, lds, col, half);
+        tile_scores<T, DI>(u, bi, lds_i, col, half);
+        const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
+        KlAcc a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, p, half);
+
+        const float* src = part + (((size_t)b * Hkv + g) * N + ii) * KP * kKlPart;
+        for (int sl = 0; sl < nnl; ++sl) {
+            const float4 x = *reinterpret_cast<const float4*>(src + sl * kKlPart);
+            const float xl = src[sl * kKlPart + 4];
+            a.A += x.x;
+            a.Bs += x.y;
+            a.P += x.z;
+            const float m = fmaxf(a.mu, x.w);
+            a.lu = a.lu * __expf(a.mu - m) + xl * __expf(x.w - m);
+            a.mu = m;
+        }
+        const float lse_u = a.mu + __logf(a.lu);
+        if (valid && hh == 0 && half == 0) kl_rows[((size_t)b * Hkv + g) * N + i] = a.A - a.Bs + lse_u * a.P;
+    }
+}
+
+// Fixed-order two-stage sum of kl_rows (deterministic for a given size).
+__global__ __launch_bounds__(kRedThreads) void kl_reduce_partial(const float* __restrict__ x, size_t n,
+                                                                 double* __restrict__ partial) {
+    __shared__ double s[kRedThreads];
+    const size_t per = (n + gridDim.x - 1) / gridDim.x;
+    const size_t lo = min(n, blockIdx.x * per), hi = min(n, lo + per);
+    double acc = 0.0;
+    for (size_t t = lo + threadIdx.x; t < hi; t += kRedThreads) acc += (double)x[t];
+    s[threadIdx.x] = acc;
+    __syncthreads();
+    for (int off = kRedThreads / 2; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = s[0];
+}
+
+__global__ __launch_bounds__(kRedThreads) void kl_reduce_final(const double* __restrict__ partial, int n,
+                                                               float* __restrict__ out) {
+    __shared__ double s[kRedThreads];
+    double acc = 0.0;
+    for (int t = threadIdx.x; t < n; t += kRedThreads) acc += partial[t];
+    s[threadIdx.x] = acc;
+    __syncthreads();
+    for (int off = kRedThreads / 2; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = (float)s[0];
+}
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int red_blocks_for(size_t rows) {
+    const size_t want = (rows + 16383) / 16384;
+    return (int)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
+}
+
+KlWorkspace kl_workspace_layout(const LaunchDims& d) {
+    KlWorkspace w{};
+    w.lists = list_layout(d, 0);
+    const size_t rows = (size_t)d.B * d.Hkv * d.N;
+    w.red_blocks = red_blocks_for(rows);
+    size_t off = w.lists.has_nonlocal ? w.lists.end : 0;
+    w.part = off;  off = align_up(off + (w.lists.has_nonlocal ? w.lists.max_entries * kKlPart * 4 : 0));
+    w.red = off;   off = align_up(off + (size_t)w.red_blocks * 8);
+    w.bytes = off;
+    return w;
+}
+
+template <typename T, int D, int DI, int G>
+static hipError_t launch_kl_t(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
+                              const void* k_idx, const int32_t* block_idx, const float* lse, float scale,
+                              float iscale, float* kl_rows, float* kl_sum, unsigned char* ws, hipStream_t st) {
+    const KlWorkspace L = kl_workspace_layout(d);
+    const float scale_log2 = scale * 1.4426950408889634f;
+    const int KP = d.k > 1 ? d.k - 1 : 1;
+    const T* tq = static_cast<const T*>(q);
+    const T* tk = static_cast<const T*>(k);
+    const T* tqi = static_cast<const T*>(q_idx);
+    const T* tki = static_cast<const T*>(k_idx);
+    float* part = nullptr;
+    if (L.lists.has_nonlocal) {
+        launch_build_lists(d, block_idx, ws, L.lists, st);
+        part = reinterpret_cast<float*>(ws + L.part);
+        const size_t grid = (L.lists.max_items + 7) / 8 * 8;
+        hipLaunchKernelGGL((kl_nonlocal_kernel<T, D, DI, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tqi,
+                           tki, lse, reinterpret_cast<const int32_t*>(ws + L.lists.list),
+                           reinterpret_cast<const int4*>(ws + L.lists.items),
+                           reinterpret_cast<const int32_t*>(ws + L.lists.total), part, d.N, d.Hkv, d.nb, KP,
+                           scale_log2, iscale);
+    }
+    hipLaunchKernelGGL((kl_local_combine_kernel<T, D, DI, G>), dim3((unsigned)(d.nb * d.B * d.Hkv)), dim3(256), 0,
+                       st, tq, tk, tqi, tki, lse, part, kl_rows, d.B, d.N, d.Hkv, d.nb,
+                       L.lists.has_nonlocal ? d.k : 1, KP, scale_log2, iscale);
+    double* red = reinterpret_cast<double*>(ws + L.red);
+    const size_t rows = (size_t)d.B * d.Hkv * d.N;
+    hipLaunchKernelGGL(kl_reduce_partial, dim3(L.red_blocks), dim3(kRedThreads), 0, st, kl_rows, rows, red);
+    hipLaunchKernelGGL(kl_reduce_final, dim3(1), dim3(kRedThreads), 0, st, red, L.red_blocks, kl_sum);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int DI>
+static hipError_t launch_kl_g(const LaunchDims& d, const void* q, const void* k, const void* qi, const void* ki,
+                              const int32_t* bi, const float* lse, float sc, float isc, float* rows, float* sum,
+                              unsigned char* ws, hipStream_t st) {
+    switch (d.G) {
+        case 1: return launch_kl_t<T, D, DI, 1>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+        case 2: return launch_kl_t<T, D, DI, 2>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+        case 4: return launch_kl_t<T, D, DI, 4>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+        case 8: return launch_kl_t<T, D, DI, 8>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+        case 16: return launch_kl_t<T, D, DI, 16>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+        default: return launch_kl_t<T, D, DI, 32>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+    }
+}
+
+template <typename T>
+static hipError_t launch_kl_dt(const LaunchDims& d, const void* q, const void* k, const void* qi, const void* ki,
+                               const int32_t* bi, const float* lse, float sc, float isc, float* rows, float* sum,
+                               unsigned char* ws, hipStream_t st) {
+    if (d.D == 128 && d.Di == 128) return launch_kl_g<T, 128, 128>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+    if (d.D == 128) return launch_kl_g<T, 128, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+    if (d.Di == 128) return launch_kl_g<T, 64, 128>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+    return launch_kl_g<T, 64, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+}
+
+hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx, const void* k_idx,
+                           const int32_t* block_idx, const float* lse, float scale, float index_scale,
+                           float* kl_rows, float* kl_sum, void* ws, hipStream_t st) {
+    if (d.B == 0 || d.N == 0) {
+        hipLaunchKernelGGL(kl_reduce_final, dim3(1), dim3(kRedThreads), 0, st, (const double*)nullptr, 0, kl_sum);
+        return hipGetLastError();
+    }
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    if (d.dtype == 0)
+        return launch_kl_dt<bf16_t>(d, q, k, q_idx, k_idx, block_idx, lse, scale, index_scale, kl_rows, kl_sum, w, st);
+    return launch_kl_dt<float>(d, q, k, q_idx, k_idx, block_idx, lse, scale, index_scale, kl_rows, kl_sum, w, st);
+}
+
+}  // namespace msa

@@ -1,0 +1,139 @@
+// C ABI of the MSA forward path: argument validation, workspace sizing and
+// dispatch to the kernels. Every check here runs on the host before any HIP
+// call, so a rejected call enqueues nothing and writes nothing.
+#include "../../include/msa.h"
+
+#include <limits.h>
+
+#include "msa_internal.h"
+
+namespace {
+
+using msa::LaunchDims;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_upto32(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32; }
+
+// Shape checks shared by all entry points; fills `out` on success. The index
+// selection does not look at group_size/head_dim and the attention does not
+// look at index_dim, so those are only checked for the ops that use them.
+int check_dims(const msa_dims* d, int op, LaunchDims* out) {
+    if (!d) return MSA_ERR_NULL;
+    const bool uses_heads = op != MSA_OP_INDEX, uses_index = op != MSA_OP_ATTN;
+    if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || d->topk < 1 ||
+        (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
+        return MSA_ERR_SHAPE;
+    if (d->block_size != 128 || d->topk > 32 || (d->dtype != MSA_BF16 && d->dtype != MSA_F32) ||
+        d->causal != 1 || (uses_heads && (!pow2_upto32(d->group_size) || (d->head_dim != 64 && d->head_dim != 128))) ||
+        (uses_index && d->index_dim != 64 && d->index_dim != 128))
+        return MSA_ERR_UNSUPPORTED;
+    // Positions are packed into 26 bits of a list entry; row counts and list
+    // offsets are 32-bit.
+    if (d->seqlen >= (int64_t(1) << 26)) return MSA_ERR_SHAPE;
+    if (d->kv_heads > 4096) return MSA_ERR_SHAPE;
+    const int64_t rows = d->batch * d->seqlen * d->kv_heads;
+    if (d->batch > INT_MAX || rows > INT_MAX || rows * (int64_t)d->topk > INT_MAX) return MSA_ERR_SHAPE;
+    out->B = (int)d->batch;
+    out->N = (int)d->seqlen;
+    out->Hkv = d->kv_heads;
+    out->G = uses_heads ? d->group_size : 1;
+    out->D = uses_heads ? d->head_dim : 0;
+    out->Di = uses_index ? d->index_dim : 0;
+    out->k = d->topk;
+    out->nb = (int)((d->seqlen + 127) / 128);
+    out->dtype = d->dtype;
+    return MSA_OK;
+}
+
+bool empty(const LaunchDims& L) { return L.B == 0 || L.N == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char* msa_strerror(int status) {
+    switch (status) {
+        case MSA_OK: return "ok";
+        case MSA_ERR_NULL: return "a required pointer is NULL";
+        case MSA_ERR_SHAPE: return "invalid or too large problem sizes";
+        case MSA_ERR_UNSUPPORTED: return "unsupported sizes or dtype (block_size 128, topk 1..32, group_size "
+                                         "power of two <= 32, head/index dim 64 or 128, bf16/fp32, causal)";
+        case MSA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case MSA_ERR_WORKSPACE: return "workspace missing or smaller than msa_workspace_bytes";
+        case MSA_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t msa_workspace_bytes(const msa_dims* dims, int op) {
+    LaunchDims L;
+    if (op != MSA_OP_INDEX && op != MSA_OP_ATTN && op != MSA_OP_KL) return 0;
+    if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
+    switch (op) {
+        case MSA_OP_INDEX: return 0;
+        case MSA_OP_ATTN: return msa::attn_workspace_layout(L).bytes;
+        case MSA_OP_KL: return msa::kl_workspace_layout(L).bytes;
+        default: return 0;
+    }
+}
+
+int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, int32_t* block_idx,
+                   void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_INDEX, &L);
+    if (st != MSA_OK) return st;
+    if (empty(L)) return MSA_OK;
+    if (!q_idx || !k_idx || !block_idx) return MSA_ERR_NULL;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_idx)) return MSA_ERR_ALIGN;
+    return hip_status(msa::launch_index_topk(L, q_idx, k_idx, block_idx, static_cast<hipStream_t>(stream)));
+}
+
+int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                        const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_ATTN, &L);
+    if (st != MSA_OK) return st;
+    if (empty(L)) return MSA_OK;
+    if (!q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(o) ||
+        !aligned16(lse))
+        return MSA_ERR_ALIGN;
+    const size_t need = msa::attn_workspace_layout(L).bytes;
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    return hip_status(msa::launch_sparse_attn(L, q, k, v, block_idx, scale, o, lse, ws,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
+                     const void* k_idx, const int32_t* block_idx, const float* lse, float softmax_scale,
+                     float index_scale, float* kl_rows, float* kl_sum, void* ws, size_t ws_bytes,
+                     void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_KL, &L);
+    if (st != MSA_OK) return st;
+    if (!kl_sum) return MSA_ERR_NULL;
+    if (!q || !k || !q_idx || !k_idx || !block_idx || !lse || !kl_rows) {
+        if (!empty(L)) return MSA_ERR_NULL;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_idx) ||
+        !aligned16(lse) || !aligned16(kl_rows))
+        return MSA_ERR_ALIGN;
+    const size_t need = msa::kl_workspace_layout(L).bytes;
+    if (!empty(L) && need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    const float iscale = index_scale > 0.f ? index_scale : 1.0f / sqrtf((float)L.Di);
+    // kl_sum is written even for an empty problem (the sum of nothing is 0).
+    return hip_status(msa::launch_kl_align(L, q, k, q_idx, k_idx, block_idx, lse, scale, iscale, kl_rows,
+                                           kl_sum, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Device helpers shared by the MSA kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16 and, for
+// fp32 inputs, eight v_mfma_f32_32x32x2_f32 covering the same 16-deep slice):
+//   A operand (32 x 16): lane l supplies row  m = l % 32, k = 8*(l/32) .. +7
+//   B operand (16 x 32): lane l supplies col  n = l % 32, k = 8*(l/32) .. +7
+//   C/D (32 x 32, 16 fp32 per lane): lane l holds column n = l % 32 and rows
+//       m = 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.
+// A 16-deep slice can use any fixed assignment of its 16 k-indices to the two
+// half-waves as long as A and B agree, which is what lets the fp32 path reuse
+// the bf16 operand layout (8 consecutive elements per lane).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 128;   // Bk: tokens per key block
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+// Eight consecutive elements of one matrix-core operand row/column.
+template <typename T> struct Op8;
+template <> struct Op8<bf16_t> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const void* p) {
+        v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+    }
+    __device__ __forceinline__ void zero() { v = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+};
+template <> struct Op8<float> {
+    float v[8];
+    __device__ __forceinline__ void load(const void* p) {
+        const float4* q = reinterpret_cast<const float4*>(p);
+        float4 a = q[0], b = q[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+};
+
+// acc(32x32) += A(32x16) * B(16x32) for one 16-deep slice.
+__device__ __forceinline__ void mma16(floatx16& acc, const Op8<bf16_t>& a, const Op8<bf16_t>& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(floatx16& acc, const Op8<float>& a, const Op8<float>& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx16 zero16() {
+    floatx16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    return z;
+}
+
+// Value held by lane l ^ 32 (the other half-wave).
+__device__ __forceinline__ float swap_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+__device__ __forceinline__ float max16(const floatx16& a) {
+    float m0 = max3f(a[0], a[1], a[2]);
+    float m1 = max3f(a[3], a[4], a[5]);
+    float m2 = max3f(a[6], a[7], a[8]);
+    float m3 = max3f(a[9], a[10], a[11]);
+    float m4 = max3f(a[12], a[13], a[14]);
+    return max3f(max3f(m0, m1, m2), max3f(m3, m4, a[15]), m0);
+}
+
+}  // namespace msa

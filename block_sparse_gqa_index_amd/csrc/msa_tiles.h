@@ -1,0 +1,169 @@
+// Tile-level building blocks shared by the attention and KL kernels: one
+// 32-row tile of query rows against one LDS-resident block of 128 keys.
+//
+// S^T = K Q^T on the matrix cores (A = keys from LDS, B = query rows held in
+// VGPRs) leaves one query row per lane: lane l holds row l % 32 and keys
+// 8*(r/4) + 4*(l/32) + r%4 (+32 per key tile) in accumulator r. P^T = the
+// probabilities in that layout feed O^T = V^T P^T as the B operand, with V^T
+// read from LDS under the same key assignment.
+#pragma once
+
+#include "msa_common.h"
+
+namespace msa {
+
+// K block [128][D] -> LDS rows of D*ES+16 bytes; V block -> LDS V^T rows of
+// 128*ES+16 bytes. Keys at or beyond `valid_keys` are zero-filled.
+template <typename T, int D>
+struct KVTile {
+    static constexpr int ES = sizeof(T);
+    static constexpr int KROWB = D * ES + 16;
+    static constexpr int VROWB = kBlock * ES + 16;
+    static constexpr int BYTES = kBlock * KROWB + D * VROWB;
+
+    __device__ static void stage(unsigned char* lds, const T* kb, const T* vb, size_t row_stride,
+                                 int valid_keys) {
+        constexpr int CPR = D * ES / 16;               // 16-byte chunks per key row
+        constexpr int EPC = 16 / ES;                   // elements per chunk
+        unsigned char* vt = lds + kBlock * KROWB;
+        for (int ch = threadIdx.x; ch < kBlock * CPR; ch += blockDim.x) {
+            const int key = ch / CPR, cc = ch % CPR;
+            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+            if (key < valid_keys) {
+                kv = *reinterpret_cast<const uint4*>(kb + key * row_stride + cc * EPC);
+                vv = *reinterpret_cast<const uint4*>(vb + key * row_stride + cc * EPC);
+            }
+            *reinterpret_cast<uint4*>(lds + key * KROWB + cc * 16) = kv;
+            const T* ve = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                *reinterpret_cast<T*>(vt + (cc * EPC + e) * VROWB + key * ES) = ve[e];
+        }
+    }
+};
+
+// A plain [128][W] tile (rows of W*ES+16 bytes, the K layout of KVTile<T, W>).
+template <typename T, int W>
+__device__ void stage_rows(unsigned char* lds, const T* src, size_t row_stride, int valid_keys) {
+    constexpr int ES = sizeof(T);
+    constexpr int ROWB = W * ES + 16;
+    constexpr int CPR = W * ES / 16;
+    constexpr int EPC = 16 / ES;
+    for (int ch = threadIdx.x; ch < kBlock * CPR; ch += blockDim.x) {
+        const int key = ch / CPR, cc = ch % CPR;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (key < valid_keys) x = *reinterpret_cast<const uint4*>(src + key * row_stride + cc * EPC);
+        *reinterpret_cast<uint4*>(lds + key * ROWB + cc * 16) = x;
+    }
+}
+
+template <typename T> struct PType;
+template <> struct PType<bf16_t> {
+    static __device__ __forceinline__ void pack(Op8<bf16_t>& o, const float* p) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)f32_to_bf16(p[2 * e]) | ((uint32_t)f32_to_bf16(p[2 * e + 1]) << 16);
+        o.v = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+};
+template <> struct PType<float> {
+    static __device__ __forceinline__ void pack(Op8<float>& o, const float* p) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.v[e] = p[e];
+    }
+};
+
+// V^T operand for 16-key slice c: keys 16c + {4h..4h+3} and 16c + 8 + {4h..4h+3}.
+template <typename T>
+__device__ __forceinline__ void load_vt_op(Op8<T>& a, const unsigned char* vrow, int c, int half) {
+    constexpr int ES = sizeof(T);
+    const unsigned char* p0 = vrow + (16 * c + 4 * half) * ES;
+    const unsigned char* p1 = vrow + (16 * c + 8 + 4 * half) * ES;
+    if constexpr (ES == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p0);
+        const uint2 y = *reinterpret_cast<const uint2*>(p1);
+        a.v = __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
+    } else {
+        const float4 x = *reinterpret_cast<const float4*>(p0);
+        const float4 y = *reinterpret_cast<const float4*>(p1);
+        a.v[0] = x.x; a.v[1] = x.y; a.v[2] = x.z; a.v[3] = x.w;
+        a.v[4] = y.x; a.v[5] = y.y; a.v[6] = y.z; a.v[7] = y.w;
+    }
+}
+
+// One 32-row tile against one LDS-resident 128-key block:
+// s[kt] = S^T tile kt (32 keys x 32 rows), scores only.
+template <typename T, int D>
+__device__ __forceinline__ void tile_scores(floatx16 (&s)[4], const Op8<T> (&bq)[D / 16],
+                                            const unsigned char* lds, int col, int half) {
+    using KV = KVTile<T, D>;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        s[kt] = zero16();
+        const unsigned char* arow = lds + (kt * 32 + col) * KV::KROWB + 8 * half * KV::ES;
+#pragma unroll
+        for (int sl = 0; sl < D / 16; ++sl) {
+            Op8<T> a;
+            a.load(arow + 16 * sl * KV::ES);
+            mma16(s[kt], a, bq[sl]);
+        }
+    }
+}
+
+// o[dt] += V^T(dt) * P^T with P taken from the score accumulators.
+template <typename T, int D>
+__device__ __forceinline__ void tile_pv(floatx16 (&o)[D / 32], const floatx16 (&p)[4],
+                                        const unsigned char* lds, int col, int half) {
+    using KV = KVTile<T, D>;
+    const unsigned char* vt = lds + kBlock * KV::KROWB;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = p[c / 2][8 * (c % 2) + e];
+        Op8<T> bp;
+        PType<T>::pack(bp, pe);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            Op8<T> a;
+            load_vt_op<T>(a, vt + (dt * 32 + col) * KV::VROWB, c, half);
+            mma16(o[dt], a, bp);
+        }
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_q_op(Op8<T> (&bq)[D / 16], const T* row, bool valid, int half) {
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) {
+        if (valid) bq[sl].load(row + 16 * sl + 8 * half);
+        else bq[sl].zero();
+    }
+}
+
+// Row softmax over the lane's 64 scores + the other half's 64 (log2 domain):
+// returns the row max of z = s * scale_log2 and the row sum of 2^(z - max),
+// and overwrites the scores with those probabilities.
+__device__ __forceinline__ void tile_softmax(floatx16 (&s)[4], float scale_log2, float& mx, float& sum) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) m = fmaxf(m, max16(s[kt]));
+    m = fmaxf(m, swap_halves(m));
+    const float mz = m * scale_log2;
+    float l = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = exp2f(fmaf(s[kt][r], scale_log2, -mz));
+            s[kt][r] = p;
+            l += p;
+        }
+    }
+    l += swap_halves(l);
+    mx = mz;
+    sum = l;
+}
+
+}  // namespace msa

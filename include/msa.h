@@ -1,0 +1,168 @@
+/*
+ * msa.h - C ABI of the MSA (MiniMax Sparse Attention) forward hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (MiniMax Sparse Attention (MSA) article on 7minutos.es, sections
+ * "¿Qué es MSA?" and "Cómo funcionan las dos ramas"): an index branch scores
+ * every causally visible key token with one index-query head per GQA group
+ * against one shared index-key head, max-pools the scores over blocks of Bk
+ * tokens, and keeps for every (query, group) the k best blocks, the block that
+ * holds the query always among them; the main branch then runs exact softmax
+ * GQA attention over the causally visible tokens of the kept blocks only. The
+ * KL alignment loss (same article, section "Cómo se entrena MSA") compares the
+ * group-mean main distribution with the index distribution over those tokens.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, densely
+ *    packed (row-major, last dimension contiguous) and 16-byte aligned.
+ *  - Batch B, tokens N (queries = keys), groups Hkv (= KV heads = index-query
+ *    heads), G query heads per group (Hq = Hkv*G), head dim D, index dim Di,
+ *    block size Bk, blocks kept k. Query head h belongs to group h / G.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    on it and outputs are valid once it has completed; the calls never
+ *    synchronise, never allocate and never free.
+ *  - Every status other than MSA_OK and MSA_ERR_HIP is returned before any
+ *    device work is enqueued, with no output written. MSA_ERR_HIP reports a
+ *    failed launch (the outputs are then unspecified).
+ *  - Calls are thread-safe; calls that share a workspace must not overlap.
+ *  - Results are deterministic: the same inputs give bitwise the same block
+ *    indices, O, LSE and kl_rows (kl_sum too: it is reduced in a fixed order).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define MSA_API __attribute__((visibility("default")))
+#else
+#define MSA_API
+#endif
+
+/* Element type of every floating-point input (and of O). */
+enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1 };
+
+/* Selector for msa_workspace_bytes. */
+enum msa_op { MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2 };
+
+enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    MSA_ERR_SHAPE = 2,       /* negative sizes, or a size that overflows indexing */
+    MSA_ERR_UNSUPPORTED = 3, /* a size or dtype this build has no kernel for      */
+    MSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned           */
+    MSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than msa_workspace_bytes */
+    MSA_ERR_HIP = 6          /* a HIP launch failed                               */
+};
+
+/*
+ * Problem sizes. Supported: batch >= 0, seqlen >= 0 (any value; the last block
+ * may be partial), kv_heads >= 1, group_size in {1,2,4,8,16,32}, head_dim and
+ * index_dim in {64,128}, block_size == 128, topk in [1,32], dtype MSA_BF16 or
+ * MSA_F32, causal == 1. batch == 0 or seqlen == 0 is a valid empty problem.
+ */
+typedef struct msa_dims {
+    int64_t batch;
+    int64_t seqlen;
+    int32_t kv_heads;
+    int32_t group_size;
+    int32_t head_dim;
+    int32_t index_dim;
+    int32_t block_size;
+    int32_t topk;
+    int32_t dtype;
+    int32_t causal;
+} msa_dims;
+
+/*
+ * Index branch: block selection.
+ * Defined by the MSA article (7minutos.es), "Cómo funcionan las dos ramas"
+ * (scores of visible keys, max-pool per block, top-k per query and group, local
+ * block always kept) and "El codiseño del kernel" (exp-free top-k on the raw
+ * scores); the Flash-MSA article (tech.kuratif.com) sets the local block's
+ * score to +inf so the window stays open.
+ *
+ *   Uses batch, seqlen, kv_heads, index_dim, block_size, topk, dtype and
+ *   causal of `dims` (group_size and head_dim are not read).
+ *   q_idx     [B, N, Hkv, Di]  index queries, dtype
+ *   k_idx     [B, N, Di]       shared index keys, dtype
+ *   block_idx [B, Hkv, N, k]   int32 OUTPUT. For query i (local block L = i/Bk)
+ *             and group g: the block ids j < L with the k-1 largest
+ *             m_j = max_{t in block j} <q_idx[b,i,g], k_idx[b,t]> (ties: lower
+ *             id first; all of them if fewer than k-1), plus L; written in
+ *             ascending order (so L is the last valid entry), padded with -1 to
+ *             length k. Scores accumulate in fp32; selection is exact when the
+ *             scores are (e.g. integer-valued inputs with |score| < 2^24).
+ *   ws        not used (may be NULL; msa_workspace_bytes(.., MSA_OP_INDEX) = 0)
+ */
+MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx,
+                   int32_t* block_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Main branch: block-sparse GQA attention forward.
+ * Defined by the MSA article (7minutos.es), "Cómo funcionan las dos ramas":
+ * exact scaled-dot-product softmax over the causally visible tokens of the
+ * group's kept blocks, each query head with its own query; the Flash-MSA
+ * article keeps the LSE of every row for the backward.
+ *
+ *   Uses every field of `dims` except index_dim.
+ *   q         [B, N, Hq, D]   dtype
+ *   k, v      [B, N, Hkv, D]  dtype
+ *   block_idx [B, Hkv, N, k]  int32, as written by msa_index_topk (per row:
+ *             ascending distinct ids <= L, L last, -1 padding). Other contents
+ *             are undefined behaviour.
+ *   softmax_scale  sigma in z = sigma * <q, k_t>; <= 0 selects 1/sqrt(D).
+ *   o         [B, N, Hq, D]   OUTPUT, dtype: sum_t exp(z_t - LSE) v_t
+ *   lse       [B, Hq, N]      OUTPUT, fp32 natural-log log-sum-exp of z_t
+ *   ws        device workspace of at least msa_workspace_bytes(dims,
+ *             MSA_OP_ATTN) bytes (partial results of the non-local blocks).
+ */
+MSA_API int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                        const int32_t* block_idx, float softmax_scale, void* o, float* lse,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * KL alignment loss forward.
+ * Defined by the MSA article (7minutos.es), "Cómo se entrena MSA": the teacher
+ * is the main-branch distribution averaged over the group's heads over the
+ * selected tokens, the student the index branch's distribution over the same
+ * tokens; the Flash-MSA article computes the loss without materialising the
+ * distributions.
+ *
+ *   q, k, q_idx, k_idx, block_idx  as above
+ *   lse       [B, Hq, N] fp32, the main-branch LSE of the same inputs (as
+ *             written by msa_sparse_attn_fwd)
+ *   softmax_scale  as above; index_scale: student logits are
+ *             index_scale * <q_idx, k_idx_t>; <= 0 selects 1/sqrt(Di).
+ *   kl_rows   [B, Hkv, N] OUTPUT fp32: sum_t p_t (ln p_t - ln s_t) with
+ *             p_t = mean_h exp(z_{h,t} - LSE_h), s_t the student softmax.
+ *   kl_sum    [1] OUTPUT fp32 (overwritten): sum of kl_rows, fixed order.
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_KL) bytes.
+ */
+MSA_API int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
+                     const void* k_idx, const int32_t* block_idx, const float* lse,
+                     float softmax_scale, float index_scale, float* kl_rows, float* kl_sum,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the given entry point needs for these sizes; 0 if the sizes
+ * are invalid or the op needs none. Pure host arithmetic. */
+MSA_API size_t msa_workspace_bytes(const msa_dims* dims, int op);
+
+/* Static description of a status code (never NULL). */
+MSA_API const char* msa_strerror(int status);
+
+/* MSA_ABI_VERSION of the library. */
+MSA_API int msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -115,27 +115,31 @@ def _pad(ids, k):
     return list(ids) + [-1] * (k - len(ids))
 
 
-def index_topk_rows(q_idx, k_idx, positions, Bk, k, key_chunk=16384):
+def index_topk_rows(q_idx, k_idx, positions, Bk, k, key_chunk=16384, q_rows=None):
     """Block indices at the given (b, i) positions.
 
-    q_idx [B, N, Hkv, Di], k_idx [B, N, Di]; positions int [M, 2].
+    q_idx [B, N, Hkv, Di], k_idx [B, N, Di]; positions int [M, 2]. Instead of
+    q_idx, ``q_rows`` [M, Hkv, Di] may give just the rows at the positions.
     Returns int32 [M, Hkv, k] (ascending ids, -1 padded).
 
     Same definition as ``visible_block_scores`` + ``select_blocks`` per row; the
     scores of all requested rows of a batch entry are obtained from one matrix
     product per key chunk (a chunk holds whole blocks), then max-pooled per block.
     """
-    qa = _arr(q_idx)
     ka = _arr(k_idx)
-    Hkv = qa.shape[2]
     positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    if q_rows is None:
+        qa = _arr(q_idx)
+        q_rows = qa[positions[:, 0], positions[:, 1]]
+    q_rows = _arr(q_rows)
+    Hkv, Di = q_rows.shape[1], q_rows.shape[2]
     out = np.full((len(positions), Hkv, k), -1, dtype=np.int32)
     key_chunk = max(Bk, key_chunk // Bk * Bk)
     for b in np.unique(positions[:, 0]):
         sel = np.nonzero(positions[:, 0] == b)[0]
         pos_i = positions[sel, 1]
         Lmax = int(pos_i.max()) // Bk
-        qrows = np.asarray(qa[b, pos_i], dtype=np.float64).reshape(-1, qa.shape[3])  # [P*Hkv, Di]
+        qrows = np.asarray(q_rows[sel], dtype=np.float64).reshape(-1, Di)           # [P*Hkv, Di]
         m = np.empty((Lmax, qrows.shape[0]))
         for t0 in range(0, Lmax * Bk, key_chunk):
             t1 = min(Lmax * Bk, t0 + key_chunk)
@@ -193,7 +197,7 @@ def _softmax_stats(z):
     return lse, e / s
 
 
-def attention_rows(q, k, v, block_idx_rows, positions, Bk, scale=None):
+def attention_rows(q, k, v, block_idx_rows, positions, Bk, scale=None, q_rows=None):
     """Main-branch output at the given (b, i) positions.
 
     [P2] "Cómo funcionan las dos ramas": exact scaled-dot-product softmax over
@@ -201,18 +205,20 @@ def attention_rows(q, k, v, block_idx_rows, positions, Bk, scale=None):
     its group. [P1] paragraph on the forward: the output goes on and the LSE is
     kept for the backward.
 
-    q [B,N,Hq,D], k/v [B,N,Hkv,D], block_idx_rows int [M, Hkv, k] for the M
-    positions. Returns (O [M, Hq, D], LSE [M, Hq]) in float64, where
+    q [B,N,Hq,D] (or ``q_rows`` [M, Hq, D], the rows at the positions), k/v
+    [B,N,Hkv,D], block_idx_rows int [M, Hkv, k] for the M positions. Returns (O [M, Hq, D], LSE [M, Hq]) in float64, where
     z_t = scale * <q, k_t>, LSE = ln sum_t exp z_t, O = sum_t exp(z_t - LSE) v_t.
     """
-    q = _arr(q)
     kk = _arr(k)
     vv = _arr(v)
-    Hq, D = q.shape[2], q.shape[3]
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    if q_rows is None:
+        q_rows = _arr(q)[positions[:, 0], positions[:, 1]]
+    q_rows = _arr(q_rows)
+    Hq, D = q_rows.shape[1], q_rows.shape[2]
     Hkv = kk.shape[2]
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
-    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
     M = len(positions)
     O = np.zeros((M, Hq, D))
     LSE = np.zeros((M, Hq))
@@ -224,8 +230,8 @@ def attention_rows(q, k, v, block_idx_rows, positions, Bk, scale=None):
             for r in rows:
                 i = int(positions[r, 1])
                 T = token_set(block_idx_rows[r, g], i, Bk)
-                qh = np.asarray(q[b, i, g * G:(g + 1) * G], dtype=np.float64)   # [G, D]
-                z = scale * (qh @ kg[T].T)                                      # [G, |T|]
+                qh = np.asarray(q_rows[r, g * G:(g + 1) * G], dtype=np.float64)  # [G, D]
+                z = scale * (qh @ kg[T].T)                                       # [G, |T|]
                 lse, p = _softmax_stats(z)
                 LSE[r, g * G:(g + 1) * G] = lse
                 O[r, g * G:(g + 1) * G] = p @ vg[T]
@@ -244,7 +250,7 @@ def sparse_attention(q, k, v, block_idx, Bk, scale=None):
 
 
 def kl_rows(q, k, q_idx, k_idx, block_idx_rows, positions, Bk, scale=None,
-            index_scale=None):
+            index_scale=None, q_rows=None, qi_rows=None):
     """KL-alignment loss per (position, group) at the given positions.
 
     [P2] "Cómo se entrena MSA": a KL alignment loss matches the index branch's
@@ -256,29 +262,34 @@ def kl_rows(q, k, q_idx, k_idx, block_idx_rows, positions, Bk, scale=None,
     Teacher p_t = mean_h softmax_t(scale <q_h, k_t>); student
     s_t = softmax_t(index_scale <q_idx, k_idx_t>); both over the row's selected
     tokens T_i. Returns float64 [M, Hkv] with sum_t p_t (ln p_t - ln s_t)
-    (terms with p_t = 0 contribute 0).
+    (terms with p_t = 0 contribute 0). ``q_rows`` [M, Hq, D] / ``qi_rows``
+    [M, Hkv, Di] may replace q / q_idx by their rows at the positions.
     """
-    q = _arr(q)
     kk = _arr(k)
-    qi = _arr(q_idx)
     ki = _arr(k_idx)
-    Hq, D = q.shape[2], q.shape[3]
-    Hkv, Di = kk.shape[2], qi.shape[3]
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    if q_rows is None:
+        q_rows = _arr(q)[positions[:, 0], positions[:, 1]]
+    if qi_rows is None:
+        qi_rows = _arr(q_idx)[positions[:, 0], positions[:, 1]]
+    q_rows, qi_rows = _arr(q_rows), _arr(qi_rows)
+    Hq, D = q_rows.shape[1], q_rows.shape[2]
+    Hkv, Di = kk.shape[2], qi_rows.shape[2]
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
     index_scale = (1.0 / math.sqrt(Di) if index_scale is None or index_scale <= 0
                    else float(index_scale))
     out = np.zeros((len(positions), Hkv))
-    for r, (b, i) in enumerate(np.asarray(positions)):
+    for r, (b, i) in enumerate(positions):
         for g in range(Hkv):
             T = token_set(block_idx_rows[r, g], int(i), Bk)
-            qh = np.asarray(q[b, i, g * G:(g + 1) * G], dtype=np.float64)
+            qh = np.asarray(q_rows[r, g * G:(g + 1) * G], dtype=np.float64)
             kt = np.asarray(kk[b, T, g], dtype=np.float64)
             z = scale * (qh @ kt.T)
             _, ph = _softmax_stats(z)
             p = ph.mean(axis=0)
             u = index_scale * (np.asarray(ki[b, T], dtype=np.float64)
-                               @ np.asarray(qi[b, i, g], dtype=np.float64))
+                               @ np.asarray(qi_rows[r, g], dtype=np.float64))
             lse_u, _ = _softmax_stats(u[None, :])
             log_s = u - lse_u[0]
             nz = p > 0

@@ -23,6 +23,7 @@ class Workload:
     seed: int = 0
     stripe_frac: float = 0.0       # fraction of key blocks that get a k_idx bias
     stripe_bias: float = 0.0
+    index_absmax: int = 4          # index inputs are integers in [-index_absmax, index_absmax]
     with_kl: bool = False
     sampled_rows: int = 0          # 0 = check every query position
 

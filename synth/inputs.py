@@ -14,12 +14,12 @@ def torch_dtype(name: str) -> torch.dtype:
     return _TORCH_DTYPE[name]
 
 
-def _randint(shape, gen, device, dtype):
+def _randint(shape, gen, device, dtype, absmax=4):
     out = torch.empty(shape, dtype=dtype, device=device)
     flat = out.view(-1)
     for s in range(0, flat.numel(), _CHUNK):
         e = min(flat.numel(), s + _CHUNK)
-        flat[s:e] = torch.randint(-4, 5, (e - s,), generator=gen, device=device).to(dtype)
+        flat[s:e] = torch.randint(-absmax, absmax + 1, (e - s,), generator=gen, device=device).to(dtype)
     return out
 
 
@@ -56,8 +56,8 @@ def make_inputs(w: Workload, device="cpu", seed=None, kinds=("q_idx", "k_idx", "
     B, N, Hkv, G, D, Di, Bk = (w.batch, w.seqlen, w.kv_heads, w.group_size,
                                w.head_dim, w.index_dim, w.block_size)
     out = {}
-    out["q_idx"] = _randint((B, N, Hkv, Di), gen, device, dt)
-    k_idx = _randint((B, N, Di), gen, device, dt)
+    out["q_idx"] = _randint((B, N, Hkv, Di), gen, device, dt, w.index_absmax)
+    k_idx = _randint((B, N, Di), gen, device, dt, w.index_absmax)
     stripes = stripe_blocks(w, gen, device)
     for j in stripes.tolist():
         k_idx[:, j * Bk:min(N, (j + 1) * Bk), :] += w.stripe_bias

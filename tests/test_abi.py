@@ -1,0 +1,147 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every
+function include/msa.h declares, and rejects bad arguments with the documented
+status before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_gqa_index_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(msa.LIB_PATH):
+        from block_sparse_gqa_index_amd import build
+        build.build()
+    return msa.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^MSA_API\s+[\w\s\*]*?\b(msa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(msa.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", msa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing but the C ABI is exported
+    assert {n for n in exported if not n.startswith("_")} == set(_declared())
+
+
+def test_version_and_strings(lib):
+    assert lib.msa_abi_version() == 1
+    for s in range(7):
+        assert lib.msa_strerror(s)
+    assert lib.msa_strerror(99) == b"unknown status"
+
+
+def _dims(**kw):
+    base = dict(batch=1, seqlen=1024, kv_heads=2, group_size=4, head_dim=128, index_dim=64,
+                topk=16, dtype=msa.MSA_BF16)
+    base.update(kw)
+    return msa.make_dims(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)      # aligned, never dereferenced: every call below is rejected
+MISALIGNED = ctypes.c_void_p(0x1008)
+
+
+def _index(lib, d, q=FAKE, k=FAKE, out=FAKE):
+    return lib.msa_index_topk(ctypes.byref(d), q, k, out, None, 0, None)
+
+
+def _attn(lib, d, ptrs=None, ws=None, nws=0):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
+    p.update(ptrs or {})
+    return lib.msa_sparse_attn_fwd(ctypes.byref(d), p["q"], p["k"], p["v"], p["bi"], 0.0,
+                                   p["o"], p["lse"], ws, nws, None)
+
+
+def _kl(lib, d, ptrs=None, ws=None, nws=0):
+    p = dict(q=FAKE, k=FAKE, qi=FAKE, ki=FAKE, bi=FAKE, lse=FAKE, rows=FAKE, sum=FAKE)
+    p.update(ptrs or {})
+    return lib.msa_kl_align_fwd(ctypes.byref(d), p["q"], p["k"], p["qi"], p["ki"], p["bi"], p["lse"],
+                                0.0, 0.0, p["rows"], p["sum"], ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=64), 3), (dict(topk=0), 2), (dict(topk=33), 3), (dict(dtype=7), 3),
+    (dict(causal=0), 3), (dict(index_dim=96), 3), (dict(kv_heads=0), 2), (dict(seqlen=-1), 2),
+    (dict(batch=-2), 2), (dict(seqlen=1 << 26), 2),
+])
+def test_index_rejects_bad_dims(lib, kw, status):
+    assert _index(lib, _dims(**kw)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 3), (dict(group_size=3), 3), (dict(group_size=64), 3),
+    (dict(block_size=256), 3), (dict(topk=40), 3), (dict(group_size=0), 2),
+])
+def test_attention_rejects_bad_dims(lib, kw, status):
+    assert _attn(lib, _dims(**kw)) == status
+
+
+def test_index_ignores_attention_fields(lib):
+    # group_size/head_dim are not read by the selection: the call goes on to
+    # the pointer checks (NULL output -> MSA_ERR_NULL, not UNSUPPORTED)
+    assert _index(lib, _dims(group_size=3, head_dim=7), out=None) == 1
+
+
+def test_null_and_alignment(lib):
+    d = _dims()
+    assert lib.msa_index_topk(None, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert _index(lib, d, q=None) == 1
+    assert _index(lib, d, k=MISALIGNED) == 4
+    assert _attn(lib, d, {"lse": None}) == 1
+    assert _attn(lib, d, {"v": MISALIGNED}) == 4
+    assert _kl(lib, d, {"sum": None}) == 1
+    assert _kl(lib, d, {"rows": None}) == 1
+    assert _kl(lib, d, {"ki": MISALIGNED}) == 4
+
+
+def test_workspace_checks(lib):
+    d = _dims()
+    need = msa.workspace_bytes(d, msa.MSA_OP_ATTN)
+    assert need > 0
+    assert _attn(lib, d) == 5                           # no workspace
+    assert _attn(lib, d, ws=FAKE, nws=need - 1) == 5    # too small
+    assert _attn(lib, d, ws=MISALIGNED, nws=need) == 5  # misaligned
+    needk = msa.workspace_bytes(d, msa.MSA_OP_KL)
+    assert needk > 0
+    assert _kl(lib, d, ws=FAKE, nws=needk - 1) == 5
+
+
+def test_empty_problems_are_accepted_without_device_work(lib):
+    for kw in (dict(batch=0), dict(seqlen=0)):
+        d = _dims(**kw)
+        assert _index(lib, d, q=None, k=None, out=None) == 0
+        assert _attn(lib, d, {k: None for k in ("q", "k", "v", "bi", "o", "lse")}) == 0
+        assert msa.workspace_bytes(d, msa.MSA_OP_ATTN) == 0
+
+
+def test_workspace_sizes(lib):
+    # a single query block, or k = 1: no non-local block anywhere -> no workspace
+    assert msa.workspace_bytes(_dims(seqlen=128), msa.MSA_OP_ATTN) == 0
+    assert msa.workspace_bytes(_dims(topk=1), msa.MSA_OP_ATTN) == 0
+    assert msa.workspace_bytes(_dims(), msa.MSA_OP_INDEX) == 0
+    assert msa.workspace_bytes(_dims(), 9) == 0
+    # the partial outputs dominate: rows * (k-1) * G * D * 2 bytes for bf16
+    d = _dims(seqlen=131072, kv_heads=8, group_size=8, topk=16)
+    need = msa.workspace_bytes(d, msa.MSA_OP_ATTN)
+    partial = 131072 * 8 * 15 * 8 * 128 * 2
+    assert partial < need < partial * 1.1
+    d32 = _dims(seqlen=131072, kv_heads=8, group_size=8, topk=16, dtype=msa.MSA_F32)
+    assert msa.workspace_bytes(d32, msa.MSA_OP_ATTN) > 1.9 * need
