@@ -75,10 +75,13 @@ __device__ __forceinline__ floatx16 zero16() {
     return z;
 }
 
-// Value held by lane l ^ 32 (the other half-wave).
+// Value held by lane l ^ 32 (the other half-wave). v_permlane32_swap applied
+// to (x, x) leaves every lane with lane (l % 32)'s x in the first result and
+// lane (l % 32 + 32)'s x in the second, so the other half's value is the
+// second result in the lower half and the first in the upper half.
 __device__ __forceinline__ float swap_halves(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]);
+    return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
