@@ -29,6 +29,77 @@ __global__ void count_kernel(const int32_t* __restrict__ block_idx, int32_t* __r
     }
 }
 
+// The same counts from per-work-group LDS histograms: a work-group takes
+// kHistPos consecutive positions of one (b, g) and issues one global atomic per
+// block its rows touched instead of one per entry.
+constexpr int kHistPos = 2048;
+constexpr int kHistMaxBins = 8192;   // 2 x 32 KB of LDS in the scatter pass
+
+__global__ __launch_bounds__(256) void count_hist_kernel(const int32_t* __restrict__ block_idx,
+                                                         int32_t* __restrict__ counts, int N, int k, int nb,
+                                                         int chunks) {
+    extern __shared__ int32_t hist[];
+    const int bg = blockIdx.x / chunks, c = blockIdx.x % chunks;
+    const int p0 = c * kHistPos, p1 = min(N, p0 + kHistPos);
+    const int nbins = (p1 - 1) / kBlock;   // every non-local block of these rows is below this
+    for (int x = threadIdx.x; x < nbins; x += blockDim.x) hist[x] = 0;
+    __syncthreads();
+    for (int i = p0 + threadIdx.x; i < p1; i += blockDim.x) {
+        const int L = i / kBlock;
+        const int32_t* row = block_idx + ((size_t)bg * N + i) * k;
+        for (int s = 0; s + 1 < k; ++s) {
+            const int j = row[s];
+            if (j >= 0 && j < L) atomicAdd(&hist[j], 1);
+        }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < nbins; x += blockDim.x)
+        if (hist[x]) atomicAdd(&counts[(size_t)bg * nb + x], hist[x]);
+}
+
+// Scatter with the same histogram: one global atomic per touched block
+// reserves the work-group's range in that block's list, LDS atomics place the
+// entries inside it.
+__global__ __launch_bounds__(256) void scatter_hist_kernel(const int32_t* __restrict__ block_idx,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ cursor, int32_t* __restrict__ list,
+                                                           int N, int k, int nb, int chunks) {
+    extern __shared__ int32_t sh[];
+    const int bg = blockIdx.x / chunks, c = blockIdx.x % chunks;
+    const int p0 = c * kHistPos, p1 = min(N, p0 + kHistPos);
+    const int nbins = (p1 - 1) / kBlock;
+    int32_t* hist = sh;
+    int32_t* base = sh + nbins;
+    for (int x = threadIdx.x; x < nbins; x += blockDim.x) hist[x] = 0;
+    __syncthreads();
+    for (int i = p0 + threadIdx.x; i < p1; i += blockDim.x) {
+        const int L = i / kBlock;
+        const int32_t* row = block_idx + ((size_t)bg * N + i) * k;
+        for (int s = 0; s + 1 < k; ++s) {
+            const int j = row[s];
+            if (j >= 0 && j < L) atomicAdd(&hist[j], 1);
+        }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < nbins; x += blockDim.x) {
+        const int n = hist[x];
+        if (n) {
+            const size_t key = (size_t)bg * nb + x;
+            base[x] = offsets[key] + atomicAdd(&cursor[key], n);
+        }
+        hist[x] = 0;
+    }
+    __syncthreads();
+    for (int i = p0 + threadIdx.x; i < p1; i += blockDim.x) {
+        const int L = i / kBlock;
+        const int32_t* row = block_idx + ((size_t)bg * N + i) * k;
+        for (int s = 0; s + 1 < k; ++s) {
+            const int j = row[s];
+            if (j >= 0 && j < L) list[base[j] + atomicAdd(&hist[j], 1)] = (i << 5) | s;
+        }
+    }
+}
+
 // Single work-group exclusive scan over the (b, g, j) keys: list offsets and
 // work-item offsets; also clears the scatter cursors.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
@@ -133,11 +204,23 @@ void launch_build_lists(const LaunchDims& d, const int32_t* block_idx, unsigned 
     const int64_t rows = (int64_t)d.B * d.Hkv * d.N;
     const int nk = (int)L.n_keys;
     hipLaunchKernelGGL(fill_i32_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, (size_t)nk, 0);
-    hipLaunchKernelGGL(count_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, counts,
-                       rows, d.N, d.k, d.nb);
+    const bool hist = d.nb <= kHistMaxBins;
+    const int chunks = (d.N + kHistPos - 1) / kHistPos;
+    const unsigned hist_grid = (unsigned)((size_t)d.B * d.Hkv * chunks);
+    const size_t hist_lds = (size_t)d.nb * 4;
+    if (hist)
+        hipLaunchKernelGGL(count_hist_kernel, dim3(hist_grid), dim3(256), hist_lds, st, block_idx, counts, d.N, d.k,
+                           d.nb, chunks);
+    else
+        hipLaunchKernelGGL(count_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, counts,
+                           rows, d.N, d.k, d.nb);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, item_offsets, cursor, total, nk);
-    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, offsets,
-                       cursor, list, rows, d.N, d.k, d.nb);
+    if (hist)
+        hipLaunchKernelGGL(scatter_hist_kernel, dim3(hist_grid), dim3(256), 2 * hist_lds, st, block_idx, offsets,
+                           cursor, list, d.N, d.k, d.nb, chunks);
+    else
+        hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx,
+                           offsets, cursor, list, rows, d.N, d.k, d.nb);
     hipLaunchKernelGGL(items_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, offsets, item_offsets, items,
                        nk);
 }

@@ -10,9 +10,10 @@
 // stream over keys that keeps running top-k candidates and accumulates no
 // output; this kernel does the same with a CDNA4 layout:
 //
-//  * A work-group owns 128*NT (query, group) rows of one query block. Rows of a
-//    query block share one candidate range (blocks j < L), so no causal mask is
-//    needed anywhere: the local block is forced in and never scored.
+//  * A work-group owns 32*NT*WAVES (query, group) rows of one query block
+//    (64 rows per wave, two waves per SIMD for bf16). Rows of a query block
+//    share one candidate range (blocks j < L), so no causal mask is needed
+//    anywhere: the local block is forced in and never scored.
 //  * The rows' index queries stay in VGPRs as the B operand of
 //    v_mfma_f32_32x32x16_bf16 for the whole kernel; each key block of k_idx
 //    (128 keys x Di) is staged once per work-group in LDS (double-buffered,
@@ -61,16 +62,18 @@ __device__ __forceinline__ void sort_ascending(int (&v)[SLOTS]) {
     }
 }
 
-template <typename T, int DI, int NT, int SLOTS>
-__global__ __launch_bounds__(256, 1) void index_topk_kernel(
+template <typename T, int DI, int NT, int WAVES, int SLOTS>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     int B, int N, int Hkv, int k, int nb, int chunks) {
+    constexpr int NTHR = 64 * WAVES;
     constexpr int ES = sizeof(T);
-    constexpr int ROWB = DI * ES + 16;       // padded LDS row, bytes
-    constexpr int KS = DI / 16;              // 16-deep slices of the contraction
-    constexpr int CPR = DI * ES / 16;        // 16-byte chunks per key row
-    constexpr int CPT = kBlock * CPR / 256;  // chunks per thread per key block
-    constexpr int NO = NT >= 2 ? NT / 2 : 1; // rows each lane keeps a top-k list for
+    constexpr int ROWB = DI * ES + 16;        // padded LDS row, bytes
+    constexpr int KS = DI / 16;               // 16-deep slices of the contraction
+    constexpr int CPR = DI * ES / 16;         // 16-byte chunks per key row
+    constexpr int CPT = kBlock * CPR / NTHR;  // chunks per thread per key block
+    constexpr int NO = NT >= 2 ? NT / 2 : 1;  // rows each lane keeps a top-k list for
+    static_assert(CPT * NTHR == kBlock * CPR, "staging must tile the block");
     __shared__ __align__(16) unsigned char lds[2][kBlock * ROWB];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(256, 1) void index_topk_kernel(
     const int qb = nb - 1 - (int)(blockIdx.x / per_qb);
     const int b = (int)(blockIdx.x % per_qb) / chunks;
     const int c = (int)(blockIdx.x % chunks);
-    const int r0 = c * (kBlock * NT) + w * (32 * NT);
+    const int r0 = c * (32 * NT * WAVES) + w * (32 * NT);
     const size_t qrow0 = ((size_t)b * N + (size_t)qb * kBlock) * Hkv;
 
     // Index queries of this wave's rows: B operand, resident for the whole kernel.
@@ -110,33 +113,30 @@ __global__ __launch_bounds__(256, 1) void index_topk_kernel(
     }
 
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
-    uint4 stage[CPT];
-    auto fetch = [&](int j) {
-        const unsigned char* src = kbase + (size_t)j * kBlock * DI * ES;
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ch = tid + 256 * u;
-            stage[u] = *reinterpret_cast<const uint4*>(src + (size_t)ch * 16);
-        }
-    };
-    auto commit = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ch = tid + 256 * u;
-            const int key = ch / CPR, cc = ch % CPR;
-            *reinterpret_cast<uint4*>(&lds[buf][key * ROWB + cc * 16]) = stage[u];
-        }
-    };
-
     if (qb > 0) {
-        fetch(0);
-        commit(0);
+        u32x4 stage[CPT];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u)
+            stage[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(tid + NTHR * u) * 16);
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + NTHR * u;
+            *reinterpret_cast<u32x4*>(&lds[0][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[u];
+        }
     }
     __syncthreads();
 
     for (int j = 0; j < qb; ++j) {
         const int cur = j & 1;
-        if (j + 1 < qb) fetch(j + 1);
+        const bool more = j + 1 < qb;
+        // Next key block: global -> VGPRs now, VGPRs -> LDS after this block's math.
+        u32x4 stage[CPT];
+        {
+            const unsigned char* src = kbase + (size_t)(more ? j + 1 : j) * kBlock * DI * ES;
+#pragma unroll
+            for (int u = 0; u < CPT; ++u)
+                stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+        }
         float bm[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) bm[t] = -__builtin_inff();
@@ -163,7 +163,13 @@ __global__ __launch_bounds__(256, 1) void index_topk_kernel(
             const float x = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
             topk_insert<SLOTS>(sc[o], id[o], x, j);
         }
-        if (j + 1 < qb) commit(cur ^ 1);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int ch = tid + NTHR * u;
+                *reinterpret_cast<u32x4*>(&lds[cur ^ 1][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[u];
+            }
+        }
         __syncthreads();
     }
 
@@ -189,33 +195,35 @@ __global__ __launch_bounds__(256, 1) void index_topk_kernel(
     }
 }
 
-template <typename T, int DI, int NT>
-static hipError_t launch_nt(const LaunchDims& d, const void* q_idx, const void* k_idx,
-                            int32_t* out, hipStream_t st) {
-    const int chunks = d.Hkv / NT;
-    const dim3 grid((unsigned)(d.nb * d.B * chunks));
+template <typename T, int DI, int NT, int WAVES>
+static hipError_t launch_cfg(const LaunchDims& d, const void* q_idx, const void* k_idx, int32_t* out,
+                             hipStream_t st) {
+    const int chunks = (kBlock * d.Hkv) / (32 * NT * WAVES);
+    const dim3 grid((unsigned)(d.nb * d.B * chunks)), block(64 * WAVES);
     const T* q = static_cast<const T*>(q_idx);
     const T* kk = static_cast<const T*>(k_idx);
     if (d.k <= 8)
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, 7>), grid, dim3(256), 0, st, q, kk, out,
-                           d.B, d.N, d.Hkv, d.k, d.nb, chunks);
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 7>), grid, block, 0, st, q, kk, out, d.B, d.N,
+                           d.Hkv, d.k, d.nb, chunks);
     else if (d.k <= 16)
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, 15>), grid, dim3(256), 0, st, q, kk, out,
-                           d.B, d.N, d.Hkv, d.k, d.nb, chunks);
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 15>), grid, block, 0, st, q, kk, out, d.B, d.N,
+                           d.Hkv, d.k, d.nb, chunks);
     else
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, 31>), grid, dim3(256), 0, st, q, kk, out,
-                           d.B, d.N, d.Hkv, d.k, d.nb, chunks);
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 31>), grid, block, 0, st, q, kk, out, d.B, d.N,
+                           d.Hkv, d.k, d.nb, chunks);
     return hipGetLastError();
 }
 
+// A work-group holds 32*NT*WAVES rows of one query block (128*Hkv rows), so
+// WAVES is the largest of 8/4/2 that divides the block's rows evenly.
 template <typename T, int DI>
 static hipError_t launch_di(const LaunchDims& d, const void* q_idx, const void* k_idx,
                             int32_t* out, hipStream_t st) {
-    if constexpr (sizeof(T) == 2) {   // fp32 operands would not fit NT > 1 in VGPRs
-        if (d.Hkv % 4 == 0) return launch_nt<T, DI, 4>(d, q_idx, k_idx, out, st);
-        if (d.Hkv % 2 == 0) return launch_nt<T, DI, 2>(d, q_idx, k_idx, out, st);
-    }
-    return launch_nt<T, DI, 1>(d, q_idx, k_idx, out, st);
+    constexpr int NT = sizeof(T) == 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
+    const int rows = kBlock * d.Hkv;
+    if (rows % (32 * NT * 8) == 0) return launch_cfg<T, DI, NT, 8>(d, q_idx, k_idx, out, st);
+    if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, q_idx, k_idx, out, st);
+    return launch_cfg<T, DI, NT, 2>(d, q_idx, k_idx, out, st);
 }
 
 hipError_t launch_index_topk(const LaunchDims& d, const void* q_idx, const void* k_idx,

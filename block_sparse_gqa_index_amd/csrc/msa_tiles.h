@@ -108,6 +108,9 @@ __device__ __forceinline__ void tile_scores(floatx16 (&s)[4], const Op8<T> (&bq)
             a.load(arow + 16 * sl * KV::ES);
             mma16(s[kt], a, bq[sl]);
         }
+        // keep the scheduler from hoisting every LDS operand load of the tile
+        // (that would need 4*D/16 operand registers live at once)
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -130,6 +133,7 @@ __device__ __forceinline__ void tile_pv(floatx16 (&o)[D / 32], const floatx16 (&
             load_vt_op<T>(a, vt + (dt * 32 + col) * KV::VROWB, c, half);
             mma16(o[dt], a, bp);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

@@ -40,7 +40,43 @@ namespace msa {
 // slice of D stored lane-major (slot dt*32 + 16*h + r holds
 // d = dt*32 + 8*(r/4) + 4*h + r%4), plse[.][G] natural-log LSE.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256, 1) void attn_nonlocal_kernel(
+__device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restrict__ plse, size_t pidx, int hh,
+                                              int half, const floatx16 (&o)[D / 32], float mz, float l) {
+    const float inv = 1.f / l;
+    T* dst = po + (pidx * G + hh) * D + 16 * half;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        if constexpr (sizeof(T) == 2) {
+            u32x4 w0, w1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                w0[r] = (uint32_t)f32_to_bf16(o[dt][2 * r] * inv) | ((uint32_t)f32_to_bf16(o[dt][2 * r + 1] * inv) << 16);
+                w1[r] = (uint32_t)f32_to_bf16(o[dt][8 + 2 * r] * inv) |
+                        ((uint32_t)f32_to_bf16(o[dt][8 + 2 * r + 1] * inv) << 16);
+            }
+            u32x4* d4 = reinterpret_cast<u32x4*>(dst + dt * 32);
+            d4[0] = w0;
+            d4[1] = w1;
+        } else {
+            floatx4* d4 = reinterpret_cast<floatx4*>(dst + dt * 32);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                floatx4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = o[dt][4 * r + e] * inv;
+                d4[r] = x;
+            }
+        }
+    }
+    if (half == 0) plse[pidx * G + hh] = (mz + __log2f(l)) * 0.69314718055994531f;
+}
+
+// One work-group per work item (batch, group, key block j, <= kSeg query
+// positions that kept j). K_j and V_j^T are staged in LDS once; each wave
+// streams 32-row tiles through them, loading the next tile's query rows while
+// the current tile is on the matrix cores.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ list, const int4* __restrict__ items, const int32_t* __restrict__ total_items,
     T* __restrict__ po, float* __restrict__ plse, int N, int Hkv, int nb, int KP, float scale_log2) {
@@ -62,67 +98,99 @@ __global__ __launch_bounds__(256, 1) void attn_nonlocal_kernel(
     const int b = key / (nb * Hkv);
     const int Hq = Hkv * G;
 
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int hh = col % G, pp = col / G;
+    const int stride = 4 * PPT;
+    const T* qbase = q + (size_t)b * N * Hq * D + (size_t)(g * G + hh) * D;
+
+    // First tile's list entry and query rows are requested before the K/V staging.
+    int base = w * PPT;
+    int e_cur = list[start + min(base + pp, count - 1)];
+    Op8<T> q_cur[D / 16];
+    load_q_op<T, D>(q_cur, qbase + (size_t)(e_cur >> 5) * Hq * D, base + pp < count, half);
+    int e_nxt = list[start + min(base + stride + pp, count - 1)];
+
     const size_t kv_row = (size_t)Hkv * D;
     const size_t kv_off = ((size_t)b * N + (size_t)j * kBlock) * kv_row + (size_t)g * D;
     KV::stage(lds, k + kv_off, v + kv_off, kv_row, kBlock);
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int half = lane >> 5, col = lane & 31;
-    const int hh = col % G;
-    for (int base = w * PPT; base < count; base += 4 * PPT) {
-        const int e = base + col / G;
-        const bool valid = e < count;
-        const int packed = list[start + (valid ? e : 0)];
-        const int i = packed >> 5, slot = packed & 31;
-        Op8<T> bq[D / 16];
-        load_q_op<T, D>(bq, q + ((size_t)b * N + i) * Hq * D + (size_t)(g * G + hh) * D, valid, half);
+    for (; base < count; base += stride) {
+        const bool valid = base + pp < count;
+        const int nbase = base + stride;
+        Op8<T> q_nxt[D / 16];
+        load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, nbase + pp < count, half);
+        const int e_nxt2 = list[start + min(nbase + stride + pp, count - 1)];
 
         floatx16 s[4];
-        tile_scores<T, D>(s, bq, lds, col, half);
+        tile_scores<T, D>(s, q_cur, lds, col, half);
         float mz, l;
         tile_softmax(s, scale_log2, mz, l);
         floatx16 o[D / 32];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
         tile_pv<T, D>(o, s, lds, col, half);
-
         if (valid) {
-            const float inv = 1.f / l;
-            const size_t pidx = (((size_t)b * Hkv + g) * N + i) * KP + slot;
-            T* dst = po + (pidx * G + hh) * D + 16 * half;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                if constexpr (sizeof(T) == 2) {
-                    uint32_t wv[8];
-#pragma unroll
-                    for (int r = 0; r < 8; ++r)
-                        wv[r] = (uint32_t)f32_to_bf16(o[dt][2 * r] * inv) |
-                                ((uint32_t)f32_to_bf16(o[dt][2 * r + 1] * inv) << 16);
-                    uint4* d4 = reinterpret_cast<uint4*>(dst + dt * 32);
-                    d4[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                    d4[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-                } else {
-                    float4* d4 = reinterpret_cast<float4*>(dst + dt * 32);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        d4[r] = make_float4(o[dt][4 * r] * inv, o[dt][4 * r + 1] * inv,
-                                            o[dt][4 * r + 2] * inv, o[dt][4 * r + 3] * inv);
-                }
-            }
-            if (half == 0) plse[pidx * G + hh] = (mz + __log2f(l)) * 0.69314718055994531f;
+            const int i = e_cur >> 5, slot = e_cur & 31;
+            store_partial<T, D, G>(po, plse, (((size_t)b * Hkv + g) * N + i) * KP + slot, hh, half, o, mz, l);
         }
+#pragma unroll
+        for (int sl = 0; sl < D / 16; ++sl) q_cur[sl] = q_nxt[sl];
+        e_cur = e_nxt;
+        e_nxt = e_nxt2;
     }
 }
 
 // ------------------------------------------------ local block + combination --
 
+// Adds w * (partial O of one slot) to the lane's output accumulators; `x`
+// holds the lane's 16 values per 32-wide slice of D in the stored order.
+template <typename T, int D>
+struct PartialRow {
+    static constexpr int NV = sizeof(T) == 2 ? D / 16 : D / 8;   // 16-byte vectors per lane
+    u32x4 x[NV];
+    __device__ __forceinline__ void load(const T* src) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) x[v] = reinterpret_cast<const u32x4*>(src)[(v / 2) * 4 + (v % 2)];
+    }
+    __device__ __forceinline__ void load_f32(const T* src) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) x[v] = reinterpret_cast<const u32x4*>(src)[(v / 4) * 8 + (v % 4)];
+    }
+    __device__ __forceinline__ void fetch(const T* src) {
+        if constexpr (sizeof(T) == 2) load(src);
+        else load_f32(src);
+    }
+    __device__ __forceinline__ void axpy(floatx16 (&acc)[D / 32], float w) const {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const uint32_t wv = x[2 * dt + r / 4][r % 4];
+                    acc[dt][2 * r] += w * __uint_as_float(wv << 16);
+                    acc[dt][2 * r + 1] += w * __uint_as_float(wv & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[dt][r] += w * __uint_as_float(x[4 * dt + r / 4][r % 4]);
+            }
+        }
+    }
+};
+
+// One work-group per (batch, query block, group): the causal local block for
+// all 128*G rows from LDS-resident K/V, then the merge with the rows'
+// non-local partials (log2 domain, slot order), which are fetched four slots
+// at a time to keep enough loads in flight.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256, 1) void attn_local_combine_kernel(
+__global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ po, const float* __restrict__ plse, T* __restrict__ o, float* __restrict__ lse,
     int B, int N, int Hkv, int nb, int topk, int KP, float scale_log2) {
     using KV = KVTile<T, D>;
+    constexpr int BATCH = 4;
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
     const int g = blockIdx.x % Hkv;
     const int b = (blockIdx.x / Hkv) % B;
@@ -147,8 +215,9 @@ __global__ __launch_bounds__(256, 1) void attn_local_combine_kernel(
         const int p = (tile * 32 + col) / G;   // position within the block
         const int i = q0 + p;
         const bool valid = i < N;
+        const int ii = valid ? i : q0;
         Op8<T> bq[D / 16];
-        load_q_op<T, D>(bq, q + ((size_t)b * N + (valid ? i : q0)) * Hq * D + (size_t)h * D, valid, half);
+        load_q_op<T, D>(bq, q + ((size_t)b * N + ii) * Hq * D + (size_t)h * D, valid, half);
 
         floatx16 s[4];
         tile_scores<T, D>(s, bq, lds, col, half);
@@ -167,13 +236,14 @@ __global__ __launch_bounds__(256, 1) void attn_local_combine_kernel(
         for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
         tile_pv<T, D>(acc, s, lds, col, half);
 
-        // Merge with the non-local partials (log2 domain), slot order.
+        // LSE over the local block and every non-local slot (log2 domain).
         const float lse_loc = mz + __log2f(l);
-        const size_t prow = (((size_t)b * Hkv + g) * N + (valid ? i : q0)) * KP;
+        const size_t prow = (((size_t)b * Hkv + g) * N + ii) * KP;
+        const float* pl = plse + prow * G + hh;
         float mx = lse_loc;
-        for (int sl = 0; sl < nnl; ++sl) mx = fmaxf(mx, plse[(prow + sl) * G + hh] * kLog2e);
+        for (int sl = 0; sl < nnl; ++sl) mx = fmaxf(mx, pl[sl * G] * kLog2e);
         float tot = exp2f(lse_loc - mx);
-        for (int sl = 0; sl < nnl; ++sl) tot += exp2f(plse[(prow + sl) * G + hh] * kLog2e - mx);
+        for (int sl = 0; sl < nnl; ++sl) tot += exp2f(pl[sl * G] * kLog2e - mx);
         const float lse_all = mx + __log2f(tot);
         const float wl = exp2f(lse_loc - lse_all) / l;
 #pragma unroll
@@ -181,32 +251,15 @@ __global__ __launch_bounds__(256, 1) void attn_local_combine_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[dt][r] *= wl;
         }
-        for (int sl = 0; sl < nnl; ++sl) {
-            const float ws = exp2f(plse[(prow + sl) * G + hh] * kLog2e - lse_all);
-            const T* src = po + ((prow + sl) * G + hh) * D + 16 * half;
+        const T* pbase = po + (prow * G + hh) * D + 16 * half;
+        for (int sl0 = 0; sl0 < nnl; sl0 += BATCH) {
+            PartialRow<T, D> pr[BATCH];
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                if constexpr (sizeof(T) == 2) {
-                    const uint4* s4 = reinterpret_cast<const uint4*>(src + dt * 32);
-                    const uint4 x0 = s4[0], x1 = s4[1];
-                    const uint32_t wv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            for (int u = 0; u < BATCH; ++u)
+                if (sl0 + u < nnl) pr[u].fetch(pbase + (size_t)(sl0 + u) * G * D);
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        acc[dt][2 * r] += ws * bf16_to_f32((bf16_t)(wv[r] & 0xffffu));
-                        acc[dt][2 * r + 1] += ws * bf16_to_f32((bf16_t)(wv[r] >> 16));
-                    }
-                } else {
-                    const float4* s4 = reinterpret_cast<const float4*>(src + dt * 32);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float4 x = s4[r];
-                        acc[dt][4 * r] += ws * x.x;
-                        acc[dt][4 * r + 1] += ws * x.y;
-                        acc[dt][4 * r + 2] += ws * x.z;
-                        acc[dt][4 * r + 3] += ws * x.w;
-                    }
-                }
-            }
+            for (int u = 0; u < BATCH; ++u)
+                if (sl0 + u < nnl) pr[u].axpy(acc, exp2f(pl[(sl0 + u) * G] * kLog2e - lse_all));
         }
         if (valid) {
             T* dst = o + ((size_t)b * N + i) * Hq * D + (size_t)h * D;
@@ -222,8 +275,10 @@ __global__ __launch_bounds__(256, 1) void attn_local_combine_kernel(
                                             ((uint32_t)f32_to_bf16(acc[dt][4 * rq + 3]) << 16);
                         *reinterpret_cast<uint2*>(d4) = make_uint2(a0, a1);
                     } else {
-                        *reinterpret_cast<float4*>(d4) = make_float4(acc[dt][4 * rq], acc[dt][4 * rq + 1],
-                                                                      acc[dt][4 * rq + 2], acc[dt][4 * rq + 3]);
+                        floatx4 x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * rq + e];
+                        *reinterpret_cast<floatx4*>(d4) = x;
                     }
                 }
             }
