@@ -109,6 +109,8 @@ def main():
     ap.add_argument("--workload", default="n128k", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MSA forward path here runs on a single MI355X "
@@ -116,8 +118,16 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    w = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
+    if args.copy_mib:
+        # Reference for HBM byte counters: one launch reads and writes exactly this many bytes.
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_mib << 20}), flush=True)
+        return
+    w = CONFIGS[args.workload]
     msa.load_library()
     log(f"[bench] workload {w.name}: generating inputs on {dev}")
     x = make_inputs(w, device=dev)

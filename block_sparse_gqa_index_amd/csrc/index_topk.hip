@@ -30,9 +30,11 @@
 
 namespace msa {
 
+// Inserts (x, j) into the descending list; a no-op when x does not beat the
+// last entry (then no comparison below succeeds), so it runs without a branch
+// and can be scheduled under the matrix-core work of the next key block.
 template <int SLOTS>
 __device__ __forceinline__ void topk_insert(float (&sc)[SLOTS], int (&id)[SLOTS], float x, int j) {
-    if (!(x > sc[SLOTS - 1])) return;
     float cs = x;
     int ci = j;
     bool ins = false;
@@ -126,6 +128,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     }
     __syncthreads();
 
+    // Block j's candidate (per owned row) is inserted while block j+1 is on the
+    // matrix cores; each key tile's max overlaps the next tile's MFMAs.
+    float x_prev[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) x_prev[o] = -__builtin_inff();
     for (int j = 0; j < qb; ++j) {
         const int cur = j & 1;
         const bool more = j + 1 < qb;
@@ -140,29 +147,36 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
         float bm[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) bm[t] = -__builtin_inff();
+        floatx16 acc[2][NT];
 #pragma unroll
         for (int kt = 0; kt < kBlock / 32; ++kt) {
-            floatx16 acc[NT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] = zero16();
+            for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
             const unsigned char* arow = &lds[cur][(kt * 32 + col) * ROWB + 8 * half * ES];
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 Op8<T> a;
                 a.load(arow + 16 * s * ES);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) mma16(acc[t], a, bq[t][s]);
+                for (int t = 0; t < NT; ++t) mma16(acc[kt & 1][t], a, bq[t][s]);
             }
+            if (kt == 0) {
+                if (j > 0) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], max16(acc[t]));
+                    for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], j - 1);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], max16(acc[(kt - 1) & 1][t]));
+            }
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], swap_halves(bm[t]));
-#pragma unroll
-        for (int o = 0; o < NO; ++o) {
-            const float x = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
-            topk_insert<SLOTS>(sc[o], id[o], x, j);
+        for (int t = 0; t < NT; ++t) {
+            bm[t] = fmaxf(bm[t], max16(acc[(kBlock / 32 - 1) & 1][t]));
+            bm[t] = fmaxf(bm[t], swap_halves(bm[t]));
         }
+#pragma unroll
+        for (int o = 0; o < NO; ++o) x_prev[o] = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
         if (more) {
 #pragma unroll
             for (int u = 0; u < CPT; ++u) {
@@ -171,6 +185,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
             }
         }
         __syncthreads();
+    }
+    if (qb > 0) {
+#pragma unroll
+        for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], qb - 1);
     }
 
     const int nvalid = min(nslots, qb);

@@ -37,6 +37,15 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     return static_cast<bf16_t>(u >> 16);
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const float2v x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
 // Eight consecutive elements of one matrix-core operand row/column.
 template <typename T> struct Op8;
 template <> struct Op8<bf16_t> {

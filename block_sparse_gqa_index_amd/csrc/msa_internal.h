@@ -24,7 +24,7 @@ struct ListLayout {
 
 struct AttnWorkspace {
     ListLayout lists;
-    size_t po, plse, bytes;
+    size_t vt, po, plse, bytes;
 };
 
 struct KlWorkspace {

@@ -12,8 +12,10 @@
 
 namespace msa {
 
-// K block [128][D] -> LDS rows of D*ES+16 bytes; V block -> LDS V^T rows of
-// 128*ES+16 bytes. Keys at or beyond `valid_keys` are zero-filled.
+// K block [128][D] -> LDS rows of D*ES+16 bytes (the A-operand layout of
+// S^T = K Q^T); V^T block [D][128] -> LDS rows of 128*ES+16 bytes (the
+// A-operand layout of O^T = V^T P^T), copied from the pre-transposed V^T.
+// Keys at or beyond `valid_keys` are zero-filled in K (V^T is zero there).
 template <typename T, int D>
 struct KVTile {
     static constexpr int ES = sizeof(T);
@@ -21,23 +23,20 @@ struct KVTile {
     static constexpr int VROWB = kBlock * ES + 16;
     static constexpr int BYTES = kBlock * KROWB + D * VROWB;
 
-    __device__ static void stage(unsigned char* lds, const T* kb, const T* vb, size_t row_stride,
+    __device__ static void stage(unsigned char* lds, const T* kb, size_t row_stride, const T* vtb,
                                  int valid_keys) {
-        constexpr int CPR = D * ES / 16;               // 16-byte chunks per key row
+        constexpr int CPR = D * ES / 16;               // 16-byte chunks per K row
+        constexpr int CPV = kBlock * ES / 16;          // 16-byte chunks per V^T row
         constexpr int EPC = 16 / ES;                   // elements per chunk
         unsigned char* vt = lds + kBlock * KROWB;
         for (int ch = threadIdx.x; ch < kBlock * CPR; ch += blockDim.x) {
             const int key = ch / CPR, cc = ch % CPR;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (key < valid_keys) {
-                kv = *reinterpret_cast<const uint4*>(kb + key * row_stride + cc * EPC);
-                vv = *reinterpret_cast<const uint4*>(vb + key * row_stride + cc * EPC);
-            }
-            *reinterpret_cast<uint4*>(lds + key * KROWB + cc * 16) = kv;
-            const T* ve = reinterpret_cast<const T*>(&vv);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                *reinterpret_cast<T*>(vt + (cc * EPC + e) * VROWB + key * ES) = ve[e];
+            u32x4 kv = {0u, 0u, 0u, 0u};
+            if (key < valid_keys) kv = *reinterpret_cast<const u32x4*>(kb + key * row_stride + cc * EPC);
+            *reinterpret_cast<u32x4*>(lds + key * KROWB + cc * 16) = kv;
+            const int d = ch / CPV, vc = ch % CPV;     // same number of chunks: D x 128 elements
+            *reinterpret_cast<u32x4*>(vt + d * VROWB + vc * 16) =
+                *reinterpret_cast<const u32x4*>(vtb + (size_t)d * kBlock + vc * EPC);
         }
     }
 };
@@ -60,11 +59,10 @@ __device__ void stage_rows(unsigned char* lds, const T* src, size_t row_stride, 
 template <typename T> struct PType;
 template <> struct PType<bf16_t> {
     static __device__ __forceinline__ void pack(Op8<bf16_t>& o, const float* p) {
-        uint32_t w[4];
+        u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)f32_to_bf16(p[2 * e]) | ((uint32_t)f32_to_bf16(p[2 * e + 1]) << 16);
-        o.v = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+        o.v = __builtin_bit_cast(bf16x8, w);
     }
 };
 template <> struct PType<float> {

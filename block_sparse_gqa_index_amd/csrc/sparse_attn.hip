@@ -34,6 +34,49 @@
 
 namespace msa {
 
+// ------------------------------------------------------------- V^T copy --
+
+// V [B, N, Hkv, D] -> V^T [B, Hkv, nb, D, 128]: one key block of one group per
+// work-group, as EPC x EPC tiles transposed in registers (EPC = elements per
+// 16 bytes). Keys past N are written as zeros.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ v, T* __restrict__ vt, int N, int Hkv,
+                                                          int nb) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int KC = kBlock / EPC, DC = D / EPC;
+    const int j = blockIdx.x % nb;
+    const int bg = blockIdx.x / nb;
+    const int g = bg % Hkv, b = bg / Hkv;
+    T* dst = vt + (size_t)blockIdx.x * D * kBlock;
+    for (int item = threadIdx.x; item < KC * DC; item += blockDim.x) {
+        const int dc = item % DC, kc = item / DC;
+        u32x4 x[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            const int key = j * kBlock + kc * EPC + e;
+            x[e] = u32x4{0u, 0u, 0u, 0u};
+            if (key < N)
+                x[e] = *reinterpret_cast<const u32x4*>(v + (((size_t)b * N + key) * Hkv + g) * D + dc * EPC);
+        }
+#pragma unroll
+        for (int dd = 0; dd < EPC; ++dd) {
+            u32x4 y;
+            if constexpr (EPC == 8) {   // bf16: word w of row dd = keys 2w, 2w+1
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t lo = (x[2 * w][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
+                    const uint32_t hi = (x[2 * w + 1][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
+                    y[w] = lo | (hi << 16);
+                }
+            } else {                    // fp32
+#pragma unroll
+                for (int w = 0; w < 4; ++w) y[w] = x[w][dd];
+            }
+            *reinterpret_cast<u32x4*>(dst + (size_t)(dc * EPC + dd) * kBlock + kc * EPC) = y;
+        }
+    }
+}
+
 // ------------------------------------------------------- non-local blocks --
 
 // Partial layout, per (row (b,g,i), slot s < k-1): po[.][G][D] with each 32-wide
@@ -50,9 +93,8 @@ __device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restr
             u32x4 w0, w1;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                w0[r] = (uint32_t)f32_to_bf16(o[dt][2 * r] * inv) | ((uint32_t)f32_to_bf16(o[dt][2 * r + 1] * inv) << 16);
-                w1[r] = (uint32_t)f32_to_bf16(o[dt][8 + 2 * r] * inv) |
-                        ((uint32_t)f32_to_bf16(o[dt][8 + 2 * r + 1] * inv) << 16);
+                w0[r] = pack_bf16x2(o[dt][2 * r] * inv, o[dt][2 * r + 1] * inv);
+                w1[r] = pack_bf16x2(o[dt][8 + 2 * r] * inv, o[dt][8 + 2 * r + 1] * inv);
             }
             u32x4* d4 = reinterpret_cast<u32x4*>(dst + dt * 32);
             d4[0] = w0;
@@ -79,7 +121,8 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ list, const int4* __restrict__ items, const int32_t* __restrict__ total_items,
-    T* __restrict__ po, float* __restrict__ plse, int N, int Hkv, int nb, int KP, float scale_log2) {
+    const T* __restrict__ vt, T* __restrict__ po, float* __restrict__ plse, int N, int Hkv, int nb, int KP,
+    float scale_log2) {
     using KV = KVTile<T, D>;
     constexpr int PPT = 32 / G;   // positions per 32-row tile
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
@@ -113,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
 
     const size_t kv_row = (size_t)Hkv * D;
     const size_t kv_off = ((size_t)b * N + (size_t)j * kBlock) * kv_row + (size_t)g * D;
-    KV::stage(lds, k + kv_off, v + kv_off, kv_row, kBlock);
+    KV::stage(lds, k + kv_off, kv_row, vt + (((size_t)b * Hkv + g) * nb + j) * D * kBlock, kBlock);
     __syncthreads();
 
     for (; base < count; base += stride) {
@@ -187,8 +230,8 @@ struct PartialRow {
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ po, const float* __restrict__ plse, T* __restrict__ o, float* __restrict__ lse,
-    int B, int N, int Hkv, int nb, int topk, int KP, float scale_log2) {
+    const T* __restrict__ vt, const T* __restrict__ po, const float* __restrict__ plse, T* __restrict__ o,
+    float* __restrict__ lse, int B, int N, int Hkv, int nb, int topk, int KP, float scale_log2) {
     using KV = KVTile<T, D>;
     constexpr int BATCH = 4;
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
@@ -201,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
 
     const size_t kv_row = (size_t)Hkv * D;
     const size_t kv_off = ((size_t)b * N + (size_t)q0) * kv_row + (size_t)g * D;
-    KV::stage(lds, k + kv_off, v + kv_off, kv_row, valid_keys);
+    KV::stage(lds, k + kv_off, kv_row, vt + (((size_t)b * Hkv + g) * nb + qb) * D * kBlock, valid_keys);
     __syncthreads();
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -269,10 +312,8 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
                 for (int rq = 0; rq < 4; ++rq) {
                     T* d4 = dst + dt * 32 + 8 * rq + 4 * half;
                     if constexpr (sizeof(T) == 2) {
-                        const uint32_t a0 = (uint32_t)f32_to_bf16(acc[dt][4 * rq]) |
-                                            ((uint32_t)f32_to_bf16(acc[dt][4 * rq + 1]) << 16);
-                        const uint32_t a1 = (uint32_t)f32_to_bf16(acc[dt][4 * rq + 2]) |
-                                            ((uint32_t)f32_to_bf16(acc[dt][4 * rq + 3]) << 16);
+                        const uint32_t a0 = pack_bf16x2(acc[dt][4 * rq], acc[dt][4 * rq + 1]);
+                        const uint32_t a1 = pack_bf16x2(acc[dt][4 * rq + 2], acc[dt][4 * rq + 3]);
                         *reinterpret_cast<uint2*>(d4) = make_uint2(a0, a1);
                     } else {
                         floatx4 x;
@@ -293,12 +334,16 @@ static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 AttnWorkspace attn_workspace_layout(const LaunchDims& d) {
     AttnWorkspace w{};
-    w.lists = list_layout(d, 0);
     const size_t es = d.dtype == 0 ? 2 : 4;
-    size_t off = w.lists.end;
-    w.po = off;    off = align_up(off + w.lists.max_entries * d.G * d.D * es);
-    w.plse = off;  off = align_up(off + w.lists.max_entries * d.G * 4);
-    w.bytes = w.lists.has_nonlocal ? off : 0;
+    size_t off = 0;
+    w.vt = off;    off = align_up(off + (size_t)d.B * d.Hkv * d.nb * d.D * kBlock * es);
+    w.lists = list_layout(d, off);
+    if (w.lists.has_nonlocal) {
+        off = w.lists.end;
+        w.po = off;    off = align_up(off + w.lists.max_entries * d.G * d.D * es);
+        w.plse = off;  off = align_up(off + w.lists.max_entries * d.G * 4);
+    }
+    w.bytes = off;
     return w;
 }
 
@@ -314,6 +359,9 @@ static hipError_t launch_attn_t(const LaunchDims& d, const void* q, const void* 
     const T* tv = static_cast<const T*>(v);
     T* po = nullptr;
     float* plse = nullptr;
+    T* vt = reinterpret_cast<T*>(ws + L.vt);
+    hipLaunchKernelGGL((transpose_v_kernel<T, D>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st, tv, vt, d.N,
+                       d.Hkv, d.nb);
     if (L.lists.has_nonlocal) {
         launch_build_lists(d, block_idx, ws, L.lists, st);
         const int4* items = reinterpret_cast<const int4*>(ws + L.lists.items);
@@ -323,10 +371,10 @@ static hipError_t launch_attn_t(const LaunchDims& d, const void* q, const void* 
         plse = reinterpret_cast<float*>(ws + L.plse);
         const size_t grid = (L.lists.max_items + 7) / 8 * 8;
         hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tv,
-                           list, items, total, po, plse, d.N, d.Hkv, d.nb, KP, scale_log2);
+                           list, items, total, vt, po, plse, d.N, d.Hkv, d.nb, KP, scale_log2);
     }
     hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G>), dim3((unsigned)(d.nb * d.B * d.Hkv)), dim3(256), 0, st,
-                       tq, tk, tv, po, plse, static_cast<T*>(o), lse, d.B, d.N, d.Hkv, d.nb,
+                       tq, tk, tv, vt, po, plse, static_cast<T*>(o), lse, d.B, d.N, d.Hkv, d.nb,
                        L.lists.has_nonlocal ? d.k : 1, KP, scale_log2);
     return hipGetLastError();
 }

@@ -133,9 +133,10 @@ def test_empty_problems_are_accepted_without_device_work(lib):
 
 
 def test_workspace_sizes(lib):
-    # a single query block, or k = 1: no non-local block anywhere -> no workspace
-    assert msa.workspace_bytes(_dims(seqlen=128), msa.MSA_OP_ATTN) == 0
-    assert msa.workspace_bytes(_dims(topk=1), msa.MSA_OP_ATTN) == 0
+    # a single query block, or k = 1: no non-local block anywhere -> only the
+    # transposed copy of V (B * Hkv * nb * D * 128 elements)
+    assert msa.workspace_bytes(_dims(seqlen=128), msa.MSA_OP_ATTN) == 2 * 128 * 128 * 2
+    assert msa.workspace_bytes(_dims(topk=1), msa.MSA_OP_ATTN) == 2 * 8 * 128 * 128 * 2
     assert msa.workspace_bytes(_dims(), msa.MSA_OP_INDEX) == 0
     assert msa.workspace_bytes(_dims(), 9) == 0
     # the partial outputs dominate: rows * (k-1) * G * D * 2 bytes for bf16
