@@ -64,7 +64,7 @@ __device__ __forceinline__ void sort_ascending(int (&v)[SLOTS]) {
     }
 }
 
-template <typename T, int DI, int NT, int WAVES, int SLOTS>
+template <typename T, int DI, int NT, int WAVES, int SLOTS, int BPB>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     int B, int N, int Hkv, int k, int nb, int chunks) {
@@ -76,7 +76,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     constexpr int CPT = kBlock * CPR / NTHR;  // chunks per thread per key block
     constexpr int NO = NT >= 2 ? NT / 2 : 1;  // rows each lane keeps a top-k list for
     static_assert(CPT * NTHR == kBlock * CPR, "staging must tile the block");
-    __shared__ __align__(16) unsigned char lds[2][kBlock * ROWB];
+    // Two stages of BPB key blocks: one barrier per BPB blocks.
+    __shared__ __align__(16) unsigned char lds[2][BPB][kBlock * ROWB];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -115,15 +116,25 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     }
 
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
-    if (qb > 0) {
-        u32x4 stage[CPT];
+    const size_t kblock_bytes = (size_t)kBlock * DI * ES;
+    {
+        u32x4 stage[BPB][CPT];
 #pragma unroll
-        for (int u = 0; u < CPT; ++u)
-            stage[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(tid + NTHR * u) * 16);
+        for (int bb = 0; bb < BPB; ++bb) {
+            const unsigned char* src = kbase + (size_t)min(bb, max(qb - 1, 0)) * kblock_bytes;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ch = tid + NTHR * u;
-            *reinterpret_cast<u32x4*>(&lds[0][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[u];
+            for (int u = 0; u < CPT; ++u)
+                stage[bb][u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+        }
+        if (qb > 0) {
+#pragma unroll
+            for (int bb = 0; bb < BPB; ++bb) {
+#pragma unroll
+                for (int u = 0; u < CPT; ++u) {
+                    const int ch = tid + NTHR * u;
+                    *reinterpret_cast<u32x4*>(&lds[0][bb][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[bb][u];
+                }
+            }
         }
     }
     __syncthreads();
@@ -133,55 +144,65 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     float x_prev[NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) x_prev[o] = -__builtin_inff();
-    for (int j = 0; j < qb; ++j) {
-        const int cur = j & 1;
-        const bool more = j + 1 < qb;
-        // Next key block: global -> VGPRs now, VGPRs -> LDS after this block's math.
-        u32x4 stage[CPT];
-        {
-            const unsigned char* src = kbase + (size_t)(more ? j + 1 : j) * kBlock * DI * ES;
+    for (int jp = 0; jp < qb; jp += BPB) {
+        const int cur = (jp / BPB) & 1;
+        const bool more = jp + BPB < qb;
+        // Next BPB key blocks: global -> VGPRs now, VGPRs -> LDS after this stage's math.
+        u32x4 stage[BPB][CPT];
+#pragma unroll
+        for (int bb = 0; bb < BPB; ++bb) {
+            const unsigned char* src = kbase + (size_t)min(jp + BPB + bb, qb - 1) * kblock_bytes;
 #pragma unroll
             for (int u = 0; u < CPT; ++u)
-                stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+                stage[bb][u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
         }
-        float bm[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bm[t] = -__builtin_inff();
-        floatx16 acc[2][NT];
+        for (int bb = 0; bb < BPB; ++bb) {
+            const int j = jp + bb;
+            if (j < qb) {
+                float bm[NT];
 #pragma unroll
-        for (int kt = 0; kt < kBlock / 32; ++kt) {
+                for (int t = 0; t < NT; ++t) bm[t] = -__builtin_inff();
+                floatx16 acc[2][NT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
-            const unsigned char* arow = &lds[cur][(kt * 32 + col) * ROWB + 8 * half * ES];
+                for (int kt = 0; kt < kBlock / 32; ++kt) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                Op8<T> a;
-                a.load(arow + 16 * s * ES);
+                    for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
+                    const unsigned char* arow = &lds[cur][bb][(kt * 32 + col) * ROWB + 8 * half * ES];
 #pragma unroll
-                for (int t = 0; t < NT; ++t) mma16(acc[kt & 1][t], a, bq[t][s]);
-            }
-            if (kt == 0) {
-                if (j > 0) {
+                    for (int s = 0; s < KS; ++s) {
+                        Op8<T> a;
+                        a.load(arow + 16 * s * ES);
 #pragma unroll
-                    for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], j - 1);
+                        for (int t = 0; t < NT; ++t) mma16(acc[kt & 1][t], a, bq[t][s]);
+                    }
+                    if (kt == 0) {
+                        if (j > 0) {
+#pragma unroll
+                            for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], j - 1);
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], max16(acc[(kt - 1) & 1][t]));
+                    }
                 }
-            } else {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], max16(acc[(kt - 1) & 1][t]));
+                for (int t = 0; t < NT; ++t) {
+                    bm[t] = fmaxf(bm[t], max16(acc[(kBlock / 32 - 1) & 1][t]));
+                    bm[t] = fmaxf(bm[t], swap_halves(bm[t]));
+                }
+#pragma unroll
+                for (int o = 0; o < NO; ++o) x_prev[o] = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
             }
         }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            bm[t] = fmaxf(bm[t], max16(acc[(kBlock / 32 - 1) & 1][t]));
-            bm[t] = fmaxf(bm[t], swap_halves(bm[t]));
-        }
-#pragma unroll
-        for (int o = 0; o < NO; ++o) x_prev[o] = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
         if (more) {
 #pragma unroll
-            for (int u = 0; u < CPT; ++u) {
-                const int ch = tid + NTHR * u;
-                *reinterpret_cast<u32x4*>(&lds[cur ^ 1][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[u];
+            for (int bb = 0; bb < BPB; ++bb) {
+#pragma unroll
+                for (int u = 0; u < CPT; ++u) {
+                    const int ch = tid + NTHR * u;
+                    *reinterpret_cast<u32x4*>(&lds[cur ^ 1][bb][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[bb][u];
+                }
             }
         }
         __syncthreads();
@@ -216,18 +237,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
 template <typename T, int DI, int NT, int WAVES>
 static hipError_t launch_cfg(const LaunchDims& d, const void* q_idx, const void* k_idx, int32_t* out,
                              hipStream_t st) {
+    // Two key blocks per barrier when the doubled LDS stage still fits (one
+    // 8-wave work-group per CU anyway); otherwise one.
+    constexpr int BPB = (WAVES == 8 && 2 * 2 * kBlock * (DI * (int)sizeof(T) + 16) <= 160 * 1024) ? 2 : 1;
     const int chunks = (kBlock * d.Hkv) / (32 * NT * WAVES);
     const dim3 grid((unsigned)(d.nb * d.B * chunks)), block(64 * WAVES);
     const T* q = static_cast<const T*>(q_idx);
     const T* kk = static_cast<const T*>(k_idx);
     if (d.k <= 8)
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 7>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 7, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, d.nb, chunks);
     else if (d.k <= 16)
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 15>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 15, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, d.nb, chunks);
     else
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 31>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 31, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, d.nb, chunks);
     return hipGetLastError();
 }

@@ -83,11 +83,9 @@ __global__ __launch_bounds__(256, 1) void kl_nonlocal_kernel(
     const float* __restrict__ lse, const int32_t* __restrict__ list, const int4* __restrict__ items,
     const int32_t* __restrict__ total_items, float* __restrict__ part, int N, int Hkv, int nb, int KP,
     float scale_log2, float iscale) {
-    constexpr int ES = sizeof(T);
-    constexpr int KROWB = D * ES + 16;
     constexpr int PPT = 32 / G;
-    __shared__ __align__(16) unsigned char lds[kBlock * KROWB + kBlock * (DI * ES + 16)];
-    unsigned char* lds_i = lds + kBlock * KROWB;
+    __shared__ __align__(16) unsigned char lds[SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES];
+    unsigned char* lds_i = lds + SwzTile<T, D>::BYTES;
 
     const int total = total_items[0];
     const int per_xcd = (total + 7) / 8;
@@ -138,10 +136,8 @@ __global__ __launch_bounds__(256, 1) void kl_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const float* __restrict__ lse, const float* __restrict__ part, float* __restrict__ kl_rows, int B, int N,
     int Hkv, int nb, int topk, int KP, float scale_log2, float iscale) {
-    constexpr int ES = sizeof(T);
-    constexpr int KROWB = D * ES + 16;
-    __shared__ __align__(16) unsigned char lds[kBlock * KROWB + kBlock * (DI * ES + 16)];
-    unsigned char* lds_i = lds + kBlock * KROWB;
+    __shared__ __align__(16) unsigned char lds[SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES];
+    unsigned char* lds_i = lds + SwzTile<T, D>::BYTES;
     const int g = blockIdx.x % Hkv;
     const int b = (blockIdx.x / Hkv) % B;
     const int qb = blockIdx.x / (Hkv * B);

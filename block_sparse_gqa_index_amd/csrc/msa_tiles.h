@@ -12,49 +12,70 @@
 
 namespace msa {
 
-// K block [128][D] -> LDS rows of D*ES+16 bytes (the A-operand layout of
-// S^T = K Q^T); V^T block [D][128] -> LDS rows of 128*ES+16 bytes (the
-// A-operand layout of O^T = V^T P^T), copied from the pre-transposed V^T.
-// Keys at or beyond `valid_keys` are zero-filled in K (V^T is zero there).
-template <typename T, int D>
-struct KVTile {
+// LDS tile of rows of W elements of T, unpadded, with the 16-byte chunks of
+// every row XOR-swizzled by the row index (physical chunk = c ^ (row % SW)).
+// Both access patterns used here then hit distinct banks: 16 lanes reading
+// the same logical chunk of 16 consecutive rows, and 16 lanes writing the 16
+// chunks of one row.
+template <typename T, int W>
+struct SwzTile {
     static constexpr int ES = sizeof(T);
-    static constexpr int KROWB = D * ES + 16;
-    static constexpr int VROWB = kBlock * ES + 16;
-    static constexpr int BYTES = kBlock * KROWB + D * VROWB;
-
-    __device__ static void stage(unsigned char* lds, const T* kb, size_t row_stride, const T* vtb,
-                                 int valid_keys) {
-        constexpr int CPR = D * ES / 16;               // 16-byte chunks per K row
-        constexpr int CPV = kBlock * ES / 16;          // 16-byte chunks per V^T row
-        constexpr int EPC = 16 / ES;                   // elements per chunk
-        unsigned char* vt = lds + kBlock * KROWB;
-        for (int ch = threadIdx.x; ch < kBlock * CPR; ch += blockDim.x) {
-            const int key = ch / CPR, cc = ch % CPR;
-            u32x4 kv = {0u, 0u, 0u, 0u};
-            if (key < valid_keys) kv = *reinterpret_cast<const u32x4*>(kb + key * row_stride + cc * EPC);
-            *reinterpret_cast<u32x4*>(lds + key * KROWB + cc * 16) = kv;
-            const int d = ch / CPV, vc = ch % CPV;     // same number of chunks: D x 128 elements
-            *reinterpret_cast<u32x4*>(vt + d * VROWB + vc * 16) =
-                *reinterpret_cast<const u32x4*>(vtb + (size_t)d * kBlock + vc * EPC);
+    static constexpr int ROWB = W * ES;
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int SW = CPR < 16 ? CPR : 16;
+    static constexpr int BYTES = kBlock * ROWB;   // for a 128-row tile
+    __device__ static __forceinline__ int offset(int row, int byte) {
+        return row * ROWB + (((byte >> 4) ^ (row & (SW - 1))) << 4) + (byte & 15);
+    }
+    // Eight consecutive elements starting at element `e` of `row`.
+    __device__ static __forceinline__ void load8(Op8<T>& a, const unsigned char* base, int row, int e) {
+        if constexpr (ES == 2) {
+            a.load(base + offset(row, e * ES));
+        } else {
+            const float4 x = *reinterpret_cast<const float4*>(base + offset(row, e * ES));
+            const float4 y = *reinterpret_cast<const float4*>(base + offset(row, e * ES + 16));
+            a.v[0] = x.x; a.v[1] = x.y; a.v[2] = x.z; a.v[3] = x.w;
+            a.v[4] = y.x; a.v[5] = y.y; a.v[6] = y.z; a.v[7] = y.w;
         }
     }
 };
 
-// A plain [128][W] tile (rows of W*ES+16 bytes, the K layout of KVTile<T, W>).
+// A [128][W] tile from global rows `row_stride` elements apart; rows at or
+// beyond `valid_rows` are zero-filled.
 template <typename T, int W>
-__device__ void stage_rows(unsigned char* lds, const T* src, size_t row_stride, int valid_keys) {
-    constexpr int ES = sizeof(T);
-    constexpr int ROWB = W * ES + 16;
-    constexpr int CPR = W * ES / 16;
-    constexpr int EPC = 16 / ES;
-    for (int ch = threadIdx.x; ch < kBlock * CPR; ch += blockDim.x) {
-        const int key = ch / CPR, cc = ch % CPR;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (key < valid_keys) x = *reinterpret_cast<const uint4*>(src + key * row_stride + cc * EPC);
-        *reinterpret_cast<uint4*>(lds + key * ROWB + cc * 16) = x;
+__device__ void stage_rows(unsigned char* lds, const T* src, size_t row_stride, int valid_rows) {
+    using S = SwzTile<T, W>;
+    constexpr int EPC = 16 / sizeof(T);
+    for (int ch = threadIdx.x; ch < kBlock * S::CPR; ch += blockDim.x) {
+        const int row = ch / S::CPR, cc = ch % S::CPR;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < valid_rows) x = *reinterpret_cast<const u32x4*>(src + row * row_stride + cc * EPC);
+        *reinterpret_cast<u32x4*>(lds + S::offset(row, cc * 16)) = x;
     }
 }
+
+// K block [128 keys][D] (the A operand of S^T = K Q^T) followed by the V^T
+// block [D][128 keys] (the A operand of O^T = V^T P^T), copied from the
+// pre-transposed V^T (zero past the last key). Keys at or beyond `valid_keys`
+// are zero-filled in K.
+template <typename T, int D>
+struct KVTile {
+    using KS = SwzTile<T, D>;
+    using VS = SwzTile<T, kBlock>;
+    static constexpr int BYTES = kBlock * KS::ROWB + D * VS::ROWB;
+
+    __device__ static void stage(unsigned char* lds, const T* kb, size_t row_stride, const T* vtb,
+                                 int valid_keys) {
+        stage_rows<T, D>(lds, kb, row_stride, valid_keys);
+        constexpr int EPC = 16 / sizeof(T);
+        unsigned char* vt = lds + kBlock * KS::ROWB;
+        for (int ch = threadIdx.x; ch < D * VS::CPR; ch += blockDim.x) {
+            const int d = ch / VS::CPR, vc = ch % VS::CPR;
+            *reinterpret_cast<u32x4*>(vt + VS::offset(d, vc * 16)) =
+                *reinterpret_cast<const u32x4*>(vtb + (size_t)d * kBlock + vc * EPC);
+        }
+    }
+};
 
 template <typename T> struct PType;
 template <> struct PType<bf16_t> {
@@ -72,12 +93,14 @@ template <> struct PType<float> {
     }
 };
 
-// V^T operand for 16-key slice c: keys 16c + {4h..4h+3} and 16c + 8 + {4h..4h+3}.
+// V^T operand for 16-key slice c: keys 16c + {4h..4h+3} and 16c + 8 + {4h..4h+3}
+// of V^T row `d`.
 template <typename T>
-__device__ __forceinline__ void load_vt_op(Op8<T>& a, const unsigned char* vrow, int c, int half) {
+__device__ __forceinline__ void load_vt_op(Op8<T>& a, const unsigned char* vt, int d, int c, int half) {
+    using VS = SwzTile<T, kBlock>;
     constexpr int ES = sizeof(T);
-    const unsigned char* p0 = vrow + (16 * c + 4 * half) * ES;
-    const unsigned char* p1 = vrow + (16 * c + 8 + 4 * half) * ES;
+    const unsigned char* p0 = vt + VS::offset(d, (16 * c + 4 * half) * ES);
+    const unsigned char* p1 = vt + VS::offset(d, (16 * c + 8 + 4 * half) * ES);
     if constexpr (ES == 2) {
         const uint2 x = *reinterpret_cast<const uint2*>(p0);
         const uint2 y = *reinterpret_cast<const uint2*>(p1);
@@ -95,15 +118,14 @@ __device__ __forceinline__ void load_vt_op(Op8<T>& a, const unsigned char* vrow,
 template <typename T, int D>
 __device__ __forceinline__ void tile_scores(floatx16 (&s)[4], const Op8<T> (&bq)[D / 16],
                                             const unsigned char* lds, int col, int half) {
-    using KV = KVTile<T, D>;
+    using KS = SwzTile<T, D>;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
         s[kt] = zero16();
-        const unsigned char* arow = lds + (kt * 32 + col) * KV::KROWB + 8 * half * KV::ES;
 #pragma unroll
         for (int sl = 0; sl < D / 16; ++sl) {
             Op8<T> a;
-            a.load(arow + 16 * sl * KV::ES);
+            KS::load8(a, lds, kt * 32 + col, 16 * sl + 8 * half);
             mma16(s[kt], a, bq[sl]);
         }
         // keep the scheduler from hoisting every LDS operand load of the tile
@@ -116,8 +138,7 @@ __device__ __forceinline__ void tile_scores(floatx16 (&s)[4], const Op8<T> (&bq)
 template <typename T, int D>
 __device__ __forceinline__ void tile_pv(floatx16 (&o)[D / 32], const floatx16 (&p)[4],
                                         const unsigned char* lds, int col, int half) {
-    using KV = KVTile<T, D>;
-    const unsigned char* vt = lds + kBlock * KV::KROWB;
+    const unsigned char* vt = lds + kBlock * SwzTile<T, D>::ROWB;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         float pe[8];
@@ -128,7 +149,7 @@ __device__ __forceinline__ void tile_pv(floatx16 (&o)[D / 32], const floatx16 (&
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             Op8<T> a;
-            load_vt_op<T>(a, vt + (dt * 32 + col) * KV::VROWB, c, half);
+            load_vt_op<T>(a, vt, dt * 32 + col, c, half);
             mma16(o[dt], a, bp);
         }
         __builtin_amdgcn_sched_barrier(0);
