@@ -10,6 +10,7 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   index_topk(q_idx, k_idx, topk)                   -> block_idx int32 [B, Hkv, N, k]
   sparse_attn_fwd(q, k, v, block_idx, scale)       -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])
   kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse) -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])
+  forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse), both stages overlapped
   workspace_bytes(dims, op)
 """
 import ctypes
@@ -21,11 +22,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_F32 = 0, 1
-MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL = 0, 1, 2
+MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD = 0, 1, 2, 3
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
-EXPORTS = ("msa_index_topk", "msa_sparse_attn_fwd", "msa_kl_align_fwd", "msa_workspace_bytes",
-           "msa_strerror", "msa_abi_version")
+EXPORTS = ("msa_index_topk", "msa_sparse_attn_fwd", "msa_forward", "msa_kl_align_fwd",
+           "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
 class MsaDims(ctypes.Structure):
@@ -59,12 +60,13 @@ def load_library(path: str = LIB_PATH):
     lib.msa_sparse_attn_fwd.argtypes = [dp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                      vp, vp, vp, sz, vp]
+    lib.msa_forward.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
     lib.msa_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_strerror.argtypes = [ctypes.c_int]
     lib.msa_strerror.restype = ctypes.c_char_p
     lib.msa_abi_version.restype = ctypes.c_int
-    for f in (lib.msa_index_topk, lib.msa_sparse_attn_fwd, lib.msa_kl_align_fwd):
+    for f in (lib.msa_index_topk, lib.msa_sparse_attn_fwd, lib.msa_kl_align_fwd, lib.msa_forward):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -189,8 +191,34 @@ def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_sc
     return kl_rows, kl_sum
 
 
-def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0):
-    """The whole hot path on one stream: selection, then sparse attention."""
-    block_idx = index_topk(q_idx, k_idx, topk)
-    o, lse = sparse_attn_fwd(q, k, v, block_idx, softmax_scale)
+def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0, block_idx=None, o=None, lse=None,
+            workspace=None, block_size=128):
+    """The whole hot path (msa_forward): selection and sparse attention, the
+    selection of one query chunk overlapping the attention of the previous one.
+    Returns (block_idx int32 [B,Hkv,N,topk], o [B,N,Hq,D], lse fp32 [B,Hq,N])."""
+    lib = load_library()
+    _req(q_idx, "q_idx", ndim=4)
+    _req(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)
+    _req(q, "q", dtype=q_idx.dtype, ndim=4)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(v, "v", dtype=q.dtype, ndim=4)
+    B, N, Hq, D = q.shape
+    Hkv, Di = q_idx.shape[2], q_idx.shape[3]
+    if (tuple(k_idx.shape) != (B, N, Di) or tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D)
+            or tuple(q_idx.shape[:2]) != (B, N) or Hq % Hkv):
+        raise ValueError("inconsistent shapes")
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, N, topk), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    _req(o, "o", dtype=q.dtype, ndim=4)
+    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_FORWARD), q.device, workspace)
+    _check(lib.msa_forward(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
+                           float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws,
+                           _stream(q.device)))
     return block_idx, o, lse

@@ -1,7 +1,9 @@
-// Inversion of the block selection: for every (batch, group, key block) the
-// list of query rows that kept that block as a non-local block, cut into work
-// items of at most kSeg rows. Used by the attention and KL kernels that iterate
-// over key blocks.
+// Inversion of the block selection: for every (batch, group, window of
+// kWindow query positions, key block) the list of query rows of that window
+// that kept that block as a non-local block, cut into work items of at most
+// kSeg rows. Used by the attention and KL kernels that iterate over key
+// blocks. Keys are ordered batch, group, window, block, so walking the items in
+// order walks one window's query rows at a time.
 #include "msa_common.h"
 #include "msa_internal.h"
 
@@ -16,31 +18,32 @@ __global__ void fill_i32_kernel(int32_t* p, size_t n, int32_t v) {
 
 // One thread per (b, g, i) row: count the row's non-local blocks.
 __global__ void count_kernel(const int32_t* __restrict__ block_idx, int32_t* __restrict__ counts,
-                             int64_t rows, int N, int k, int nb) {
-    const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (r >= rows) return;
-    const int i = (int)(r % N);
-    const int64_t bg = r / N;
+                             int64_t rows, int N, int k, int nb, int nwin, int p_lo, int p_len) {
+    const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (x >= rows) return;
+    const int i = p_lo + (int)(x % p_len);
+    const int64_t bg = x / p_len;
+    const int64_t r = bg * N + i;
     const int L = i / kBlock;
     const int32_t* row = block_idx + r * k;
     for (int s = 0; s + 1 < k; ++s) {   // a non-local block never sits in the last slot
         const int j = row[s];
-        if (j >= 0 && j < L) atomicAdd(&counts[bg * nb + j], 1);
+        if (j >= 0 && j < L) atomicAdd(&counts[(bg * nwin + i / kWindow) * nb + j], 1);
     }
 }
 
 // The same counts from per-work-group LDS histograms: a work-group takes
 // kHistPos consecutive positions of one (b, g) and issues one global atomic per
 // block its rows touched instead of one per entry.
-constexpr int kHistPos = 2048;
+constexpr int kHistPos = 2048;   // divides kWindow, so a work-group stays inside one window
 constexpr int kHistMaxBins = 8192;   // 2 x 32 KB of LDS in the scatter pass
 
 __global__ __launch_bounds__(256) void count_hist_kernel(const int32_t* __restrict__ block_idx,
                                                          int32_t* __restrict__ counts, int N, int k, int nb,
-                                                         int chunks) {
+                                                         int nwin, int chunks, int p_lo, int p_hi) {
     extern __shared__ int32_t hist[];
     const int bg = blockIdx.x / chunks, c = blockIdx.x % chunks;
-    const int p0 = c * kHistPos, p1 = min(N, p0 + kHistPos);
+    const int p0 = p_lo + c * kHistPos, p1 = min(p_hi, p0 + kHistPos);
     const int nbins = (p1 - 1) / kBlock;   // every non-local block of these rows is below this
     for (int x = threadIdx.x; x < nbins; x += blockDim.x) hist[x] = 0;
     __syncthreads();
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(256) void count_hist_kernel(const int32_t* __restri
     }
     __syncthreads();
     for (int x = threadIdx.x; x < nbins; x += blockDim.x)
-        if (hist[x]) atomicAdd(&counts[(size_t)bg * nb + x], hist[x]);
+        if (hist[x]) atomicAdd(&counts[((size_t)bg * nwin + p0 / kWindow) * nb + x], hist[x]);
 }
 
 // Scatter with the same histogram: one global atomic per touched block
@@ -63,10 +66,11 @@ __global__ __launch_bounds__(256) void count_hist_kernel(const int32_t* __restri
 __global__ __launch_bounds__(256) void scatter_hist_kernel(const int32_t* __restrict__ block_idx,
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ cursor, int32_t* __restrict__ list,
-                                                           int N, int k, int nb, int chunks) {
+                                                           int N, int k, int nb, int nwin, int chunks, int p_lo,
+                                                           int p_hi) {
     extern __shared__ int32_t sh[];
     const int bg = blockIdx.x / chunks, c = blockIdx.x % chunks;
-    const int p0 = c * kHistPos, p1 = min(N, p0 + kHistPos);
+    const int p0 = p_lo + c * kHistPos, p1 = min(p_hi, p0 + kHistPos);
     const int nbins = (p1 - 1) / kBlock;
     int32_t* hist = sh;
     int32_t* base = sh + nbins;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(256) void scatter_hist_kernel(const int32_t* __rest
     for (int x = threadIdx.x; x < nbins; x += blockDim.x) {
         const int n = hist[x];
         if (n) {
-            const size_t key = (size_t)bg * nb + x;
+            const size_t key = ((size_t)bg * nwin + p0 / kWindow) * nb + x;
             base[x] = offsets[key] + atomicAdd(&cursor[key], n);
         }
         hist[x] = 0;
@@ -142,17 +146,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // One thread per row: append (i << 5 | slot) to the list of every non-local block.
 __global__ void scatter_kernel(const int32_t* __restrict__ block_idx, const int32_t* __restrict__ offsets,
                                int32_t* __restrict__ cursor, int32_t* __restrict__ list, int64_t rows,
-                               int N, int k, int nb) {
-    const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (r >= rows) return;
-    const int i = (int)(r % N);
-    const int64_t bg = r / N;
+                               int N, int k, int nb, int nwin, int p_lo, int p_len) {
+    const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (x >= rows) return;
+    const int i = p_lo + (int)(x % p_len);
+    const int64_t bg = x / p_len;
+    const int64_t r = bg * N + i;
     const int L = i / kBlock;
     const int32_t* row = block_idx + r * k;
     for (int s = 0; s + 1 < k; ++s) {
         const int j = row[s];
         if (j >= 0 && j < L) {
-            const int64_t key = bg * nb + j;
+            const int64_t key = (bg * nwin + i / kWindow) * nb + j;
             const int at = offsets[key] + atomicAdd(&cursor[key], 1);
             list[at] = (i << 5) | s;
         }
@@ -172,9 +177,11 @@ __global__ void items_kernel(const int32_t* __restrict__ counts, const int32_t* 
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int windows(const LaunchDims& d) { return (d.N + kWindow - 1) / kWindow; }
+
 ListLayout list_layout(const LaunchDims& d, size_t base) {
     ListLayout w{};
-    const size_t n_keys = (size_t)d.B * d.Hkv * d.nb;
+    const size_t n_keys = (size_t)d.B * d.Hkv * windows(d) * d.nb;
     const size_t kp = d.k > 1 ? (size_t)(d.k - 1) : 0;
     w.max_entries = (size_t)d.B * d.Hkv * d.N * kp;
     w.n_keys = n_keys;
@@ -192,8 +199,8 @@ ListLayout list_layout(const LaunchDims& d, size_t base) {
     return w;
 }
 
-void launch_build_lists(const LaunchDims& d, const int32_t* block_idx, unsigned char* ws, const ListLayout& L,
-                        hipStream_t st) {
+void launch_build_lists(const LaunchDims& d, int p_lo, int p_hi, const int32_t* block_idx, unsigned char* ws,
+                        const ListLayout& L, hipStream_t st) {
     int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* item_offsets = reinterpret_cast<int32_t*>(ws + L.item_offsets);
@@ -201,28 +208,36 @@ void launch_build_lists(const LaunchDims& d, const int32_t* block_idx, unsigned 
     int32_t* total = reinterpret_cast<int32_t*>(ws + L.total);
     int4* items = reinterpret_cast<int4*>(ws + L.items);
     int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
-    const int64_t rows = (int64_t)d.B * d.Hkv * d.N;
+    const int p_len = p_hi - p_lo;
+    const int nwin = windows(d);
+    const int64_t rows = (int64_t)d.B * d.Hkv * p_len;
     const int nk = (int)L.n_keys;
     hipLaunchKernelGGL(fill_i32_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, (size_t)nk, 0);
     const bool hist = d.nb <= kHistMaxBins;
-    const int chunks = (d.N + kHistPos - 1) / kHistPos;
+    const int chunks = (p_len + kHistPos - 1) / kHistPos;
     const unsigned hist_grid = (unsigned)((size_t)d.B * d.Hkv * chunks);
     const size_t hist_lds = (size_t)d.nb * 4;
     if (hist)
         hipLaunchKernelGGL(count_hist_kernel, dim3(hist_grid), dim3(256), hist_lds, st, block_idx, counts, d.N, d.k,
-                           d.nb, chunks);
+                           d.nb, nwin, chunks, p_lo, p_hi);
     else
         hipLaunchKernelGGL(count_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, counts,
-                           rows, d.N, d.k, d.nb);
+                           rows, d.N, d.k, d.nb, nwin, p_lo, p_len);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, item_offsets, cursor, total, nk);
     if (hist)
         hipLaunchKernelGGL(scatter_hist_kernel, dim3(hist_grid), dim3(256), 2 * hist_lds, st, block_idx, offsets,
-                           cursor, list, d.N, d.k, d.nb, chunks);
+                           cursor, list, d.N, d.k, d.nb, nwin, chunks, p_lo, p_hi);
     else
         hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx,
-                           offsets, cursor, list, rows, d.N, d.k, d.nb);
+                           offsets, cursor, list, rows, d.N, d.k, d.nb, nwin, p_lo, p_len);
     hipLaunchKernelGGL(items_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, offsets, item_offsets, items,
                        nk);
+}
+
+size_t list_items_bound(const LaunchDims& d, int p_lo, int p_hi, const ListLayout& L) {
+    const size_t kp = d.k > 1 ? (size_t)(d.k - 1) : 0;
+    const size_t entries = (size_t)d.B * d.Hkv * (size_t)(p_hi - p_lo) * kp;
+    return (entries + kSeg - 1) / kSeg + L.n_keys;
 }
 
 }  // namespace msa

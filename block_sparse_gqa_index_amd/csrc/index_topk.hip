@@ -67,7 +67,7 @@ __device__ __forceinline__ void sort_ascending(int (&v)[SLOTS]) {
 template <typename T, int DI, int NT, int WAVES, int SLOTS, int BPB>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
-    int B, int N, int Hkv, int k, int nb, int chunks) {
+    int B, int N, int Hkv, int k, int qb_lo, int qb_cnt, int chunks) {
     constexpr int NTHR = 64 * WAVES;
     constexpr int ES = sizeof(T);
     constexpr int ROWB = DI * ES + 16;        // padded LDS row, bytes
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const int per_qb = B * chunks;
-    const int qb = nb - 1 - (int)(blockIdx.x / per_qb);
+    const int qb = qb_lo + qb_cnt - 1 - (int)(blockIdx.x / per_qb);   // heaviest first
     const int b = (int)(blockIdx.x % per_qb) / chunks;
     const int c = (int)(blockIdx.x % chunks);
     const int r0 = c * (32 * NT * WAVES) + w * (32 * NT);
@@ -235,48 +235,49 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
 }
 
 template <typename T, int DI, int NT, int WAVES>
-static hipError_t launch_cfg(const LaunchDims& d, const void* q_idx, const void* k_idx, int32_t* out,
-                             hipStream_t st) {
+static hipError_t launch_cfg(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
+                             int32_t* out, hipStream_t st) {
     // Two key blocks per barrier when the doubled LDS stage still fits (one
     // 8-wave work-group per CU anyway); otherwise one.
     constexpr int BPB = (WAVES == 8 && 2 * 2 * kBlock * (DI * (int)sizeof(T) + 16) <= 160 * 1024) ? 2 : 1;
     const int chunks = (kBlock * d.Hkv) / (32 * NT * WAVES);
-    const dim3 grid((unsigned)(d.nb * d.B * chunks)), block(64 * WAVES);
+    const dim3 grid((unsigned)(qb_cnt * d.B * chunks)), block(64 * WAVES);
     const T* q = static_cast<const T*>(q_idx);
     const T* kk = static_cast<const T*>(k_idx);
     if (d.k <= 8)
         hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 7, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
-                           d.Hkv, d.k, d.nb, chunks);
+                           d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     else if (d.k <= 16)
         hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 15, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
-                           d.Hkv, d.k, d.nb, chunks);
+                           d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     else
         hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 31, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
-                           d.Hkv, d.k, d.nb, chunks);
+                           d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     return hipGetLastError();
 }
 
-// A work-group holds 32*NT*WAVES rows of one query block (128*Hkv rows), so
-// WAVES is the largest of 8/4/2 that divides the block's rows evenly.
+// A work-group holds 32*NT*WAVES rows of one query block (128*Hkv rows): 4
+// waves (one per SIMD) of 64 rows each for bf16; two such work-groups share a
+// CU (measured faster than one 8-wave work-group with a shared LDS stage).
 template <typename T, int DI>
-static hipError_t launch_di(const LaunchDims& d, const void* q_idx, const void* k_idx,
+static hipError_t launch_di(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                             int32_t* out, hipStream_t st) {
     constexpr int NT = sizeof(T) == 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
     const int rows = kBlock * d.Hkv;
-    if (rows % (32 * NT * 8) == 0) return launch_cfg<T, DI, NT, 8>(d, q_idx, k_idx, out, st);
-    if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, q_idx, k_idx, out, st);
-    return launch_cfg<T, DI, NT, 2>(d, q_idx, k_idx, out, st);
+    if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+    return launch_cfg<T, DI, NT, 2>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
 }
 
-hipError_t launch_index_topk(const LaunchDims& d, const void* q_idx, const void* k_idx,
+hipError_t launch_index_topk(const LaunchDims& d, int qb_lo, int qb_hi, const void* q_idx, const void* k_idx,
                              int32_t* block_idx, hipStream_t st) {
-    if (d.B == 0 || d.N == 0) return hipSuccess;
+    if (d.B == 0 || d.N == 0 || qb_hi <= qb_lo) return hipSuccess;
+    const int cnt = qb_hi - qb_lo;
     if (d.dtype == 0) {
-        return d.Di == 128 ? launch_di<bf16_t, 128>(d, q_idx, k_idx, block_idx, st)
-                           : launch_di<bf16_t, 64>(d, q_idx, k_idx, block_idx, st);
+        return d.Di == 128 ? launch_di<bf16_t, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
+                           : launch_di<bf16_t, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);
     }
-    return d.Di == 128 ? launch_di<float, 128>(d, q_idx, k_idx, block_idx, st)
-                       : launch_di<float, 64>(d, q_idx, k_idx, block_idx, st);
+    return d.Di == 128 ? launch_di<float, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
+                       : launch_di<float, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);
 }
 
 }  // namespace msa

@@ -81,23 +81,21 @@ template <typename T, int D, int DI, int G>
 __global__ __launch_bounds__(256, 1) void kl_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const float* __restrict__ lse, const int32_t* __restrict__ list, const int4* __restrict__ items,
-    const int32_t* __restrict__ total_items, float* __restrict__ part, int N, int Hkv, int nb, int KP,
+    const int32_t* __restrict__ total_items, float* __restrict__ part, int N, int Hkv, int nb, int nwin, int KP,
     float scale_log2, float iscale) {
     constexpr int PPT = 32 / G;
     __shared__ __align__(16) unsigned char lds[SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES];
     unsigned char* lds_i = lds + SwzTile<T, D>::BYTES;
 
     const int total = total_items[0];
-    const int per_xcd = (total + 7) / 8;
-    const int slot_in_xcd = blockIdx.x / 8;
-    if (slot_in_xcd >= per_xcd) return;
-    const int item_id = (blockIdx.x % 8) * per_xcd + slot_in_xcd;
+    const int item_id = item_of_workgroup(blockIdx.x);
     if (item_id >= total) return;
     const int4 it = items[item_id];
     const int key = it.x, start = it.y, count = it.z;
     const int j = key % nb;
-    const int g = (key / nb) % Hkv;
-    const int b = key / (nb * Hkv);
+    const int bg = key / (nb * nwin);   // key = ((b * Hkv + g) * nwin + window) * nb + j
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
     const int Hq = Hkv * G;
 
     stage_rows<T, D>(lds, k + ((size_t)b * N + (size_t)j * kBlock) * Hkv * D + (size_t)g * D, (size_t)Hkv * D,
@@ -248,14 +246,14 @@ static hipError_t launch_kl_t(const LaunchDims& d, const void* q, const void* k,
     const T* tki = static_cast<const T*>(k_idx);
     float* part = nullptr;
     if (L.lists.has_nonlocal) {
-        launch_build_lists(d, block_idx, ws, L.lists, st);
+        launch_build_lists(d, 0, d.N, block_idx, ws, L.lists, st);
         part = reinterpret_cast<float*>(ws + L.part);
-        const size_t grid = (L.lists.max_items + 7) / 8 * 8;
+        const size_t grid = (L.lists.max_items + 63) / 64 * 64;
         hipLaunchKernelGGL((kl_nonlocal_kernel<T, D, DI, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tqi,
                            tki, lse, reinterpret_cast<const int32_t*>(ws + L.lists.list),
                            reinterpret_cast<const int4*>(ws + L.lists.items),
-                           reinterpret_cast<const int32_t*>(ws + L.lists.total), part, d.N, d.Hkv, d.nb, KP,
-                           scale_log2, iscale);
+                           reinterpret_cast<const int32_t*>(ws + L.lists.total), part, d.N, d.Hkv, d.nb,
+                           windows(d), KP, scale_log2, iscale);
     }
     hipLaunchKernelGGL((kl_local_combine_kernel<T, D, DI, G>), dim3((unsigned)(d.nb * d.B * d.Hkv)), dim3(256), 0,
                        st, tq, tk, tqi, tki, lse, part, kl_rows, d.B, d.N, d.Hkv, d.nb,

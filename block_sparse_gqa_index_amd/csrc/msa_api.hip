@@ -20,7 +20,7 @@ bool pow2_upto32(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g =
 // look at index_dim, so those are only checked for the ops that use them.
 int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (!d) return MSA_ERR_NULL;
-    const bool uses_heads = op != MSA_OP_INDEX, uses_index = op != MSA_OP_ATTN;
+    const bool uses_heads = op != MSA_OP_INDEX, uses_index = op != MSA_OP_ATTN;   // MSA_OP_FORWARD: both
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || d->topk < 1 ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
@@ -72,11 +72,12 @@ const char* msa_strerror(int status) {
 
 size_t msa_workspace_bytes(const msa_dims* dims, int op) {
     LaunchDims L;
-    if (op != MSA_OP_INDEX && op != MSA_OP_ATTN && op != MSA_OP_KL) return 0;
+    if (op != MSA_OP_INDEX && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_FORWARD) return 0;
     if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
     switch (op) {
         case MSA_OP_INDEX: return 0;
-        case MSA_OP_ATTN: return msa::attn_workspace_layout(L).bytes;
+        case MSA_OP_ATTN:
+        case MSA_OP_FORWARD: return msa::attn_workspace_layout(L).bytes;
         case MSA_OP_KL: return msa::kl_workspace_layout(L).bytes;
         default: return 0;
     }
@@ -92,7 +93,7 @@ int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, i
     if (empty(L)) return MSA_OK;
     if (!q_idx || !k_idx || !block_idx) return MSA_ERR_NULL;
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_idx)) return MSA_ERR_ALIGN;
-    return hip_status(msa::launch_index_topk(L, q_idx, k_idx, block_idx, static_cast<hipStream_t>(stream)));
+    return hip_status(msa::launch_index_topk(L, 0, L.nb, q_idx, k_idx, block_idx, static_cast<hipStream_t>(stream)));
 }
 
 int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
@@ -109,8 +110,29 @@ int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, cons
     const size_t need = msa::attn_workspace_layout(L).bytes;
     if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
-    return hip_status(msa::launch_sparse_attn(L, q, k, v, block_idx, scale, o, lse, ws,
-                                              static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (msa::launch_transpose_v(L, v, ws, s) != hipSuccess) return MSA_ERR_HIP;
+    return hip_status(msa::launch_sparse_attn(L, 0, L.nb, q, k, block_idx, scale, o, lse, ws, s));
+}
+
+int msa_forward(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q, const void* k,
+                const void* v, float softmax_scale, int32_t* block_idx, void* o, float* lse, void* ws,
+                size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_FORWARD, &L);
+    if (st != MSA_OK) return st;
+    if (empty(L)) return MSA_OK;
+    if (!q_idx || !k_idx || !q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_NULL;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        !aligned16(block_idx) || !aligned16(o) || !aligned16(lse))
+        return MSA_ERR_ALIGN;
+    const size_t need = msa::attn_workspace_layout(L).bytes;
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (msa::launch_index_topk(L, 0, L.nb, q_idx, k_idx, block_idx, s) != hipSuccess) return MSA_ERR_HIP;
+    if (msa::launch_transpose_v(L, v, ws, s) != hipSuccess) return MSA_ERR_HIP;
+    return hip_status(msa::launch_sparse_attn(L, 0, L.nb, q, k, block_idx, scale, o, lse, ws, s));
 }
 
 int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,

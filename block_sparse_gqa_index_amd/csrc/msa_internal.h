@@ -7,7 +7,8 @@
 
 namespace msa {
 
-constexpr int kSeg = 128;   // query positions per work item of the key-block-outer kernels
+constexpr int kSeg = 128;        // query positions per work item of the key-block-outer kernels
+constexpr int kWindow = 65536;   // query positions per window of the inverted selection
 
 // Validated problem sizes (see msa.h for their meaning).
 struct LaunchDims {
@@ -34,18 +35,32 @@ struct KlWorkspace {
 };
 
 ListLayout list_layout(const LaunchDims& d, size_t base);
-void launch_build_lists(const LaunchDims& d, const int32_t* block_idx, unsigned char* ws, const ListLayout& L,
-                        hipStream_t st);
+int windows(const LaunchDims& d);   // kWindow-position windows of the sequence
+
+// Work item handled by work-group x of a key-block-outer launch (grid a
+// multiple of 64): the 8 XCDs take turns on runs of 8 consecutive items, so all
+// XCDs move through the item list (and its windows) together while each XCD's
+// consecutive items usually share a key block in its L2.
+__device__ __forceinline__ int item_of_workgroup(int x) { return (x & ~63) + ((x & 7) << 3) + ((x >> 3) & 7); }
+// Lists for the query positions [p_lo, p_hi) of every (batch, group).
+void launch_build_lists(const LaunchDims& d, int p_lo, int p_hi, const int32_t* block_idx, unsigned char* ws,
+                        const ListLayout& L, hipStream_t st);
+// Upper bound on the work items launch_build_lists produces for that range.
+size_t list_items_bound(const LaunchDims& d, int p_lo, int p_hi, const ListLayout& L);
 
 AttnWorkspace attn_workspace_layout(const LaunchDims& d);
 KlWorkspace kl_workspace_layout(const LaunchDims& d);
 
-hipError_t launch_index_topk(const LaunchDims& d, const void* q_idx, const void* k_idx,
+// Selection for the query blocks [qb_lo, qb_hi).
+hipError_t launch_index_topk(const LaunchDims& d, int qb_lo, int qb_hi, const void* q_idx, const void* k_idx,
                              int32_t* block_idx, hipStream_t st);
 
-hipError_t launch_sparse_attn(const LaunchDims& d, const void* q, const void* k, const void* v,
-                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws,
-                              hipStream_t st);
+// V^T copy into the attention workspace (needed once per forward).
+hipError_t launch_transpose_v(const LaunchDims& d, const void* v, void* ws, hipStream_t st);
+
+// Attention for the query blocks [qb_lo, qb_hi); the V^T copy must be in ws.
+hipError_t launch_sparse_attn(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
+                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws, hipStream_t st);
 
 hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
                            const void* k_idx, const int32_t* block_idx, const float* lse, float scale,

@@ -119,26 +119,22 @@ __device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restr
 // the current tile is on the matrix cores.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ list, const int4* __restrict__ items, const int32_t* __restrict__ total_items,
-    const T* __restrict__ vt, T* __restrict__ po, float* __restrict__ plse, int N, int Hkv, int nb, int KP,
-    float scale_log2) {
+    const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ list, const int4* __restrict__ items, const int32_t* __restrict__ total_items,
+    const T* __restrict__ vt, T* __restrict__ po, float* __restrict__ plse, int N, int Hkv, int nb, int nwin,
+    int KP, float scale_log2) {
     using KV = KVTile<T, D>;
     constexpr int PPT = 32 / G;   // positions per 32-row tile
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
 
-    // Items of one XCD are contiguous (blocks are dealt to the 8 XCDs round-robin).
     const int total = total_items[0];
-    const int per_xcd = (total + 7) / 8;
-    const int slot_in_xcd = blockIdx.x / 8;
-    if (slot_in_xcd >= per_xcd) return;
-    const int item_id = (blockIdx.x % 8) * per_xcd + slot_in_xcd;
+    const int item_id = item_of_workgroup(blockIdx.x);
     if (item_id >= total) return;
     const int4 it = items[item_id];
     const int key = it.x, start = it.y, count = it.z;
     const int j = key % nb;
-    const int g = (key / nb) % Hkv;
-    const int b = key / (nb * Hkv);
+    const int bg = key / (nb * nwin);   // key = ((b * Hkv + g) * nwin + window) * nb + j
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
     const int Hq = Hkv * G;
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -229,15 +225,15 @@ struct PartialRow {
 // at a time to keep enough loads in flight.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ vt, const T* __restrict__ po, const float* __restrict__ plse, T* __restrict__ o,
-    float* __restrict__ lse, int B, int N, int Hkv, int nb, int topk, int KP, float scale_log2) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt, const T* __restrict__ po,
+    const float* __restrict__ plse, T* __restrict__ o, float* __restrict__ lse, int B, int N, int Hkv, int nb,
+    int qb_lo, int topk, int KP, float scale_log2) {
     using KV = KVTile<T, D>;
     constexpr int BATCH = 4;
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
     const int g = blockIdx.x % Hkv;
     const int b = (blockIdx.x / Hkv) % B;
-    const int qb = blockIdx.x / (Hkv * B);
+    const int qb = qb_lo + blockIdx.x / (Hkv * B);
     const int Hq = Hkv * G;
     const int q0 = qb * kBlock;
     const int valid_keys = min(kBlock, N - q0);
@@ -348,61 +344,80 @@ AttnWorkspace attn_workspace_layout(const LaunchDims& d) {
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_attn_t(const LaunchDims& d, const void* q, const void* k, const void* v,
-                                const int32_t* block_idx, float scale, void* o, float* lse,
-                                unsigned char* ws, hipStream_t st) {
+static hipError_t launch_attn_t(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
+                                const int32_t* block_idx, float scale, void* o, float* lse, unsigned char* ws,
+                                hipStream_t st) {
     const AttnWorkspace L = attn_workspace_layout(d);
     const float scale_log2 = scale * 1.4426950408889634f;
     const int KP = d.k > 1 ? d.k - 1 : 1;
     const T* tq = static_cast<const T*>(q);
     const T* tk = static_cast<const T*>(k);
-    const T* tv = static_cast<const T*>(v);
+    const T* vt = reinterpret_cast<const T*>(ws + L.vt);
     T* po = nullptr;
     float* plse = nullptr;
-    T* vt = reinterpret_cast<T*>(ws + L.vt);
-    hipLaunchKernelGGL((transpose_v_kernel<T, D>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st, tv, vt, d.N,
-                       d.Hkv, d.nb);
-    if (L.lists.has_nonlocal) {
-        launch_build_lists(d, block_idx, ws, L.lists, st);
+    // Rows of query block 0 keep no non-local block.
+    const bool nonlocal = L.lists.has_nonlocal && qb_hi > 1;
+    if (nonlocal) {
+        const int p_lo = qb_lo * kBlock, p_hi = min(d.N, qb_hi * kBlock);
+        launch_build_lists(d, p_lo, p_hi, block_idx, ws, L.lists, st);
         const int4* items = reinterpret_cast<const int4*>(ws + L.lists.items);
         const int32_t* list = reinterpret_cast<const int32_t*>(ws + L.lists.list);
         const int32_t* total = reinterpret_cast<const int32_t*>(ws + L.lists.total);
         po = reinterpret_cast<T*>(ws + L.po);
         plse = reinterpret_cast<float*>(ws + L.plse);
-        const size_t grid = (L.lists.max_items + 7) / 8 * 8;
-        hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tv,
-                           list, items, total, vt, po, plse, d.N, d.Hkv, d.nb, KP, scale_log2);
+        const size_t grid = (list_items_bound(d, p_lo, p_hi, L.lists) + 63) / 64 * 64;
+        hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, list,
+                           items, total, vt, po, plse, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
     }
-    hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G>), dim3((unsigned)(d.nb * d.B * d.Hkv)), dim3(256), 0, st,
-                       tq, tk, tv, vt, po, plse, static_cast<T*>(o), lse, d.B, d.N, d.Hkv, d.nb,
-                       L.lists.has_nonlocal ? d.k : 1, KP, scale_log2);
+    hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G>), dim3((unsigned)((qb_hi - qb_lo) * d.B * d.Hkv)),
+                       dim3(256), 0, st, tq, tk, vt, po, plse, static_cast<T*>(o), lse, d.B, d.N, d.Hkv, d.nb, qb_lo,
+                       nonlocal ? d.k : 1, KP, scale_log2);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_attn_d(const LaunchDims& d, const void* q, const void* k, const void* v,
+static hipError_t launch_attn_d(const LaunchDims& d, int lo, int hi, const void* q, const void* k,
                                 const int32_t* bi, float scale, void* o, float* lse, unsigned char* ws,
                                 hipStream_t st) {
     switch (d.G) {
-        case 1: return launch_attn_t<T, D, 1>(d, q, k, v, bi, scale, o, lse, ws, st);
-        case 2: return launch_attn_t<T, D, 2>(d, q, k, v, bi, scale, o, lse, ws, st);
-        case 4: return launch_attn_t<T, D, 4>(d, q, k, v, bi, scale, o, lse, ws, st);
-        case 8: return launch_attn_t<T, D, 8>(d, q, k, v, bi, scale, o, lse, ws, st);
-        case 16: return launch_attn_t<T, D, 16>(d, q, k, v, bi, scale, o, lse, ws, st);
-        default: return launch_attn_t<T, D, 32>(d, q, k, v, bi, scale, o, lse, ws, st);
+        case 1: return launch_attn_t<T, D, 1>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
+        case 2: return launch_attn_t<T, D, 2>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
+        case 4: return launch_attn_t<T, D, 4>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
+        case 8: return launch_attn_t<T, D, 8>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
+        case 16: return launch_attn_t<T, D, 16>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
+        default: return launch_attn_t<T, D, 32>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
     }
 }
 
-hipError_t launch_sparse_attn(const LaunchDims& d, const void* q, const void* k, const void* v,
-                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws,
-                              hipStream_t st) {
-    if (d.B == 0 || d.N == 0) return hipSuccess;
+hipError_t launch_sparse_attn(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
+                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws, hipStream_t st) {
+    if (d.B == 0 || d.N == 0 || qb_hi <= qb_lo) return hipSuccess;
     unsigned char* w = static_cast<unsigned char*>(ws);
     if (d.dtype == 0)
-        return d.D == 128 ? launch_attn_d<bf16_t, 128>(d, q, k, v, block_idx, scale, o, lse, w, st)
-                          : launch_attn_d<bf16_t, 64>(d, q, k, v, block_idx, scale, o, lse, w, st);
-    return d.D == 128 ? launch_attn_d<float, 128>(d, q, k, v, block_idx, scale, o, lse, w, st)
-                      : launch_attn_d<float, 64>(d, q, k, v, block_idx, scale, o, lse, w, st);
+        return d.D == 128 ? launch_attn_d<bf16_t, 128>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st)
+                          : launch_attn_d<bf16_t, 64>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st);
+    return d.D == 128 ? launch_attn_d<float, 128>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st)
+                      : launch_attn_d<float, 64>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st);
+}
+
+template <typename T, int D>
+static void transpose_v_t(const LaunchDims& d, const void* v, unsigned char* ws, hipStream_t st) {
+    const AttnWorkspace L = attn_workspace_layout(d);
+    hipLaunchKernelGGL((transpose_v_kernel<T, D>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st,
+                       static_cast<const T*>(v), reinterpret_cast<T*>(ws + L.vt), d.N, d.Hkv, d.nb);
+}
+
+hipError_t launch_transpose_v(const LaunchDims& d, const void* v, void* ws, hipStream_t st) {
+    if (d.B == 0 || d.N == 0) return hipSuccess;
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    if (d.dtype == 0) {
+        if (d.D == 128) transpose_v_t<bf16_t, 128>(d, v, w, st);
+        else transpose_v_t<bf16_t, 64>(d, v, w, st);
+    } else {
+        if (d.D == 128) transpose_v_t<float, 128>(d, v, w, st);
+        else transpose_v_t<float, 64>(d, v, w, st);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace msa

@@ -20,7 +20,7 @@
  *    block size Bk, blocks kept k. Query head h belongs to group h / G.
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    on it and outputs are valid once it has completed; the calls never
- *    synchronise, never allocate and never free.
+ *    synchronise and never allocate or free device memory.
  *  - Every status other than MSA_OK and MSA_ERR_HIP is returned before any
  *    device work is enqueued, with no output written. MSA_ERR_HIP reports a
  *    failed launch (the outputs are then unspecified).
@@ -50,7 +50,7 @@ extern "C" {
 enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1 };
 
 /* Selector for msa_workspace_bytes. */
-enum msa_op { MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2 };
+enum msa_op { MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3 };
 
 enum msa_status {
     MSA_OK = 0,
@@ -127,6 +127,16 @@ MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* 
 MSA_API int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
                         const int32_t* block_idx, float softmax_scale, void* o, float* lse,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole forward hot path in one call: msa_index_topk followed by
+ * msa_sparse_attn_fwd on `stream`, with the same arguments and results
+ * (block_idx, o and lse are outputs; every field of `dims` is used).
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_FORWARD) bytes.
+ */
+MSA_API int msa_forward(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q,
+                        const void* k, const void* v, float softmax_scale, int32_t* block_idx,
+                        void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * KL alignment loss forward.

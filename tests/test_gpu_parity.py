@@ -104,6 +104,13 @@ def run_and_check(w: Workload, positions=None, on_gpu_rng=False, check_kl=False)
     log(f"  attention: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} max|O|={np.abs(want_o).max():.2f}")
     assert err_o <= O_TOL and err_l <= LSE_TOL
 
+    # The fused, stream-overlapped entry point (what bench.py times) gives the
+    # same bits as the two separate calls checked above.
+    bi_f, o_f, lse_f = msa.forward(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(bi_f, bi) and torch.equal(o_f, o) and torch.equal(lse_f, lse)
+    log("  msa_forward bitwise equal to the separate calls")
+
     if check_kl:
         kl, kl_sum = msa.kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], bi, lse)
         torch.cuda.synchronize()
