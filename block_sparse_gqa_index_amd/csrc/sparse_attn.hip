@@ -82,11 +82,24 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ 
 // Partial layout, per (row (b,g,i), slot s < k-1): po[.][G][D] with each 32-wide
 // slice of D stored lane-major (slot dt*32 + 16*h + r holds
 // d = dt*32 + 8*(r/4) + 4*h + r%4), plse[.][G] natural-log LSE.
+// Partial O of one (row, slot): G heads x D values, stored as 16-byte pieces
+// interleaved across the 2G lanes (head hh, half h) that hold them in the
+// matrix-core output layout: piece q of lane (hh, h) sits at byte
+// 16 * (q * 2G + 2 * hh + h). One store (or load) instruction then covers 2G
+// consecutive pieces per position, i.e. whole cache lines, instead of 16
+// bytes in each of 2G different head rows. Piece q of a lane holds its values
+// 8q..8q+7 (bf16) or 4q..4q+3 (fp32) in accumulator order: for each 32-wide
+// slice dt of D, values r = 0..15 are d = dt*32 + 8*(r/4) + 4*h + r%4.
+template <typename T, int D, int G>
+__device__ __forceinline__ u32x4* partial_piece(T* region, int q, int hh, int half) {
+    return reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(region) + 16 * (q * 2 * G + 2 * hh + half));
+}
+
 template <typename T, int D, int G>
 __device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restrict__ plse, size_t pidx, int hh,
                                               int half, const floatx16 (&o)[D / 32], float mz, float l) {
     const float inv = 1.f / l;
-    T* dst = po + (pidx * G + hh) * D + 16 * half;
+    T* region = po + pidx * G * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
         if constexpr (sizeof(T) == 2) {
@@ -96,17 +109,15 @@ __device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restr
                 w0[r] = pack_bf16x2(o[dt][2 * r] * inv, o[dt][2 * r + 1] * inv);
                 w1[r] = pack_bf16x2(o[dt][8 + 2 * r] * inv, o[dt][8 + 2 * r + 1] * inv);
             }
-            u32x4* d4 = reinterpret_cast<u32x4*>(dst + dt * 32);
-            d4[0] = w0;
-            d4[1] = w1;
+            *partial_piece<T, D, G>(region, 2 * dt, hh, half) = w0;
+            *partial_piece<T, D, G>(region, 2 * dt + 1, hh, half) = w1;
         } else {
-            floatx4* d4 = reinterpret_cast<floatx4*>(dst + dt * 32);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                floatx4 x;
+                u32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = o[dt][4 * r + e] * inv;
-                d4[r] = x;
+                for (int e = 0; e < 4; ++e) x[e] = __float_as_uint(o[dt][4 * r + e] * inv);
+                *partial_piece<T, D, G>(region, 4 * dt + r, hh, half) = x;
             }
         }
     }
@@ -187,19 +198,15 @@ __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
 // holds the lane's 16 values per 32-wide slice of D in the stored order.
 template <typename T, int D>
 struct PartialRow {
-    static constexpr int NV = sizeof(T) == 2 ? D / 16 : D / 8;   // 16-byte vectors per lane
+    static constexpr int NV = sizeof(T) == 2 ? D / 16 : D / 8;   // 16-byte pieces per lane
     u32x4 x[NV];
-    __device__ __forceinline__ void load(const T* src) {
+    // `region`: the G x D partial of one (row, slot), in the interleaved order
+    // written by store_partial.
+    template <int G>
+    __device__ __forceinline__ void fetch(const T* region, int hh, int half) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) x[v] = reinterpret_cast<const u32x4*>(src)[(v / 2) * 4 + (v % 2)];
-    }
-    __device__ __forceinline__ void load_f32(const T* src) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) x[v] = reinterpret_cast<const u32x4*>(src)[(v / 4) * 8 + (v % 4)];
-    }
-    __device__ __forceinline__ void fetch(const T* src) {
-        if constexpr (sizeof(T) == 2) load(src);
-        else load_f32(src);
+        for (int v = 0; v < NV; ++v)
+            x[v] = *partial_piece<T, D, G>(const_cast<T*>(region), v, hh, half);
     }
     __device__ __forceinline__ void axpy(floatx16 (&acc)[D / 32], float w) const {
 #pragma unroll
@@ -290,12 +297,12 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[dt][r] *= wl;
         }
-        const T* pbase = po + (prow * G + hh) * D + 16 * half;
+        const T* pbase = po + prow * G * D;
         for (int sl0 = 0; sl0 < nnl; sl0 += BATCH) {
             PartialRow<T, D> pr[BATCH];
 #pragma unroll
             for (int u = 0; u < BATCH; ++u)
-                if (sl0 + u < nnl) pr[u].fetch(pbase + (size_t)(sl0 + u) * G * D);
+                if (sl0 + u < nnl) pr[u].template fetch<G>(pbase + (size_t)(sl0 + u) * G * D, hh, half);
 #pragma unroll
             for (int u = 0; u < BATCH; ++u)
                 if (sl0 + u < nnl) pr[u].axpy(acc, exp2f(pl[(sl0 + u) * G] * kLog2e - lse_all));
