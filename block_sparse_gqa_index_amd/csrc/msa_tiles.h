@@ -115,21 +115,35 @@ __device__ __forceinline__ void load_vt_op(Op8<T>& a, const unsigned char* vt, i
 
 // One 32-row tile against one LDS-resident 128-key block:
 // s[kt] = S^T tile kt (32 keys x 32 rows), scores only.
-template <typename T, int D>
+// WIDE: k-slice outer, key tile inner (four independent accumulation chains
+// per slice, the slice's four key operands live at a time); otherwise key tile
+// outer (one chain at a time, one operand live: fewer VGPRs).
+template <typename T, int D, bool WIDE = true>
 __device__ __forceinline__ void tile_scores(floatx16 (&s)[4], const Op8<T> (&bq)[D / 16],
                                             const unsigned char* lds, int col, int half) {
     using KS = SwzTile<T, D>;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        s[kt] = zero16();
+    for (int kt = 0; kt < 4; ++kt) s[kt] = zero16();
+    if constexpr (!WIDE) {
 #pragma unroll
-        for (int sl = 0; sl < D / 16; ++sl) {
-            Op8<T> a;
-            KS::load8(a, lds, kt * 32 + col, 16 * sl + 8 * half);
-            mma16(s[kt], a, bq[sl]);
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+            for (int sl = 0; sl < D / 16; ++sl) {
+                Op8<T> a;
+                KS::load8(a, lds, kt * 32 + col, 16 * sl + 8 * half);
+                mma16(s[kt], a, bq[sl]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // keep the scheduler from hoisting every LDS operand load of the tile
-        // (that would need 4*D/16 operand registers live at once)
+        return;
+    }
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) {
+        Op8<T> a[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) KS::load8(a[kt], lds, kt * 32 + col, 16 * sl + 8 * half);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) mma16(s[kt], a[kt], bq[sl]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
         load_q_op<T, D>(bq, q + ((size_t)b * N + ii) * Hq * D + (size_t)h * D, valid, half);
 
         floatx16 s[4];
-        tile_scores<T, D>(s, bq, lds, col, half);
+        tile_scores<T, D, false>(s, bq, lds, col, half);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
