@@ -1,15 +1,17 @@
 """Benchmark of the MSA forward hot path on one MI355X.
 
 One step = the whole hot path on one batch of synthetic input already resident
-in HBM: msa_forward, i.e. the selection (index scores, block max-pool,
-forced-local exp-free top-k) and the block-sparse GQA attention with LSE, the
-selection of each query chunk overlapping the attention of the previous one. Default workload: N = 128K tokens, Hkv = 8, G = 8,
-D = Di = 128, Bk = 128, k = 16, bf16, with long-range stripes.
+in HBM: the selection (index scores, block max-pool, forced-local exp-free
+top-k: msa_index_topk) and the block-sparse GQA attention with LSE (the three
+stages of msa_sparse_attn_fwd_stages), back to back on one stream. HIP events
+between the four calls time every kernel stage inside the timed steps.
+Default workload: N = 128K tokens, Hkv = 8, G = 8, D = Di = 128, Bk = 128,
+k = 16, bf16, with long-range stripes.
 
 Prints one JSON line: tokens/s (value), TFLOP/s and the fraction of the bf16
-MFMA peak for the step, a roofline entry for the dominant kernel (the fused
-index kernel, timed with HIP events on its stream), and the CPU oracle timed on
-a bounded sample of the same workload.
+MFMA peak for the step, a roofline entry for the dominant (longest) kernel and
+for the other two main kernels, and the CPU oracle timed on a bounded sample of
+the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload n128k] [--no-cpu-baseline]
 """
@@ -31,9 +33,9 @@ from synth import CONFIGS, make_inputs, sample_rows  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and MFMA)
-INDEX_KERNEL = "index_topk_kernel"
-INDEX_SOURCE = os.path.join(ROOT, "block_sparse_gqa_index_amd", "csrc", "index_topk.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_topk_n128k_traffic.json")
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CSRC = os.path.join(ROOT, "block_sparse_gqa_index_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_n128k.json")
 
 
 def log(msg):
@@ -59,17 +61,46 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_entry():
-    """HBM bytes per launch of the index kernel from the committed counter
-    summary, if it was taken on the current kernel source; else None."""
+def traffic_entry(kernel, workload):
+    """Measured HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE,
+    calibrated against a copy of known size) from the committed counter
+    summary, if it was taken on this workload and on the current source of the
+    file that holds the kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != source_digest(INDEX_SOURCE):
+    if t.get("workload") != workload:
         return None
-    return t.get("bytes_per_launch")
+    e = t.get("kernels", {}).get(kernel)
+    if not e or e.get("source_sha256_16") != source_digest(os.path.join(CSRC, e.get("source", "?"))):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def attention_bytes(w, block_idx):
+    """Algorithmic HBM bytes of the two attention kernels for this selection.
+
+    Non-local kernel, per kept non-local block of a (b, g, i) row: the row's G
+    query vectors (gathered), its normalised partial output (G x D) and G LSEs,
+    and its list entry; per distinct kept (b, g, j): K_j and V_j^T once.
+    Local + combine kernel: every row's partials and LSEs back, Q, the local
+    K/V block, O and LSE."""
+    es = 2 if w.dtype == "bf16" else 4
+    B, N, Hkv, G, D, Bk = w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim, w.block_size
+    L = (torch.arange(N, device=block_idx.device) // Bk).view(1, 1, N, 1)
+    nl = (block_idx >= 0) & (block_idx < L)
+    sel = int(nl.sum())
+    nb = (N + Bk - 1) // Bk
+    bg = torch.arange(B * Hkv, device=block_idx.device).view(B, Hkv, 1, 1).expand_as(block_idx)
+    kv_blocks = int(torch.unique((bg * nb + block_idx.long())[nl]).numel())
+    per_sel_nl = 2 * G * D * es + 4 * G + 4
+    kvb = 2 * Bk * D * es
+    nonlocal_b = sel * per_sel_nl + kv_blocks * kvb
+    combine_b = (sel * (G * D * es + 4 * G) + 2 * B * N * Hkv * G * D * es + B * Hkv * G * N * 4
+                 + B * Hkv * nb * kvb)
+    return {"selections": sel, "kv_blocks": kv_blocks, "nonlocal": nonlocal_b, "combine": combine_b}
 
 
 def cpu_baseline(w, x, seconds_target=15.0):
@@ -139,44 +170,63 @@ def main():
     ws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_FORWARD)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        msa.forward(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], w.topk, block_idx=block_idx, o=o,
-                    lse=lse, workspace=ws)
-
-    def staged(ev):
-        """The two stages as separate calls on one stream, with HIP events between
-        them: the index kernel's own duration on its stream."""
+    def step(ev):
+        """One step; ev[0..4] bracket the selection and the three attention stages."""
         ev[0].record(stream)
         msa.index_topk(x["q_idx"], x["k_idx"], w.topk, block_idx=block_idx)
         ev[1].record(stream)
-        msa.sparse_attn_fwd(x["q"], x["k"], x["v"], block_idx, o=o, lse=lse, workspace=ws)
-        ev[2].record(stream)
+        for s, e in ((msa.STAGE_PREPARE, ev[2]), (msa.STAGE_NONLOCAL, ev[3]), (msa.STAGE_COMBINE, ev[4])):
+            msa.sparse_attn_fwd(x["q"], x["k"], x["v"], block_idx, o=o, lse=lse, workspace=ws, stages=s)
+            e.record(stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        step()
+        step(events())
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
+    evs = [events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for ev in evs:
+        step(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    # Per-stage durations (not part of the timed steps): each stage alone on the stream.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(1, min(args.steps, 5)))]
-    for ev in events:
-        staged(ev)
+    stage_ms = {name: float(np.mean([ev[a].elapsed_time(ev[a + 1]) for ev in evs]))
+                for a, name in enumerate(("index_topk_kernel", "prepare", "attn_nonlocal_kernel",
+                                          "attn_local_combine_kernel"))}
+    # The forward entry point gives the same bits as the four calls.
+    ref = (block_idx.clone(), o.clone(), lse.clone())
+    msa.forward(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], w.topk, block_idx=block_idx, o=o, lse=lse,
+                workspace=ws)
     torch.cuda.synchronize()
-    idx_ms = [e[0].elapsed_time(e[1]) for e in events]
-    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
+    same = all(torch.equal(a, b) for a, b in zip(ref, (block_idx, o, lse)))
 
     f_idx, f_main = flops(w)
     tokens = B * N
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    t_idx = float(np.mean(idx_ms)) * 1e-3
-    achieved = f_idx / t_idx / 1e12
+    ab = attention_bytes(w, block_idx)
+    wl = w.name
+
+    def mfma_entry(kernel, work_flop):
+        a = work_flop / (stage_ms[kernel] * 1e-3) / 1e12
+        return {"kernel": kernel, "bound": "mfma", "achieved": a, "peak": peak, "unit": "TFLOP/s",
+                "frac": a / peak, "traffic": traffic_entry(kernel, wl), "algorithmic_tflop": work_flop / 1e12,
+                "ms": stage_ms[kernel]}
+
+    def hbm_entry(kernel, nbytes):
+        a = nbytes / (stage_ms[kernel] * 1e-3) / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": a / PEAK_HBM_GBS, "traffic": traffic_entry(kernel, wl), "algorithmic_bytes": nbytes,
+                "ms": stage_ms[kernel]}
+
+    rooflines = {"index_topk_kernel": mfma_entry("index_topk_kernel", f_idx),
+                 "attn_nonlocal_kernel": hbm_entry("attn_nonlocal_kernel", ab["nonlocal"]),
+                 "attn_local_combine_kernel": hbm_entry("attn_local_combine_kernel", ab["combine"])}
+    dominant = max(rooflines, key=lambda k: stage_ms[k])
     out = {
         "metric": "MSA fwd tokens/s and TFLOP/s (% bf16 MFMA peak) at N=128K, k=16, Bk=128",
         "value": tokens / (ms_step * 1e-3),
@@ -198,10 +248,10 @@ def main():
         "tflops": (f_idx + f_main) / (ms_step * 1e-3) / 1e12,
         "frac_of_peak": (f_idx + f_main) / (ms_step * 1e-3) / 1e12 / peak,
         "algorithmic_tflop": {"index": f_idx / 1e12, "attention": f_main / 1e12},
-        "stage_ms_unoverlapped": {"msa_index_topk": float(np.mean(idx_ms)),
-                                  "msa_sparse_attn_fwd": float(np.mean(attn_ms))},
-        "roofline": {"kernel": INDEX_KERNEL, "bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic_entry()},
+        "stage_ms": stage_ms,
+        "forward_matches_stages": same,
+        "roofline": rooflines[dominant],
+        "rooflines": rooflines,
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")

@@ -9,8 +9,9 @@ the library is missing, every call raises.
 Entry points (same names as the C ABI, without the ``msa_`` prefix):
   index_topk(q_idx, k_idx, topk)                   -> block_idx int32 [B, Hkv, N, k]
   sparse_attn_fwd(q, k, v, block_idx, scale)       -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])
+      (stages=... enqueues only some of its three stages: msa_sparse_attn_fwd_stages)
   kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse) -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])
-  forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse), both stages overlapped
+  forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse): selection, then attention
   workspace_bytes(dims, op)
 """
 import ctypes
@@ -23,9 +24,10 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_F32 = 0, 1
 MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD = 0, 1, 2, 3
+STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
-EXPORTS = ("msa_index_topk", "msa_sparse_attn_fwd", "msa_forward", "msa_kl_align_fwd",
+EXPORTS = ("msa_index_topk", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages", "msa_forward", "msa_kl_align_fwd",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -58,6 +60,8 @@ def load_library(path: str = LIB_PATH):
     dp = ctypes.POINTER(MsaDims)
     lib.msa_index_topk.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_fwd.argtypes = [dp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_fwd_stages.argtypes = [dp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz,
+                                               ctypes.c_int, vp]
     lib.msa_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                      vp, vp, vp, sz, vp]
     lib.msa_forward.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
@@ -66,7 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.msa_strerror.argtypes = [ctypes.c_int]
     lib.msa_strerror.restype = ctypes.c_char_p
     lib.msa_abi_version.restype = ctypes.c_int
-    for f in (lib.msa_index_topk, lib.msa_sparse_attn_fwd, lib.msa_kl_align_fwd, lib.msa_forward):
+    for f in (lib.msa_index_topk, lib.msa_sparse_attn_fwd, lib.msa_sparse_attn_fwd_stages,
+              lib.msa_kl_align_fwd, lib.msa_forward):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -136,9 +141,11 @@ def index_topk(q_idx, k_idx, topk, block_idx=None, block_size=128):
 
 
 def sparse_attn_fwd(q, k, v, block_idx, softmax_scale=0.0, o=None, lse=None, workspace=None,
-                    block_size=128):
+                    block_size=128, stages=STAGE_ALL):
     """Block-sparse GQA attention. q [B,N,Hq,D], k/v [B,N,Hkv,D], block_idx int32
-    [B,Hkv,N,topk] -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])."""
+    [B,Hkv,N,topk] -> (o [B,N,Hq,D], lse fp32 [B,Hq,N]). `stages` (a subset of
+    STAGE_ALL) enqueues only those stages; the stages of one result must run
+    in order on the same workspace, which the caller then passes in."""
     lib = load_library()
     _req(q, "q", ndim=4)
     _req(k, "k", dtype=q.dtype, ndim=4)
@@ -159,9 +166,16 @@ def sparse_attn_fwd(q, k, v, block_idx, softmax_scale=0.0, o=None, lse=None, wor
     _req(o, "o", dtype=q.dtype, ndim=4)
     _req(lse, "lse", dtype=torch.float32, ndim=3)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_ATTN), q.device, workspace)
-    _check(lib.msa_sparse_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
-                                   float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), nws,
-                                   _stream(q.device)))
+    if stages == STAGE_ALL:
+        _check(lib.msa_sparse_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
+                                       float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), nws,
+                                       _stream(q.device)))
+    else:
+        if stages != STAGE_PREPARE and ws is not None and ws is not workspace:
+            raise ValueError("a later stage needs the workspace of the earlier ones: pass workspace=")
+        _check(lib.msa_sparse_attn_fwd_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
+                                              float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), nws,
+                                              int(stages), _stream(q.device)))
     return o, lse
 
 
@@ -193,9 +207,8 @@ def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_sc
 
 def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0, block_idx=None, o=None, lse=None,
             workspace=None, block_size=128):
-    """The whole hot path (msa_forward): selection and sparse attention, the
-    selection of one query chunk overlapping the attention of the previous one.
-    Returns (block_idx int32 [B,Hkv,N,topk], o [B,N,Hq,D], lse fp32 [B,Hq,N])."""
+    """The whole hot path (msa_forward): the selection, then the sparse
+    attention on the same stream. Returns (block_idx int32 [B,Hkv,N,topk], o [B,N,Hq,D], lse fp32 [B,Hq,N])."""
     lib = load_library()
     _req(q_idx, "q_idx", ndim=4)
     _req(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)

@@ -96,12 +96,13 @@ int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, i
     return hip_status(msa::launch_index_topk(L, 0, L.nb, q_idx, k_idx, block_idx, static_cast<hipStream_t>(stream)));
 }
 
-int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
-                        const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
-                        size_t ws_bytes, void* stream) {
+int msa_sparse_attn_fwd_stages(const msa_dims* dims, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
+                               size_t ws_bytes, int stages, void* stream) {
     LaunchDims L;
     int st = check_dims(dims, MSA_OP_ATTN, &L);
     if (st != MSA_OK) return st;
+    if (stages <= 0 || (stages & ~MSA_STAGE_ALL)) return MSA_ERR_UNSUPPORTED;
     if (empty(L)) return MSA_OK;
     if (!q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(o) ||
@@ -111,8 +112,15 @@ int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, cons
     if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (msa::launch_transpose_v(L, v, ws, s) != hipSuccess) return MSA_ERR_HIP;
-    return hip_status(msa::launch_sparse_attn(L, 0, L.nb, q, k, block_idx, scale, o, lse, ws, s));
+    if ((stages & MSA_STAGE_PREPARE) && msa::launch_transpose_v(L, v, ws, s) != hipSuccess) return MSA_ERR_HIP;
+    return hip_status(msa::launch_sparse_attn(L, 0, L.nb, q, k, block_idx, scale, o, lse, ws, stages, s));
+}
+
+int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                        const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
+    return msa_sparse_attn_fwd_stages(dims, q, k, v, block_idx, softmax_scale, o, lse, ws, ws_bytes,
+                                      MSA_STAGE_ALL, stream);
 }
 
 int msa_forward(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q, const void* k,
@@ -132,7 +140,7 @@ int msa_forward(const msa_dims* dims, const void* q_idx, const void* k_idx, cons
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (msa::launch_index_topk(L, 0, L.nb, q_idx, k_idx, block_idx, s) != hipSuccess) return MSA_ERR_HIP;
     if (msa::launch_transpose_v(L, v, ws, s) != hipSuccess) return MSA_ERR_HIP;
-    return hip_status(msa::launch_sparse_attn(L, 0, L.nb, q, k, block_idx, scale, o, lse, ws, s));
+    return hip_status(msa::launch_sparse_attn(L, 0, L.nb, q, k, block_idx, scale, o, lse, ws, MSA_STAGE_ALL, s));
 }
 
 int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,

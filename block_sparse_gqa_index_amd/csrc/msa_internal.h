@@ -59,8 +59,11 @@ hipError_t launch_index_topk(const LaunchDims& d, int qb_lo, int qb_hi, const vo
 hipError_t launch_transpose_v(const LaunchDims& d, const void* v, void* ws, hipStream_t st);
 
 // Attention for the query blocks [qb_lo, qb_hi); the V^T copy must be in ws.
+// `stages`: bit 0 builds the query lists, bit 1 runs the non-local blocks,
+// bit 2 the local blocks and the merge (the MSA_STAGE_* values).
 hipError_t launch_sparse_attn(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
-                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws, hipStream_t st);
+                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws, int stages,
+                              hipStream_t st);
 
 hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
                            const void* k_idx, const int32_t* block_idx, const float* lse, float scale,

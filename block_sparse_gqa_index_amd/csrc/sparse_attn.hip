@@ -353,7 +353,7 @@ AttnWorkspace attn_workspace_layout(const LaunchDims& d) {
 template <typename T, int D, int G>
 static hipError_t launch_attn_t(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
                                 const int32_t* block_idx, float scale, void* o, float* lse, unsigned char* ws,
-                                hipStream_t st) {
+                                int stages, hipStream_t st) {
     const AttnWorkspace L = attn_workspace_layout(d);
     const float scale_log2 = scale * 1.4426950408889634f;
     const int KP = d.k > 1 ? d.k - 1 : 1;
@@ -366,17 +366,19 @@ static hipError_t launch_attn_t(const LaunchDims& d, int qb_lo, int qb_hi, const
     const bool nonlocal = L.lists.has_nonlocal && qb_hi > 1;
     if (nonlocal) {
         const int p_lo = qb_lo * kBlock, p_hi = min(d.N, qb_hi * kBlock);
-        launch_build_lists(d, p_lo, p_hi, block_idx, ws, L.lists, st);
+        if (stages & 1) launch_build_lists(d, p_lo, p_hi, block_idx, ws, L.lists, st);
         const int4* items = reinterpret_cast<const int4*>(ws + L.lists.items);
         const int32_t* list = reinterpret_cast<const int32_t*>(ws + L.lists.list);
         const int32_t* total = reinterpret_cast<const int32_t*>(ws + L.lists.total);
         po = reinterpret_cast<T*>(ws + L.po);
         plse = reinterpret_cast<float*>(ws + L.plse);
         const size_t grid = (list_items_bound(d, p_lo, p_hi, L.lists) + 63) / 64 * 64;
-        hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, list,
-                           items, total, vt, po, plse, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
+        if (stages & 2)
+            hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
+                               list, items, total, vt, po, plse, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
     }
-    hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G>), dim3((unsigned)((qb_hi - qb_lo) * d.B * d.Hkv)),
+    if (stages & 4)
+        hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G>), dim3((unsigned)((qb_hi - qb_lo) * d.B * d.Hkv)),
                        dim3(256), 0, st, tq, tk, vt, po, plse, static_cast<T*>(o), lse, d.B, d.N, d.Hkv, d.nb, qb_lo,
                        nonlocal ? d.k : 1, KP, scale_log2);
     return hipGetLastError();
@@ -384,27 +386,28 @@ static hipError_t launch_attn_t(const LaunchDims& d, int qb_lo, int qb_hi, const
 
 template <typename T, int D>
 static hipError_t launch_attn_d(const LaunchDims& d, int lo, int hi, const void* q, const void* k,
-                                const int32_t* bi, float scale, void* o, float* lse, unsigned char* ws,
+                                const int32_t* bi, float scale, void* o, float* lse, unsigned char* ws, int sg,
                                 hipStream_t st) {
     switch (d.G) {
-        case 1: return launch_attn_t<T, D, 1>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
-        case 2: return launch_attn_t<T, D, 2>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
-        case 4: return launch_attn_t<T, D, 4>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
-        case 8: return launch_attn_t<T, D, 8>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
-        case 16: return launch_attn_t<T, D, 16>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
-        default: return launch_attn_t<T, D, 32>(d, lo, hi, q, k, bi, scale, o, lse, ws, st);
+        case 1: return launch_attn_t<T, D, 1>(d, lo, hi, q, k, bi, scale, o, lse, ws, sg, st);
+        case 2: return launch_attn_t<T, D, 2>(d, lo, hi, q, k, bi, scale, o, lse, ws, sg, st);
+        case 4: return launch_attn_t<T, D, 4>(d, lo, hi, q, k, bi, scale, o, lse, ws, sg, st);
+        case 8: return launch_attn_t<T, D, 8>(d, lo, hi, q, k, bi, scale, o, lse, ws, sg, st);
+        case 16: return launch_attn_t<T, D, 16>(d, lo, hi, q, k, bi, scale, o, lse, ws, sg, st);
+        default: return launch_attn_t<T, D, 32>(d, lo, hi, q, k, bi, scale, o, lse, ws, sg, st);
     }
 }
 
 hipError_t launch_sparse_attn(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
-                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws, hipStream_t st) {
+                              const int32_t* block_idx, float scale, void* o, float* lse, void* ws, int stages,
+                              hipStream_t st) {
     if (d.B == 0 || d.N == 0 || qb_hi <= qb_lo) return hipSuccess;
     unsigned char* w = static_cast<unsigned char*>(ws);
     if (d.dtype == 0)
-        return d.D == 128 ? launch_attn_d<bf16_t, 128>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st)
-                          : launch_attn_d<bf16_t, 64>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st);
-    return d.D == 128 ? launch_attn_d<float, 128>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st)
-                      : launch_attn_d<float, 64>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, st);
+        return d.D == 128 ? launch_attn_d<bf16_t, 128>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, stages, st)
+                          : launch_attn_d<bf16_t, 64>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, stages, st);
+    return d.D == 128 ? launch_attn_d<float, 128>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, stages, st)
+                      : launch_attn_d<float, 64>(d, qb_lo, qb_hi, q, k, block_idx, scale, o, lse, w, stages, st);
 }
 
 template <typename T, int D>

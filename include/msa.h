@@ -129,6 +129,26 @@ MSA_API int msa_sparse_attn_fwd(const msa_dims* dims, const void* q, const void*
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The attention of msa_sparse_attn_fwd in separately enqueued stages, for
+ * callers that time or interleave them. Same arguments and results as
+ * msa_sparse_attn_fwd; `stages` is a bitwise OR of
+ *   MSA_STAGE_PREPARE   V^T copy and the inversion of block_idx into per-key-
+ *                       block query lists (workspace only)
+ *   MSA_STAGE_NONLOCAL  every non-local kept block: per-(row, slot) partial
+ *                       outputs and LSEs (workspace only)
+ *   MSA_STAGE_COMBINE   the local block of every row and the merge of its
+ *                       partials: writes o and lse
+ * A stage reads what the earlier stages left in `ws`, so for one result the
+ * three must run in this order on the same workspace, with unchanged inputs
+ * (separate calls are fine). MSA_STAGE_ALL is msa_sparse_attn_fwd. `stages`
+ * == 0 or with other bits set is MSA_ERR_UNSUPPORTED.
+ */
+enum { MSA_STAGE_PREPARE = 1, MSA_STAGE_NONLOCAL = 2, MSA_STAGE_COMBINE = 4, MSA_STAGE_ALL = 7 };
+MSA_API int msa_sparse_attn_fwd_stages(const msa_dims* dims, const void* q, const void* k, const void* v,
+                        const int32_t* block_idx, float softmax_scale, void* o, float* lse,
+                        void* ws, size_t ws_bytes, int stages, void* stream);
+
+/*
  * The whole forward hot path in one call: msa_index_topk followed by
  * msa_sparse_attn_fwd on `stream`, with the same arguments and results
  * (block_idx, o and lse are outputs; every field of `dims` is used).

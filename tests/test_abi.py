@@ -112,6 +112,18 @@ def test_null_and_alignment(lib):
     assert _kl(lib, d, {"ki": MISALIGNED}) == 4
 
 
+def test_attention_stages_argument(lib):
+    d = _dims()
+    p = [FAKE] * 4
+    for bad in (0, 8, -1, 9):
+        assert lib.msa_sparse_attn_fwd_stages(ctypes.byref(d), *p, 0.0, FAKE, FAKE, None, 0, bad, None) == 3
+    # a valid stage set goes on to the workspace check
+    assert lib.msa_sparse_attn_fwd_stages(ctypes.byref(d), *p, 0.0, FAKE, FAKE, None, 0, 2, None) == 5
+    # bad dims are reported before the stage set
+    assert lib.msa_sparse_attn_fwd_stages(ctypes.byref(_dims(head_dim=96)), *p, 0.0, FAKE, FAKE, None, 0, 0,
+                                          None) == 3
+
+
 def test_workspace_checks(lib):
     d = _dims()
     need = msa.workspace_bytes(d, msa.MSA_OP_ATTN)

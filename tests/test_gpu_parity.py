@@ -104,12 +104,20 @@ def run_and_check(w: Workload, positions=None, on_gpu_rng=False, check_kl=False)
     log(f"  attention: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} max|O|={np.abs(want_o).max():.2f}")
     assert err_o <= O_TOL and err_l <= LSE_TOL
 
-    # The fused, stream-overlapped entry point (what bench.py times) gives the
-    # same bits as the two separate calls checked above.
+    # The one-call forward and the staged attention (what bench.py times)
+    # give the same bits as the two separate calls checked above.
     bi_f, o_f, lse_f = msa.forward(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], w.topk)
     torch.cuda.synchronize()
     assert torch.equal(bi_f, bi) and torch.equal(o_f, o) and torch.equal(lse_f, lse)
-    log("  msa_forward bitwise equal to the separate calls")
+    dims = msa.make_dims(w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim, w.index_dim, w.topk,
+                         x["q"].dtype)
+    ws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_ATTN)), dtype=torch.uint8, device=x["q"].device)
+    o_s, lse_s = torch.empty_like(o), torch.empty_like(lse)
+    for stage in (msa.STAGE_PREPARE, msa.STAGE_NONLOCAL, msa.STAGE_COMBINE):
+        msa.sparse_attn_fwd(x["q"], x["k"], x["v"], bi, o=o_s, lse=lse_s, workspace=ws, stages=stage)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o) and torch.equal(lse_s, lse)
+    log("  msa_forward and the staged attention bitwise equal to the separate calls")
 
     if check_kl:
         kl, kl_sum = msa.kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], bi, lse)
