@@ -94,6 +94,13 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
 }
 
+// 2^x on the transcendental unit (v_exp_f32), without the library's rescaling
+// of arguments below -126: such results may come out as 0 instead of a
+// denormal. Every use here is a softmax term 2^(z - max) <= 1 summed with a
+// term equal to 1 (or weighted by one), so a lost term below 2^-126 changes no
+// result beyond fp32 rounding.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 __device__ __forceinline__ float max16(const floatx16& a) {

@@ -94,20 +94,17 @@ template <> struct PType<float> {
 };
 
 // V^T operand for 16-key slice c: keys 16c + {4h..4h+3} and 16c + 8 + {4h..4h+3}
-// of V^T row `d`.
+// of V^T row `d`, which the V^T copy stores contiguously at positions
+// 16c + 8h .. 16c + 8h + 7.
 template <typename T>
 __device__ __forceinline__ void load_vt_op(Op8<T>& a, const unsigned char* vt, int d, int c, int half) {
     using VS = SwzTile<T, kBlock>;
     constexpr int ES = sizeof(T);
-    const unsigned char* p0 = vt + VS::offset(d, (16 * c + 4 * half) * ES);
-    const unsigned char* p1 = vt + VS::offset(d, (16 * c + 8 + 4 * half) * ES);
     if constexpr (ES == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(p0);
-        const uint2 y = *reinterpret_cast<const uint2*>(p1);
-        a.v = __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
+        a.load(vt + VS::offset(d, (16 * c + 8 * half) * ES));
     } else {
-        const float4 x = *reinterpret_cast<const float4*>(p0);
-        const float4 y = *reinterpret_cast<const float4*>(p1);
+        const float4 x = *reinterpret_cast<const float4*>(vt + VS::offset(d, (16 * c + 8 * half) * ES));
+        const float4 y = *reinterpret_cast<const float4*>(vt + VS::offset(d, (16 * c + 8 * half + 4) * ES));
         a.v[0] = x.x; a.v[1] = x.y; a.v[2] = x.z; a.v[3] = x.w;
         a.v[4] = y.x; a.v[5] = y.y; a.v[6] = y.z; a.v[7] = y.w;
     }
@@ -193,7 +190,7 @@ __device__ __forceinline__ void tile_softmax(floatx16 (&s)[4], float scale_log2,
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = exp2f(fmaf(s[kt][r], scale_log2, -mz));
+            const float p = exp2_hw(fmaf(s[kt][r], scale_log2, -mz));
             s[kt][r] = p;
             l += p;
         }

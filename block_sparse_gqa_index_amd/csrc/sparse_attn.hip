@@ -37,42 +37,57 @@ namespace msa {
 // ------------------------------------------------------------- V^T copy --
 
 // V [B, N, Hkv, D] -> V^T [B, Hkv, nb, D, 128]: one key block of one group per
-// work-group, as EPC x EPC tiles transposed in registers (EPC = elements per
-// 16 bytes). Keys past N are written as zeros.
+// work-group. Within every group of 16 keys the positions are permuted so that
+// position 8h + e holds key 8*(e/4) + 4h + e%4 (h = 0, 1; e = 0..7): the keys a
+// lane of half-wave h feeds to the P V product for that 16-key slice (the
+// accumulator layout of the scores) then sit in one contiguous 16-byte chunk.
+// A thread transposes one 16-key x (16 bytes of dims) tile in registers. Keys
+// past N are written as zeros.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ v, T* __restrict__ vt, int N, int Hkv,
                                                           int nb) {
     constexpr int EPC = 16 / sizeof(T);
-    constexpr int KC = kBlock / EPC, DC = D / EPC;
+    constexpr int KG = kBlock / 16, DC = D / EPC;
     const int j = blockIdx.x % nb;
     const int bg = blockIdx.x / nb;
     const int g = bg % Hkv, b = bg / Hkv;
     T* dst = vt + (size_t)blockIdx.x * D * kBlock;
-    for (int item = threadIdx.x; item < KC * DC; item += blockDim.x) {
-        const int dc = item % DC, kc = item / DC;
-        u32x4 x[EPC];
+    for (int item = threadIdx.x; item < KG * DC; item += blockDim.x) {
+        const int dc = item % DC, kg = item / DC;
+        u32x4 x[16];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-            const int key = j * kBlock + kc * EPC + e;
+        for (int e = 0; e < 16; ++e) {
+            const int key = j * kBlock + kg * 16 + e;
             x[e] = u32x4{0u, 0u, 0u, 0u};
             if (key < N)
                 x[e] = *reinterpret_cast<const u32x4*>(v + (((size_t)b * N + key) * Hkv + g) * D + dc * EPC);
         }
 #pragma unroll
         for (int dd = 0; dd < EPC; ++dd) {
-            u32x4 y;
-            if constexpr (EPC == 8) {   // bf16: word w of row dd = keys 2w, 2w+1
+            T* row = dst + (size_t)(dc * EPC + dd) * kBlock + kg * 16;
+            if constexpr (EPC == 8) {   // bf16: chunk h holds keys 4h..4h+3, 8+4h..8+4h+3
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t lo = (x[2 * w][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
-                    const uint32_t hi = (x[2 * w + 1][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
-                    y[w] = lo | (hi << 16);
+                for (int h = 0; h < 2; ++h) {
+                    u32x4 y;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const int k0 = 8 * (w / 2) + 4 * h + 2 * (w % 2);
+                        const uint32_t lo = (x[k0][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
+                        const uint32_t hi = (x[k0 + 1][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
+                        y[w] = lo | (hi << 16);
+                    }
+                    *reinterpret_cast<u32x4*>(row + 8 * h) = y;
                 }
-            } else {                    // fp32
+            } else {                    // fp32: 4-key chunk q holds keys 8*(q%2) + 4*(q/2) + 0..3
 #pragma unroll
-                for (int w = 0; w < 4; ++w) y[w] = x[w][dd];
+                for (int qc = 0; qc < 4; ++qc) {
+                    u32x4 y;
+                    const int k0 = 8 * (qc % 2) + 4 * (qc / 2);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) y[w] = x[k0 + w][dd];
+                    *reinterpret_cast<u32x4*>(row + 4 * qc) = y;
+                }
             }
-            *reinterpret_cast<u32x4*>(dst + (size_t)(dc * EPC + dd) * kBlock + kc * EPC) = y;
         }
     }
 }
@@ -124,6 +139,28 @@ __device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restr
     if (half == 0) plse[pidx * G + hh] = (mz + __log2f(l)) * 0.69314718055994531f;
 }
 
+// One 32-row tile of a non-local work item: the lane's row is list entry `e`
+// (position << 5 | slot); scores against the staged block, softmax, P V and
+// the partial store (skipped for the padding rows past the item's end).
+template <typename T, int D, int G>
+__device__ __forceinline__ void nonlocal_tile(const Op8<T> (&qop)[D / 16], int e, bool valid,
+                                              const unsigned char* lds, T* __restrict__ po,
+                                              float* __restrict__ plse, int b, int g, int N, int Hkv, int KP,
+                                              float scale_log2, int hh, int col, int half) {
+    floatx16 s[4];
+    tile_scores<T, D>(s, qop, lds, col, half);
+    float mz, l;
+    tile_softmax(s, scale_log2, mz, l);
+    floatx16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
+    tile_pv<T, D>(o, s, lds, col, half);
+    if (valid) {
+        const int i = e >> 5, slot = e & 31;
+        store_partial<T, D, G>(po, plse, (((size_t)b * Hkv + g) * N + i) * KP + slot, hh, half, o, mz, l);
+    }
+}
+
 // One work-group per work item (batch, group, key block j, <= kSeg query
 // positions that kept j). K_j and V_j^T are staged in LDS once; each wave
 // streams 32-row tiles through them, loading the next tile's query rows while
@@ -166,29 +203,22 @@ __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     KV::stage(lds, k + kv_off, kv_row, vt + (((size_t)b * Hkv + g) * nb + j) * D * kBlock, kBlock);
     __syncthreads();
 
-    for (; base < count; base += stride) {
-        const bool valid = base + pp < count;
-        const int nbase = base + stride;
-        Op8<T> q_nxt[D / 16];
-        load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, nbase + pp < count, half);
-        const int e_nxt2 = list[start + min(nbase + stride + pp, count - 1)];
-
-        floatx16 s[4];
-        tile_scores<T, D>(s, q_cur, lds, col, half);
-        float mz, l;
-        tile_softmax(s, scale_log2, mz, l);
-        floatx16 o[D / 32];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
-        tile_pv<T, D>(o, s, lds, col, half);
-        if (valid) {
-            const int i = e_cur >> 5, slot = e_cur & 31;
-            store_partial<T, D, G>(po, plse, (((size_t)b * Hkv + g) * N + i) * KP + slot, hh, half, o, mz, l);
-        }
-#pragma unroll
-        for (int sl = 0; sl < D / 16; ++sl) q_cur[sl] = q_nxt[sl];
-        e_cur = e_nxt;
-        e_nxt = e_nxt2;
+    // Two query-operand buffers in turn (the loop body is written out twice so
+    // neither is copied into the other): the tile at `base` runs from one while
+    // the next tile's rows load into the other.
+    Op8<T> q_nxt[D / 16];
+    for (; base < count; base += 2 * stride) {
+        load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, base + stride + pp < count, half);
+        const int e_2 = list[start + min(base + 2 * stride + pp, count - 1)];
+        nonlocal_tile<T, D, G>(q_cur, e_cur, base + pp < count, lds, po, plse, b, g, N, Hkv, KP, scale_log2, hh,
+                               col, half);
+        if (base + stride >= count) break;
+        load_q_op<T, D>(q_cur, qbase + (size_t)(e_2 >> 5) * Hq * D, base + 2 * stride + pp < count, half);
+        const int e_3 = list[start + min(base + 3 * stride + pp, count - 1)];
+        nonlocal_tile<T, D, G>(q_nxt, e_nxt, base + stride + pp < count, lds, po, plse, b, g, N, Hkv, KP,
+                               scale_log2, hh, col, half);
+        e_cur = e_2;
+        e_nxt = e_3;
     }
 }
 
