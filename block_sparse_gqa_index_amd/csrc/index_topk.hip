@@ -30,6 +30,8 @@
 
 namespace msa {
 
+constexpr bool kPipelined = true;
+
 // Inserts (x, j) into the descending list; a no-op when x does not beat the
 // last entry (then no comparison below succeeds), so it runs without a branch
 // and can be scheduled under the matrix-core work of the next key block.
@@ -146,7 +148,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     for (int o = 0; o < NO; ++o) x_prev[o] = -__builtin_inff();
     for (int jp = 0; jp < qb; jp += BPB) {
         const int cur = (jp / BPB) & 1;
-        const bool more = jp + BPB < qb;
         // Next BPB key blocks: global -> VGPRs now, VGPRs -> LDS after this stage's math.
         u32x4 stage[BPB][CPT];
 #pragma unroll
@@ -195,14 +196,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
                 for (int o = 0; o < NO; ++o) x_prev[o] = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
             }
         }
-        if (more) {
+        // Unconditional (the last iteration writes a copy of the last block that
+        // nobody reads): a store under a branch lets the compiler sink the
+        // global loads above into that branch, after the math, where their
+        // latency is no longer hidden. The buffer written was last read before
+        // the previous barrier.
 #pragma unroll
-            for (int bb = 0; bb < BPB; ++bb) {
+        for (int bb = 0; bb < BPB; ++bb) {
 #pragma unroll
-                for (int u = 0; u < CPT; ++u) {
-                    const int ch = tid + NTHR * u;
-                    *reinterpret_cast<u32x4*>(&lds[cur ^ 1][bb][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[bb][u];
-                }
+            for (int u = 0; u < CPT; ++u) {
+                const int ch = tid + NTHR * u;
+                *reinterpret_cast<u32x4*>(&lds[cur ^ 1][bb][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[bb][u];
             }
         }
         __syncthreads();
@@ -210,6 +214,180 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     if (qb > 0) {
 #pragma unroll
         for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], qb - 1);
+    }
+
+    const int nvalid = min(nslots, qb);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+        const int t = NT >= 2 ? 2 * o + half : 0;
+        const int R = r0 + 32 * t + col;
+        const int pos = qb * kBlock + R / Hkv;
+        const int g = R % Hkv;
+        const bool writer = pos < N && (NT >= 2 || half == 0);
+        int v[SLOTS];
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) v[s] = id[o][s] < 0 ? 0x7fffffff : id[o][s];
+        sort_ascending<SLOTS>(v);
+        if (writer) {
+            int32_t* dst = block_idx + (((size_t)b * Hkv + g) * N + pos) * k;
+#pragma unroll
+            for (int s = 0; s <= SLOTS; ++s) {
+                if (s < k) dst[s] = s < nvalid ? v[s < SLOTS ? s : SLOTS - 1] : (s == nvalid ? qb : -1);
+            }
+        }
+    }
+}
+
+// Software-pipelined variant for 8-wave work-groups (one per CU, two waves
+// per SIMD): three LDS stages so that the first operands of key block j+1 can
+// be requested while block j is still on the matrix cores (block j+2 is
+// written to the third stage meanwhile, block j+3 is in flight in VGPRs, one
+// barrier per block), and the A operands of a block are requested PF ahead of
+// the MFMA that uses them, across block boundaries. The last key tile's max of
+// block j is taken under block j+1's first MFMAs, and its candidate inserted
+// right after.
+template <typename T, int DI, int NT, int WAVES, int SLOTS>
+__global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
+    const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
+    int B, int N, int Hkv, int k, int qb_lo, int qb_cnt, int chunks) {
+    constexpr int NTHR = 64 * WAVES;
+    constexpr int ES = sizeof(T);
+    constexpr int ROWB = DI * ES + 16;        // padded LDS row, bytes
+    constexpr int BUF = kBlock * ROWB;        // one stage
+    constexpr int KS = DI / 16;               // 16-deep slices of the contraction
+    constexpr int CPR = DI * ES / 16;         // 16-byte chunks per key row
+    constexpr int CPT = kBlock * CPR / NTHR;  // chunks per thread per key block
+    constexpr int NO = NT >= 2 ? NT / 2 : 1;  // rows each lane keeps a top-k list for
+    constexpr int NOPS = (kBlock / 32) * KS;  // A operands per key block
+    constexpr int RING = 8, PF = 6;           // operand registers; requests ahead of use
+    static_assert(CPT * NTHR == kBlock * CPR, "staging must tile the block");
+    static_assert(NOPS % RING == 0 && PF < RING, "operand ring must tile the block");
+    static_assert(NT % 2 == 0, "lanes of both half-waves own rows");
+    __shared__ __align__(16) unsigned char lds[3 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int per_qb = B * chunks;
+    const int qb = qb_lo + qb_cnt - 1 - (int)(blockIdx.x / per_qb);   // heaviest first
+    const int b = (int)(blockIdx.x % per_qb) / chunks;
+    const int c = (int)(blockIdx.x % chunks);
+    const int r0 = c * (32 * NT * WAVES) + w * (32 * NT);
+    const size_t qrow0 = ((size_t)b * N + (size_t)qb * kBlock) * Hkv;
+
+    Op8<T> bq[NT][KS];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int R = r0 + 32 * t + col;
+        const bool valid = qb * kBlock + R / Hkv < N;
+        const T* src = q_idx + (qrow0 + R) * DI + 8 * half;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (valid) bq[t][s].load(src + 16 * s);
+            else bq[t][s].zero();
+        }
+    }
+
+    float sc[NO][SLOTS];
+    int id[NO][SLOTS];
+    const int nslots = k - 1;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const bool dummy = s < SLOTS - nslots;   // unused slots sit above every score
+            sc[o][s] = dummy ? __builtin_inff() : -__builtin_inff();
+            id[o][s] = dummy ? -2 : -1;
+        }
+    }
+
+    // Stage offsets of this thread's chunks (global: linear; LDS: padded rows).
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
+    const size_t kblock_bytes = (size_t)kBlock * DI * ES;
+    const unsigned char* opbase = lds + col * ROWB + 8 * half * ES;   // + stage + operand offset
+    u32x4 stage[CPT];
+    Op8<T> a[RING];
+    if (qb > 0) {   // a row of query block 0 has no candidate block
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const unsigned char* src = kbase + (size_t)min(bb, qb - 1) * kblock_bytes;
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int ch = tid + NTHR * u;
+                *reinterpret_cast<u32x4*>(lds + bb * BUF + (ch / CPR) * ROWB + (ch % CPR) * 16) = stage[u];
+            }
+        }
+        const unsigned char* src = kbase + (size_t)min(2, qb - 1) * kblock_bytes;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+    }
+    __syncthreads();
+    if (qb > 0) {
+#pragma unroll
+        for (int m = 0; m < PF; ++m) a[m].load(opbase + ((m / KS) * 32) * ROWB + 16 * (m % KS) * ES);
+    }
+
+    float bm[NT], bm_prev[NT];
+    floatx16 acc[2][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        bm_prev[t] = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[1][t][r] = -__builtin_inff();
+    }
+    int sb = 0;   // stage of block j
+    for (int j = 0; j < qb; ++j) {
+        const int nb1 = sb == 2 ? 0 : sb + 1;    // stage of block j+1
+        const int wb = nb1 == 2 ? 0 : nb1 + 1;   // stage of block j+2 (= that of block j-1)
+#pragma unroll
+        for (int n = 0; n < NOPS; ++n) {
+            const int kt = n / KS, s = n % KS;
+            const int m = n + PF;
+            if (m < NOPS) a[m % RING].load(opbase + sb * BUF + ((m / KS) * 32) * ROWB + 16 * (m % KS) * ES);
+            else a[m % RING].load(opbase + nb1 * BUF + (((m - NOPS) / KS) * 32) * ROWB + 16 * ((m - NOPS) % KS) * ES);
+            if (s == 0) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) mma16(acc[kt & 1][t], a[n % RING], bq[t][s]);
+            if (s == KS - 1) {
+                if (kt == 0) {
+                    // block j-1: last tile's max, then its candidate
+#pragma unroll
+                    for (int o = 0; o < NO; ++o)
+                        topk_insert<SLOTS>(sc[o], id[o],
+                                           pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
+                                                        fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1]))),
+                                           j - 1);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) bm[t] = kt == 1 ? max16(acc[0][t]) : fmaxf(bm[t], max16(acc[(kt - 1) & 1][t]));
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bm_prev[t] = bm[t];
+        // Block j+2 into the stage block j-1 used; block j+3 into VGPRs.
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + NTHR * u;
+            *reinterpret_cast<u32x4*>(lds + wb * BUF + (ch / CPR) * ROWB + (ch % CPR) * 16) = stage[u];
+        }
+        const unsigned char* src = kbase + (size_t)min(j + 3, qb - 1) * kblock_bytes;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+        __syncthreads();
+        sb = nb1;
+    }
+    if (qb > 0) {
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+            topk_insert<SLOTS>(sc[o], id[o],
+                               pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
+                                            fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1]))),
+                               qb - 1);
     }
 
     const int nvalid = min(nslots, qb);
@@ -260,10 +438,33 @@ static hipError_t launch_cfg(const LaunchDims& d, int qb_lo, int qb_cnt, const v
 // waves (one per SIMD) of 64 rows each for bf16; two such work-groups share a
 // CU (measured faster than one 8-wave work-group with a shared LDS stage).
 template <typename T, int DI>
+static hipError_t launch_pipe(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
+                              int32_t* out, hipStream_t st) {
+    constexpr int NT = 2, WAVES = 8;
+    const int chunks = (kBlock * d.Hkv) / (32 * NT * WAVES);
+    const dim3 grid((unsigned)(qb_cnt * d.B * chunks)), block(64 * WAVES);
+    const T* q = static_cast<const T*>(q_idx);
+    const T* kk = static_cast<const T*>(k_idx);
+    if (d.k <= 8)
+        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 7>), grid, block, 0, st, q, kk, out, d.B, d.N,
+                           d.Hkv, d.k, qb_lo, qb_cnt, chunks);
+    else if (d.k <= 16)
+        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 15>), grid, block, 0, st, q, kk, out, d.B, d.N,
+                           d.Hkv, d.k, qb_lo, qb_cnt, chunks);
+    else
+        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 31>), grid, block, 0, st, q, kk, out, d.B, d.N,
+                           d.Hkv, d.k, qb_lo, qb_cnt, chunks);
+    return hipGetLastError();
+}
+
+template <typename T, int DI>
 static hipError_t launch_di(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                             int32_t* out, hipStream_t st) {
     constexpr int NT = sizeof(T) == 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
     const int rows = kBlock * d.Hkv;
+    if constexpr (sizeof(T) == 2) {
+        if (kPipelined && rows % (32 * 2 * 8) == 0) return launch_pipe<T, DI>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+    }
     if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
     return launch_cfg<T, DI, NT, 2>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
 }

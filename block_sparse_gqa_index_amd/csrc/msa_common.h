@@ -94,6 +94,15 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
 }
 
+// For a pair of per-half partial values a (row set A) and b (row set B), one
+// v_permlane32_swap leaves lane l < 32 with a[l] and a[l + 32] and lane
+// l >= 32 with b[l - 32] and b[l]: their max is the full value of row set A in
+// the lower half-wave and of row set B in the upper one, with no select.
+__device__ __forceinline__ float pair_max_own(float a, float b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // 2^x on the transcendental unit (v_exp_f32), without the library's rescaling
 // of arguments below -126: such results may come out as 0 instead of a
 // denormal. Every use here is a softmax term 2^(z - max) <= 1 summed with a
