@@ -119,16 +119,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
 
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
     const size_t kblock_bytes = (size_t)kBlock * DI * ES;
-    {
+    if (qb > 0) {   // a row of query block 0 has no candidate block (and block 0 may be short)
         u32x4 stage[BPB][CPT];
 #pragma unroll
         for (int bb = 0; bb < BPB; ++bb) {
-            const unsigned char* src = kbase + (size_t)min(bb, max(qb - 1, 0)) * kblock_bytes;
+            const unsigned char* src = kbase + (size_t)min(bb, qb - 1) * kblock_bytes;
 #pragma unroll
             for (int u = 0; u < CPT; ++u)
                 stage[bb][u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
         }
-        if (qb > 0) {
+        {
 #pragma unroll
             for (int bb = 0; bb < BPB; ++bb) {
 #pragma unroll
