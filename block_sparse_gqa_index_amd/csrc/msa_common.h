@@ -94,13 +94,20 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
 }
 
+// max of two scores with IEEE 754-2019 "maximum" semantics (NaN propagates;
+// +0 above -0): gfx950 has it as v_maximum3_f32, which needs none of the
+// operand canonicalisation fmaxf's IEEE-mode lowering adds for values that
+// come straight from the matrix cores. Identical to fmaxf on the finite
+// scores used here (+0 and -0 compare equal in every later comparison).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // For a pair of per-half partial values a (row set A) and b (row set B), one
 // v_permlane32_swap leaves lane l < 32 with a[l] and a[l + 32] and lane
 // l >= 32 with b[l - 32] and b[l]: their max is the full value of row set A in
 // the lower half-wave and of row set B in the upper one, with no select.
 __device__ __forceinline__ float pair_max_own(float a, float b) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // 2^x on the transcendental unit (v_exp_f32), without the library's rescaling
@@ -110,14 +117,14 @@ __device__ __forceinline__ float pair_max_own(float a, float b) {
 // result beyond fp32 rounding.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return vmax(a, vmax(b, c)); }
 
 __device__ __forceinline__ float max16(const floatx16& a) {
-    float m0 = max3f(a[0], a[1], a[2]);
-    float m1 = max3f(a[3], a[4], a[5]);
-    float m2 = max3f(a[6], a[7], a[8]);
-    float m3 = max3f(a[9], a[10], a[11]);
-    float m4 = max3f(a[12], a[13], a[14]);
+    const float m0 = max3f(a[0], a[1], a[2]);
+    const float m1 = max3f(a[3], a[4], a[5]);
+    const float m2 = max3f(a[6], a[7], a[8]);
+    const float m3 = max3f(a[9], a[10], a[11]);
+    const float m4 = max3f(a[12], a[13], a[14]);
     return max3f(max3f(m0, m1, m2), max3f(m3, m4, a[15]), m0);
 }
 

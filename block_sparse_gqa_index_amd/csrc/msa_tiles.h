@@ -182,8 +182,8 @@ __device__ __forceinline__ void load_q_op(Op8<T> (&bq)[D / 16], const T* row, bo
 __device__ __forceinline__ void tile_softmax(floatx16 (&s)[4], float scale_log2, float& mx, float& sum) {
     float m = -__builtin_inff();
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) m = fmaxf(m, max16(s[kt]));
-    m = fmaxf(m, swap_halves(m));
+    for (int kt = 0; kt < 4; ++kt) m = vmax(m, max16(s[kt]));
+    m = vmax(m, swap_halves(m));
     const float mz = m * scale_log2;
     float l = 0.f;
 #pragma unroll
