@@ -56,6 +56,17 @@ def flops(w):
     return f_idx, f_main
 
 
+def kl_flops(w):
+    """F_KL = (2·D·Hq + 2·Di·Hkv)·B·sum_i |T_i|: the main scores of the G heads and
+    the index scores over every selected token."""
+    B, N, Hkv, G, D, Di, Bk, k = (w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim,
+                                  w.index_dim, w.block_size, w.topk)
+    i = np.arange(N, dtype=np.int64)
+    L = i // Bk
+    tokens = float(((np.minimum(k, L + 1) - 1) * Bk + (i % Bk) + 1).sum())
+    return (2.0 * D * Hkv * G + 2.0 * Di * Hkv) * B * tokens
+
+
 def source_digest(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -140,6 +151,8 @@ def main():
     ap.add_argument("--workload", default="n128k", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--kl", action="store_true",
+                    help="also time the KL-alignment forward (msa_kl_align_fwd) on the step's outputs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -258,6 +271,26 @@ def main():
         "roofline": rooflines[dominant],
         "rooflines": rooflines,
     }
+    if args.kl:
+        log("[bench] KL-alignment forward")
+        kws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_KL)), dtype=torch.uint8, device=dev)
+        kl_rows = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev)
+        kl_sum = torch.empty((1,), dtype=torch.float32, device=dev)
+
+        def kl():
+            msa.kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], block_idx, lse, kl_rows=kl_rows,
+                             kl_sum=kl_sum, workspace=kws)
+        kl()
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(1, args.steps))]
+        for e in kev:
+            e[0].record(stream)
+            kl()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        kl_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
+        fk = kl_flops(w)
+        out["kl_align"] = {"ms": kl_ms, "algorithmic_tflop": fk / 1e12, "tflops": fk / (kl_ms * 1e-3) / 1e12,
+                           "frac_of_peak": fk / (kl_ms * 1e-3) / 1e12 / peak, "kl_sum": float(kl_sum.item())}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

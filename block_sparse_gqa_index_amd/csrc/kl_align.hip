@@ -24,56 +24,90 @@ namespace msa {
 constexpr int kKlPart = 8;          // floats per (row, slot) partial record
 constexpr int kRedThreads = 256;
 
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) x += __shfl_xor(x, m);
-    return x;
-}
-
 struct KlAcc {
     float A, Bs, P, mu, lu;
 };
 
-// Partial sums of one 32-row tile over one 128-key block. With MASK, keys past
-// `p_limit` (the query's offset in its block) are not visible.
+// Merges another (max, sum of exp(x - max)) pair into (mu, lu); -inf maxima
+// stand for empty sets.
+__device__ __forceinline__ void merge_lse(float& mu, float& lu, float omu, float olu) {
+    const float m = fmaxf(mu, omu);
+    lu = (mu == -__builtin_inff() ? 0.f : lu * exp2_hw((mu - m) * 1.4426950408889634f)) +
+         (omu == -__builtin_inff() ? 0.f : olu * exp2_hw((omu - m) * 1.4426950408889634f));
+    mu = m;
+}
+
+// Partial sums of one 32-row tile (32/G positions x G heads) over one 128-key
+// block. With MASK, keys past `p_limit` (the query's offset in its block) are
+// not visible. The teacher probability of a token is the mean over the G head
+// lanes of a position, so the per-token terms are the same in those G lanes:
+// a reduce-scatter over them (log2 G exchange steps, halving the values kept
+// per lane each time) leaves every lane with the head-sum of 64/G of the 64
+// tokens it holds, and the logarithms and exponentials below run once per
+// token instead of G times. The index scores u are equal in the G lanes (same
+// index query) and are only narrowed the same way.
 template <int G, bool MASK>
-__device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], floatx16 (&u)[4], float scale_log2, float lse2,
-                                         float iscale, int p_limit, int half) {
+__device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 (&u)[4], float scale_log2, float lse2,
+                                         float iscale, int p_limit, int half, int hh) {
     constexpr float kLn2 = 0.69314718055994531f;
-    KlAcc a{0.f, 0.f, 0.f, -__builtin_inff(), 0.f};
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr int NV = 64 / G;   // tokens per lane after the reduce-scatter
+    float v[64], uv[64];         // token t = kt * 16 + r of the lane's accumulator layout
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
             const bool vis = !MASK || key <= p_limit;
-            const float ph = vis ? exp2f(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
-            const float p = group_sum<G>(ph) * (1.0f / G);
-            const float uu = u[kt][r] * iscale;
-            u[kt][r] = vis ? uu : -__builtin_inff();
-            if (vis) {
-                if (p > 0.f) a.A += p * (__log2f(p) * kLn2);
-                a.Bs += p * uu;
-                a.P += p;
-                a.mu = fmaxf(a.mu, uu);
-            }
+            v[kt * 16 + r] = vis ? exp2_hw(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
+            uv[kt * 16 + r] = u[kt][r];
+        }
+    }
+    int base = 0;   // first token index the lane keeps
+#pragma unroll
+    for (int m = 1, n = 64; m < G; m <<= 1, n >>= 1) {
+        const bool hi = (hh & m) != 0;   // keep the upper half of the current n tokens
+#pragma unroll
+        for (int t = 0; t < n / 2; ++t) {
+            const float send = hi ? v[t] : v[t + n / 2];
+            const float keep = hi ? v[t + n / 2] : v[t];
+            v[t] = keep + __shfl_xor(send, m);
+            uv[t] = hi ? uv[t + n / 2] : uv[t];
+        }
+        base += hi ? n / 2 : 0;
+    }
+    KlAcc a{0.f, 0.f, 0.f, -__builtin_inff(), 0.f};
+    float uk[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+        const int t = base + e, kt = t >> 4, r = t & 15;
+        const int key = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool vis = !MASK || key <= p_limit;
+        const float p = v[e] * (1.0f / G);
+        const float uu = uv[e] * iscale;
+        uk[e] = vis ? uu : -__builtin_inff();
+        if (vis) {
+            if (p > 0.f) a.A += p * (__log2f(p) * kLn2);
+            a.Bs += p * uu;
+            a.P += p;
+            a.mu = fmaxf(a.mu, uu);
         }
     }
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) a.lu += __expf(u[kt][r] - a.mu);   // exp(-inf) = 0 for masked keys
-    }
+    for (int e = 0; e < NV; ++e) a.lu += exp2_hw((uk[e] - a.mu) * kLog2e);   // 0 for masked tokens
     if (a.mu == -__builtin_inff()) a.lu = 0.f;
+    // Combine the G lanes of the position, then the two half-waves.
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) {
+        a.A += __shfl_xor(a.A, m);
+        a.Bs += __shfl_xor(a.Bs, m);
+        a.P += __shfl_xor(a.P, m);
+        merge_lse(a.mu, a.lu, __shfl_xor(a.mu, m), __shfl_xor(a.lu, m));
+    }
     a.A += swap_halves(a.A);
     a.Bs += swap_halves(a.Bs);
     a.P += swap_halves(a.P);
-    const float omu = swap_halves(a.mu), olu = swap_halves(a.lu);
-    const float m = fmaxf(a.mu, omu);
-    a.lu = (a.mu == -__builtin_inff() ? 0.f : a.lu * __expf(a.mu - m)) +
-           (omu == -__builtin_inff() ? 0.f : olu * __expf(omu - m));
-    a.mu = m;
+    merge_lse(a.mu, a.lu, swap_halves(a.mu), swap_halves(a.lu));
     return a;
 }
 
@@ -120,7 +154,7 @@ __global__ __launch_bounds__(256, 1) void kl_nonlocal_kernel(
         tile_scores<T, D>(s, bq, lds, col, half);
         tile_scores<T, DI>(u, bi, lds_i, col, half);
         const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
-        const KlAcc a = tile_kl<G, false>(s, u, scale_log2, lse2, iscale, 0, half);
+        const KlAcc a = tile_kl<G, false>(s, u, scale_log2, lse2, iscale, 0, half, hh);
         if (valid && hh == 0 && half == 0) {
             float* dst = part + ((((size_t)b * Hkv + g) * N + i) * KP + slot) * kKlPart;
             *reinterpret_cast<float4*>(dst) = make_float4(a.A, a.Bs, a.P, a.mu);
@@ -165,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void kl_local_combine_kernel(
         tile_scores<T, D>(s, bq, lds, col, half);
         tile_scores<T, DI>(u, bi, lds_i, col, half);
         const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
-        KlAcc a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, p, half);
+        KlAcc a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, p, half, hh);
 
         const float* src = part + (((size_t)b * Hkv + g) * N + ii) * KP * kKlPart;
         for (int sl = 0; sl < nnl; ++sl) {
@@ -174,9 +208,7 @@ __global__ __launch_bounds__(256, 1) void kl_local_combine_kernel(
             a.A += x.x;
             a.Bs += x.y;
             a.P += x.z;
-            const float m = fmaxf(a.mu, x.w);
-            a.lu = a.lu * __expf(a.mu - m) + xl * __expf(x.w - m);
-            a.mu = m;
+            merge_lse(a.mu, a.lu, x.w, xl);
         }
         const float lse_u = a.mu + __logf(a.lu);
         if (valid && hh == 0 && half == 0) kl_rows[((size_t)b * Hkv + g) * N + i] = a.A - a.Bs + lse_u * a.P;
