@@ -47,20 +47,20 @@ __device__ __forceinline__ void merge_lse(float& mu, float& lu, float omu, float
 // token instead of G times. The index scores u are equal in the G lanes (same
 // index query) and are only narrowed the same way.
 template <int G, bool MASK>
-__device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 (&u)[4], float scale_log2, float lse2,
+__device__ __forceinline__ KlAcc tile_kl(floatx16 (&s)[4], floatx16 (&u)[4], float scale_log2, float lse2,
                                          float iscale, int p_limit, int half, int hh) {
     constexpr float kLn2 = 0.69314718055994531f;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr int NV = 64 / G;   // tokens per lane after the reduce-scatter
-    float v[64], uv[64];         // token t = kt * 16 + r of the lane's accumulator layout
+    // In place: s becomes the per-head probabilities, token t = kt * 16 + r of
+    // the lane's accumulator layout sitting at s[t / 16][t % 16].
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
             const bool vis = !MASK || key <= p_limit;
-            v[kt * 16 + r] = vis ? exp2_hw(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
-            uv[kt * 16 + r] = u[kt][r];
+            s[kt][r] = vis ? exp2_hw(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
         }
     }
     int base = 0;   // first token index the lane keeps
@@ -69,12 +69,19 @@ __device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 
         const bool hi = (hh & m) != 0;   // keep the upper half of the current n tokens
 #pragma unroll
         for (int t = 0; t < n / 2; ++t) {
-            const float send = hi ? v[t] : v[t + n / 2];
-            const float keep = hi ? v[t + n / 2] : v[t];
-            v[t] = keep + __shfl_xor(send, m);
-            uv[t] = hi ? uv[t + n / 2] : uv[t];
+            const int a0 = t, a1 = t + n / 2;
+            const float send = hi ? s[a0 >> 4][a0 & 15] : s[a1 >> 4][a1 & 15];
+            const float keep = hi ? s[a1 >> 4][a1 & 15] : s[a0 >> 4][a0 & 15];
+            s[a0 >> 4][a0 & 15] = keep + __shfl_xor(send, m);
+            u[a0 >> 4][a0 & 15] = hi ? u[a1 >> 4][a1 & 15] : u[a0 >> 4][a0 & 15];
         }
         base += hi ? n / 2 : 0;
+    }
+    float v[NV], uv[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+        v[e] = s[e >> 4][e & 15];
+        uv[e] = u[e >> 4][e & 15];
     }
     KlAcc a{0.f, 0.f, 0.f, -__builtin_inff(), 0.f};
     float uk[NV];
@@ -112,7 +119,7 @@ __device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 
 }
 
 template <typename T, int D, int DI, int G>
-__global__ __launch_bounds__(256, 1) void kl_nonlocal_kernel(
+__global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const float* __restrict__ lse, const int32_t* __restrict__ list, const int4* __restrict__ items,
     const int32_t* __restrict__ total_items, float* __restrict__ part, int N, int Hkv, int nb, int nwin, int KP,
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(256, 1) void kl_nonlocal_kernel(
 }
 
 template <typename T, int D, int DI, int G>
-__global__ __launch_bounds__(256, 1) void kl_local_combine_kernel(
+__global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const float* __restrict__ lse, const float* __restrict__ part, float* __restrict__ kl_rows, int B, int N,
     int Hkv, int nb, int topk, int KP, float scale_log2, float iscale) {
