@@ -151,6 +151,9 @@ SMALL = [
     Workload("ties", 1, 2048, 4, 8, 128, 128, topk=8, index_absmax=1),
     Workload("warmup_dense", 1, 520, 2, 4, 128, 64, topk=8),
     Workload("f32_d128_g8", 1, 700, 2, 8, 128, 64, topk=5, dtype="f32"),
+    # the 8-wave pipelined selection kernel (bf16, Hkv % 4 == 0): ragged N, B > 1, Di 64, k = 32
+    Workload("pipe_ragged_b2_di64", 2, 1500, 4, 2, 64, 64, topk=6),
+    Workload("pipe_k32_g1", 1, 3000, 8, 1, 64, 128, topk=32),
 ]
 
 
