@@ -8,6 +8,7 @@ the library is missing, every call raises.
 
 Entry points (same names as the C ABI, without the ``msa_`` prefix):
   index_topk(q_idx, k_idx, topk)                   -> block_idx int32 [B, Hkv, N, k]
+  check_block_idx(block_idx)                       -> int32 [1] on the device: rows breaking the layout
   sparse_attn_fwd(q, k, v, block_idx, scale)       -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])
       (stages=... enqueues only some of its three stages: msa_sparse_attn_fwd_stages)
   kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse) -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])
@@ -27,7 +28,8 @@ MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD = 0, 1, 2, 3
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
-EXPORTS = ("msa_index_topk", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages", "msa_forward", "msa_kl_align_fwd",
+EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
+           "msa_forward", "msa_kl_align_fwd",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -59,6 +61,7 @@ def load_library(path: str = LIB_PATH):
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     dp = ctypes.POINTER(MsaDims)
     lib.msa_index_topk.argtypes = [dp, vp, vp, vp, vp, sz, vp]
+    lib.msa_check_block_idx.argtypes = [dp, vp, vp, vp]
     lib.msa_sparse_attn_fwd.argtypes = [dp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_fwd_stages.argtypes = [dp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz,
                                                ctypes.c_int, vp]
@@ -70,7 +73,7 @@ def load_library(path: str = LIB_PATH):
     lib.msa_strerror.argtypes = [ctypes.c_int]
     lib.msa_strerror.restype = ctypes.c_char_p
     lib.msa_abi_version.restype = ctypes.c_int
-    for f in (lib.msa_index_topk, lib.msa_sparse_attn_fwd, lib.msa_sparse_attn_fwd_stages,
+    for f in (lib.msa_index_topk, lib.msa_check_block_idx, lib.msa_sparse_attn_fwd, lib.msa_sparse_attn_fwd_stages,
               lib.msa_kl_align_fwd, lib.msa_forward):
         f.restype = ctypes.c_int
     _lib = lib
@@ -138,6 +141,20 @@ def index_topk(q_idx, k_idx, topk, block_idx=None, block_size=128):
     _check(lib.msa_index_topk(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
                               None, 0, _stream(q_idx.device)))
     return block_idx
+
+
+def check_block_idx(block_idx, bad_rows=None, block_size=128):
+    """Number of rows of block_idx [B, Hkv, N, k] that do not follow the layout
+    index_topk writes (int32 [1] on the device, filled on the current stream)."""
+    lib = load_library()
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    B, Hkv, N, topk = block_idx.shape
+    if bad_rows is None:
+        bad_rows = torch.empty((1,), dtype=torch.int32, device=block_idx.device)
+    _req(bad_rows, "bad_rows", dtype=torch.int32)
+    dims = make_dims(B, N, Hkv, 1, 64, 64, topk, MSA_BF16, block_size)
+    _check(lib.msa_check_block_idx(ctypes.byref(dims), _ptr(block_idx), _ptr(bad_rows), _stream(block_idx.device)))
+    return bad_rows
 
 
 def sparse_attn_fwd(q, k, v, block_idx, softmax_scale=0.0, o=None, lse=None, workspace=None,

@@ -175,6 +175,42 @@ __global__ void items_kernel(const int32_t* __restrict__ counts, const int32_t* 
 }
 
 
+// ------------------------------------------------------- layout check --
+
+// One thread per (b, g, i) row: does the row follow the selection layout (the
+// first min(k, L+1) entries strictly ascending in [0, L] ending with L, then
+// -1)? Broken rows are counted into *bad (cleared first by the caller).
+__global__ __launch_bounds__(256) void check_rows_kernel(const int32_t* __restrict__ block_idx, int32_t* bad,
+                                                         int64_t rows, int N, int k) {
+    const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (x >= rows) return;
+    const int i = (int)(x % N);
+    const int L = i / kBlock;
+    const int nv = min(k, L + 1);
+    const int32_t* row = block_idx + x * k;
+    bool ok = true;
+    int prev = -1;
+    for (int s = 0; s < k; ++s) {
+        const int j = row[s];
+        if (s < nv) {
+            ok &= j > prev && j <= L && (s + 1 < nv || j == L);
+            prev = j;
+        } else {
+            ok &= j == -1;
+        }
+    }
+    if (!ok) atomicAdd(bad, 1);
+}
+
+hipError_t launch_check_block_idx(const LaunchDims& d, const int32_t* block_idx, int32_t* bad, hipStream_t st) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, bad, (size_t)1, 0);
+    const int64_t rows = (int64_t)d.B * d.Hkv * d.N;
+    if (rows > 0)
+        hipLaunchKernelGGL(check_rows_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, bad,
+                           rows, d.N, d.k);
+    return hipGetLastError();
+}
+
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int windows(const LaunchDims& d) { return (d.N + kWindow - 1) / kWindow; }

@@ -15,12 +15,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool pow2_upto32(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32; }
 
+constexpr int kOpLayout = -1;   // the block_idx layout check: neither heads nor index dims
+
 // Shape checks shared by all entry points; fills `out` on success. The index
 // selection does not look at group_size/head_dim and the attention does not
 // look at index_dim, so those are only checked for the ops that use them.
 int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (!d) return MSA_ERR_NULL;
-    const bool uses_heads = op != MSA_OP_INDEX, uses_index = op != MSA_OP_ATTN;   // MSA_OP_FORWARD: both
+    const bool uses_heads = op != MSA_OP_INDEX && op != kOpLayout;   // MSA_OP_FORWARD: both
+    const bool uses_index = op != MSA_OP_ATTN && op != kOpLayout;
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || d->topk < 1 ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
@@ -94,6 +97,15 @@ int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, i
     if (!q_idx || !k_idx || !block_idx) return MSA_ERR_NULL;
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_idx)) return MSA_ERR_ALIGN;
     return hip_status(msa::launch_index_topk(L, 0, L.nb, q_idx, k_idx, block_idx, static_cast<hipStream_t>(stream)));
+}
+
+int msa_check_block_idx(const msa_dims* dims, const int32_t* block_idx, int32_t* bad_rows, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, kOpLayout, &L);
+    if (st != MSA_OK) return st;
+    if (!bad_rows || (!empty(L) && !block_idx)) return MSA_ERR_NULL;
+    if (!aligned16(block_idx) || (reinterpret_cast<uintptr_t>(bad_rows) & 3u)) return MSA_ERR_ALIGN;
+    return hip_status(msa::launch_check_block_idx(L, block_idx, bad_rows, static_cast<hipStream_t>(stream)));
 }
 
 int msa_sparse_attn_fwd_stages(const msa_dims* dims, const void* q, const void* k, const void* v,

@@ -48,6 +48,9 @@ void launch_build_lists(const LaunchDims& d, int p_lo, int p_hi, const int32_t* 
 // Upper bound on the work items launch_build_lists produces for that range.
 size_t list_items_bound(const LaunchDims& d, int p_lo, int p_hi, const ListLayout& L);
 
+// Number of rows of block_idx that break the selection layout -> *bad.
+hipError_t launch_check_block_idx(const LaunchDims& d, const int32_t* block_idx, int32_t* bad, hipStream_t st);
+
 AttnWorkspace attn_workspace_layout(const LaunchDims& d);
 KlWorkspace kl_workspace_layout(const LaunchDims& d);
 

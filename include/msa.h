@@ -106,6 +106,20 @@ MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* 
                    int32_t* block_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Checks block_idx against the layout msa_index_topk writes, which is the
+ * precondition of msa_sparse_attn_fwd(_stages) and msa_kl_align_fwd: for the
+ * row of query i (local block L = i/Bk), the first min(k, L+1) entries are
+ * strictly ascending block ids in [0, L] with L last, and the other entries
+ * are -1. For callers that bring their own selection.
+ *
+ *   Uses batch, seqlen, kv_heads, block_size, topk, dtype and causal of `dims`.
+ *   block_idx [B, Hkv, N, k]  int32
+ *   bad_rows  [1] int32 OUTPUT on the device (overwritten): the number of rows
+ *             that break the layout (0 for an empty problem).
+ */
+MSA_API int msa_check_block_idx(const msa_dims* dims, const int32_t* block_idx, int32_t* bad_rows, void* stream);
+
+/*
  * Main branch: block-sparse GQA attention forward.
  * Defined by the MSA article (7minutos.es), "Cómo funcionan las dos ramas":
  * exact scaled-dot-product softmax over the causally visible tokens of the
@@ -116,8 +130,9 @@ MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* 
  *   q         [B, N, Hq, D]   dtype
  *   k, v      [B, N, Hkv, D]  dtype
  *   block_idx [B, Hkv, N, k]  int32, as written by msa_index_topk (per row:
- *             ascending distinct ids <= L, L last, -1 padding). Other contents
- *             are undefined behaviour.
+ *             ascending distinct ids <= L, L last, -1 padding; see
+ *             msa_check_block_idx). Other contents give unspecified outputs
+ *             (the kernels never access memory outside the given buffers).
  *   softmax_scale  sigma in z = sigma * <q, k_t>; <= 0 selects 1/sqrt(D).
  *   o         [B, N, Hq, D]   OUTPUT, dtype: sum_t exp(z_t - LSE) v_t
  *   lse       [B, Hq, N]      OUTPUT, fp32 natural-log log-sum-exp of z_t

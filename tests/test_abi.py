@@ -112,6 +112,19 @@ def test_null_and_alignment(lib):
     assert _kl(lib, d, {"ki": MISALIGNED}) == 4
 
 
+def test_layout_check_arguments(lib):
+    chk = lambda d, bi=FAKE, out=FAKE: lib.msa_check_block_idx(ctypes.byref(d), bi, out, None)
+    assert chk(_dims(topk=0)) == 2
+    assert chk(_dims(topk=33)) == 3
+    assert chk(_dims(block_size=64)) == 3
+    # head and index dims are not read
+    assert chk(_dims(head_dim=96, index_dim=96, group_size=3), out=None) == 1
+    assert chk(_dims(), bi=None) == 1
+    assert chk(_dims(), bi=MISALIGNED) == 4
+    assert chk(_dims(), out=ctypes.c_void_p(0x1002)) == 4
+    assert lib.msa_check_block_idx(None, FAKE, FAKE, None) == 1
+
+
 def test_attention_stages_argument(lib):
     d = _dims()
     p = [FAKE] * 4

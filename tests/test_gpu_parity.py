@@ -199,6 +199,26 @@ def test_deterministic_rerun():
         assert torch.equal(a, b)
 
 
+def test_block_idx_layout_check():
+    w = SMALL[0]
+    x = inputs_for(w, on_gpu_rng=False)
+    bi = msa.index_topk(x["q_idx"], x["k_idx"], w.topk)
+    assert int(msa.check_block_idx(bi).item()) == 0
+    bad = bi.clone()
+    bad[0, 0, 500, 0] = bad[0, 0, 500, 1]          # repeated id
+    bad[0, 1, 700, w.topk - 1] = 0                 # local block not last
+    bad[0, 2, 5, 1] = 3                            # padding that is not -1
+    bad[0, 3, 900, 0] = -1                         # hole among the kept blocks
+    torch.cuda.synchronize()
+    assert int(msa.check_block_idx(bad).item()) == 4
+    # the oracle's selection follows the layout too
+    kih = host(x["k_idx"])
+    pos = all_positions(w)[::97]
+    want = O.index_topk_rows(host(x["q_idx"]), kih, pos, w.block_size, w.topk)
+    got = rows_of(bi, pos)
+    assert np.array_equal(got, want)
+
+
 def test_empty_problems():
     for B, N in ((0, 256), (1, 0)):
         q_idx = torch.zeros((B, N, 2, 64), dtype=torch.bfloat16, device=DEV)
