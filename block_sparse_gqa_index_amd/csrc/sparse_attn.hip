@@ -258,15 +258,17 @@ struct PartialRow {
 
 // One work-group per (batch, query block, group): the causal local block for
 // all 128*G rows from LDS-resident K/V, then the merge with the rows'
-// non-local partials (log2 domain, slot order), which are fetched four slots
-// at a time to keep enough loads in flight.
-template <typename T, int D, int G>
+// non-local partials (log2 domain, slot order). The partial LSEs of all SL
+// possible slots are requested before the local block's math and kept in
+// registers (the loops over slots are unrolled, predicated on the row's slot
+// count); the partial outputs are fetched two slots at a time.
+template <typename T, int D, int G, int SL>
 __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt, const T* __restrict__ po,
     const float* __restrict__ plse, T* __restrict__ o, float* __restrict__ lse, int B, int N, int Hkv, int nb,
     int qb_lo, int topk, int KP, float scale_log2) {
     using KV = KVTile<T, D>;
-    constexpr int BATCH = 4;
+    constexpr int BATCH = 2;
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
     const int g = blockIdx.x % Hkv;
     const int b = (blockIdx.x / Hkv) % B;
@@ -294,6 +296,11 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
         const int ii = valid ? i : q0;
         Op8<T> bq[D / 16];
         load_q_op<T, D>(bq, q + ((size_t)b * N + ii) * Hq * D + (size_t)h * D, valid, half);
+        const size_t prow = (((size_t)b * Hkv + g) * N + ii) * KP;
+        const float* pl = plse + prow * G + hh;
+        float pls[SL];   // log2-domain LSE of each non-local slot (-inf past the row's count)
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) pls[sl] = sl < nnl ? pl[sl * G] * kLog2e : -__builtin_inff();
 
         floatx16 s[4];
         tile_scores<T, D, false>(s, bq, lds, col, half);
@@ -314,28 +321,31 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
 
         // LSE over the local block and every non-local slot (log2 domain).
         const float lse_loc = mz + __log2f(l);
-        const size_t prow = (((size_t)b * Hkv + g) * N + ii) * KP;
-        const float* pl = plse + prow * G + hh;
         float mx = lse_loc;
-        for (int sl = 0; sl < nnl; ++sl) mx = fmaxf(mx, pl[sl * G] * kLog2e);
-        float tot = exp2f(lse_loc - mx);
-        for (int sl = 0; sl < nnl; ++sl) tot += exp2f(pl[sl * G] * kLog2e - mx);
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) mx = fmaxf(mx, pls[sl]);
+        float tot = exp2_hw(lse_loc - mx);
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) tot += exp2_hw(pls[sl] - mx);   // 0 for absent slots
         const float lse_all = mx + __log2f(tot);
-        const float wl = exp2f(lse_loc - lse_all) / l;
+        const float wl = exp2_hw(lse_loc - lse_all) / l;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[dt][r] *= wl;
         }
         const T* pbase = po + prow * G * D;
-        for (int sl0 = 0; sl0 < nnl; sl0 += BATCH) {
-            PartialRow<T, D> pr[BATCH];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u)
-                if (sl0 + u < nnl) pr[u].template fetch<G>(pbase + (size_t)(sl0 + u) * G * D, hh, half);
+        for (int sl0 = 0; sl0 < SL; sl0 += BATCH) {
+            if (sl0 < nnl) {
+                PartialRow<T, D> pr[BATCH];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u)
-                if (sl0 + u < nnl) pr[u].axpy(acc, exp2f(pl[(sl0 + u) * G] * kLog2e - lse_all));
+                for (int u = 0; u < BATCH; ++u)
+                    if (sl0 + u < SL && sl0 + u < nnl) pr[u].template fetch<G>(pbase + (size_t)(sl0 + u) * G * D, hh, half);
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u)
+                    if (sl0 + u < SL && sl0 + u < nnl) pr[u].axpy(acc, exp2_hw(pls[sl0 + u] - lse_all));
+            }
         }
         if (valid) {
             T* dst = o + ((size_t)b * N + i) * Hq * D + (size_t)h * D;
@@ -407,10 +417,20 @@ static hipError_t launch_attn_t(const LaunchDims& d, int qb_lo, int qb_hi, const
             hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
                                list, items, total, vt, po, plse, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
     }
-    if (stages & 4)
-        hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G>), dim3((unsigned)((qb_hi - qb_lo) * d.B * d.Hkv)),
-                       dim3(256), 0, st, tq, tk, vt, po, plse, static_cast<T*>(o), lse, d.B, d.N, d.Hkv, d.nb, qb_lo,
-                       nonlocal ? d.k : 1, KP, scale_log2);
+    if (stages & 4) {
+        const dim3 grid((unsigned)((qb_hi - qb_lo) * d.B * d.Hkv));
+        const int kk = nonlocal ? d.k : 1;
+        T* to = static_cast<T*>(o);
+        if (kk <= 8)
+            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 7>), grid, dim3(256), 0, st, tq, tk, vt, po, plse,
+                               to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+        else if (kk <= 16)
+            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 15>), grid, dim3(256), 0, st, tq, tk, vt, po, plse,
+                               to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+        else
+            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 31>), grid, dim3(256), 0, st, tq, tk, vt, po, plse,
+                               to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+    }
     return hipGetLastError();
 }
 
