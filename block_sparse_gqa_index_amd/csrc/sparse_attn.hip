@@ -102,7 +102,10 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ 
 // matrix-core output layout: piece q of lane (hh, h) sits at byte
 // 16 * (q * 2G + 2 * hh + h). One store (or load) instruction then covers 2G
 // consecutive pieces per position, i.e. whole cache lines, instead of 16
-// bytes in each of 2G different head rows. Piece q of a lane holds its values
+// bytes in each of 2G different head rows. The pieces are stored
+// non-temporally: they are read back only by the merge kernel, and written
+// through the caches they would evict the query rows that the other items of
+// the same window gather again. Piece q of a lane holds its values
 // 8q..8q+7 (bf16) or 4q..4q+3 (fp32) in accumulator order: for each 32-wide
 // slice dt of D, values r = 0..15 are d = dt*32 + 8*(r/4) + 4*h + r%4.
 template <typename T, int D, int G>
@@ -124,15 +127,15 @@ __device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restr
                 w0[r] = pack_bf16x2(o[dt][2 * r] * inv, o[dt][2 * r + 1] * inv);
                 w1[r] = pack_bf16x2(o[dt][8 + 2 * r] * inv, o[dt][8 + 2 * r + 1] * inv);
             }
-            *partial_piece<T, D, G>(region, 2 * dt, hh, half) = w0;
-            *partial_piece<T, D, G>(region, 2 * dt + 1, hh, half) = w1;
+            __builtin_nontemporal_store(w0, partial_piece<T, D, G>(region, 2 * dt, hh, half));
+            __builtin_nontemporal_store(w1, partial_piece<T, D, G>(region, 2 * dt + 1, hh, half));
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 u32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = __float_as_uint(o[dt][4 * r + e] * inv);
-                *partial_piece<T, D, G>(region, 4 * dt + r, hh, half) = x;
+                __builtin_nontemporal_store(x, partial_piece<T, D, G>(region, 4 * dt + r, hh, half));
             }
         }
     }
@@ -231,12 +234,12 @@ struct PartialRow {
     static constexpr int NV = sizeof(T) == 2 ? D / 16 : D / 8;   // 16-byte pieces per lane
     u32x4 x[NV];
     // `region`: the G x D partial of one (row, slot), in the interleaved order
-    // written by store_partial.
+    // written by store_partial; read once, so non-temporally.
     template <int G>
     __device__ __forceinline__ void fetch(const T* region, int hh, int half) {
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-            x[v] = *partial_piece<T, D, G>(const_cast<T*>(region), v, hh, half);
+            x[v] = __builtin_nontemporal_load(partial_piece<T, D, G>(const_cast<T*>(region), v, hh, half));
     }
     __device__ __forceinline__ void axpy(floatx16 (&acc)[D / 32], float w) const {
 #pragma unroll
