@@ -28,6 +28,40 @@ struct KlAcc {
     float A, Bs, P, mu, lu;
 };
 
+// Value of the partner lane whose hh differs from this lane's in bit BIT and
+// agrees in every higher bit (lower bits may differ): DPP quad permutes for
+// bits 0 and 1, the 8- and 16-lane mirrors for bits 2 and 3 (lane i <-> 7-i,
+// 15-i), an LDS permute only for bit 4.
+template <int BIT>
+__device__ __forceinline__ float lane_pair(float x) {
+    const int v = __float_as_int(x);
+    if constexpr (BIT == 0) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+    else if constexpr (BIT == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+    else if constexpr (BIT == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));
+    else if constexpr (BIT == 3) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));
+    else return __shfl_xor(x, 1 << BIT);
+}
+
+// One reduce-scatter step over bit BIT of the head index (see tile_kl): keeps
+// the upper or lower half of the first N tokens, adding the partner's half.
+// The u values (equal in all lanes of the group) are narrowed with an exact
+// 0/1 blend rather than a select: selects of plain copies of accumulator
+// elements are folded by the compiler, across the unrolled steps, into one
+// lane-dependent element index that it expands as a compare chain per value.
+template <int BIT, int N>
+__device__ __forceinline__ void scatter_step(float (&v)[64], float (&uv)[64], int hh, int& base) {
+    const bool hi = (hh >> BIT) & 1;
+    const float fh = hi ? 1.f : 0.f, fl = 1.f - fh;
+#pragma unroll
+    for (int t = 0; t < N / 2; ++t) {
+        const float send = hi ? v[t] : v[t + N / 2];
+        const float keep = hi ? v[t + N / 2] : v[t];
+        v[t] = keep + lane_pair<BIT>(send);
+        uv[t] = fmaf(uv[t + N / 2], fh, uv[t] * fl);   // finite values: exact
+    }
+    base += hi ? N / 2 : 0;
+}
+
 // Merges another (max, sum of exp(x - max)) pair into (mu, lu); -inf maxima
 // stand for empty sets.
 __device__ __forceinline__ void merge_lse(float& mu, float& lu, float omu, float olu) {
@@ -35,6 +69,18 @@ __device__ __forceinline__ void merge_lse(float& mu, float& lu, float omu, float
     lu = (mu == -__builtin_inff() ? 0.f : lu * exp2_hw((mu - m) * 1.4426950408889634f)) +
          (omu == -__builtin_inff() ? 0.f : olu * exp2_hw((omu - m) * 1.4426950408889634f));
     mu = m;
+}
+
+// All-reduce step of the five sums over bit BIT of the head index (no-op when
+// the group has no such bit).
+template <int BIT, int G>
+__device__ __forceinline__ void combine_bit(KlAcc& a) {
+    if constexpr ((1 << BIT) < G) {
+        a.A += lane_pair<BIT>(a.A);
+        a.Bs += lane_pair<BIT>(a.Bs);
+        a.P += lane_pair<BIT>(a.P);
+        merge_lse(a.mu, a.lu, lane_pair<BIT>(a.mu), lane_pair<BIT>(a.lu));
+    }
 }
 
 // Partial sums of one 32-row tile (32/G positions x G heads) over one 128-key
@@ -47,42 +93,35 @@ __device__ __forceinline__ void merge_lse(float& mu, float& lu, float omu, float
 // token instead of G times. The index scores u are equal in the G lanes (same
 // index query) and are only narrowed the same way.
 template <int G, bool MASK>
-__device__ __forceinline__ KlAcc tile_kl(floatx16 (&s)[4], floatx16 (&u)[4], float scale_log2, float lse2,
+__device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 (&u)[4], float scale_log2, float lse2,
                                          float iscale, int p_limit, int half, int hh) {
     constexpr float kLn2 = 0.69314718055994531f;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr int NV = 64 / G;   // tokens per lane after the reduce-scatter
-    // In place: s becomes the per-head probabilities, token t = kt * 16 + r of
-    // the lane's accumulator layout sitting at s[t / 16][t % 16].
+    // Per-token values as plain scalars (token t = kt * 16 + r of the lane's
+    // accumulator layout): selecting between two elements of one vector
+    // register tuple with a lane-dependent condition is compiled as a dynamic
+    // element index (a compare chain per element), between scalars as one
+    // v_cndmask.
+    float v[64], uv[64];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
             const bool vis = !MASK || key <= p_limit;
-            s[kt][r] = vis ? exp2_hw(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
+            v[kt * 16 + r] = vis ? exp2_hw(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
+            uv[kt * 16 + r] = u[kt][r];
         }
     }
+    // Highest head bit first: the mirror pairings flip the lower bits too,
+    // which is harmless while those bits are still to be reduced.
     int base = 0;   // first token index the lane keeps
-#pragma unroll
-    for (int m = 1, n = 64; m < G; m <<= 1, n >>= 1) {
-        const bool hi = (hh & m) != 0;   // keep the upper half of the current n tokens
-#pragma unroll
-        for (int t = 0; t < n / 2; ++t) {
-            const int a0 = t, a1 = t + n / 2;
-            const float send = hi ? s[a0 >> 4][a0 & 15] : s[a1 >> 4][a1 & 15];
-            const float keep = hi ? s[a1 >> 4][a1 & 15] : s[a0 >> 4][a0 & 15];
-            s[a0 >> 4][a0 & 15] = keep + __shfl_xor(send, m);
-            u[a0 >> 4][a0 & 15] = hi ? u[a1 >> 4][a1 & 15] : u[a0 >> 4][a0 & 15];
-        }
-        base += hi ? n / 2 : 0;
-    }
-    float v[NV], uv[NV];
-#pragma unroll
-    for (int e = 0; e < NV; ++e) {
-        v[e] = s[e >> 4][e & 15];
-        uv[e] = u[e >> 4][e & 15];
-    }
+    if constexpr (G >= 32) scatter_step<4, 64>(v, uv, hh, base);
+    if constexpr (G >= 16) scatter_step<3, 64 * 16 / G>(v, uv, hh, base);
+    if constexpr (G >= 8) scatter_step<2, 64 * 8 / G>(v, uv, hh, base);
+    if constexpr (G >= 4) scatter_step<1, 64 * 4 / G>(v, uv, hh, base);
+    if constexpr (G >= 2) scatter_step<0, 64 * 2 / G>(v, uv, hh, base);
     KlAcc a{0.f, 0.f, 0.f, -__builtin_inff(), 0.f};
     float uk[NV];
 #pragma unroll
@@ -104,13 +143,11 @@ __device__ __forceinline__ KlAcc tile_kl(floatx16 (&s)[4], floatx16 (&u)[4], flo
     for (int e = 0; e < NV; ++e) a.lu += exp2_hw((uk[e] - a.mu) * kLog2e);   // 0 for masked tokens
     if (a.mu == -__builtin_inff()) a.lu = 0.f;
     // Combine the G lanes of the position, then the two half-waves.
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) {
-        a.A += __shfl_xor(a.A, m);
-        a.Bs += __shfl_xor(a.Bs, m);
-        a.P += __shfl_xor(a.P, m);
-        merge_lse(a.mu, a.lu, __shfl_xor(a.mu, m), __shfl_xor(a.lu, m));
-    }
+    combine_bit<0, G>(a);
+    combine_bit<1, G>(a);
+    combine_bit<2, G>(a);
+    combine_bit<3, G>(a);
+    combine_bit<4, G>(a);
     a.A += swap_halves(a.A);
     a.Bs += swap_halves(a.Bs);
     a.P += swap_halves(a.P);
