@@ -356,11 +356,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
                 if (kt == 0) {
                     // block j-1: last tile's max, then its candidate
 #pragma unroll
-                    for (int o = 0; o < NO; ++o)
-                        topk_insert<SLOTS>(sc[o], id[o],
-                                           pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
-                                                        fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1]))),
-                                           j - 1);
+                    for (int o = 0; o < NO; ++o) {
+                        const float x = pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
+                                                     fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1])));
+                        // skipped by the whole wave when no row's candidate beats its
+                        // current last entry (rare for late blocks of long rows)
+                        if (__builtin_amdgcn_ballot_w64(x > sc[o][SLOTS - 1]))
+                            topk_insert<SLOTS>(sc[o], id[o], x, j - 1);
+                    }
                 } else {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) bm[t] = kt == 1 ? max16(acc[0][t]) : fmaxf(bm[t], max16(acc[(kt - 1) & 1][t]));
