@@ -8,7 +8,7 @@
 // order, so the ranking runs on raw scores: no max/exp/sum before selection).
 // The Flash-MSA article (tech.kuratif.com) describes the proxy pass as a
 // stream over keys that keeps running top-k candidates and accumulates no
-// output; this kernel does the same with a CDNA4 layout:
+// output; these kernels do the same with a CDNA4 layout:
 //
 //  * A work-group owns 32*NT*WAVES (query, group) rows of one query block
 //    (64 rows per wave, two waves per SIMD for bf16). Rows of a query block
@@ -16,21 +16,24 @@
 //    anywhere: the local block is forced in and never scored.
 //  * The rows' index queries stay in VGPRs as the B operand of
 //    v_mfma_f32_32x32x16_bf16 for the whole kernel; each key block of k_idx
-//    (128 keys x Di) is staged once per work-group in LDS (double-buffered,
-//    16-byte padded rows) and read as the A operand, so the product is S^T:
-//    every lane's 16 accumulators belong to ONE query row. The 128-key block max
-//    is then 4 x 16 in-lane maxima plus one half-wave swap (v_permlane32_swap).
+//    (128 keys x Di) is staged once per work-group in LDS (16-byte padded
+//    rows) and read as the A operand, so the product is S^T: every lane's 16
+//    accumulators belong to ONE query row. The 128-key block max is then
+//    4 x 16 in-lane maxima plus one half-wave exchange (v_permlane32_swap).
 //  * Each lane keeps the running top-(k-1) of its rows in registers, sorted by
 //    score; blocks arrive in ascending id order, so "strictly greater" is the
 //    whole tie-break (an equal score never displaces a lower id).
 //  * Work-groups are numbered heaviest query block first (longest-processing-
 //    time order over the triangular load).
+//
+// index_topk_pipe_kernel (bf16 when 512 rows tile a query block) is the
+// software-pipelined form with three LDS stages and one 8-wave work-group per
+// CU; index_topk_kernel (2- or 4-wave work-groups, two LDS stages) serves the
+// other shapes and fp32.
 #include "msa_common.h"
 #include "msa_internal.h"
 
 namespace msa {
-
-constexpr bool kPipelined = true;
 
 // Inserts (x, j) into the descending list; a no-op when x does not beat the
 // last entry (then no comparison below succeeds), so it runs without a branch
@@ -418,9 +421,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
 template <typename T, int DI, int NT, int WAVES>
 static hipError_t launch_cfg(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                              int32_t* out, hipStream_t st) {
-    // Two key blocks per barrier when the doubled LDS stage still fits (one
-    // 8-wave work-group per CU anyway); otherwise one.
-    constexpr int BPB = (WAVES == 8 && 2 * 2 * kBlock * (DI * (int)sizeof(T) + 16) <= 160 * 1024) ? 2 : 1;
+    // One key block per barrier: two such work-groups share a CU (two LDS
+    // stages each), which measured faster than fewer, larger stages.
+    constexpr int BPB = 1;
     const int chunks = (kBlock * d.Hkv) / (32 * NT * WAVES);
     const dim3 grid((unsigned)(qb_cnt * d.B * chunks)), block(64 * WAVES);
     const T* q = static_cast<const T*>(q_idx);
@@ -437,9 +440,9 @@ static hipError_t launch_cfg(const LaunchDims& d, int qb_lo, int qb_cnt, const v
     return hipGetLastError();
 }
 
-// A work-group holds 32*NT*WAVES rows of one query block (128*Hkv rows): 4
-// waves (one per SIMD) of 64 rows each for bf16; two such work-groups share a
-// CU (measured faster than one 8-wave work-group with a shared LDS stage).
+// Shapes: the pipelined 8-wave kernel when 512 rows tile a query block (128*Hkv
+// rows) in bf16; else 4-wave work-groups (one wave per SIMD, 64 rows per wave
+// for bf16, two work-groups per CU) when 256 rows do, else 2-wave ones.
 template <typename T, int DI>
 static hipError_t launch_pipe(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                               int32_t* out, hipStream_t st) {
@@ -466,7 +469,7 @@ static hipError_t launch_di(const LaunchDims& d, int qb_lo, int qb_cnt, const vo
     constexpr int NT = sizeof(T) == 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
     const int rows = kBlock * d.Hkv;
     if constexpr (sizeof(T) == 2) {
-        if (kPipelined && rows % (32 * 2 * 8) == 0) return launch_pipe<T, DI>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+        if (rows % (32 * 2 * 8) == 0) return launch_pipe<T, DI>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
     }
     if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
     return launch_cfg<T, DI, NT, 2>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
