@@ -176,34 +176,48 @@ __global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
     const int b = bg / Hkv;
     const int Hq = Hkv * G;
 
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int hh = col % G, pp = col / G;
+    const int stride = 4 * PPT;
+    constexpr float kLog2e = 1.4426950408889634f;
+    auto entry = [&](int at) { return list[start + min(at + pp, count - 1)]; };
+    auto qrow = [&](int e) { return q + ((size_t)b * N + (e >> 5)) * Hq * D + (size_t)(g * G + hh) * D; };
+    auto qirow = [&](int e) { return q_idx + (((size_t)b * N + (e >> 5)) * Hkv + g) * DI; };
+
+    // The first tile's rows are requested before the K staging; afterwards each
+    // tile's query operands are refilled with the next tile's rows as soon as
+    // its scores are on the matrix cores.
+    int base = w * PPT;
+    int e_cur = entry(base);
+    Op8<T> bq[D / 16];
+    Op8<T> bi[DI / 16];
+    load_q_op<T, D>(bq, qrow(e_cur), base + pp < count, half);
+    load_q_op<T, DI>(bi, qirow(e_cur), base + pp < count, half);
+
     stage_rows<T, D>(lds, k + ((size_t)b * N + (size_t)j * kBlock) * Hkv * D + (size_t)g * D, (size_t)Hkv * D,
                      kBlock);
     stage_rows<T, DI>(lds_i, k_idx + ((size_t)b * N + (size_t)j * kBlock) * DI, DI, kBlock);
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int half = lane >> 5, col = lane & 31;
-    const int hh = col % G;
-    constexpr float kLog2e = 1.4426950408889634f;
-    for (int base = w * PPT; base < count; base += 4 * PPT) {
-        const int e = base + col / G;
-        const bool valid = e < count;
-        const int packed = list[start + (valid ? e : 0)];
-        const int i = packed >> 5, slot = packed & 31;
-        Op8<T> bq[D / 16];
-        load_q_op<T, D>(bq, q + ((size_t)b * N + i) * Hq * D + (size_t)(g * G + hh) * D, valid, half);
-        Op8<T> bi[DI / 16];
-        load_q_op<T, DI>(bi, q_idx + (((size_t)b * N + i) * Hkv + g) * DI, valid, half);
+    for (; base < count; base += stride) {
+        const bool valid = base + pp < count;
+        const int i = e_cur >> 5, slot = e_cur & 31;
+        const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
+        const int e_nxt = entry(base + stride);
+        const bool nvalid = base + stride + pp < count;
         floatx16 s[4], u[4];
         tile_scores<T, D>(s, bq, lds, col, half);
+        load_q_op<T, D>(bq, qrow(e_nxt), nvalid, half);
         tile_scores<T, DI>(u, bi, lds_i, col, half);
-        const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
+        load_q_op<T, DI>(bi, qirow(e_nxt), nvalid, half);
         const KlAcc a = tile_kl<G, false>(s, u, scale_log2, lse2, iscale, 0, half, hh);
         if (valid && hh == 0 && half == 0) {
             float* dst = part + ((((size_t)b * Hkv + g) * N + i) * KP + slot) * kKlPart;
             *reinterpret_cast<float4*>(dst) = make_float4(a.A, a.Bs, a.P, a.mu);
             dst[4] = a.lu;
         }
+        e_cur = e_nxt;
     }
 }
 
