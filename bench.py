@@ -33,6 +33,7 @@ from synth import CONFIGS, make_inputs, sample_rows  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and MFMA)
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CSRC = os.path.join(ROOT, "block_sparse_gqa_index_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_n128k.json")
@@ -153,6 +154,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kl", action="store_true",
                     help="also time the KL-alignment forward (msa_kl_align_fwd) on the step's outputs")
+    ap.add_argument("--index-fp8", action="store_true",
+                    help="also time the step with the selection on fp8 e4m3 copies of the index inputs "
+                         "(reported beside the bf16 headline, never as it)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -188,13 +192,13 @@ def main():
     index_kernel = ("index_topk_pipe_kernel" if w.dtype == "bf16" and (w.block_size * Hkv) % 512 == 0
                     else "index_topk_kernel")
 
-    def step(ev):
+    def step(ev, q_idx=x["q_idx"], k_idx=x["k_idx"], bi=block_idx):
         """One step; ev[0..4] bracket the selection and the three attention stages."""
         ev[0].record(stream)
-        msa.index_topk(x["q_idx"], x["k_idx"], w.topk, block_idx=block_idx)
+        msa.index_topk(q_idx, k_idx, w.topk, block_idx=bi)
         ev[1].record(stream)
         for s, e in ((msa.STAGE_PREPARE, ev[2]), (msa.STAGE_NONLOCAL, ev[3]), (msa.STAGE_COMBINE, ev[4])):
-            msa.sparse_attn_fwd(x["q"], x["k"], x["v"], block_idx, o=o, lse=lse, workspace=ws, stages=s)
+            msa.sparse_attn_fwd(x["q"], x["k"], x["v"], bi, o=o, lse=lse, workspace=ws, stages=s)
             e.record(stream)
 
     def events():
@@ -271,6 +275,30 @@ def main():
         "roofline": rooflines[dominant],
         "rooflines": rooflines,
     }
+    if args.index_fp8:
+        # Same workload with the index inputs held as fp8 e4m3 (their integer
+        # values are exact in it, so the selection must not change).
+        log("[bench] step with the fp8 selection")
+        fp8 = torch.float8_e4m3fn
+        qi8, ki8 = x["q_idx"].to(fp8), x["k_idx"].to(fp8)
+        bi8 = torch.empty_like(block_idx)
+        for _ in range(args.warmup):
+            step(events(), qi8, ki8, bi8)
+        evs8 = [events() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for ev in evs8:
+            step(ev, qi8, ki8, bi8)
+        torch.cuda.synchronize()
+        ms8 = (time.perf_counter() - t0) * 1e3 / args.steps
+        idx8 = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs8]))
+        a8 = f_idx / (idx8 * 1e-3) / 1e12
+        out["index_fp8"] = {
+            "kernel": index_kernel, "dtype": "fp8 e4m3 index inputs, fp32 accumulation", "ms": idx8,
+            "achieved": a8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": a8 / PEAK_FP8_TFLOPS,
+            "speedup_vs_bf16_index": stage_ms[index_kernel] / idx8,
+            "ms_per_step": ms8, "tokens_per_s": tokens / (ms8 * 1e-3),
+            "same_selection": bool(torch.equal(bi8, block_idx))}
     if args.kl:
         log("[bench] KL-alignment forward")
         kws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_KL)), dtype=torch.uint8, device=dev)

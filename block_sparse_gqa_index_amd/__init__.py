@@ -23,7 +23,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
-MSA_BF16, MSA_F32 = 0, 1
+MSA_BF16, MSA_F32, MSA_FP8_E4M3 = 0, 1, 2
 MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD = 0, 1, 2, 3
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
@@ -88,7 +88,8 @@ def _check(status):
 def make_dims(batch, seqlen, kv_heads, group_size, head_dim, index_dim, topk, dtype,
               block_size=128, causal=1) -> MsaDims:
     if isinstance(dtype, torch.dtype):
-        dtype = {torch.bfloat16: MSA_BF16, torch.float32: MSA_F32}.get(dtype, -1)
+        dtype = {torch.bfloat16: MSA_BF16, torch.float32: MSA_F32,
+                 torch.float8_e4m3fn: MSA_FP8_E4M3}.get(dtype, -1)
     return MsaDims(batch, seqlen, kv_heads, group_size, head_dim, index_dim, block_size, topk,
                    dtype, causal)
 
@@ -127,7 +128,8 @@ def _req(t, name, dtype=None, ndim=None):
 
 
 def index_topk(q_idx, k_idx, topk, block_idx=None, block_size=128):
-    """Block selection. q_idx [B,N,Hkv,Di], k_idx [B,N,Di] -> int32 [B,Hkv,N,topk]."""
+    """Block selection. q_idx [B,N,Hkv,Di], k_idx [B,N,Di] (bf16, fp32 or
+    float8_e4m3fn) -> int32 [B,Hkv,N,topk]."""
     lib = load_library()
     _req(q_idx, "q_idx", ndim=4)
     _req(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)

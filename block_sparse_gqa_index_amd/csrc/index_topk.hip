@@ -35,6 +35,37 @@
 
 namespace msa {
 
+// Matrix-core contraction step of the index scores per element type: one
+// 32 x 32 S^T tile accumulates KD-deep slices; an operand holds the KD/2
+// consecutive contraction elements of one row (A) or column (B) that a lane
+// supplies (lane l: row/column l % 32, elements (KD/2)*(l/32) .. + KD/2 - 1).
+template <typename T> struct IdxMma;
+template <> struct IdxMma<bf16_t> {   // v_mfma_f32_32x32x16_bf16
+    using Op = Op8<bf16_t>;
+    static constexpr int KD = 16;
+    static __device__ __forceinline__ void mma(floatx16& acc, const Op& a, const Op& b) { mma16(acc, a, b); }
+};
+template <> struct IdxMma<float> {    // 8 x v_mfma_f32_32x32x2_f32 over the same 16-deep slice
+    using Op = Op8<float>;
+    static constexpr int KD = 16;
+    static __device__ __forceinline__ void mma(floatx16& acc, const Op& a, const Op& b) { mma16(acc, a, b); }
+};
+template <> struct IdxMma<fp8_t> {    // v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 x e4m3, unit scales
+    struct Op {
+        i32x8 v;
+        __device__ __forceinline__ void load(const void* p) {
+            const uint4 lo = reinterpret_cast<const uint4*>(p)[0], hi = reinterpret_cast<const uint4*>(p)[1];
+            v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        __device__ __forceinline__ void zero() { v = i32x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    };
+    static constexpr int KD = 64;
+    static __device__ __forceinline__ void mma(floatx16& acc, const Op& a, const Op& b) {
+        // format codes 0 (fp8 e4m3) for both operands; scale exponents 127 = 2^0
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, acc, 0, 0, 0, 127, 0, 127);
+    }
+};
+
 // Inserts (x, j) into the descending list; a no-op when x does not beat the
 // last entry (then no comparison below succeeds), so it runs without a branch
 // and can be scheduled under the matrix-core work of the next key block.
@@ -76,7 +107,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     constexpr int NTHR = 64 * WAVES;
     constexpr int ES = sizeof(T);
     constexpr int ROWB = DI * ES + 16;        // padded LDS row, bytes
-    constexpr int KS = DI / 16;               // 16-deep slices of the contraction
+    using MM = IdxMma<T>;
+    constexpr int KD = MM::KD;
+    constexpr int KS = DI / KD;               // KD-deep slices of the contraction
     constexpr int CPR = DI * ES / 16;         // 16-byte chunks per key row
     constexpr int CPT = kBlock * CPR / NTHR;  // chunks per thread per key block
     constexpr int NO = NT >= 2 ? NT / 2 : 1;  // rows each lane keeps a top-k list for
@@ -94,15 +127,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     const size_t qrow0 = ((size_t)b * N + (size_t)qb * kBlock) * Hkv;
 
     // Index queries of this wave's rows: B operand, resident for the whole kernel.
-    Op8<T> bq[NT][KS];
+    typename MM::Op bq[NT][KS];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int R = r0 + 32 * t + col;
         const bool valid = qb * kBlock + R / Hkv < N;
-        const T* src = q_idx + (qrow0 + R) * DI + 8 * half;
+        const T* src = q_idx + (qrow0 + R) * DI + (KD / 2) * half;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (valid) bq[t][s].load(src + 16 * s);
+            if (valid) bq[t][s].load(src + KD * s);
             else bq[t][s].zero();
         }
     }
@@ -172,13 +205,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
                 for (int kt = 0; kt < kBlock / 32; ++kt) {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
-                    const unsigned char* arow = &lds[cur][bb][(kt * 32 + col) * ROWB + 8 * half * ES];
+                    const unsigned char* arow = &lds[cur][bb][(kt * 32 + col) * ROWB + (KD / 2) * half * ES];
 #pragma unroll
                     for (int s = 0; s < KS; ++s) {
-                        Op8<T> a;
-                        a.load(arow + 16 * s * ES);
+                        typename MM::Op a;
+                        a.load(arow + KD * s * ES);
 #pragma unroll
-                        for (int t = 0; t < NT; ++t) mma16(acc[kt & 1][t], a, bq[t][s]);
+                        for (int t = 0; t < NT; ++t) MM::mma(acc[kt & 1][t], a, bq[t][s]);
                     }
                     if (kt == 0) {
                         if (j > 0) {
@@ -257,12 +290,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     constexpr int ES = sizeof(T);
     constexpr int ROWB = DI * ES + 16;        // padded LDS row, bytes
     constexpr int BUF = kBlock * ROWB;        // one stage
-    constexpr int KS = DI / 16;               // 16-deep slices of the contraction
+    using MM = IdxMma<T>;
+    constexpr int KD = MM::KD;
+    constexpr int KS = DI / KD;               // KD-deep slices of the contraction
     constexpr int CPR = DI * ES / 16;         // 16-byte chunks per key row
     constexpr int CPT = kBlock * CPR / NTHR;  // chunks per thread per key block
     constexpr int NO = NT >= 2 ? NT / 2 : 1;  // rows each lane keeps a top-k list for
     constexpr int NOPS = (kBlock / 32) * KS;  // A operands per key block
-    constexpr int RING = 8, PF = 6;           // operand registers; requests ahead of use
+    constexpr int RING = NOPS < 8 ? NOPS : 8, PF = RING - 2;   // operand registers; requests ahead of use
     static_assert(CPT * NTHR == kBlock * CPR, "staging must tile the block");
     static_assert(NOPS % RING == 0 && PF < RING, "operand ring must tile the block");
     static_assert(NT % 2 == 0, "lanes of both half-waves own rows");
@@ -277,15 +312,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     const int r0 = c * (32 * NT * WAVES) + w * (32 * NT);
     const size_t qrow0 = ((size_t)b * N + (size_t)qb * kBlock) * Hkv;
 
-    Op8<T> bq[NT][KS];
+    typename MM::Op bq[NT][KS];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int R = r0 + 32 * t + col;
         const bool valid = qb * kBlock + R / Hkv < N;
-        const T* src = q_idx + (qrow0 + R) * DI + 8 * half;
+        const T* src = q_idx + (qrow0 + R) * DI + (KD / 2) * half;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (valid) bq[t][s].load(src + 16 * s);
+            if (valid) bq[t][s].load(src + KD * s);
             else bq[t][s].zero();
         }
     }
@@ -306,9 +341,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     // Stage offsets of this thread's chunks (global: linear; LDS: padded rows).
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
     const size_t kblock_bytes = (size_t)kBlock * DI * ES;
-    const unsigned char* opbase = lds + col * ROWB + 8 * half * ES;   // + stage + operand offset
+    const unsigned char* opbase = lds + col * ROWB + (KD / 2) * half * ES;   // + stage + operand offset
     u32x4 stage[CPT];
-    Op8<T> a[RING];
+    typename MM::Op a[RING];
     if (qb > 0) {   // a row of query block 0 has no candidate block
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
@@ -328,7 +363,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     __syncthreads();
     if (qb > 0) {
 #pragma unroll
-        for (int m = 0; m < PF; ++m) a[m].load(opbase + ((m / KS) * 32) * ROWB + 16 * (m % KS) * ES);
+        for (int m = 0; m < PF; ++m) a[m].load(opbase + ((m / KS) * 32) * ROWB + KD * (m % KS) * ES);
     }
 
     float bm[NT], bm_prev[NT];
@@ -347,14 +382,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
         for (int n = 0; n < NOPS; ++n) {
             const int kt = n / KS, s = n % KS;
             const int m = n + PF;
-            if (m < NOPS) a[m % RING].load(opbase + sb * BUF + ((m / KS) * 32) * ROWB + 16 * (m % KS) * ES);
-            else a[m % RING].load(opbase + nb1 * BUF + (((m - NOPS) / KS) * 32) * ROWB + 16 * ((m - NOPS) % KS) * ES);
+            if (m < NOPS) a[m % RING].load(opbase + sb * BUF + ((m / KS) * 32) * ROWB + KD * (m % KS) * ES);
+            else a[m % RING].load(opbase + nb1 * BUF + (((m - NOPS) / KS) * 32) * ROWB + KD * ((m - NOPS) % KS) * ES);
             if (s == 0) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
             }
 #pragma unroll
-            for (int t = 0; t < NT; ++t) mma16(acc[kt & 1][t], a[n % RING], bq[t][s]);
+            for (int t = 0; t < NT; ++t) MM::mma(acc[kt & 1][t], a[n % RING], bq[t][s]);
             if (s == KS - 1) {
                 if (kt == 0) {
                     // block j-1: last tile's max, then its candidate
@@ -466,9 +501,9 @@ static hipError_t launch_pipe(const LaunchDims& d, int qb_lo, int qb_cnt, const 
 template <typename T, int DI>
 static hipError_t launch_di(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                             int32_t* out, hipStream_t st) {
-    constexpr int NT = sizeof(T) == 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
+    constexpr int NT = sizeof(T) <= 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
     const int rows = kBlock * d.Hkv;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) <= 2) {
         if (rows % (32 * 2 * 8) == 0) return launch_pipe<T, DI>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
     }
     if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
@@ -482,6 +517,10 @@ hipError_t launch_index_topk(const LaunchDims& d, int qb_lo, int qb_hi, const vo
     if (d.dtype == 0) {
         return d.Di == 128 ? launch_di<bf16_t, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
                            : launch_di<bf16_t, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);
+    }
+    if (d.dtype == 2) {
+        return d.Di == 128 ? launch_di<fp8_t, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
+                           : launch_di<fp8_t, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);
     }
     return d.Di == 128 ? launch_di<float, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
                        : launch_di<float, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);

@@ -27,7 +27,9 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || d->topk < 1 ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
-    if (d->block_size != 128 || d->topk > 32 || (d->dtype != MSA_BF16 && d->dtype != MSA_F32) ||
+    const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout;   // fp8 index inputs: selection only
+    if (d->block_size != 128 || d->topk > 32 ||
+        (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3)) ||
         d->causal != 1 || (uses_heads && (!pow2_upto32(d->group_size) || (d->head_dim != 64 && d->head_dim != 128))) ||
         (uses_index && d->index_dim != 64 && d->index_dim != 128))
         return MSA_ERR_UNSUPPORTED;
@@ -65,7 +67,8 @@ const char* msa_strerror(int status) {
         case MSA_ERR_NULL: return "a required pointer is NULL";
         case MSA_ERR_SHAPE: return "invalid or too large problem sizes";
         case MSA_ERR_UNSUPPORTED: return "unsupported sizes or dtype (block_size 128, topk 1..32, group_size "
-                                         "power of two <= 32, head/index dim 64 or 128, bf16/fp32, causal)";
+                                         "power of two <= 32, head/index dim 64 or 128, bf16/fp32 (fp8 e4m3 "
+                                         "for the selection only), causal)";
         case MSA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case MSA_ERR_WORKSPACE: return "workspace missing or smaller than msa_workspace_bytes";
         case MSA_ERR_HIP: return "HIP kernel launch failed";

@@ -17,10 +17,12 @@
 namespace msa {
 
 typedef uint16_t bf16_t;
+typedef uint8_t fp8_t;   // OCP fp8 e4m3 bits (the variant without infinities)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBlock = 128;   // Bk: tokens per key block
 constexpr int kWave = 64;

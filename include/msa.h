@@ -47,7 +47,11 @@ extern "C" {
 #endif
 
 /* Element type of every floating-point input (and of O). */
-enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1 };
+/* Element type of the tensors. MSA_FP8_E4M3 (OCP fp8 e4m3, the variant with no
+ * infinities, |x| <= 448) is accepted by msa_index_topk and msa_check_block_idx
+ * only: q_idx and k_idx in fp8 on the fp8 matrix cores, scores accumulated in
+ * fp32 (exact, and the selection bit-exact, for integer-valued inputs). */
+enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
 
 /* Selector for msa_workspace_bytes. */
 enum msa_op { MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3 };
@@ -66,7 +70,8 @@ enum msa_status {
  * Problem sizes. Supported: batch >= 0, seqlen >= 0 (any value; the last block
  * may be partial), kv_heads >= 1, group_size in {1,2,4,8,16,32}, head_dim and
  * index_dim in {64,128}, block_size == 128, topk in [1,32], dtype MSA_BF16 or
- * MSA_F32, causal == 1. batch == 0 or seqlen == 0 is a valid empty problem.
+ * MSA_F32 (MSA_FP8_E4M3 for the selection only), causal == 1. batch == 0 or
+ * seqlen == 0 is a valid empty problem.
  */
 typedef struct msa_dims {
     int64_t batch;
@@ -91,7 +96,7 @@ typedef struct msa_dims {
  *
  *   Uses batch, seqlen, kv_heads, index_dim, block_size, topk, dtype and
  *   causal of `dims` (group_size and head_dim are not read).
- *   q_idx     [B, N, Hkv, Di]  index queries, dtype
+ *   q_idx     [B, N, Hkv, Di]  index queries, dtype (bf16, fp32 or fp8 e4m3)
  *   k_idx     [B, N, Di]       shared index keys, dtype
  *   block_idx [B, Hkv, N, k]   int32 OUTPUT. For query i (local block L = i/Bk)
  *             and group g: the block ids j < L with the k-1 largest

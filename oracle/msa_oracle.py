@@ -51,14 +51,15 @@ __all__ = [
 
 
 def _arr(x):
-    """Tensor or array -> numpy array without a copy where possible (bf16 tensors
-    widen exactly to float32; everything is cast to float64 where it is used)."""
+    """Tensor or array -> numpy array without a copy where possible (bf16, fp16
+    and fp8 tensors widen exactly to float32; everything is cast to float64
+    where it is used)."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
             x = x.detach().to("cpu")
-            if x.dtype == torch.bfloat16 or x.dtype == torch.float16:
-                x = x.float()
+            if x.dtype.is_floating_point and x.element_size() < 4:
+                x = x.float()   # bf16, fp16 and fp8 widen exactly to float32
             return x.numpy()
     except ImportError:  # pragma: no cover
         pass

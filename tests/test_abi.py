@@ -94,6 +94,16 @@ def test_attention_rejects_bad_dims(lib, kw, status):
     assert _attn(lib, _dims(**kw)) == status
 
 
+def test_fp8_is_for_the_selection_only(lib):
+    d = _dims(dtype=msa.MSA_FP8_E4M3)
+    assert _index(lib, d, out=None) == 1          # accepted: goes on to the pointer checks
+    assert _attn(lib, d) == 3
+    assert _kl(lib, d) == 3
+    p = [FAKE] * 5
+    assert lib.msa_forward(ctypes.byref(d), *p, 0.0, FAKE, FAKE, FAKE, None, 0, None) == 3
+    assert lib.msa_check_block_idx(ctypes.byref(d), FAKE, None, None) == 1
+
+
 def test_index_ignores_attention_fields(lib):
     # group_size/head_dim are not read by the selection: the call goes on to
     # the pointer checks (NULL output -> MSA_ERR_NULL, not UNSUPPORTED)

@@ -80,6 +80,25 @@ def test_selection_matches_brute_force(seed, N, Bk, k, Di, Hkv):
             assert got[0, g, i].tolist() == want, (g, i)
 
 
+def test_fp8_inputs_are_decoded_exactly():
+    """OCP fp8 e4m3 (no infinities, bias 7): 0x38 = 1, 0xB8 = -1, 0x7E = 448
+    (largest finite: exponent 15, mantissa 6/8), 0x08 = 2^-6 (smallest normal),
+    0x01 = 2^-9 (smallest subnormal), 0x54 = 12 (2^3 * 1.5), 0x7F = NaN."""
+    bits = torch.tensor([0x38, 0xB8, 0x7E, 0x08, 0x01, 0x54, 0x7F], dtype=torch.uint8)
+    got = O._arr(bits.view(torch.float8_e4m3fn)).astype(np.float64)
+    want = [1.0, -1.0, 448.0, 2.0 ** -6, 2.0 ** -9, 12.0]
+    assert got[:6].tolist() == want and np.isnan(got[6])
+    # and the selection over fp8 tensors is the brute-force one
+    rng = np.random.default_rng(5)
+    N, Bk, k, Di = 30, 4, 4, 3
+    q8 = torch.as_tensor(rng.integers(-7, 8, size=(1, N, 1, Di)), dtype=torch.float32).to(torch.float8_e4m3fn)
+    k8 = torch.as_tensor(rng.integers(-7, 8, size=(1, N, Di)), dtype=torch.float32).to(torch.float8_e4m3fn)
+    got = O.index_topk(q8, k8, Bk, k)
+    qf, kf = q8.float().numpy(), k8.float().numpy()
+    for i in range(N):
+        assert got[0, 0, i].tolist() == _brute_force_row(qf[0, i, 0], kf[0], i, Bk, k), i
+
+
 def test_selection_invariants_tiny_workload():
     from synth import get_workload, make_inputs
     w = get_workload("tiny")
