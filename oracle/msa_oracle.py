@@ -1,4 +1,5 @@
-"""Plain CPU oracle of the MSA (MiniMax Sparse Attention) forward path.
+"""Plain CPU oracle of the MSA (MiniMax Sparse Attention) forward path and of
+the main branch's backward over the cached block indices.
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this module. The product path (the HIP
@@ -35,6 +36,9 @@ Readings of points the pages leave open (each listed in the design notes):
   * KL is KL(teacher || student) summed over the row's selected tokens, with
     the teacher the group-mean of the G heads' main-branch probabilities and the
     student the softmax of index_scale * index score over the same tokens.
+  * the backward differentiates the main-branch forward above for the loss
+    <dO, O> (dO given); every key's gradient sums the contributions of all rows
+    that selected its block.
 
 Parity: every function here is pinned by tests that do not re-use its code
 (brute force, closed forms, torch's dense SDPA, scipy's entropy, invariants).
@@ -46,7 +50,7 @@ import numpy as np
 __all__ = [
     "local_block", "visible_block_scores", "select_blocks", "index_topk_rows",
     "index_topk", "token_set", "token_count", "attention_rows", "sparse_attention",
-    "kl_rows", "kl_align", "map_positions",
+    "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "map_positions",
 ]
 
 
@@ -248,6 +252,85 @@ def sparse_attention(q, k, v, block_idx, Bk, scale=None):
     rows = bi.transpose(0, 2, 1, 3).reshape(B * N, bi.shape[1], bi.shape[3])
     O, LSE = attention_rows(q, k, v, rows, pos, Bk, scale)
     return O.reshape(B, N, Hq, D), LSE.reshape(B, N, Hq).transpose(0, 2, 1).copy()
+
+
+def _row_backward(qh, kt, vt, doh, scale):
+    """Gradients of L = sum_h <dO_h, O_h> for one (position, group) row set.
+
+    qh/doh [G, D] (the group's query heads and their output gradients), kt/vt
+    [|T|, D] (keys and values of the row's selected tokens). Chain rule through
+    O_h = sum_t P_ht v_t, P_h = softmax_t(z_h), z_ht = scale <q_h, k_t>:
+      dV_t = sum_h P_ht dO_h,  dP_ht = <dO_h, v_t>,
+      dz_ht = P_ht (dP_ht - sum_u P_hu dP_hu)   (softmax Jacobian),
+      dQ_h = scale sum_t dz_ht k_t,  dK_t = scale sum_h dz_ht q_h.
+    Returns (dQ [G, D], dK [|T|, D], dV [|T|, D])."""
+    z = scale * (qh @ kt.T)                      # [G, |T|]
+    _, p = _softmax_stats(z)
+    dv = p.T @ doh
+    dp = doh @ vt.T
+    dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (dz @ kt), scale * (dz.T @ qh), dv
+
+
+def attention_backward(q, k, v, do, block_idx, Bk, scale=None):
+    """Gradients of the main branch for every position: (dQ [B,N,Hq,D],
+    dK [B,N,Hkv,D], dV [B,N,Hkv,D]) in float64, for the loss <dO, O>.
+
+    [P1] paragraph on the backward: with the block indices cached by the
+    forward, the backward runs over the same sparse blocks (linear in N). The
+    function differentiated is the forward of ``attention_rows``; a key's
+    gradient sums the contributions of every row that selected its block.
+    """
+    qq, kk, vv, dd = _arr(q), _arr(k), _arr(v), _arr(do)
+    B, N, Hq, D = qq.shape
+    Hkv = kk.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    bi = np.asarray(block_idx)
+    dQ = np.zeros((B, N, Hq, D))
+    dK = np.zeros((B, N, Hkv, D))
+    dV = np.zeros((B, N, Hkv, D))
+    for b in range(B):
+        for g in range(Hkv):
+            kg = np.asarray(kk[b, :, g], dtype=np.float64)
+            vg = np.asarray(vv[b, :, g], dtype=np.float64)
+            for i in range(N):
+                T = token_set(bi[b, g, i], i, Bk)
+                hs = slice(g * G, (g + 1) * G)
+                dq, dk, dv = _row_backward(np.asarray(qq[b, i, hs], dtype=np.float64), kg[T], vg[T],
+                                           np.asarray(dd[b, i, hs], dtype=np.float64), scale)
+                dQ[b, i, hs] = dq
+                dK[b, T, g] += dk          # T holds distinct tokens
+                dV[b, T, g] += dv
+    return dQ, dK, dV
+
+
+def attention_dq_rows(q, k, v, do, block_idx_rows, positions, Bk, scale=None, q_rows=None, do_rows=None):
+    """dQ at the given (b, i) positions only ([M, Hq, D], float64): a row's dQ
+    depends on its own selection alone, so large workloads are checked on
+    sampled rows. Arguments as in ``attention_rows``; ``do_rows`` [M, Hq, D]
+    may replace do by its rows at the positions."""
+    kk, vv = _arr(k), _arr(v)
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    if q_rows is None:
+        q_rows = _arr(q)[positions[:, 0], positions[:, 1]]
+    if do_rows is None:
+        do_rows = _arr(do)[positions[:, 0], positions[:, 1]]
+    q_rows, do_rows = _arr(q_rows), _arr(do_rows)
+    Hq, D = q_rows.shape[1], q_rows.shape[2]
+    Hkv = kk.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    out = np.zeros((len(positions), Hq, D))
+    for r, (b, i) in enumerate(positions):
+        for g in range(Hkv):
+            T = token_set(block_idx_rows[r, g], int(i), Bk)
+            hs = slice(g * G, (g + 1) * G)
+            out[r, hs] = _row_backward(np.asarray(q_rows[r, hs], dtype=np.float64),
+                                       np.asarray(kk[b, T, g], dtype=np.float64),
+                                       np.asarray(vv[b, T, g], dtype=np.float64),
+                                       np.asarray(do_rows[r, hs], dtype=np.float64), scale)[0]
+    return out
 
 
 def kl_rows(q, k, q_idx, k_idx, block_idx_rows, positions, Bk, scale=None,

@@ -347,3 +347,136 @@ def test_planted_mistakes_are_caught(monkeypatch):
                             [[O._pad(real_select(mean_pool(qi[b, i, g], ki[b], i, Bk), i // Bk, k), k)
                               for g in range(qi.shape[2])] for b, i in pos], dtype=np.int32))
     assert not selection_ok()
+
+
+# ----------------------------------------------------------------- backward --
+
+def _masked_dense_grads(q, kk, vv, do, bi, Bk, scale):
+    """Gradients by torch autograd (float64) of dense attention whose logits are
+    masked to each row's selected tokens: an independent derivation of the
+    backward formulas."""
+    B, N, Hq, D = q.shape
+    Hkv = kk.shape[2]
+    G = Hq // Hkv
+    mask = torch.zeros(B, Hq, N, N, dtype=torch.bool)
+    for b in range(B):
+        for g in range(Hkv):
+            for i in range(N):
+                mask[b, g * G:(g + 1) * G, i, O.token_set(bi[b, g, i], i, Bk)] = True
+    qt = torch.tensor(q).permute(0, 2, 1, 3).requires_grad_()
+    kt = torch.tensor(kk).permute(0, 2, 1, 3).requires_grad_()
+    vt = torch.tensor(vv).permute(0, 2, 1, 3).requires_grad_()
+    ke = kt.repeat_interleave(G, dim=1)
+    ve = vt.repeat_interleave(G, dim=1)
+    logits = (scale * (qt @ ke.transpose(-1, -2))).masked_fill(~mask, float("-inf"))
+    out = torch.softmax(logits, dim=-1) @ ve
+    (out * torch.tensor(do).permute(0, 2, 1, 3)).sum().backward()
+    return (qt.grad.permute(0, 2, 1, 3).numpy(), kt.grad.permute(0, 2, 1, 3).numpy(),
+            vt.grad.permute(0, 2, 1, 3).numpy())
+
+
+@pytest.mark.parametrize("seed,N,Bk,k,G", [(0, 64, 8, 3, 2), (1, 61, 8, 4, 1), (2, 40, 4, 16, 3)])
+def test_backward_matches_autograd(seed, N, Bk, k, G):
+    Hkv, D = 2, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(seed, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    do = np.random.default_rng(seed + 100).standard_normal(q.shape)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    scale = 0.3
+    got = O.attention_backward(q, kk, vv, do, bi, Bk, scale)
+    want = _masked_dense_grads(q, kk, vv, do, bi, Bk, scale)
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, atol=1e-12, rtol=0)
+    pos = np.array([(0, i) for i in range(0, N, 5)])
+    rows = bi.transpose(0, 2, 1, 3)[0, pos[:, 1]]
+    np.testing.assert_allclose(O.attention_dq_rows(q, kk, vv, do, rows, pos, Bk, scale), got[0][0, pos[:, 1]],
+                               atol=1e-14, rtol=0)
+
+
+def test_backward_finite_differences():
+    """Directional derivative of <dO, O> (the pinned forward) by central
+    differences equals <dQ, a> + <dK, b> + <dV, c>."""
+    N, Bk, k, Hkv, G, D = 48, 8, 3, 2, 2, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(7, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    rng = np.random.default_rng(8)
+    do = rng.standard_normal(q.shape)
+    a, b, c = rng.standard_normal(q.shape), rng.standard_normal(kk.shape), rng.standard_normal(vv.shape)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    dq, dk, dv = O.attention_backward(q, kk, vv, do, bi, Bk)
+
+    def f(t):
+        o, _ = O.sparse_attention(q + t * a, kk + t * b, vv + t * c, bi, Bk)
+        return float((o * do).sum())
+
+    eps = 1e-5
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    an = float((dq * a).sum() + (dk * b).sum() + (dv * c).sum())
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+@pytest.mark.parametrize("N,Bk", [(64, 8), (50, 8)])
+def test_backward_warmup_matches_sdpa(N, Bk):
+    """k >= number of blocks: the gradients of dense causal GQA attention,
+    here torch's SDPA backward in float64."""
+    Hkv, G, D = 2, 2, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(9, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    do = np.random.default_rng(10).standard_normal(q.shape)
+    bi = O.index_topk(q_idx, k_idx, Bk, -(-N // Bk) + 1)
+    got = O.attention_backward(q, kk, vv, do, bi, Bk)
+    qt = torch.tensor(q).permute(0, 2, 1, 3).requires_grad_()
+    kt = torch.tensor(kk).permute(0, 2, 1, 3).requires_grad_()
+    vt = torch.tensor(vv).permute(0, 2, 1, 3).requires_grad_()
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, enable_gqa=True)
+    (out * torch.tensor(do).permute(0, 2, 1, 3)).sum().backward()
+    for a, t in zip(got, (qt, kt, vt)):
+        np.testing.assert_allclose(a, t.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
+
+
+def test_backward_invariants():
+    """Per group: the dV of all keys sums to the sum of the group's dO rows
+    (every row's probabilities sum to 1), and the dK of all keys sums to 0
+    (every row's logit gradients sum to 0)."""
+    N, Bk, k, Hkv, G, D = 80, 8, 4, 2, 3, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(11, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    do = np.random.default_rng(12).standard_normal(q.shape)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    _, dk, dv = O.attention_backward(q, kk, vv, do, bi, Bk)
+    for g in range(Hkv):
+        np.testing.assert_allclose(dv[0, :, g].sum(axis=0), do[0, :, g * G:(g + 1) * G].sum(axis=(0, 1)),
+                                   atol=1e-10)
+        np.testing.assert_allclose(dk[0, :, g].sum(axis=0), 0.0, atol=1e-10)
+
+
+def test_backward_planted_mistakes_are_caught(monkeypatch):
+    """A dropped softmax-Jacobian term, a transposed probability matrix or a
+    missing scale in the row gradients each fails the autograd pin."""
+    N, Bk, k, Hkv, G, D = 40, 8, 3, 1, 2, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(13, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    do = np.random.default_rng(14).standard_normal(q.shape)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    want = _masked_dense_grads(q, kk, vv, do, bi, Bk, 1 / math.sqrt(D))
+
+    def ok():
+        got = O.attention_backward(q, kk, vv, do, bi, Bk)
+        return all(np.allclose(a, b, atol=1e-9) for a, b in zip(got, want))
+
+    assert ok()
+    real = O._row_backward
+
+    def no_jacobian_term(qh, kt, vt, doh, scale):
+        _, p = O._softmax_stats(scale * (qh @ kt.T))
+        dz = p * (doh @ vt.T)
+        return scale * (dz @ kt), scale * (dz.T @ qh), p.T @ doh
+
+    def no_scale(qh, kt, vt, doh, scale):
+        dq, dk, dv = real(qh, kt, vt, doh, scale)
+        return dq / scale, dk / scale, dv
+
+    def transposed_dv(qh, kt, vt, doh, scale):
+        dq, dk, dv = real(qh, kt, vt, doh, scale)
+        _, p = O._softmax_stats(scale * (qh @ kt.T))
+        return dq, dk, (p.T[::-1] @ doh)
+
+    for bad in (no_jacobian_term, no_scale, transposed_dv):
+        monkeypatch.setattr(O, "_row_backward", bad)
+        assert not ok(), bad.__name__
+    monkeypatch.setattr(O, "_row_backward", real)
