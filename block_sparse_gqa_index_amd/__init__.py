@@ -1,4 +1,5 @@
-"""MSA (MiniMax Sparse Attention) forward hot path on AMD Instinct MI355X.
+"""MSA (MiniMax Sparse Attention) forward hot path (and the main branch's
+backward) on AMD Instinct MI355X.
 
 Thin ctypes binding over ``libmsa.so`` (the C ABI declared in include/msa.h).
 This module only marshals arguments: shapes and pointers of torch device
@@ -13,6 +14,7 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
       (stages=... enqueues only some of its three stages: msa_sparse_attn_fwd_stages)
   kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse) -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])
   forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse): selection, then attention
+  sparse_attn_bwd(q, k, v, block_idx, o, lse, dout) -> (dq, dk, dv), bf16
   workspace_bytes(dims, op)
 """
 import ctypes
@@ -24,12 +26,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_F32, MSA_FP8_E4M3 = 0, 1, 2
-MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD = 0, 1, 2, 3
+MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD = 0, 1, 2, 3, 4
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
 EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
-           "msa_forward", "msa_kl_align_fwd",
+           "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -68,6 +70,7 @@ def load_library(path: str = LIB_PATH):
     lib.msa_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                      vp, vp, vp, sz, vp]
     lib.msa_forward.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
     lib.msa_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_strerror.argtypes = [ctypes.c_int]
@@ -196,6 +199,40 @@ def sparse_attn_fwd(q, k, v, block_idx, softmax_scale=0.0, o=None, lse=None, wor
                                               float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), nws,
                                               int(stages), _stream(q.device)))
     return o, lse
+
+
+def sparse_attn_bwd(q, k, v, block_idx, o, lse, dout, softmax_scale=0.0, dq=None, dk=None, dv=None,
+                    workspace=None, block_size=128):
+    """Backward of sparse_attn_fwd for the loss <dout, o> (bf16): o and lse
+    from the forward of the same inputs -> (dq [B,N,Hq,D], dk, dv [B,N,Hkv,D])."""
+    lib = load_library()
+    _req(q, "q", ndim=4)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _req(t, name, dtype=q.dtype, ndim=4)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D) or Hq % Hkv:
+        raise ValueError("k/v must be [B, N, Hkv, D] with Hq a multiple of Hkv")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("o/dout must be [B, N, Hq, D] and lse [B, Hq, N]")
+    topk = block_idx.shape[3]
+    if tuple(block_idx.shape) != (B, Hkv, N, topk):
+        raise ValueError("block_idx must be [B, Hkv, N, topk]")
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, 64, topk, q.dtype, block_size)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _req(t, name, dtype=q.dtype, ndim=4)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have the shape of {name[1:]}")
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_ATTN_BWD), q.device, workspace)
+    _check(lib.msa_sparse_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(o),
+                                   _ptr(lse), _ptr(dout), float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(ws), nws, _stream(q.device)))
+    return dq, dk, dv
 
 
 def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_scale=0.0,

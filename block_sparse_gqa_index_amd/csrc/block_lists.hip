@@ -7,6 +7,8 @@
 #include "msa_common.h"
 #include "msa_internal.h"
 
+#include <algorithm>
+
 namespace msa {
 
 // ---------------------------------------------------------------- inversion --
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ item_offsets,
                                                     int32_t* __restrict__ cursor,
-                                                    int32_t* __restrict__ total_items, int n_keys) {
+                                                    int32_t* __restrict__ total_items, int n_keys, int seg) {
     __shared__ int64_t s_sum[1024];
     __shared__ int64_t s_items[1024];
     const int t = threadIdx.x;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     int64_t a = 0, it = 0;
     for (int x = lo; x < hi; ++x) {
         a += counts[x];
-        it += (counts[x] + kSeg - 1) / kSeg;
+        it += (counts[x] + seg - 1) / seg;
     }
     s_sum[t] = a;
     s_items[t] = it;
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
         item_offsets[x] = (int32_t)run_it;
         cursor[x] = 0;
         run += counts[x];
-        run_it += (counts[x] + kSeg - 1) / kSeg;
+        run_it += (counts[x] + seg - 1) / seg;
     }
     if (t == 1023) total_items[0] = (int32_t)s_items[1023];
 }
@@ -166,12 +168,94 @@ __global__ void scatter_kernel(const int32_t* __restrict__ block_idx, const int3
 
 // One thread per key: its work items (key, first list entry, entry count).
 __global__ void items_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-                             const int32_t* __restrict__ item_offsets, int4* __restrict__ items, int n_keys) {
+                             const int32_t* __restrict__ item_offsets, int4* __restrict__ items, int n_keys,
+                             int seg) {
     const int x = blockIdx.x * blockDim.x + threadIdx.x;
     if (x >= n_keys) return;
     const int c = counts[x];
     int at = item_offsets[x];
-    for (int u = 0; u * kSeg < c; ++u) items[at++] = make_int4(x, offsets[x] + u * kSeg, min(kSeg, c - u * kSeg), 0);
+    for (int u = 0; u * seg < c; ++u) items[at++] = make_int4(x, offsets[x] + u * seg, min(seg, c - u * seg), 0);
+}
+
+// ------------------------------------------------ position-sorted lists --
+
+// Sorted variant of the inversion, for kernels whose results depend on the
+// order in which they visit a key's rows (sums over rows): every (b, g,
+// window, j) key owns a bitmap over the window's positions; a row sets its bit
+// in the bitmap of each of its non-local blocks (atomic OR: the result does
+// not depend on the order), and the lists are read back from the bitmaps in
+// ascending position order. The work items, cut every `seg` entries, then hold
+// the same rows on every run.
+__global__ void mark_kernel(const int32_t* __restrict__ block_idx, uint32_t* __restrict__ bits, int64_t rows,
+                            int N, int k, int nb, int nwin, int wpk) {
+    const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (x >= rows) return;
+    const int i = (int)(x % N);
+    const int64_t bg = x / N;
+    const int L = i / kBlock;
+    const int32_t* row = block_idx + x * k;
+    for (int s = 0; s + 1 < k; ++s) {
+        const int j = row[s];
+        if (j >= 0 && j < L)
+            atomicOr(&bits[((bg * nwin + i / kWindow) * nb + j) * wpk + (i % kWindow) / 32], 1u << (i & 31));
+    }
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// One wave per key: counts[key] = set bits of its bitmap.
+__global__ __launch_bounds__(256) void count_bits_kernel(const uint32_t* __restrict__ bits,
+                                                         int32_t* __restrict__ counts, int n_keys, int wpk) {
+    const int key = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (key >= n_keys) return;
+    const uint32_t* bw = bits + (size_t)key * wpk;
+    int c = 0;
+    for (int w = lane; w < wpk; w += 64) c += __popc(bw[w]);
+    c = wave_sum(c);
+    if (lane == 0) counts[key] = c;
+}
+
+// One wave per key: the list entries (i << 5 | slot) of its set bits in
+// ascending position order, at the key's offset. The slot is where the row
+// keeps j (the row holds j: the bit came from it).
+__global__ __launch_bounds__(256) void compact_kernel(const uint32_t* __restrict__ bits,
+                                                      const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ block_idx,
+                                                      int32_t* __restrict__ list, int n_keys, int wpk, int N, int k,
+                                                      int nb, int nwin) {
+    const int key = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (key >= n_keys || counts[key] == 0) return;
+    const int j = key % nb;
+    const int win = (key / nb) % nwin;
+    const size_t bg = (size_t)key / ((size_t)nb * nwin);
+    const uint32_t* bw = bits + (size_t)key * wpk;
+    int at = offsets[key];
+    for (int w0 = 0; w0 < wpk; w0 += 64) {
+        uint32_t word = w0 + lane < wpk ? bw[w0 + lane] : 0u;
+        const int pc = __popc(word);
+        int incl = pc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        int pos = at + incl - pc;
+        while (word) {
+            const int bit = __ffs(word) - 1;
+            word &= word - 1;
+            const int i = win * kWindow + (w0 + lane) * 32 + bit;
+            const int32_t* row = block_idx + (bg * N + i) * k;
+            int slot = 0;
+            while (slot + 2 < k && row[slot] != j) ++slot;
+            list[pos++] = (i << 5) | slot;
+        }
+        at += __shfl(incl, 63);
+    }
 }
 
 
@@ -215,14 +299,22 @@ static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int windows(const LaunchDims& d) { return (d.N + kWindow - 1) / kWindow; }
 
-ListLayout list_layout(const LaunchDims& d, size_t base) {
+int bitmap_words_per_key(const LaunchDims& d) { return (min(d.N, kWindow) + 31) / 32; }
+
+ListLayout list_layout(const LaunchDims& d, size_t base, int seg, bool sorted) {
     ListLayout w{};
     const size_t n_keys = (size_t)d.B * d.Hkv * windows(d) * d.nb;
     const size_t kp = d.k > 1 ? (size_t)(d.k - 1) : 0;
     w.max_entries = (size_t)d.B * d.Hkv * d.N * kp;
     w.n_keys = n_keys;
-    w.max_items = (w.max_entries + kSeg - 1) / kSeg + n_keys;
+    w.seg = seg;
+    w.sorted = sorted;
+    w.max_items = (w.max_entries + seg - 1) / seg + n_keys;
     size_t off = align_up(base);
+    if (sorted) {
+        w.bits = off;
+        off = align_up(off + n_keys * bitmap_words_per_key(d) * 4);
+    }
     w.counts = off;        off = align_up(off + n_keys * 4);
     w.offsets = off;       off = align_up(off + n_keys * 4);
     w.item_offsets = off;  off = align_up(off + n_keys * 4);
@@ -248,6 +340,23 @@ void launch_build_lists(const LaunchDims& d, int p_lo, int p_hi, const int32_t* 
     const int nwin = windows(d);
     const int64_t rows = (int64_t)d.B * d.Hkv * p_len;
     const int nk = (int)L.n_keys;
+    if (L.sorted) {   // every position of the sequence (p_lo = 0, p_hi = N)
+        uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+        const int wpk = bitmap_words_per_key(d);
+        const size_t nw = L.n_keys * (size_t)wpk;
+        hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<size_t>((nw + 255) / 256, 65536)), dim3(256), 0, st,
+                           reinterpret_cast<int32_t*>(bits), nw, 0);
+        hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, bits, rows,
+                           d.N, d.k, d.nb, nwin, wpk);
+        hipLaunchKernelGGL(count_bits_kernel, dim3((nk + 3) / 4), dim3(256), 0, st, bits, counts, nk, wpk);
+        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, item_offsets, cursor, total, nk,
+                           L.seg);
+        hipLaunchKernelGGL(compact_kernel, dim3((nk + 3) / 4), dim3(256), 0, st, bits, counts, offsets, block_idx,
+                           list, nk, wpk, d.N, d.k, d.nb, nwin);
+        hipLaunchKernelGGL(items_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, offsets, item_offsets,
+                           items, nk, L.seg);
+        return;
+    }
     hipLaunchKernelGGL(fill_i32_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, (size_t)nk, 0);
     const bool hist = d.nb <= kHistMaxBins;
     const int chunks = (p_len + kHistPos - 1) / kHistPos;
@@ -259,7 +368,8 @@ void launch_build_lists(const LaunchDims& d, int p_lo, int p_hi, const int32_t* 
     else
         hipLaunchKernelGGL(count_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, counts,
                            rows, d.N, d.k, d.nb, nwin, p_lo, p_len);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, item_offsets, cursor, total, nk);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, item_offsets, cursor, total, nk,
+                       L.seg);
     if (hist)
         hipLaunchKernelGGL(scatter_hist_kernel, dim3(hist_grid), dim3(256), 2 * hist_lds, st, block_idx, offsets,
                            cursor, list, d.N, d.k, d.nb, nwin, chunks, p_lo, p_hi);
@@ -267,13 +377,13 @@ void launch_build_lists(const LaunchDims& d, int p_lo, int p_hi, const int32_t* 
         hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx,
                            offsets, cursor, list, rows, d.N, d.k, d.nb, nwin, p_lo, p_len);
     hipLaunchKernelGGL(items_kernel, dim3((nk + 255) / 256), dim3(256), 0, st, counts, offsets, item_offsets, items,
-                       nk);
+                       nk, L.seg);
 }
 
 size_t list_items_bound(const LaunchDims& d, int p_lo, int p_hi, const ListLayout& L) {
     const size_t kp = d.k > 1 ? (size_t)(d.k - 1) : 0;
     const size_t entries = (size_t)d.B * d.Hkv * (size_t)(p_hi - p_lo) * kp;
-    return (entries + kSeg - 1) / kSeg + L.n_keys;
+    return (entries + L.seg - 1) / L.seg + L.n_keys;
 }
 
 }  // namespace msa

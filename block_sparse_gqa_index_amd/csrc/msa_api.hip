@@ -1,6 +1,7 @@
-// C ABI of the MSA forward path: argument validation, workspace sizing and
-// dispatch to the kernels. Every check here runs on the host before any HIP
-// call, so a rejected call enqueues nothing and writes nothing.
+// C ABI of the MSA forward path and of the main branch's backward: argument
+// validation, workspace sizing and dispatch to the kernels. Every check here
+// runs on the host before any HIP call, so a rejected call enqueues nothing
+// and writes nothing.
 #include "../../include/msa.h"
 
 #include <limits.h>
@@ -23,13 +24,14 @@ constexpr int kOpLayout = -1;   // the block_idx layout check: neither heads nor
 int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (!d) return MSA_ERR_NULL;
     const bool uses_heads = op != MSA_OP_INDEX && op != kOpLayout;   // MSA_OP_FORWARD: both
-    const bool uses_index = op != MSA_OP_ATTN && op != kOpLayout;
+    const bool uses_index = op != MSA_OP_ATTN && op != MSA_OP_ATTN_BWD && op != kOpLayout;
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || d->topk < 1 ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
     const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout;   // fp8 index inputs: selection only
     if (d->block_size != 128 || d->topk > 32 ||
         (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3)) ||
+        (op == MSA_OP_ATTN_BWD && d->dtype != MSA_BF16) ||
         d->causal != 1 || (uses_heads && (!pow2_upto32(d->group_size) || (d->head_dim != 64 && d->head_dim != 128))) ||
         (uses_index && d->index_dim != 64 && d->index_dim != 128))
         return MSA_ERR_UNSUPPORTED;
@@ -68,7 +70,7 @@ const char* msa_strerror(int status) {
         case MSA_ERR_SHAPE: return "invalid or too large problem sizes";
         case MSA_ERR_UNSUPPORTED: return "unsupported sizes or dtype (block_size 128, topk 1..32, group_size "
                                          "power of two <= 32, head/index dim 64 or 128, bf16/fp32 (fp8 e4m3 "
-                                         "for the selection only), causal)";
+                                         "for the selection only, bf16 for the backward), causal)";
         case MSA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case MSA_ERR_WORKSPACE: return "workspace missing or smaller than msa_workspace_bytes";
         case MSA_ERR_HIP: return "HIP kernel launch failed";
@@ -78,12 +80,15 @@ const char* msa_strerror(int status) {
 
 size_t msa_workspace_bytes(const msa_dims* dims, int op) {
     LaunchDims L;
-    if (op != MSA_OP_INDEX && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_FORWARD) return 0;
+    if (op != MSA_OP_INDEX && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_FORWARD &&
+        op != MSA_OP_ATTN_BWD)
+        return 0;
     if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
     switch (op) {
         case MSA_OP_INDEX: return 0;
         case MSA_OP_ATTN:
         case MSA_OP_FORWARD: return msa::attn_workspace_layout(L).bytes;
+        case MSA_OP_ATTN_BWD: return msa::bwd_workspace_layout(L).bytes;
         case MSA_OP_KL: return msa::kl_workspace_layout(L).bytes;
         default: return 0;
     }
@@ -156,6 +161,24 @@ int msa_forward(const msa_dims* dims, const void* q_idx, const void* k_idx, cons
     if (msa::launch_index_topk(L, 0, L.nb, q_idx, k_idx, block_idx, s) != hipSuccess) return MSA_ERR_HIP;
     if (msa::launch_transpose_v(L, v, ws, s) != hipSuccess) return MSA_ERR_HIP;
     return hip_status(msa::launch_sparse_attn(L, 0, L.nb, q, k, block_idx, scale, o, lse, ws, MSA_STAGE_ALL, s));
+}
+
+int msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                        const int32_t* block_idx, const void* o, const float* lse, const void* dout,
+                        float softmax_scale, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_ATTN_BWD, &L);
+    if (st != MSA_OK) return st;
+    if (empty(L)) return MSA_OK;
+    if (!q || !k || !v || !block_idx || !o || !lse || !dout || !dq || !dk || !dv) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(o) ||
+        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return MSA_ERR_ALIGN;
+    const size_t need = msa::bwd_workspace_layout(L).bytes;
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    return hip_status(msa::launch_sparse_attn_bwd(L, q, k, v, block_idx, o, lse, dout, scale, dq, dk, dv, ws,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,

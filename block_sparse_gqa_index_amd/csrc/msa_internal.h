@@ -7,7 +7,8 @@
 
 namespace msa {
 
-constexpr int kSeg = 128;        // query positions per work item of the key-block-outer kernels
+constexpr int kSeg = 128;        // query positions per work item of the key-block-outer forward kernels
+constexpr int kSegBwd = 1024;    // query positions per work item of the backward kernel
 constexpr int kWindow = 65536;   // query positions per window of the inverted selection
 
 // Validated problem sizes (see msa.h for their meaning).
@@ -19,7 +20,9 @@ struct LaunchDims {
 // Byte offsets (from the workspace base) of the selection-inversion buffers.
 struct ListLayout {
     size_t n_keys, max_entries, max_items;
-    size_t counts, offsets, item_offsets, cursor, total, items, list, end;
+    size_t bits, counts, offsets, item_offsets, cursor, total, items, list, end;
+    int seg;             // list entries per work item
+    bool sorted;         // lists in ascending position order (built through per-key bitmaps)
     bool has_nonlocal;   // some row keeps a block other than its local one
 };
 
@@ -28,13 +31,19 @@ struct AttnWorkspace {
     size_t vt, po, plse, bytes;
 };
 
+struct BwdWorkspace {
+    ListLayout lists;   // position-sorted, kSegBwd entries per item
+    size_t kt, dl, dq_part, dkv_part, bytes;
+    size_t local_items, dkv_items;   // dK/dV partials: list items first, then one per (b, g, block)
+};
+
 struct KlWorkspace {
     ListLayout lists;
     size_t part, red, bytes;
     int red_blocks;
 };
 
-ListLayout list_layout(const LaunchDims& d, size_t base);
+ListLayout list_layout(const LaunchDims& d, size_t base, int seg = kSeg, bool sorted = false);
 int windows(const LaunchDims& d);   // kWindow-position windows of the sequence
 
 // Work item handled by work-group x of a key-block-outer launch (grid a
@@ -42,7 +51,8 @@ int windows(const LaunchDims& d);   // kWindow-position windows of the sequence
 // XCDs move through the item list (and its windows) together while each XCD's
 // consecutive items usually share a key block in its L2.
 __device__ __forceinline__ int item_of_workgroup(int x) { return (x & ~63) + ((x & 7) << 3) + ((x >> 3) & 7); }
-// Lists for the query positions [p_lo, p_hi) of every (batch, group).
+// Lists for the query positions [p_lo, p_hi) of every (batch, group) (sorted
+// layouts: the whole sequence only).
 void launch_build_lists(const LaunchDims& d, int p_lo, int p_hi, const int32_t* block_idx, unsigned char* ws,
                         const ListLayout& L, hipStream_t st);
 // Upper bound on the work items launch_build_lists produces for that range.
@@ -52,6 +62,7 @@ size_t list_items_bound(const LaunchDims& d, int p_lo, int p_hi, const ListLayou
 hipError_t launch_check_block_idx(const LaunchDims& d, const int32_t* block_idx, int32_t* bad, hipStream_t st);
 
 AttnWorkspace attn_workspace_layout(const LaunchDims& d);
+BwdWorkspace bwd_workspace_layout(const LaunchDims& d);
 KlWorkspace kl_workspace_layout(const LaunchDims& d);
 
 // Selection for the query blocks [qb_lo, qb_hi).
@@ -60,6 +71,9 @@ hipError_t launch_index_topk(const LaunchDims& d, int qb_lo, int qb_hi, const vo
 
 // V^T copy into the attention workspace (needed once per forward).
 hipError_t launch_transpose_v(const LaunchDims& d, const void* v, void* ws, hipStream_t st);
+// The same per-block transposed copy of any [B, N, Hkv, D] tensor into dst
+// [B, Hkv, nb, D, 128] (keys permuted within groups of 16, zeros past N).
+hipError_t launch_transpose_kv(const LaunchDims& d, const void* src, void* dst, hipStream_t st);
 
 // Attention for the query blocks [qb_lo, qb_hi); the V^T copy must be in ws.
 // `stages`: bit 0 builds the query lists, bit 1 runs the non-local blocks,
@@ -67,6 +81,11 @@ hipError_t launch_transpose_v(const LaunchDims& d, const void* v, void* ws, hipS
 hipError_t launch_sparse_attn(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
                               const int32_t* block_idx, float scale, void* o, float* lse, void* ws, int stages,
                               hipStream_t st);
+
+// Main-branch backward (bf16): dq [B,N,Hq,D], dk, dv [B,N,Hkv,D].
+hipError_t launch_sparse_attn_bwd(const LaunchDims& d, const void* q, const void* k, const void* v,
+                                  const int32_t* block_idx, const void* o, const float* lse, const void* dout,
+                                  float scale, void* dq, void* dk, void* dv, void* ws, hipStream_t st);
 
 hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
                            const void* k_idx, const int32_t* block_idx, const float* lse, float scale,

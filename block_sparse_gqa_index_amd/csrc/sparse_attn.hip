@@ -464,23 +464,25 @@ hipError_t launch_sparse_attn(const LaunchDims& d, int qb_lo, int qb_hi, const v
 }
 
 template <typename T, int D>
-static void transpose_v_t(const LaunchDims& d, const void* v, unsigned char* ws, hipStream_t st) {
-    const AttnWorkspace L = attn_workspace_layout(d);
+static void transpose_t(const LaunchDims& d, const void* src, void* dst, hipStream_t st) {
     hipLaunchKernelGGL((transpose_v_kernel<T, D>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st,
-                       static_cast<const T*>(v), reinterpret_cast<T*>(ws + L.vt), d.N, d.Hkv, d.nb);
+                       static_cast<const T*>(src), static_cast<T*>(dst), d.N, d.Hkv, d.nb);
+}
+
+hipError_t launch_transpose_kv(const LaunchDims& d, const void* src, void* dst, hipStream_t st) {
+    if (d.B == 0 || d.N == 0) return hipSuccess;
+    if (d.dtype == 0) {
+        if (d.D == 128) transpose_t<bf16_t, 128>(d, src, dst, st);
+        else transpose_t<bf16_t, 64>(d, src, dst, st);
+    } else {
+        if (d.D == 128) transpose_t<float, 128>(d, src, dst, st);
+        else transpose_t<float, 64>(d, src, dst, st);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose_v(const LaunchDims& d, const void* v, void* ws, hipStream_t st) {
-    if (d.B == 0 || d.N == 0) return hipSuccess;
-    unsigned char* w = static_cast<unsigned char*>(ws);
-    if (d.dtype == 0) {
-        if (d.D == 128) transpose_v_t<bf16_t, 128>(d, v, w, st);
-        else transpose_v_t<bf16_t, 64>(d, v, w, st);
-    } else {
-        if (d.D == 128) transpose_v_t<float, 128>(d, v, w, st);
-        else transpose_v_t<float, 64>(d, v, w, st);
-    }
-    return hipGetLastError();
+    return launch_transpose_kv(d, v, static_cast<unsigned char*>(ws) + attn_workspace_layout(d).vt, st);
 }
 
 }  // namespace msa

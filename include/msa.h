@@ -26,7 +26,8 @@
  *    failed launch (the outputs are then unspecified).
  *  - Calls are thread-safe; calls that share a workspace must not overlap.
  *  - Results are deterministic: the same inputs give bitwise the same block
- *    indices, O, LSE and kl_rows (kl_sum too: it is reduced in a fixed order).
+ *    indices, O, LSE, kl_rows (kl_sum too: it is reduced in a fixed order)
+ *    and gradients.
  */
 #ifndef MSA_H
 #define MSA_H
@@ -54,7 +55,7 @@ extern "C" {
 enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
 
 /* Selector for msa_workspace_bytes. */
-enum msa_op { MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3 };
+enum msa_op { MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4 };
 
 enum msa_status {
     MSA_OK = 0,
@@ -177,6 +178,37 @@ MSA_API int msa_sparse_attn_fwd_stages(const msa_dims* dims, const void* q, cons
 MSA_API int msa_forward(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q,
                         const void* k, const void* v, float softmax_scale, int32_t* block_idx,
                         void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Main branch: backward of msa_sparse_attn_fwd over the cached block indices.
+ * Defined by the Flash-MSA article (tech.kuratif.com), paragraph on the
+ * backward: with the block indices kept from the forward, the backward visits
+ * only the selected blocks (linear in N) and uses the forward's LSE; the
+ * function differentiated is the forward above (MSA article, "Cómo funcionan
+ * las dos ramas"). For the loss <dO, O>, with z_t = sigma <q, k_t> and
+ * P_t = exp(z_t - LSE) over the row's selected tokens T:
+ *   dV_t = sum over the rows that see t of P_t dO,
+ *   dS_t = P_t (<dO, v_t> - <dO, O>),
+ *   dQ = sigma sum_t dS_t k_t,  dK_t = sigma sum over those rows of dS_t q.
+ *
+ *   Uses every field of `dims` except index_dim; dtype MSA_BF16 only (others:
+ *   MSA_ERR_UNSUPPORTED).
+ *   q, k, v, block_idx, softmax_scale  as for msa_sparse_attn_fwd
+ *   o         [B, N, Hq, D]   bf16, the forward output of the same inputs
+ *   lse       [B, Hq, N]      fp32, the forward LSE of the same inputs
+ *   dout      [B, N, Hq, D]   bf16, gradient of the loss w.r.t. o
+ *   dq        [B, N, Hq, D]   OUTPUT bf16
+ *   dk, dv    [B, N, Hkv, D]  OUTPUT bf16 (every key is written; keys no row
+ *             selects get 0)
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_ATTN_BWD) bytes
+ *             (per-(row, slot) dQ partials and per-work-item dK/dV partials;
+ *             about 37 GB for N = 128K, Hkv = 8, G = 8, D = 128, k = 16).
+ * Deterministic: every sum runs in a fixed order.
+ */
+MSA_API int msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                                const int32_t* block_idx, const void* o, const float* lse, const void* dout,
+                                float softmax_scale, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * KL alignment loss forward.

@@ -292,16 +292,21 @@ def attention_backward(q, k, v, do, block_idx, Bk, scale=None):
     dV = np.zeros((B, N, Hkv, D))
     for b in range(B):
         for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
             kg = np.asarray(kk[b, :, g], dtype=np.float64)
             vg = np.asarray(vv[b, :, g], dtype=np.float64)
+            qg = np.asarray(qq[b, :, hs], dtype=np.float64)
+            dg = np.asarray(dd[b, :, hs], dtype=np.float64)
+            dKg = np.zeros((N, D))
+            dVg = np.zeros((N, D))
             for i in range(N):
                 T = token_set(bi[b, g, i], i, Bk)
-                hs = slice(g * G, (g + 1) * G)
-                dq, dk, dv = _row_backward(np.asarray(qq[b, i, hs], dtype=np.float64), kg[T], vg[T],
-                                           np.asarray(dd[b, i, hs], dtype=np.float64), scale)
+                dq, dk, dv = _row_backward(qg[i], kg[T], vg[T], dg[i], scale)
                 dQ[b, i, hs] = dq
-                dK[b, T, g] += dk          # T holds distinct tokens
-                dV[b, T, g] += dv
+                dKg[T] += dk          # T holds distinct tokens
+                dVg[T] += dv
+            dK[b, :, g] = dKg
+            dV[b, :, g] = dVg
     return dQ, dK, dV
 
 

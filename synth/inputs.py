@@ -93,3 +93,13 @@ def sample_rows(w: Workload, n=None, seed=1):
     edges = [b * w.seqlen + p for b in range(w.batch) for p in edge_positions(w)]
     flat = np.unique(np.concatenate([flat, np.asarray(edges, dtype=np.int64)]))
     return np.stack([flat // w.seqlen, flat % w.seqlen], axis=1)
+
+
+def make_grad_output(w: Workload, device="cpu", seed=None):
+    """Seeded output gradient dO [B, N, Hq, D] for the backward: standard
+    normal in the workload dtype, from its own generator (seed + 1000), so the
+    forward inputs do not change."""
+    seed = (w.seed if seed is None else seed) + 1000
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return _randn((w.batch, w.seqlen, w.q_heads, w.head_dim), gen, device, torch_dtype(w.dtype))

@@ -104,6 +104,33 @@ def test_fp8_is_for_the_selection_only(lib):
     assert lib.msa_check_block_idx(ctypes.byref(d), FAKE, None, None) == 1
 
 
+def _bwd(lib, d, ptrs=None, ws=FAKE, nws=1 << 50):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, bi=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE)
+    p.update(ptrs or {})
+    return lib.msa_sparse_attn_bwd(ctypes.byref(d), p["q"], p["k"], p["v"], p["bi"], p["o"], p["lse"], p["do"],
+                                   0.0, p["dq"], p["dk"], p["dv"], ws, nws, None)
+
+
+def test_backward_rejects_before_any_launch(lib):
+    d = _dims()
+    need = lib.msa_workspace_bytes(ctypes.byref(d), msa.MSA_OP_ATTN_BWD)
+    assert need > lib.msa_workspace_bytes(ctypes.byref(d), msa.MSA_OP_ATTN) > 0
+    assert _bwd(lib, _dims(dtype=msa.MSA_F32)) == 3              # bf16 only
+    assert lib.msa_workspace_bytes(ctypes.byref(_dims(dtype=msa.MSA_F32)), msa.MSA_OP_ATTN_BWD) == 0
+    assert _bwd(lib, _dims(dtype=msa.MSA_FP8_E4M3)) == 3
+    assert _bwd(lib, _dims(head_dim=96)) == 3
+    assert _bwd(lib, _dims(index_dim=96), ws=None, nws=0) == 5   # index_dim is not read
+    for name in ("q", "k", "v", "bi", "o", "lse", "do", "dq", "dk", "dv"):
+        assert _bwd(lib, d, ptrs={name: None}) == 1, name
+        assert _bwd(lib, d, ptrs={name: MISALIGNED}) == 4, name
+    assert _bwd(lib, d, ws=None, nws=0) == 5
+    assert _bwd(lib, d, nws=need - 1) == 5
+    assert _bwd(lib, d, ws=MISALIGNED, nws=need) == 5
+    none = {n: None for n in ("q", "k", "v", "bi", "o", "lse", "do", "dq", "dk", "dv")}
+    assert _bwd(lib, _dims(batch=0), ptrs=none, ws=None, nws=0) == 0
+    assert _bwd(lib, _dims(seqlen=0), ptrs=none, ws=None, nws=0) == 0
+
+
 def test_index_ignores_attention_fields(lib):
     # group_size/head_dim are not read by the selection: the call goes on to
     # the pointer checks (NULL output -> MSA_ERR_NULL, not UNSUPPORTED)
