@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import block_sparse_gqa_index_amd as msa  # noqa: E402
-from synth import CONFIGS, make_inputs, sample_rows  # noqa: E402
+from synth import CONFIGS, make_grad_output, make_inputs, sample_rows  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and MFMA)
@@ -157,6 +157,8 @@ def main():
     ap.add_argument("--index-fp8", action="store_true",
                     help="also time the step with the selection on fp8 e4m3 copies of the index inputs "
                          "(reported beside the bf16 headline, never as it)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="also time the main-branch backward (msa_sparse_attn_bwd) on the step's outputs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -299,6 +301,27 @@ def main():
             "speedup_vs_bf16_index": stage_ms[index_kernel] / idx8,
             "ms_per_step": ms8, "tokens_per_s": tokens / (ms8 * 1e-3),
             "same_selection": bool(torch.equal(bi8, block_idx))}
+    if args.bwd:
+        log("[bench] main-branch backward")
+        dout = make_grad_output(w, device=dev)
+        bws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_ATTN_BWD)), dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+
+        def bwd():
+            msa.sparse_attn_bwd(x["q"], x["k"], x["v"], block_idx, o, lse, dout, dq=dq, dk=dk, dv=dv, workspace=bws)
+        for _ in range(max(1, args.warmup)):
+            bwd()
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(1, args.steps))]
+        for e in bev:
+            e[0].record(stream)
+            bwd()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in bev]))
+        fb = 2.5 * f_main   # S, dP, dV, dK, dQ: five D-deep products per (row, token) against the forward's two
+        out["backward"] = {"ms": bwd_ms, "algorithmic_tflop": fb / 1e12, "tflops": fb / (bwd_ms * 1e-3) / 1e12,
+                           "frac_of_peak": fb / (bwd_ms * 1e-3) / 1e12 / peak,
+                           "tokens_per_s": tokens / (bwd_ms * 1e-3)}
     if args.kl:
         log("[bench] KL-alignment forward")
         kws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_KL)), dtype=torch.uint8, device=dev)

@@ -83,6 +83,7 @@ struct BwdLds {
     unsigned char q[ROWB], dout[ROWB], qt[COLB], dot[COLB], ds[DSB];
     float lse2[32], dl[32];
     int pos[32], slot[32];
+    int entries[kSegBwd];   // the item's list entries (non-local items)
 };
 
 // One 8-row x 16-byte unit of the tile staging: rows 16c + {4h..4h+3, 8+4h..8+4h+3}
@@ -94,14 +95,14 @@ struct StageUnit {
 template <int D, int G, bool LOCAL>
 struct BwdItem {
     int b, g, j, count, start, q0, lslot;
-    const int32_t* list;
+    const int* entries;   // LDS copy of the item's list entries
     // (position, slot) of entry e < count.
     __device__ __forceinline__ void entry(int e, int& i, int& s) const {
         if constexpr (LOCAL) {
             i = q0 + e;
             s = lslot;
         } else {
-            const int v = list[start + e];
+            const int v = entries[e];
             i = v >> 5;
             s = v & 31;
         }
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
         it.count = min(kBlock, N - it.q0);
         it.lslot = min(topk, it.j + 1) - 1;
         it.start = 0;
-        it.list = nullptr;
+        it.entries = nullptr;
         pidx = local_base + ((size_t)it.b * Hkv + it.g) * nb + it.j;
     } else {
         const int item_id = item_of_workgroup(blockIdx.x);
@@ -204,8 +205,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
         it.count = e.z;
         it.q0 = 0;
         it.lslot = 0;
-        it.list = list;
+        it.entries = sh.entries;
         pidx = item_id;
+        for (int x = threadIdx.x; x < it.count; x += blockDim.x) sh.entries[x] = list[it.start + x];
+        __syncthreads();
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -243,14 +246,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
     }
 
     constexpr float kLog2e = 1.4426950408889634f;
+    // Tiles are staged two ahead: the threads of half `par` (threadIdx.x / 128)
+    // stage the tiles t with t % 2 == par, the global loads of tile t + 2
+    // being issued while tiles t and t + 1 are on the matrix cores.
     StageUnit su;
-    const int u = threadIdx.x;
-    if (u < NSTAGE && ntiles > 0) stage_load<D, G, LOCAL>(su, it, 0, u, q, dout, N, Hq);
+    const int par = threadIdx.x >> 7;
+    const int u = threadIdx.x & 127;
+    if (u < NSTAGE && par < ntiles) stage_load<D, G, LOCAL>(su, it, par, u, q, dout, N, Hq);
     float r_lse = 0.f, r_dl = 0.f;
     int r_pos = -1, r_slot = 0;
     auto row_load = [&](int t) {
-        // thread 255 - m loads the scalars of row m (rows past the item: P = 0)
-        const int m = 255 - threadIdx.x;
+        // thread 127 - m of each half loads the scalars of row m (rows past the item: P = 0)
+        const int m = 127 - u;
         if (m < 32) {
             const int pe = t * PPT + m / G;
             r_pos = -1;
@@ -267,13 +274,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             }
         }
     };
-    row_load(0);
+    if (par < ntiles) row_load(par);
 
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();   // the previous tile's LDS reads are done
-        if (u < NSTAGE) stage_store<D>(su, sh, u);
-        {
-            const int m = 255 - threadIdx.x;
+        const bool mine = (t & 1) == par;
+        if (mine) {
+            if (u < NSTAGE) stage_store<D>(su, sh, u);
+            const int m = 127 - u;
             if (m < 32) {
                 sh.lse2[m] = r_lse;
                 sh.dl[m] = r_dl;
@@ -282,9 +290,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             }
         }
         __syncthreads();
-        if (t + 1 < ntiles) {   // next tile's global loads overlap this tile's math
-            if (u < NSTAGE) stage_load<D, G, LOCAL>(su, it, t + 1, u, q, dout, N, Hq);
-            row_load(t + 1);
+        if (mine && t + 2 < ntiles) {   // tile t + 2's global loads overlap tiles t and t + 1
+            if (u < NSTAGE) stage_load<D, G, LOCAL>(su, it, t + 2, u, q, dout, N, Hq);
+            row_load(t + 2);
         }
 
         // S = Q K_w^T and dP = dO V_w^T: lane = key, accumulators = rows.
