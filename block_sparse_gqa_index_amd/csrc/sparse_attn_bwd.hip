@@ -74,12 +74,24 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16_t* __restrict
 
 // LDS of one work-group: the current 32-row tile (natural and transposed),
 // the dS tile, per-row scalars.
+// Transposed 32-row tile [D][32 rows, permuted], stored chunk-major: the
+// 16-byte chunk q (rows 8q .. 8q+7 of the permuted order) of dim d sits at
+// q * (16 D + 16) + 16 d. The 16 lanes of a read phase (consecutive d, one q)
+// then cover all banks once; the 16-byte pad between chunk columns spreads the
+// staging writes of different q.
+template <int D>
+struct ColTile {
+    static constexpr int QSTRIDE = 16 * D + 16;
+    static constexpr int BYTES = 4 * QSTRIDE;
+    __device__ static __forceinline__ int offset(int d, int q) { return q * QSTRIDE + 16 * d; }
+};
+
 template <int D>
 struct BwdLds {
     using RowT = SwzTile<bf16_t, D>;        // [32 rows][D]
-    using ColT = SwzTile<bf16_t, 32>;       // [D][32 rows, permuted]
+    using ColT = ColTile<D>;                // [D][32 rows, permuted]
     using DsT = SwzTile<bf16_t, kBlock>;    // [32 rows][128 keys, permuted]
-    static constexpr int ROWB = 32 * RowT::ROWB, COLB = D * ColT::ROWB, DSB = 32 * DsT::ROWB;
+    static constexpr int ROWB = 32 * RowT::ROWB, COLB = ColT::BYTES, DSB = 32 * DsT::ROWB;
     unsigned char q[ROWB], dout[ROWB], qt[COLB], dot[COLB], ds[DSB];
     float lse2[32], dl[32];
     int pos[32], slot[32];
@@ -117,7 +129,7 @@ __device__ __forceinline__ void stage_load(StageUnit& su, const BwdItem<D, G, LO
                                            int Hq) {
     constexpr int DC = D / 8, PPT = 32 / G;
     const int tensor = u / (4 * DC), v = u % (4 * DC);
-    const int grp = v / DC, dc = v % DC;
+    const int grp = v & 3, dc = v >> 2;   // the row group varies fastest across lanes
     const int c = grp >> 1, h = grp & 1;
     const bf16_t* src = tensor ? dout : q;
 #pragma unroll
@@ -140,7 +152,7 @@ template <int D>
 __device__ __forceinline__ void stage_store(const StageUnit& su, BwdLds<D>& sh, int u) {
     constexpr int DC = D / 8;
     const int tensor = u / (4 * DC), v = u % (4 * DC);
-    const int grp = v / DC, dc = v % DC;
+    const int grp = v & 3, dc = v >> 2;   // the row group varies fastest across lanes
     const int c = grp >> 1, h = grp & 1;
     unsigned char* nat = tensor ? sh.dout : sh.q;
     unsigned char* tr = tensor ? sh.dot : sh.qt;
@@ -160,7 +172,7 @@ __device__ __forceinline__ void stage_store(const StageUnit& su, BwdLds<D>& sh, 
             const uint32_t hi = (su.x[2 * w + 1][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
             y[w] = lo | (hi << 16);
         }
-        *reinterpret_cast<u32x4*>(tr + ColT::offset(dc * 8 + dd, (16 * c + 8 * h) * 2)) = y;
+        *reinterpret_cast<u32x4*>(tr + ColT::offset(dc * 8 + dd, 2 * c + h)) = y;
     }
 }
 
@@ -269,12 +281,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
                 const size_t r = ((size_t)it.b * Hq + it.g * G + m % G) * N + i;
                 r_pos = i;
                 r_slot = s;
-                r_lse = lse[r] * kLog2e;
+                r_lse = lse[r];   // scaled when stored: no use right after the load
                 r_dl = dl[r];
             }
         }
     };
     if (par < ntiles) row_load(par);
+    // Every load issued so far (the key block's operands, the first two tiles)
+    // completes here, so the loop below only ever waits for its own prefetches.
+    __builtin_amdgcn_s_waitcnt(0);
 
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();   // the previous tile's LDS reads are done
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             if (u < NSTAGE) stage_store<D>(su, sh, u);
             const int m = 127 - u;
             if (m < 32) {
-                sh.lse2[m] = r_lse;
+                sh.lse2[m] = r_lse * kLog2e;
                 sh.dl[m] = r_dl;
                 sh.pos[m] = r_pos;
                 sh.slot[m] = r_slot;
@@ -325,8 +340,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 Op8<bf16_t> a, b;
-                a.load(sh.dot + BwdLds<D>::ColT::offset(32 * dt + col, (16 * sl + 8 * half) * 2));
-                b.load(sh.qt + BwdLds<D>::ColT::offset(32 * dt + col, (16 * sl + 8 * half) * 2));
+                a.load(sh.dot + BwdLds<D>::ColT::offset(32 * dt + col, 2 * sl + half));
+                b.load(sh.qt + BwdLds<D>::ColT::offset(32 * dt + col, 2 * sl + half));
                 mma16(dvt[dt], a, bp);
                 mma16(dkt[dt], b, bds);
             }
