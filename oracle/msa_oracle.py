@@ -38,7 +38,9 @@ Readings of points the pages leave open (each listed in the design notes):
     student the softmax of index_scale * index score over the same tokens.
   * the backward differentiates the main-branch forward above for the loss
     <dO, O> (dO given); every key's gradient sums the contributions of all rows
-    that selected its block.
+    that selected its block;
+  * the KL term's backward holds the teacher fixed (gradient stopped at the
+    index branch input) and reaches q_idx and k_idx only.
 
 Parity: every function here is pinned by tests that do not re-use its code
 (brute force, closed forms, torch's dense SDPA, scipy's entropy, invariants).
@@ -50,7 +52,7 @@ import numpy as np
 __all__ = [
     "local_block", "visible_block_scores", "select_blocks", "index_topk_rows",
     "index_topk", "token_set", "token_count", "attention_rows", "sparse_attention",
-    "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "map_positions",
+    "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "kl_backward", "map_positions",
 ]
 
 
@@ -397,6 +399,61 @@ def kl_align(q, k, q_idx, k_idx, block_idx, Bk, scale=None, index_scale=None):
     kl = kl_rows(q, k, q_idx, k_idx, rows, pos, Bk, scale, index_scale)
     kl = kl.reshape(B, N, -1).transpose(0, 2, 1).copy()
     return kl, float(kl.sum())
+
+
+def _kl_row_backward(qh, kt, qi, kit, scale, index_scale):
+    """Gradient of one row's KL term w.r.t. its student logits' inputs.
+
+    qh [G, D] (the group's query heads), kt [|T|, D] (keys of the selected
+    tokens), qi [Di] (the row's index query), kit [|T|, Di] (index keys).
+    Teacher p = mean_h softmax_t(scale <q_h, k_t>) is held fixed (no gradient
+    flows into the main branch); student s = softmax_t(index_scale <qi, kit_t>).
+    KL = sum_t p_t (ln p_t - ln s_t) with ln s_t = index_scale u_t - LSE_u has
+    dKL/du_t = index_scale (s_t sum_v p_v - p_t) = index_scale (s_t - p_t) for
+    u_t = <qi, kit_t>, since the teacher sums to 1 over the same tokens.
+    Returns (dKL/dqi [Di], dKL/dkit [|T|, Di])."""
+    _, ph = _softmax_stats(scale * (qh @ kt.T))
+    p = ph.mean(axis=0)
+    _, sv = _softmax_stats(index_scale * (kit @ qi)[None, :])
+    du = index_scale * (sv[0] - p)
+    return du @ kit, np.outer(du, qi)
+
+
+def kl_backward(q, k, q_idx, k_idx, block_idx, Bk, dkl_rows=None, scale=None, index_scale=None):
+    """Gradients of L = sum over rows of dkl_rows[b, g, i] * KL_row (dkl_rows = 1
+    everywhere: L = kl_sum) w.r.t. q_idx and k_idx: (dq_idx [B,N,Hkv,Di],
+    dk_idx [B,N,Di]) in float64.
+
+    [P2] "Cómo se entrena MSA": the KL alignment loss trains the index branch
+    toward the main branch's attention pattern, and the gradient is stopped at
+    the index branch's input, so the loss reaches the index projections only:
+    the teacher (main-branch probabilities) is a constant here. [P1] paragraph
+    on the backward: the proxy gradient comes from the cached block indices.
+    k_idx is shared by the groups, so its gradient sums over every group's rows.
+    """
+    qq, kk, qi, ki = _arr(q), _arr(k), _arr(q_idx), _arr(k_idx)
+    B, N, Hq, D = qq.shape
+    Hkv, Di = kk.shape[2], ki.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    index_scale = (1.0 / math.sqrt(Di) if index_scale is None or index_scale <= 0
+                   else float(index_scale))
+    bi = np.asarray(block_idx)
+    w = np.ones((B, Hkv, N)) if dkl_rows is None else np.asarray(_arr(dkl_rows), dtype=np.float64)
+    dqi = np.zeros((B, N, Hkv, Di))
+    dki = np.zeros((B, N, Di))
+    for b in range(B):
+        kib = np.asarray(ki[b], dtype=np.float64)
+        for g in range(Hkv):
+            kg = np.asarray(kk[b, :, g], dtype=np.float64)
+            qg = np.asarray(qq[b, :, g * G:(g + 1) * G], dtype=np.float64)
+            qig = np.asarray(qi[b, :, g], dtype=np.float64)
+            for i in range(N):
+                T = token_set(bi[b, g, i], i, Bk)
+                a, c = _kl_row_backward(qg[i], kg[T], qig[i], kib[T], scale, index_scale)
+                dqi[b, i, g] = w[b, g, i] * a
+                dki[b, T] += w[b, g, i] * c
+    return dqi, dki
 
 
 def map_positions(fn, positions, row_arrays=(), workers=1, chunk=256):

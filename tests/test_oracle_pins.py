@@ -480,3 +480,104 @@ def test_backward_planted_mistakes_are_caught(monkeypatch):
         monkeypatch.setattr(O, "_row_backward", bad)
         assert not ok(), bad.__name__
     monkeypatch.setattr(O, "_row_backward", real)
+
+
+# -------------------------------------------------------------- KL backward --
+
+def _kl_autograd(q, kk, q_idx, k_idx, bi, Bk, w, scale, iscale):
+    """torch autograd (float64) of sum_rows w * KL over dense masked
+    distributions, with the teacher detached."""
+    B, N, Hq, D = q.shape
+    Hkv = kk.shape[2]
+    G = Hq // Hkv
+    qi = torch.tensor(q_idx).requires_grad_()
+    ki = torch.tensor(k_idx).requires_grad_()
+    mask = torch.zeros(B, Hkv, N, N, dtype=torch.bool)
+    for b in range(B):
+        for g in range(Hkv):
+            for i in range(N):
+                mask[b, g, i, O.token_set(bi[b, g, i], i, Bk)] = True
+    qt = torch.tensor(q).view(B, N, Hkv, G, D)
+    kt = torch.tensor(kk)
+    logits = scale * torch.einsum("bighd,btgd->bghit", qt, kt)
+    logits = logits.masked_fill(~mask[:, :, None], float("-inf"))
+    p = torch.softmax(logits, dim=-1).mean(dim=2).detach()          # [B, Hkv, N, N]
+    u = iscale * torch.einsum("bigd,btd->bgit", qi, ki)
+    log_s = torch.log_softmax(u.masked_fill(~mask, float("-inf")), dim=-1)
+    terms = torch.where(mask & (p > 0), p * (torch.log(p) - log_s), torch.zeros((), dtype=torch.float64))
+    loss = (torch.tensor(w) * terms.sum(dim=-1)).sum()
+    loss.backward()
+    return qi.grad.numpy(), ki.grad.numpy(), float(loss.detach())
+
+
+@pytest.mark.parametrize("seed,N,Bk,k,G", [(0, 48, 8, 3, 2), (1, 45, 8, 4, 1), (2, 40, 4, 16, 4)])
+def test_kl_backward_matches_autograd(seed, N, Bk, k, G):
+    Hkv, D, Di = 2, 8, 4
+    q_idx, k_idx, q, kk, vv = _rand_case(seed, N=N, Hkv=Hkv, G=G, D=D, Di=Di, Bk=Bk)
+    q_idx, k_idx = q_idx / 2, k_idx / 2
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    w = np.random.default_rng(seed + 50).uniform(0.5, 2.0, size=(1, Hkv, N))
+    got = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk, dkl_rows=w, scale=0.4, index_scale=0.3)
+    gq, gk, loss = _kl_autograd(q, kk, q_idx, k_idx, bi, Bk, w, 0.4, 0.3)
+    np.testing.assert_allclose(got[0], gq, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(got[1], gk, atol=1e-12, rtol=0)
+    rows, _ = O.kl_align(q, kk, q_idx, k_idx, bi, Bk, scale=0.4, index_scale=0.3)
+    assert abs(loss - float((w * rows).sum())) <= 1e-10 * max(1.0, abs(loss))
+
+
+def test_kl_backward_finite_differences():
+    """Directional derivative of kl_sum (the pinned forward) along (a, c) in
+    (q_idx, k_idx) equals <dq_idx, a> + <dk_idx, c>; the selection is held
+    fixed (it is an input of the loss)."""
+    N, Bk, k, Hkv, G, D, Di = 40, 8, 3, 2, 2, 8, 4
+    q_idx, k_idx, q, kk, vv = _rand_case(21, N=N, Hkv=Hkv, G=G, D=D, Di=Di, Bk=Bk)
+    q_idx, k_idx = q_idx / 3, k_idx / 3
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    rng = np.random.default_rng(22)
+    a, c = rng.standard_normal(q_idx.shape), rng.standard_normal(k_idx.shape)
+    dqi, dki = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk)
+
+    def f(t):
+        return O.kl_align(q, kk, q_idx + t * a, k_idx + t * c, bi, Bk)[1]
+
+    eps = 1e-5
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    an = float((dqi * a).sum() + (dki * c).sum())
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def test_kl_backward_sum_rule_and_mistakes(monkeypatch):
+    """The dk_idx of all keys sums to 0 (every row's logit gradients sum to 0);
+    a sign flip, a missing index scale or a non-detached-teacher-shaped term
+    fails the autograd pin."""
+    N, Bk, k, Hkv, G, D, Di = 40, 8, 3, 2, 2, 8, 4
+    q_idx, k_idx, q, kk, vv = _rand_case(23, N=N, Hkv=Hkv, G=G, D=D, Di=Di, Bk=Bk)
+    q_idx, k_idx = q_idx / 2, k_idx / 2
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    dqi, dki = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk)
+    np.testing.assert_allclose(dki.sum(axis=(0, 1)), 0.0, atol=1e-10)
+    w = np.ones((1, Hkv, N))
+    want = _kl_autograd(q, kk, q_idx, k_idx, bi, Bk, w, 1 / math.sqrt(D), 1 / math.sqrt(Di))[:2]
+
+    def ok():
+        got = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk)
+        return all(np.allclose(x, y, atol=1e-9) for x, y in zip(got, want))
+
+    assert ok()
+    real = O._kl_row_backward
+
+    def flipped(qh, kt, qi, kit, scale, index_scale):
+        a, c = real(qh, kt, qi, kit, scale, index_scale)
+        return -a, -c
+
+    def unscaled(qh, kt, qi, kit, scale, index_scale):
+        a, c = real(qh, kt, qi, kit, scale, index_scale)
+        return a / index_scale, c / index_scale
+
+    def head0_teacher(qh, kt, qi, kit, scale, index_scale):   # first head instead of the group mean
+        return real(qh[:1], kt, qi, kit, scale, index_scale)
+
+    for bad in (flipped, unscaled, head0_teacher):
+        monkeypatch.setattr(O, "_kl_row_backward", bad)
+        assert not ok(), bad.__name__
+    monkeypatch.setattr(O, "_kl_row_backward", real)
