@@ -13,6 +13,8 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   sparse_attn_fwd(q, k, v, block_idx, scale)       -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])
       (stages=... enqueues only some of its three stages: msa_sparse_attn_fwd_stages)
   kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse) -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])
+      (index_lse=<fp32 [B,Hkv,N] tensor> also receives the student LSE per row)
+  kl_align_bwd(q, k, q_idx, k_idx, block_idx, lse, index_lse) -> (dq_idx, dk_idx), bf16
   forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse): selection, then attention
   sparse_attn_bwd(q, k, v, block_idx, o, lse, dout) -> (dq, dk, dv), bf16
   workspace_bytes(dims, op)
@@ -26,12 +28,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_F32, MSA_FP8_E4M3 = 0, 1, 2
-MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD = 0, 1, 2, 3, 4
+MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD, MSA_OP_KL_BWD = 0, 1, 2, 3, 4, 5
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
 EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
-           "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd",
+           "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -68,7 +70,9 @@ def load_library(path: str = LIB_PATH):
     lib.msa_sparse_attn_fwd_stages.argtypes = [dp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz,
                                                ctypes.c_int, vp]
     lib.msa_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
-                                     vp, vp, vp, sz, vp]
+                                     vp, vp, vp, vp, sz, vp]
+    lib.msa_kl_align_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp,
+                                     ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_forward.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
@@ -236,9 +240,10 @@ def sparse_attn_bwd(q, k, v, block_idx, o, lse, dout, softmax_scale=0.0, dq=None
 
 
 def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_scale=0.0,
-                 kl_rows=None, kl_sum=None, workspace=None, block_size=128):
+                 kl_rows=None, kl_sum=None, workspace=None, block_size=128, index_lse=None):
     """KL(group-mean main softmax || index softmax) over the selected tokens,
-    per row -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])."""
+    per row -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1]); `index_lse` (an fp32
+    [B,Hkv,N] tensor, optional) receives the student's LSE per row."""
     lib = load_library()
     _req(q, "q", ndim=4)
     _req(k, "k", dtype=q.dtype, ndim=4)
@@ -254,11 +259,49 @@ def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_sc
         kl_rows = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
     if kl_sum is None:
         kl_sum = torch.empty((1,), dtype=torch.float32, device=q.device)
+    if index_lse is not None:
+        _req(index_lse, "index_lse", dtype=torch.float32, ndim=3)
+        if tuple(index_lse.shape) != (B, Hkv, N):
+            raise ValueError("index_lse must be [B, Hkv, N]")
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_KL), q.device, workspace)
     _check(lib.msa_kl_align_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
                                 _ptr(block_idx), _ptr(lse), float(softmax_scale), float(index_scale),
-                                _ptr(kl_rows), _ptr(kl_sum), _ptr(ws), nws, _stream(q.device)))
+                                _ptr(kl_rows), _ptr(kl_sum), _ptr(index_lse), _ptr(ws), nws, _stream(q.device)))
     return kl_rows, kl_sum
+
+
+def kl_align_bwd(q, k, q_idx, k_idx, block_idx, lse, index_lse, softmax_scale=0.0, index_scale=0.0,
+                 dkl_rows=None, kl_weight=1.0, dq_idx=None, dk_idx=None, workspace=None, block_size=128):
+    """Gradients of sum_rows w_row KL_row (w_row = kl_weight * dkl_rows, or
+    kl_weight) w.r.t. q_idx and k_idx, the teacher held fixed (bf16) ->
+    (dq_idx [B,N,Hkv,Di], dk_idx [B,N,Di]). lse and index_lse come from the
+    forward of the same inputs."""
+    lib = load_library()
+    _req(q, "q", ndim=4)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(q_idx, "q_idx", dtype=q.dtype, ndim=4)
+    _req(k_idx, "k_idx", dtype=q.dtype, ndim=3)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    _req(index_lse, "index_lse", dtype=torch.float32, ndim=3)
+    B, N, Hq, D = q.shape
+    Hkv, Di = q_idx.shape[2], q_idx.shape[3]
+    topk = block_idx.shape[3]
+    if tuple(index_lse.shape) != (B, Hkv, N) or (dkl_rows is not None and tuple(dkl_rows.shape) != (B, Hkv, N)):
+        raise ValueError("index_lse and dkl_rows must be [B, Hkv, N]")
+    if dkl_rows is not None:
+        _req(dkl_rows, "dkl_rows", dtype=torch.float32, ndim=3)
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
+    dq_idx = torch.empty_like(q_idx) if dq_idx is None else dq_idx
+    dk_idx = torch.empty_like(k_idx) if dk_idx is None else dk_idx
+    _req(dq_idx, "dq_idx", dtype=q.dtype, ndim=4)
+    _req(dk_idx, "dk_idx", dtype=q.dtype, ndim=3)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_KL_BWD), q.device, workspace)
+    _check(lib.msa_kl_align_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                                _ptr(lse), _ptr(index_lse), float(softmax_scale), float(index_scale),
+                                _ptr(dkl_rows), float(kl_weight), _ptr(dq_idx), _ptr(dk_idx), _ptr(ws), nws,
+                                _stream(q.device)))
+    return dq_idx, dk_idx
 
 
 def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0, block_idx=None, o=None, lse=None,

@@ -224,8 +224,8 @@ __global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
 template <typename T, int D, int DI, int G>
 __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
-    const float* __restrict__ lse, const float* __restrict__ part, float* __restrict__ kl_rows, int B, int N,
-    int Hkv, int nb, int topk, int KP, float scale_log2, float iscale) {
+    const float* __restrict__ lse, const float* __restrict__ part, float* __restrict__ kl_rows,
+    float* __restrict__ index_lse, int B, int N, int Hkv, int nb, int topk, int KP, float scale_log2, float iscale) {
     __shared__ __align__(16) unsigned char lds[SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES];
     unsigned char* lds_i = lds + SwzTile<T, D>::BYTES;
     const int g = blockIdx.x % Hkv;
@@ -269,7 +269,10 @@ __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
             merge_lse(a.mu, a.lu, x.w, xl);
         }
         const float lse_u = a.mu + __logf(a.lu);
-        if (valid && hh == 0 && half == 0) kl_rows[((size_t)b * Hkv + g) * N + i] = a.A - a.Bs + lse_u * a.P;
+        if (valid && hh == 0 && half == 0) {
+            kl_rows[((size_t)b * Hkv + g) * N + i] = a.A - a.Bs + lse_u * a.P;
+            if (index_lse) index_lse[((size_t)b * Hkv + g) * N + i] = lse_u;
+        }
     }
 }
 
@@ -326,7 +329,8 @@ KlWorkspace kl_workspace_layout(const LaunchDims& d) {
 template <typename T, int D, int DI, int G>
 static hipError_t launch_kl_t(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
                               const void* k_idx, const int32_t* block_idx, const float* lse, float scale,
-                              float iscale, float* kl_rows, float* kl_sum, unsigned char* ws, hipStream_t st) {
+                              float iscale, float* kl_rows, float* kl_sum, float* index_lse, unsigned char* ws,
+                              hipStream_t st) {
     const KlWorkspace L = kl_workspace_layout(d);
     const float scale_log2 = scale * 1.4426950408889634f;
     const int KP = d.k > 1 ? d.k - 1 : 1;
@@ -346,7 +350,7 @@ static hipError_t launch_kl_t(const LaunchDims& d, const void* q, const void* k,
                            windows(d), KP, scale_log2, iscale);
     }
     hipLaunchKernelGGL((kl_local_combine_kernel<T, D, DI, G>), dim3((unsigned)(d.nb * d.B * d.Hkv)), dim3(256), 0,
-                       st, tq, tk, tqi, tki, lse, part, kl_rows, d.B, d.N, d.Hkv, d.nb,
+                       st, tq, tk, tqi, tki, lse, part, kl_rows, index_lse, d.B, d.N, d.Hkv, d.nb,
                        L.lists.has_nonlocal ? d.k : 1, KP, scale_log2, iscale);
     double* red = reinterpret_cast<double*>(ws + L.red);
     const size_t rows = (size_t)d.B * d.Hkv * d.N;
@@ -358,38 +362,41 @@ static hipError_t launch_kl_t(const LaunchDims& d, const void* q, const void* k,
 template <typename T, int D, int DI>
 static hipError_t launch_kl_g(const LaunchDims& d, const void* q, const void* k, const void* qi, const void* ki,
                               const int32_t* bi, const float* lse, float sc, float isc, float* rows, float* sum,
-                              unsigned char* ws, hipStream_t st) {
+                              float* ilse, unsigned char* ws, hipStream_t st) {
     switch (d.G) {
-        case 1: return launch_kl_t<T, D, DI, 1>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-        case 2: return launch_kl_t<T, D, DI, 2>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-        case 4: return launch_kl_t<T, D, DI, 4>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-        case 8: return launch_kl_t<T, D, DI, 8>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-        case 16: return launch_kl_t<T, D, DI, 16>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-        default: return launch_kl_t<T, D, DI, 32>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+        case 1: return launch_kl_t<T, D, DI, 1>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+        case 2: return launch_kl_t<T, D, DI, 2>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+        case 4: return launch_kl_t<T, D, DI, 4>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+        case 8: return launch_kl_t<T, D, DI, 8>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+        case 16: return launch_kl_t<T, D, DI, 16>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+        default: return launch_kl_t<T, D, DI, 32>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
     }
 }
 
 template <typename T>
 static hipError_t launch_kl_dt(const LaunchDims& d, const void* q, const void* k, const void* qi, const void* ki,
                                const int32_t* bi, const float* lse, float sc, float isc, float* rows, float* sum,
-                               unsigned char* ws, hipStream_t st) {
-    if (d.D == 128 && d.Di == 128) return launch_kl_g<T, 128, 128>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-    if (d.D == 128) return launch_kl_g<T, 128, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-    if (d.Di == 128) return launch_kl_g<T, 64, 128>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
-    return launch_kl_g<T, 64, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ws, st);
+                               float* ilse, unsigned char* ws, hipStream_t st) {
+    if (d.D == 128 && d.Di == 128)
+        return launch_kl_g<T, 128, 128>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+    if (d.D == 128) return launch_kl_g<T, 128, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+    if (d.Di == 128) return launch_kl_g<T, 64, 128>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+    return launch_kl_g<T, 64, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
 }
 
 hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx, const void* k_idx,
                            const int32_t* block_idx, const float* lse, float scale, float index_scale,
-                           float* kl_rows, float* kl_sum, void* ws, hipStream_t st) {
+                           float* kl_rows, float* kl_sum, float* index_lse, void* ws, hipStream_t st) {
     if (d.B == 0 || d.N == 0) {
         hipLaunchKernelGGL(kl_reduce_final, dim3(1), dim3(kRedThreads), 0, st, (const double*)nullptr, 0, kl_sum);
         return hipGetLastError();
     }
     unsigned char* w = static_cast<unsigned char*>(ws);
     if (d.dtype == 0)
-        return launch_kl_dt<bf16_t>(d, q, k, q_idx, k_idx, block_idx, lse, scale, index_scale, kl_rows, kl_sum, w, st);
-    return launch_kl_dt<float>(d, q, k, q_idx, k_idx, block_idx, lse, scale, index_scale, kl_rows, kl_sum, w, st);
+        return launch_kl_dt<bf16_t>(d, q, k, q_idx, k_idx, block_idx, lse, scale, index_scale, kl_rows, kl_sum,
+                                    index_lse, w, st);
+    return launch_kl_dt<float>(d, q, k, q_idx, k_idx, block_idx, lse, scale, index_scale, kl_rows, kl_sum, index_lse,
+                               w, st);
 }
 
 }  // namespace msa

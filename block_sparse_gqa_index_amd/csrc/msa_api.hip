@@ -31,7 +31,7 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout;   // fp8 index inputs: selection only
     if (d->block_size != 128 || d->topk > 32 ||
         (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3)) ||
-        (op == MSA_OP_ATTN_BWD && d->dtype != MSA_BF16) ||
+        ((op == MSA_OP_ATTN_BWD || op == MSA_OP_KL_BWD) && d->dtype != MSA_BF16) ||
         d->causal != 1 || (uses_heads && (!pow2_upto32(d->group_size) || (d->head_dim != 64 && d->head_dim != 128))) ||
         (uses_index && d->index_dim != 64 && d->index_dim != 128))
         return MSA_ERR_UNSUPPORTED;
@@ -81,7 +81,7 @@ const char* msa_strerror(int status) {
 size_t msa_workspace_bytes(const msa_dims* dims, int op) {
     LaunchDims L;
     if (op != MSA_OP_INDEX && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_FORWARD &&
-        op != MSA_OP_ATTN_BWD)
+        op != MSA_OP_ATTN_BWD && op != MSA_OP_KL_BWD)
         return 0;
     if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
     switch (op) {
@@ -90,6 +90,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, int op) {
         case MSA_OP_FORWARD: return msa::attn_workspace_layout(L).bytes;
         case MSA_OP_ATTN_BWD: return msa::bwd_workspace_layout(L).bytes;
         case MSA_OP_KL: return msa::kl_workspace_layout(L).bytes;
+        case MSA_OP_KL_BWD: return msa::kl_bwd_workspace_layout(L).bytes;
         default: return 0;
     }
 }
@@ -183,8 +184,8 @@ int msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* k, cons
 
 int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
                      const void* k_idx, const int32_t* block_idx, const float* lse, float softmax_scale,
-                     float index_scale, float* kl_rows, float* kl_sum, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     float index_scale, float* kl_rows, float* kl_sum, float* index_lse, void* ws,
+                     size_t ws_bytes, void* stream) {
     LaunchDims L;
     int st = check_dims(dims, MSA_OP_KL, &L);
     if (st != MSA_OK) return st;
@@ -193,7 +194,7 @@ int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const v
         if (!empty(L)) return MSA_ERR_NULL;
     }
     if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_idx) ||
-        !aligned16(lse) || !aligned16(kl_rows))
+        !aligned16(lse) || !aligned16(kl_rows) || (reinterpret_cast<uintptr_t>(index_lse) & 3u))
         return MSA_ERR_ALIGN;
     const size_t need = msa::kl_workspace_layout(L).bytes;
     if (!empty(L) && need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
@@ -201,7 +202,29 @@ int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const v
     const float iscale = index_scale > 0.f ? index_scale : 1.0f / sqrtf((float)L.Di);
     // kl_sum is written even for an empty problem (the sum of nothing is 0).
     return hip_status(msa::launch_kl_align(L, q, k, q_idx, k_idx, block_idx, lse, scale, iscale, kl_rows,
-                                           kl_sum, ws, static_cast<hipStream_t>(stream)));
+                                           kl_sum, index_lse, ws, static_cast<hipStream_t>(stream)));
+}
+
+int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx, const void* k_idx,
+                     const int32_t* block_idx, const float* lse, const float* index_lse, float softmax_scale,
+                     float index_scale, const float* dkl_rows, float kl_weight, void* dq_idx, void* dk_idx,
+                     void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_KL_BWD, &L);
+    if (st != MSA_OK) return st;
+    if (empty(L)) return MSA_OK;
+    if (!q || !k || !q_idx || !k_idx || !block_idx || !lse || !index_lse || !dq_idx || !dk_idx) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_idx) ||
+        !aligned16(lse) || !aligned16(index_lse) || !aligned16(dkl_rows) || !aligned16(dq_idx) ||
+        !aligned16(dk_idx))
+        return MSA_ERR_ALIGN;
+    const size_t need = msa::kl_bwd_workspace_layout(L).bytes;
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    const float iscale = index_scale > 0.f ? index_scale : 1.0f / sqrtf((float)L.Di);
+    return hip_status(msa::launch_kl_align_bwd(L, q, k, q_idx, k_idx, block_idx, lse, index_lse, scale, iscale,
+                                               dkl_rows, kl_weight, dq_idx, dk_idx, ws,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -87,8 +87,24 @@ hipError_t launch_sparse_attn_bwd(const LaunchDims& d, const void* q, const void
                                   const int32_t* block_idx, const void* o, const float* lse, const void* dout,
                                   float scale, void* dq, void* dk, void* dv, void* ws, hipStream_t st);
 
+// KL forward; index_lse (nullable) receives the student's natural-log LSE per row.
 hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
                            const void* k_idx, const int32_t* block_idx, const float* lse, float scale,
-                           float index_scale, float* kl_rows, float* kl_sum, void* ws, hipStream_t st);
+                           float index_scale, float* kl_rows, float* kl_sum, float* index_lse, void* ws,
+                           hipStream_t st);
+
+struct KlBwdWorkspace {
+    ListLayout lists;   // position-sorted, kSegBwd entries per item
+    size_t kit, dqi_part, dki_part, bytes;
+    size_t local_items, dki_items;
+};
+KlBwdWorkspace kl_bwd_workspace_layout(const LaunchDims& d);
+
+// KL backward (bf16): dq_idx [B,N,Hkv,Di], dk_idx [B,N,Di] for the loss
+// sum_rows w_row KL_row, w_row = kl_weight * (dkl_rows ? dkl_rows[row] : 1).
+hipError_t launch_kl_align_bwd(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
+                               const void* k_idx, const int32_t* block_idx, const float* lse,
+                               const float* index_lse, float scale, float index_scale, const float* dkl_rows,
+                               float kl_weight, void* dq_idx, void* dk_idx, void* ws, hipStream_t st);
 
 }  // namespace msa

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define MSA_API __attribute__((visibility("default")))
@@ -55,7 +55,9 @@ extern "C" {
 enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
 
 /* Selector for msa_workspace_bytes. */
-enum msa_op { MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4 };
+enum msa_op {
+    MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4, MSA_OP_KL_BWD = 5
+};
 
 enum msa_status {
     MSA_OK = 0,
@@ -226,12 +228,46 @@ MSA_API int msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void*
  *   kl_rows   [B, Hkv, N] OUTPUT fp32: sum_t p_t (ln p_t - ln s_t) with
  *             p_t = mean_h exp(z_{h,t} - LSE_h), s_t the student softmax.
  *   kl_sum    [1] OUTPUT fp32 (overwritten): sum of kl_rows, fixed order.
+ *   index_lse [B, Hkv, N] optional OUTPUT fp32 (NULL: not written): the
+ *             student's natural-log LSE_u = ln sum_t exp(index_scale u_t) per
+ *             row, which msa_kl_align_bwd takes.
  *   ws        at least msa_workspace_bytes(dims, MSA_OP_KL) bytes.
  */
 MSA_API int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
                      const void* k_idx, const int32_t* block_idx, const float* lse,
                      float softmax_scale, float index_scale, float* kl_rows, float* kl_sum,
-                     void* ws, size_t ws_bytes, void* stream);
+                     float* index_lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * KL alignment loss backward: gradients of L = sum over rows of
+ * w_row * KL_row, w_row = kl_weight * (dkl_rows ? dkl_rows[row] : 1), with
+ * respect to q_idx and k_idx.
+ * Defined by the MSA article (7minutos.es), "Cómo se entrena MSA": the KL loss
+ * trains the index branch toward the main branch's attention pattern and the
+ * gradient is stopped at the index branch's input, so the teacher is held
+ * fixed and nothing flows into q, k; the Flash-MSA article computes the proxy
+ * gradient from the cached block indices. With u_t = <q_idx, k_idx_t>,
+ * s the student softmax and p the teacher of msa_kl_align_fwd:
+ *   dU_t = w_row index_scale (s_t - p_t),
+ *   dq_idx[b,i,g] = sum_t dU_t k_idx_t,  dk_idx[b,t] = sum over the rows of
+ *   every group that see t of dU_t q_idx[b,i,g].
+ *
+ *   Uses every field of `dims`; dtype MSA_BF16 only (others:
+ *   MSA_ERR_UNSUPPORTED).
+ *   q, k, q_idx, k_idx, block_idx, lse, softmax_scale, index_scale  as for
+ *             msa_kl_align_fwd (the same values)
+ *   index_lse [B, Hkv, N] fp32, as written by msa_kl_align_fwd
+ *   dkl_rows  [B, Hkv, N] fp32 row weights, or NULL for all ones
+ *   dq_idx    [B, N, Hkv, Di] OUTPUT bf16
+ *   dk_idx    [B, N, Di]      OUTPUT bf16 (every key written; 0 if unseen)
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_KL_BWD) bytes.
+ * Deterministic: every sum runs in a fixed order.
+ */
+MSA_API int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
+                             const void* k_idx, const int32_t* block_idx, const float* lse,
+                             const float* index_lse, float softmax_scale, float index_scale,
+                             const float* dkl_rows, float kl_weight, void* dq_idx, void* dk_idx, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Workspace bytes the given entry point needs for these sizes; 0 if the sizes
  * are invalid or the op needs none. Pure host arithmetic. */

@@ -52,7 +52,8 @@ import numpy as np
 __all__ = [
     "local_block", "visible_block_scores", "select_blocks", "index_topk_rows",
     "index_topk", "token_set", "token_count", "attention_rows", "sparse_attention",
-    "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "kl_backward", "map_positions",
+    "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "kl_backward", "kl_dq_idx_rows",
+    "map_positions",
 ]
 
 
@@ -454,6 +455,35 @@ def kl_backward(q, k, q_idx, k_idx, block_idx, Bk, dkl_rows=None, scale=None, in
                 dqi[b, i, g] = w[b, g, i] * a
                 dki[b, T] += w[b, g, i] * c
     return dqi, dki
+
+
+def kl_dq_idx_rows(q, k, k_idx, block_idx_rows, positions, Bk, w_rows=None, scale=None, index_scale=None,
+                   q_rows=None, qi_rows=None):
+    """dq_idx at the given (b, i) positions only ([M, Hkv, Di], float64): a
+    row's dq_idx depends on its own selection alone. ``w_rows`` [M, Hkv] are the
+    rows' loss weights (1 if None); ``q_rows`` [M, Hq, D] and ``qi_rows``
+    [M, Hkv, Di] are the query and index-query rows at the positions."""
+    kk, ki = _arr(k), _arr(k_idx)
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    if q_rows is None:
+        q_rows = _arr(q)[positions[:, 0], positions[:, 1]]
+    q_rows, qi_rows = _arr(q_rows), _arr(qi_rows)
+    Hq, D = q_rows.shape[1], q_rows.shape[2]
+    Hkv, Di = kk.shape[2], ki.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    index_scale = (1.0 / math.sqrt(Di) if index_scale is None or index_scale <= 0
+                   else float(index_scale))
+    out = np.zeros((len(positions), Hkv, Di))
+    for r, (b, i) in enumerate(positions):
+        for g in range(Hkv):
+            T = token_set(block_idx_rows[r, g], int(i), Bk)
+            a, _ = _kl_row_backward(np.asarray(q_rows[r, g * G:(g + 1) * G], dtype=np.float64),
+                                    np.asarray(kk[b, T, g], dtype=np.float64),
+                                    np.asarray(qi_rows[r, g], dtype=np.float64),
+                                    np.asarray(ki[b, T], dtype=np.float64), scale, index_scale)
+            out[r, g] = (1.0 if w_rows is None else float(w_rows[r, g])) * a
+    return out
 
 
 def map_positions(fn, positions, row_arrays=(), workers=1, chunk=256):

@@ -19,7 +19,8 @@ torch.Generator on the target device):
   and rounded to the workload dtype (round-to-nearest-even for bf16).
 """
 from .configs import CONFIGS, Workload, get_workload
-from .inputs import make_inputs, make_grad_output, sample_rows, edge_positions
+from .inputs import make_inputs, make_grad_output, make_row_weights, sample_rows, edge_positions
 
-__all__ = ["CONFIGS", "Workload", "get_workload", "make_inputs", "make_grad_output", "sample_rows",
+__all__ = ["CONFIGS", "Workload", "get_workload", "make_inputs", "make_grad_output", "make_row_weights",
+           "sample_rows",
            "edge_positions"]

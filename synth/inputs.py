@@ -103,3 +103,12 @@ def make_grad_output(w: Workload, device="cpu", seed=None):
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     return _randn((w.batch, w.seqlen, w.q_heads, w.head_dim), gen, device, torch_dtype(w.dtype))
+
+
+def make_row_weights(w: Workload, device="cpu", seed=None):
+    """Seeded per-row loss weights [B, Hkv, N] for the KL backward, uniform on
+    [0.5, 2), fp32, from their own generator (seed + 2000)."""
+    seed = (w.seed if seed is None else seed) + 2000
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return 0.5 + 1.5 * torch.rand((w.batch, w.kv_heads, w.seqlen), generator=gen, device=device)

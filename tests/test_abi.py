@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.msa_abi_version() == 1
+    assert lib.msa_abi_version() == 2
     for s in range(7):
         assert lib.msa_strerror(s)
     assert lib.msa_strerror(99) == b"unknown status"
@@ -74,7 +74,7 @@ def _kl(lib, d, ptrs=None, ws=None, nws=0):
     p = dict(q=FAKE, k=FAKE, qi=FAKE, ki=FAKE, bi=FAKE, lse=FAKE, rows=FAKE, sum=FAKE)
     p.update(ptrs or {})
     return lib.msa_kl_align_fwd(ctypes.byref(d), p["q"], p["k"], p["qi"], p["ki"], p["bi"], p["lse"],
-                                0.0, 0.0, p["rows"], p["sum"], ws, nws, None)
+                                0.0, 0.0, p["rows"], p["sum"], p.get("ilse"), ws, nws, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -129,6 +129,31 @@ def test_backward_rejects_before_any_launch(lib):
     none = {n: None for n in ("q", "k", "v", "bi", "o", "lse", "do", "dq", "dk", "dv")}
     assert _bwd(lib, _dims(batch=0), ptrs=none, ws=None, nws=0) == 0
     assert _bwd(lib, _dims(seqlen=0), ptrs=none, ws=None, nws=0) == 0
+
+
+def _klb(lib, d, ptrs=None, ws=FAKE, nws=1 << 50):
+    p = dict(q=FAKE, k=FAKE, qi=FAKE, ki=FAKE, bi=FAKE, lse=FAKE, ilse=FAKE, w=None, dqi=FAKE, dki=FAKE)
+    p.update(ptrs or {})
+    return lib.msa_kl_align_bwd(ctypes.byref(d), p["q"], p["k"], p["qi"], p["ki"], p["bi"], p["lse"], p["ilse"],
+                                0.0, 0.0, p["w"], 1.0, p["dqi"], p["dki"], ws, nws, None)
+
+
+def test_kl_backward_rejects_before_any_launch(lib):
+    d = _dims()
+    need = lib.msa_workspace_bytes(ctypes.byref(d), msa.MSA_OP_KL_BWD)
+    assert need > 0
+    assert _klb(lib, _dims(dtype=msa.MSA_F32)) == 3
+    assert _klb(lib, _dims(index_dim=96)) == 3
+    for name in ("q", "k", "qi", "ki", "bi", "lse", "ilse", "dqi", "dki"):
+        assert _klb(lib, d, ptrs={name: None}) == 1, name
+        assert _klb(lib, d, ptrs={name: MISALIGNED}) == 4, name
+    assert _klb(lib, d, ptrs={"w": MISALIGNED}) == 4
+    assert _klb(lib, d, ws=None, nws=0) == 5
+    assert _klb(lib, d, nws=need - 1) == 5
+    none = {n: None for n in ("q", "k", "qi", "ki", "bi", "lse", "ilse", "dqi", "dki")}
+    assert _klb(lib, _dims(seqlen=0), ptrs=none, ws=None, nws=0) == 0
+    # the forward's optional student-LSE output: 4-byte alignment only
+    assert _kl(lib, _dims(), ptrs={"ilse": ctypes.c_void_p(0x1002)}) == 4
 
 
 def test_index_ignores_attention_fields(lib):

@@ -581,3 +581,16 @@ def test_kl_backward_sum_rule_and_mistakes(monkeypatch):
         monkeypatch.setattr(O, "_kl_row_backward", bad)
         assert not ok(), bad.__name__
     monkeypatch.setattr(O, "_kl_row_backward", real)
+
+
+def test_kl_dq_idx_rows_is_the_full_backward_at_those_rows():
+    N, Bk, k, Hkv, G, D, Di = 40, 8, 3, 2, 2, 8, 4
+    q_idx, k_idx, q, kk, vv = _rand_case(24, N=N, Hkv=Hkv, G=G, D=D, Di=Di, Bk=Bk)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    w = np.random.default_rng(25).uniform(0.5, 2.0, size=(1, Hkv, N))
+    full, _ = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk, dkl_rows=w)
+    pos = np.array([(0, i) for i in range(0, N, 3)])
+    rows = bi.transpose(0, 2, 1, 3)[0, pos[:, 1]]
+    got = O.kl_dq_idx_rows(q, kk, k_idx, rows, pos, Bk, w_rows=w[0][:, pos[:, 1]].T,
+                           qi_rows=q_idx[0, pos[:, 1]])
+    np.testing.assert_allclose(got, full[0, pos[:, 1]], atol=1e-14, rtol=0)
