@@ -68,6 +68,18 @@ def kl_flops(w):
     return (2.0 * D * Hkv * G + 2.0 * Di * Hkv) * B * tokens
 
 
+def kl_backward_flops(w):
+    """F_KL_bwd = (2·D·Hq + 3 · 2·Di·Hkv)·B·sum_i |T_i|: the teacher scores of the
+    G heads, and per (position, token) the student score, its dk_idx and its
+    dq_idx products."""
+    B, N, Hkv, G, D, Di, Bk, k = (w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim,
+                                  w.index_dim, w.block_size, w.topk)
+    i = np.arange(N, dtype=np.int64)
+    L = i // Bk
+    tokens = float(((np.minimum(k, L + 1) - 1) * Bk + (i % Bk) + 1).sum())
+    return (2.0 * D * Hkv * G + 6.0 * Di * Hkv) * B * tokens
+
+
 def source_digest(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -342,6 +354,29 @@ def main():
         fk = kl_flops(w)
         out["kl_align"] = {"ms": kl_ms, "algorithmic_tflop": fk / 1e12, "tflops": fk / (kl_ms * 1e-3) / 1e12,
                            "frac_of_peak": fk / (kl_ms * 1e-3) / 1e12 / peak, "kl_sum": float(kl_sum.item())}
+        if args.bwd:
+            # KL-term backward (index-branch gradients) on the same rows, unit row weights.
+            ilse = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev)
+            msa.kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], block_idx, lse, kl_rows=kl_rows,
+                             kl_sum=kl_sum, workspace=kws, index_lse=ilse)
+            kbws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_KL_BWD)), dtype=torch.uint8,
+                               device=dev)
+            dqi, dki = torch.empty_like(x["q_idx"]), torch.empty_like(x["k_idx"])
+
+            def klb():
+                msa.kl_align_bwd(x["q"], x["k"], x["q_idx"], x["k_idx"], block_idx, lse, ilse, dq_idx=dqi,
+                                 dk_idx=dki, workspace=kbws)
+            klb()
+            for e in kev:
+                e[0].record(stream)
+                klb()
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            klb_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
+            fkb = kl_backward_flops(w)
+            out["kl_align_bwd"] = {"ms": klb_ms, "algorithmic_tflop": fkb / 1e12,
+                                   "tflops": fkb / (klb_ms * 1e-3) / 1e12,
+                                   "frac_of_peak": fkb / (klb_ms * 1e-3) / 1e12 / peak}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

@@ -95,9 +95,9 @@ __device__ __forceinline__ void kl_stage_store(const KlUnit& su, KlBwdLds<D, DI>
             u32x4 y;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t lo = (su.x[2 * w][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
-                const uint32_t hi = (su.x[2 * w + 1][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
-                y[w] = lo | (hi << 16);
+                // the 16-bit element dd of rows 2w and 2w + 1 (low and high half of the word)
+                y[w] = __builtin_amdgcn_perm(su.x[2 * w + 1][dd / 2], su.x[2 * w][dd / 2],
+                                         dd % 2 ? 0x07060302u : 0x05040100u);
             }
             *reinterpret_cast<u32x4*>(sh.qit + L::ICT::offset(dc * 8 + dd, 2 * c + h)) = y;
         }
@@ -300,9 +300,11 @@ __global__ __launch_bounds__(256, 1) void kl_bwd_kernel(
             uint16_t* dul = reinterpret_cast<uint16_t*>(sh.du);
             const int pk = perm16(key);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; r += 2) {   // rows m and m + 1: one conversion, two 16-bit stores
                 const int m = 8 * (r / 4) + 4 * half + r % 4;
-                dul[L::DuT::offset(m, pk * 2) / 2] = f32_to_bf16(du[r]);
+                const uint32_t v2 = pack_bf16x2(du[r], du[r + 1]);
+                dul[L::DuT::offset(m, pk * 2) / 2] = (uint16_t)(v2 & 0xffffu);
+                dul[L::DuT::offset(m + 1, pk * 2) / 2] = (uint16_t)(v2 >> 16);
             }
         }
         __syncthreads();

@@ -70,17 +70,27 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16_t* __restrict
     }
 }
 
-// LDS of one work-group: the current 32-row tile (natural and transposed),
-// the dS tile, per-row scalars.
+// One staged 32-row tile: Q and dO natural and transposed, per-row scalars.
 template <int D>
-struct BwdLds {
+struct BwdTile {
     using RowT = SwzTile<bf16_t, D>;        // [32 rows][D]
     using ColT = ColTile<D>;                // [D][32 rows, permuted]
-    using DsT = SwzTile<bf16_t, kBlock>;    // [32 rows][128 keys, permuted]
-    static constexpr int ROWB = 32 * RowT::ROWB, COLB = ColT::BYTES, DSB = 32 * DsT::ROWB;
-    unsigned char q[ROWB], dout[ROWB], qt[COLB], dot[COLB], ds[DSB];
+    static constexpr int ROWB = 32 * RowT::ROWB, COLB = ColT::BYTES;
+    unsigned char q[ROWB], dout[ROWB], qt[COLB], dot[COLB];
     float lse2[32], dl[32];
     int pos[32], slot[32];
+};
+
+// LDS of one work-group: two tile buffers (tile t is computed from one while
+// tile t + 1 is written into the other), the dS tile, the item's entries.
+template <int D>
+struct BwdLds {
+    using RowT = SwzTile<bf16_t, D>;
+    using ColT = ColTile<D>;
+    using DsT = SwzTile<bf16_t, kBlock>;    // [32 rows][128 keys, permuted]
+    static constexpr int DSB = 32 * DsT::ROWB;
+    BwdTile<D> tile[2];
+    unsigned char ds[DSB];
     int entries[kSegBwd];   // the item's list entries (non-local items)
 };
 
@@ -118,15 +128,15 @@ __device__ __forceinline__ void stage_load(StageUnit& su, const BwdItem<LOCAL>& 
 // LDS writes of a staged unit: 8 natural 16-byte rows and 8 transposed
 // 16-byte chunks (one per dim).
 template <int D>
-__device__ __forceinline__ void stage_store(const StageUnit& su, BwdLds<D>& sh, int u) {
+__device__ __forceinline__ void stage_store(const StageUnit& su, BwdTile<D>& sh, int u) {
     constexpr int DC = D / 8;
     const int tensor = u / (4 * DC), v = u % (4 * DC);
     const int grp = v & 3, dc = v >> 2;   // the row group varies fastest across lanes
     const int c = grp >> 1, h = grp & 1;
     unsigned char* nat = tensor ? sh.dout : sh.q;
     unsigned char* tr = tensor ? sh.dot : sh.qt;
-    using RowT = typename BwdLds<D>::RowT;
-    using ColT = typename BwdLds<D>::ColT;
+    using RowT = typename BwdTile<D>::RowT;
+    using ColT = typename BwdTile<D>::ColT;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int m = 16 * c + 8 * (e / 4) + 4 * h + e % 4;
@@ -137,9 +147,9 @@ __device__ __forceinline__ void stage_store(const StageUnit& su, BwdLds<D>& sh, 
         u32x4 y;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = (su.x[2 * w][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
-            const uint32_t hi = (su.x[2 * w + 1][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
-            y[w] = lo | (hi << 16);
+            // the 16-bit element dd of rows 2w and 2w + 1 (low and high half of the word)
+            y[w] = __builtin_amdgcn_perm(su.x[2 * w + 1][dd / 2], su.x[2 * w][dd / 2],
+                                         dd % 2 ? 0x07060302u : 0x05040100u);
         }
         *reinterpret_cast<u32x4*>(tr + ColT::offset(dc * 8 + dd, 2 * c + h)) = y;
     }
@@ -259,46 +269,66 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
     // Every load issued so far (the key block's operands, the first two tiles)
     // completes here, so the loop below only ever waits for its own prefetches.
     __builtin_amdgcn_s_waitcnt(0);
-
-    for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();   // the previous tile's LDS reads are done
-        const bool mine = (t & 1) == par;
-        if (mine) {
-            if (u < NSTAGE) stage_store<D>(su, sh, u);
-            const int m = 127 - u;
-            if (m < 32) {
-                sh.lse2[m] = r_lse * kLog2e;
-                sh.dl[m] = r_dl;
-                sh.pos[m] = r_pos;
-                sh.slot[m] = r_slot;
-            }
+    // Staging of tile t into buffer t % 2 by the threads of its parity, who
+    // then request tile t + 2.
+    auto commit = [&](int t) {
+        BwdTile<D>& tb = sh.tile[t & 1];
+        if (u < NSTAGE) stage_store<D>(su, tb, u);
+        const int m = 127 - u;
+        if (m < 32) {
+            tb.lse2[m] = r_lse * kLog2e;
+            tb.dl[m] = r_dl;
+            tb.pos[m] = r_pos;
+            tb.slot[m] = r_slot;
         }
-        __syncthreads();
-        if (mine && t + 2 < ntiles) {   // tile t + 2's global loads overlap tiles t and t + 1
+        if (t + 2 < ntiles) {
             if (u < NSTAGE) stage_load<D, G, LOCAL>(su, it, t + 2, u, q, dout, N, Hq);
             row_load(t + 2);
         }
+    };
+    if (par == 0 && ntiles > 0) commit(0);
 
-        // S = Q K_w^T and dP = dO V_w^T: lane = key, accumulators = rows.
+    for (int t = 0; t < ntiles; ++t) {
+        // Tile t is complete in its buffer; the other buffer's readers (tile
+        // t - 1) and the dS readers are done.
+        __syncthreads();
+        if (t + 1 < ntiles && ((t + 1) & 1) == par) commit(t + 1);   // overlaps tile t's math
+        const BwdTile<D>& sh_t = sh.tile[t & 1];
+
+        // S = Q K_w^T and dP = dO V_w^T: lane = key, accumulators = rows. The
+        // phase's LDS operands are all requested before its first product.
         floatx16 s = zero16(), dp = zero16();
+        {
+            Op8<bf16_t> a[KS], b[KS];
 #pragma unroll
-        for (int sl = 0; sl < KS; ++sl) {
-            Op8<bf16_t> a, b;
-            a.load(sh.q + BwdLds<D>::RowT::offset(col, (16 * sl + 8 * half) * 2));
-            b.load(sh.dout + BwdLds<D>::RowT::offset(col, (16 * sl + 8 * half) * 2));
-            mma16(s, a, kop[sl]);
-            mma16(dp, b, vop[sl]);
+            for (int sl = 0; sl < KS; ++sl) {
+                a[sl].load(sh_t.q + BwdLds<D>::RowT::offset(col, (16 * sl + 8 * half) * 2));
+                b[sl].load(sh_t.dout + BwdLds<D>::RowT::offset(col, (16 * sl + 8 * half) * 2));
+            }
+#pragma unroll
+            for (int sl = 0; sl < KS; ++sl) {
+                mma16(s, a[sl], kop[sl]);
+                mma16(dp, b[sl], vop[sl]);
+            }
+        }
+        float rl[16], rd[16];
+        int rp[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 8 * (r / 4) + 4 * half + r % 4;
+            rl[r] = sh_t.lse2[m];
+            rd[r] = sh_t.dl[m];
+            if constexpr (LOCAL) rp[r] = sh_t.pos[m];
         }
         float p[16], ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int m = 8 * (r / 4) + 4 * half + r % 4;
-            float pr = exp2_hw(fmaf(s[r], scale_log2, -sh.lse2[m]));
+            float pr = exp2_hw(fmaf(s[r], scale_log2, -rl[r]));
             if constexpr (LOCAL) {
-                if (it.q0 + key > sh.pos[m]) pr = 0.f;   // also the rows past the item (pos = -1)
+                if (it.q0 + key > rp[r]) pr = 0.f;   // also the rows past the item (pos = -1)
             }
             p[r] = pr;
-            ds[r] = pr * (dp[r] - sh.dl[m]);
+            ds[r] = pr * (dp[r] - rd[r]);
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the tile's two 16-row slices.
 #pragma unroll
@@ -306,13 +336,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             Op8<bf16_t> bp, bds;
             PType<bf16_t>::pack(bp, p + 8 * sl);
             PType<bf16_t>::pack(bds, ds + 8 * sl);
+            Op8<bf16_t> a[DT], b[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                Op8<bf16_t> a, b;
-                a.load(sh.dot + BwdLds<D>::ColT::offset(32 * dt + col, 2 * sl + half));
-                b.load(sh.qt + BwdLds<D>::ColT::offset(32 * dt + col, 2 * sl + half));
-                mma16(dvt[dt], a, bp);
-                mma16(dkt[dt], b, bds);
+                a[dt].load(sh_t.dot + BwdLds<D>::ColT::offset(32 * dt + col, 2 * sl + half));
+                b[dt].load(sh_t.qt + BwdLds<D>::ColT::offset(32 * dt + col, 2 * sl + half));
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                mma16(dvt[dt], a[dt], bp);
+                mma16(dkt[dt], b[dt], bds);
             }
         }
         // dS -> LDS as [row][permuted key] for the dQ product.
@@ -320,26 +353,33 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             uint16_t* dsl = reinterpret_cast<uint16_t*>(sh.ds);
             const int pk = perm16(key);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; r += 2) {   // rows m and m + 1: one conversion, two 16-bit stores
                 const int m = 8 * (r / 4) + 4 * half + r % 4;
-                dsl[BwdLds<D>::DsT::offset(m, pk * 2) / 2] = f32_to_bf16(ds[r]);
+                const uint32_t v2 = pack_bf16x2(ds[r], ds[r + 1]);
+                dsl[BwdLds<D>::DsT::offset(m, pk * 2) / 2] = (uint16_t)(v2 & 0xffffu);
+                dsl[BwdLds<D>::DsT::offset(m + 1, pk * 2) / 2] = (uint16_t)(v2 >> 16);
             }
         }
         __syncthreads();
         // dQ^T (dims 32w.., rows) = K^T dS^T over the block's 128 keys.
         if (w < DT) {
-            floatx16 acc = zero16();
+            // two accumulation chains (even and odd 16-key slices)
+            floatx16 acc = zero16(), acc2 = zero16();
+            Op8<bf16_t> b[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                Op8<bf16_t> b;
-                b.load(sh.ds + BwdLds<D>::DsT::offset(col, (16 * c + 8 * half) * 2));
-                mma16(acc, ktop[c], b);
+            for (int c = 0; c < 8; ++c) b[c].load(sh.ds + BwdLds<D>::DsT::offset(col, (16 * c + 8 * half) * 2));
+#pragma unroll
+            for (int c = 0; c < 8; c += 2) {
+                mma16(acc, ktop[c], b[c]);
+                mma16(acc2, ktop[c + 1], b[c + 1]);
             }
-            const int i = sh.pos[col];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
+            const int i = sh_t.pos[col];
             if (i >= 0) {
                 // partial of (row (b, g, i), slot), head col % G: [G][D] bf16, each 32-dim slice lane-major
                 // (element 32w + 16h + r holds dim 32w + 8*(r/4) + 4h + r%4)
-                bf16_t* dst = dq_part + ((((size_t)it.b * Hkv + it.g) * N + i) * topk + sh.slot[col]) * G * D +
+                bf16_t* dst = dq_part + ((((size_t)it.b * Hkv + it.g) * N + i) * topk + sh_t.slot[col]) * G * D +
                               (size_t)(col % G) * D + 32 * w + 16 * half;
                 u32x4 w0, w1;
 #pragma unroll
