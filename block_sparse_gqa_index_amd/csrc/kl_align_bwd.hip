@@ -31,15 +31,28 @@
 
 namespace msa {
 
+// One staged 32-row tile: query rows, index-query rows (natural and
+// transposed), per-row scalars.
 template <int D, int DI>
-struct KlBwdLds {
+struct KlTile {
     using QT = SwzTile<bf16_t, D>;        // [32 rows][D]
     using IT = SwzTile<bf16_t, DI>;       // [32 rows][DI]
     using ICT = ColTile<DI>;              // [DI][32 rows, permuted]
-    using DuT = SwzTile<bf16_t, kBlock>;  // [32 rows][128 keys, permuted]
-    unsigned char q[32 * QT::ROWB], qi[32 * IT::ROWB], qit[ICT::BYTES], du[32 * DuT::ROWB];
+    unsigned char q[32 * QT::ROWB], qi[32 * IT::ROWB], qit[ICT::BYTES];
     float lse2[32], lseu2[32], w[32];
     int pos[32], slot[32];
+};
+
+// Two tile buffers (tile t computed from one while tile t + 1 is written into
+// the other), the dU tile, the item's entries.
+template <int D, int DI>
+struct KlBwdLds {
+    using QT = SwzTile<bf16_t, D>;
+    using IT = SwzTile<bf16_t, DI>;
+    using ICT = ColTile<DI>;
+    using DuT = SwzTile<bf16_t, kBlock>;  // [32 rows][128 keys, permuted]
+    KlTile<D, DI> tile[2];
+    unsigned char du[32 * DuT::ROWB];
     int entries[kSegBwd];
 };
 
@@ -76,9 +89,9 @@ __device__ __forceinline__ void kl_stage_load(KlUnit& su, const BwdItem<LOCAL>& 
 }
 
 template <int D, int DI>
-__device__ __forceinline__ void kl_stage_store(const KlUnit& su, KlBwdLds<D, DI>& sh, int u) {
+__device__ __forceinline__ void kl_stage_store(const KlUnit& su, KlTile<D, DI>& sh, int u) {
     constexpr int NQ = 4 * (D / 8);
-    using L = KlBwdLds<D, DI>;
+    using L = KlTile<D, DI>;
     const bool isq = u < NQ;
     const int v = isq ? u : u - NQ;
     const int grp = v & 3, dc = v >> 2;
@@ -226,48 +239,54 @@ __global__ __launch_bounds__(256, 1) void kl_bwd_kernel(
     };
     if (par < ntiles) row_load(par);
     __builtin_amdgcn_s_waitcnt(0);
-
-    for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();
-        const bool mine = (t & 1) == par;
-        if (mine) {
-            if (u < NST) kl_stage_store<D, DI>(su, sh, u);
-            const int m = 127 - u;
-            if (m < 32) {
-                sh.lse2[m] = r_lse * kLog2e;
-                sh.lseu2[m] = r_lseu * kLog2e;
-                sh.w[m] = r_w * kl_weight * iscale;
-                sh.pos[m] = r_pos;
-                sh.slot[m] = r_slot;
-            }
+    // Staging of tile t into buffer t % 2 by the threads of its parity, who
+    // then request tile t + 2.
+    auto commit = [&](int t) {
+        KlTile<D, DI>& tb = sh.tile[t & 1];
+        if (u < NST) kl_stage_store<D, DI>(su, tb, u);
+        const int m = 127 - u;
+        if (m < 32) {
+            tb.lse2[m] = r_lse * kLog2e;
+            tb.lseu2[m] = r_lseu * kLog2e;
+            tb.w[m] = r_w * kl_weight * iscale;
+            tb.pos[m] = r_pos;
+            tb.slot[m] = r_slot;
         }
-        __syncthreads();
-        if (mine && t + 2 < ntiles) {
+        if (t + 2 < ntiles) {
             if (u < NST) kl_stage_load<D, DI, G, LOCAL>(su, it, t + 2, u, q, q_idx, N, Hkv);
             row_load(t + 2);
         }
+    };
+    if (par == 0 && ntiles > 0) commit(0);
+
+    for (int t = 0; t < ntiles; ++t) {
+        // Tile t is complete in its buffer; the other buffer's readers (tile
+        // t - 1) and the dU readers are done.
+        __syncthreads();
+        if (t + 1 < ntiles && ((t + 1) & 1) == par) commit(t + 1);   // overlaps tile t's math
+        const KlTile<D, DI>& sh_t = sh.tile[t & 1];
 
         // S = Q K_w^T (teacher scores) and U = Q_idx K_idx,w^T (student logits / c).
         floatx16 s = zero16(), uu = zero16();
 #pragma unroll
         for (int sl = 0; sl < D / 16; ++sl) {
             Op8<bf16_t> a;
-            a.load(sh.q + L::QT::offset(col, (16 * sl + 8 * half) * 2));
+            a.load(sh_t.q + L::QT::offset(col, (16 * sl + 8 * half) * 2));
             mma16(s, a, kop[sl]);
         }
 #pragma unroll
         for (int sl = 0; sl < DI / 16; ++sl) {
             Op8<bf16_t> a;
-            a.load(sh.qi + L::IT::offset(col, (16 * sl + 8 * half) * 2));
+            a.load(sh_t.qi + L::IT::offset(col, (16 * sl + 8 * half) * 2));
             mma16(uu, a, kiop[sl]);
         }
         float p[16], du[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = 8 * (r / 4) + 4 * half + r % 4;
-            float pr = exp2_hw(fmaf(s[r], scale_log2, -sh.lse2[m]));
+            float pr = exp2_hw(fmaf(s[r], scale_log2, -sh_t.lse2[m]));
             if constexpr (LOCAL) {
-                if (it.q0 + key > sh.pos[m]) pr = 0.f;
+                if (it.q0 + key > sh_t.pos[m]) pr = 0.f;
             }
             p[r] = pr;
         }
@@ -275,11 +294,11 @@ __global__ __launch_bounds__(256, 1) void kl_bwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = 8 * (r / 4) + 4 * half + r % 4;
-            float st = exp2_hw(fmaf(uu[r], iscale_log2, -sh.lseu2[m]));
+            float st = exp2_hw(fmaf(uu[r], iscale_log2, -sh_t.lseu2[m]));
             if constexpr (LOCAL) {
-                if (it.q0 + key > sh.pos[m]) st = 0.f;
+                if (it.q0 + key > sh_t.pos[m]) st = 0.f;
             }
-            du[r] = sh.w[m] * (st - p[r]);
+            du[r] = sh_t.w[m] * (st - p[r]);
         }
         // dk_idx^T += Q_idx^T (dU / G): every position's G replicated rows count once.
 #pragma unroll
@@ -292,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void kl_bwd_kernel(
 #pragma unroll
             for (int dt = 0; dt < DIT; ++dt) {
                 Op8<bf16_t> a;
-                a.load(sh.qit + L::ICT::offset(32 * dt + col, 2 * sl + half));
+                a.load(sh_t.qit + L::ICT::offset(32 * dt + col, 2 * sl + half));
                 mma16(dkit[dt], a, b);
             }
         }
@@ -318,9 +337,9 @@ __global__ __launch_bounds__(256, 1) void kl_bwd_kernel(
                 b.load(sh.du + L::DuT::offset(col, (16 * c + 8 * half) * 2));
                 mma16(acc, kitop[c], b);
             }
-            const int i = sh.pos[col];
+            const int i = sh_t.pos[col];
             if (i >= 0 && col % G == 0) {
-                bf16_t* dst = dqi_part + ((((size_t)it.b * Hkv + it.g) * N + i) * topk + sh.slot[col]) * DI +
+                bf16_t* dst = dqi_part + ((((size_t)it.b * Hkv + it.g) * N + i) * topk + sh_t.slot[col]) * DI +
                               32 * w + 16 * half;
                 u32x4 w0, w1;
 #pragma unroll
