@@ -1,5 +1,6 @@
-"""Plain CPU oracle of the MSA (MiniMax Sparse Attention) forward path and of
-the main branch's backward over the cached block indices.
+"""Plain CPU oracle of the MSA (MiniMax Sparse Attention) forward path, of the
+backward over the cached block indices, and of decoding (one new query per
+sequence against a cache).
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this module. The product path (the HIP
@@ -40,7 +41,12 @@ Readings of points the pages leave open (each listed in the design notes):
     <dO, O> (dO given); every key's gradient sums the contributions of all rows
     that selected its block;
   * the KL term's backward holds the teacher fixed (gradient stopped at the
-    index branch input) and reaches q_idx and k_idx only.
+    index branch input) and reaches q_idx and k_idx only;
+  * decoding appends one token per sequence: sequence b holds n_b cached
+    tokens (positions 0 .. n_b - 1, the new one last) and its new query is the
+    query of position n_b - 1, so its selection and attention are exactly the
+    forward's row n_b - 1; cache slots at or past n_b are never read; a length
+    outside [1, capacity] gives an all -1 selection, O = 0 and LSE = -inf.
 
 Parity: every function here is pinned by tests that do not re-use its code
 (brute force, closed forms, torch's dense SDPA, scipy's entropy, invariants).
@@ -53,7 +59,7 @@ __all__ = [
     "local_block", "visible_block_scores", "select_blocks", "index_topk_rows",
     "index_topk", "token_set", "token_count", "attention_rows", "sparse_attention",
     "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "kl_backward", "kl_dq_idx_rows",
-    "map_positions",
+    "map_positions", "decode_index_topk", "decode_attention",
 ]
 
 
@@ -484,6 +490,55 @@ def kl_dq_idx_rows(q, k, k_idx, block_idx_rows, positions, Bk, w_rows=None, scal
                                     np.asarray(ki[b, T], dtype=np.float64), scale, index_scale)
             out[r, g] = (1.0 if w_rows is None else float(w_rows[r, g])) * a
     return out
+
+
+def _decode_positions(seqlens, capacity):
+    """(b, n_b - 1) for the sequences whose length is in [1, capacity], and
+    their batch indices."""
+    n = np.asarray(seqlens, dtype=np.int64).reshape(-1)
+    ok = np.nonzero((n >= 1) & (n <= capacity))[0]
+    return np.stack([ok, n[ok] - 1], axis=1).reshape(-1, 2), ok
+
+
+def decode_index_topk(q_idx, k_idx, seqlens, Bk, k):
+    """Block selection of one new query per sequence against a cache.
+
+    [P2] "Cómo funcionan las dos ramas" and "El codiseño del kernel" (the same
+    selection as the forward; only the query row differs); [P3] (the block
+    indices are all a sparse layer caches). q_idx [B, Hkv, Di] holds the new
+    token's index queries, k_idx [B, C, Di] the index-key cache, seqlens [B]
+    the cached lengths n_b (new token included). The query is position
+    i = n_b - 1. Returns int32 [B, Hkv, k]; rows with n_b outside [1, C] are -1.
+    """
+    qi = _arr(q_idx)
+    ka = _arr(k_idx)
+    B, Hkv = qi.shape[0], qi.shape[1]
+    out = np.full((B, Hkv, k), -1, dtype=np.int32)
+    pos, ok = _decode_positions(seqlens, ka.shape[1])
+    if len(ok):
+        out[ok] = index_topk_rows(None, ka, pos, Bk, k, q_rows=qi[ok])
+    return out
+
+
+def decode_attention(q, k, v, seqlens, block_idx, Bk, scale=None):
+    """Main-branch attention of one new query per sequence over its selected
+    blocks of the cache ([P2] "Cómo funcionan las dos ramas", as for
+    ``attention_rows`` at position i = n_b - 1).
+
+    q [B, Hq, D] the new queries, k/v [B, C, Hkv, D] the caches, seqlens [B],
+    block_idx int [B, Hkv, k]. Returns (O [B, Hq, D], LSE [B, Hq]) in float64;
+    rows with n_b outside [1, C] get O = 0 and LSE = -inf.
+    """
+    qa = _arr(q)
+    kk = _arr(k)
+    B, Hq, D = qa.shape
+    O = np.zeros((B, Hq, D))
+    LSE = np.full((B, Hq), -np.inf)
+    pos, ok = _decode_positions(seqlens, kk.shape[1])
+    if len(ok):
+        bi = np.asarray(block_idx)[ok]
+        O[ok], LSE[ok] = attention_rows(None, kk, v, bi, pos, Bk, scale, q_rows=qa[ok])
+    return O, LSE
 
 
 def map_positions(fn, positions, row_arrays=(), workers=1, chunk=256):

@@ -17,10 +17,14 @@ torch.Generator on the target device):
   tokens (so a learned indexer's "stripe" pattern shows up in the selection).
 * Q ``[B, N, Hq, D]``, K and V ``[B, N, Hkv, D]``: standard normal, drawn in fp32
   and rounded to the workload dtype (round-to-nearest-even for bf16).
+* Decode batches: caches of capacity N per sequence drawn as above, one new
+  query per sequence, cached lengths uniform on [1, N] (``make_decode_inputs``).
 """
-from .configs import CONFIGS, Workload, get_workload
-from .inputs import make_inputs, make_grad_output, make_row_weights, sample_rows, edge_positions
+from .configs import CONFIGS, DECODE_CONFIGS, Workload, get_workload
+from .inputs import (make_inputs, make_decode_inputs, make_grad_output, make_row_weights, sample_rows,
+                     edge_positions)
 
-__all__ = ["CONFIGS", "Workload", "get_workload", "make_inputs", "make_grad_output", "make_row_weights",
+__all__ = ["CONFIGS", "DECODE_CONFIGS", "Workload", "get_workload", "make_inputs", "make_decode_inputs",
+           "make_grad_output", "make_row_weights",
            "sample_rows",
            "edge_positions"]

@@ -58,3 +58,13 @@ CONFIGS = {
 
 def get_workload(name: str) -> Workload:
     return CONFIGS[name]
+
+
+# Decode batches: ``batch`` sequences, a cache of ``seqlen`` tokens each (the
+# capacity; the cached lengths are drawn uniformly on [1, seqlen]), one new
+# query per sequence, the model sizes of the 128K workload.
+DECODE_CONFIGS = {
+    "decode_n8k_b8": Workload("decode_n8k_b8", 8, 8192, 8, 8, 128, 128),
+    "decode_n128k_b64": Workload("decode_n128k_b64", 64, 131072, 8, 8, 128, 128, stripe_frac=0.01,
+                                 stripe_bias=3.0),
+}

@@ -112,3 +112,41 @@ def make_row_weights(w: Workload, device="cpu", seed=None):
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     return 0.5 + 1.5 * torch.rand((w.batch, w.kv_heads, w.seqlen), generator=gen, device=device)
+
+
+def make_decode_inputs(w: Workload, device="cpu", seed=None, lengths=None):
+    """Seeded decode batch: ``w.batch`` sequences with a cache of capacity
+    ``w.seqlen`` tokens and one new query each.
+
+    Draw order from one generator: k_idx cache [B, C, Di] (integers, as for the
+    forward, with the same stripe rule), stripes, K and V caches [B, C, Hkv, D]
+    (standard normal), the new index queries q_idx [B, Hkv, Di] (integers) and
+    queries q [B, Hq, D] (standard normal). Cache slots past a sequence's length
+    hold random values too (they must never be read). ``lengths`` (cached
+    tokens per sequence, the new one included) default to integers uniform on
+    [1, C] from their own generator (seed + 3000); returned as int32 on
+    ``device`` under 'seqlens'.
+    """
+    seed = w.seed if seed is None else seed
+    dt = torch_dtype(w.dtype)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    B, C, Hkv, G, D, Di, Bk = (w.batch, w.seqlen, w.kv_heads, w.group_size,
+                               w.head_dim, w.index_dim, w.block_size)
+    out = {}
+    k_idx = _randint((B, C, Di), gen, device, dt, w.index_absmax)
+    stripes = stripe_blocks(w, gen, device)
+    for j in stripes.tolist():
+        k_idx[:, j * Bk:min(C, (j + 1) * Bk), :] += w.stripe_bias
+    out["k_idx"] = k_idx
+    out["stripes"] = stripes
+    out["k"] = _randn((B, C, Hkv, D), gen, device, dt)
+    out["v"] = _randn((B, C, Hkv, D), gen, device, dt)
+    out["q_idx"] = _randint((B, Hkv, Di), gen, device, dt, w.index_absmax)
+    out["q"] = _randn((B, Hkv * G, D), gen, device, dt)
+    if lengths is None:
+        lgen = torch.Generator(device="cpu")
+        lgen.manual_seed(seed + 3000)
+        lengths = torch.randint(1, C + 1, (B,), generator=lgen)
+    out["seqlens"] = torch.as_tensor(lengths, dtype=torch.int32).reshape(B).to(device)
+    return out
