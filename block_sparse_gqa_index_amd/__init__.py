@@ -17,6 +17,9 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   kl_align_bwd(q, k, q_idx, k_idx, block_idx, lse, index_lse) -> (dq_idx, dk_idx), bf16
   forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse): selection, then attention
   sparse_attn_bwd(q, k, v, block_idx, o, lse, dout) -> (dq, dk, dv), bf16
+  decode_index_topk(q_idx, k_idx, seqlens, topk)   -> block_idx int32 [B, Hkv, k] (one new query per sequence)
+  decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq])
+  decode(q_idx, k_idx, q, k, v, seqlens, topk)     -> (block_idx, o, lse): both decode steps
   workspace_bytes(dims, op)
 """
 import ctypes
@@ -29,11 +32,13 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_F32, MSA_FP8_E4M3 = 0, 1, 2
 MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD, MSA_OP_KL_BWD = 0, 1, 2, 3, 4, 5
+MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE = 6, 7, 8
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
 EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
            "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
+           "msa_decode_index_topk", "msa_decode_attn", "msa_decode",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -75,13 +80,17 @@ def load_library(path: str = LIB_PATH):
                                      ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_forward.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode_index_topk.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode_attn.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.msa_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
     lib.msa_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_strerror.argtypes = [ctypes.c_int]
     lib.msa_strerror.restype = ctypes.c_char_p
     lib.msa_abi_version.restype = ctypes.c_int
     for f in (lib.msa_index_topk, lib.msa_check_block_idx, lib.msa_sparse_attn_fwd, lib.msa_sparse_attn_fwd_stages,
-              lib.msa_kl_align_fwd, lib.msa_forward):
+              lib.msa_kl_align_fwd, lib.msa_forward, lib.msa_kl_align_bwd, lib.msa_sparse_attn_bwd,
+              lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -333,4 +342,101 @@ def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0, block_idx=None, o=No
     _check(lib.msa_forward(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
                            float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws,
                            _stream(q.device)))
+    return block_idx, o, lse
+
+
+def _decode_shapes(q_idx=None, k_idx=None, q=None, k=None, v=None, seqlens=None):
+    """(B, C, Hkv, G, D, Di) from whichever decode tensors are given, checked
+    against each other."""
+    B = C = Hkv = G = D = Di = None
+    if seqlens is not None:
+        _req(seqlens, "seqlens", dtype=torch.int32, ndim=1)
+        B = seqlens.shape[0]
+    if k_idx is not None:
+        _req(k_idx, "k_idx", ndim=3)
+        B2, C, Di = k_idx.shape
+        if B is not None and B2 != B:
+            raise ValueError("k_idx must be [B, C, Di]")
+        B = B2
+    if q_idx is not None:
+        _req(q_idx, "q_idx", dtype=None if k_idx is None else k_idx.dtype, ndim=3)
+        if tuple(q_idx.shape) != (B, q_idx.shape[1], Di):
+            raise ValueError("q_idx must be [B, Hkv, Di]")
+        Hkv = q_idx.shape[1]
+    if k is not None:
+        _req(k, "k", ndim=4)
+        _req(v, "v", dtype=k.dtype, ndim=4)
+        _req(q, "q", dtype=k.dtype, ndim=3)
+        Bk_, Ck, Hk, D = k.shape
+        if (B is not None and Bk_ != B) or (C is not None and Ck != C) or (Hkv is not None and Hk != Hkv):
+            raise ValueError("k/v must be [B, C, Hkv, D] consistent with the other inputs")
+        B, C, Hkv = Bk_, Ck, Hk
+        if tuple(v.shape) != tuple(k.shape) or q.shape[0] != B or q.shape[2] != D or q.shape[1] % Hkv:
+            raise ValueError("q must be [B, Hq, D] with Hq a multiple of Hkv, v like k")
+        G = q.shape[1] // Hkv
+    return B, C, Hkv, G, D, Di
+
+
+def decode_index_topk(q_idx, k_idx, seqlens, topk, block_idx=None, workspace=None, block_size=128):
+    """Selection for one new query per sequence: q_idx [B, Hkv, Di], index-key
+    cache k_idx [B, C, Di], seqlens int32 [B] (cached tokens, the new one
+    included) -> block_idx int32 [B, Hkv, topk]."""
+    lib = load_library()
+    B, C, Hkv, _, _, Di = _decode_shapes(q_idx=q_idx, k_idx=k_idx, seqlens=seqlens)
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q_idx.device)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
+    dims = make_dims(B, C, Hkv, 1, 64, Di, topk, q_idx.dtype, block_size)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_INDEX), q_idx.device, workspace)
+    _check(lib.msa_decode_index_topk(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(seqlens),
+                                     _ptr(block_idx), _ptr(ws), nws, _stream(q_idx.device)))
+    return block_idx
+
+
+def decode_attn(q, k, v, seqlens, block_idx, softmax_scale=0.0, o=None, lse=None, workspace=None,
+                block_size=128):
+    """Attention of one new query per sequence: q [B, Hq, D], caches k/v
+    [B, C, Hkv, D], seqlens int32 [B], block_idx int32 [B, Hkv, topk] ->
+    (o [B, Hq, D], lse fp32 [B, Hq])."""
+    lib = load_library()
+    B, C, Hkv, G, D, _ = _decode_shapes(q=q, k=k, v=v, seqlens=seqlens)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
+    topk = block_idx.shape[2]
+    if tuple(block_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("block_idx must be [B, Hkv, topk]")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
+    _req(o, "o", dtype=q.dtype, ndim=3)
+    _req(lse, "lse", dtype=torch.float32, ndim=2)
+    dims = make_dims(B, C, Hkv, G, D, 64, topk, q.dtype, block_size)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_ATTN), q.device, workspace)
+    _check(lib.msa_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(block_idx),
+                               float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(q.device)))
+    return o, lse
+
+
+def decode(q_idx, k_idx, q, k, v, seqlens, topk, softmax_scale=0.0, block_idx=None, o=None, lse=None,
+           workspace=None, block_size=128):
+    """One decode step (msa_decode): the selection, then the attention.
+    Returns (block_idx int32 [B, Hkv, topk], o [B, Hq, D], lse fp32 [B, Hq])."""
+    lib = load_library()
+    B, C, Hkv, G, D, Di = _decode_shapes(q_idx=q_idx, k_idx=k_idx, q=q, k=k, v=v, seqlens=seqlens)
+    if q.dtype != q_idx.dtype:
+        raise ValueError("q and q_idx must share a dtype")
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
+    _req(o, "o", dtype=q.dtype, ndim=3)
+    _req(lse, "lse", dtype=torch.float32, ndim=2)
+    dims = make_dims(B, C, Hkv, G, D, Di, topk, q.dtype, block_size)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE), q.device, workspace)
+    _check(lib.msa_decode(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
+                          float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws,
+                          _stream(q.device)))
     return block_idx, o, lse

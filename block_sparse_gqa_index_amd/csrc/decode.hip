@@ -1,0 +1,448 @@
+// Decoding: one new query per sequence against a cache of keys.
+//
+// Sequence b holds n_b cached tokens (positions 0 .. n_b - 1, the new token
+// last); its new query is position i = n_b - 1, so selection and attention are
+// those of the forward's row i (MiniMax Sparse Attention article on
+// 7minutos.es, "Cómo funcionan las dos ramas": index scores of the visible
+// keys, block max-pool, top-k per query and group with the local block forced
+// in, then exact softmax attention over the kept blocks' causally visible
+// tokens; "El codiseño del kernel": the ranking runs on the raw scores). Only
+// the block indices need caching per layer (Flash-MSA article on
+// tech.kuratif.com, block-wise sparsity).
+//
+// Per decode step the work is a stream over the index-key cache (every
+// competing block of every sequence: Di values per token) plus a gather of the
+// kept blocks' K and V (k * 128 tokens per (sequence, group)); both are bound
+// by HBM bandwidth, so the kernels aim at full-line, many-in-flight loads and
+// use the matrix cores only to keep the VALU off the critical path:
+//   decode_scores_kernel  one wave per (sequence, competing block, 32 groups):
+//                         S^T = K_idx Q_idx^T on the matrix cores straight from
+//                         global memory (no LDS), block max in-lane plus one
+//                         half-wave swap -> block scores [B, Hkv, nb] fp32
+//   decode_topk_kernel    one wave per (sequence, group): a lane-local sorted
+//                         list over a strided share of the block scores, then
+//                         k-1 wave-wide maxima of packed (score, -id) keys;
+//                         ids sorted ascending, the local block appended
+//   decode_attn_kernel    one work-group per (sequence, group, kept block):
+//                         S^T = K Q^T per wave (32 keys each, K from global),
+//                         block softmax across the four waves through LDS,
+//                         O^T = V^T P^T with V staged in LDS; a normalised
+//                         fp32 partial output and its LSE per head
+//   decode_combine_kernel one work-group per (sequence, group): the kept
+//                         blocks' partials merged in slot order -> O, LSE.
+// Every sum runs in a fixed order: results are bitwise reproducible.
+#include "msa_decode.h"
+#include "msa_tiles.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kGroupCols = 32;   // groups (index scores) or heads (attention) per matrix-core column set
+
+__device__ __forceinline__ bool length_ok(int n, int C) { return n >= 1 && n <= C; }
+
+// ------------------------------------------------------------ block scores --
+
+template <typename T, int DI>
+__global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict__ q_idx,
+                                                            const T* __restrict__ k_idx,
+                                                            const int32_t* __restrict__ seqlens,
+                                                            float* __restrict__ scores, int C, int Hkv,
+                                                            int nbs, int gchunks) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int b = blockIdx.y / gchunks, gc = blockIdx.y % gchunks;
+    const int j = blockIdx.x * 4 + wave;
+    const int n = seqlens[b];
+    if (!length_ok(n, C)) return;
+    const int L = (n - 1) / kBlock;   // competing blocks: 0 .. L-1
+    if (j >= L) return;
+    const int g = gc * kGroupCols + col;
+
+    Op8<T> bq[DI / 16];
+    load_q_op<T, DI>(bq, q_idx + ((size_t)b * Hkv + (g < Hkv ? g : 0)) * DI, g < Hkv, half);
+
+    // Tiles of 32 keys; bf16 keeps all four tiles' operands in flight, fp32 two.
+    constexpr int TF = sizeof(T) == 2 ? 4 : 2;
+    const T* kb = k_idx + ((size_t)b * C + (size_t)j * kBlock) * DI;
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int t0 = 0; t0 < 4; t0 += TF) {
+        Op8<T> a[TF][DI / 16];
+#pragma unroll
+        for (int t = 0; t < TF; ++t) {
+            const T* row = kb + (size_t)((t0 + t) * 32 + col) * DI;
+#pragma unroll
+            for (int sl = 0; sl < DI / 16; ++sl) a[t][sl].load(row + 16 * sl + 8 * half);
+        }
+#pragma unroll
+        for (int t = 0; t < TF; ++t) {
+            floatx16 acc = zero16();
+#pragma unroll
+            for (int sl = 0; sl < DI / 16; ++sl) mma16(acc, a[t][sl], bq[sl]);
+            m = vmax(m, max16(acc));
+        }
+    }
+    m = vmax(m, swap_halves(m));
+    if (half == 0 && g < Hkv) scores[((size_t)b * Hkv + g) * nbs + j] = m;
+}
+
+// ------------------------------------------------------------------- top-k --
+
+// Orderable 64-bit key: score bits mapped to an unsigned order (larger score
+// -> larger key) in the high word, ~id in the low word (lower id -> larger key
+// among equal scores). 0 is below every key of a real score.
+__device__ __forceinline__ uint64_t rank_key(float s, int id) {
+    uint32_t u = __float_as_uint(s + 0.0f);   // -0 -> +0: equal scores compare equal
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)id);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
+    const uint32_t lo = __shfl_xor((uint32_t)x, mask);
+    const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), mask);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int K1MAX>
+__global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ seqlens,
+                                                          int32_t* __restrict__ block_idx, int B, int C, int Hkv,
+                                                          int nbs, int k) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);   // (sequence, group) row of this wave
+    if (r >= B * Hkv) return;
+    const int b = r / Hkv;
+    const int n = seqlens[b];
+    int32_t* out = block_idx + (size_t)r * k;
+    if (!length_ok(n, C)) {
+        if (lane < k) out[lane] = -1;
+        return;
+    }
+    const int L = (n - 1) / kBlock;
+    const int k1 = min(k - 1, L);
+    const float* row = scores + (size_t)r * nbs;
+
+    // Lane-local best K1MAX keys, descending (0 = empty).
+    uint64_t best[K1MAX];
+#pragma unroll
+    for (int e = 0; e < K1MAX; ++e) best[e] = 0;
+    for (int j = lane; j < L; j += kWave) {
+        uint64_t key = rank_key(row[j], j);
+        if (key > best[K1MAX - 1]) {
+#pragma unroll
+            for (int e = 0; e < K1MAX; ++e) {
+                const uint64_t hi = key > best[e] ? key : best[e];
+                key = key > best[e] ? best[e] : key;
+                best[e] = hi;
+            }
+        }
+    }
+    // k1 rounds: the wave-wide largest head is taken and its lane pops it.
+    int mine = 0;   // lane q keeps the id chosen in round q
+    for (int q = 0; q < k1; ++q) {
+        uint64_t mx = best[0];
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+            const uint64_t o = shfl_xor_u64(mx, s);
+            mx = o > mx ? o : mx;
+        }
+        if (best[0] == mx) {
+#pragma unroll
+            for (int e = 0; e + 1 < K1MAX; ++e) best[e] = best[e + 1];
+            best[K1MAX - 1] = 0;
+        }
+        if (lane == q) mine = (int)(~(uint32_t)mx);
+    }
+    // Ascending order: lane q's rank among the k1 chosen ids.
+    int rank = 0;
+    for (int q = 0; q < k1; ++q) rank += __shfl(mine, q) < mine ? 1 : 0;
+    if (lane < k1) out[rank] = mine;
+    else if (lane == k1) out[k1] = L;
+    else if (lane < k) out[lane] = -1;
+}
+
+// --------------------------------------------------------------- attention --
+
+template <typename T, int D>
+struct DecodeLds {
+    static constexpr int ES = sizeof(T);
+    static constexpr int VROW = D * ES + 16;            // padded V row: the two half-waves hit other banks
+    static constexpr int V_BYTES = kBlock * VROW;
+    static constexpr int P_BYTES = 4 * 2 * kWave * 8 * ES;   // [wave][slice][lane] P operands
+    static constexpr int RED_BYTES = 2 * 4 * kGroupCols * 4;
+    static constexpr int BYTES = V_BYTES + P_BYTES + RED_BYTES;
+};
+
+template <typename T>
+__device__ __forceinline__ T lds_elem(const unsigned char* p) { return *reinterpret_cast<const T*>(p); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ q, const T* __restrict__ kc,
+                                                          const T* __restrict__ vc,
+                                                          const int32_t* __restrict__ seqlens,
+                                                          const int32_t* __restrict__ block_idx,
+                                                          float* __restrict__ po, float* __restrict__ plse, int C,
+                                                          int Hkv, int G, int k, float scale_log2) {
+    using LD = DecodeLds<T, D>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LD::BYTES];
+    unsigned char* vs = lds;
+    unsigned char* pl = lds + LD::V_BYTES;
+    float* red_m = reinterpret_cast<float*>(lds + LD::V_BYTES + LD::P_BYTES);
+    float* red_l = red_m + 4 * kGroupCols;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const size_t item = ((size_t)b * Hkv + g) * k + slot;
+    const int n = seqlens[b];
+    const int i = n - 1;
+    const int j = block_idx[item];
+    // Empty slot (padding, a block past the query, or an invalid length): no
+    // tokens, LSE -inf, and the merge skips the slot.
+    if (!length_ok(n, C) || j < 0 || (int64_t)j * kBlock > i) {
+        if (threadIdx.x < G) plse[item * G + threadIdx.x] = -__builtin_inff();
+        return;
+    }
+    const int t0 = j * kBlock;
+    const int t_last = min(t0 + kBlock - 1, i);
+    const size_t kv_row = (size_t)Hkv * D;   // elements between consecutive tokens of one head
+    const T* kbase = kc + ((size_t)b * C * Hkv + g) * D;
+    const T* vbase = vc + ((size_t)b * C * Hkv + g) * D;
+
+    // V block -> LDS (rows past the last visible token zero-filled).
+    constexpr int EPC = 16 / LD::ES;
+    constexpr int CPR = D / EPC;
+    for (int ch = threadIdx.x; ch < kBlock * CPR; ch += blockDim.x) {
+        const int row = ch / CPR, cc = ch % CPR;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (t0 + row <= t_last) x = *reinterpret_cast<const u32x4*>(vbase + (size_t)(t0 + row) * kv_row + cc * EPC);
+        *reinterpret_cast<u32x4*>(vs + row * LD::VROW + cc * 16) = x;
+    }
+
+    // Scores of this wave's 32 keys against the group's heads (columns).
+    Op8<T> bq[D / 16];
+    const int Hq = Hkv * G;
+    load_q_op<T, D>(bq, q + ((size_t)b * Hq + (size_t)g * G + (col < G ? col : 0)) * D, col < G, half);
+    const int key = t0 + wave * 32 + col;
+    floatx16 s = zero16();
+    {
+        Op8<T> a[D / 16];
+#pragma unroll
+        for (int sl = 0; sl < D / 16; ++sl) {
+            if (key <= t_last) a[sl].load(kbase + (size_t)key * kv_row + 16 * sl + 8 * half);
+            else a[sl].zero();
+        }
+#pragma unroll
+        for (int sl = 0; sl < D / 16; ++sl) mma16(s, a[sl], bq[sl]);
+    }
+    // Lane holds head `col`, keys t0 + 32*wave + 8*(r/4) + 4*half + r%4.
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int t = t0 + wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        s[r] = t <= t_last ? s[r] * scale_log2 : -__builtin_inff();
+        m = vmax(m, s[r]);
+    }
+    m = vmax(m, swap_halves(m));
+    if (half == 0) red_m[wave * kGroupCols + col] = m;
+    __syncthreads();
+    const float M = max3f(red_m[col], red_m[kGroupCols + col],
+                          vmax(red_m[2 * kGroupCols + col], red_m[3 * kGroupCols + col]));
+    float l = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        s[r] = exp2_hw(s[r] - M);
+        l += s[r];
+    }
+    l += swap_halves(l);
+    if (half == 0) red_l[wave * kGroupCols + col] = l;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = s[8 * s2 + e];
+        Op8<T> bp;
+        PType<T>::pack(bp, pe);
+        *reinterpret_cast<Op8<T>*>(pl + ((wave * 2 + s2) * kWave + lane) * 8 * LD::ES) = bp;
+    }
+    __syncthreads();
+    const float lsum = red_l[col] + red_l[kGroupCols + col] + red_l[2 * kGroupCols + col] + red_l[3 * kGroupCols + col];
+
+    // O^T (32 dims of tile `wave`) = V^T P^T over the 128 keys: slice (w2, s2)
+    // pairs element e of both operands with key
+    // 32*w2 + 16*s2 + 8*(e/4) + 4*half + e%4.
+    if (wave < D / 32) {
+        const int d = wave * 32 + col;
+        floatx16 o = zero16();
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const Op8<T> bp = *reinterpret_cast<const Op8<T>*>(pl + ((w2 * 2 + s2) * kWave + lane) * 8 * LD::ES);
+                Op8<T> a;
+                if constexpr (LD::ES == 2) {
+                    uint16_t u[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int kk = 32 * w2 + 16 * s2 + 8 * (e >> 2) + 4 * half + (e & 3);
+                        u[e] = lds_elem<uint16_t>(vs + kk * LD::VROW + d * 2);
+                    }
+                    u32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)u[2 * e] | ((uint32_t)u[2 * e + 1] << 16);
+                    a.v = __builtin_bit_cast(bf16x8, w);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int kk = 32 * w2 + 16 * s2 + 8 * (e >> 2) + 4 * half + (e & 3);
+                        a.v[e] = lds_elem<float>(vs + kk * LD::VROW + d * 4);
+                    }
+                }
+                mma16(o, a, bp);
+            }
+        }
+        // Lane holds head `col`, dims wave*32 + 8*(r/4) + 4*half + r%4.
+        if (col < G) {
+            const float inv = 1.0f / lsum;
+            float* dst = po + (item * G + col) * D + wave * 32 + 4 * half;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 x = make_float4(o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv,
+                                             o[4 * q4 + 3] * inv);
+                *reinterpret_cast<float4*>(dst + 8 * q4) = x;
+            }
+        }
+    }
+    if (wave == 0 && half == 0 && col < G) plse[item * G + col] = (M + log2f(lsum)) * 0.69314718055994531f;
+}
+
+// ------------------------------------------------------------------- merge --
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, float x);
+template <>
+__device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float x) { *p = x; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ po,
+                                                             const float* __restrict__ plse, T* __restrict__ o,
+                                                             float* __restrict__ lse, int Hkv, int G, int D,
+                                                             int k) {
+    __shared__ float wts[32 * 32];   // [head][slot] merge weights
+    const int g = blockIdx.x, b = blockIdx.y;
+    const size_t item0 = ((size_t)b * Hkv + g) * k;
+    const int Hq = Hkv * G;
+    if ((int)threadIdx.x < G) {
+        const int h = threadIdx.x;
+        float mx = -__builtin_inff();
+        for (int s = 0; s < k; ++s) mx = fmaxf(mx, plse[(item0 + s) * G + h]);
+        float total = -__builtin_inff();
+        if (mx > -__builtin_inff()) {
+            float sum = 0.f;
+            for (int s = 0; s < k; ++s) {
+                const float x = plse[(item0 + s) * G + h];
+                if (x > -__builtin_inff()) sum += __expf(x - mx);
+            }
+            total = mx + __logf(sum);
+        }
+        for (int s = 0; s < k; ++s) {
+            const float x = plse[(item0 + s) * G + h];
+            wts[h * 32 + s] = x > -__builtin_inff() ? __expf(x - total) : 0.f;
+        }
+        lse[(size_t)b * Hq + (size_t)g * G + h] = total;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+        const int h = e / D, d = e % D;
+        float acc = 0.f;
+        for (int s = 0; s < k; ++s) {
+            const float w = wts[h * 32 + s];
+            if (w != 0.f) acc = fmaf(w, po[((item0 + s) * G + h) * D + d], acc);
+        }
+        store_out<T>(o + ((size_t)b * Hq + (size_t)g * G + h) * D + d, acc);
+    }
+}
+
+template <int K1MAX>
+void launch_topk(const float* scores, const int32_t* seqlens, int32_t* block_idx, int B, int C, int Hkv, int nbs,
+                 int k, hipStream_t st) {
+    const int rows = B * Hkv;
+    hipLaunchKernelGGL(decode_topk_kernel<K1MAX>, dim3((rows + 3) / 4), dim3(256), 0, st, scores, seqlens,
+                       block_idx, B, C, Hkv, nbs, k);
+}
+
+template <typename T, int DI>
+void launch_scores(const DecodeDims& d, const void* q_idx, const void* k_idx, const int32_t* seqlens,
+                   float* scores, hipStream_t st) {
+    const int gchunks = (d.Hkv + kGroupCols - 1) / kGroupCols;
+    const int lmax = (d.C - 1) / kBlock;   // competing blocks of a full cache
+    if (lmax == 0) return;
+    hipLaunchKernelGGL((decode_scores_kernel<T, DI>), dim3((lmax + 3) / 4, d.B * gchunks), dim3(256), 0, st,
+                       static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, scores, d.C, d.Hkv,
+                       d.nbs(), gchunks);
+}
+
+template <typename T, int D>
+void launch_attn(const DecodeDims& d, const void* q, const void* k, const void* v, const int32_t* seqlens,
+                 const int32_t* block_idx, float scale, void* o, float* lse, const DecodeWorkspace& W,
+                 unsigned char* ws, hipStream_t st) {
+    float* po = reinterpret_cast<float*>(ws + W.po);
+    float* pl = reinterpret_cast<float*>(ws + W.plse);
+    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.k, d.Hkv, d.B), dim3(256), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), seqlens,
+                       block_idx, po, pl, d.C, d.Hkv, d.G, d.k, scale * 1.4426950408889634f);
+    hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(d.Hkv, d.B), dim3(256), 0, st, po, pl,
+                       static_cast<T*>(o), lse, d.Hkv, d.G, D, d.k);
+}
+
+}  // namespace
+
+DecodeWorkspace decode_workspace_layout(const DecodeDims& d) {
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    DecodeWorkspace W;
+    W.scores = 0;
+    W.index_bytes = up((size_t)d.B * d.Hkv * d.nbs() * sizeof(float));
+    W.po = 0;
+    W.plse = up((size_t)d.B * d.Hkv * d.k * d.G * d.D * sizeof(float));
+    W.attn_bytes = W.plse + up((size_t)d.B * d.Hkv * d.k * d.G * sizeof(float));
+    return W;
+}
+
+hipError_t launch_decode_index(const DecodeDims& d, const void* q_idx, const void* k_idx, const int32_t* seqlens,
+                               int32_t* block_idx, void* ws, hipStream_t st) {
+    float* scores = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + decode_workspace_layout(d).scores);
+    if (d.dtype == 0) {
+        if (d.Di == 128) launch_scores<bf16_t, 128>(d, q_idx, k_idx, seqlens, scores, st);
+        else launch_scores<bf16_t, 64>(d, q_idx, k_idx, seqlens, scores, st);
+    } else {
+        if (d.Di == 128) launch_scores<float, 128>(d, q_idx, k_idx, seqlens, scores, st);
+        else launch_scores<float, 64>(d, q_idx, k_idx, seqlens, scores, st);
+    }
+    const int k1 = d.k - 1;
+    if (k1 <= 3) launch_topk<3>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
+    else if (k1 <= 7) launch_topk<7>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
+    else if (k1 <= 15) launch_topk<15>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
+    else launch_topk<31>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const DecodeDims& d, const void* q, const void* k, const void* v,
+                              const int32_t* seqlens, const int32_t* block_idx, float scale, void* o, float* lse,
+                              void* ws, hipStream_t st) {
+    const DecodeWorkspace W = decode_workspace_layout(d);
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    if (d.dtype == 0) {
+        if (d.D == 128) launch_attn<bf16_t, 128>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
+        else launch_attn<bf16_t, 64>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
+    } else {
+        if (d.D == 128) launch_attn<float, 128>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
+        else launch_attn<float, 64>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace msa

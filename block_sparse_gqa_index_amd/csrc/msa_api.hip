@@ -6,6 +6,9 @@
 
 #include <limits.h>
 
+#include <initializer_list>
+
+#include "msa_decode.h"
 #include "msa_internal.h"
 
 namespace {
@@ -23,8 +26,9 @@ constexpr int kOpLayout = -1;   // the block_idx layout check: neither heads nor
 // look at index_dim, so those are only checked for the ops that use them.
 int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (!d) return MSA_ERR_NULL;
-    const bool uses_heads = op != MSA_OP_INDEX && op != kOpLayout;   // MSA_OP_FORWARD: both
-    const bool uses_index = op != MSA_OP_ATTN && op != MSA_OP_ATTN_BWD && op != kOpLayout;
+    // MSA_OP_FORWARD and MSA_OP_DECODE: both
+    const bool uses_heads = op != MSA_OP_INDEX && op != kOpLayout && op != MSA_OP_DECODE_INDEX;
+    const bool uses_index = op != MSA_OP_ATTN && op != MSA_OP_ATTN_BWD && op != kOpLayout && op != MSA_OP_DECODE_ATTN;
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || d->topk < 1 ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
@@ -39,8 +43,12 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     // offsets are 32-bit.
     if (d->seqlen >= (int64_t(1) << 26)) return MSA_ERR_SHAPE;
     if (d->kv_heads > 4096) return MSA_ERR_SHAPE;
+    const bool decode = op == MSA_OP_DECODE_INDEX || op == MSA_OP_DECODE_ATTN || op == MSA_OP_DECODE;
+    // Decode grids: sequences x group chunks of 32 on one grid axis.
+    if (decode && (d->batch > 65535 || d->batch * ((d->kv_heads + 31) / 32) > 65535)) return MSA_ERR_SHAPE;
+    // (Decode kernels index the caches with 64-bit offsets; only their grids are bounded.)
     const int64_t rows = d->batch * d->seqlen * d->kv_heads;
-    if (d->batch > INT_MAX || rows > INT_MAX || rows * (int64_t)d->topk > INT_MAX) return MSA_ERR_SHAPE;
+    if (!decode && (d->batch > INT_MAX || rows > INT_MAX || rows * (int64_t)d->topk > INT_MAX)) return MSA_ERR_SHAPE;
     out->B = (int)d->batch;
     out->N = (int)d->seqlen;
     out->Hkv = d->kv_heads;
@@ -54,6 +62,27 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
 }
 
 bool empty(const LaunchDims& L) { return L.B == 0 || L.N == 0; }
+
+msa::DecodeDims decode_dims(const LaunchDims& L) {
+    return msa::DecodeDims{L.B, L.N, L.Hkv, L.G, L.D, L.Di, L.k, L.dtype};
+}
+
+// Decode calls share their argument checks: sizes, the per-op pointers, and
+// the workspace of `op`.
+int check_decode(const msa_dims* dims, int op, LaunchDims* L, std::initializer_list<const void*> ptrs,
+                 const void* ws, size_t ws_bytes) {
+    int st = check_dims(dims, op, L);
+    if (st != MSA_OK) return st;
+    if (dims->dtype != MSA_BF16 && dims->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
+    if (empty(*L)) return MSA_OK;
+    for (const void* p : ptrs)
+        if (!p) return MSA_ERR_NULL;
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MSA_ERR_ALIGN;
+    const size_t need = msa_workspace_bytes(dims, op);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
+    return MSA_OK;
+}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
@@ -80,9 +109,7 @@ const char* msa_strerror(int status) {
 
 size_t msa_workspace_bytes(const msa_dims* dims, int op) {
     LaunchDims L;
-    if (op != MSA_OP_INDEX && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_FORWARD &&
-        op != MSA_OP_ATTN_BWD && op != MSA_OP_KL_BWD)
-        return 0;
+    if (op < MSA_OP_INDEX || op > MSA_OP_DECODE) return 0;
     if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
     switch (op) {
         case MSA_OP_INDEX: return 0;
@@ -91,6 +118,12 @@ size_t msa_workspace_bytes(const msa_dims* dims, int op) {
         case MSA_OP_ATTN_BWD: return msa::bwd_workspace_layout(L).bytes;
         case MSA_OP_KL: return msa::kl_workspace_layout(L).bytes;
         case MSA_OP_KL_BWD: return msa::kl_bwd_workspace_layout(L).bytes;
+        case MSA_OP_DECODE_INDEX: return msa::decode_workspace_layout(decode_dims(L)).index_bytes;
+        case MSA_OP_DECODE_ATTN: return msa::decode_workspace_layout(decode_dims(L)).attn_bytes;
+        case MSA_OP_DECODE: {
+            const msa::DecodeWorkspace W = msa::decode_workspace_layout(decode_dims(L));
+            return W.index_bytes > W.attn_bytes ? W.index_bytes : W.attn_bytes;
+        }
         default: return 0;
     }
 }
@@ -225,6 +258,40 @@ int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k, const v
     return hip_status(msa::launch_kl_align_bwd(L, q, k, q_idx, k_idx, block_idx, lse, index_lse, scale, iscale,
                                                dkl_rows, kl_weight, dq_idx, dk_idx, ws,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int msa_decode_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, const int32_t* seqlens,
+                          int32_t* block_idx, void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_decode(dims, MSA_OP_DECODE_INDEX, &L, {q_idx, k_idx, seqlens, block_idx}, ws, ws_bytes);
+    if (st != MSA_OK || empty(L)) return st;
+    return hip_status(msa::launch_decode_index(decode_dims(L), q_idx, k_idx, seqlens, block_idx, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int msa_decode_attn(const msa_dims* dims, const void* q, const void* k, const void* v, const int32_t* seqlens,
+                    const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+    LaunchDims L;
+    int st = check_decode(dims, MSA_OP_DECODE_ATTN, &L, {q, k, v, seqlens, block_idx, o, lse}, ws, ws_bytes);
+    if (st != MSA_OK || empty(L)) return st;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    return hip_status(msa::launch_decode_attn(decode_dims(L), q, k, v, seqlens, block_idx, scale, o, lse, ws,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int msa_decode(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q, const void* k,
+               const void* v, const int32_t* seqlens, float softmax_scale, int32_t* block_idx, void* o, float* lse,
+               void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_decode(dims, MSA_OP_DECODE, &L, {q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse}, ws,
+                          ws_bytes);
+    if (st != MSA_OK || empty(L)) return st;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const msa::DecodeDims d = decode_dims(L);
+    if (msa::launch_decode_index(d, q_idx, k_idx, seqlens, block_idx, ws, s) != hipSuccess) return MSA_ERR_HIP;
+    return hip_status(msa::launch_decode_attn(d, q, k, v, seqlens, block_idx, scale, o, lse, ws, s));
 }
 
 }  // extern "C"

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define MSA_API __attribute__((visibility("default")))
@@ -56,7 +56,8 @@ enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
 
 /* Selector for msa_workspace_bytes. */
 enum msa_op {
-    MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4, MSA_OP_KL_BWD = 5
+    MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4, MSA_OP_KL_BWD = 5,
+    MSA_OP_DECODE_INDEX = 6, MSA_OP_DECODE_ATTN = 7, MSA_OP_DECODE = 8
 };
 
 enum msa_status {
@@ -268,6 +269,63 @@ MSA_API int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k,
                              const float* index_lse, float softmax_scale, float index_scale,
                              const float* dkl_rows, float kl_weight, void* dq_idx, void* dk_idx, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * Decoding: one new query per sequence against a cache.
+ * Defined by the same passages as msa_index_topk and msa_sparse_attn_fwd (MSA
+ * article on 7minutos.es, "Cómo funcionan las dos ramas" and "El codiseño del
+ * kernel"): sequence b holds n_b = seqlens[b] cached tokens, positions
+ * 0 .. n_b - 1 with the new token last, and its new query is position
+ * i = n_b - 1, so the selection and the attention are exactly those of the
+ * forward's row i; the per-layer state a sparse layer keeps is the block ids
+ * (Flash-MSA article on tech.kuratif.com, block-wise sparsity).
+ *
+ * `dims`: batch = B sequences (<= 65535, and B * ceil(Hkv / 32) <= 65535),
+ * seqlen = C, the cache capacity in tokens per sequence; other fields as above
+ * (dtype MSA_BF16 or MSA_F32). Cache slots at or past n_b are never read.
+ *   seqlens   [B] int32 on the DEVICE (read by the kernels, so a step can be
+ *             enqueued without a host round trip). A length outside [1, C]
+ *             is not an error: that sequence's outputs are block ids all -1,
+ *             O = 0 and LSE = -inf.
+ */
+
+/*
+ *   Uses batch, seqlen, kv_heads, index_dim, block_size, topk, dtype, causal.
+ *   q_idx     [B, Hkv, Di]    the new tokens' index queries, dtype
+ *   k_idx     [B, C, Di]      index-key cache, dtype
+ *   block_idx [B, Hkv, k]     int32 OUTPUT, the layout of msa_index_topk's rows
+ *             (ascending kept ids, local block L = (n_b - 1) / Bk last, -1
+ *             padding), bit-identical to the forward's row n_b - 1.
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_DECODE_INDEX) bytes
+ *             (block scores of the competing blocks).
+ */
+MSA_API int msa_decode_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx,
+                                  const int32_t* seqlens, int32_t* block_idx, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/*
+ *   Uses every field of `dims` except index_dim.
+ *   q         [B, Hq, D]      the new tokens' queries, dtype
+ *   k, v      [B, C, Hkv, D]  key and value caches, dtype
+ *   block_idx [B, Hkv, k]     int32 kept blocks (as msa_decode_index_topk
+ *             writes them). Ids < 0 or past the query's block are skipped
+ *             (no memory is read for them); other layouts give unspecified
+ *             outputs but never an access outside the given buffers.
+ *   softmax_scale  as for msa_sparse_attn_fwd
+ *   o         [B, Hq, D]      OUTPUT, dtype
+ *   lse       [B, Hq]         OUTPUT fp32, natural log
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_DECODE_ATTN) bytes
+ *             (one fp32 partial output and LSE per kept block and head).
+ */
+MSA_API int msa_decode_attn(const msa_dims* dims, const void* q, const void* k, const void* v,
+                            const int32_t* seqlens, const int32_t* block_idx, float softmax_scale, void* o,
+                            float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* msa_decode_index_topk then msa_decode_attn on `stream` (every field of
+ * `dims` used); ws at least msa_workspace_bytes(dims, MSA_OP_DECODE). */
+MSA_API int msa_decode(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q, const void* k,
+                       const void* v, const int32_t* seqlens, float softmax_scale, int32_t* block_idx, void* o,
+                       float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes the given entry point needs for these sizes; 0 if the sizes
  * are invalid or the op needs none. Pure host arithmetic. */

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.msa_abi_version() == 2
+    assert lib.msa_abi_version() == 3
     for s in range(7):
         assert lib.msa_strerror(s)
     assert lib.msa_strerror(99) == b"unknown status"
@@ -233,3 +233,66 @@ def test_workspace_sizes(lib):
     assert partial < need < partial * 1.1
     d32 = _dims(seqlen=131072, kv_heads=8, group_size=8, topk=16, dtype=msa.MSA_F32)
     assert msa.workspace_bytes(d32, msa.MSA_OP_ATTN) > 1.9 * need
+
+
+# ------------------------------------------------------------------ decode --
+
+def _dec_index(lib, d, ptrs=None, ws=None, nws=0):
+    p = dict(qi=FAKE, ki=FAKE, lens=FAKE, bi=FAKE)
+    p.update(ptrs or {})
+    return lib.msa_decode_index_topk(ctypes.byref(d), p["qi"], p["ki"], p["lens"], p["bi"], ws, nws, None)
+
+
+def _dec_attn(lib, d, ptrs=None, ws=None, nws=0):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
+    p.update(ptrs or {})
+    return lib.msa_decode_attn(ctypes.byref(d), p["q"], p["k"], p["v"], p["lens"], p["bi"], 0.0, p["o"],
+                               p["lse"], ws, nws, None)
+
+
+def _dec(lib, d, ptrs=None, ws=None, nws=0):
+    p = dict(qi=FAKE, ki=FAKE, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
+    p.update(ptrs or {})
+    return lib.msa_decode(ctypes.byref(d), p["qi"], p["ki"], p["q"], p["k"], p["v"], p["lens"], 0.0, p["bi"],
+                          p["o"], p["lse"], ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=msa.MSA_FP8_E4M3), 3), (dict(topk=33), 3), (dict(block_size=64), 3), (dict(causal=0), 3),
+    (dict(batch=65536), 2), (dict(batch=2048, kv_heads=1024), 2), (dict(seqlen=1 << 26), 2),
+    (dict(index_dim=96), 3), (dict(head_dim=96), 3), (dict(group_size=64), 3),
+])
+def test_decode_rejects_bad_dims(lib, kw, status):
+    d = _dims(**kw)
+    assert _dec(lib, d) == status
+    # the selection alone ignores the head fields, the attention alone the index dim
+    if "head_dim" not in kw and "group_size" not in kw:
+        assert _dec_index(lib, d) == status
+    if "index_dim" not in kw:
+        assert _dec_attn(lib, d) == status
+
+
+def test_decode_pointers_workspace_and_sizes(lib):
+    d = _dims(batch=4, seqlen=5000, kv_heads=8, group_size=8, topk=16)
+    nbs = (5000 + 127) // 128
+    need_i = msa.workspace_bytes(d, msa.MSA_OP_DECODE_INDEX)
+    need_a = msa.workspace_bytes(d, msa.MSA_OP_DECODE_ATTN)
+    # block scores [B, Hkv, nb] fp32; partial outputs and LSEs [B, Hkv, k, G, D + 1] fp32 (256-byte aligned pieces)
+    assert need_i == -(-4 * 8 * nbs * 4 // 256) * 256
+    assert need_a == 4 * 8 * 16 * 8 * 128 * 4 + -(-4 * 8 * 16 * 8 * 4 // 256) * 256
+    assert msa.workspace_bytes(d, msa.MSA_OP_DECODE) == max(need_i, need_a)
+    assert _dec_index(lib, d, dict(lens=None), ws=FAKE, nws=need_i) == 1
+    assert _dec_index(lib, d, dict(bi=MISALIGNED), ws=FAKE, nws=need_i) == 4
+    assert _dec_index(lib, d, ws=FAKE, nws=need_i - 1) == 5
+    assert _dec_index(lib, d, ws=MISALIGNED, nws=need_i) == 5
+    assert _dec_attn(lib, d, dict(o=None), ws=FAKE, nws=need_a) == 1
+    assert _dec_attn(lib, d, ws=None, nws=0) == 5
+    assert _dec(lib, d, dict(q=MISALIGNED), ws=FAKE, nws=need_a) == 4
+
+
+def test_decode_empty_batch_needs_nothing(lib):
+    for kw in (dict(batch=0), dict(seqlen=0)):
+        d = _dims(**kw)
+        none = dict(qi=None, ki=None, q=None, k=None, v=None, lens=None, bi=None, o=None, lse=None)
+        assert _dec(lib, d, none) == 0
+        assert msa.workspace_bytes(d, msa.MSA_OP_DECODE) == 0
