@@ -14,6 +14,11 @@ for the other two main kernels, and the CPU oracle timed on a bounded sample of
 the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload n128k] [--no-cpu-baseline]
+
+With --decode the line is for one decode step instead (msa_decode_index_topk
+then msa_decode_attn: one new token for each of 64 sequences with 128K-token
+caches, lengths uniform on [1, 128K]); value = sequences (new tokens) per
+second, roofline = HBM bytes the step must move per second.
 """
 import argparse
 import hashlib
@@ -29,7 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import block_sparse_gqa_index_amd as msa  # noqa: E402
-from synth import CONFIGS, make_grad_output, make_inputs, sample_rows  # noqa: E402
+from synth import (CONFIGS, DECODE_CONFIGS, make_decode_inputs, make_grad_output, make_inputs,  # noqa: E402
+                   sample_rows)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and MFMA)
@@ -156,6 +162,129 @@ def cpu_baseline(w, x, seconds_target=15.0):
                       f"{spent:.1f} s"}
 
 
+def decode_bytes(w, seqlens):
+    """Algorithmic HBM bytes of one decode step, per stage.
+
+    Selection: the competing blocks' index keys (L_b * Bk tokens of Di values
+    for sequence b, L_b = (n_b - 1) // Bk), the new index queries, the lengths
+    and the block ids written. Attention: the selected tokens' K and V
+    (|T_b| = (min(k, L_b + 1) - 1) Bk + (n_b - 1) % Bk + 1 per group), the new
+    queries, O, LSE and the block ids read."""
+    es = 2 if w.dtype == "bf16" else 4
+    Hkv, G, D, Di, Bk, k = w.kv_heads, w.group_size, w.head_dim, w.index_dim, w.block_size, w.topk
+    n = np.asarray(seqlens, dtype=np.int64)
+    i = n - 1
+    L = i // Bk
+    T = (np.minimum(k, L + 1) - 1) * Bk + (i % Bk) + 1
+    B = len(n)
+    sel = int((L * Bk).sum()) * Di * es + B * Hkv * Di * es + B * 4 + B * Hkv * k * 4
+    att = int(T.sum()) * Hkv * 2 * D * es + 2 * B * Hkv * G * D * es + B * Hkv * G * 4 + B * Hkv * k * 4
+    return {"selection": sel, "attention": att, "selected_tokens": int(T.sum()) * Hkv}
+
+
+def decode_cpu_baseline(w, x, seconds_target=15.0):
+    """The oracle's decode on a bounded sample of the batch's sequences."""
+    from oracle import msa_oracle as O
+    lens = x["seqlens"].cpu().numpy()
+    order = np.random.default_rng(2).permutation(w.batch)
+    spent, done = 0.0, 0
+    for b in order:
+        n = int(lens[b])
+        sl = slice(int(b), int(b) + 1)
+        qi, ki = x["q_idx"][sl].cpu(), x["k_idx"][sl, :n].cpu()
+        q, kc, vc = x["q"][sl].cpu(), x["k"][sl, :n].cpu(), x["v"][sl, :n].cpu()
+        t0 = time.perf_counter()
+        bi = O.decode_index_topk(qi, ki, np.array([n]), w.block_size, w.topk)
+        O.decode_attention(q, kc, vc, np.array([n]), bi, w.block_size)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= seconds_target * 0.5:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas")
+    except (ImportError, ValueError):
+        cores = os.cpu_count()
+    return {"value": done / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of the {w.batch} sequences of the {w.name} batch (one new token each: "
+                      f"selection + attention, float64 oracle, numpy BLAS threads); {spent:.1f} s"}
+
+
+def bench_decode(args, dev):
+    w = DECODE_CONFIGS["decode_n128k_b64"]
+    log(f"[bench] decode batch {w.name}: generating caches on {dev}")
+    x = make_decode_inputs(w, device=dev)
+    B, C, Hkv, G, D = w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim
+    dims = msa.make_dims(B, C, Hkv, G, D, w.index_dim, w.topk, x["q"].dtype)
+    ws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_DECODE)), dtype=torch.uint8, device=dev)
+    bi = torch.empty((B, Hkv, w.topk), dtype=torch.int32, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev):
+        ev[0].record(stream)
+        msa.decode_index_topk(x["q_idx"], x["k_idx"], x["seqlens"], w.topk, block_idx=bi, workspace=ws)
+        ev[1].record(stream)
+        msa.decode_attn(x["q"], x["k"], x["v"], x["seqlens"], bi, o=o, lse=lse, workspace=ws)
+        ev[2].record(stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} decode steps")
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev[a].elapsed_time(ev[a + 1]) for ev in evs]))
+                for a, name in enumerate(("selection", "attention"))}
+    ref = (bi.clone(), o.clone(), lse.clone())
+    msa.decode(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], x["seqlens"], w.topk, block_idx=bi, o=o, lse=lse,
+               workspace=ws)
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(ref, (bi, o, lse)))
+    nb = decode_bytes(w, x["seqlens"].cpu().numpy())
+    kernels = {"selection": "decode_scores_kernel + decode_topk_kernel",
+               "attention": "decode_attn_kernel + decode_combine_kernel"}
+
+    def hbm(stage):
+        a = nb[stage] / (stage_ms[stage] * 1e-3) / 1e9
+        return {"kernel": kernels[stage], "bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": a / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes": nb[stage], "ms": stage_ms[stage]}
+
+    rooflines = {s: hbm(s) for s in ("selection", "attention")}
+    dominant = max(rooflines, key=lambda s: stage_ms[s])
+    lens = x["seqlens"].cpu().numpy()
+    out = {
+        "metric": "MSA decode tokens/s (one new token per sequence; 64 sequences, 128K-token caches, k=16, Bk=128)",
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B} sequences, cache capacity {C}, lengths uniform on [1, {C}] "
+                               f"(mean {lens.mean():.0f}), Hkv={Hkv} G={G} D={D} Di={w.index_dim} "
+                               f"Bk={w.block_size} k={w.topk} {w.dtype}",
+                   "global_batch": B, "seq_len": C, "parallelism": "single GPU"},
+        "stage_ms": stage_ms,
+        "hbm_gbs": (nb["selection"] + nb["attention"]) / (ms_step * 1e-3) / 1e9,
+        "decode_matches_stages": same,
+        "roofline": rooflines[dominant],
+        "rooflines": rooflines,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle decode on a bounded sample)")
+        out["cpu_baseline"] = decode_cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +300,8 @@ def main():
                          "(reported beside the bf16 headline, never as it)")
     ap.add_argument("--bwd", action="store_true",
                     help="also time the main-branch backward (msa_sparse_attn_bwd) on the step's outputs")
+    ap.add_argument("--decode", action="store_true",
+                    help="time one decode step (64 sequences, 128K-token caches) instead of the forward")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -188,6 +319,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_mib << 20}), flush=True)
+        return
+    if args.decode:
+        msa.load_library()
+        bench_decode(args, dev)
         return
     w = CONFIGS[args.workload]
     msa.load_library()

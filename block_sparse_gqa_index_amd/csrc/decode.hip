@@ -21,8 +21,9 @@
 //                         half-wave swap -> block scores [B, Hkv, nb] fp32
 //   decode_topk_kernel    one wave per (sequence, group): a lane-local sorted
 //                         list over a strided share of the block scores, then
-//                         k-1 wave-wide maxima of packed (score, -id) keys;
-//                         ids sorted ascending, the local block appended
+//                         k-1 wave-wide maxima (DPP within rows, lane reads
+//                         across them) of packed (score, -id) keys; ids
+//                         sorted ascending, the local block appended
 //   decode_attn_kernel    one work-group per (sequence, group, kept block):
 //                         S^T = K Q^T per wave (32 keys each, K from global),
 //                         block softmax across the four waves through LDS,
@@ -99,10 +100,31 @@ __device__ __forceinline__ uint64_t rank_key(float s, int id) {
     return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)id);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
-    const uint32_t lo = __shfl_xor((uint32_t)x, mask);
-    const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), mask);
+// Key of a partner lane by DPP: CTRL 0xB1 / 0x4E are the quad permutes
+// [1,0,3,2] / [2,3,0,1], 0x141 / 0x140 the 8- and 16-lane mirrors.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
     return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest key of the wave (the same value in every lane): in-row maxima by
+// DPP (each 16-lane row ends uniform), then the four rows' values read out.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+    x = max_u64(x, dpp_u64<0xB1>(x));
+    x = max_u64(x, dpp_u64<0x4E>(x));
+    x = max_u64(x, dpp_u64<0x141>(x));
+    x = max_u64(x, dpp_u64<0x140>(x));
+    return max_u64(max_u64(readlane_u64(x, 0), readlane_u64(x, 16)), max_u64(readlane_u64(x, 32), readlane_u64(x, 48)));
 }
 
 template <int K1MAX>
@@ -128,26 +150,33 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
     uint64_t best[K1MAX];
 #pragma unroll
     for (int e = 0; e < K1MAX; ++e) best[e] = 0;
-    for (int j = lane; j < L; j += kWave) {
-        uint64_t key = rank_key(row[j], j);
-        if (key > best[K1MAX - 1]) {
+    // Chunks of 16 scores per lane, all requested before the first insert.
+    constexpr int kPer = 16;
+    for (int j0 = 0; j0 < L; j0 += kPer * kWave) {
+        float v[kPer];
 #pragma unroll
-            for (int e = 0; e < K1MAX; ++e) {
-                const uint64_t hi = key > best[e] ? key : best[e];
-                key = key > best[e] ? best[e] : key;
-                best[e] = hi;
+        for (int u = 0; u < kPer; ++u) {
+            const int j = j0 + u * kWave + lane;
+            v[u] = j < L ? row[j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int j = j0 + u * kWave + lane;
+            uint64_t key = j < L ? rank_key(v[u], j) : 0;
+            if (key > best[K1MAX - 1]) {
+#pragma unroll
+                for (int e = 0; e < K1MAX; ++e) {
+                    const uint64_t hi = key > best[e] ? key : best[e];
+                    key = key > best[e] ? best[e] : key;
+                    best[e] = hi;
+                }
             }
         }
     }
     // k1 rounds: the wave-wide largest head is taken and its lane pops it.
     int mine = 0;   // lane q keeps the id chosen in round q
     for (int q = 0; q < k1; ++q) {
-        uint64_t mx = best[0];
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {
-            const uint64_t o = shfl_xor_u64(mx, s);
-            mx = o > mx ? o : mx;
-        }
+        const uint64_t mx = wave_max_u64(best[0]);
         if (best[0] == mx) {
 #pragma unroll
             for (int e = 0; e + 1 < K1MAX; ++e) best[e] = best[e + 1];
@@ -157,7 +186,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
     }
     // Ascending order: lane q's rank among the k1 chosen ids.
     int rank = 0;
-    for (int q = 0; q < k1; ++q) rank += __shfl(mine, q) < mine ? 1 : 0;
+    for (int q = 0; q < k1; ++q) rank += __builtin_amdgcn_readlane(mine, q) < mine ? 1 : 0;
     if (lane < k1) out[rank] = mine;
     else if (lane == k1) out[k1] = L;
     else if (lane < k) out[lane] = -1;
@@ -332,38 +361,64 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
                                                              const float* __restrict__ plse, T* __restrict__ o,
                                                              float* __restrict__ lse, int Hkv, int G, int D,
                                                              int k) {
-    __shared__ float wts[32 * 32];   // [head][slot] merge weights
+    __shared__ float sl[32 * 32];    // slot LSEs [slot][head], then merge weights
+    __shared__ float tot[32];        // merged LSE per head
     const int g = blockIdx.x, b = blockIdx.y;
     const size_t item0 = ((size_t)b * Hkv + g) * k;
     const int Hq = Hkv * G;
+    // The row's k * G slot LSEs are contiguous: one load per thread.
+    for (int t = threadIdx.x; t < k * G; t += blockDim.x) sl[t] = plse[item0 * G + t];
+    __syncthreads();
     if ((int)threadIdx.x < G) {
         const int h = threadIdx.x;
         float mx = -__builtin_inff();
-        for (int s = 0; s < k; ++s) mx = fmaxf(mx, plse[(item0 + s) * G + h]);
+        for (int s = 0; s < k; ++s) mx = fmaxf(mx, sl[s * G + h]);
         float total = -__builtin_inff();
         if (mx > -__builtin_inff()) {
             float sum = 0.f;
             for (int s = 0; s < k; ++s) {
-                const float x = plse[(item0 + s) * G + h];
+                const float x = sl[s * G + h];
                 if (x > -__builtin_inff()) sum += __expf(x - mx);
             }
             total = mx + __logf(sum);
         }
-        for (int s = 0; s < k; ++s) {
-            const float x = plse[(item0 + s) * G + h];
-            wts[h * 32 + s] = x > -__builtin_inff() ? __expf(x - total) : 0.f;
-        }
+        tot[h] = total;
         lse[(size_t)b * Hq + (size_t)g * G + h] = total;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    for (int t = threadIdx.x; t < k * G; t += blockDim.x) {
+        const float x = sl[t];
+        sl[t] = x > -__builtin_inff() ? __expf(x - tot[t % G]) : 0.f;
+    }
+    __syncthreads();
+    // Each thread: 4 consecutive dims of one head; the slots' partials are
+    // requested four slots at a time, summed in slot order.
+    for (int e = threadIdx.x * 4; e < G * D; e += blockDim.x * 4) {
         const int h = e / D, d = e % D;
-        float acc = 0.f;
-        for (int s = 0; s < k; ++s) {
-            const float w = wts[h * 32 + s];
-            if (w != 0.f) acc = fmaf(w, po[((item0 + s) * G + h) * D + d], acc);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < k; s0 += 4) {
+            float4 x[4];
+            float wv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = s0 + u;
+                wv[u] = s < k ? sl[s * G + h] : 0.f;
+                x[u] = wv[u] != 0.f ? *reinterpret_cast<const float4*>(po + ((item0 + s) * G + h) * D + d)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc.x = fmaf(wv[u], x[u].x, acc.x);
+                acc.y = fmaf(wv[u], x[u].y, acc.y);
+                acc.z = fmaf(wv[u], x[u].z, acc.z);
+                acc.w = fmaf(wv[u], x[u].w, acc.w);
+            }
         }
-        store_out<T>(o + ((size_t)b * Hq + (size_t)g * G + h) * D + d, acc);
+        T* dst = o + ((size_t)b * Hq + (size_t)g * G + h) * D + d;
+        store_out<T>(dst, acc.x);
+        store_out<T>(dst + 1, acc.y);
+        store_out<T>(dst + 2, acc.z);
+        store_out<T>(dst + 3, acc.w);
     }
 }
 
