@@ -20,6 +20,7 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   decode_index_topk(q_idx, k_idx, seqlens, topk)   -> block_idx int32 [B, Hkv, k] (one new query per sequence)
   decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq])
   decode(q_idx, k_idx, q, k, v, seqlens, topk)     -> (block_idx, o, lse): both decode steps
+  dense_attn_fwd(q, k, v)                          -> (o, lse): causal attention over every visible key (warm-up)
   workspace_bytes(dims, op)
 """
 import ctypes
@@ -32,13 +33,13 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_F32, MSA_FP8_E4M3 = 0, 1, 2
 MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD, MSA_OP_KL_BWD = 0, 1, 2, 3, 4, 5
-MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE = 6, 7, 8
+MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE, MSA_OP_DENSE_ATTN = 6, 7, 8, 9
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
 EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
            "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
-           "msa_decode_index_topk", "msa_decode_attn", "msa_decode",
+           "msa_decode_index_topk", "msa_decode_attn", "msa_decode", "msa_dense_attn_fwd",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -83,6 +84,7 @@ def load_library(path: str = LIB_PATH):
     lib.msa_decode_index_topk.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode_attn.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.msa_dense_attn_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
     lib.msa_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_strerror.argtypes = [ctypes.c_int]
@@ -90,7 +92,7 @@ def load_library(path: str = LIB_PATH):
     lib.msa_abi_version.restype = ctypes.c_int
     for f in (lib.msa_index_topk, lib.msa_check_block_idx, lib.msa_sparse_attn_fwd, lib.msa_sparse_attn_fwd_stages,
               lib.msa_kl_align_fwd, lib.msa_forward, lib.msa_kl_align_bwd, lib.msa_sparse_attn_bwd,
-              lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode):
+              lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode, lib.msa_dense_attn_fwd):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -440,3 +442,27 @@ def decode(q_idx, k_idx, q, k, v, seqlens, topk, softmax_scale=0.0, block_idx=No
                           float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws,
                           _stream(q.device)))
     return block_idx, o, lse
+
+
+def dense_attn_fwd(q, k, v, softmax_scale=0.0, o=None, lse=None, workspace=None, block_size=128):
+    """Dense causal GQA attention (the warm-up's full attention): q [B,N,Hq,D],
+    k/v [B,N,Hkv,D] -> (o [B,N,Hq,D], lse fp32 [B,Hq,N])."""
+    lib = load_library()
+    _req(q, "q", ndim=4)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(v, "v", dtype=q.dtype, ndim=4)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D) or Hq % Hkv:
+        raise ValueError("k/v must be [B, N, Hkv, D] with Hq a multiple of Hkv")
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, 64, 1, q.dtype, block_size)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _req(o, "o", dtype=q.dtype, ndim=4)
+    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DENSE_ATTN), q.device, workspace)
+    _check(lib.msa_dense_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), float(softmax_scale), _ptr(o),
+                                  _ptr(lse), _ptr(ws), nws, _stream(q.device)))
+    return o, lse

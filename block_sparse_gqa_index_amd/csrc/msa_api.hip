@@ -28,12 +28,14 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (!d) return MSA_ERR_NULL;
     // MSA_OP_FORWARD and MSA_OP_DECODE: both
     const bool uses_heads = op != MSA_OP_INDEX && op != kOpLayout && op != MSA_OP_DECODE_INDEX;
-    const bool uses_index = op != MSA_OP_ATTN && op != MSA_OP_ATTN_BWD && op != kOpLayout && op != MSA_OP_DECODE_ATTN;
-    if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || d->topk < 1 ||
+    const bool uses_index = op != MSA_OP_ATTN && op != MSA_OP_ATTN_BWD && op != kOpLayout &&
+                            op != MSA_OP_DECODE_ATTN && op != MSA_OP_DENSE_ATTN;
+    const bool uses_topk = op != MSA_OP_DENSE_ATTN;
+    if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || (uses_topk && d->topk < 1) ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
     const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout;   // fp8 index inputs: selection only
-    if (d->block_size != 128 || d->topk > 32 ||
+    if (d->block_size != 128 || (uses_topk && d->topk > 32) ||
         (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3)) ||
         ((op == MSA_OP_ATTN_BWD || op == MSA_OP_KL_BWD) && d->dtype != MSA_BF16) ||
         d->causal != 1 || (uses_heads && (!pow2_upto32(d->group_size) || (d->head_dim != 64 && d->head_dim != 128))) ||
@@ -48,14 +50,15 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (decode && (d->batch > 65535 || d->batch * ((d->kv_heads + 31) / 32) > 65535)) return MSA_ERR_SHAPE;
     // (Decode kernels index the caches with 64-bit offsets; only their grids are bounded.)
     const int64_t rows = d->batch * d->seqlen * d->kv_heads;
-    if (!decode && (d->batch > INT_MAX || rows > INT_MAX || rows * (int64_t)d->topk > INT_MAX)) return MSA_ERR_SHAPE;
+    if (!decode && (d->batch > INT_MAX || rows > INT_MAX || rows * (int64_t)(uses_topk ? d->topk : 1) > INT_MAX))
+        return MSA_ERR_SHAPE;
     out->B = (int)d->batch;
     out->N = (int)d->seqlen;
     out->Hkv = d->kv_heads;
     out->G = uses_heads ? d->group_size : 1;
     out->D = uses_heads ? d->head_dim : 0;
     out->Di = uses_index ? d->index_dim : 0;
-    out->k = d->topk;
+    out->k = uses_topk ? d->topk : 1;
     out->nb = (int)((d->seqlen + 127) / 128);
     out->dtype = d->dtype;
     return MSA_OK;
@@ -109,7 +112,7 @@ const char* msa_strerror(int status) {
 
 size_t msa_workspace_bytes(const msa_dims* dims, int op) {
     LaunchDims L;
-    if (op < MSA_OP_INDEX || op > MSA_OP_DECODE) return 0;
+    if (op < MSA_OP_INDEX || op > MSA_OP_DENSE_ATTN) return 0;
     if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
     switch (op) {
         case MSA_OP_INDEX: return 0;
@@ -120,6 +123,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, int op) {
         case MSA_OP_KL_BWD: return msa::kl_bwd_workspace_layout(L).bytes;
         case MSA_OP_DECODE_INDEX: return msa::decode_workspace_layout(decode_dims(L)).index_bytes;
         case MSA_OP_DECODE_ATTN: return msa::decode_workspace_layout(decode_dims(L)).attn_bytes;
+        case MSA_OP_DENSE_ATTN: return msa::dense_workspace_bytes(L);
         case MSA_OP_DECODE: {
             const msa::DecodeWorkspace W = msa::decode_workspace_layout(decode_dims(L));
             return W.index_bytes > W.attn_bytes ? W.index_bytes : W.attn_bytes;
@@ -258,6 +262,20 @@ int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k, const v
     return hip_status(msa::launch_kl_align_bwd(L, q, k, q_idx, k_idx, block_idx, lse, index_lse, scale, iscale,
                                                dkl_rows, kl_weight, dq_idx, dk_idx, ws,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int msa_dense_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v, float softmax_scale,
+                       void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_DENSE_ATTN, &L);
+    if (st != MSA_OK) return st;
+    if (empty(L)) return MSA_OK;
+    if (!q || !k || !v || !o || !lse) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return MSA_ERR_ALIGN;
+    const size_t need = msa::dense_workspace_bytes(L);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    return hip_status(msa::launch_dense_attn(L, q, k, v, scale, o, lse, ws, static_cast<hipStream_t>(stream)));
 }
 
 int msa_decode_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, const int32_t* seqlens,

@@ -107,4 +107,10 @@ hipError_t launch_kl_align_bwd(const LaunchDims& d, const void* q, const void* k
                                const float* index_lse, float scale, float index_scale, const float* dkl_rows,
                                float kl_weight, void* dq_idx, void* dk_idx, void* ws, hipStream_t st);
 
+// Dense causal attention (every visible key kept): V^T copy into ws, then the
+// query-block-outer kernel. ws holds dense_workspace_bytes(d).
+size_t dense_workspace_bytes(const LaunchDims& d);
+hipError_t launch_dense_attn(const LaunchDims& d, const void* q, const void* k, const void* v, float scale, void* o,
+                             float* lse, void* ws, hipStream_t st);
+
 }  // namespace msa

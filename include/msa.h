@@ -57,7 +57,7 @@ enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
 /* Selector for msa_workspace_bytes. */
 enum msa_op {
     MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4, MSA_OP_KL_BWD = 5,
-    MSA_OP_DECODE_INDEX = 6, MSA_OP_DECODE_ATTN = 7, MSA_OP_DECODE = 8
+    MSA_OP_DECODE_INDEX = 6, MSA_OP_DECODE_ATTN = 7, MSA_OP_DECODE = 8, MSA_OP_DENSE_ATTN = 9
 };
 
 enum msa_status {
@@ -269,6 +269,25 @@ MSA_API int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k,
                              const float* index_lse, float softmax_scale, float index_scale,
                              const float* dkl_rows, float kl_weight, void* dq_idx, void* dk_idx, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * Dense causal GQA attention forward: the main branch with every causally
+ * visible key kept.
+ * Defined by the MSA article (7minutos.es), "Cómo se entrena MSA": during the
+ * indexer warm-up both branches attend to everything; this is the main
+ * branch's output then, i.e. msa_sparse_attn_fwd's result when every row keeps
+ * all of its visible blocks (which that entry point cannot be given once the
+ * blocks outnumber topk <= 32).
+ *
+ *   Uses batch, seqlen, kv_heads, group_size, head_dim, block_size, dtype and
+ *   causal of `dims` (topk and index_dim are not read).
+ *   q [B, N, Hq, D], k, v [B, N, Hkv, D], softmax_scale, o [B, N, Hq, D] and
+ *   lse [B, Hq, N] as for msa_sparse_attn_fwd, with T_i = {0 .. i}.
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_DENSE_ATTN) bytes (a
+ *             per-block transposed copy of V, the size of v).
+ */
+MSA_API int msa_dense_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                               float softmax_scale, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Decoding: one new query per sequence against a cache.

@@ -59,7 +59,7 @@ __all__ = [
     "local_block", "visible_block_scores", "select_blocks", "index_topk_rows",
     "index_topk", "token_set", "token_count", "attention_rows", "sparse_attention",
     "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "kl_backward", "kl_dq_idx_rows",
-    "map_positions", "decode_index_topk", "decode_attention",
+    "map_positions", "decode_index_topk", "decode_attention", "dense_block_idx_rows",
 ]
 
 
@@ -489,6 +489,20 @@ def kl_dq_idx_rows(q, k, k_idx, block_idx_rows, positions, Bk, w_rows=None, scal
                                     np.asarray(qi_rows[r, g], dtype=np.float64),
                                     np.asarray(ki[b, T], dtype=np.float64), scale, index_scale)
             out[r, g] = (1.0 if w_rows is None else float(w_rows[r, g])) * a
+    return out
+
+
+def dense_block_idx_rows(positions, Hkv, Bk):
+    """Every causally visible block of each position, for the warm-up's full
+    attention ([P2] "Cómo se entrena MSA": during the first iterations both
+    branches attend to everything): int32 [M, Hkv, nb] with ids 0..L ascending,
+    -1 padded, nb = the most blocks any of the positions sees. Passed to
+    ``attention_rows`` this is dense causal attention."""
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1, 2)
+    nb = int(positions[:, 1].max()) // Bk + 1 if len(positions) else 1
+    out = np.full((len(positions), Hkv, nb), -1, dtype=np.int32)
+    for r, (_, i) in enumerate(positions):
+        out[r, :, : i // Bk + 1] = np.arange(i // Bk + 1, dtype=np.int32)
     return out
 
 

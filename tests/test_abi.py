@@ -225,7 +225,7 @@ def test_workspace_sizes(lib):
     assert msa.workspace_bytes(_dims(seqlen=128), msa.MSA_OP_ATTN) == 2 * 128 * 128 * 2
     assert msa.workspace_bytes(_dims(topk=1), msa.MSA_OP_ATTN) == 2 * 8 * 128 * 128 * 2
     assert msa.workspace_bytes(_dims(), msa.MSA_OP_INDEX) == 0
-    assert msa.workspace_bytes(_dims(), 9) == 0
+    assert msa.workspace_bytes(_dims(), 10) == 0
     # the partial outputs dominate: rows * (k-1) * G * D * 2 bytes for bf16
     d = _dims(seqlen=131072, kv_heads=8, group_size=8, topk=16)
     need = msa.workspace_bytes(d, msa.MSA_OP_ATTN)
@@ -296,3 +296,21 @@ def test_decode_empty_batch_needs_nothing(lib):
         none = dict(qi=None, ki=None, q=None, k=None, v=None, lens=None, bi=None, o=None, lse=None)
         assert _dec(lib, d, none) == 0
         assert msa.workspace_bytes(d, msa.MSA_OP_DECODE) == 0
+
+
+def test_dense_attention_arguments(lib):
+    d = _dims(topk=0)                    # topk is not read by the dense attention
+    need = msa.workspace_bytes(d, msa.MSA_OP_DENSE_ATTN)
+    nb = (1024 + 127) // 128
+    assert need == 1 * 2 * nb * 128 * 128 * 2   # V^T copy [B, Hkv, nb, D, 128] bf16
+
+    def call(ptrs=None, ws=FAKE, nws=need, dd=d):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE)
+        p.update(ptrs or {})
+        return lib.msa_dense_attn_fwd(ctypes.byref(dd), p["q"], p["k"], p["v"], 0.0, p["o"], p["lse"], ws, nws, None)
+    assert call(dict(v=None)) == 1
+    assert call(dict(o=MISALIGNED)) == 4
+    assert call(nws=need - 1) == 5
+    assert call(dd=_dims(head_dim=96)) == 3
+    assert call(dd=_dims(dtype=msa.MSA_FP8_E4M3)) == 3
+    assert call(dd=_dims(seqlen=0), ptrs=dict(q=None, k=None, v=None, o=None, lse=None), ws=None, nws=0) == 0

@@ -594,3 +594,26 @@ def test_kl_dq_idx_rows_is_the_full_backward_at_those_rows():
     got = O.kl_dq_idx_rows(q, kk, k_idx, rows, pos, Bk, w_rows=w[0][:, pos[:, 1]].T,
                            qi_rows=q_idx[0, pos[:, 1]])
     np.testing.assert_allclose(got, full[0, pos[:, 1]], atol=1e-14, rtol=0)
+
+
+def test_dense_rows_are_causal_sdpa():
+    """All visible blocks kept (the warm-up's full attention): the oracle's rows
+    equal torch's causal GQA SDPA in float64, and the LSE the masked logsumexp."""
+    rng = np.random.default_rng(11)
+    B, N, Hkv, G, D, Bk = 2, 45, 2, 3, 8, 8
+    q = rng.standard_normal((B, N, Hkv * G, D))
+    k = rng.standard_normal((B, N, Hkv, D))
+    v = rng.standard_normal((B, N, Hkv, D))
+    pos = np.array([(b, i) for b in range(B) for i in range(N)])
+    rows = O.dense_block_idx_rows(pos, Hkv, Bk)
+    assert rows.shape == (B * N, Hkv, (N - 1) // Bk + 1)
+    o, lse = O.attention_rows(q, k, v, rows, pos, Bk)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    z = (qt @ kt.transpose(-1, -2)) / math.sqrt(D)
+    z = z.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), -math.inf)
+    want_lse = torch.logsumexp(z, dim=-1)                                  # [B, Hq, N]
+    np.testing.assert_allclose(o.reshape(B, N, Hkv * G, D), want.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    np.testing.assert_allclose(lse.reshape(B, N, Hkv * G), want_lse.permute(0, 2, 1).numpy(), atol=1e-12)
