@@ -285,6 +285,65 @@ def bench_decode(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_dense(args, dev):
+    """The warm-up's dense causal attention on the 128K workload's shapes."""
+    w = CONFIGS["n128k"]
+    log(f"[bench] dense attention on {w.name} shapes: generating inputs on {dev}")
+    x = make_inputs(w, device=dev, kinds=("q", "k", "v"))
+    B, N, Hkv, G, D = w.batch, w.seqlen, w.kv_heads, w.group_size, w.head_dim
+    dims = msa.make_dims(B, N, Hkv, G, D, w.index_dim, 1, x["q"].dtype)
+    ws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_DENSE_ATTN)), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, Hkv * G, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        msa.dense_attn_fwd(x["q"], x["k"], x["v"], o=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} dense steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        msa.dense_attn_fwd(x["q"], x["k"], x["v"], o=o, lse=lse, workspace=ws)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_ev = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    # F_dense = 4 * D * Hq * sum_i (i + 1): QK^T and PV over every causally visible key.
+    f = 4.0 * D * B * Hkv * G * N * (N + 1) / 2
+    a = f / (ms_ev * 1e-3) / 1e12
+    out = {
+        "metric": "MSA dense (warm-up) causal GQA attention fwd tokens/s and TFLOP/s at N=128K",
+        "value": B * N / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"dense causal attention, n128k shapes: B={B} N={N} Hkv={Hkv} G={G} D={D} {w.dtype}",
+                   "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+        "tflops": f / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": "dense_attn_kernel (+ V^T copy)", "bound": "mfma", "achieved": a,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_tflop": f / 1e12, "ms": ms_ev},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import msa_oracle as O
+        log("[bench] cpu baseline (oracle dense rows on a bounded sample)")
+        kh, vh = x["k"].cpu(), x["v"].cpu()
+        workers = max(1, min(16, os.cpu_count() or 1))
+        pos = sample_rows(w, n=128, seed=3)
+        b = torch.as_tensor(pos[:, 0], device=dev)
+        i = torch.as_tensor(pos[:, 1], device=dev)
+        q_rows = x["q"][b, i].cpu()
+        rows = O.dense_block_idx_rows(pos, Hkv, w.block_size)
+        t0 = time.perf_counter()
+        O.map_positions(lambda c, br, qr: O.attention_rows(None, kh, vh, br, c, w.block_size, q_rows=qr),
+                        pos, (rows, q_rows), workers=workers)
+        spent = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": len(pos) / spent, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+                               "sample": f"{len(pos)} query positions of the 128K sequence (all 64 heads, every "
+                                         f"visible key), float64 oracle; {spent:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +361,8 @@ def main():
                     help="also time the main-branch backward (msa_sparse_attn_bwd) on the step's outputs")
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step (64 sequences, 128K-token caches) instead of the forward")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the warm-up's dense causal attention (msa_dense_attn_fwd) on the 128K shapes instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -323,6 +384,10 @@ def main():
     if args.decode:
         msa.load_library()
         bench_decode(args, dev)
+        return
+    if args.dense:
+        msa.load_library()
+        bench_dense(args, dev)
         return
     w = CONFIGS[args.workload]
     msa.load_library()
