@@ -279,6 +279,27 @@ def bench_decode(args, dev):
         "roofline": rooflines[dominant],
         "rooflines": rooflines,
     }
+    if args.index_fp8:
+        # The selection on an fp8 e4m3 index cache (integer values: exact, same selection).
+        fp8 = torch.float8_e4m3fn
+        qi8, ki8 = x["q_idx"].to(fp8), x["k_idx"].to(fp8)
+        bi8 = torch.empty_like(bi)
+        for _ in range(args.warmup):
+            msa.decode_index_topk(qi8, ki8, x["seqlens"], w.topk, block_idx=bi8, workspace=ws)
+        ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev8:
+            e[0].record(stream)
+            msa.decode_index_topk(qi8, ki8, x["seqlens"], w.topk, block_idx=bi8, workspace=ws)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ms8 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
+        b8 = (nb["selection"] - B * Hkv * w.index_dim - int(((lens - 1) // w.block_size * w.block_size).sum())
+              * w.index_dim)   # one byte per index value instead of two
+        out["selection_fp8"] = {"ms": ms8, "algorithmic_bytes": b8, "achieved_gbs": b8 / (ms8 * 1e-3) / 1e9,
+                                "frac_of_hbm": b8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                "speedup_vs_bf16_selection": stage_ms["selection"] / ms8,
+                                "step_ms_with_fp8_selection": ms8 + stage_ms["attention"],
+                                "same_selection": bool(torch.equal(bi8, bi))}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle decode on a bounded sample)")
         out["cpu_baseline"] = decode_cpu_baseline(w, x, args.cpu_seconds)

@@ -18,7 +18,8 @@
 //   decode_scores_kernel  one wave per (sequence, competing block, 32 groups):
 //                         S^T = K_idx Q_idx^T on the matrix cores straight from
 //                         global memory (no LDS), block max in-lane plus one
-//                         half-wave swap -> block scores [B, Hkv, nb] fp32
+//                         half-wave swap -> block scores [B, Hkv, nb] fp32;
+//                         an fp8 e4m3 index cache halves the bytes streamed
 //   decode_topk_kernel    one wave per (sequence, group): a lane-local sorted
 //                         list over a strided share of the block scores, then
 //                         k-1 wave-wide maxima (DPP within rows, lane reads
@@ -45,6 +46,36 @@ __device__ __forceinline__ bool length_ok(int n, int C) { return n >= 1 && n <= 
 
 // ------------------------------------------------------------ block scores --
 
+// Matrix-core step of the index scores per element type: a 32 x 32 S^T tile
+// accumulates KD-deep slices; lane l supplies row/column l % 32 and the KD/2
+// consecutive contraction elements starting at (KD/2) * (l / 32).
+template <typename T> struct DecMma;
+template <> struct DecMma<bf16_t> {   // v_mfma_f32_32x32x16_bf16
+    using Op = Op8<bf16_t>;
+    static constexpr int KD = 16;
+    static __device__ __forceinline__ void mma(floatx16& acc, const Op& a, const Op& b) { mma16(acc, a, b); }
+};
+template <> struct DecMma<float> {    // eight v_mfma_f32_32x32x2_f32 per 16-deep slice
+    using Op = Op8<float>;
+    static constexpr int KD = 16;
+    static __device__ __forceinline__ void mma(floatx16& acc, const Op& a, const Op& b) { mma16(acc, a, b); }
+};
+template <> struct DecMma<fp8_t> {    // v_mfma_scale_f32_32x32x64_f8f6f4: e4m3 x e4m3, unit scales
+    struct Op {
+        i32x8 v;
+        __device__ __forceinline__ void load(const void* p) {
+            const uint4 lo = reinterpret_cast<const uint4*>(p)[0], hi = reinterpret_cast<const uint4*>(p)[1];
+            v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        __device__ __forceinline__ void zero() { v = i32x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    };
+    static constexpr int KD = 64;
+    static __device__ __forceinline__ void mma(floatx16& acc, const Op& a, const Op& b) {
+        // format code 0 (fp8 e4m3) for both operands; scale exponents 127 (= 2^0)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, acc, 0, 0, 0, 127, 0, 127);
+    }
+};
+
 template <typename T, int DI>
 __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict__ q_idx,
                                                             const T* __restrict__ k_idx,
@@ -61,27 +92,35 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
     if (j >= L) return;
     const int g = gc * kGroupCols + col;
 
-    Op8<T> bq[DI / 16];
-    load_q_op<T, DI>(bq, q_idx + ((size_t)b * Hkv + (g < Hkv ? g : 0)) * DI, g < Hkv, half);
+    using MM = DecMma<T>;
+    constexpr int NS = DI / MM::KD;   // contraction slices
+    constexpr int KH = MM::KD / 2;    // elements per lane and slice
+    typename MM::Op bq[NS];
+    const T* qrow = q_idx + ((size_t)b * Hkv + (g < Hkv ? g : 0)) * DI;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        if (g < Hkv) bq[sl].load(qrow + MM::KD * sl + KH * half);
+        else bq[sl].zero();
+    }
 
-    // Tiles of 32 keys; bf16 keeps all four tiles' operands in flight, fp32 two.
-    constexpr int TF = sizeof(T) == 2 ? 4 : 2;
+    // Tiles of 32 keys; bf16 and fp8 keep all four tiles' operands in flight, fp32 two.
+    constexpr int TF = sizeof(T) == 4 ? 2 : 4;
     const T* kb = k_idx + ((size_t)b * C + (size_t)j * kBlock) * DI;
     float m = -__builtin_inff();
 #pragma unroll
     for (int t0 = 0; t0 < 4; t0 += TF) {
-        Op8<T> a[TF][DI / 16];
+        typename MM::Op a[TF][NS];
 #pragma unroll
         for (int t = 0; t < TF; ++t) {
             const T* row = kb + (size_t)((t0 + t) * 32 + col) * DI;
 #pragma unroll
-            for (int sl = 0; sl < DI / 16; ++sl) a[t][sl].load(row + 16 * sl + 8 * half);
+            for (int sl = 0; sl < NS; ++sl) a[t][sl].load(row + MM::KD * sl + KH * half);
         }
 #pragma unroll
         for (int t = 0; t < TF; ++t) {
             floatx16 acc = zero16();
 #pragma unroll
-            for (int sl = 0; sl < DI / 16; ++sl) mma16(acc, a[t][sl], bq[sl]);
+            for (int sl = 0; sl < NS; ++sl) MM::mma(acc, a[t][sl], bq[sl]);
             m = vmax(m, max16(acc));
         }
     }
@@ -473,6 +512,9 @@ hipError_t launch_decode_index(const DecodeDims& d, const void* q_idx, const voi
     if (d.dtype == 0) {
         if (d.Di == 128) launch_scores<bf16_t, 128>(d, q_idx, k_idx, seqlens, scores, st);
         else launch_scores<bf16_t, 64>(d, q_idx, k_idx, seqlens, scores, st);
+    } else if (d.dtype == 2) {
+        if (d.Di == 128) launch_scores<fp8_t, 128>(d, q_idx, k_idx, seqlens, scores, st);
+        else launch_scores<fp8_t, 64>(d, q_idx, k_idx, seqlens, scores, st);
     } else {
         if (d.Di == 128) launch_scores<float, 128>(d, q_idx, k_idx, seqlens, scores, st);
         else launch_scores<float, 64>(d, q_idx, k_idx, seqlens, scores, st);

@@ -34,7 +34,8 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || (uses_topk && d->topk < 1) ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
-    const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout;   // fp8 index inputs: selection only
+    // fp8 index inputs: selection only
+    const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout || op == MSA_OP_DECODE_INDEX;
     if (d->block_size != 128 || (uses_topk && d->topk > 32) ||
         (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3)) ||
         ((op == MSA_OP_ATTN_BWD || op == MSA_OP_KL_BWD) && d->dtype != MSA_BF16) ||
@@ -76,7 +77,9 @@ int check_decode(const msa_dims* dims, int op, LaunchDims* L, std::initializer_l
                  const void* ws, size_t ws_bytes) {
     int st = check_dims(dims, op, L);
     if (st != MSA_OK) return st;
-    if (dims->dtype != MSA_BF16 && dims->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
+    if (dims->dtype != MSA_BF16 && dims->dtype != MSA_F32 &&
+        !(op == MSA_OP_DECODE_INDEX && dims->dtype == MSA_FP8_E4M3))
+        return MSA_ERR_UNSUPPORTED;
     if (empty(*L)) return MSA_OK;
     for (const void* p : ptrs)
         if (!p) return MSA_ERR_NULL;

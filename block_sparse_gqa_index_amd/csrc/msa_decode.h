@@ -8,7 +8,8 @@
 
 namespace msa {
 
-// Validated decode sizes: B sequences, cache capacity C tokens, dtype 0 = bf16, 1 = fp32.
+// Validated decode sizes: B sequences, cache capacity C tokens, dtype 0 = bf16, 1 = fp32, 2 = fp8 e4m3
+// (the selection only).
 struct DecodeDims {
     int B, C, Hkv, G, D, Di, k, dtype;
     int nbs() const { return (C + 127) / 128; }   // blocks of a full cache

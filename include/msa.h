@@ -49,8 +49,8 @@ extern "C" {
 
 /* Element type of every floating-point input (and of O). */
 /* Element type of the tensors. MSA_FP8_E4M3 (OCP fp8 e4m3, the variant with no
- * infinities, |x| <= 448) is accepted by msa_index_topk and msa_check_block_idx
- * only: q_idx and k_idx in fp8 on the fp8 matrix cores, scores accumulated in
+ * infinities, |x| <= 448) is accepted by msa_index_topk, msa_decode_index_topk
+ * and msa_check_block_idx only: q_idx and k_idx in fp8 on the fp8 matrix cores, scores accumulated in
  * fp32 (exact, and the selection bit-exact, for integer-valued inputs). */
 enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
 
@@ -301,7 +301,9 @@ MSA_API int msa_dense_attn_fwd(const msa_dims* dims, const void* q, const void* 
  *
  * `dims`: batch = B sequences (<= 65535, and B * ceil(Hkv / 32) <= 65535),
  * seqlen = C, the cache capacity in tokens per sequence; other fields as above
- * (dtype MSA_BF16 or MSA_F32). Cache slots at or past n_b are never read.
+ * (dtype MSA_BF16 or MSA_F32; msa_decode_index_topk also takes MSA_FP8_E4M3
+ * for an fp8 index cache, scores accumulated in fp32 as in msa_index_topk).
+ * Cache slots at or past n_b are never read.
  *   seqlens   [B] int32 on the DEVICE (read by the kernels, so a step can be
  *             enqueued without a host round trip). A length outside [1, C]
  *             is not an error: that sequence's outputs are block ids all -1,

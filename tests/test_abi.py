@@ -265,8 +265,10 @@ def _dec(lib, d, ptrs=None, ws=None, nws=0):
 def test_decode_rejects_bad_dims(lib, kw, status):
     d = _dims(**kw)
     assert _dec(lib, d) == status
-    # the selection alone ignores the head fields, the attention alone the index dim
-    if "head_dim" not in kw and "group_size" not in kw:
+    # the selection alone ignores the head fields and takes fp8; the attention alone ignores the index dim
+    if kw.get("dtype") == msa.MSA_FP8_E4M3:
+        assert _dec_index(lib, d, dict(lens=None)) == 1      # accepted: goes on to the pointer checks
+    elif "head_dim" not in kw and "group_size" not in kw:
         assert _dec_index(lib, d) == status
     if "index_dim" not in kw:
         assert _dec_attn(lib, d) == status

@@ -155,3 +155,31 @@ def test_decode_n128k_b64_sampled_sequences():
         assert np.array_equal(bi_h[b], want[0]), b
     log(f"  block indices exact on {len(pick)} sequences")
     _check(w, x, bi, o, lse, seqs=pick[:8])
+
+
+def test_decode_fp8_index_cache():
+    """An fp8 e4m3 index cache (integer index values are exact in it): the same
+    selection as the bf16 cache and as the oracle, on a ragged batch and on the
+    benchmark's 64 x 128K batch."""
+    fp8 = torch.float8_e4m3fn
+    w = Workload("dec_fp8", 12, 3000, 8, 8, 128, 128, topk=16)
+    lengths = [min(x, w.seqlen) for x in EDGE] + [2999, 3000]
+    x = _dev(make_decode_inputs(w, device="cpu", lengths=lengths))
+    bi = msa.decode_index_topk(x["q_idx"], x["k_idx"], x["seqlens"], w.topk)
+    bi8 = msa.decode_index_topk(x["q_idx"].to(fp8), x["k_idx"].to(fp8), x["seqlens"], w.topk)
+    w64 = Workload("dec_fp8_di64", 5, 900, 3, 1, 64, 64, topk=4)
+    y = _dev(make_decode_inputs(w64, device="cpu", lengths=[900, 1, 129, 256, 640]))
+    bj = msa.decode_index_topk(y["q_idx"], y["k_idx"], y["seqlens"], w64.topk)
+    bj8 = msa.decode_index_topk(y["q_idx"].to(fp8), y["k_idx"].to(fp8), y["seqlens"], w64.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(bi, bi8) and torch.equal(bj, bj8)
+    want = O.decode_index_topk(x["q_idx"].to(fp8).cpu(), x["k_idx"].to(fp8).cpu(), np.array(lengths),
+                               w.block_size, w.topk)
+    assert np.array_equal(bi8.cpu().numpy(), want)
+
+    w = DECODE_CONFIGS["decode_n128k_b64"]
+    x = make_decode_inputs(w, device=DEV)
+    bi = msa.decode_index_topk(x["q_idx"], x["k_idx"], x["seqlens"], w.topk)
+    bi8 = msa.decode_index_topk(x["q_idx"].to(fp8), x["k_idx"].to(fp8), x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(bi, bi8)
