@@ -345,6 +345,29 @@ def bench_dense(args, dev):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
                      "algorithmic_tflop": f / 1e12, "ms": ms_ev},
     }
+    if args.kl:
+        # The warm-up's KL over every visible token, on the dense LSE.
+        log("[bench] dense KL")
+        xi = make_inputs(w, device=dev, kinds=("q_idx", "k_idx"))
+        kws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_DENSE_KL)), dtype=torch.uint8, device=dev)
+        kl_rows = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev)
+        kl_sum = torch.empty((1,), dtype=torch.float32, device=dev)
+
+        def kl():
+            msa.dense_kl_align_fwd(x["q"], x["k"], xi["q_idx"], xi["k_idx"], lse, kl_rows=kl_rows, kl_sum=kl_sum,
+                                   workspace=kws)
+        kl()
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in kev:
+            e[0].record(stream)
+            kl()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        kl_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
+        fk = (2.0 * D * Hkv * G + 2.0 * w.index_dim * Hkv) * B * N * (N + 1) / 2
+        out["dense_kl_align"] = {"ms": kl_ms, "algorithmic_tflop": fk / 1e12, "tflops": fk / (kl_ms * 1e-3) / 1e12,
+                                 "frac_of_peak": fk / (kl_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                 "kl_sum": float(kl_sum.item())}
     if not args.no_cpu_baseline:
         from oracle import msa_oracle as O
         log("[bench] cpu baseline (oracle dense rows on a bounded sample)")

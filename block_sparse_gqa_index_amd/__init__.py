@@ -21,6 +21,7 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq])
   decode(q_idx, k_idx, q, k, v, seqlens, topk)     -> (block_idx, o, lse): both decode steps
   dense_attn_fwd(q, k, v)                          -> (o, lse): causal attention over every visible key (warm-up)
+  dense_kl_align_fwd(q, k, q_idx, k_idx, lse)      -> (kl_rows, kl_sum): the KL loss over every visible token
   workspace_bytes(dims, op)
 """
 import ctypes
@@ -33,13 +34,14 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_F32, MSA_FP8_E4M3 = 0, 1, 2
 MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD, MSA_OP_KL_BWD = 0, 1, 2, 3, 4, 5
-MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE, MSA_OP_DENSE_ATTN = 6, 7, 8, 9
+MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE, MSA_OP_DENSE_ATTN, MSA_OP_DENSE_KL = 6, 7, 8, 9, 10
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
 EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
            "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
            "msa_decode_index_topk", "msa_decode_attn", "msa_decode", "msa_dense_attn_fwd",
+           "msa_dense_kl_align_fwd",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -85,6 +87,8 @@ def load_library(path: str = LIB_PATH):
     lib.msa_decode_attn.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_dense_attn_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.msa_dense_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
+                                           sz, vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
     lib.msa_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_strerror.argtypes = [ctypes.c_int]
@@ -92,7 +96,8 @@ def load_library(path: str = LIB_PATH):
     lib.msa_abi_version.restype = ctypes.c_int
     for f in (lib.msa_index_topk, lib.msa_check_block_idx, lib.msa_sparse_attn_fwd, lib.msa_sparse_attn_fwd_stages,
               lib.msa_kl_align_fwd, lib.msa_forward, lib.msa_kl_align_bwd, lib.msa_sparse_attn_bwd,
-              lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode, lib.msa_dense_attn_fwd):
+              lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode, lib.msa_dense_attn_fwd,
+              lib.msa_dense_kl_align_fwd):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -466,3 +471,30 @@ def dense_attn_fwd(q, k, v, softmax_scale=0.0, o=None, lse=None, workspace=None,
     _check(lib.msa_dense_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), float(softmax_scale), _ptr(o),
                                   _ptr(lse), _ptr(ws), nws, _stream(q.device)))
     return o, lse
+
+
+def dense_kl_align_fwd(q, k, q_idx, k_idx, lse, softmax_scale=0.0, index_scale=0.0, kl_rows=None, kl_sum=None,
+                       index_lse=None, workspace=None, block_size=128):
+    """The warm-up's KL loss over every visible token (lse from dense_attn_fwd)
+    -> (kl_rows fp32 [B,Hkv,N], kl_sum fp32 [1])."""
+    lib = load_library()
+    _req(q, "q", ndim=4)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(q_idx, "q_idx", dtype=q.dtype, ndim=4)
+    _req(k_idx, "k_idx", dtype=q.dtype, ndim=3)
+    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    B, N, Hq, D = q.shape
+    Hkv, Di = q_idx.shape[2], q_idx.shape[3]
+    if (tuple(k.shape) != (B, N, Hkv, D) or tuple(k_idx.shape) != (B, N, Di) or tuple(lse.shape) != (B, Hq, N)
+            or Hq % Hkv):
+        raise ValueError("inconsistent shapes")
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, 1, q.dtype, block_size)
+    if kl_rows is None:
+        kl_rows = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
+    if kl_sum is None:
+        kl_sum = torch.empty((1,), dtype=torch.float32, device=q.device)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DENSE_KL), q.device, workspace)
+    _check(lib.msa_dense_kl_align_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(lse),
+                                      float(softmax_scale), float(index_scale), _ptr(kl_rows), _ptr(kl_sum),
+                                      _ptr(index_lse), _ptr(ws), nws, _stream(q.device)))
+    return kl_rows, kl_sum

@@ -15,6 +15,7 @@
 // exactly. Non-local blocks are processed key-block-outer from the same
 // inverted selection as the attention; the local block and the merge run per
 // (batch, query block, group); kl_sum is a fixed-order two-stage reduction.
+// dense_kl_kernel computes the same loss over every visible token (warm-up).
 #include "msa_common.h"
 #include "msa_internal.h"
 #include "msa_tiles.h"
@@ -276,6 +277,139 @@ __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
     }
 }
 
+// ------------------------------------------------------------- dense KL --
+//
+// The warm-up's KL (MSA article, "Cómo se entrena MSA": during the first
+// iterations both branches attend to every visible token): the same per-row
+// KL with T_i = {0 .. i}, the teacher normalised by the dense attention's LSE.
+// Query-block outer like the dense attention: one 8-wave work-group per
+// (batch, query block, group, 256-row part), each wave one resident 32-row
+// tile (main and index query operands, the five running sums); K_j and
+// K_idx_j stream through two LDS buffers, the next block's rows requested into
+// registers before the current block's scores and stored after them.
+
+constexpr int kDenseKlWaves = 8;
+
+// Rows [128][W] of T moved global -> registers -> LDS (SwzTile<T, W>) by NT
+// threads; rows at or past valid_rows are zero-filled.
+template <typename T, int W, int NT>
+struct RowPrefetch {
+    using S = SwzTile<T, W>;
+    static constexpr int EPC = 16 / sizeof(T);
+    static constexpr int CH = kBlock * S::CPR;
+    static constexpr int PER = CH / NT;
+    static_assert(CH % NT == 0, "chunk split");
+    u32x4 r[PER];
+    __device__ __forceinline__ void load(const T* src, size_t row_stride, int valid_rows) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int ch = threadIdx.x + u * NT;
+            const int row = ch / S::CPR, cc = ch % S::CPR;
+            r[u] = row < valid_rows ? *reinterpret_cast<const u32x4*>(src + row * row_stride + cc * EPC)
+                                    : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void commit(unsigned char* lds) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int ch = threadIdx.x + u * NT;
+            const int row = ch / S::CPR, cc = ch % S::CPR;
+            *reinterpret_cast<u32x4*>(lds + S::offset(row, cc * 16)) = r[u];
+        }
+    }
+};
+
+template <typename T, int D, int DI, int G, int NBUF>
+__global__ __launch_bounds__(kDenseKlWaves * kWave) void dense_kl_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
+    const float* __restrict__ lse, float* __restrict__ kl_rows, float* __restrict__ index_lse, int B, int N,
+    int Hkv, int nb, int parts, float scale_log2, float iscale) {
+    constexpr int NT = kDenseKlWaves * kWave;
+    constexpr int KB = SwzTile<T, D>::BYTES, BUF = KB + SwzTile<T, DI>::BYTES;
+    __shared__ __align__(16) unsigned char lds[NBUF * BUF];
+    const int x = blockIdx.x;
+    const int pt = x % parts;
+    const int g = (x / parts) % Hkv;
+    const int b = (x / (parts * Hkv)) % B;
+    const int qb = nb - 1 - x / (parts * Hkv * B);   // latest (heaviest) query blocks first
+    const int Hq = Hkv * G;
+    const int q0 = qb * kBlock;
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int tile = pt * kDenseKlWaves + w;
+    const bool tile_ok = tile < kBlock * G / 32;   // wave-uniform
+    const int p = (tile * 32 + col) / G;
+    const int hh = col % G;
+    const int i = q0 + p;
+    const bool valid = tile_ok && i < N;
+    const int ii = valid ? i : 0;
+    Op8<T> bq[D / 16];
+    load_q_op<T, D>(bq, q + ((size_t)b * N + ii) * Hq * D + (size_t)(g * G + hh) * D, valid, half);
+    Op8<T> bi[DI / 16];
+    load_q_op<T, DI>(bi, q_idx + (((size_t)b * N + ii) * Hkv + g) * DI, valid, half);
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
+
+    const size_t krow = (size_t)Hkv * D;
+    const T* kbase = k + (size_t)b * N * krow + (size_t)g * D;
+    const T* kibase = k_idx + (size_t)b * N * DI;
+    RowPrefetch<T, D, NT> pk;
+    RowPrefetch<T, DI, NT> pi;
+    pk.load(kbase, krow, min(kBlock, N));
+    pi.load(kibase, DI, min(kBlock, N));
+    pk.commit(lds);
+    pi.commit(lds + KB);
+    __syncthreads();
+
+    KlAcc acc{0.f, 0.f, 0.f, -__builtin_inff(), 0.f};
+    for (int j = 0; j <= qb; ++j) {
+        const unsigned char* cur = lds + (NBUF == 2 ? (j & 1) * BUF : 0);
+        unsigned char* nxt = lds + (NBUF == 2 ? ((j + 1) & 1) * BUF : 0);
+        const bool more = j < qb;
+        const int nvalid = more ? min(kBlock, N - (j + 1) * kBlock) : 0;
+        if (more) pk.load(kbase + (size_t)(j + 1) * kBlock * krow, krow, nvalid);
+        if (tile_ok) {
+            floatx16 s[4], u[4];
+            tile_scores<T, D>(s, bq, cur, col, half);
+            tile_scores<T, DI>(u, bi, cur + KB, col, half);
+            if constexpr (NBUF == 2) {
+                if (more) {
+                    pi.load(kibase + (size_t)(j + 1) * kBlock * DI, DI, nvalid);
+                    pk.commit(nxt);
+                }
+            }
+            // Every key of a block before the query's own is visible.
+            const KlAcc a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, j == qb ? p : kBlock - 1, half, hh);
+            acc.A += a.A;
+            acc.Bs += a.Bs;
+            acc.P += a.P;
+            merge_lse(acc.mu, acc.lu, a.mu, a.lu);
+        } else if constexpr (NBUF == 2) {
+            if (more) {
+                pi.load(kibase + (size_t)(j + 1) * kBlock * DI, DI, nvalid);
+                pk.commit(nxt);
+            }
+        }
+        if (more) {
+            if constexpr (NBUF == 2) {
+                pi.commit(nxt + KB);
+            } else {
+                pi.load(kibase + (size_t)(j + 1) * kBlock * DI, DI, nvalid);
+                __syncthreads();   // everyone is done reading the single buffer
+                pk.commit(nxt);
+                pi.commit(nxt + KB);
+            }
+        }
+        __syncthreads();
+    }
+    if (valid && hh == 0 && half == 0) {
+        const float lse_u = acc.mu + __logf(acc.lu);
+        kl_rows[((size_t)b * Hkv + g) * N + i] = acc.A - acc.Bs + lse_u * acc.P;
+        if (index_lse) index_lse[((size_t)b * Hkv + g) * N + i] = lse_u;
+    }
+}
+
 // Fixed-order two-stage sum of kl_rows (deterministic for a given size).
 __global__ __launch_bounds__(kRedThreads) void kl_reduce_partial(const float* __restrict__ x, size_t n,
                                                                  double* __restrict__ partial) {
@@ -382,6 +516,67 @@ static hipError_t launch_kl_dt(const LaunchDims& d, const void* q, const void* k
     if (d.D == 128) return launch_kl_g<T, 128, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
     if (d.Di == 128) return launch_kl_g<T, 64, 128>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
     return launch_kl_g<T, 64, 64>(d, q, k, qi, ki, bi, lse, sc, isc, rows, sum, ilse, ws, st);
+}
+
+size_t dense_kl_workspace_bytes(const LaunchDims& d) {
+    return align_up((size_t)red_blocks_for((size_t)d.B * d.Hkv * d.N) * 8);
+}
+
+template <typename T, int D, int DI, int G>
+static void launch_dense_kl_t(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
+                              const void* k_idx, const float* lse, float scale_log2, float iscale, float* kl_rows,
+                              float* index_lse, hipStream_t st) {
+    constexpr int kTiles = kBlock * G / 32;
+    const int parts = (kTiles + kDenseKlWaves - 1) / kDenseKlWaves;
+    constexpr int BUF = SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES;
+    constexpr int NBUF = 2 * BUF <= 160 * 1024 ? 2 : 1;
+    const size_t grid = (size_t)d.nb * d.B * d.Hkv * parts;
+    hipLaunchKernelGGL((dense_kl_kernel<T, D, DI, G, NBUF>), dim3((unsigned)grid), dim3(kDenseKlWaves * kWave), 0,
+                       st, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(q_idx),
+                       static_cast<const T*>(k_idx), lse, kl_rows, index_lse, d.B, d.N, d.Hkv, d.nb, parts,
+                       scale_log2, iscale);
+}
+
+template <typename T, int D, int DI>
+static void launch_dense_kl_g(const LaunchDims& d, const void* q, const void* k, const void* qi, const void* ki,
+                              const float* lse, float sl2, float isc, float* rows, float* ilse, hipStream_t st) {
+    switch (d.G) {
+        case 1: launch_dense_kl_t<T, D, DI, 1>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st); break;
+        case 2: launch_dense_kl_t<T, D, DI, 2>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st); break;
+        case 4: launch_dense_kl_t<T, D, DI, 4>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st); break;
+        case 8: launch_dense_kl_t<T, D, DI, 8>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st); break;
+        case 16: launch_dense_kl_t<T, D, DI, 16>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st); break;
+        default: launch_dense_kl_t<T, D, DI, 32>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st); break;
+    }
+}
+
+template <typename T>
+static void launch_dense_kl_dt(const LaunchDims& d, const void* q, const void* k, const void* qi, const void* ki,
+                               const float* lse, float sl2, float isc, float* rows, float* ilse, hipStream_t st) {
+    if (d.D == 128 && d.Di == 128) launch_dense_kl_g<T, 128, 128>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st);
+    else if (d.D == 128) launch_dense_kl_g<T, 128, 64>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st);
+    else if (d.Di == 128) launch_dense_kl_g<T, 64, 128>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st);
+    else launch_dense_kl_g<T, 64, 64>(d, q, k, qi, ki, lse, sl2, isc, rows, ilse, st);
+}
+
+hipError_t launch_dense_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
+                                 const void* k_idx, const float* lse, float scale, float index_scale, float* kl_rows,
+                                 float* kl_sum, float* index_lse, void* ws, hipStream_t st) {
+    if (d.B == 0 || d.N == 0) {
+        hipLaunchKernelGGL(kl_reduce_final, dim3(1), dim3(kRedThreads), 0, st, (const double*)nullptr, 0, kl_sum);
+        return hipGetLastError();
+    }
+    const float scale_log2 = scale * 1.4426950408889634f;
+    if (d.dtype == 0)
+        launch_dense_kl_dt<bf16_t>(d, q, k, q_idx, k_idx, lse, scale_log2, index_scale, kl_rows, index_lse, st);
+    else
+        launch_dense_kl_dt<float>(d, q, k, q_idx, k_idx, lse, scale_log2, index_scale, kl_rows, index_lse, st);
+    const size_t rows = (size_t)d.B * d.Hkv * d.N;
+    const int red_blocks = red_blocks_for(rows);
+    double* red = static_cast<double*>(ws);
+    hipLaunchKernelGGL(kl_reduce_partial, dim3(red_blocks), dim3(kRedThreads), 0, st, kl_rows, rows, red);
+    hipLaunchKernelGGL(kl_reduce_final, dim3(1), dim3(kRedThreads), 0, st, red, red_blocks, kl_sum);
+    return hipGetLastError();
 }
 
 hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx, const void* k_idx,

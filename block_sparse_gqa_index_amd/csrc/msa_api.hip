@@ -30,7 +30,7 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     const bool uses_heads = op != MSA_OP_INDEX && op != kOpLayout && op != MSA_OP_DECODE_INDEX;
     const bool uses_index = op != MSA_OP_ATTN && op != MSA_OP_ATTN_BWD && op != kOpLayout &&
                             op != MSA_OP_DECODE_ATTN && op != MSA_OP_DENSE_ATTN;
-    const bool uses_topk = op != MSA_OP_DENSE_ATTN;
+    const bool uses_topk = op != MSA_OP_DENSE_ATTN && op != MSA_OP_DENSE_KL;
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || (uses_topk && d->topk < 1) ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
@@ -115,7 +115,7 @@ const char* msa_strerror(int status) {
 
 size_t msa_workspace_bytes(const msa_dims* dims, int op) {
     LaunchDims L;
-    if (op < MSA_OP_INDEX || op > MSA_OP_DENSE_ATTN) return 0;
+    if (op < MSA_OP_INDEX || op > MSA_OP_DENSE_KL) return 0;
     if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
     switch (op) {
         case MSA_OP_INDEX: return 0;
@@ -127,6 +127,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, int op) {
         case MSA_OP_DECODE_INDEX: return msa::decode_workspace_layout(decode_dims(L)).index_bytes;
         case MSA_OP_DECODE_ATTN: return msa::decode_workspace_layout(decode_dims(L)).attn_bytes;
         case MSA_OP_DENSE_ATTN: return msa::dense_workspace_bytes(L);
+        case MSA_OP_DENSE_KL: return msa::dense_kl_workspace_bytes(L);
         case MSA_OP_DECODE: {
             const msa::DecodeWorkspace W = msa::decode_workspace_layout(decode_dims(L));
             return W.index_bytes > W.attn_bytes ? W.index_bytes : W.attn_bytes;
@@ -279,6 +280,26 @@ int msa_dense_attn_fwd(const msa_dims* dims, const void* q, const void* k, const
     if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
     return hip_status(msa::launch_dense_attn(L, q, k, v, scale, o, lse, ws, static_cast<hipStream_t>(stream)));
+}
+
+int msa_dense_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx, const void* k_idx,
+                           const float* lse, float softmax_scale, float index_scale, float* kl_rows, float* kl_sum,
+                           float* index_lse, void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_DENSE_KL, &L);
+    if (st != MSA_OK) return st;
+    if (!kl_sum) return MSA_ERR_NULL;
+    if (!empty(L) && (!q || !k || !q_idx || !k_idx || !lse || !kl_rows)) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) || !aligned16(lse) ||
+        !aligned16(kl_rows) || (reinterpret_cast<uintptr_t>(index_lse) & 3u))
+        return MSA_ERR_ALIGN;
+    const size_t need = msa::dense_kl_workspace_bytes(L);
+    if (!empty(L) && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    const float iscale = index_scale > 0.f ? index_scale : 1.0f / sqrtf((float)L.Di);
+    // kl_sum is written even for an empty problem (the sum of nothing is 0).
+    return hip_status(msa::launch_dense_kl_align(L, q, k, q_idx, k_idx, lse, scale, iscale, kl_rows, kl_sum,
+                                                 index_lse, ws, static_cast<hipStream_t>(stream)));
 }
 
 int msa_decode_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, const int32_t* seqlens,

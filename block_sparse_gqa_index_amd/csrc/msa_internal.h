@@ -113,4 +113,11 @@ size_t dense_workspace_bytes(const LaunchDims& d);
 hipError_t launch_dense_attn(const LaunchDims& d, const void* q, const void* k, const void* v, float scale, void* o,
                              float* lse, void* ws, hipStream_t st);
 
+// Dense KL (every visible token; lse from the dense attention): kl_rows, the
+// fixed-order kl_sum, optional index_lse. ws holds dense_kl_workspace_bytes(d).
+size_t dense_kl_workspace_bytes(const LaunchDims& d);
+hipError_t launch_dense_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
+                                 const void* k_idx, const float* lse, float scale, float index_scale, float* kl_rows,
+                                 float* kl_sum, float* index_lse, void* ws, hipStream_t st);
+
 }  // namespace msa

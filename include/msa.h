@@ -57,7 +57,7 @@ enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
 /* Selector for msa_workspace_bytes. */
 enum msa_op {
     MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4, MSA_OP_KL_BWD = 5,
-    MSA_OP_DECODE_INDEX = 6, MSA_OP_DECODE_ATTN = 7, MSA_OP_DECODE = 8, MSA_OP_DENSE_ATTN = 9
+    MSA_OP_DECODE_INDEX = 6, MSA_OP_DECODE_ATTN = 7, MSA_OP_DECODE = 8, MSA_OP_DENSE_ATTN = 9, MSA_OP_DENSE_KL = 10
 };
 
 enum msa_status {
@@ -288,6 +288,26 @@ MSA_API int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k,
  */
 MSA_API int msa_dense_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
                                float softmax_scale, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * KL alignment loss forward over every causally visible token: the index
+ * branch's side of the warm-up (MSA article, "Cómo se entrena MSA": during
+ * the first iterations both branches attend to everything and the indexer
+ * learns from the KL loss before it routes). msa_kl_align_fwd's loss with
+ * T_i = {0 .. i} for every row.
+ *
+ *   Uses every field of `dims` except topk.
+ *   q, k, q_idx, k_idx, softmax_scale, index_scale, kl_rows, kl_sum and
+ *   index_lse as for msa_kl_align_fwd;
+ *   lse       [B, Hq, N] fp32, the dense main-branch LSE of the same inputs (as
+ *             written by msa_dense_attn_fwd).
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_DENSE_KL) bytes (the
+ *             fixed-order reduction's partial sums).
+ */
+MSA_API int msa_dense_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
+                                   const void* k_idx, const float* lse, float softmax_scale, float index_scale,
+                                   float* kl_rows, float* kl_sum, float* index_lse, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /*
  * Decoding: one new query per sequence against a cache.

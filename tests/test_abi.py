@@ -225,7 +225,7 @@ def test_workspace_sizes(lib):
     assert msa.workspace_bytes(_dims(seqlen=128), msa.MSA_OP_ATTN) == 2 * 128 * 128 * 2
     assert msa.workspace_bytes(_dims(topk=1), msa.MSA_OP_ATTN) == 2 * 8 * 128 * 128 * 2
     assert msa.workspace_bytes(_dims(), msa.MSA_OP_INDEX) == 0
-    assert msa.workspace_bytes(_dims(), 10) == 0
+    assert msa.workspace_bytes(_dims(), 11) == 0
     # the partial outputs dominate: rows * (k-1) * G * D * 2 bytes for bf16
     d = _dims(seqlen=131072, kv_heads=8, group_size=8, topk=16)
     need = msa.workspace_bytes(d, msa.MSA_OP_ATTN)
@@ -316,3 +316,20 @@ def test_dense_attention_arguments(lib):
     assert call(dd=_dims(head_dim=96)) == 3
     assert call(dd=_dims(dtype=msa.MSA_FP8_E4M3)) == 3
     assert call(dd=_dims(seqlen=0), ptrs=dict(q=None, k=None, v=None, o=None, lse=None), ws=None, nws=0) == 0
+
+
+def test_dense_kl_arguments(lib):
+    d = _dims(topk=0)
+    need = msa.workspace_bytes(d, msa.MSA_OP_DENSE_KL)
+    assert need == 256                  # one double per reduction block, 256-byte aligned
+
+    def call(ptrs=None, ws=FAKE, nws=need, dd=d):
+        p = dict(q=FAKE, k=FAKE, qi=FAKE, ki=FAKE, lse=FAKE, rows=FAKE, sum=FAKE, ilse=None)
+        p.update(ptrs or {})
+        return lib.msa_dense_kl_align_fwd(ctypes.byref(dd), p["q"], p["k"], p["qi"], p["ki"], p["lse"], 0.0, 0.0,
+                                          p["rows"], p["sum"], p["ilse"], ws, nws, None)
+    assert call(dict(sum=None)) == 1
+    assert call(dict(ki=None)) == 1
+    assert call(dict(lse=MISALIGNED)) == 4
+    assert call(ws=None, nws=0) == 5
+    assert call(dd=_dims(index_dim=96)) == 3

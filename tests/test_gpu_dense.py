@@ -1,8 +1,9 @@
-"""Parity of the dense causal attention (the warm-up's full attention) through
-the C ABI with the CPU oracle: O within max-abs 1e-2 and LSE within abs 1e-3
-of the float64 oracle given every visible block (pinned against torch's causal
-SDPA). Small shapes on every row, the 32K and 128K shapes on seeded sampled
-rows plus the block-edge rows."""
+"""Parity of the warm-up's dense paths through the C ABI with the CPU oracle:
+the dense causal attention (O within max-abs 1e-2, LSE within abs 1e-3 of the
+float64 oracle given every visible block, which is pinned against torch's
+causal SDPA) and the dense KL loss (rows within 1e-3 + 1e-3|KL|, kl_sum within
+relative 1e-3, the forward KL's bars). Small shapes on every row, the 32K and
+128K shapes on seeded sampled rows plus the block-edge rows."""
 import sys
 import time
 
@@ -88,3 +89,59 @@ def test_dense_large_sampled(name, B, N, rows):
     log(f"  dense forward done ({time.time() - t0:.2f}s)")
     pos = sample_rows(w, n=rows, seed=1)
     _check(w, x, o, lse, pos)
+
+
+def _check_kl(w, x, kl, kl_sum, pos, full_sum=False):
+    b = torch.as_tensor(pos[:, 0], device=x["q"].device)
+    i = torch.as_tensor(pos[:, 1], device=x["q"].device)
+    kh, kih = x["k"].cpu(), x["k_idx"].cpu()
+    rows = O.dense_block_idx_rows(pos, w.kv_heads, w.block_size)
+    want = O.map_positions(
+        lambda c, br, qr, qir: O.kl_rows(None, kh, None, kih, br, c, w.block_size, q_rows=qr, qi_rows=qir),
+        pos, (rows, x["q"][b, i].cpu(), x["q_idx"][b, i].cpu()), workers=16)          # [M, Hkv]
+    got = kl.permute(0, 2, 1)[b, i].cpu().numpy()
+    err = float(np.abs(got - want).max())
+    tol = 1e-3 + 1e-3 * float(np.abs(want).max())
+    log(f"  {w.name}: dense KL on {len(pos)} rows, max|dKL|={err:.2e} (tol {tol:.2e})")
+    assert err <= tol
+    if full_sum:
+        assert abs(float(kl_sum.item()) - float(want.sum())) <= 1e-3 * abs(float(want.sum())) + 1e-3
+
+
+@pytest.mark.parametrize("w", [
+    Workload("dkl_f32", 2, 700, 2, 4, 64, 64, dtype="f32"),
+    Workload("dkl_bf16", 1, 1500, 2, 8, 128, 128),
+    Workload("dkl_g1_mixed_dims", 1, 900, 3, 1, 128, 64),
+    Workload("dkl_g32", 1, 300, 1, 32, 64, 128),
+    Workload("dkl_ragged", 1, 129, 2, 2, 64, 64),
+])
+def test_dense_kl_small(w):
+    log(f"{w.name}: B={w.batch} N={w.seqlen} Hkv={w.kv_heads} G={w.group_size} D={w.head_dim} Di={w.index_dim}")
+    x = {k: (v.to(DEV) if k != "stripes" else v) for k, v in make_inputs(w, device="cpu").items()}
+    _, lse = msa.dense_attn_fwd(x["q"], x["k"], x["v"])
+    kl, kl_sum = msa.dense_kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], lse)
+    torch.cuda.synchronize()
+    pos = np.array([(b, i) for b in range(w.batch) for i in range(w.seqlen)], dtype=np.int64)
+    _check_kl(w, x, kl, kl_sum, pos, full_sum=True)
+
+
+def test_dense_kl_equals_sparse_kl_with_every_block():
+    w = Workload("dkl_vs_sparse", 1, 4096, 2, 8, 128, 128, topk=32)
+    x = make_inputs(w, device=DEV)
+    bi = msa.index_topk(x["q_idx"], x["k_idx"], w.topk)
+    _, lse_s = msa.sparse_attn_fwd(x["q"], x["k"], x["v"], bi)
+    kl_s, sum_s = msa.kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], bi, lse_s)
+    _, lse_d = msa.dense_attn_fwd(x["q"], x["k"], x["v"])
+    kl_d, sum_d = msa.dense_kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], lse_d)
+    torch.cuda.synchronize()
+    assert float((kl_s - kl_d).abs().max()) <= 1e-3 + 1e-3 * float(kl_s.abs().max())
+    assert abs(float(sum_s.item()) - float(sum_d.item())) <= 1e-3 * abs(float(sum_s.item()))
+
+
+def test_dense_kl_n32k_sampled():
+    w = Workload("dkl_n32k", 1, 32768, 8, 8, 128, 128)
+    x = make_inputs(w, device=DEV, kinds=("q_idx", "k_idx", "q", "k", "v"))
+    _, lse = msa.dense_attn_fwd(x["q"], x["k"], x["v"])
+    kl, kl_sum = msa.dense_kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], lse)
+    torch.cuda.synchronize()
+    _check_kl(w, x, kl, kl_sum, sample_rows(w, n=128, seed=1))
