@@ -282,13 +282,14 @@ __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
 // The warm-up's KL (MSA article, "Cómo se entrena MSA": during the first
 // iterations both branches attend to every visible token): the same per-row
 // KL with T_i = {0 .. i}, the teacher normalised by the dense attention's LSE.
-// Query-block outer like the dense attention: one 8-wave work-group per
-// (batch, query block, group, 256-row part), each wave one resident 32-row
-// tile (main and index query operands, the five running sums); K_j and
+// Query-block outer like the dense attention: one 4-wave work-group per
+// (batch, query block, group, 128-row part), each wave one resident 32-row
+// tile (main and index query operands, the five running sums; one wave per
+// SIMD, so the KL tile's temporaries fit without spilling); K_j and
 // K_idx_j stream through two LDS buffers, the next block's rows requested into
 // registers before the current block's scores and stored after them.
 
-constexpr int kDenseKlWaves = 8;
+constexpr int kDenseKlWaves = 4;
 
 // Rows [128][W] of T moved global -> registers -> LDS (SwzTile<T, W>) by NT
 // threads; rows at or past valid_rows are zero-filled.
