@@ -279,31 +279,37 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     const T* kbase = kc + ((size_t)b * C * Hkv + g) * D;
     const T* vbase = vc + ((size_t)b * C * Hkv + g) * D;
 
-    // V block -> LDS (rows past the last visible token zero-filled).
-    constexpr int EPC = 16 / LD::ES;
-    constexpr int CPR = D / EPC;
-    for (int ch = threadIdx.x; ch < kBlock * CPR; ch += blockDim.x) {
-        const int row = ch / CPR, cc = ch % CPR;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (t0 + row <= t_last) x = *reinterpret_cast<const u32x4*>(vbase + (size_t)(t0 + row) * kv_row + cc * EPC);
-        *reinterpret_cast<u32x4*>(vs + row * LD::VROW + cc * 16) = x;
-    }
-
-    // Scores of this wave's 32 keys against the group's heads (columns).
+    // Requests in flight together: this wave's query and key operands, then the
+    // V block (rows past the last visible token zero-filled), which goes to LDS
+    // once the scores are on the matrix cores.
     Op8<T> bq[D / 16];
     const int Hq = Hkv * G;
     load_q_op<T, D>(bq, q + ((size_t)b * Hq + (size_t)g * G + (col < G ? col : 0)) * D, col < G, half);
     const int key = t0 + wave * 32 + col;
+    Op8<T> a[D / 16];
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) {
+        if (key <= t_last) a[sl].load(kbase + (size_t)key * kv_row + 16 * sl + 8 * half);
+        else a[sl].zero();
+    }
+    constexpr int EPC = 16 / LD::ES;
+    constexpr int CPR = D / EPC;
+    constexpr int VPER = kBlock * CPR / 256;
+    static_assert(kBlock * CPR % 256 == 0, "V chunk split");
+    u32x4 vr[VPER];
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+        const int ch = threadIdx.x + u * 256, row = ch / CPR, cc = ch % CPR;
+        vr[u] = t0 + row <= t_last ? *reinterpret_cast<const u32x4*>(vbase + (size_t)(t0 + row) * kv_row + cc * EPC)
+                                   : u32x4{0u, 0u, 0u, 0u};
+    }
     floatx16 s = zero16();
-    {
-        Op8<T> a[D / 16];
 #pragma unroll
-        for (int sl = 0; sl < D / 16; ++sl) {
-            if (key <= t_last) a[sl].load(kbase + (size_t)key * kv_row + 16 * sl + 8 * half);
-            else a[sl].zero();
-        }
+    for (int sl = 0; sl < D / 16; ++sl) mma16(s, a[sl], bq[sl]);
 #pragma unroll
-        for (int sl = 0; sl < D / 16; ++sl) mma16(s, a[sl], bq[sl]);
+    for (int u = 0; u < VPER; ++u) {
+        const int ch = threadIdx.x + u * 256, row = ch / CPR, cc = ch % CPR;
+        *reinterpret_cast<u32x4*>(vs + row * LD::VROW + cc * 16) = vr[u];
     }
     // Lane holds head `col`, keys t0 + 32*wave + 8*(r/4) + 4*half + r%4.
     float m = -__builtin_inff();
