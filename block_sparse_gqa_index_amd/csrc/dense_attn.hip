@@ -139,15 +139,16 @@ __global__ __launch_bounds__(NW * kWave) void dense_attn_kernel(const T* __restr
             for (int t = 0; t < TPW; ++t)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) s[t][kt] = zero16();
+            // Slice outer, key tile inner: four independent accumulation chains.
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
+            for (int sl = 0; sl < D / 16; ++sl) {
+                Op8<T> a[4];
 #pragma unroll
-                for (int sl = 0; sl < D / 16; ++sl) {
-                    Op8<T> a;
-                    KS::load8(a, cur, kt * 32 + col, 16 * sl + 8 * half);
+                for (int kt = 0; kt < 4; ++kt) KS::load8(a[kt], cur, kt * 32 + col, 16 * sl + 8 * half);
 #pragma unroll
-                    for (int t = 0; t < TPW; ++t) mma16(s[t][kt], a, bq[t][sl]);
-                }
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) mma16(s[t][kt], a[kt], bq[t][sl]);
             }
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
