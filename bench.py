@@ -43,6 +43,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CSRC = os.path.join(ROOT, "block_sparse_gqa_index_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_n128k.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_n128k_b64.json")
 
 
 def log(msg):
@@ -91,13 +92,13 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_entry(kernel, workload):
+def traffic_entry(kernel, workload, path=TRAFFIC_FILE):
     """Measured HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE,
     calibrated against a copy of known size) from the committed counter
     summary, if it was taken on this workload and on the current source of the
     file that holds the kernel; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -257,8 +258,10 @@ def bench_decode(args, dev):
 
     def hbm(stage):
         a = nb[stage] / (stage_ms[stage] * 1e-3) / 1e9
+        parts = [traffic_entry(k.strip(), w.name, DECODE_TRAFFIC_FILE) for k in kernels[stage].split("+")]
         return {"kernel": kernels[stage], "bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": a / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes": nb[stage], "ms": stage_ms[stage]}
+                "frac": a / PEAK_HBM_GBS, "traffic": None if None in parts else sum(parts),
+                "algorithmic_bytes": nb[stage], "ms": stage_ms[stage]}
 
     rooflines = {s: hbm(s) for s in ("selection", "attention")}
     dominant = max(rooflines, key=lambda s: stage_ms[s])
