@@ -282,6 +282,34 @@ def bench_decode(args, dev):
         "roofline": rooflines[dominant],
         "rooflines": rooflines,
     }
+    if args.paged:
+        # The same step on paged caches: 128-token pages in a seeded random order and a block table.
+        nbs = -(-C // w.block_size)
+        perm = torch.randperm(B * nbs, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+        table = perm.view(B, nbs).to(dev)
+        pools = {}
+        for name in ("k_idx", "k", "v"):
+            t = x[name]
+            pool = torch.empty((B * nbs, w.block_size) + tuple(t.shape[2:]), dtype=t.dtype, device=dev)
+            pool[perm.long().to(dev)] = t.reshape((B * nbs, w.block_size) + tuple(t.shape[2:]))
+            pools[name] = pool
+        bip = torch.empty_like(bi)
+        op, lsep = torch.empty_like(o), torch.empty_like(lse)
+
+        def pstep():
+            msa.decode_paged(x["q_idx"], pools["k_idx"], x["q"], pools["k"], pools["v"], table, x["seqlens"], w.topk,
+                             block_idx=bip, o=op, lse=lsep, workspace=ws)
+        for _ in range(args.warmup):
+            pstep()
+        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in evp:
+            e[0].record(stream)
+            pstep()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        out["paged"] = {"ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evp])),
+                        "same_results": bool(torch.equal(bip, bi) and torch.equal(op, o) and torch.equal(lsep, lse))}
+        del pools
     if args.index_fp8:
         # The selection on an fp8 e4m3 index cache (integer values: exact, same selection).
         fp8 = torch.float8_e4m3fn
@@ -408,6 +436,8 @@ def main():
                     help="also time the main-branch backward (msa_sparse_attn_bwd) on the step's outputs")
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step (64 sequences, 128K-token caches) instead of the forward")
+    ap.add_argument("--paged", action="store_true",
+                    help="with --decode: also time the step on paged caches (block table, random page order)")
     ap.add_argument("--dense", action="store_true",
                     help="time the warm-up's dense causal attention (msa_dense_attn_fwd) on the 128K shapes instead")
     ap.add_argument("--copy-mib", type=int, default=0,

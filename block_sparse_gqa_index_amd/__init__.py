@@ -20,6 +20,7 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   decode_index_topk(q_idx, k_idx, seqlens, topk)   -> block_idx int32 [B, Hkv, k] (one new query per sequence)
   decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq])
   decode(q_idx, k_idx, q, k, v, seqlens, topk)     -> (block_idx, o, lse): both decode steps
+  decode_paged*(..., block_table, ...)             -> the decode calls on page pools [P, 128, ...] + a block table
   dense_attn_fwd(q, k, v)                          -> (o, lse): causal attention over every visible key (warm-up)
   dense_kl_align_fwd(q, k, q_idx, k_idx, lse)      -> (kl_rows, kl_sum): the KL loss over every visible token
   workspace_bytes(dims, op)
@@ -41,7 +42,7 @@ STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPP
 EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
            "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
            "msa_decode_index_topk", "msa_decode_attn", "msa_decode", "msa_dense_attn_fwd",
-           "msa_dense_kl_align_fwd",
+           "msa_dense_kl_align_fwd", "msa_decode_paged_index_topk", "msa_decode_paged_attn", "msa_decode_paged",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -89,6 +90,10 @@ def load_library(path: str = LIB_PATH):
     lib.msa_dense_attn_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_dense_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
                                            sz, vp]
+    i32 = ctypes.c_int32
+    lib.msa_decode_paged_index_topk.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.msa_decode_paged_attn.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.msa_decode_paged.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
     lib.msa_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_strerror.argtypes = [ctypes.c_int]
@@ -97,7 +102,8 @@ def load_library(path: str = LIB_PATH):
     for f in (lib.msa_index_topk, lib.msa_check_block_idx, lib.msa_sparse_attn_fwd, lib.msa_sparse_attn_fwd_stages,
               lib.msa_kl_align_fwd, lib.msa_forward, lib.msa_kl_align_bwd, lib.msa_sparse_attn_bwd,
               lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode, lib.msa_dense_attn_fwd,
-              lib.msa_dense_kl_align_fwd):
+              lib.msa_dense_kl_align_fwd, lib.msa_decode_paged_index_topk, lib.msa_decode_paged_attn,
+              lib.msa_decode_paged):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -498,3 +504,94 @@ def dense_kl_align_fwd(q, k, q_idx, k_idx, lse, softmax_scale=0.0, index_scale=0
                                       float(softmax_scale), float(index_scale), _ptr(kl_rows), _ptr(kl_sum),
                                       _ptr(index_lse), _ptr(ws), nws, _stream(q.device)))
     return kl_rows, kl_sum
+
+
+def _paged_shapes(block_table, seqlens, k_idx_pages=None, k_pages=None, v_pages=None):
+    _req(block_table, "block_table", dtype=torch.int32, ndim=2)
+    _req(seqlens, "seqlens", dtype=torch.int32, ndim=1)
+    B, MB = block_table.shape
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must be [B] with B = block_table.shape[0]")
+    P = None
+    if k_idx_pages is not None:
+        _req(k_idx_pages, "k_idx_pages", ndim=3)
+        if k_idx_pages.shape[1] != 128:
+            raise ValueError("k_idx_pages must be [P, 128, Di]")
+        P = k_idx_pages.shape[0]
+    if k_pages is not None:
+        _req(k_pages, "k_pages", ndim=4)
+        _req(v_pages, "v_pages", dtype=k_pages.dtype, ndim=4)
+        if k_pages.shape[1] != 128 or tuple(v_pages.shape) != tuple(k_pages.shape):
+            raise ValueError("k_pages and v_pages must be [P, 128, Hkv, D]")
+        if P is not None and k_pages.shape[0] != P:
+            raise ValueError("the page pools must hold the same number of pages")
+        P = k_pages.shape[0]
+    return B, MB * 128, P
+
+
+def decode_paged_index_topk(q_idx, k_idx_pages, block_table, seqlens, topk, block_idx=None, workspace=None):
+    """decode_index_topk on a paged index-key cache: k_idx_pages [P, 128, Di],
+    block_table int32 [B, max_blocks] (page of each block) -> int32 [B, Hkv, topk]."""
+    lib = load_library()
+    B, C, P = _paged_shapes(block_table, seqlens, k_idx_pages=k_idx_pages)
+    _req(q_idx, "q_idx", dtype=k_idx_pages.dtype, ndim=3)
+    Hkv, Di = q_idx.shape[1], q_idx.shape[2]
+    if q_idx.shape[0] != B or k_idx_pages.shape[2] != Di:
+        raise ValueError("q_idx must be [B, Hkv, Di]")
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q_idx.device)
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
+    dims = make_dims(B, C, Hkv, 1, 64, Di, topk, q_idx.dtype)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_INDEX), q_idx.device, workspace)
+    _check(lib.msa_decode_paged_index_topk(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx_pages), _ptr(block_table), P,
+                                           _ptr(seqlens), _ptr(block_idx), _ptr(ws), nws, _stream(q_idx.device)))
+    return block_idx
+
+
+def decode_paged_attn(q, k_pages, v_pages, block_table, seqlens, block_idx, softmax_scale=0.0, o=None, lse=None,
+                      workspace=None):
+    """decode_attn on paged K/V caches [P, 128, Hkv, D] -> (o [B,Hq,D], lse fp32 [B,Hq])."""
+    lib = load_library()
+    B, C, P = _paged_shapes(block_table, seqlens, k_pages=k_pages, v_pages=v_pages)
+    _req(q, "q", dtype=k_pages.dtype, ndim=3)
+    Hkv, D = k_pages.shape[2], k_pages.shape[3]
+    if q.shape[0] != B or q.shape[2] != D or q.shape[1] % Hkv:
+        raise ValueError("q must be [B, Hq, D] with Hq a multiple of Hkv")
+    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
+    topk = block_idx.shape[2]
+    G = q.shape[1] // Hkv
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
+    dims = make_dims(B, C, Hkv, G, D, 64, topk, q.dtype)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_ATTN), q.device, workspace)
+    _check(lib.msa_decode_paged_attn(ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), P,
+                                     _ptr(seqlens), _ptr(block_idx), float(softmax_scale), _ptr(o), _ptr(lse),
+                                     _ptr(ws), nws, _stream(q.device)))
+    return o, lse
+
+
+def decode_paged(q_idx, k_idx_pages, q, k_pages, v_pages, block_table, seqlens, topk, softmax_scale=0.0,
+                 block_idx=None, o=None, lse=None, workspace=None):
+    """One decode step on paged caches (msa_decode_paged) -> (block_idx, o, lse)."""
+    lib = load_library()
+    B, C, P = _paged_shapes(block_table, seqlens, k_idx_pages=k_idx_pages, k_pages=k_pages, v_pages=v_pages)
+    _req(q_idx, "q_idx", dtype=q.dtype, ndim=3)
+    _req(q, "q", dtype=k_pages.dtype, ndim=3)
+    Hkv, Di, D = q_idx.shape[1], q_idx.shape[2], k_pages.shape[3]
+    if k_pages.shape[2] != Hkv or q.shape[1] % Hkv or q.shape[2] != D:
+        raise ValueError("inconsistent shapes")
+    G = q.shape[1] // Hkv
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
+    dims = make_dims(B, C, Hkv, G, D, Di, topk, q.dtype)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE), q.device, workspace)
+    _check(lib.msa_decode_paged(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx_pages), _ptr(q), _ptr(k_pages),
+                                _ptr(v_pages), _ptr(block_table), P, _ptr(seqlens), float(softmax_scale),
+                                _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(q.device)))
+    return block_idx, o, lse

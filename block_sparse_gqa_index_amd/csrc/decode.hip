@@ -33,6 +33,11 @@
 //   decode_combine_kernel one work-group per (sequence, group): the kept
 //                         blocks' partials merged in slot order -> O, LSE.
 // Every sum runs in a fixed order: results are bitwise reproducible.
+//
+// The caches are either contiguous per sequence ([B, C, ...]) or paged: a pool
+// of 128-token pages ([P, 128, ...]) and a block table [B, ceil(C/128)] naming
+// the page of every block of every sequence (the block ids MSA selects are then
+// page-table entries: one lookup per block, no other change).
 #include "msa_decode.h"
 #include "msa_tiles.h"
 
@@ -80,6 +85,7 @@ template <typename T, int DI>
 __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict__ q_idx,
                                                             const T* __restrict__ k_idx,
                                                             const int32_t* __restrict__ seqlens,
+                                                            const int32_t* __restrict__ pages, int num_pages,
                                                             float* __restrict__ scores, int C, int Hkv,
                                                             int nbs, int gchunks) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -91,6 +97,16 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
     const int L = (n - 1) / kBlock;   // competing blocks: 0 .. L-1
     if (j >= L) return;
     const int g = gc * kGroupCols + col;
+    // Block j of the sequence: contiguous in the cache, or the page the block table names.
+    const T* kb = k_idx + ((size_t)b * C + (size_t)j * kBlock) * DI;
+    if (pages) {
+        const int pg = pages[(size_t)b * nbs + j];
+        if (pg < 0 || pg >= num_pages) {   // not a page of the pool: the block scores -inf, nothing is read
+            if (half == 0 && g < Hkv) scores[((size_t)b * Hkv + g) * nbs + j] = -__builtin_inff();
+            return;
+        }
+        kb = k_idx + (size_t)pg * kBlock * DI;
+    }
 
     using MM = DecMma<T>;
     constexpr int NS = DI / MM::KD;   // contraction slices
@@ -105,7 +121,6 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
 
     // Tiles of 32 keys; bf16 and fp8 keep all four tiles' operands in flight, fp32 two.
     constexpr int TF = sizeof(T) == 4 ? 2 : 4;
-    const T* kb = k_idx + ((size_t)b * C + (size_t)j * kBlock) * DI;
     float m = -__builtin_inff();
 #pragma unroll
     for (int t0 = 0; t0 < 4; t0 += TF) {
@@ -251,6 +266,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
                                                           const T* __restrict__ vc,
                                                           const int32_t* __restrict__ seqlens,
                                                           const int32_t* __restrict__ block_idx,
+                                                          const int32_t* __restrict__ pages, int num_pages,
                                                           float* __restrict__ po, float* __restrict__ plse, int C,
                                                           int Hkv, int G, int k, float scale_log2) {
     using LD = DecodeLds<T, D>;
@@ -269,15 +285,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     const int j = block_idx[item];
     // Empty slot (padding, a block past the query, or an invalid length): no
     // tokens, LSE -inf, and the merge skips the slot.
-    if (!length_ok(n, C) || j < 0 || (int64_t)j * kBlock > i) {
+    const int nbs = (C + kBlock - 1) / kBlock;
+    const int pg = (pages && j >= 0 && j < nbs) ? pages[(size_t)b * nbs + j] : 0;
+    if (!length_ok(n, C) || j < 0 || (int64_t)j * kBlock > i || (pages && (pg < 0 || pg >= num_pages))) {
         if (threadIdx.x < G) plse[item * G + threadIdx.x] = -__builtin_inff();
         return;
     }
     const int t0 = j * kBlock;
     const int t_last = min(t0 + kBlock - 1, i);
     const size_t kv_row = (size_t)Hkv * D;   // elements between consecutive tokens of one head
-    const T* kbase = kc + ((size_t)b * C * Hkv + g) * D;
-    const T* vbase = vc + ((size_t)b * C * Hkv + g) * D;
+    // First token of the block (contiguous cache, or the named page); token
+    // t0 + r is r rows further.
+    const size_t first = pages ? (size_t)pg * kBlock : (size_t)b * C + t0;
+    const T* kbase = kc + (first * Hkv + g) * D;
+    const T* vbase = vc + (first * Hkv + g) * D;
 
     // Requests in flight together: this wave's query and key operands, then the
     // V block (rows past the last visible token zero-filled), which goes to LDS
@@ -289,7 +310,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     Op8<T> a[D / 16];
 #pragma unroll
     for (int sl = 0; sl < D / 16; ++sl) {
-        if (key <= t_last) a[sl].load(kbase + (size_t)key * kv_row + 16 * sl + 8 * half);
+        if (key <= t_last) a[sl].load(kbase + (size_t)(key - t0) * kv_row + 16 * sl + 8 * half);
         else a[sl].zero();
     }
     constexpr int EPC = 16 / LD::ES;
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
 #pragma unroll
     for (int u = 0; u < VPER; ++u) {
         const int ch = threadIdx.x + u * 256, row = ch / CPR, cc = ch % CPR;
-        vr[u] = t0 + row <= t_last ? *reinterpret_cast<const u32x4*>(vbase + (size_t)(t0 + row) * kv_row + cc * EPC)
+        vr[u] = t0 + row <= t_last ? *reinterpret_cast<const u32x4*>(vbase + (size_t)row * kv_row + cc * EPC)
                                    : u32x4{0u, 0u, 0u, 0u};
     }
     floatx16 s = zero16();
@@ -477,24 +498,24 @@ void launch_topk(const float* scores, const int32_t* seqlens, int32_t* block_idx
 
 template <typename T, int DI>
 void launch_scores(const DecodeDims& d, const void* q_idx, const void* k_idx, const int32_t* seqlens,
-                   float* scores, hipStream_t st) {
+                   const int32_t* pages, int num_pages, float* scores, hipStream_t st) {
     const int gchunks = (d.Hkv + kGroupCols - 1) / kGroupCols;
     const int lmax = (d.C - 1) / kBlock;   // competing blocks of a full cache
     if (lmax == 0) return;
     hipLaunchKernelGGL((decode_scores_kernel<T, DI>), dim3((lmax + 3) / 4, d.B * gchunks), dim3(256), 0, st,
-                       static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, scores, d.C, d.Hkv,
-                       d.nbs(), gchunks);
+                       static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, pages, num_pages, scores,
+                       d.C, d.Hkv, d.nbs(), gchunks);
 }
 
 template <typename T, int D>
 void launch_attn(const DecodeDims& d, const void* q, const void* k, const void* v, const int32_t* seqlens,
-                 const int32_t* block_idx, float scale, void* o, float* lse, const DecodeWorkspace& W,
-                 unsigned char* ws, hipStream_t st) {
+                 const int32_t* block_idx, const int32_t* pages, int num_pages, float scale, void* o, float* lse,
+                 const DecodeWorkspace& W, unsigned char* ws, hipStream_t st) {
     float* po = reinterpret_cast<float*>(ws + W.po);
     float* pl = reinterpret_cast<float*>(ws + W.plse);
     hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.k, d.Hkv, d.B), dim3(256), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), seqlens,
-                       block_idx, po, pl, d.C, d.Hkv, d.G, d.k, scale * 1.4426950408889634f);
+                       block_idx, pages, num_pages, po, pl, d.C, d.Hkv, d.G, d.k, scale * 1.4426950408889634f);
     hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(d.Hkv, d.B), dim3(256), 0, st, po, pl,
                        static_cast<T*>(o), lse, d.Hkv, d.G, D, d.k);
 }
@@ -513,17 +534,17 @@ DecodeWorkspace decode_workspace_layout(const DecodeDims& d) {
 }
 
 hipError_t launch_decode_index(const DecodeDims& d, const void* q_idx, const void* k_idx, const int32_t* seqlens,
-                               int32_t* block_idx, void* ws, hipStream_t st) {
+                               const int32_t* pages, int num_pages, int32_t* block_idx, void* ws, hipStream_t st) {
     float* scores = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + decode_workspace_layout(d).scores);
     if (d.dtype == 0) {
-        if (d.Di == 128) launch_scores<bf16_t, 128>(d, q_idx, k_idx, seqlens, scores, st);
-        else launch_scores<bf16_t, 64>(d, q_idx, k_idx, seqlens, scores, st);
+        if (d.Di == 128) launch_scores<bf16_t, 128>(d, q_idx, k_idx, seqlens, pages, num_pages, scores, st);
+        else launch_scores<bf16_t, 64>(d, q_idx, k_idx, seqlens, pages, num_pages, scores, st);
     } else if (d.dtype == 2) {
-        if (d.Di == 128) launch_scores<fp8_t, 128>(d, q_idx, k_idx, seqlens, scores, st);
-        else launch_scores<fp8_t, 64>(d, q_idx, k_idx, seqlens, scores, st);
+        if (d.Di == 128) launch_scores<fp8_t, 128>(d, q_idx, k_idx, seqlens, pages, num_pages, scores, st);
+        else launch_scores<fp8_t, 64>(d, q_idx, k_idx, seqlens, pages, num_pages, scores, st);
     } else {
-        if (d.Di == 128) launch_scores<float, 128>(d, q_idx, k_idx, seqlens, scores, st);
-        else launch_scores<float, 64>(d, q_idx, k_idx, seqlens, scores, st);
+        if (d.Di == 128) launch_scores<float, 128>(d, q_idx, k_idx, seqlens, pages, num_pages, scores, st);
+        else launch_scores<float, 64>(d, q_idx, k_idx, seqlens, pages, num_pages, scores, st);
     }
     const int k1 = d.k - 1;
     if (k1 <= 3) launch_topk<3>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
@@ -534,16 +555,16 @@ hipError_t launch_decode_index(const DecodeDims& d, const void* q_idx, const voi
 }
 
 hipError_t launch_decode_attn(const DecodeDims& d, const void* q, const void* k, const void* v,
-                              const int32_t* seqlens, const int32_t* block_idx, float scale, void* o, float* lse,
-                              void* ws, hipStream_t st) {
+                              const int32_t* seqlens, const int32_t* block_idx, const int32_t* pages, int num_pages,
+                              float scale, void* o, float* lse, void* ws, hipStream_t st) {
     const DecodeWorkspace W = decode_workspace_layout(d);
     unsigned char* base = static_cast<unsigned char*>(ws);
     if (d.dtype == 0) {
-        if (d.D == 128) launch_attn<bf16_t, 128>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
-        else launch_attn<bf16_t, 64>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
+        if (d.D == 128) launch_attn<bf16_t, 128>(d, q, k, v, seqlens, block_idx, pages, num_pages, scale, o, lse, W, base, st);
+        else launch_attn<bf16_t, 64>(d, q, k, v, seqlens, block_idx, pages, num_pages, scale, o, lse, W, base, st);
     } else {
-        if (d.D == 128) launch_attn<float, 128>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
-        else launch_attn<float, 64>(d, q, k, v, seqlens, block_idx, scale, o, lse, W, base, st);
+        if (d.D == 128) launch_attn<float, 128>(d, q, k, v, seqlens, block_idx, pages, num_pages, scale, o, lse, W, base, st);
+        else launch_attn<float, 64>(d, q, k, v, seqlens, block_idx, pages, num_pages, scale, o, lse, W, base, st);
     }
     return hipGetLastError();
 }

@@ -307,7 +307,7 @@ int msa_decode_index_topk(const msa_dims* dims, const void* q_idx, const void* k
     LaunchDims L;
     int st = check_decode(dims, MSA_OP_DECODE_INDEX, &L, {q_idx, k_idx, seqlens, block_idx}, ws, ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
-    return hip_status(msa::launch_decode_index(decode_dims(L), q_idx, k_idx, seqlens, block_idx, ws,
+    return hip_status(msa::launch_decode_index(decode_dims(L), q_idx, k_idx, seqlens, nullptr, 0, block_idx, ws,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -318,7 +318,7 @@ int msa_decode_attn(const msa_dims* dims, const void* q, const void* k, const vo
     int st = check_decode(dims, MSA_OP_DECODE_ATTN, &L, {q, k, v, seqlens, block_idx, o, lse}, ws, ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
-    return hip_status(msa::launch_decode_attn(decode_dims(L), q, k, v, seqlens, block_idx, scale, o, lse, ws,
+    return hip_status(msa::launch_decode_attn(decode_dims(L), q, k, v, seqlens, block_idx, nullptr, 0, scale, o, lse, ws,
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -332,8 +332,55 @@ int msa_decode(const msa_dims* dims, const void* q_idx, const void* k_idx, const
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const msa::DecodeDims d = decode_dims(L);
-    if (msa::launch_decode_index(d, q_idx, k_idx, seqlens, block_idx, ws, s) != hipSuccess) return MSA_ERR_HIP;
-    return hip_status(msa::launch_decode_attn(d, q, k, v, seqlens, block_idx, scale, o, lse, ws, s));
+    if (msa::launch_decode_index(d, q_idx, k_idx, seqlens, nullptr, 0, block_idx, ws, s) != hipSuccess)
+        return MSA_ERR_HIP;
+    return hip_status(msa::launch_decode_attn(d, q, k, v, seqlens, block_idx, nullptr, 0, scale, o, lse, ws, s));
+}
+
+int msa_decode_paged_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx_pages,
+                                const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
+                                int32_t* block_idx, void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    if (num_pages < 0) return MSA_ERR_SHAPE;
+    int st = check_decode(dims, MSA_OP_DECODE_INDEX, &L, {q_idx, k_idx_pages, block_table, seqlens, block_idx}, ws,
+                          ws_bytes);
+    if (st != MSA_OK || empty(L)) return st;
+    return hip_status(msa::launch_decode_index(decode_dims(L), q_idx, k_idx_pages, seqlens, block_table, num_pages,
+                                               block_idx, ws, static_cast<hipStream_t>(stream)));
+}
+
+int msa_decode_paged_attn(const msa_dims* dims, const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
+                          const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
+                          size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    if (num_pages < 0) return MSA_ERR_SHAPE;
+    int st = check_decode(dims, MSA_OP_DECODE_ATTN, &L, {q, k_pages, v_pages, block_table, seqlens, block_idx, o, lse},
+                          ws, ws_bytes);
+    if (st != MSA_OK || empty(L)) return st;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    return hip_status(msa::launch_decode_attn(decode_dims(L), q, k_pages, v_pages, seqlens, block_idx, block_table,
+                                              num_pages, scale, o, lse, ws, static_cast<hipStream_t>(stream)));
+}
+
+int msa_decode_paged(const msa_dims* dims, const void* q_idx, const void* k_idx_pages, const void* q,
+                     const void* k_pages, const void* v_pages, const int32_t* block_table, int32_t num_pages,
+                     const int32_t* seqlens, float softmax_scale, int32_t* block_idx, void* o, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    if (num_pages < 0) return MSA_ERR_SHAPE;
+    int st = check_decode(dims, MSA_OP_DECODE, &L,
+                          {q_idx, k_idx_pages, q, k_pages, v_pages, block_table, seqlens, block_idx, o, lse}, ws,
+                          ws_bytes);
+    if (st != MSA_OK || empty(L)) return st;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const msa::DecodeDims d = decode_dims(L);
+    if (msa::launch_decode_index(d, q_idx, k_idx_pages, seqlens, block_table, num_pages, block_idx, ws, s) !=
+        hipSuccess)
+        return MSA_ERR_HIP;
+    return hip_status(msa::launch_decode_attn(d, q, k_pages, v_pages, seqlens, block_idx, block_table, num_pages,
+                                              scale, o, lse, ws, s));
 }
 
 }  // extern "C"

@@ -24,13 +24,14 @@ struct DecodeWorkspace {
 
 DecodeWorkspace decode_workspace_layout(const DecodeDims& d);
 
-// Block scores then top-k -> block_idx [B, Hkv, k].
+// Block scores then top-k -> block_idx [B, Hkv, k]. `pages` (nullable): block
+// table [B, ceil(C/128)] into a pool of num_pages 128-token pages holding k_idx.
 hipError_t launch_decode_index(const DecodeDims& d, const void* q_idx, const void* k_idx, const int32_t* seqlens,
-                               int32_t* block_idx, void* ws, hipStream_t st);
+                               const int32_t* pages, int num_pages, int32_t* block_idx, void* ws, hipStream_t st);
 
-// Per-block partials then their merge -> o [B, Hq, D], lse [B, Hq].
+// Per-block partials then their merge -> o [B, Hq, D], lse [B, Hq]; `pages` as above for K and V.
 hipError_t launch_decode_attn(const DecodeDims& d, const void* q, const void* k, const void* v,
-                              const int32_t* seqlens, const int32_t* block_idx, float scale, void* o, float* lse,
-                              void* ws, hipStream_t st);
+                              const int32_t* seqlens, const int32_t* block_idx, const int32_t* pages, int num_pages,
+                              float scale, void* o, float* lse, void* ws, hipStream_t st);
 
 }  // namespace msa

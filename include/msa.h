@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define MSA_API __attribute__((visibility("default")))
@@ -367,6 +367,33 @@ MSA_API int msa_decode_attn(const msa_dims* dims, const void* q, const void* k, 
 MSA_API int msa_decode(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q, const void* k,
                        const void* v, const int32_t* seqlens, float softmax_scale, int32_t* block_idx, void* o,
                        float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decoding against a paged cache: the same computation as msa_decode_index_topk,
+ * msa_decode_attn and msa_decode, with each cache held as a pool of 128-token
+ * pages and a block table naming the page of every block of every sequence
+ * (the MSA block, the unit the index branch selects, is the page: Flash-MSA
+ * article, block-wise sparsity).
+ *   k_idx_pages [P, 128, Di], k_pages and v_pages [P, 128, Hkv, D]: pools of
+ *             P = num_pages pages (dtype as for the contiguous calls).
+ *   block_table [B, ceil(C / 128)] int32 on the DEVICE: page of block j of
+ *             sequence b (C = dims.seqlen, the capacity). Entries of blocks
+ *             at or past ceil(n_b / 128) are not read. An entry outside
+ *             [0, num_pages) is not an error: that block is never read, it
+ *             scores -inf in the selection and contributes no tokens.
+ *   Other arguments, outputs and workspaces as for the contiguous calls.
+ */
+MSA_API int msa_decode_paged_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx_pages,
+                                        const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
+                                        int32_t* block_idx, void* ws, size_t ws_bytes, void* stream);
+MSA_API int msa_decode_paged_attn(const msa_dims* dims, const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
+                                  const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream);
+MSA_API int msa_decode_paged(const msa_dims* dims, const void* q_idx, const void* k_idx_pages, const void* q,
+                             const void* k_pages, const void* v_pages, const int32_t* block_table,
+                             int32_t num_pages, const int32_t* seqlens, float softmax_scale, int32_t* block_idx,
+                             void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes the given entry point needs for these sizes; 0 if the sizes
  * are invalid or the op needs none. Pure host arithmetic. */

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.msa_abi_version() == 3
+    assert lib.msa_abi_version() == 4
     for s in range(7):
         assert lib.msa_strerror(s)
     assert lib.msa_strerror(99) == b"unknown status"
@@ -333,3 +333,23 @@ def test_dense_kl_arguments(lib):
     assert call(dict(lse=MISALIGNED)) == 4
     assert call(ws=None, nws=0) == 5
     assert call(dd=_dims(index_dim=96)) == 3
+
+
+def test_paged_decode_arguments(lib):
+    d = _dims(batch=4, seqlen=5000, kv_heads=8, group_size=8, topk=16)
+    need = msa.workspace_bytes(d, msa.MSA_OP_DECODE)
+
+    def call(ptrs=None, pages=10, ws=FAKE, nws=need, dd=d):
+        p = dict(qi=FAKE, ki=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
+        p.update(ptrs or {})
+        return lib.msa_decode_paged(ctypes.byref(dd), p["qi"], p["ki"], p["q"], p["k"], p["v"], p["bt"], pages,
+                                    p["lens"], 0.0, p["bi"], p["o"], p["lse"], ws, nws, None)
+    assert call(dict(bt=None)) == 1
+    assert call(dict(bt=MISALIGNED)) == 4
+    assert call(pages=-1) == 2
+    assert call(nws=need - 1) == 5
+    assert call(dd=_dims(dtype=msa.MSA_FP8_E4M3)) == 3
+    assert lib.msa_decode_paged_index_topk(ctypes.byref(_dims(dtype=msa.MSA_FP8_E4M3)), FAKE, FAKE, None, 10,
+                                           FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert lib.msa_decode_paged_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -3, FAKE, FAKE, 0.0, FAKE, FAKE,
+                                     FAKE, need, None) == 2

@@ -183,3 +183,69 @@ def test_decode_fp8_index_cache():
     bi8 = msa.decode_index_topk(x["q_idx"].to(fp8), x["k_idx"].to(fp8), x["seqlens"], w.topk)
     torch.cuda.synchronize()
     assert torch.equal(bi, bi8)
+
+
+def _to_pages(x, w, spare=5, seed=7):
+    """The caches of x as page pools [P, 128, ...] in a seeded random page
+    order (plus `spare` pages of other values) and the block table [B, nb]."""
+    B, C = w.batch, w.seqlen
+    nb = -(-C // 128)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    P = B * nb + spare
+    perm = torch.randperm(P, generator=g)[: B * nb].to(torch.int32)
+    table = perm.view(B, nb)
+    pools = {}
+    for name in ("k_idx", "k", "v"):
+        t = x[name]
+        pad = nb * 128 - C
+        if pad:
+            t = torch.cat([t, torch.zeros((B, pad) + tuple(t.shape[2:]), dtype=t.dtype, device=t.device)], dim=1)
+        pool = torch.randn((P, 128) + tuple(t.shape[2:]), generator=g).to(t.dtype).to(t.device)
+        pool[perm.long().to(t.device)] = t.reshape((B * nb, 128) + tuple(t.shape[2:]))
+        pools[name] = pool
+    return pools, table.to(x["k"].device), P
+
+
+@pytest.mark.parametrize("w", [
+    Workload("paged_bf16", 10, 1000, 2, 8, 128, 128, topk=3),
+    Workload("paged_f32", 10, 1000, 1, 4, 64, 64, topk=4, dtype="f32"),
+    Workload("paged_k16", 6, 4096, 8, 8, 128, 128, topk=16),
+])
+def test_decode_paged_equals_contiguous(w):
+    """Paged caches (random page order) give bitwise the contiguous decode's
+    results, which the oracle checks."""
+    lengths = [min(x, w.seqlen) for x in EDGE][: w.batch]
+    lengths[-1] = w.seqlen
+    x, bi, o, lse = _run(w, lengths)
+    pools, table, P = _to_pages(x, w)
+    bip, op, lsep = msa.decode_paged(x["q_idx"], pools["k_idx"], x["q"], pools["k"], pools["v"], table, x["seqlens"],
+                                     w.topk)
+    bip2 = msa.decode_paged_index_topk(x["q_idx"], pools["k_idx"], table, x["seqlens"], w.topk)
+    op2, lsep2 = msa.decode_paged_attn(x["q"], pools["k"], pools["v"], table, x["seqlens"], bip2)
+    torch.cuda.synchronize()
+    assert torch.equal(bip, bi) and torch.equal(op, o) and torch.equal(lsep, lse)
+    assert torch.equal(bip2, bi) and torch.equal(op2, o) and torch.equal(lsep2, lse)
+    _check(w, x, bip, op, lsep)
+
+
+def test_decode_paged_fp8_index_and_bad_pages():
+    fp8 = torch.float8_e4m3fn
+    w = Workload("paged_fp8", 4, 3000, 4, 4, 128, 128, topk=8)
+    x = _dev(make_decode_inputs(w, device="cpu", lengths=[3000, 2000, 700, 129]))
+    pools, table, P = _to_pages(x, w)
+    bi = msa.decode_index_topk(x["q_idx"], x["k_idx"], x["seqlens"], w.topk)
+    bi8 = msa.decode_paged_index_topk(x["q_idx"].to(fp8), pools["k_idx"].to(fp8), table, x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(bi8, bi)
+    # Page ids outside the pool: those blocks are never read; the other sequences are unchanged.
+    bad = table.clone()
+    bad[0, 3] = -1
+    bad[0, 5] = P
+    bip, op, lsep = msa.decode_paged(x["q_idx"], pools["k_idx"], x["q"], pools["k"], pools["v"], bad, x["seqlens"],
+                                     w.topk)
+    bic, oc, lsec = msa.decode(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(bip[1:], bic[1:]) and torch.equal(op[1:], oc[1:]) and torch.equal(lsep[1:], lsec[1:])
+    # 23 competing blocks for k - 1 = 7 slots: the -inf blocks are never kept
+    assert torch.isfinite(lsep[0]).all() and bool(((bip[0] != 3) & (bip[0] != 5)).all())
