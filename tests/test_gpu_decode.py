@@ -249,3 +249,16 @@ def test_decode_paged_fp8_index_and_bad_pages():
     assert torch.equal(bip[1:], bic[1:]) and torch.equal(op[1:], oc[1:]) and torch.equal(lsep[1:], lsec[1:])
     # 23 competing blocks for k - 1 = 7 slots: the -inf blocks are never kept
     assert torch.isfinite(lsep[0]).all() and bool(((bip[0] != 3) & (bip[0] != 5)).all())
+
+
+def test_decode_1m_capacity():
+    """Million-token caches (up to 8191 competing blocks: the top-k scans its
+    scores in several chunks per lane), the 1M workload's model sizes."""
+    w = Workload("dec_1m", 2, 1048576, 4, 8, 128, 128, topk=16)
+    x = make_decode_inputs(w, device=DEV, lengths=[1048576, 700001])
+    bi, o, lse = msa.decode(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], x["seqlens"], w.topk)
+    bi8 = msa.decode_index_topk(x["q_idx"].to(torch.float8_e4m3fn), x["k_idx"].to(torch.float8_e4m3fn),
+                                x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(bi, bi8)
+    _check(w, x, bi, o, lse)
