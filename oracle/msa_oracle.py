@@ -42,11 +42,12 @@ Readings of points the pages leave open (each listed in the design notes):
     that selected its block;
   * the KL term's backward holds the teacher fixed (gradient stopped at the
     index branch input) and reaches q_idx and k_idx only;
-  * decoding appends one token per sequence: sequence b holds n_b cached
-    tokens (positions 0 .. n_b - 1, the new one last) and its new query is the
-    query of position n_b - 1, so its selection and attention are exactly the
-    forward's row n_b - 1; cache slots at or past n_b are never read; a length
-    outside [1, capacity] gives an all -1 selection, O = 0 and LSE = -inf.
+  * decoding appends R >= 1 tokens per sequence: sequence b holds n_b cached
+    tokens (positions 0 .. n_b - 1, the new ones last) and its r-th new query
+    is the query of position n_b - R + r, so its selection and attention are
+    exactly the forward's row there; cache slots at or past n_b are never
+    read; a length outside [1, capacity] (or a negative position) gives an
+    all -1 selection, O = 0 and LSE = -inf.
 
 Parity: every function here is pinned by tests that do not re-use its code
 (brute force, closed forms, torch's dense SDPA, scipy's entropy, invariants).
@@ -506,53 +507,70 @@ def dense_block_idx_rows(positions, Hkv, Bk):
     return out
 
 
-def _decode_positions(seqlens, capacity):
-    """(b, n_b - 1) for the sequences whose length is in [1, capacity], and
-    their batch indices."""
+def _decode_positions(seqlens, capacity, R=1):
+    """Query positions of a decode step: R new tokens per sequence, the r-th at
+    position n_b - R + r. Returns (positions [M, 2] as (b, i), the (b, r) of
+    each) for the rows that exist: n_b in [1, capacity] and i >= 0."""
     n = np.asarray(seqlens, dtype=np.int64).reshape(-1)
-    ok = np.nonzero((n >= 1) & (n <= capacity))[0]
-    return np.stack([ok, n[ok] - 1], axis=1).reshape(-1, 2), ok
+    rows = [(b, r, int(n[b]) - R + r) for b in range(len(n)) for r in range(R)
+            if 1 <= n[b] <= capacity and int(n[b]) - R + r >= 0]
+    pos = np.array([(b, i) for b, _, i in rows], dtype=np.int64).reshape(-1, 2)
+    br = np.array([(b, r) for b, r, _ in rows], dtype=np.int64).reshape(-1, 2)
+    return pos, br
 
 
 def decode_index_topk(q_idx, k_idx, seqlens, Bk, k):
-    """Block selection of one new query per sequence against a cache.
+    """Block selection of the new queries of each sequence against a cache.
 
     [P2] "Cómo funcionan las dos ramas" and "El codiseño del kernel" (the same
-    selection as the forward; only the query row differs); [P3] (the block
-    indices are all a sparse layer caches). q_idx [B, Hkv, Di] holds the new
-    token's index queries, k_idx [B, C, Di] the index-key cache, seqlens [B]
-    the cached lengths n_b (new token included). The query is position
-    i = n_b - 1. Returns int32 [B, Hkv, k]; rows with n_b outside [1, C] are -1.
+    selection as the forward; only the query rows differ); [P3] (the block
+    indices are all a sparse layer caches). k_idx [B, C, Di] is the index-key
+    cache, seqlens [B] the cached lengths n_b (new tokens included). q_idx is
+    [B, Hkv, Di] (one new token, position n_b - 1; returns int32 [B, Hkv, k])
+    or [B, R, Hkv, Di] (R new tokens, the r-th at position n_b - R + r; returns
+    [B, Hkv, R, k]). Rows of sequences with n_b outside [1, C], and rows at a
+    negative position, are -1.
     """
     qi = _arr(q_idx)
     ka = _arr(k_idx)
-    B, Hkv = qi.shape[0], qi.shape[1]
-    out = np.full((B, Hkv, k), -1, dtype=np.int32)
-    pos, ok = _decode_positions(seqlens, ka.shape[1])
-    if len(ok):
-        out[ok] = index_topk_rows(None, ka, pos, Bk, k, q_rows=qi[ok])
-    return out
+    single = qi.ndim == 3
+    if single:
+        qi = qi[:, None]
+    B, R, Hkv = qi.shape[0], qi.shape[1], qi.shape[2]
+    out = np.full((B, Hkv, R, k), -1, dtype=np.int32)
+    pos, br = _decode_positions(seqlens, ka.shape[1], R)
+    if len(pos):
+        rows = index_topk_rows(None, ka, pos, Bk, k, q_rows=qi[br[:, 0], br[:, 1]])   # [M, Hkv, k]
+        out[br[:, 0], :, br[:, 1]] = rows
+    return out[:, :, 0] if single else out
 
 
 def decode_attention(q, k, v, seqlens, block_idx, Bk, scale=None):
-    """Main-branch attention of one new query per sequence over its selected
-    blocks of the cache ([P2] "Cómo funcionan las dos ramas", as for
-    ``attention_rows`` at position i = n_b - 1).
+    """Main-branch attention of the new queries of each sequence over their
+    selected blocks of the cache ([P2] "Cómo funcionan las dos ramas", as for
+    ``attention_rows`` at the queries' positions).
 
-    q [B, Hq, D] the new queries, k/v [B, C, Hkv, D] the caches, seqlens [B],
-    block_idx int [B, Hkv, k]. Returns (O [B, Hq, D], LSE [B, Hq]) in float64;
-    rows with n_b outside [1, C] get O = 0 and LSE = -inf.
+    k/v [B, C, Hkv, D] the caches, seqlens [B]. q [B, Hq, D] with block_idx
+    [B, Hkv, k] (one new token) returns (O [B, Hq, D], LSE [B, Hq]); q
+    [B, R, Hq, D] with block_idx [B, Hkv, R, k] returns (O [B, R, Hq, D], LSE
+    [B, Hq, R]), float64. Rows that do not exist (see ``decode_index_topk``)
+    get O = 0 and LSE = -inf.
     """
     qa = _arr(q)
     kk = _arr(k)
-    B, Hq, D = qa.shape
-    O = np.zeros((B, Hq, D))
-    LSE = np.full((B, Hq), -np.inf)
-    pos, ok = _decode_positions(seqlens, kk.shape[1])
-    if len(ok):
-        bi = np.asarray(block_idx)[ok]
-        O[ok], LSE[ok] = attention_rows(None, kk, v, bi, pos, Bk, scale, q_rows=qa[ok])
-    return O, LSE
+    bi = np.asarray(block_idx)
+    single = qa.ndim == 3
+    if single:
+        qa, bi = qa[:, None], bi[:, :, None]
+    B, R, Hq, D = qa.shape
+    O = np.zeros((B, R, Hq, D))
+    LSE = np.full((B, Hq, R), -np.inf)
+    pos, br = _decode_positions(seqlens, kk.shape[1], R)
+    if len(pos):
+        o, lse = attention_rows(None, kk, v, bi[br[:, 0], :, br[:, 1]], pos, Bk, scale, q_rows=qa[br[:, 0], br[:, 1]])
+        O[br[:, 0], br[:, 1]] = o
+        LSE[br[:, 0], :, br[:, 1]] = lse
+    return (O[:, 0], LSE[:, :, 0]) if single else (O, LSE)
 
 
 def map_positions(fn, positions, row_arrays=(), workers=1, chunk=256):

@@ -182,3 +182,37 @@ def test_decode_planted_mistakes_are_caught():
     last_block[:, :, -1] = (C - 1) // Bk
     o_bad, _ = O.decode_attention(q, kc, v, lens, last_block, Bk)
     assert np.abs(o - o_bad).max() > 1e-3
+
+
+def test_multi_query_decode_is_the_forward_rows():
+    """R new tokens per sequence: row r (position n_b - R + r) is the forward
+    oracle's row there; rows at negative positions do not exist."""
+    rng = np.random.default_rng(12)
+    B, C, Hkv, G, D, Di, Bk, k, R = 3, 70, 2, 4, 8, 6, 8, 4, 3
+    _, k_idx, _, kc, v = _caches(rng, B, C, Hkv, G, D, Di, lo=-3, hi=3)
+    lens = np.array([70, 33, 2])
+    q_full = rng.standard_normal((B, C, Hkv * G, D))
+    qi_full = rng.integers(-3, 4, size=(B, C, Hkv, Di)).astype(np.float64)
+    q_new = np.zeros((B, R, Hkv * G, D))
+    qi_new = np.zeros((B, R, Hkv, Di))
+    for b in range(B):
+        for r in range(R):
+            i = lens[b] - R + r
+            if i >= 0:
+                q_new[b, r], qi_new[b, r] = q_full[b, i], qi_full[b, i]
+    bi_full = O.index_topk(qi_full, k_idx, Bk, k)
+    o_full, lse_full = O.sparse_attention(q_full, kc, v, bi_full, Bk)
+    bi = O.decode_index_topk(qi_new, k_idx, lens, Bk, k)            # [B, Hkv, R, k]
+    o, lse = O.decode_attention(q_new, kc, v, lens, bi, Bk)         # [B, R, Hq, D], [B, Hq, R]
+    for b in range(B):
+        for r in range(R):
+            i = int(lens[b]) - R + r
+            if i < 0:
+                assert (bi[b, :, r] == -1).all() and (o[b, r] == 0).all() and np.isneginf(lse[b, :, r]).all()
+                continue
+            assert np.array_equal(bi[b, :, r], bi_full[b, :, i])
+            np.testing.assert_allclose(o[b, r], o_full[b, i], atol=1e-12)
+            np.testing.assert_allclose(lse[b, :, r], lse_full[b, :, i], atol=1e-12)
+    # the last row alone is the single-query decode
+    bi1 = O.decode_index_topk(qi_new[:, -1], k_idx, lens, Bk, k)
+    assert np.array_equal(bi1, bi[:, :, -1])
