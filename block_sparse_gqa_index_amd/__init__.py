@@ -17,8 +17,9 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   kl_align_bwd(q, k, q_idx, k_idx, block_idx, lse, index_lse) -> (dq_idx, dk_idx), bf16
   forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse): selection, then attention
   sparse_attn_bwd(q, k, v, block_idx, o, lse, dout) -> (dq, dk, dv), bf16
-  decode_index_topk(q_idx, k_idx, seqlens, topk)   -> block_idx int32 [B, Hkv, k] (one new query per sequence)
-  decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq])
+  decode_index_topk(q_idx, k_idx, seqlens, topk)   -> block_idx int32 [B, Hkv, k] (one new query per sequence;
+                                                      q_idx [B, R, Hkv, Di]: R new queries -> [B, Hkv, R, k])
+  decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq]) (or [B,R,Hq,D], [B,Hq,R])
   decode(q_idx, k_idx, q, k, v, seqlens, topk)     -> (block_idx, o, lse): both decode steps
   decode_paged*(..., block_table, ...)             -> the decode calls on page pools [P, 128, ...] + a block table
   dense_attn_fwd(q, k, v)                          -> (o, lse): causal attention over every visible key (warm-up)
@@ -43,6 +44,7 @@ EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_
            "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
            "msa_decode_index_topk", "msa_decode_attn", "msa_decode", "msa_dense_attn_fwd",
            "msa_dense_kl_align_fwd", "msa_decode_paged_index_topk", "msa_decode_paged_attn", "msa_decode_paged",
+           "msa_decode_workspace_bytes",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -84,16 +86,19 @@ def load_library(path: str = LIB_PATH):
                                      ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_forward.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
-    lib.msa_decode_index_topk.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
-    lib.msa_decode_attn.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
-    lib.msa_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    i32 = ctypes.c_int32
+    lib.msa_decode_index_topk.argtypes = [dp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode_attn.argtypes = [dp, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.msa_decode.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode_workspace_bytes.argtypes = [dp, ctypes.c_int, i32]
+    lib.msa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_dense_attn_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_dense_kl_align_fwd.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
                                            sz, vp]
-    i32 = ctypes.c_int32
-    lib.msa_decode_paged_index_topk.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
-    lib.msa_decode_paged_attn.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
-    lib.msa_decode_paged.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode_paged_index_topk.argtypes = [dp, i32, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.msa_decode_paged_attn.argtypes = [dp, i32, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.msa_decode_paged.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, vp, vp, sz,
+                                     vp]
     lib.msa_workspace_bytes.argtypes = [dp, ctypes.c_int]
     lib.msa_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_strerror.argtypes = [ctypes.c_int]
@@ -358,74 +363,84 @@ def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0, block_idx=None, o=No
     return block_idx, o, lse
 
 
-def _decode_shapes(q_idx=None, k_idx=None, q=None, k=None, v=None, seqlens=None):
-    """(B, C, Hkv, G, D, Di) from whichever decode tensors are given, checked
-    against each other."""
-    B = C = Hkv = G = D = Di = None
-    if seqlens is not None:
-        _req(seqlens, "seqlens", dtype=torch.int32, ndim=1)
-        B = seqlens.shape[0]
-    if k_idx is not None:
-        _req(k_idx, "k_idx", ndim=3)
-        B2, C, Di = k_idx.shape
-        if B is not None and B2 != B:
-            raise ValueError("k_idx must be [B, C, Di]")
-        B = B2
-    if q_idx is not None:
-        _req(q_idx, "q_idx", dtype=None if k_idx is None else k_idx.dtype, ndim=3)
-        if tuple(q_idx.shape) != (B, q_idx.shape[1], Di):
-            raise ValueError("q_idx must be [B, Hkv, Di]")
-        Hkv = q_idx.shape[1]
-    if k is not None:
-        _req(k, "k", ndim=4)
-        _req(v, "v", dtype=k.dtype, ndim=4)
-        _req(q, "q", dtype=k.dtype, ndim=3)
-        Bk_, Ck, Hk, D = k.shape
-        if (B is not None and Bk_ != B) or (C is not None and Ck != C) or (Hkv is not None and Hk != Hkv):
-            raise ValueError("k/v must be [B, C, Hkv, D] consistent with the other inputs")
-        B, C, Hkv = Bk_, Ck, Hk
-        if tuple(v.shape) != tuple(k.shape) or q.shape[0] != B or q.shape[2] != D or q.shape[1] % Hkv:
-            raise ValueError("q must be [B, Hq, D] with Hq a multiple of Hkv, v like k")
-        G = q.shape[1] // Hkv
-    return B, C, Hkv, G, D, Di
+def _rows(t, name, inner):
+    """Decode query tensor: [B, inner...] (one new token) or [B, R, inner...];
+    returns R and whether the R axis is present."""
+    _req(t, name)
+    if t.dim() == 1 + inner:
+        return 1, False
+    if t.dim() == 2 + inner:
+        return t.shape[1], True
+    raise ValueError(f"{name} must have {1 + inner} or {2 + inner} dimensions")
+
+
+def _decode_outputs(B, R, multi, Hkv, Hq, D, topk, like, block_idx, o, lse, want_sel=True, want_attn=True):
+    dev = like.device
+    if want_sel and block_idx is None:
+        block_idx = torch.empty((B, Hkv, R, topk) if multi else (B, Hkv, topk), dtype=torch.int32, device=dev)
+    if want_attn:
+        if o is None:
+            o = torch.empty((B, R, Hq, D) if multi else (B, Hq, D), dtype=like.dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((B, Hq, R) if multi else (B, Hq), dtype=torch.float32, device=dev)
+    return block_idx, o, lse
+
+
+def _check_sel(block_idx, B, Hkv, R, multi):
+    _req(block_idx, "block_idx", dtype=torch.int32)
+    want = (B, Hkv, R) if multi else (B, Hkv)
+    if tuple(block_idx.shape[:-1]) != want:
+        raise ValueError(f"block_idx must be {want + ('topk',)}")
+    return block_idx.shape[-1]
+
+
+def decode_workspace_bytes(dims: MsaDims, op: int, num_queries: int = 1) -> int:
+    return int(load_library().msa_decode_workspace_bytes(ctypes.byref(dims), op, num_queries))
 
 
 def decode_index_topk(q_idx, k_idx, seqlens, topk, block_idx=None, workspace=None, block_size=128):
-    """Selection for one new query per sequence: q_idx [B, Hkv, Di], index-key
-    cache k_idx [B, C, Di], seqlens int32 [B] (cached tokens, the new one
-    included) -> block_idx int32 [B, Hkv, topk]."""
+    """Selection for the new queries of each sequence: q_idx [B, Hkv, Di] (one
+    new token) or [B, R, Hkv, Di] (R new tokens, the r-th at position
+    n_b - R + r), index-key cache k_idx [B, C, Di], seqlens int32 [B] (cached
+    tokens, the new ones included) -> block_idx int32 [B, Hkv, topk] or
+    [B, Hkv, R, topk]."""
     lib = load_library()
-    B, C, Hkv, _, _, Di = _decode_shapes(q_idx=q_idx, k_idx=k_idx, seqlens=seqlens)
-    if block_idx is None:
-        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q_idx.device)
-    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
+    R, multi = _rows(q_idx, "q_idx", 2)
+    _req(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)
+    _req(seqlens, "seqlens", dtype=torch.int32, ndim=1)
+    B, C, Di = k_idx.shape
+    Hkv = q_idx.shape[-2]
+    if q_idx.shape[0] != B or q_idx.shape[-1] != Di or seqlens.shape[0] != B:
+        raise ValueError("q_idx must be [B, (R,) Hkv, Di], k_idx [B, C, Di], seqlens [B]")
+    block_idx, _, _ = _decode_outputs(B, R, multi, Hkv, 0, 0, topk, q_idx, block_idx, None, None, want_attn=False)
+    _check_sel(block_idx, B, Hkv, R, multi)
     dims = make_dims(B, C, Hkv, 1, 64, Di, topk, q_idx.dtype, block_size)
-    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_INDEX), q_idx.device, workspace)
-    _check(lib.msa_decode_index_topk(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(seqlens),
+    ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_INDEX, R), q_idx.device, workspace)
+    _check(lib.msa_decode_index_topk(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx), _ptr(seqlens),
                                      _ptr(block_idx), _ptr(ws), nws, _stream(q_idx.device)))
     return block_idx
 
 
 def decode_attn(q, k, v, seqlens, block_idx, softmax_scale=0.0, o=None, lse=None, workspace=None,
                 block_size=128):
-    """Attention of one new query per sequence: q [B, Hq, D], caches k/v
-    [B, C, Hkv, D], seqlens int32 [B], block_idx int32 [B, Hkv, topk] ->
-    (o [B, Hq, D], lse fp32 [B, Hq])."""
+    """Attention of the new queries of each sequence: q [B, Hq, D] or
+    [B, R, Hq, D], caches k/v [B, C, Hkv, D], seqlens int32 [B], block_idx
+    int32 [B, Hkv, (R,) topk] -> (o like q, lse fp32 [B, Hq] or [B, Hq, R])."""
     lib = load_library()
-    B, C, Hkv, G, D, _ = _decode_shapes(q=q, k=k, v=v, seqlens=seqlens)
-    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
-    topk = block_idx.shape[2]
-    if tuple(block_idx.shape[:2]) != (B, Hkv):
-        raise ValueError("block_idx must be [B, Hkv, topk]")
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
-    _req(o, "o", dtype=q.dtype, ndim=3)
-    _req(lse, "lse", dtype=torch.float32, ndim=2)
-    dims = make_dims(B, C, Hkv, G, D, 64, topk, q.dtype, block_size)
-    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_ATTN), q.device, workspace)
-    _check(lib.msa_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(block_idx),
+    R, multi = _rows(q, "q", 2)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(v, "v", dtype=q.dtype, ndim=4)
+    _req(seqlens, "seqlens", dtype=torch.int32, ndim=1)
+    B, C, Hkv, D = k.shape
+    Hq = q.shape[-2]
+    if (tuple(v.shape) != tuple(k.shape) or q.shape[0] != B or q.shape[-1] != D or Hq % Hkv
+            or seqlens.shape[0] != B):
+        raise ValueError("q must be [B, (R,) Hq, D] with Hq a multiple of Hkv; k, v [B, C, Hkv, D]")
+    topk = _check_sel(block_idx, B, Hkv, R, multi)
+    _, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, None, o, lse, want_sel=False)
+    dims = make_dims(B, C, Hkv, Hq // Hkv, D, 64, topk, q.dtype, block_size)
+    ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_ATTN, R), q.device, workspace)
+    _check(lib.msa_decode_attn(ctypes.byref(dims), R, _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(block_idx),
                                float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(q.device)))
     return o, lse
 
@@ -433,23 +448,26 @@ def decode_attn(q, k, v, seqlens, block_idx, softmax_scale=0.0, o=None, lse=None
 def decode(q_idx, k_idx, q, k, v, seqlens, topk, softmax_scale=0.0, block_idx=None, o=None, lse=None,
            workspace=None, block_size=128):
     """One decode step (msa_decode): the selection, then the attention.
-    Returns (block_idx int32 [B, Hkv, topk], o [B, Hq, D], lse fp32 [B, Hq])."""
+    Returns (block_idx, o, lse) in the layouts of decode_index_topk and decode_attn."""
     lib = load_library()
-    B, C, Hkv, G, D, Di = _decode_shapes(q_idx=q_idx, k_idx=k_idx, q=q, k=k, v=v, seqlens=seqlens)
-    if q.dtype != q_idx.dtype:
-        raise ValueError("q and q_idx must share a dtype")
-    if block_idx is None:
-        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
-    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
-    _req(o, "o", dtype=q.dtype, ndim=3)
-    _req(lse, "lse", dtype=torch.float32, ndim=2)
-    dims = make_dims(B, C, Hkv, G, D, Di, topk, q.dtype, block_size)
-    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE), q.device, workspace)
-    _check(lib.msa_decode(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
+    R, multi = _rows(q_idx, "q_idx", 2)
+    R2, multi2 = _rows(q, "q", 2)
+    if (R2, multi2) != (R, multi) or q.dtype != q_idx.dtype:
+        raise ValueError("q and q_idx must have the same new-query axis and dtype")
+    _req(k_idx, "k_idx", dtype=q.dtype, ndim=3)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(v, "v", dtype=q.dtype, ndim=4)
+    _req(seqlens, "seqlens", dtype=torch.int32, ndim=1)
+    B, C, Hkv, D = k.shape
+    Di, Hq = k_idx.shape[2], q.shape[-2]
+    if (tuple(k_idx.shape[:2]) != (B, C) or tuple(v.shape) != tuple(k.shape) or q_idx.shape[-2:] != (Hkv, Di)
+            or q.shape[-1] != D or Hq % Hkv or seqlens.shape[0] != B):
+        raise ValueError("inconsistent shapes")
+    block_idx, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, block_idx, o, lse)
+    _check_sel(block_idx, B, Hkv, R, multi)
+    dims = make_dims(B, C, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
+    ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE, R), q.device, workspace)
+    _check(lib.msa_decode(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
                           float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws,
                           _stream(q.device)))
     return block_idx, o, lse
@@ -531,43 +549,38 @@ def _paged_shapes(block_table, seqlens, k_idx_pages=None, k_pages=None, v_pages=
 
 def decode_paged_index_topk(q_idx, k_idx_pages, block_table, seqlens, topk, block_idx=None, workspace=None):
     """decode_index_topk on a paged index-key cache: k_idx_pages [P, 128, Di],
-    block_table int32 [B, max_blocks] (page of each block) -> int32 [B, Hkv, topk]."""
+    block_table int32 [B, max_blocks] (page of each block)."""
     lib = load_library()
     B, C, P = _paged_shapes(block_table, seqlens, k_idx_pages=k_idx_pages)
-    _req(q_idx, "q_idx", dtype=k_idx_pages.dtype, ndim=3)
-    Hkv, Di = q_idx.shape[1], q_idx.shape[2]
-    if q_idx.shape[0] != B or k_idx_pages.shape[2] != Di:
-        raise ValueError("q_idx must be [B, Hkv, Di]")
-    if block_idx is None:
-        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q_idx.device)
-    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
+    R, multi = _rows(q_idx, "q_idx", 2)
+    Hkv, Di = q_idx.shape[-2], q_idx.shape[-1]
+    if q_idx.dtype != k_idx_pages.dtype or q_idx.shape[0] != B or k_idx_pages.shape[2] != Di:
+        raise ValueError("q_idx must be [B, (R,) Hkv, Di] in the pool's dtype")
+    block_idx, _, _ = _decode_outputs(B, R, multi, Hkv, 0, 0, topk, q_idx, block_idx, None, None, want_attn=False)
+    _check_sel(block_idx, B, Hkv, R, multi)
     dims = make_dims(B, C, Hkv, 1, 64, Di, topk, q_idx.dtype)
-    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_INDEX), q_idx.device, workspace)
-    _check(lib.msa_decode_paged_index_topk(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx_pages), _ptr(block_table), P,
-                                           _ptr(seqlens), _ptr(block_idx), _ptr(ws), nws, _stream(q_idx.device)))
+    ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_INDEX, R), q_idx.device, workspace)
+    _check(lib.msa_decode_paged_index_topk(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx_pages), _ptr(block_table),
+                                           P, _ptr(seqlens), _ptr(block_idx), _ptr(ws), nws, _stream(q_idx.device)))
     return block_idx
 
 
 def decode_paged_attn(q, k_pages, v_pages, block_table, seqlens, block_idx, softmax_scale=0.0, o=None, lse=None,
                       workspace=None):
-    """decode_attn on paged K/V caches [P, 128, Hkv, D] -> (o [B,Hq,D], lse fp32 [B,Hq])."""
+    """decode_attn on paged K/V caches [P, 128, Hkv, D]."""
     lib = load_library()
     B, C, P = _paged_shapes(block_table, seqlens, k_pages=k_pages, v_pages=v_pages)
-    _req(q, "q", dtype=k_pages.dtype, ndim=3)
+    R, multi = _rows(q, "q", 2)
     Hkv, D = k_pages.shape[2], k_pages.shape[3]
-    if q.shape[0] != B or q.shape[2] != D or q.shape[1] % Hkv:
-        raise ValueError("q must be [B, Hq, D] with Hq a multiple of Hkv")
-    _req(block_idx, "block_idx", dtype=torch.int32, ndim=3)
-    topk = block_idx.shape[2]
-    G = q.shape[1] // Hkv
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
-    dims = make_dims(B, C, Hkv, G, D, 64, topk, q.dtype)
-    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE_ATTN), q.device, workspace)
-    _check(lib.msa_decode_paged_attn(ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), P,
-                                     _ptr(seqlens), _ptr(block_idx), float(softmax_scale), _ptr(o), _ptr(lse),
+    Hq = q.shape[-2]
+    if q.dtype != k_pages.dtype or q.shape[0] != B or q.shape[-1] != D or Hq % Hkv:
+        raise ValueError("q must be [B, (R,) Hq, D] with Hq a multiple of Hkv")
+    topk = _check_sel(block_idx, B, Hkv, R, multi)
+    _, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, None, o, lse, want_sel=False)
+    dims = make_dims(B, C, Hkv, Hq // Hkv, D, 64, topk, q.dtype)
+    ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_ATTN, R), q.device, workspace)
+    _check(lib.msa_decode_paged_attn(ctypes.byref(dims), R, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                     P, _ptr(seqlens), _ptr(block_idx), float(softmax_scale), _ptr(o), _ptr(lse),
                                      _ptr(ws), nws, _stream(q.device)))
     return o, lse
 
@@ -577,21 +590,19 @@ def decode_paged(q_idx, k_idx_pages, q, k_pages, v_pages, block_table, seqlens, 
     """One decode step on paged caches (msa_decode_paged) -> (block_idx, o, lse)."""
     lib = load_library()
     B, C, P = _paged_shapes(block_table, seqlens, k_idx_pages=k_idx_pages, k_pages=k_pages, v_pages=v_pages)
-    _req(q_idx, "q_idx", dtype=q.dtype, ndim=3)
-    _req(q, "q", dtype=k_pages.dtype, ndim=3)
-    Hkv, Di, D = q_idx.shape[1], q_idx.shape[2], k_pages.shape[3]
-    if k_pages.shape[2] != Hkv or q.shape[1] % Hkv or q.shape[2] != D:
+    R, multi = _rows(q_idx, "q_idx", 2)
+    R2, multi2 = _rows(q, "q", 2)
+    if (R2, multi2) != (R, multi) or q.dtype != q_idx.dtype or q.dtype != k_pages.dtype:
+        raise ValueError("q and q_idx must have the same new-query axis and dtype")
+    Hkv, Di, D = q_idx.shape[-2], q_idx.shape[-1], k_pages.shape[3]
+    Hq = q.shape[-2]
+    if k_pages.shape[2] != Hkv or Hq % Hkv or q.shape[-1] != D:
         raise ValueError("inconsistent shapes")
-    G = q.shape[1] // Hkv
-    if block_idx is None:
-        block_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=q.device)
-    dims = make_dims(B, C, Hkv, G, D, Di, topk, q.dtype)
-    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DECODE), q.device, workspace)
-    _check(lib.msa_decode_paged(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx_pages), _ptr(q), _ptr(k_pages),
+    block_idx, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, block_idx, o, lse)
+    _check_sel(block_idx, B, Hkv, R, multi)
+    dims = make_dims(B, C, Hkv, Hq // Hkv, D, Di, topk, q.dtype)
+    ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE, R), q.device, workspace)
+    _check(lib.msa_decode_paged(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx_pages), _ptr(q), _ptr(k_pages),
                                 _ptr(v_pages), _ptr(block_table), P, _ptr(seqlens), float(softmax_scale),
                                 _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(q.device)))
     return block_idx, o, lse

@@ -1,8 +1,8 @@
-// Decoding: one new query per sequence against a cache of keys.
+// Decoding: R new queries per sequence against a cache of keys.
 //
-// Sequence b holds n_b cached tokens (positions 0 .. n_b - 1, the new token
-// last); its new query is position i = n_b - 1, so selection and attention are
-// those of the forward's row i (MiniMax Sparse Attention article on
+// Sequence b holds n_b cached tokens (positions 0 .. n_b - 1, the new ones
+// last); its r-th new query is position i = n_b - R + r, so selection and
+// attention are those of the forward's row i (MiniMax Sparse Attention article on
 // 7minutos.es, "Cómo funcionan las dos ramas": index scores of the visible
 // keys, block max-pool, top-k per query and group with the local block forced
 // in, then exact softmax attention over the kept blocks' causally visible
@@ -28,8 +28,9 @@
 //   decode_attn_kernel    one work-group per (sequence, group, kept block):
 //                         S^T = K Q^T per wave (32 keys each, K from global),
 //                         block softmax across the four waves through LDS,
-//                         O^T = V^T P^T with V staged in LDS; a normalised
-//                         fp32 partial output and its LSE per head
+//                         O^T = V^T P^T with V staged in LDS (P as a bf16
+//                         hi + lo pair: two products, exact to ~2^-17 of P);
+//                         a normalised fp32 partial output and its LSE per head
 //   decode_combine_kernel one work-group per (sequence, group): the kept
 //                         blocks' partials merged in slot order -> O, LSE.
 // Every sum runs in a fixed order: results are bitwise reproducible.
@@ -87,22 +88,25 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
                                                             const int32_t* __restrict__ seqlens,
                                                             const int32_t* __restrict__ pages, int num_pages,
                                                             float* __restrict__ scores, int C, int Hkv,
-                                                            int nbs, int gchunks) {
+                                                            int R, int nbs, int gchunks) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 31, half = lane >> 5;
     const int b = blockIdx.y / gchunks, gc = blockIdx.y % gchunks;
     const int j = blockIdx.x * 4 + wave;
     const int n = seqlens[b];
     if (!length_ok(n, C)) return;
-    const int L = (n - 1) / kBlock;   // competing blocks: 0 .. L-1
+    const int L = (n - 1) / kBlock;   // competing blocks of the last new query: 0 .. L-1
     if (j >= L) return;
-    const int g = gc * kGroupCols + col;
+    // Columns are the (new query r, group g) pairs of the sequence, c = r * Hkv + g;
+    // an earlier query reads only the blocks it sees.
+    const int RH = R * Hkv;
+    const int c = gc * kGroupCols + col;
     // Block j of the sequence: contiguous in the cache, or the page the block table names.
     const T* kb = k_idx + ((size_t)b * C + (size_t)j * kBlock) * DI;
     if (pages) {
         const int pg = pages[(size_t)b * nbs + j];
         if (pg < 0 || pg >= num_pages) {   // not a page of the pool: the block scores -inf, nothing is read
-            if (half == 0 && g < Hkv) scores[((size_t)b * Hkv + g) * nbs + j] = -__builtin_inff();
+            if (half == 0 && c < RH) scores[((size_t)b * RH + c) * nbs + j] = -__builtin_inff();
             return;
         }
         kb = k_idx + (size_t)pg * kBlock * DI;
@@ -112,10 +116,10 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
     constexpr int NS = DI / MM::KD;   // contraction slices
     constexpr int KH = MM::KD / 2;    // elements per lane and slice
     typename MM::Op bq[NS];
-    const T* qrow = q_idx + ((size_t)b * Hkv + (g < Hkv ? g : 0)) * DI;
+    const T* qrow = q_idx + ((size_t)b * RH + (c < RH ? c : 0)) * DI;   // q_idx [B, R, Hkv, Di]
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
-        if (g < Hkv) bq[sl].load(qrow + MM::KD * sl + KH * half);
+        if (c < RH) bq[sl].load(qrow + MM::KD * sl + KH * half);
         else bq[sl].zero();
     }
 
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
         }
     }
     m = vmax(m, swap_halves(m));
-    if (half == 0 && g < Hkv) scores[((size_t)b * Hkv + g) * nbs + j] = m;
+    if (half == 0 && c < RH) scores[((size_t)b * RH + c) * nbs + j] = m;
 }
 
 // ------------------------------------------------------------------- top-k --
@@ -185,20 +189,22 @@ template <int K1MAX>
 __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ seqlens,
                                                           int32_t* __restrict__ block_idx, int B, int C, int Hkv,
-                                                          int nbs, int k) {
+                                                          int R, int nbs, int k) {
     const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);   // (sequence, group) row of this wave
-    if (r >= B * Hkv) return;
-    const int b = r / Hkv;
+    const int rr = blockIdx.x * 4 + (threadIdx.x >> 6);   // (sequence, new query, group) row of this wave
+    const int RH = R * Hkv;
+    if (rr >= B * RH) return;
+    const int b = rr / RH, qr = (rr % RH) / Hkv, g = rr % Hkv;
     const int n = seqlens[b];
-    int32_t* out = block_idx + (size_t)r * k;
-    if (!length_ok(n, C)) {
+    const int i = n - R + qr;   // the query's position
+    int32_t* out = block_idx + (((size_t)b * Hkv + g) * R + qr) * k;   // [B, Hkv, R, k]
+    if (!length_ok(n, C) || i < 0) {
         if (lane < k) out[lane] = -1;
         return;
     }
-    const int L = (n - 1) / kBlock;
+    const int L = i / kBlock;
     const int k1 = min(k - 1, L);
-    const float* row = scores + (size_t)r * nbs;
+    const float* row = scores + (size_t)rr * nbs;
 
     // Lane-local best K1MAX keys, descending (0 = empty).
     uint64_t best[K1MAX];
@@ -253,7 +259,10 @@ struct DecodeLds {
     static constexpr int ES = sizeof(T);
     static constexpr int VROW = D * ES + 16;            // padded V row: the two half-waves hit other banks
     static constexpr int V_BYTES = kBlock * VROW;
-    static constexpr int P_BYTES = 4 * 2 * kWave * 8 * ES;   // [wave][slice][lane] P operands
+    // [wave][slice][lane] P operands; bf16 keeps P = hi + lo as two operands
+    // (hi = bf16(p), lo = bf16(p - hi)), so P V is exact to ~2^-17 of p.
+    static constexpr int P_HALF = 4 * 2 * kWave * 8 * ES;
+    static constexpr int P_BYTES = (ES == 2 ? 2 : 1) * P_HALF;
     static constexpr int RED_BYTES = 2 * 4 * kGroupCols * 4;
     static constexpr int BYTES = V_BYTES + P_BYTES + RED_BYTES;
 };
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
                                                           const int32_t* __restrict__ block_idx,
                                                           const int32_t* __restrict__ pages, int num_pages,
                                                           float* __restrict__ po, float* __restrict__ plse, int C,
-                                                          int Hkv, int G, int k, float scale_log2) {
+                                                          int Hkv, int G, int R, int k, float scale_log2) {
     using LD = DecodeLds<T, D>;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LD::BYTES];
     unsigned char* vs = lds;
@@ -278,11 +287,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 31, half = lane >> 5;
-    const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const size_t item = ((size_t)b * Hkv + g) * k + slot;
+    const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z / R, qr = blockIdx.z % R;
+    const size_t item = ((size_t)blockIdx.z * Hkv + g) * k + slot;   // (sequence, new query, group, slot)
     const int n = seqlens[b];
-    const int i = n - 1;
-    const int j = block_idx[item];
+    const int i = n - R + qr;   // the query's position
+    const int j = i >= 0 ? block_idx[(((size_t)b * Hkv + g) * R + qr) * k + slot] : -1;
     // Empty slot (padding, a block past the query, or an invalid length): no
     // tokens, LSE -inf, and the merge skips the slot.
     const int nbs = (C + kBlock - 1) / kBlock;
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     // once the scores are on the matrix cores.
     Op8<T> bq[D / 16];
     const int Hq = Hkv * G;
-    load_q_op<T, D>(bq, q + ((size_t)b * Hq + (size_t)g * G + (col < G ? col : 0)) * D, col < G, half);
+    load_q_op<T, D>(bq, q + ((size_t)blockIdx.z * Hq + (size_t)g * G + (col < G ? col : 0)) * D, col < G, half);
     const int key = t0 + wave * 32 + col;
     Op8<T> a[D / 16];
 #pragma unroll
@@ -361,6 +370,18 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
         Op8<T> bp;
         PType<T>::pack(bp, pe);
         *reinterpret_cast<Op8<T>*>(pl + ((wave * 2 + s2) * kWave + lane) * 8 * LD::ES) = bp;
+        if constexpr (LD::ES == 2) {
+            const u32x4 hw = __builtin_bit_cast(u32x4, bp.v);
+            float lo[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[2 * e] = pe[2 * e] - __uint_as_float(hw[e] << 16);
+                lo[2 * e + 1] = pe[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u);
+            }
+            Op8<T> bl;
+            PType<T>::pack(bl, lo);
+            *reinterpret_cast<Op8<T>*>(pl + LD::P_HALF + ((wave * 2 + s2) * kWave + lane) * 8 * LD::ES) = bl;
+        }
     }
     __syncthreads();
     const float lsum = red_l[col] + red_l[kGroupCols + col] + red_l[2 * kGroupCols + col] + red_l[3 * kGroupCols + col];
@@ -396,6 +417,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
                     }
                 }
                 mma16(o, a, bp);
+                if constexpr (LD::ES == 2) {
+                    const Op8<T> bl =
+                        *reinterpret_cast<const Op8<T>*>(pl + LD::P_HALF + ((w2 * 2 + s2) * kWave + lane) * 8 * LD::ES);
+                    mma16(o, a, bl);
+                }
             }
         }
         // Lane holds head `col`, dims wave*32 + 8*(r/4) + 4*half + r%4.
@@ -426,11 +452,11 @@ template <typename T>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ po,
                                                              const float* __restrict__ plse, T* __restrict__ o,
                                                              float* __restrict__ lse, int Hkv, int G, int D,
-                                                             int k) {
+                                                             int R, int k) {
     __shared__ float sl[32 * 32];    // slot LSEs [slot][head], then merge weights
     __shared__ float tot[32];        // merged LSE per head
-    const int g = blockIdx.x, b = blockIdx.y;
-    const size_t item0 = ((size_t)b * Hkv + g) * k;
+    const int g = blockIdx.x, z = blockIdx.y;   // z = (sequence, new query)
+    const size_t item0 = ((size_t)z * Hkv + g) * k;
     const int Hq = Hkv * G;
     // The row's k * G slot LSEs are contiguous: one load per thread.
     for (int t = threadIdx.x; t < k * G; t += blockDim.x) sl[t] = plse[item0 * G + t];
@@ -449,7 +475,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
             total = mx + __logf(sum);
         }
         tot[h] = total;
-        lse[(size_t)b * Hq + (size_t)g * G + h] = total;
+        lse[((size_t)(z / R) * Hq + (size_t)g * G + h) * R + z % R] = total;   // [B, Hq, R]
     }
     __syncthreads();
     for (int t = threadIdx.x; t < k * G; t += blockDim.x) {
@@ -480,7 +506,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
                 acc.w = fmaf(wv[u], x[u].w, acc.w);
             }
         }
-        T* dst = o + ((size_t)b * Hq + (size_t)g * G + h) * D + d;
+        T* dst = o + ((size_t)z * Hq + (size_t)g * G + h) * D + d;   // [B, R, Hq, D]
         store_out<T>(dst, acc.x);
         store_out<T>(dst + 1, acc.y);
         store_out<T>(dst + 2, acc.z);
@@ -489,22 +515,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 }
 
 template <int K1MAX>
-void launch_topk(const float* scores, const int32_t* seqlens, int32_t* block_idx, int B, int C, int Hkv, int nbs,
-                 int k, hipStream_t st) {
-    const int rows = B * Hkv;
+void launch_topk(const float* scores, const int32_t* seqlens, int32_t* block_idx, int B, int C, int Hkv, int R,
+                 int nbs, int k, hipStream_t st) {
+    const int rows = B * R * Hkv;
     hipLaunchKernelGGL(decode_topk_kernel<K1MAX>, dim3((rows + 3) / 4), dim3(256), 0, st, scores, seqlens,
-                       block_idx, B, C, Hkv, nbs, k);
+                       block_idx, B, C, Hkv, R, nbs, k);
 }
 
 template <typename T, int DI>
 void launch_scores(const DecodeDims& d, const void* q_idx, const void* k_idx, const int32_t* seqlens,
                    const int32_t* pages, int num_pages, float* scores, hipStream_t st) {
-    const int gchunks = (d.Hkv + kGroupCols - 1) / kGroupCols;
+    const int gchunks = (d.R * d.Hkv + kGroupCols - 1) / kGroupCols;
     const int lmax = (d.C - 1) / kBlock;   // competing blocks of a full cache
     if (lmax == 0) return;
     hipLaunchKernelGGL((decode_scores_kernel<T, DI>), dim3((lmax + 3) / 4, d.B * gchunks), dim3(256), 0, st,
                        static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, pages, num_pages, scores,
-                       d.C, d.Hkv, d.nbs(), gchunks);
+                       d.C, d.Hkv, d.R, d.nbs(), gchunks);
 }
 
 template <typename T, int D>
@@ -513,11 +539,11 @@ void launch_attn(const DecodeDims& d, const void* q, const void* k, const void* 
                  const DecodeWorkspace& W, unsigned char* ws, hipStream_t st) {
     float* po = reinterpret_cast<float*>(ws + W.po);
     float* pl = reinterpret_cast<float*>(ws + W.plse);
-    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.k, d.Hkv, d.B), dim3(256), 0, st,
+    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.k, d.Hkv, d.B * d.R), dim3(256), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), seqlens,
-                       block_idx, pages, num_pages, po, pl, d.C, d.Hkv, d.G, d.k, scale * 1.4426950408889634f);
-    hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(d.Hkv, d.B), dim3(256), 0, st, po, pl,
-                       static_cast<T*>(o), lse, d.Hkv, d.G, D, d.k);
+                       block_idx, pages, num_pages, po, pl, d.C, d.Hkv, d.G, d.R, d.k, scale * 1.4426950408889634f);
+    hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(d.Hkv, d.B * d.R), dim3(256), 0, st, po, pl,
+                       static_cast<T*>(o), lse, d.Hkv, d.G, D, d.R, d.k);
 }
 
 }  // namespace
@@ -526,10 +552,10 @@ DecodeWorkspace decode_workspace_layout(const DecodeDims& d) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     DecodeWorkspace W;
     W.scores = 0;
-    W.index_bytes = up((size_t)d.B * d.Hkv * d.nbs() * sizeof(float));
+    W.index_bytes = up((size_t)d.B * d.R * d.Hkv * d.nbs() * sizeof(float));
     W.po = 0;
-    W.plse = up((size_t)d.B * d.Hkv * d.k * d.G * d.D * sizeof(float));
-    W.attn_bytes = W.plse + up((size_t)d.B * d.Hkv * d.k * d.G * sizeof(float));
+    W.plse = up((size_t)d.B * d.R * d.Hkv * d.k * d.G * d.D * sizeof(float));
+    W.attn_bytes = W.plse + up((size_t)d.B * d.R * d.Hkv * d.k * d.G * sizeof(float));
     return W;
 }
 
@@ -547,10 +573,10 @@ hipError_t launch_decode_index(const DecodeDims& d, const void* q_idx, const voi
         else launch_scores<float, 64>(d, q_idx, k_idx, seqlens, pages, num_pages, scores, st);
     }
     const int k1 = d.k - 1;
-    if (k1 <= 3) launch_topk<3>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
-    else if (k1 <= 7) launch_topk<7>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
-    else if (k1 <= 15) launch_topk<15>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
-    else launch_topk<31>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.nbs(), d.k, st);
+    if (k1 <= 3) launch_topk<3>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.R, d.nbs(), d.k, st);
+    else if (k1 <= 7) launch_topk<7>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.R, d.nbs(), d.k, st);
+    else if (k1 <= 15) launch_topk<15>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.R, d.nbs(), d.k, st);
+    else launch_topk<31>(scores, seqlens, block_idx, d.B, d.C, d.Hkv, d.R, d.nbs(), d.k, st);
     return hipGetLastError();
 }
 

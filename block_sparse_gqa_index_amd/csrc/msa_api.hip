@@ -67,16 +67,27 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
 
 bool empty(const LaunchDims& L) { return L.B == 0 || L.N == 0; }
 
-msa::DecodeDims decode_dims(const LaunchDims& L) {
-    return msa::DecodeDims{L.B, L.N, L.Hkv, L.G, L.D, L.Di, L.k, L.dtype};
+msa::DecodeDims decode_dims(const LaunchDims& L, int R = 1) {
+    return msa::DecodeDims{L.B, L.N, L.Hkv, L.G, L.D, L.Di, L.k, L.dtype, R};
+}
+
+size_t decode_ws(const LaunchDims& L, int op, int R) {
+    const msa::DecodeWorkspace W = msa::decode_workspace_layout(decode_dims(L, R));
+    if (op == MSA_OP_DECODE_INDEX) return W.index_bytes;
+    if (op == MSA_OP_DECODE_ATTN) return W.attn_bytes;
+    return W.index_bytes > W.attn_bytes ? W.index_bytes : W.attn_bytes;
 }
 
 // Decode calls share their argument checks: sizes, the per-op pointers, and
 // the workspace of `op`.
-int check_decode(const msa_dims* dims, int op, LaunchDims* L, std::initializer_list<const void*> ptrs,
+int check_decode(const msa_dims* dims, int R, int op, LaunchDims* L, std::initializer_list<const void*> ptrs,
                  const void* ws, size_t ws_bytes) {
     int st = check_dims(dims, op, L);
     if (st != MSA_OK) return st;
+    // R new queries per sequence; the grids put sequences x queries (x group chunks of 32) on one axis.
+    if (R < 1 || R > 65535 || (int64_t)L->B * R > 65535 ||
+        (int64_t)L->B * (((int64_t)R * L->Hkv + 31) / 32) > 65535)
+        return MSA_ERR_SHAPE;
     if (dims->dtype != MSA_BF16 && dims->dtype != MSA_F32 &&
         !(op == MSA_OP_DECODE_INDEX && dims->dtype == MSA_FP8_E4M3))
         return MSA_ERR_UNSUPPORTED;
@@ -85,7 +96,7 @@ int check_decode(const msa_dims* dims, int op, LaunchDims* L, std::initializer_l
         if (!p) return MSA_ERR_NULL;
     for (const void* p : ptrs)
         if (!aligned16(p)) return MSA_ERR_ALIGN;
-    const size_t need = msa_workspace_bytes(dims, op);
+    const size_t need = decode_ws(*L, op, R);
     if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
     return MSA_OK;
 }
@@ -124,14 +135,11 @@ size_t msa_workspace_bytes(const msa_dims* dims, int op) {
         case MSA_OP_ATTN_BWD: return msa::bwd_workspace_layout(L).bytes;
         case MSA_OP_KL: return msa::kl_workspace_layout(L).bytes;
         case MSA_OP_KL_BWD: return msa::kl_bwd_workspace_layout(L).bytes;
-        case MSA_OP_DECODE_INDEX: return msa::decode_workspace_layout(decode_dims(L)).index_bytes;
-        case MSA_OP_DECODE_ATTN: return msa::decode_workspace_layout(decode_dims(L)).attn_bytes;
+        case MSA_OP_DECODE_INDEX:
+        case MSA_OP_DECODE_ATTN: return decode_ws(L, op, 1);
         case MSA_OP_DENSE_ATTN: return msa::dense_workspace_bytes(L);
         case MSA_OP_DENSE_KL: return msa::dense_kl_workspace_bytes(L);
-        case MSA_OP_DECODE: {
-            const msa::DecodeWorkspace W = msa::decode_workspace_layout(decode_dims(L));
-            return W.index_bytes > W.attn_bytes ? W.index_bytes : W.attn_bytes;
-        }
+        case MSA_OP_DECODE: return decode_ws(L, op, 1);
         default: return 0;
     }
 }
@@ -282,6 +290,13 @@ int msa_dense_attn_fwd(const msa_dims* dims, const void* q, const void* k, const
     return hip_status(msa::launch_dense_attn(L, q, k, v, scale, o, lse, ws, static_cast<hipStream_t>(stream)));
 }
 
+size_t msa_decode_workspace_bytes(const msa_dims* dims, int op, int32_t num_queries) {
+    LaunchDims L;
+    if (op != MSA_OP_DECODE_INDEX && op != MSA_OP_DECODE_ATTN && op != MSA_OP_DECODE) return 0;
+    if (num_queries < 1 || check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
+    return decode_ws(L, op, num_queries);
+}
+
 int msa_dense_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx, const void* k_idx,
                            const float* lse, float softmax_scale, float index_scale, float* kl_rows, float* kl_sum,
                            float* index_lse, void* ws, size_t ws_bytes, void* stream) {
@@ -302,80 +317,80 @@ int msa_dense_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, c
                                                  index_lse, ws, static_cast<hipStream_t>(stream)));
 }
 
-int msa_decode_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, const int32_t* seqlens,
+int msa_decode_index_topk(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx, const int32_t* seqlens,
                           int32_t* block_idx, void* ws, size_t ws_bytes, void* stream) {
     LaunchDims L;
-    int st = check_decode(dims, MSA_OP_DECODE_INDEX, &L, {q_idx, k_idx, seqlens, block_idx}, ws, ws_bytes);
+    int st = check_decode(dims, num_queries, MSA_OP_DECODE_INDEX, &L, {q_idx, k_idx, seqlens, block_idx}, ws, ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
-    return hip_status(msa::launch_decode_index(decode_dims(L), q_idx, k_idx, seqlens, nullptr, 0, block_idx, ws,
+    return hip_status(msa::launch_decode_index(decode_dims(L, num_queries), q_idx, k_idx, seqlens, nullptr, 0, block_idx, ws,
                                                static_cast<hipStream_t>(stream)));
 }
 
-int msa_decode_attn(const msa_dims* dims, const void* q, const void* k, const void* v, const int32_t* seqlens,
+int msa_decode_attn(const msa_dims* dims, int32_t num_queries, const void* q, const void* k, const void* v, const int32_t* seqlens,
                     const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws, size_t ws_bytes,
                     void* stream) {
     LaunchDims L;
-    int st = check_decode(dims, MSA_OP_DECODE_ATTN, &L, {q, k, v, seqlens, block_idx, o, lse}, ws, ws_bytes);
+    int st = check_decode(dims, num_queries, MSA_OP_DECODE_ATTN, &L, {q, k, v, seqlens, block_idx, o, lse}, ws, ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
-    return hip_status(msa::launch_decode_attn(decode_dims(L), q, k, v, seqlens, block_idx, nullptr, 0, scale, o, lse, ws,
+    return hip_status(msa::launch_decode_attn(decode_dims(L, num_queries), q, k, v, seqlens, block_idx, nullptr, 0, scale, o, lse, ws,
                                               static_cast<hipStream_t>(stream)));
 }
 
-int msa_decode(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q, const void* k,
+int msa_decode(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx, const void* q, const void* k,
                const void* v, const int32_t* seqlens, float softmax_scale, int32_t* block_idx, void* o, float* lse,
                void* ws, size_t ws_bytes, void* stream) {
     LaunchDims L;
-    int st = check_decode(dims, MSA_OP_DECODE, &L, {q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse}, ws,
+    int st = check_decode(dims, num_queries, MSA_OP_DECODE, &L, {q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse}, ws,
                           ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const msa::DecodeDims d = decode_dims(L);
+    const msa::DecodeDims d = decode_dims(L, num_queries);
     if (msa::launch_decode_index(d, q_idx, k_idx, seqlens, nullptr, 0, block_idx, ws, s) != hipSuccess)
         return MSA_ERR_HIP;
     return hip_status(msa::launch_decode_attn(d, q, k, v, seqlens, block_idx, nullptr, 0, scale, o, lse, ws, s));
 }
 
-int msa_decode_paged_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx_pages,
+int msa_decode_paged_index_topk(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx_pages,
                                 const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
                                 int32_t* block_idx, void* ws, size_t ws_bytes, void* stream) {
     LaunchDims L;
     if (num_pages < 0) return MSA_ERR_SHAPE;
-    int st = check_decode(dims, MSA_OP_DECODE_INDEX, &L, {q_idx, k_idx_pages, block_table, seqlens, block_idx}, ws,
+    int st = check_decode(dims, num_queries, MSA_OP_DECODE_INDEX, &L, {q_idx, k_idx_pages, block_table, seqlens, block_idx}, ws,
                           ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
-    return hip_status(msa::launch_decode_index(decode_dims(L), q_idx, k_idx_pages, seqlens, block_table, num_pages,
+    return hip_status(msa::launch_decode_index(decode_dims(L, num_queries), q_idx, k_idx_pages, seqlens, block_table, num_pages,
                                                block_idx, ws, static_cast<hipStream_t>(stream)));
 }
 
-int msa_decode_paged_attn(const msa_dims* dims, const void* q, const void* k_pages, const void* v_pages,
+int msa_decode_paged_attn(const msa_dims* dims, int32_t num_queries, const void* q, const void* k_pages, const void* v_pages,
                           const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
                           const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
                           size_t ws_bytes, void* stream) {
     LaunchDims L;
     if (num_pages < 0) return MSA_ERR_SHAPE;
-    int st = check_decode(dims, MSA_OP_DECODE_ATTN, &L, {q, k_pages, v_pages, block_table, seqlens, block_idx, o, lse},
+    int st = check_decode(dims, num_queries, MSA_OP_DECODE_ATTN, &L, {q, k_pages, v_pages, block_table, seqlens, block_idx, o, lse},
                           ws, ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
-    return hip_status(msa::launch_decode_attn(decode_dims(L), q, k_pages, v_pages, seqlens, block_idx, block_table,
+    return hip_status(msa::launch_decode_attn(decode_dims(L, num_queries), q, k_pages, v_pages, seqlens, block_idx, block_table,
                                               num_pages, scale, o, lse, ws, static_cast<hipStream_t>(stream)));
 }
 
-int msa_decode_paged(const msa_dims* dims, const void* q_idx, const void* k_idx_pages, const void* q,
+int msa_decode_paged(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx_pages, const void* q,
                      const void* k_pages, const void* v_pages, const int32_t* block_table, int32_t num_pages,
                      const int32_t* seqlens, float softmax_scale, int32_t* block_idx, void* o, float* lse, void* ws,
                      size_t ws_bytes, void* stream) {
     LaunchDims L;
     if (num_pages < 0) return MSA_ERR_SHAPE;
-    int st = check_decode(dims, MSA_OP_DECODE, &L,
+    int st = check_decode(dims, num_queries, MSA_OP_DECODE, &L,
                           {q_idx, k_idx_pages, q, k_pages, v_pages, block_table, seqlens, block_idx, o, lse}, ws,
                           ws_bytes);
     if (st != MSA_OK || empty(L)) return st;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const msa::DecodeDims d = decode_dims(L);
+    const msa::DecodeDims d = decode_dims(L, num_queries);
     if (msa::launch_decode_index(d, q_idx, k_idx_pages, seqlens, block_table, num_pages, block_idx, ws, s) !=
         hipSuccess)
         return MSA_ERR_HIP;

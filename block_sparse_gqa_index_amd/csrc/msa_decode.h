@@ -12,14 +12,15 @@ namespace msa {
 // (the selection only).
 struct DecodeDims {
     int B, C, Hkv, G, D, Di, k, dtype;
+    int R;   // new queries per sequence (positions n_b - R .. n_b - 1)
     int nbs() const { return (C + 127) / 128; }   // blocks of a full cache
 };
 
 // Byte offsets from the workspace base. The selection's block scores and the
 // attention's partials are never live at the same time, so both start at 0.
 struct DecodeWorkspace {
-    size_t scores, index_bytes;   // block scores [B, Hkv, nbs] fp32
-    size_t po, plse, attn_bytes;  // partial outputs [B, Hkv, k, G, D] fp32 and LSEs [B, Hkv, k, G] fp32
+    size_t scores, index_bytes;   // block scores [B, R * Hkv, nbs] fp32
+    size_t po, plse, attn_bytes;  // partial outputs [B, R, Hkv, k, G, D] fp32 and LSEs [B, R, Hkv, k, G] fp32
 };
 
 DecodeWorkspace decode_workspace_layout(const DecodeDims& d);

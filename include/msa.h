@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 4
+#define MSA_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define MSA_API __attribute__((visibility("default")))
@@ -310,70 +310,61 @@ MSA_API int msa_dense_kl_align_fwd(const msa_dims* dims, const void* q, const vo
                                    void* stream);
 
 /*
- * Decoding: one new query per sequence against a cache.
+ * Decoding: R >= 1 new queries per sequence against a cache (one decode step,
+ * or several tokens appended at once, e.g. speculative drafts).
  * Defined by the same passages as msa_index_topk and msa_sparse_attn_fwd (MSA
  * article on 7minutos.es, "Cómo funcionan las dos ramas" and "El codiseño del
  * kernel"): sequence b holds n_b = seqlens[b] cached tokens, positions
- * 0 .. n_b - 1 with the new token last, and its new query is position
- * i = n_b - 1, so the selection and the attention are exactly those of the
+ * 0 .. n_b - 1 with the new tokens last, and its r-th new query is position
+ * i = n_b - R + r, so the selection and the attention are exactly those of the
  * forward's row i; the per-layer state a sparse layer keeps is the block ids
  * (Flash-MSA article on tech.kuratif.com, block-wise sparsity).
  *
- * `dims`: batch = B sequences (<= 65535, and B * ceil(Hkv / 32) <= 65535),
- * seqlen = C, the cache capacity in tokens per sequence; other fields as above
- * (dtype MSA_BF16 or MSA_F32; msa_decode_index_topk also takes MSA_FP8_E4M3
- * for an fp8 index cache, scores accumulated in fp32 as in msa_index_topk).
- * Cache slots at or past n_b are never read.
+ * `dims`: batch = B sequences, seqlen = C, the cache capacity in tokens per
+ * sequence; other fields as above (dtype MSA_BF16 or MSA_F32; the selection
+ * calls also take MSA_FP8_E4M3 for an fp8 index cache, scores accumulated in
+ * fp32 as in msa_index_topk). num_queries = R >= 1, with B * R <= 65535 and
+ * B * ceil(R * Hkv / 32) <= 65535 (MSA_ERR_SHAPE otherwise). Cache slots at or
+ * past n_b are never read.
  *   seqlens   [B] int32 on the DEVICE (read by the kernels, so a step can be
- *             enqueued without a host round trip). A length outside [1, C]
- *             is not an error: that sequence's outputs are block ids all -1,
- *             O = 0 and LSE = -inf.
+ *             enqueued without a host round trip). A sequence whose length is
+ *             outside [1, C], and a query whose position is negative, is not
+ *             an error: its block ids are -1, O = 0 and LSE = -inf.
+ * Tensor layouts (for R = 1 they are the same bytes as [B, Hkv, Di], [B, Hq, D],
+ * [B, Hkv, k] and [B, Hq]):
+ *   q_idx     [B, R, Hkv, Di]  the new tokens' index queries
+ *   k_idx     [B, C, Di]       index-key cache
+ *   q         [B, R, Hq, D]    the new tokens' queries
+ *   k, v      [B, C, Hkv, D]   key and value caches
+ *   block_idx [B, Hkv, R, k]   int32, the layout of msa_index_topk's rows
+ *             (ascending kept ids, local block i / Bk last, -1 padding),
+ *             bit-identical to the forward's rows; an OUTPUT of the selection
+ *             calls, an input of the attention call (ids < 0 or past the
+ *             query's block are skipped without any read; other layouts give
+ *             unspecified outputs but never an access outside the buffers).
+ *   o         [B, R, Hq, D]    OUTPUT, dtype
+ *   lse       [B, Hq, R]       OUTPUT fp32, natural log
+ *   ws        at least msa_decode_workspace_bytes(dims, op, R) bytes (op
+ *             MSA_OP_DECODE_INDEX: block scores; MSA_OP_DECODE_ATTN: one fp32
+ *             partial output and LSE per kept block and head; MSA_OP_DECODE:
+ *             the larger of the two, as the stages run one after the other).
  */
-
-/*
- *   Uses batch, seqlen, kv_heads, index_dim, block_size, topk, dtype, causal.
- *   q_idx     [B, Hkv, Di]    the new tokens' index queries, dtype
- *   k_idx     [B, C, Di]      index-key cache, dtype
- *   block_idx [B, Hkv, k]     int32 OUTPUT, the layout of msa_index_topk's rows
- *             (ascending kept ids, local block L = (n_b - 1) / Bk last, -1
- *             padding), bit-identical to the forward's row n_b - 1.
- *   ws        at least msa_workspace_bytes(dims, MSA_OP_DECODE_INDEX) bytes
- *             (block scores of the competing blocks).
- */
-MSA_API int msa_decode_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx,
+MSA_API int msa_decode_index_topk(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx,
                                   const int32_t* seqlens, int32_t* block_idx, void* ws, size_t ws_bytes,
                                   void* stream);
-
-/*
- *   Uses every field of `dims` except index_dim.
- *   q         [B, Hq, D]      the new tokens' queries, dtype
- *   k, v      [B, C, Hkv, D]  key and value caches, dtype
- *   block_idx [B, Hkv, k]     int32 kept blocks (as msa_decode_index_topk
- *             writes them). Ids < 0 or past the query's block are skipped
- *             (no memory is read for them); other layouts give unspecified
- *             outputs but never an access outside the given buffers.
- *   softmax_scale  as for msa_sparse_attn_fwd
- *   o         [B, Hq, D]      OUTPUT, dtype
- *   lse       [B, Hq]         OUTPUT fp32, natural log
- *   ws        at least msa_workspace_bytes(dims, MSA_OP_DECODE_ATTN) bytes
- *             (one fp32 partial output and LSE per kept block and head).
- */
-MSA_API int msa_decode_attn(const msa_dims* dims, const void* q, const void* k, const void* v,
+MSA_API int msa_decode_attn(const msa_dims* dims, int32_t num_queries, const void* q, const void* k, const void* v,
                             const int32_t* seqlens, const int32_t* block_idx, float softmax_scale, void* o,
                             float* lse, void* ws, size_t ws_bytes, void* stream);
-
-/* msa_decode_index_topk then msa_decode_attn on `stream` (every field of
- * `dims` used); ws at least msa_workspace_bytes(dims, MSA_OP_DECODE). */
-MSA_API int msa_decode(const msa_dims* dims, const void* q_idx, const void* k_idx, const void* q, const void* k,
-                       const void* v, const int32_t* seqlens, float softmax_scale, int32_t* block_idx, void* o,
-                       float* lse, void* ws, size_t ws_bytes, void* stream);
+/* msa_decode_index_topk then msa_decode_attn on `stream`. */
+MSA_API int msa_decode(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx,
+                       const void* q, const void* k, const void* v, const int32_t* seqlens, float softmax_scale,
+                       int32_t* block_idx, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Decoding against a paged cache: the same computation as msa_decode_index_topk,
- * msa_decode_attn and msa_decode, with each cache held as a pool of 128-token
- * pages and a block table naming the page of every block of every sequence
- * (the MSA block, the unit the index branch selects, is the page: Flash-MSA
- * article, block-wise sparsity).
+ * Decoding against a paged cache: the same computation as the three calls
+ * above, with each cache held as a pool of 128-token pages and a block table
+ * naming the page of every block of every sequence (the MSA block, the unit the
+ * index branch selects, is the page: Flash-MSA article, block-wise sparsity).
  *   k_idx_pages [P, 128, Di], k_pages and v_pages [P, 128, Hkv, D]: pools of
  *             P = num_pages pages (dtype as for the contiguous calls).
  *   block_table [B, ceil(C / 128)] int32 on the DEVICE: page of block j of
@@ -381,19 +372,26 @@ MSA_API int msa_decode(const msa_dims* dims, const void* q_idx, const void* k_id
  *             at or past ceil(n_b / 128) are not read. An entry outside
  *             [0, num_pages) is not an error: that block is never read, it
  *             scores -inf in the selection and contributes no tokens.
- *   Other arguments, outputs and workspaces as for the contiguous calls.
+ *   num_pages < 0 is MSA_ERR_SHAPE. Other arguments, outputs and workspaces
+ *   as for the contiguous calls.
  */
-MSA_API int msa_decode_paged_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx_pages,
-                                        const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
-                                        int32_t* block_idx, void* ws, size_t ws_bytes, void* stream);
-MSA_API int msa_decode_paged_attn(const msa_dims* dims, const void* q, const void* k_pages, const void* v_pages,
-                                  const int32_t* block_table, int32_t num_pages, const int32_t* seqlens,
-                                  const int32_t* block_idx, float softmax_scale, void* o, float* lse, void* ws,
-                                  size_t ws_bytes, void* stream);
-MSA_API int msa_decode_paged(const msa_dims* dims, const void* q_idx, const void* k_idx_pages, const void* q,
-                             const void* k_pages, const void* v_pages, const int32_t* block_table,
+MSA_API int msa_decode_paged_index_topk(const msa_dims* dims, int32_t num_queries, const void* q_idx,
+                                        const void* k_idx_pages, const int32_t* block_table, int32_t num_pages,
+                                        const int32_t* seqlens, int32_t* block_idx, void* ws, size_t ws_bytes,
+                                        void* stream);
+MSA_API int msa_decode_paged_attn(const msa_dims* dims, int32_t num_queries, const void* q, const void* k_pages,
+                                  const void* v_pages, const int32_t* block_table, int32_t num_pages,
+                                  const int32_t* seqlens, const int32_t* block_idx, float softmax_scale, void* o,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream);
+MSA_API int msa_decode_paged(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx_pages,
+                             const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                              int32_t num_pages, const int32_t* seqlens, float softmax_scale, int32_t* block_idx,
                              void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of a decode call with num_queries new queries per sequence
+ * (op MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN or MSA_OP_DECODE); 0 if the sizes
+ * are invalid. msa_workspace_bytes gives the same for num_queries = 1. */
+MSA_API size_t msa_decode_workspace_bytes(const msa_dims* dims, int op, int32_t num_queries);
 
 /* Workspace bytes the given entry point needs for these sizes; 0 if the sizes
  * are invalid or the op needs none. Pure host arithmetic. */

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.msa_abi_version() == 4
+    assert lib.msa_abi_version() == 5
     for s in range(7):
         assert lib.msa_strerror(s)
     assert lib.msa_strerror(99) == b"unknown status"
@@ -240,21 +240,22 @@ def test_workspace_sizes(lib):
 def _dec_index(lib, d, ptrs=None, ws=None, nws=0):
     p = dict(qi=FAKE, ki=FAKE, lens=FAKE, bi=FAKE)
     p.update(ptrs or {})
-    return lib.msa_decode_index_topk(ctypes.byref(d), p["qi"], p["ki"], p["lens"], p["bi"], ws, nws, None)
+    return lib.msa_decode_index_topk(ctypes.byref(d), p.get("R", 1), p["qi"], p["ki"], p["lens"], p["bi"], ws, nws,
+                                     None)
 
 
 def _dec_attn(lib, d, ptrs=None, ws=None, nws=0):
     p = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
     p.update(ptrs or {})
-    return lib.msa_decode_attn(ctypes.byref(d), p["q"], p["k"], p["v"], p["lens"], p["bi"], 0.0, p["o"],
-                               p["lse"], ws, nws, None)
+    return lib.msa_decode_attn(ctypes.byref(d), p.get("R", 1), p["q"], p["k"], p["v"], p["lens"], p["bi"], 0.0,
+                               p["o"], p["lse"], ws, nws, None)
 
 
 def _dec(lib, d, ptrs=None, ws=None, nws=0):
     p = dict(qi=FAKE, ki=FAKE, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
     p.update(ptrs or {})
-    return lib.msa_decode(ctypes.byref(d), p["qi"], p["ki"], p["q"], p["k"], p["v"], p["lens"], 0.0, p["bi"],
-                          p["o"], p["lse"], ws, nws, None)
+    return lib.msa_decode(ctypes.byref(d), p.get("R", 1), p["qi"], p["ki"], p["q"], p["k"], p["v"], p["lens"], 0.0,
+                          p["bi"], p["o"], p["lse"], ws, nws, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -342,14 +343,29 @@ def test_paged_decode_arguments(lib):
     def call(ptrs=None, pages=10, ws=FAKE, nws=need, dd=d):
         p = dict(qi=FAKE, ki=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
         p.update(ptrs or {})
-        return lib.msa_decode_paged(ctypes.byref(dd), p["qi"], p["ki"], p["q"], p["k"], p["v"], p["bt"], pages,
+        return lib.msa_decode_paged(ctypes.byref(dd), 1, p["qi"], p["ki"], p["q"], p["k"], p["v"], p["bt"], pages,
                                     p["lens"], 0.0, p["bi"], p["o"], p["lse"], ws, nws, None)
     assert call(dict(bt=None)) == 1
     assert call(dict(bt=MISALIGNED)) == 4
     assert call(pages=-1) == 2
     assert call(nws=need - 1) == 5
     assert call(dd=_dims(dtype=msa.MSA_FP8_E4M3)) == 3
-    assert lib.msa_decode_paged_index_topk(ctypes.byref(_dims(dtype=msa.MSA_FP8_E4M3)), FAKE, FAKE, None, 10,
+    assert lib.msa_decode_paged_index_topk(ctypes.byref(_dims(dtype=msa.MSA_FP8_E4M3)), 1, FAKE, FAKE, None, 10,
                                            FAKE, FAKE, FAKE, 1 << 20, None) == 1
-    assert lib.msa_decode_paged_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -3, FAKE, FAKE, 0.0, FAKE, FAKE,
+    assert lib.msa_decode_paged_attn(ctypes.byref(d), 1, FAKE, FAKE, FAKE, FAKE, -3, FAKE, FAKE, 0.0, FAKE, FAKE,
                                      FAKE, need, None) == 2
+
+
+def test_multi_query_decode_arguments(lib):
+    d = _dims(batch=4, seqlen=5000, kv_heads=8, group_size=8, topk=16)
+    one = msa.decode_workspace_bytes(d, msa.MSA_OP_DECODE_ATTN, 1)
+    assert one == msa.workspace_bytes(d, msa.MSA_OP_DECODE_ATTN)
+    four = msa.decode_workspace_bytes(d, msa.MSA_OP_DECODE_ATTN, 4)
+    assert four == 4 * 8 * 4 * 16 * 8 * 128 * 4 + -(-4 * 4 * 8 * 16 * 8 * 4 // 256) * 256
+    assert msa.decode_workspace_bytes(d, msa.MSA_OP_DECODE_INDEX, 3) == -(-4 * 3 * 8 * 40 * 4 // 256) * 256
+    assert msa.decode_workspace_bytes(d, msa.MSA_OP_DECODE, 0) == 0
+    assert msa.decode_workspace_bytes(d, msa.MSA_OP_ATTN, 2) == 0
+    assert _dec(lib, d, dict(R=0)) == 2
+    assert _dec(lib, _dims(batch=20000), dict(R=4)) == 2              # B * R > 65535
+    assert _dec(lib, d, dict(R=4), ws=FAKE, nws=four - 1) == 5       # the R-query workspace is required
+    assert _dec_attn(lib, d, dict(R=4, o=None), ws=FAKE, nws=four) == 1

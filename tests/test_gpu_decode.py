@@ -262,3 +262,55 @@ def test_decode_1m_capacity():
     torch.cuda.synchronize()
     assert torch.equal(bi, bi8)
     _check(w, x, bi, o, lse)
+
+
+def _multi_queries(w, R, seed=11):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qi = torch.randint(-4, 5, (w.batch, R, w.kv_heads, w.index_dim), generator=g).to(dt)
+    q = torch.randn((w.batch, R, w.q_heads, w.head_dim), generator=g).to(dt)
+    return qi.to(DEV), q.to(DEV)
+
+
+@pytest.mark.parametrize("R", [2, 4, 7])
+def test_decode_multi_query(R):
+    """R new tokens per sequence (row r at position n_b - R + r): block ids,
+    O and LSE against the oracle; each row bitwise equal to a one-query decode
+    of the prefix that ends at it; rows at negative positions empty."""
+    w = Workload(f"dec_r{R}", 6, 3000, 4, 8, 128, 128, topk=8)
+    lengths = [1, 3, 129, 1000, 2999, 3000]
+    x = _dev(make_decode_inputs(w, device="cpu", lengths=lengths))
+    qi, q = _multi_queries(w, R)
+    bi, o, lse = msa.decode(qi, x["k_idx"], q, x["k"], x["v"], x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    assert tuple(bi.shape) == (6, 4, R, 8) and tuple(o.shape) == (6, R, 32, 128) and tuple(lse.shape) == (6, 32, R)
+    lens = np.array(lengths)
+    want_bi = O.decode_index_topk(qi.cpu(), x["k_idx"].cpu(), lens, w.block_size, w.topk)
+    assert np.array_equal(bi.cpu().numpy(), want_bi)
+    want_o, want_l = O.decode_attention(q.cpu(), x["k"].cpu(), x["v"].cpu(), lens, want_bi, w.block_size)
+    got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+    fin = np.isfinite(want_l)
+    assert np.array_equal(fin, np.isfinite(got_l))
+    assert (got_o[~fin.any(axis=1)] == 0).all()
+    # O is stored in bf16: where |O| >= 4 its spacing is 2^-5, so the rounding
+    # alone (half a spacing, 0.0156) exceeds 1e-2; there the bar is that
+    # rounding plus 2e-3 (rows with one or two tokens, as at positions 1-2, can
+    # reach |O| >= 4).
+    big = np.abs(want_o) >= 4.0
+    err = np.abs(got_o - want_o)
+    eo = float(err[~big].max())
+    el = float(np.abs(got_l[fin] - want_l[fin]).max())
+    log(f"  dec_r{R}: max|dO|={eo:.2e} (|O| < 4), {int(big.sum())} elements with |O| >= 4 "
+        f"(max err {float(err[big].max()) if big.any() else 0.0:.2e}), max|dLSE|={el:.2e}")
+    assert eo <= O_TOL and el <= LSE_TOL
+    assert (err[big] <= 2.0 ** -6 + 2e-3).all()
+    for r in range(R):
+        n_r = torch.clamp(x["seqlens"] - R + r + 1, min=0).to(torch.int32)
+        b1, o1, l1 = msa.decode(qi[:, r].contiguous(), x["k_idx"], q[:, r].contiguous(), x["k"], x["v"], n_r, w.topk)
+        torch.cuda.synchronize()
+        assert torch.equal(b1, bi[:, :, r]) and torch.equal(o1, o[:, r]) and torch.equal(l1, lse[:, :, r])
+    pools, table, P = _to_pages(x, w)
+    bp, op, lp = msa.decode_paged(qi, pools["k_idx"], q, pools["k"], pools["v"], table, x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(bp, bi) and torch.equal(op, o) and torch.equal(lp, lse)
