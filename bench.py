@@ -282,6 +282,28 @@ def bench_decode(args, dev):
         "roofline": rooflines[dominant],
         "rooflines": rooflines,
     }
+    if args.decode_queries > 1:
+        # R new tokens per sequence at once (positions n_b - R .. n_b - 1): one step.
+        R = args.decode_queries
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed + 4000)
+        qiR = torch.randint(-4, 5, (B, R, Hkv, w.index_dim), generator=g, device=dev).to(x["q_idx"].dtype)
+        qR = torch.randn((B, R, Hkv * G, D), generator=g, device=dev).to(x["q"].dtype)
+        wsR = torch.empty(max(1, msa.decode_workspace_bytes(dims, msa.MSA_OP_DECODE, R)), dtype=torch.uint8,
+                          device=dev)
+
+        def rstep():
+            msa.decode(qiR, x["k_idx"], qR, x["k"], x["v"], x["seqlens"], w.topk, workspace=wsR)
+        for _ in range(args.warmup):
+            rstep()
+        evr = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in evr:
+            e[0].record(stream)
+            rstep()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        msr = float(np.mean([e[0].elapsed_time(e[1]) for e in evr]))
+        out["multi_query"] = {"queries_per_sequence": R, "ms": msr, "tokens_per_s": B * R / (msr * 1e-3)}
     if args.paged:
         # The same step on paged caches: 128-token pages in a seeded random order and a block table.
         nbs = -(-C // w.block_size)
@@ -436,6 +458,8 @@ def main():
                     help="also time the main-branch backward (msa_sparse_attn_bwd) on the step's outputs")
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step (64 sequences, 128K-token caches) instead of the forward")
+    ap.add_argument("--decode-queries", type=int, default=1,
+                    help="with --decode: also time one step with this many new tokens per sequence")
     ap.add_argument("--paged", action="store_true",
                     help="with --decode: also time the step on paged caches (block table, random page order)")
     ap.add_argument("--dense", action="store_true",
