@@ -314,3 +314,27 @@ def test_decode_multi_query(R):
     bp, op, lp = msa.decode_paged(qi, pools["k_idx"], q, pools["k"], pools["v"], table, x["seqlens"], w.topk)
     torch.cuda.synchronize()
     assert torch.equal(bp, bi) and torch.equal(op, o) and torch.equal(lp, lse)
+
+
+@pytest.mark.parametrize("w,R", [
+    (Workload("dec_r3_hkv40", 4, 1300, 40, 1, 64, 64, topk=7), 3),        # R * Hkv = 120: four column chunks
+    (Workload("dec_r5_k32_g32", 3, 5000, 2, 32, 64, 128, topk=32), 5),    # k = 32, G = 32
+    (Workload("dec_r2_f32", 4, 700, 1, 4, 64, 64, topk=4, dtype="f32"), 2),
+])
+def test_decode_multi_query_shapes(w, R):
+    lengths = [w.seqlen, 129, 2, w.seqlen - 1][: w.batch]
+    x = _dev(make_decode_inputs(w, device="cpu", lengths=lengths))
+    qi, q = _multi_queries(w, R, seed=13)
+    bi, o, lse = msa.decode(qi, x["k_idx"], q, x["k"], x["v"], x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    lens = np.array(lengths)
+    want_bi = O.decode_index_topk(qi.cpu(), x["k_idx"].cpu(), lens, w.block_size, w.topk)
+    assert np.array_equal(bi.cpu().numpy(), want_bi)
+    want_o, want_l = O.decode_attention(q.cpu(), x["k"].cpu(), x["v"].cpu(), lens, want_bi, w.block_size)
+    got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+    fin = np.isfinite(want_l)
+    assert np.array_equal(fin, np.isfinite(got_l))
+    err = np.abs(got_o - want_o)
+    big = np.abs(want_o) >= 4.0
+    assert float(err[~big].max()) <= O_TOL and (err[big] <= 2.0 ** -6 + 2e-3).all()
+    assert float(np.abs(got_l[fin] - want_l[fin]).max()) <= LSE_TOL
