@@ -78,11 +78,17 @@ __global__ __launch_bounds__(NW * kWave) void dense_attn_kernel(const T* __restr
     using KS = SwzTile<T, D>;
     constexpr int NT = NW * kWave;
     __shared__ __align__(16) unsigned char lds[NBUF * KV::BYTES];
+    // The parts of one (batch, query block, group) unit read the same K/V
+    // blocks at about the same time: runs of 8 * parts work-groups give each of
+    // the 8 XCDs (work-group x runs on XCD x % 8) one whole unit, so its parts
+    // share that XCD's L2. Units are numbered latest (heaviest) query block first.
     const int x = blockIdx.x;
-    const int pt = x % parts;
-    const int g = (x / parts) % Hkv;
-    const int b = (x / (parts * Hkv)) % B;
-    const int qb = nb - 1 - x / (parts * Hkv * B);   // latest (heaviest) query blocks first
+    const int unit = (x / (8 * parts)) * 8 + x % 8;
+    if (unit >= nb * B * Hkv) return;   // padding of the last run
+    const int pt = (x / 8) % parts;
+    const int g = unit % Hkv;
+    const int b = (unit / Hkv) % B;
+    const int qb = nb - 1 - unit / (Hkv * B);
     const int Hq = Hkv * G;
     const int q0 = qb * kBlock;
 
@@ -275,7 +281,8 @@ void launch_dense_t(const LaunchDims& d, const void* q, const void* k, const voi
     constexpr int kTiles = kBlock * G / 32;
     const int parts = (kTiles + NW * TPW - 1) / (NW * TPW);
     constexpr int NBUF = 2 * KVTile<T, D>::BYTES <= 160 * 1024 ? 2 : 1;
-    const size_t grid = (size_t)d.nb * d.B * d.Hkv * parts;
+    const size_t units = (size_t)d.nb * d.B * d.Hkv;
+    const size_t grid = (units + 7) / 8 * 8 * parts;
     hipLaunchKernelGGL((dense_attn_kernel<T, D, G, NBUF, NW, TPW>), dim3((unsigned)grid), dim3(NW * kWave), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(vt),
                        static_cast<T*>(o), lse, d.B, d.N, d.Hkv, d.nb, parts, scale_log2);

@@ -328,11 +328,16 @@ __global__ __launch_bounds__(kDenseKlWaves * kWave) void dense_kl_kernel(
     constexpr int NT = kDenseKlWaves * kWave;
     constexpr int KB = SwzTile<T, D>::BYTES, BUF = KB + SwzTile<T, DI>::BYTES;
     __shared__ __align__(16) unsigned char lds[NBUF * BUF];
+    // Runs of 8 * parts work-groups give each XCD one whole (batch, query
+    // block, group) unit, so the unit's parts share that XCD's L2 for the K and
+    // K_idx blocks they all stream; latest (heaviest) query blocks first.
     const int x = blockIdx.x;
-    const int pt = x % parts;
-    const int g = (x / parts) % Hkv;
-    const int b = (x / (parts * Hkv)) % B;
-    const int qb = nb - 1 - x / (parts * Hkv * B);   // latest (heaviest) query blocks first
+    const int unit = (x / (8 * parts)) * 8 + x % 8;
+    if (unit >= nb * B * Hkv) return;   // padding of the last run
+    const int pt = (x / 8) % parts;
+    const int g = unit % Hkv;
+    const int b = (unit / Hkv) % B;
+    const int qb = nb - 1 - unit / (Hkv * B);
     const int Hq = Hkv * G;
     const int q0 = qb * kBlock;
 
@@ -531,7 +536,8 @@ static void launch_dense_kl_t(const LaunchDims& d, const void* q, const void* k,
     const int parts = (kTiles + kDenseKlWaves - 1) / kDenseKlWaves;
     constexpr int BUF = SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES;
     constexpr int NBUF = 2 * BUF <= 160 * 1024 ? 2 : 1;
-    const size_t grid = (size_t)d.nb * d.B * d.Hkv * parts;
+    const size_t units = (size_t)d.nb * d.B * d.Hkv;
+    const size_t grid = (units + 7) / 8 * 8 * parts;
     hipLaunchKernelGGL((dense_kl_kernel<T, D, DI, G, NBUF>), dim3((unsigned)grid), dim3(kDenseKlWaves * kWave), 0,
                        st, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(q_idx),
                        static_cast<const T*>(k_idx), lse, kl_rows, index_lse, d.B, d.N, d.Hkv, d.nb, parts,
