@@ -15,24 +15,26 @@
 // kept blocks' K and V (k * 128 tokens per (sequence, group)); both are bound
 // by HBM bandwidth, so the kernels aim at full-line, many-in-flight loads and
 // use the matrix cores only to keep the VALU off the critical path:
-//   decode_scores_kernel  one wave per (sequence, competing block, 32 groups):
-//                         S^T = K_idx Q_idx^T on the matrix cores straight from
-//                         global memory (no LDS), block max in-lane plus one
-//                         half-wave swap -> block scores [B, Hkv, nb] fp32;
-//                         an fp8 e4m3 index cache halves the bytes streamed
-//   decode_topk_kernel    one wave per (sequence, group): a lane-local sorted
-//                         list over a strided share of the block scores, then
-//                         k-1 wave-wide maxima (DPP within rows, lane reads
-//                         across them) of packed (score, -id) keys; ids
-//                         sorted ascending, the local block appended
-//   decode_attn_kernel    one work-group per (sequence, group, kept block):
-//                         S^T = K Q^T per wave (32 keys each, K from global),
-//                         block softmax across the four waves through LDS,
-//                         O^T = V^T P^T with V staged in LDS (P as a bf16
+//   decode_scores_kernel  one wave per (sequence, competing block, 32 columns
+//                         of (new query, group) pairs): S^T = K_idx Q_idx^T on
+//                         the matrix cores straight from global memory (no
+//                         LDS; the index keys are read once for all R queries),
+//                         block max in-lane plus one half-wave swap -> block
+//                         scores [B, R * Hkv, nb] fp32; an fp8 e4m3 index cache
+//                         halves the bytes streamed
+//   decode_topk_kernel    one wave per (sequence, new query, group): a
+//                         lane-local sorted list over a strided share of the
+//                         block scores, then k-1 wave-wide maxima (DPP within
+//                         rows, lane reads across them) of packed (score, -id)
+//                         keys; ids sorted ascending, the local block appended
+//   decode_attn_kernel    one work-group per (sequence, new query, group, kept
+//                         block): S^T = K Q^T per wave (32 keys each, K from
+//                         global), block softmax across the four waves through
+//                         LDS, O^T = V^T P^T with V staged in LDS (P as a bf16
 //                         hi + lo pair: two products, exact to ~2^-17 of P);
 //                         a normalised fp32 partial output and its LSE per head
-//   decode_combine_kernel one work-group per (sequence, group): the kept
-//                         blocks' partials merged in slot order -> O, LSE.
+//   decode_combine_kernel one work-group per (sequence, new query, group): the
+//                         kept blocks' partials merged in slot order -> O, LSE.
 // Every sum runs in a fixed order: results are bitwise reproducible.
 //
 // The caches are either contiguous per sequence ([B, C, ...]) or paged: a pool
