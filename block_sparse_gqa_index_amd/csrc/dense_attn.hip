@@ -114,10 +114,32 @@ __global__ __launch_bounds__(NW * kWave) void dense_attn_kernel(const T* __restr
     const T* vtbase = vt + ((size_t)b * Hkv + g) * nb * D * kBlock;
     KVPrefetch<T, D, 0, NT> pk;
     KVPrefetch<T, D, 1, NT> pv;
-    pk.load(kbase, kv_row, min(kBlock, N));
-    pv.load(vtbase, 0, 0);
-    pk.commit(lds);
-    pv.commit(lds);
+    // bf16 with two buffers: K_{j+1} and V_{j+1} are copied global -> LDS
+    // directly (no registers) into the other buffer at the start of block j;
+    // the barrier that ends block j waits for them. Rows of K past the
+    // sequence repeat its last key (masked for every stored row).
+    constexpr bool kDma = sizeof(T) == 2 && NBUF == 2;
+    auto dma_kv = [&](unsigned char* buf, int jb) {
+        if constexpr (kDma) {
+            constexpr int KROWS = 64 / KS::CPR, VROWS = 64 / SwzTile<T, kBlock>::CPR;
+            const int last = min(kBlock, N - jb * kBlock) - 1;
+            for (int r0 = w * KROWS; r0 < kBlock; r0 += NW * KROWS)
+                dma_rows<D>(buf, reinterpret_cast<const bf16_t*>(kbase) + (size_t)jb * kBlock * kv_row, kv_row, r0,
+                            last, lane);
+            for (int r0 = w * VROWS; r0 < D; r0 += NW * VROWS)
+                dma_rows<kBlock>(buf + kBlock * KS::ROWB,
+                                 reinterpret_cast<const bf16_t*>(vtbase) + (size_t)jb * D * kBlock, kBlock, r0, D - 1,
+                                 lane);
+        }
+    };
+    if constexpr (kDma) {
+        dma_kv(lds, 0);
+    } else {
+        pk.load(kbase, kv_row, min(kBlock, N));
+        pv.load(vtbase, 0, 0);
+        pk.commit(lds);
+        pv.commit(lds);
+    }
     __syncthreads();
 
     float m_run[TPW], l_run[TPW];
@@ -138,7 +160,11 @@ __global__ __launch_bounds__(NW * kWave) void dense_attn_kernel(const T* __restr
         // stored after them, V^T_{j+1} requested after the softmax and stored
         // after the P V product. Single-buffered: both are stored after a
         // barrier that ends block j.
-        if (more) pk.load(kbase + (size_t)(j + 1) * kBlock * kv_row, kv_row, min(kBlock, N - (j + 1) * kBlock));
+        if constexpr (kDma) {
+            if (more) dma_kv(nxt, j + 1);
+        } else {
+            if (more) pk.load(kbase + (size_t)(j + 1) * kBlock * kv_row, kv_row, min(kBlock, N - (j + 1) * kBlock));
+        }
         if (wave_ok) {
             floatx16 s[TPW][4];
 #pragma unroll
@@ -197,7 +223,7 @@ __global__ __launch_bounds__(NW * kWave) void dense_attn_kernel(const T* __restr
                     }
                 }
             }
-            if constexpr (NBUF == 2) {
+            if constexpr (NBUF == 2 && !kDma) {
                 if (more) {
                     pv.load(vtbase + (size_t)(j + 1) * D * kBlock, 0, 0);
                     pk.commit(nxt);
@@ -223,14 +249,15 @@ __global__ __launch_bounds__(NW * kWave) void dense_attn_kernel(const T* __restr
                     for (int t = 0; t < TPW; ++t) mma16(acc[t][dt], a, bp[t]);
                 }
             }
-        } else if constexpr (NBUF == 2) {
+        } else if constexpr (NBUF == 2 && !kDma) {
             if (more) {
                 pv.load(vtbase + (size_t)(j + 1) * D * kBlock, 0, 0);
                 pk.commit(nxt);
             }
         }
         if (more) {
-            if constexpr (NBUF == 2) {
+            if constexpr (kDma) {
+            } else if constexpr (NBUF == 2) {
                 pv.commit(nxt);
             } else {
                 pv.load(vtbase + (size_t)(j + 1) * D * kBlock, 0, 0);

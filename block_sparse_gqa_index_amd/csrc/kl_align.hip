@@ -362,10 +362,32 @@ __global__ __launch_bounds__(kDenseKlWaves * kWave) void dense_kl_kernel(
     const T* kibase = k_idx + (size_t)b * N * DI;
     RowPrefetch<T, D, NT> pk;
     RowPrefetch<T, DI, NT> pi;
-    pk.load(kbase, krow, min(kBlock, N));
-    pi.load(kibase, DI, min(kBlock, N));
-    pk.commit(lds);
-    pi.commit(lds + KB);
+    // bf16 with two buffers: K_{j+1} and K_idx_{j+1} are copied global -> LDS
+    // directly (no registers) into the other buffer at the start of block j;
+    // the barrier that ends block j waits for them. Rows past the sequence
+    // repeat its last key (masked for every stored row; a row past the
+    // sequence has zero queries).
+    constexpr bool kDma = sizeof(T) == 2 && NBUF == 2;
+    auto dma_keys = [&](unsigned char* buf, int jb) {
+        if constexpr (kDma) {
+            constexpr int KR = 64 / SwzTile<T, D>::CPR, IR = 64 / SwzTile<T, DI>::CPR;
+            const int last = min(kBlock, N - jb * kBlock) - 1;
+            for (int r0 = w * KR; r0 < kBlock; r0 += kDenseKlWaves * KR)
+                dma_rows<D>(buf, reinterpret_cast<const bf16_t*>(kbase) + (size_t)jb * kBlock * krow, krow, r0, last,
+                            lane);
+            for (int r0 = w * IR; r0 < kBlock; r0 += kDenseKlWaves * IR)
+                dma_rows<DI>(buf + KB, reinterpret_cast<const bf16_t*>(kibase) + (size_t)jb * kBlock * DI, DI, r0,
+                             last, lane);
+        }
+    };
+    if constexpr (kDma) {
+        dma_keys(lds, 0);
+    } else {
+        pk.load(kbase, krow, min(kBlock, N));
+        pi.load(kibase, DI, min(kBlock, N));
+        pk.commit(lds);
+        pi.commit(lds + KB);
+    }
     __syncthreads();
 
     KlAcc acc{0.f, 0.f, 0.f, -__builtin_inff(), 0.f};
@@ -374,12 +396,16 @@ __global__ __launch_bounds__(kDenseKlWaves * kWave) void dense_kl_kernel(
         unsigned char* nxt = lds + (NBUF == 2 ? ((j + 1) & 1) * BUF : 0);
         const bool more = j < qb;
         const int nvalid = more ? min(kBlock, N - (j + 1) * kBlock) : 0;
-        if (more) pk.load(kbase + (size_t)(j + 1) * kBlock * krow, krow, nvalid);
+        if constexpr (kDma) {
+            if (more) dma_keys(nxt, j + 1);
+        } else {
+            if (more) pk.load(kbase + (size_t)(j + 1) * kBlock * krow, krow, nvalid);
+        }
         if (tile_ok) {
             floatx16 s[4], u[4];
             tile_scores<T, D>(s, bq, cur, col, half);
             tile_scores<T, DI>(u, bi, cur + KB, col, half);
-            if constexpr (NBUF == 2) {
+            if constexpr (NBUF == 2 && !kDma) {
                 if (more) {
                     pi.load(kibase + (size_t)(j + 1) * kBlock * DI, DI, nvalid);
                     pk.commit(nxt);
@@ -391,14 +417,15 @@ __global__ __launch_bounds__(kDenseKlWaves * kWave) void dense_kl_kernel(
             acc.Bs += a.Bs;
             acc.P += a.P;
             merge_lse(acc.mu, acc.lu, a.mu, a.lu);
-        } else if constexpr (NBUF == 2) {
+        } else if constexpr (NBUF == 2 && !kDma) {
             if (more) {
                 pi.load(kibase + (size_t)(j + 1) * kBlock * DI, DI, nvalid);
                 pk.commit(nxt);
             }
         }
         if (more) {
-            if constexpr (NBUF == 2) {
+            if constexpr (kDma) {
+            } else if constexpr (NBUF == 2) {
                 pi.commit(nxt + KB);
             } else {
                 pi.load(kibase + (size_t)(j + 1) * kBlock * DI, DI, nvalid);

@@ -40,6 +40,22 @@ struct SwzTile {
     }
 };
 
+// Direct global -> LDS copy (no registers) of rows [r0, r0 + 64 / CPR) of a
+// swizzled bf16 tile [rows][W] (SwzTile layout): the wave's 64 lanes fill 64
+// consecutive 16-byte LDS chunks, lane i physical chunk i % CPR of row
+// r0 + i / CPR, so it reads logical chunk (i % CPR) ^ (row % SW) of that row.
+// Source rows past max_row repeat row max_row.
+template <int W>
+__device__ __forceinline__ void dma_rows(unsigned char* tile, const bf16_t* src, size_t stride, int r0, int max_row,
+                                         int lane) {
+    using S = SwzTile<bf16_t, W>;
+    const int row = r0 + lane / S::CPR, pc = lane % S::CPR;
+    const int lc = pc ^ (row & (S::SW - 1));
+    const bf16_t* g = src + (size_t)min(row, max_row) * stride + lc * (16 / sizeof(bf16_t));
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)(tile + r0 * S::ROWB), 16, 0, 0);
+}
+
 // A [128][W] tile from global rows `row_stride` elements apart; rows at or
 // beyond `valid_rows` are zero-filled.
 template <typename T, int W>
