@@ -282,14 +282,15 @@ __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
 // The warm-up's KL (MSA article, "Cómo se entrena MSA": during the first
 // iterations both branches attend to every visible token): the same per-row
 // KL with T_i = {0 .. i}, the teacher normalised by the dense attention's LSE.
-// Query-block outer like the dense attention: one 4-wave work-group per
-// (batch, query block, group, 128-row part), each wave one resident 32-row
-// tile (main and index query operands, the five running sums; one wave per
-// SIMD, so the KL tile's temporaries fit without spilling); K_j and
-// K_idx_j stream through two LDS buffers, the next block's rows requested into
-// registers before the current block's scores and stored after them.
+// Query-block outer like the dense attention: one 8-wave work-group per
+// (batch, query block, group, 256-row part), each wave one resident 32-row
+// tile (main and index query operands, the five running sums; two waves per
+// SIMD, so one wave's KL-tile vector work can run beside the other's matrix
+// products); K_j and K_idx_j stream through two LDS buffers (bf16: the next
+// block's rows copied global -> LDS directly, which keeps the wave within 256
+// registers; fp32: through registers).
 
-constexpr int kDenseKlWaves = 4;
+constexpr int kDenseKlWaves = 8;
 
 // Rows [128][W] of T moved global -> registers -> LDS (SwzTile<T, W>) by NT
 // threads; rows at or past valid_rows are zero-filled.
