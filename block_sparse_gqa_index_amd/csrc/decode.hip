@@ -16,7 +16,8 @@
 // by HBM bandwidth, so the kernels aim at full-line, many-in-flight loads and
 // use the matrix cores only to keep the VALU off the critical path:
 //   decode_scores_kernel  one wave per (sequence, competing block, 32 columns
-//                         of (new query, group) pairs): S^T = K_idx Q_idx^T on
+//                         of (new query, group) pairs; 16 when there are at
+//                         most 16, bf16): S^T = K_idx Q_idx^T on
 //                         the matrix cores straight from global memory (no
 //                         LDS; the index keys are read once for all R queries),
 //                         block max in-lane plus one half-wave swap -> block
@@ -84,7 +85,11 @@ template <> struct DecMma<fp8_t> {    // v_mfma_scale_f32_32x32x64_f8f6f4: e4m3 
     }
 };
 
-template <typename T, int DI>
+// COLS columns per wave: 32 (32 x 32 tiles, any element type) or 16 (bf16:
+// v_mfma_f32_16x16x32_bf16 on 16-key tiles, lane l supplying row l % 16 and
+// the 8 contraction elements at 8 * (l / 16) of each 32-deep slice, so one
+// load instruction covers 64 contiguous bytes of each of 16 key rows).
+template <typename T, int DI, int COLS>
 __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict__ q_idx,
                                                             const T* __restrict__ k_idx,
                                                             const int32_t* __restrict__ seqlens,
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
                                                             float* __restrict__ scores, int C, int Hkv,
                                                             int R, int nbs, int gchunks) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 31, half = lane >> 5;
+    const int col = lane % COLS, half = lane >> 5;
     const int b = blockIdx.y / gchunks, gc = blockIdx.y % gchunks;
     const int j = blockIdx.x * 4 + wave;
     const int n = seqlens[b];
@@ -102,16 +107,55 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
     // Columns are the (new query r, group g) pairs of the sequence, c = r * Hkv + g;
     // an earlier query reads only the blocks it sees.
     const int RH = R * Hkv;
-    const int c = gc * kGroupCols + col;
+    const int c = gc * COLS + col;
+    const bool writer = lane < COLS;   // one lane per column stores its block score
     // Block j of the sequence: contiguous in the cache, or the page the block table names.
     const T* kb = k_idx + ((size_t)b * C + (size_t)j * kBlock) * DI;
     if (pages) {
         const int pg = pages[(size_t)b * nbs + j];
         if (pg < 0 || pg >= num_pages) {   // not a page of the pool: the block scores -inf, nothing is read
-            if (half == 0 && c < RH) scores[((size_t)b * RH + c) * nbs + j] = -__builtin_inff();
+            if (writer && c < RH) scores[((size_t)b * RH + c) * nbs + j] = -__builtin_inff();
             return;
         }
         kb = k_idx + (size_t)pg * kBlock * DI;
+    }
+
+    if constexpr (COLS == 16) {
+        static_assert(sizeof(T) == 2, "16-column tiles are bf16 only");
+        constexpr int NS = DI / 32;   // 32-deep contraction slices
+        const int grp = lane >> 4;    // contraction group of the lane
+        Op8<T> bq[NS];
+        const T* qrow = q_idx + ((size_t)b * RH + (c < RH ? c : 0)) * DI;   // q_idx [B, R, Hkv, Di]
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            if (c < RH) bq[sl].load(qrow + 32 * sl + 8 * grp);
+            else bq[sl].zero();
+        }
+        float m = -__builtin_inff();
+        // Eight 16-key tiles, four tiles' operands in flight.
+#pragma unroll
+        for (int t0 = 0; t0 < 8; t0 += 4) {
+            Op8<T> a[4][NS];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const T* row = kb + (size_t)((t0 + t) * 16 + col) * DI;
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl) a[t][sl].load(row + 32 * sl + 8 * grp);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][sl].v, bq[sl].v, acc, 0, 0, 0);
+                m = vmax(m, vmax(vmax(acc[0], acc[1]), vmax(acc[2], acc[3])));
+            }
+        }
+        // Lanes l, l + 16, l + 32, l + 48 hold the four row quarters of column l % 16.
+        m = vmax(m, __shfl_xor(m, 16));
+        m = vmax(m, __shfl_xor(m, 32));
+        if (writer && c < RH) scores[((size_t)b * RH + c) * nbs + j] = m;
+        return;
     }
 
     using MM = DecMma<T>;
@@ -146,7 +190,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
         }
     }
     m = vmax(m, swap_halves(m));
-    if (half == 0 && c < RH) scores[((size_t)b * RH + c) * nbs + j] = m;
+    if (writer && c < RH) scores[((size_t)b * RH + c) * nbs + j] = m;
 }
 
 // ------------------------------------------------------------------- top-k --
@@ -527,12 +571,24 @@ void launch_topk(const float* scores, const int32_t* seqlens, int32_t* block_idx
 template <typename T, int DI>
 void launch_scores(const DecodeDims& d, const void* q_idx, const void* k_idx, const int32_t* seqlens,
                    const int32_t* pages, int num_pages, float* scores, hipStream_t st) {
-    const int gchunks = (d.R * d.Hkv + kGroupCols - 1) / kGroupCols;
     const int lmax = (d.C - 1) / kBlock;   // competing blocks of a full cache
     if (lmax == 0) return;
-    hipLaunchKernelGGL((decode_scores_kernel<T, DI>), dim3((lmax + 3) / 4, d.B * gchunks), dim3(256), 0, st,
+    const int RH = d.R * d.Hkv;
+    // bf16 with at most 16 columns: one 16-column set per sequence, each key
+    // block still read once. More columns take 32-column sets (a 16-column
+    // wave per set would read every block twice as often).
+    if constexpr (sizeof(T) == 2) {
+        if (RH <= 16) {
+            hipLaunchKernelGGL((decode_scores_kernel<T, DI, 16>), dim3((lmax + 3) / 4, d.B), dim3(256), 0, st,
+                               static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, pages, num_pages,
+                               scores, d.C, d.Hkv, d.R, d.nbs(), 1);
+            return;
+        }
+    }
+    const int g32 = (RH + kGroupCols - 1) / kGroupCols;
+    hipLaunchKernelGGL((decode_scores_kernel<T, DI, 32>), dim3((lmax + 3) / 4, d.B * g32), dim3(256), 0, st,
                        static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, pages, num_pages, scores,
-                       d.C, d.Hkv, d.R, d.nbs(), gchunks);
+                       d.C, d.Hkv, d.R, d.nbs(), g32);
 }
 
 template <typename T, int D>
