@@ -17,7 +17,7 @@
 // use the matrix cores only to keep the VALU off the critical path:
 //   decode_scores_kernel  one wave per (sequence, competing block, 32 columns
 //                         of (new query, group) pairs; 16 when there are at
-//                         most 16, bf16): S^T = K_idx Q_idx^T on
+//                         most 16, bf16 or fp8): S^T = K_idx Q_idx^T on
 //                         the matrix cores straight from global memory (no
 //                         LDS; the index keys are read once for all R queries),
 //                         block max in-lane plus one half-wave swap -> block
@@ -120,8 +120,36 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
         kb = k_idx + (size_t)pg * kBlock * DI;
     }
 
-    if constexpr (COLS == 16) {
-        static_assert(sizeof(T) == 2, "16-column tiles are bf16 only");
+    if constexpr (COLS == 16 && sizeof(T) == 1) {
+        static_assert(DI == 128, "16-column fp8 tiles take one 128-deep product");
+        // v_mfma_scale_f32_16x16x128_f8f6f4: lane l supplies row l % 16 and 32
+        // contraction bytes, here the 16-byte chunks grp and grp + 4 of the
+        // row (the same for keys and queries), so one load instruction covers
+        // 64 contiguous bytes of each of 16 key rows.
+        const int grp = lane >> 4;
+        auto ld = [&](const T* row) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(row + 16 * grp);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(row + 64 + 16 * grp);
+            return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+        };
+        const i32x8 bq = c < RH ? ld(q_idx + ((size_t)b * RH + c) * DI) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        i32x8 a[8];   // eight 16-key tiles, all in flight
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a[t] = ld(kb + (size_t)(t * 16 + col) * DI);
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            // format code 0 (fp8 e4m3) for both operands; scale exponents 127 (= 2^0)
+            const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a[t], bq, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            m = vmax(m, vmax(vmax(acc[0], acc[1]), vmax(acc[2], acc[3])));
+        }
+        m = vmax(m, __shfl_xor(m, 16));
+        m = vmax(m, __shfl_xor(m, 32));
+        if (writer && c < RH) scores[((size_t)b * RH + c) * nbs + j] = m;
+        return;
+    } else if constexpr (COLS == 16) {
+        static_assert(sizeof(T) == 2, "16-column tiles are bf16 or fp8");
         constexpr int NS = DI / 32;   // 32-deep contraction slices
         const int grp = lane >> 4;    // contraction group of the lane
         Op8<T> bq[NS];
@@ -574,10 +602,11 @@ void launch_scores(const DecodeDims& d, const void* q_idx, const void* k_idx, co
     const int lmax = (d.C - 1) / kBlock;   // competing blocks of a full cache
     if (lmax == 0) return;
     const int RH = d.R * d.Hkv;
-    // bf16 with at most 16 columns: one 16-column set per sequence, each key
-    // block still read once. More columns take 32-column sets (a 16-column
-    // wave per set would read every block twice as often).
-    if constexpr (sizeof(T) == 2) {
+    // bf16 (or fp8 with Di = 128) with at most 16 columns: one 16-column set
+    // per sequence, each key block still read once. More columns take
+    // 32-column sets (a 16-column wave per set would read every block twice as
+    // often).
+    if constexpr (sizeof(T) == 2 || (sizeof(T) == 1 && DI == 128)) {
         if (RH <= 16) {
             hipLaunchKernelGGL((decode_scores_kernel<T, DI, 16>), dim3((lmax + 3) / 4, d.B), dim3(256), 0, st,
                                static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, pages, num_pages,
