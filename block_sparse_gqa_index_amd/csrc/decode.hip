@@ -16,8 +16,8 @@
 // by HBM bandwidth, so the kernels aim at full-line, many-in-flight loads and
 // use the matrix cores only to keep the VALU off the critical path:
 //   decode_scores_kernel  one wave per (sequence, competing block, 32 columns
-//                         of (new query, group) pairs; 16 when there are at
-//                         most 16, bf16 or fp8): S^T = K_idx Q_idx^T on
+//                         of (new query, group) pairs; one or two sets of 16
+//                         when there are at most 32, bf16 or fp8): S^T = K_idx Q_idx^T on
 //                         the matrix cores straight from global memory (no
 //                         LDS; the index keys are read once for all R queries),
 //                         block max in-lane plus one half-wave swap -> block
@@ -85,17 +85,19 @@ template <> struct DecMma<fp8_t> {    // v_mfma_scale_f32_32x32x64_f8f6f4: e4m3 
     }
 };
 
-// COLS columns per wave: 32 (32 x 32 tiles, any element type) or 16 (bf16:
-// v_mfma_f32_16x16x32_bf16 on 16-key tiles, lane l supplying row l % 16 and
-// the 8 contraction elements at 8 * (l / 16) of each 32-deep slice, so one
-// load instruction covers 64 contiguous bytes of each of 16 key rows).
-template <typename T, int DI, int COLS>
+// COLS columns per wave: 32 (32 x 32 tiles, any element type) or 16 x NCS
+// (bf16: v_mfma_f32_16x16x32_bf16 on 16-key tiles, lane l supplying row l % 16
+// and the 8 contraction elements at 8 * (l / 16) of each 32-deep slice, so one
+// load instruction covers 64 contiguous bytes of each of 16 key rows; each key
+// operand feeds the NCS column sets).
+template <typename T, int DI, int COLS, int NCS = 1>
 __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict__ q_idx,
                                                             const T* __restrict__ k_idx,
                                                             const int32_t* __restrict__ seqlens,
                                                             const int32_t* __restrict__ pages, int num_pages,
                                                             float* __restrict__ scores, int C, int Hkv,
                                                             int R, int nbs, int gchunks) {
+    static_assert(COLS == 16 || NCS == 1, "32-column waves take one column set");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane % COLS, half = lane >> 5;
     const int b = blockIdx.y / gchunks, gc = blockIdx.y % gchunks;
@@ -114,7 +116,9 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
     if (pages) {
         const int pg = pages[(size_t)b * nbs + j];
         if (pg < 0 || pg >= num_pages) {   // not a page of the pool: the block scores -inf, nothing is read
-            if (writer && c < RH) scores[((size_t)b * RH + c) * nbs + j] = -__builtin_inff();
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs)
+                if (writer && c + 16 * cs < RH) scores[((size_t)b * RH + c + 16 * cs) * nbs + j] = -__builtin_inff();
             return;
         }
         kb = k_idx + (size_t)pg * kBlock * DI;
@@ -132,34 +136,51 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
             const u32x4 y = *reinterpret_cast<const u32x4*>(row + 64 + 16 * grp);
             return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
         };
-        const i32x8 bq = c < RH ? ld(q_idx + ((size_t)b * RH + c) * DI) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        i32x8 bq[NCS];
+        float m[NCS];
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs) {
+            const int cc = c + 16 * cs;
+            bq[cs] = cc < RH ? ld(q_idx + ((size_t)b * RH + cc) * DI) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            m[cs] = -__builtin_inff();
+        }
         i32x8 a[8];   // eight 16-key tiles, all in flight
 #pragma unroll
         for (int t = 0; t < 8; ++t) a[t] = ld(kb + (size_t)(t * 16 + col) * DI);
-        float m = -__builtin_inff();
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            // format code 0 (fp8 e4m3) for both operands; scale exponents 127 (= 2^0)
-            const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                a[t], bq, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            m = vmax(m, vmax(vmax(acc[0], acc[1]), vmax(acc[2], acc[3])));
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                // format code 0 (fp8 e4m3) for both operands; scale exponents 127 (= 2^0)
+                const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    a[t], bq[cs], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                m[cs] = vmax(m[cs], vmax(vmax(acc[0], acc[1]), vmax(acc[2], acc[3])));
+            }
         }
-        m = vmax(m, __shfl_xor(m, 16));
-        m = vmax(m, __shfl_xor(m, 32));
-        if (writer && c < RH) scores[((size_t)b * RH + c) * nbs + j] = m;
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs) {
+            float x = vmax(m[cs], __shfl_xor(m[cs], 16));
+            x = vmax(x, __shfl_xor(x, 32));
+            if (writer && c + 16 * cs < RH) scores[((size_t)b * RH + c + 16 * cs) * nbs + j] = x;
+        }
         return;
     } else if constexpr (COLS == 16) {
         static_assert(sizeof(T) == 2, "16-column tiles are bf16 or fp8");
         constexpr int NS = DI / 32;   // 32-deep contraction slices
         const int grp = lane >> 4;    // contraction group of the lane
-        Op8<T> bq[NS];
-        const T* qrow = q_idx + ((size_t)b * RH + (c < RH ? c : 0)) * DI;   // q_idx [B, R, Hkv, Di]
+        Op8<T> bq[NCS][NS];
+        float m[NCS];
 #pragma unroll
-        for (int sl = 0; sl < NS; ++sl) {
-            if (c < RH) bq[sl].load(qrow + 32 * sl + 8 * grp);
-            else bq[sl].zero();
+        for (int cs = 0; cs < NCS; ++cs) {
+            const int cc = c + 16 * cs;
+            const T* qrow = q_idx + ((size_t)b * RH + (cc < RH ? cc : 0)) * DI;   // q_idx [B, R, Hkv, Di]
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                if (cc < RH) bq[cs][sl].load(qrow + 32 * sl + 8 * grp);
+                else bq[cs][sl].zero();
+            }
+            m[cs] = -__builtin_inff();
         }
-        float m = -__builtin_inff();
         // Eight 16-key tiles, four tiles' operands in flight.
 #pragma unroll
         for (int t0 = 0; t0 < 8; t0 += 4) {
@@ -172,17 +193,23 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const T* __restrict_
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int sl = 0; sl < NS; ++sl)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][sl].v, bq[sl].v, acc, 0, 0, 0);
-                m = vmax(m, vmax(vmax(acc[0], acc[1]), vmax(acc[2], acc[3])));
+                for (int cs = 0; cs < NCS; ++cs) {
+                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][sl].v, bq[cs][sl].v, acc, 0, 0, 0);
+                    m[cs] = vmax(m[cs], vmax(vmax(acc[0], acc[1]), vmax(acc[2], acc[3])));
+                }
             }
         }
         // Lanes l, l + 16, l + 32, l + 48 hold the four row quarters of column l % 16.
-        m = vmax(m, __shfl_xor(m, 16));
-        m = vmax(m, __shfl_xor(m, 32));
-        if (writer && c < RH) scores[((size_t)b * RH + c) * nbs + j] = m;
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs) {
+            float x = vmax(m[cs], __shfl_xor(m[cs], 16));
+            x = vmax(x, __shfl_xor(x, 32));
+            if (writer && c + 16 * cs < RH) scores[((size_t)b * RH + c + 16 * cs) * nbs + j] = x;
+        }
         return;
     }
 
@@ -602,13 +629,18 @@ void launch_scores(const DecodeDims& d, const void* q_idx, const void* k_idx, co
     const int lmax = (d.C - 1) / kBlock;   // competing blocks of a full cache
     if (lmax == 0) return;
     const int RH = d.R * d.Hkv;
-    // bf16 (or fp8 with Di = 128) with at most 16 columns: one 16-column set
-    // per sequence, each key block still read once. More columns take
-    // 32-column sets (a 16-column wave per set would read every block twice as
-    // often).
+    // bf16 (or fp8 with Di = 128) with at most 32 columns: one wave takes one
+    // or two 16-column sets, each key block read once per sequence. More
+    // columns take 32-column sets, one wave each.
     if constexpr (sizeof(T) == 2 || (sizeof(T) == 1 && DI == 128)) {
         if (RH <= 16) {
-            hipLaunchKernelGGL((decode_scores_kernel<T, DI, 16>), dim3((lmax + 3) / 4, d.B), dim3(256), 0, st,
+            hipLaunchKernelGGL((decode_scores_kernel<T, DI, 16, 1>), dim3((lmax + 3) / 4, d.B), dim3(256), 0, st,
+                               static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, pages, num_pages,
+                               scores, d.C, d.Hkv, d.R, d.nbs(), 1);
+            return;
+        }
+        if (RH <= 32) {
+            hipLaunchKernelGGL((decode_scores_kernel<T, DI, 16, 2>), dim3((lmax + 3) / 4, d.B), dim3(256), 0, st,
                                static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), seqlens, pages, num_pages,
                                scores, d.C, d.Hkv, d.R, d.nbs(), 1);
             return;

@@ -251,6 +251,36 @@ def test_decode_paged_fp8_index_and_bad_pages():
     assert torch.isfinite(lsep[0]).all() and bool(((bip[0] != 3) & (bip[0] != 5)).all())
 
 
+@pytest.mark.parametrize("R", [3, 4])
+def test_decode_two_column_sets(R):
+    """R * Hkv in (16, 32] (24 and 32 (query, group) columns): the block scores
+    run two 16-column sets per wave. bf16 and fp8 index caches against the
+    oracle, and paged caches with pages outside the pool."""
+    fp8 = torch.float8_e4m3fn
+    w = Workload(f"dec_cs2_r{R}", 4, 2000, 8, 2, 128, 128, topk=8)
+    lengths = [2000, 129, 2, 1999]
+    x = _dev(make_decode_inputs(w, device="cpu", lengths=lengths))
+    qi, q = _multi_queries(w, R, seed=17)
+    bi = msa.decode_index_topk(qi, x["k_idx"], x["seqlens"], w.topk)
+    bi8 = msa.decode_index_topk(qi.to(fp8), x["k_idx"].to(fp8), x["seqlens"], w.topk)
+    torch.cuda.synchronize()
+    want = O.decode_index_topk(qi.cpu(), x["k_idx"].cpu(), np.array(lengths), w.block_size, w.topk)
+    assert np.array_equal(bi.cpu().numpy(), want)
+    want8 = O.decode_index_topk(qi.to(fp8).cpu(), x["k_idx"].to(fp8).cpu(), np.array(lengths), w.block_size, w.topk)
+    assert np.array_equal(bi8.cpu().numpy(), want8)
+    pools, table, P = _to_pages(x, w)
+    bad = table.clone()
+    bad[0, 3] = -1
+    bad[0, 5] = P
+    for ki, bref in ((pools["k_idx"], bi), (pools["k_idx"].to(fp8), bi8)):
+        qq = qi if ki.dtype != fp8 else qi.to(fp8)
+        bp = msa.decode_paged_index_topk(qq, ki, table, x["seqlens"], w.topk)
+        bb = msa.decode_paged_index_topk(qq, ki, bad, x["seqlens"], w.topk)
+        torch.cuda.synchronize()
+        assert torch.equal(bp, bref) and torch.equal(bb[1:], bref[1:])
+        assert bool(((bb[0] != 3) & (bb[0] != 5)).all())
+
+
 def test_decode_1m_capacity():
     """Million-token caches (up to 8191 competing blocks: the top-k scans its
     scores in several chunks per lane), the 1M workload's model sizes."""
