@@ -7,11 +7,13 @@
 //
 // Query-block outer (flash-attention order): one work-group per (batch, query
 // block, group, part) of 256 rows (32-row tiles of 32/G positions x G heads of
-// the block's 128*G rows; bf16: 4 waves x 2 tiles), held for the whole sweep
-// over key blocks 0 .. qb. K_j and V_j^T (from the per-block transposed copy of V) sit
-// in LDS in the swizzled layout of the sparse kernels; the next block's K/V are
-// requested into registers before the current block's math and written to the
-// other LDS buffer after it, so one barrier per key block separates the two.
+// the block's 128*G rows; 8 waves x 1 tile, two waves per SIMD), held for the
+// whole sweep over key blocks 0 .. qb. K_j and V_j^T (from the per-block
+// transposed copy of V) sit in LDS in the swizzled layout of the sparse
+// kernels, in two buffers: the next block's K/V are copied into the other
+// buffer while the current block is computed (bf16: global -> LDS directly;
+// fp32: through registers, stored after the block's math), so one barrier per
+// key block separates the two.
 // Per block and tile: S^T = K Q^T, online softmax (log2 domain, running max
 // and sum per row, accumulator rescaled), O^T += V^T P^T. The local block
 // (j = qb) is masked causally; heavy (late) query blocks are launched first.
