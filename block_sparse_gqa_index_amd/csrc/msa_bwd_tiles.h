@@ -44,18 +44,22 @@ struct BwdItem {
 };
 
 // Per row: the sum of its slots' bf16 partials in slot order (dQ, with G heads
-// of D dims per row; the KL term's dq_idx, with G = 1 and D = Di). One thread
-// per (row, head, 16 stored elements = one (32-dim slice, half) of the
-// lane-major order).
+// of D dims per row; the KL term's dq_idx, with G = 1 and D = Di). A slot's
+// partial is G * D contiguous stored elements; thread t of a row sums the
+// 8-element groups t and t + TPR of it, so each of the wave's two load
+// instructions per slot reads whole cache lines (64 consecutive 16-byte
+// chunks or whole 128-byte halves of rows) and no line is split between them.
+// Stored element 16*qg + r of a head is dim 32*(qg/2) + 8*(r/4) + 4*(qg%2) + r%4
+// (the lane-major order of the partials).
 template <int D, int G>
 __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restrict__ dq_part, bf16_t* __restrict__ dq,
                                                          int64_t units, int N, int Hkv, int topk) {
-    constexpr int QPH = D / 16;   // 16-element groups per head
+    constexpr int SPAN = G * D;      // stored elements per (row, slot)
+    constexpr int TPR = SPAN / 16;   // threads per row
     const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (x >= units) return;
-    const int qg = (int)(x % QPH);
-    const int hh = (int)((x / QPH) % G);
-    const int64_t row = x / (QPH * G);   // (b * Hkv + g) * N + i
+    const int t = (int)(x % TPR);
+    const int64_t row = x / TPR;   // (b * Hkv + g) * N + i
     const int i = (int)(row % N);
     const int64_t bg = row / N;
     const int g = (int)(bg % Hkv), b = (int)(bg / Hkv);
@@ -63,10 +67,11 @@ __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restric
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const bf16_t* src = dq_part + (size_t)row * topk * G * D + (size_t)hh * D + 16 * qg;
+    const bf16_t* src = dq_part + (size_t)row * topk * SPAN;
     for (int s = 0; s < nv; ++s) {
-        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)s * G * D));
-        const u32x4 c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)s * G * D + 8));
+        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)s * SPAN + 8 * t));
+        const u32x4 c =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)s * SPAN + 8 * (t + TPR)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             acc[2 * e] += __uint_as_float(a[e] << 16);
@@ -75,15 +80,20 @@ __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restric
             acc[8 + 2 * e + 1] += __uint_as_float(c[e] & 0xffff0000u);
         }
     }
-    // stored element 16*qg + r of the head: slice dt = qg/2, half h = qg%2,
-    // dim 32*dt + 8*(r/4) + 4*h + r%4
-    const int dt = qg / 2, h = qg % 2;
     const int Hq = Hkv * G;
-    bf16_t* dst = dq + (((size_t)b * N + i) * Hq + g * G + hh) * D + 32 * dt + 4 * h;
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq)
-        *reinterpret_cast<uint2*>(dst + 8 * rq) = make_uint2(pack_bf16x2(acc[4 * rq], acc[4 * rq + 1]),
-                                                             pack_bf16x2(acc[4 * rq + 2], acc[4 * rq + 3]));
+    for (int part = 0; part < 2; ++part) {
+        const int e0 = 8 * (t + part * TPR);   // first stored element of the group in the slot's partial
+        const int hh = e0 / D, se = e0 % D;
+        const int qg = se / 16, r0 = se % 16;   // r0 = 0 or 8
+        bf16_t* dst = dq + (((size_t)b * N + i) * Hq + g * G + hh) * D + 32 * (qg / 2) + 4 * (qg % 2);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const float* v = acc + 8 * part + 4 * q2;
+            *reinterpret_cast<uint2*>(dst + 8 * (r0 / 4 + q2)) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+    }
 }
 
 }  // namespace msa
