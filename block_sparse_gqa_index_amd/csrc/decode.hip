@@ -29,8 +29,9 @@
 //                         rows, lane reads across them) of packed (score, -id)
 //                         keys; ids sorted ascending, the local block appended
 //   decode_attn_kernel    one work-group per (sequence, new query, group, kept
-//                         block): S^T = K Q^T per wave (32 keys each, K from
-//                         global), block softmax across the four waves through
+//                         block): S^T = K Q^T per wave (32 keys each; the K
+//                         block loaded as whole rows and staged in LDS, in the
+//                         rows V takes afterwards), block softmax across the four waves through
 //                         LDS, O^T = V^T P^T with V staged in LDS (P as a bf16
 //                         hi + lo pair: two products, exact to ~2^-17 of P);
 //                         a normalised fp32 partial output and its LSE per head
@@ -410,33 +411,47 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
     const T* kbase = kc + (first * Hkv + g) * D;
     const T* vbase = vc + (first * Hkv + g) * D;
 
-    // Requests in flight together: this wave's query and key operands, then the
-    // V block (rows past the last visible token zero-filled), which goes to LDS
-    // once the scores are on the matrix cores.
+    // Requests in flight together: the query operands, then the K and V blocks
+    // as whole rows (each load instruction covers 4 rows of the block; rows past
+    // the last visible token zero-filled). K goes to LDS first and is read back
+    // as this wave's operands; V then takes the same LDS rows.
     Op8<T> bq[D / 16];
     const int Hq = Hkv * G;
     load_q_op<T, D>(bq, q + ((size_t)blockIdx.z * Hq + (size_t)g * G + (col < G ? col : 0)) * D, col < G, half);
-    const int key = t0 + wave * 32 + col;
-    Op8<T> a[D / 16];
-#pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) {
-        if (key <= t_last) a[sl].load(kbase + (size_t)(key - t0) * kv_row + 16 * sl + 8 * half);
-        else a[sl].zero();
-    }
     constexpr int EPC = 16 / LD::ES;
     constexpr int CPR = D / EPC;
     constexpr int VPER = kBlock * CPR / 256;
-    static_assert(kBlock * CPR % 256 == 0, "V chunk split");
-    u32x4 vr[VPER];
+    static_assert(kBlock * CPR % 256 == 0, "K/V chunk split");
+    u32x4 kr[VPER], vr[VPER];
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+        const int ch = threadIdx.x + u * 256, row = ch / CPR, cc = ch % CPR;
+        kr[u] = t0 + row <= t_last ? *reinterpret_cast<const u32x4*>(kbase + (size_t)row * kv_row + cc * EPC)
+                                   : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int u = 0; u < VPER; ++u) {
         const int ch = threadIdx.x + u * 256, row = ch / CPR, cc = ch % CPR;
         vr[u] = t0 + row <= t_last ? *reinterpret_cast<const u32x4*>(vbase + (size_t)row * kv_row + cc * EPC)
                                    : u32x4{0u, 0u, 0u, 0u};
     }
-    floatx16 s = zero16();
 #pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) mma16(s, a[sl], bq[sl]);
+    for (int u = 0; u < VPER; ++u) {
+        const int ch = threadIdx.x + u * 256, row = ch / CPR, cc = ch % CPR;
+        *reinterpret_cast<u32x4*>(vs + row * LD::VROW + cc * 16) = kr[u];
+    }
+    __syncthreads();
+    floatx16 s = zero16();
+    {
+        const unsigned char* krow = vs + (wave * 32 + col) * LD::VROW;
+#pragma unroll
+        for (int sl = 0; sl < D / 16; ++sl) {
+            Op8<T> a;
+            a.load(krow + (16 * sl + 8 * half) * LD::ES);
+            mma16(s, a, bq[sl]);
+        }
+    }
+    __syncthreads();   // every wave has read its key operands: V takes the rows
 #pragma unroll
     for (int u = 0; u < VPER; ++u) {
         const int ch = threadIdx.x + u * 256, row = ch / CPR, cc = ch % CPR;
