@@ -143,22 +143,38 @@ def _stream(device):
 def _workspace(nbytes, device, ws):
     if nbytes == 0:
         return None, 0
+    if ws is not None:
+        _req(ws, "workspace", device=device)
     if ws is None or ws.numel() * ws.element_size() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 
-def _req(t, name, dtype=None, ndim=None):
+def _on_gpu(t):
+    """Whether t lives in device memory (its own function so that host-only
+    tests can stand in for it and reach the shape checks)."""
+    return t.is_cuda
+
+
+def _req(t, name, dtype=None, ndim=None, shape=None, device=None):
+    """Checks a tensor argument before anything is enqueued: type, dtype, rank,
+    exact shape, contiguity, device memory and (if given) the device the call
+    runs on. An output the kernels write must pass `shape`, so that a short
+    buffer is refused here instead of being written past its end."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not _on_gpu(t):
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
 def index_topk(q_idx, k_idx, topk, block_idx=None, block_size=128):
@@ -170,9 +186,10 @@ def index_topk(q_idx, k_idx, topk, block_idx=None, block_size=128):
     B, N, Hkv, Di = q_idx.shape
     if tuple(k_idx.shape) != (B, N, Di):
         raise ValueError(f"k_idx shape {tuple(k_idx.shape)} != {(B, N, Di)}")
+    _req(k_idx, "k_idx", device=q_idx.device)
     if block_idx is None:
         block_idx = torch.empty((B, Hkv, N, topk), dtype=torch.int32, device=q_idx.device)
-    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
+    _req(block_idx, "block_idx", dtype=torch.int32, shape=(B, Hkv, N, topk), device=q_idx.device)
     dims = make_dims(B, N, Hkv, 1, 64, Di, topk, q_idx.dtype, block_size)
     _check(lib.msa_index_topk(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
                               None, 0, _stream(q_idx.device)))
@@ -187,7 +204,7 @@ def check_block_idx(block_idx, bad_rows=None, block_size=128):
     B, Hkv, N, topk = block_idx.shape
     if bad_rows is None:
         bad_rows = torch.empty((1,), dtype=torch.int32, device=block_idx.device)
-    _req(bad_rows, "bad_rows", dtype=torch.int32)
+    _req(bad_rows, "bad_rows", dtype=torch.int32, shape=(1,), device=block_idx.device)
     dims = make_dims(B, N, Hkv, 1, 64, 64, topk, MSA_BF16, block_size)
     _check(lib.msa_check_block_idx(ctypes.byref(dims), _ptr(block_idx), _ptr(bad_rows), _stream(block_idx.device)))
     return bad_rows
@@ -211,13 +228,15 @@ def sparse_attn_fwd(q, k, v, block_idx, softmax_scale=0.0, o=None, lse=None, wor
     topk = block_idx.shape[3]
     if tuple(block_idx.shape) != (B, Hkv, N, topk):
         raise ValueError("block_idx must be [B, Hkv, N, topk]")
+    for name, t in (("k", k), ("v", v), ("block_idx", block_idx)):
+        _req(t, name, device=q.device)
     dims = make_dims(B, N, Hkv, Hq // Hkv, D, 64, topk, q.dtype, block_size)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    _req(o, "o", dtype=q.dtype, ndim=4)
-    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    _req(o, "o", dtype=q.dtype, shape=q.shape, device=q.device)
+    _req(lse, "lse", dtype=torch.float32, shape=(B, Hq, N), device=q.device)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_ATTN), q.device, workspace)
     if stages == STAGE_ALL:
         _check(lib.msa_sparse_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
@@ -251,19 +270,33 @@ def sparse_attn_bwd(q, k, v, block_idx, o, lse, dout, softmax_scale=0.0, dq=None
     topk = block_idx.shape[3]
     if tuple(block_idx.shape) != (B, Hkv, N, topk):
         raise ValueError("block_idx must be [B, Hkv, N, topk]")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("block_idx", block_idx), ("lse", lse)):
+        _req(t, name, device=q.device)
     dims = make_dims(B, N, Hkv, Hq // Hkv, D, 64, topk, q.dtype, block_size)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        _req(t, name, dtype=q.dtype, ndim=4)
-        if t.shape != ref.shape:
-            raise ValueError(f"{name} must have the shape of {name[1:]}")
+        _req(t, name, dtype=q.dtype, shape=ref.shape, device=q.device)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_ATTN_BWD), q.device, workspace)
     _check(lib.msa_sparse_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(o),
                                    _ptr(lse), _ptr(dout), float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
                                    _ptr(ws), nws, _stream(q.device)))
     return dq, dk, dv
+
+
+def _kl_input_shapes(q, k, q_idx, k_idx, lse, block_idx):
+    """Shapes and device of the KL calls' inputs (q [B,N,Hq,D] sets B, N, Hq, D;
+    q_idx [., ., Hkv, Di] sets Hkv and Di; block_idx sets topk)."""
+    B, N, Hq, D = q.shape
+    Hkv, Di = q_idx.shape[2], q_idx.shape[3]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    _req(k, "k", shape=(B, N, Hkv, D), device=q.device)
+    _req(q_idx, "q_idx", shape=(B, N, Hkv, Di), device=q.device)
+    _req(k_idx, "k_idx", shape=(B, N, Di), device=q.device)
+    _req(lse, "lse", shape=(B, Hq, N), device=q.device)
+    _req(block_idx, "block_idx", shape=(B, Hkv, N, block_idx.shape[3]), device=q.device)
 
 
 def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_scale=0.0,
@@ -281,15 +314,16 @@ def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_sc
     B, N, Hq, D = q.shape
     Hkv, Di = q_idx.shape[2], q_idx.shape[3]
     topk = block_idx.shape[3]
+    _kl_input_shapes(q, k, q_idx, k_idx, lse, block_idx)
     dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
     if kl_rows is None:
         kl_rows = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
     if kl_sum is None:
         kl_sum = torch.empty((1,), dtype=torch.float32, device=q.device)
+    _req(kl_rows, "kl_rows", dtype=torch.float32, shape=(B, Hkv, N), device=q.device)
+    _req(kl_sum, "kl_sum", dtype=torch.float32, shape=(1,), device=q.device)
     if index_lse is not None:
-        _req(index_lse, "index_lse", dtype=torch.float32, ndim=3)
-        if tuple(index_lse.shape) != (B, Hkv, N):
-            raise ValueError("index_lse must be [B, Hkv, N]")
+        _req(index_lse, "index_lse", dtype=torch.float32, shape=(B, Hkv, N), device=q.device)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_KL), q.device, workspace)
     _check(lib.msa_kl_align_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
                                 _ptr(block_idx), _ptr(lse), float(softmax_scale), float(index_scale),
@@ -314,15 +348,15 @@ def kl_align_bwd(q, k, q_idx, k_idx, block_idx, lse, index_lse, softmax_scale=0.
     B, N, Hq, D = q.shape
     Hkv, Di = q_idx.shape[2], q_idx.shape[3]
     topk = block_idx.shape[3]
-    if tuple(index_lse.shape) != (B, Hkv, N) or (dkl_rows is not None and tuple(dkl_rows.shape) != (B, Hkv, N)):
-        raise ValueError("index_lse and dkl_rows must be [B, Hkv, N]")
+    _kl_input_shapes(q, k, q_idx, k_idx, lse, block_idx)
+    _req(index_lse, "index_lse", shape=(B, Hkv, N), device=q.device)
     if dkl_rows is not None:
-        _req(dkl_rows, "dkl_rows", dtype=torch.float32, ndim=3)
+        _req(dkl_rows, "dkl_rows", dtype=torch.float32, shape=(B, Hkv, N), device=q.device)
     dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
     dq_idx = torch.empty_like(q_idx) if dq_idx is None else dq_idx
     dk_idx = torch.empty_like(k_idx) if dk_idx is None else dk_idx
-    _req(dq_idx, "dq_idx", dtype=q.dtype, ndim=4)
-    _req(dk_idx, "dk_idx", dtype=q.dtype, ndim=3)
+    _req(dq_idx, "dq_idx", dtype=q.dtype, shape=q_idx.shape, device=q.device)
+    _req(dk_idx, "dk_idx", dtype=q.dtype, shape=k_idx.shape, device=q.device)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_KL_BWD), q.device, workspace)
     _check(lib.msa_kl_align_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
                                 _ptr(lse), _ptr(index_lse), float(softmax_scale), float(index_scale),
@@ -353,9 +387,11 @@ def forward(q_idx, k_idx, q, k, v, topk, softmax_scale=0.0, block_idx=None, o=No
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    _req(block_idx, "block_idx", dtype=torch.int32, ndim=4)
-    _req(o, "o", dtype=q.dtype, ndim=4)
-    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    for name, t in (("q_idx", q_idx), ("k_idx", k_idx), ("k", k), ("v", v)):
+        _req(t, name, device=q.device)
+    _req(block_idx, "block_idx", dtype=torch.int32, shape=(B, Hkv, N, topk), device=q.device)
+    _req(o, "o", dtype=q.dtype, shape=q.shape, device=q.device)
+    _req(lse, "lse", dtype=torch.float32, shape=(B, Hq, N), device=q.device)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_FORWARD), q.device, workspace)
     _check(lib.msa_forward(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
                            float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws,
@@ -386,12 +422,20 @@ def _decode_outputs(B, R, multi, Hkv, Hq, D, topk, like, block_idx, o, lse, want
     return block_idx, o, lse
 
 
-def _check_sel(block_idx, B, Hkv, R, multi):
+def _check_sel(block_idx, B, Hkv, R, multi, device, topk=None):
+    """block_idx of a decode call: [B, Hkv, (R,) topk] int32 on `device`
+    (topk = the call's argument when it has one, else the tensor's last
+    dimension). Returns topk."""
     _req(block_idx, "block_idx", dtype=torch.int32)
     want = (B, Hkv, R) if multi else (B, Hkv)
-    if tuple(block_idx.shape[:-1]) != want:
-        raise ValueError(f"block_idx must be {want + ('topk',)}")
-    return block_idx.shape[-1]
+    k = block_idx.shape[-1] if topk is None else int(topk)
+    _req(block_idx, "block_idx", shape=want + (k,), device=device)
+    return k
+
+
+def _check_decode_out(o, lse, B, R, multi, Hq, D, dtype, device):
+    _req(o, "o", dtype=dtype, shape=(B, R, Hq, D) if multi else (B, Hq, D), device=device)
+    _req(lse, "lse", dtype=torch.float32, shape=(B, Hq, R) if multi else (B, Hq), device=device)
 
 
 def decode_workspace_bytes(dims: MsaDims, op: int, num_queries: int = 1) -> int:
@@ -412,8 +456,10 @@ def decode_index_topk(q_idx, k_idx, seqlens, topk, block_idx=None, workspace=Non
     Hkv = q_idx.shape[-2]
     if q_idx.shape[0] != B or q_idx.shape[-1] != Di or seqlens.shape[0] != B:
         raise ValueError("q_idx must be [B, (R,) Hkv, Di], k_idx [B, C, Di], seqlens [B]")
+    for name, t in (("k_idx", k_idx), ("seqlens", seqlens)):
+        _req(t, name, device=q_idx.device)
     block_idx, _, _ = _decode_outputs(B, R, multi, Hkv, 0, 0, topk, q_idx, block_idx, None, None, want_attn=False)
-    _check_sel(block_idx, B, Hkv, R, multi)
+    _check_sel(block_idx, B, Hkv, R, multi, q_idx.device, topk)
     dims = make_dims(B, C, Hkv, 1, 64, Di, topk, q_idx.dtype, block_size)
     ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_INDEX, R), q_idx.device, workspace)
     _check(lib.msa_decode_index_topk(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx), _ptr(seqlens),
@@ -436,8 +482,11 @@ def decode_attn(q, k, v, seqlens, block_idx, softmax_scale=0.0, o=None, lse=None
     if (tuple(v.shape) != tuple(k.shape) or q.shape[0] != B or q.shape[-1] != D or Hq % Hkv
             or seqlens.shape[0] != B):
         raise ValueError("q must be [B, (R,) Hq, D] with Hq a multiple of Hkv; k, v [B, C, Hkv, D]")
-    topk = _check_sel(block_idx, B, Hkv, R, multi)
+    for name, t in (("k", k), ("v", v), ("seqlens", seqlens)):
+        _req(t, name, device=q.device)
+    topk = _check_sel(block_idx, B, Hkv, R, multi, q.device)
     _, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, None, o, lse, want_sel=False)
+    _check_decode_out(o, lse, B, R, multi, Hq, D, q.dtype, q.device)
     dims = make_dims(B, C, Hkv, Hq // Hkv, D, 64, topk, q.dtype, block_size)
     ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_ATTN, R), q.device, workspace)
     _check(lib.msa_decode_attn(ctypes.byref(dims), R, _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(block_idx),
@@ -463,8 +512,13 @@ def decode(q_idx, k_idx, q, k, v, seqlens, topk, softmax_scale=0.0, block_idx=No
     if (tuple(k_idx.shape[:2]) != (B, C) or tuple(v.shape) != tuple(k.shape) or q_idx.shape[-2:] != (Hkv, Di)
             or q.shape[-1] != D or Hq % Hkv or seqlens.shape[0] != B):
         raise ValueError("inconsistent shapes")
+    if q_idx.shape[0] != B or q.shape[0] != B:
+        raise ValueError("q_idx and q must have the caches' batch")
+    for name, t in (("q_idx", q_idx), ("k_idx", k_idx), ("k", k), ("v", v), ("seqlens", seqlens)):
+        _req(t, name, device=q.device)
     block_idx, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, block_idx, o, lse)
-    _check_sel(block_idx, B, Hkv, R, multi)
+    _check_sel(block_idx, B, Hkv, R, multi, q.device, topk)
+    _check_decode_out(o, lse, B, R, multi, Hq, D, q.dtype, q.device)
     dims = make_dims(B, C, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
     ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE, R), q.device, workspace)
     _check(lib.msa_decode(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
@@ -484,13 +538,15 @@ def dense_attn_fwd(q, k, v, softmax_scale=0.0, o=None, lse=None, workspace=None,
     Hkv = k.shape[2]
     if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D) or Hq % Hkv:
         raise ValueError("k/v must be [B, N, Hkv, D] with Hq a multiple of Hkv")
+    for name, t in (("k", k), ("v", v)):
+        _req(t, name, device=q.device)
     dims = make_dims(B, N, Hkv, Hq // Hkv, D, 64, 1, q.dtype, block_size)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    _req(o, "o", dtype=q.dtype, ndim=4)
-    _req(lse, "lse", dtype=torch.float32, ndim=3)
+    _req(o, "o", dtype=q.dtype, shape=q.shape, device=q.device)
+    _req(lse, "lse", dtype=torch.float32, shape=(B, Hq, N), device=q.device)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DENSE_ATTN), q.device, workspace)
     _check(lib.msa_dense_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), float(softmax_scale), _ptr(o),
                                   _ptr(lse), _ptr(ws), nws, _stream(q.device)))
@@ -512,11 +568,19 @@ def dense_kl_align_fwd(q, k, q_idx, k_idx, lse, softmax_scale=0.0, index_scale=0
     if (tuple(k.shape) != (B, N, Hkv, D) or tuple(k_idx.shape) != (B, N, Di) or tuple(lse.shape) != (B, Hq, N)
             or Hq % Hkv):
         raise ValueError("inconsistent shapes")
+    for name, t in (("k", k), ("q_idx", q_idx), ("k_idx", k_idx), ("lse", lse)):
+        _req(t, name, device=q.device)
+    if tuple(q_idx.shape[:2]) != (B, N):
+        raise ValueError("q_idx must be [B, N, Hkv, Di]")
     dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, 1, q.dtype, block_size)
     if kl_rows is None:
         kl_rows = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
     if kl_sum is None:
         kl_sum = torch.empty((1,), dtype=torch.float32, device=q.device)
+    _req(kl_rows, "kl_rows", dtype=torch.float32, shape=(B, Hkv, N), device=q.device)
+    _req(kl_sum, "kl_sum", dtype=torch.float32, shape=(1,), device=q.device)
+    if index_lse is not None:
+        _req(index_lse, "index_lse", dtype=torch.float32, shape=(B, Hkv, N), device=q.device)
     ws, nws = _workspace(workspace_bytes(dims, MSA_OP_DENSE_KL), q.device, workspace)
     _check(lib.msa_dense_kl_align_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(lse),
                                       float(softmax_scale), float(index_scale), _ptr(kl_rows), _ptr(kl_sum),
@@ -556,8 +620,10 @@ def decode_paged_index_topk(q_idx, k_idx_pages, block_table, seqlens, topk, bloc
     Hkv, Di = q_idx.shape[-2], q_idx.shape[-1]
     if q_idx.dtype != k_idx_pages.dtype or q_idx.shape[0] != B or k_idx_pages.shape[2] != Di:
         raise ValueError("q_idx must be [B, (R,) Hkv, Di] in the pool's dtype")
+    for name, t in (("k_idx_pages", k_idx_pages), ("block_table", block_table), ("seqlens", seqlens)):
+        _req(t, name, device=q_idx.device)
     block_idx, _, _ = _decode_outputs(B, R, multi, Hkv, 0, 0, topk, q_idx, block_idx, None, None, want_attn=False)
-    _check_sel(block_idx, B, Hkv, R, multi)
+    _check_sel(block_idx, B, Hkv, R, multi, q_idx.device, topk)
     dims = make_dims(B, C, Hkv, 1, 64, Di, topk, q_idx.dtype)
     ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_INDEX, R), q_idx.device, workspace)
     _check(lib.msa_decode_paged_index_topk(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx_pages), _ptr(block_table),
@@ -575,8 +641,11 @@ def decode_paged_attn(q, k_pages, v_pages, block_table, seqlens, block_idx, soft
     Hq = q.shape[-2]
     if q.dtype != k_pages.dtype or q.shape[0] != B or q.shape[-1] != D or Hq % Hkv:
         raise ValueError("q must be [B, (R,) Hq, D] with Hq a multiple of Hkv")
-    topk = _check_sel(block_idx, B, Hkv, R, multi)
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table), ("seqlens", seqlens)):
+        _req(t, name, device=q.device)
+    topk = _check_sel(block_idx, B, Hkv, R, multi, q.device)
     _, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, None, o, lse, want_sel=False)
+    _check_decode_out(o, lse, B, R, multi, Hq, D, q.dtype, q.device)
     dims = make_dims(B, C, Hkv, Hq // Hkv, D, 64, topk, q.dtype)
     ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE_ATTN, R), q.device, workspace)
     _check(lib.msa_decode_paged_attn(ctypes.byref(dims), R, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
@@ -598,8 +667,14 @@ def decode_paged(q_idx, k_idx_pages, q, k_pages, v_pages, block_table, seqlens, 
     Hq = q.shape[-2]
     if k_pages.shape[2] != Hkv or Hq % Hkv or q.shape[-1] != D:
         raise ValueError("inconsistent shapes")
+    if q_idx.shape[0] != B or q.shape[0] != B or k_idx_pages.shape[2] != Di:
+        raise ValueError("q_idx and q must have the block table's batch, k_idx_pages the index dim of q_idx")
+    for name, t in (("q_idx", q_idx), ("k_idx_pages", k_idx_pages), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("block_table", block_table), ("seqlens", seqlens)):
+        _req(t, name, device=q.device)
     block_idx, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, block_idx, o, lse)
-    _check_sel(block_idx, B, Hkv, R, multi)
+    _check_sel(block_idx, B, Hkv, R, multi, q.device, topk)
+    _check_decode_out(o, lse, B, R, multi, Hq, D, q.dtype, q.device)
     dims = make_dims(B, C, Hkv, Hq // Hkv, D, Di, topk, q.dtype)
     ws, nws = _workspace(decode_workspace_bytes(dims, MSA_OP_DECODE, R), q.device, workspace)
     _check(lib.msa_decode_paged(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx_pages), _ptr(q), _ptr(k_pages),

@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256) void dki_reduce_kernel(const float* __restrict
         add(local_base + (size_t)bg * nb + j);
         if (has_lists) {
             for (int win = 0; win < nwin; ++win) {
-                const int key = (bg * nwin + win) * nb + j;
+                const size_t key = ((size_t)bg * nwin + win) * nb + j;
                 const int n = (counts[key] + seg - 1) / seg;
                 const int first = item_offsets[key];
                 for (int v = 0; v < n; ++v) add((size_t)first + v);

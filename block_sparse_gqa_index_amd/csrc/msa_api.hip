@@ -53,6 +53,10 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     const int64_t rows = d->batch * d->seqlen * d->kv_heads;
     if (!decode && (d->batch > INT_MAX || rows > INT_MAX || rows * (int64_t)(uses_topk ? d->topk : 1) > INT_MAX))
         return MSA_ERR_SHAPE;
+    // Work items of the inverted selection carry a 32-bit key per (batch,
+    // group, query window, key block).
+    const int64_t nb64 = (d->seqlen + 127) / 128, nwin64 = (d->seqlen + msa::kWindow - 1) / msa::kWindow;
+    if (!decode && d->batch * d->kv_heads * nwin64 * nb64 > INT_MAX) return MSA_ERR_SHAPE;
     out->B = (int)d->batch;
     out->N = (int)d->seqlen;
     out->Hkv = d->kv_heads;
