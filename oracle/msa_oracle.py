@@ -60,18 +60,35 @@ __all__ = [
     "local_block", "visible_block_scores", "select_blocks", "index_topk_rows",
     "index_topk", "token_set", "token_count", "attention_rows", "sparse_attention",
     "kl_rows", "kl_align", "attention_backward", "attention_dq_rows", "kl_backward", "kl_dq_idx_rows",
-    "map_positions", "decode_index_topk", "decode_attention", "dense_block_idx_rows",
+    "map_positions", "decode_index_topk", "decode_attention", "dense_block_idx_rows", "fp4_e2m1_values",
 ]
+
+
+def fp4_e2m1_values(packed):
+    """Values of OCP MX fp4 e2m1 data stored two to a byte (element 2c in bits
+    0-3 of byte c, element 2c+1 in bits 4-7), as float32 with the last axis
+    doubled. Per the format: bit 3 is the sign, bits 2-1 the exponent E (bias
+    1), bit 0 the mantissa M; E = 0 encodes the subnormals 0 and 0.5 (M / 2),
+    E > 0 the normals 2^(E-1) (1 + M/2). [P2] "El codiseño del kernel": the
+    open kernel runs in FP4 among other precisions."""
+    b = np.asarray(packed, dtype=np.uint8)
+    codes = np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    e = ((codes >> 1) & 3).astype(np.float64)
+    m = (codes & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, 2.0 ** (e - 1) * (1.0 + 0.5 * m))
+    return np.where(codes & 8, -mag, mag).astype(np.float32)
 
 
 def _arr(x):
     """Tensor or array -> numpy array without a copy where possible (bf16, fp16
-    and fp8 tensors widen exactly to float32; everything is cast to float64
-    where it is used)."""
+    and fp8 tensors widen exactly to float32, packed fp4 tensors are decoded
+    exactly to float32; everything is cast to float64 where it is used)."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
             x = x.detach().to("cpu")
+            if x.dtype == getattr(torch, "float4_e2m1fn_x2", None):
+                return fp4_e2m1_values(x.view(torch.uint8).numpy())
             if x.dtype.is_floating_point and x.element_size() < 4:
                 x = x.float()   # bf16, fp16 and fp8 widen exactly to float32
             return x.numpy()
@@ -282,7 +299,7 @@ def _row_backward(qh, kt, vt, doh, scale):
     return scale * (dz @ kt), scale * (dz.T @ qh), dv
 
 
-def attention_backward(q, k, v, do, block_idx, Bk, scale=None):
+def attention_backward(q, k, v, do, block_idx, Bk, scale=None, row_range=None):
     """Gradients of the main branch for every position: (dQ [B,N,Hq,D],
     dK [B,N,Hkv,D], dV [B,N,Hkv,D]) in float64, for the loss <dO, O>.
 
@@ -290,6 +307,8 @@ def attention_backward(q, k, v, do, block_idx, Bk, scale=None):
     forward, the backward runs over the same sparse blocks (linear in N). The
     function differentiated is the forward of ``attention_rows``; a key's
     gradient sums the contributions of every row that selected its block.
+    ``row_range`` = (i0, i1) keeps only the rows i0 <= i < i1 in that sum (and
+    in dQ): the results of disjoint ranges covering [0, N) add up to the whole.
     """
     qq, kk, vv, dd = _arr(q), _arr(k), _arr(v), _arr(do)
     B, N, Hq, D = qq.shape
@@ -309,7 +328,7 @@ def attention_backward(q, k, v, do, block_idx, Bk, scale=None):
             dg = np.asarray(dd[b, :, hs], dtype=np.float64)
             dKg = np.zeros((N, D))
             dVg = np.zeros((N, D))
-            for i in range(N):
+            for i in range(*(row_range or (0, N))):
                 T = token_set(bi[b, g, i], i, Bk)
                 dq, dk, dv = _row_backward(qg[i], kg[T], vg[T], dg[i], scale)
                 dQ[b, i, hs] = dq
@@ -427,7 +446,7 @@ def _kl_row_backward(qh, kt, qi, kit, scale, index_scale):
     return du @ kit, np.outer(du, qi)
 
 
-def kl_backward(q, k, q_idx, k_idx, block_idx, Bk, dkl_rows=None, scale=None, index_scale=None):
+def kl_backward(q, k, q_idx, k_idx, block_idx, Bk, dkl_rows=None, scale=None, index_scale=None, row_range=None):
     """Gradients of L = sum over rows of dkl_rows[b, g, i] * KL_row (dkl_rows = 1
     everywhere: L = kl_sum) w.r.t. q_idx and k_idx: (dq_idx [B,N,Hkv,Di],
     dk_idx [B,N,Di]) in float64.
@@ -438,6 +457,8 @@ def kl_backward(q, k, q_idx, k_idx, block_idx, Bk, dkl_rows=None, scale=None, in
     the teacher (main-branch probabilities) is a constant here. [P1] paragraph
     on the backward: the proxy gradient comes from the cached block indices.
     k_idx is shared by the groups, so its gradient sums over every group's rows.
+    ``row_range`` = (i0, i1) keeps only the rows i0 <= i < i1, as in
+    ``attention_backward``.
     """
     qq, kk, qi, ki = _arr(q), _arr(k), _arr(q_idx), _arr(k_idx)
     B, N, Hq, D = qq.shape
@@ -456,7 +477,7 @@ def kl_backward(q, k, q_idx, k_idx, block_idx, Bk, dkl_rows=None, scale=None, in
             kg = np.asarray(kk[b, :, g], dtype=np.float64)
             qg = np.asarray(qq[b, :, g * G:(g + 1) * G], dtype=np.float64)
             qig = np.asarray(qi[b, :, g], dtype=np.float64)
-            for i in range(N):
+            for i in range(*(row_range or (0, N))):
                 T = token_set(bi[b, g, i], i, Bk)
                 a, c = _kl_row_backward(qg[i], kg[T], qig[i], kib[T], scale, index_scale)
                 dqi[b, i, g] = w[b, g, i] * a

@@ -62,13 +62,20 @@ def compare(name, got, want):
 _JOB = None
 
 
-def _group_job(bg):
+def _group_job(job):
+    bg, rows = job
     q, k, v, dout, bi, w = _JOB
     b, g = divmod(bg, w.kv_heads)
     G = w.group_size
     hs = slice(g * G, (g + 1) * G)
     return O.attention_backward(q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1],
-                                dout[b:b + 1, :, hs], bi[b:b + 1, g:g + 1], w.block_size)
+                                dout[b:b + 1, :, hs], bi[b:b + 1, g:g + 1], w.block_size, row_range=rows)
+
+
+def row_chunks(N, parts):
+    """Contiguous row ranges covering [0, N): the oracle's results over them add up."""
+    step = -(-N // parts)
+    return [(i, min(N, i + step)) for i in range(0, N, step)]
 
 
 def _one_thread():
@@ -85,20 +92,23 @@ def oracle_backward_by_group(host, dout, bi, w):
     global _JOB
     _JOB = tuple(t.float().numpy() for t in (host["q"], host["k"], host["v"], dout)) + (bi, w)
     n = w.batch * w.kv_heads
-    if n == 1 or WORKERS == 1:
-        parts = [_group_job(x) for x in range(n)]
+    # long sequences: every (batch, group) split into row ranges as well
+    chunks = max(1, WORKERS // n) if w.seqlen >= 16384 else 1
+    jobs = [(bg, rows) for bg in range(n) for rows in row_chunks(w.seqlen, chunks)]
+    if len(jobs) == 1 or WORKERS == 1:
+        parts = [_group_job(j) for j in jobs]
     else:
-        with mp.get_context("fork").Pool(min(WORKERS, n), initializer=_one_thread) as pool:
-            parts = pool.map(_group_job, range(n))
+        with mp.get_context("fork").Pool(min(WORKERS, len(jobs)), initializer=_one_thread) as pool:
+            parts = pool.map(_group_job, jobs)
     B, N, G, D = w.batch, w.seqlen, w.group_size, w.head_dim
     dq = np.zeros((B, N, w.q_heads, D))
     dk = np.zeros((B, N, w.kv_heads, D))
     dv = np.zeros((B, N, w.kv_heads, D))
-    for x, (a, c, e) in enumerate(parts):
-        b, g = divmod(x, w.kv_heads)
-        dq[b, :, g * G:(g + 1) * G] = a[0]
-        dk[b, :, g] = c[0, :, 0]
-        dv[b, :, g] = e[0, :, 0]
+    for (bg, _), (a, c, e) in zip(jobs, parts):
+        b, g = divmod(bg, w.kv_heads)
+        dq[b, :, g * G:(g + 1) * G] += a[0]
+        dk[b, :, g] += c[0, :, 0]
+        dv[b, :, g] += e[0, :, 0]
     return dq, dk, dv
 
 
@@ -137,6 +147,16 @@ def test_backward_every_element(w):
 
 def test_backward_n8k_every_element():
     check_every_element(CONFIGS["n8k"], on_gpu_rng=True)
+
+
+# Query positions past 65,536 fall in a second window of the inverted
+# selection, so a key block's dK/dV sums the items of both windows (and the
+# block's own causal rows); the last block is partial.
+TWO_WINDOWS = Workload("two_windows", 1, 65536 + 300, 2, 8, 128, 128, topk=8)
+
+
+def test_backward_two_windows_every_element():
+    check_every_element(TWO_WINDOWS, on_gpu_rng=True)
 
 
 def test_backward_n128k_sampled_rows_and_sum_rule():

@@ -100,10 +100,12 @@ def _check_kl(w, x, kl, kl_sum, pos, full_sum=False):
         lambda c, br, qr, qir: O.kl_rows(None, kh, None, kih, br, c, w.block_size, q_rows=qr, qi_rows=qir),
         pos, (rows, x["q"][b, i].cpu(), x["q_idx"][b, i].cpu()), workers=16)          # [M, Hkv]
     got = kl.permute(0, 2, 1)[b, i].cpu().numpy()
-    err = float(np.abs(got - want).max())
-    tol = 1e-3 + 1e-3 * float(np.abs(want).max())
-    log(f"  {w.name}: dense KL on {len(pos)} rows, max|dKL|={err:.2e} (tol {tol:.2e})")
-    assert err <= tol
+    err = np.abs(got - want)
+    tol = 1e-3 + 1e-3 * np.abs(want)          # per row, as the sparse KL's bar
+    worst = float((err / tol).max())
+    log(f"  {w.name}: dense KL on {len(pos)} rows, max|dKL|={float(err.max()):.2e}, "
+        f"worst error / per-row tolerance = {worst:.3f}")
+    assert worst <= 1.0
     if full_sum:
         assert abs(float(kl_sum.item()) - float(want.sum())) <= 1e-3 * abs(float(want.sum())) + 1e-3
 
@@ -145,3 +147,17 @@ def test_dense_kl_n32k_sampled():
     kl, kl_sum = msa.dense_kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], lse)
     torch.cuda.synchronize()
     _check_kl(w, x, kl, kl_sum, sample_rows(w, n=128, seed=1))
+
+
+def test_dense_kl_n128k_sampled():
+    """The dense KL at the 128K shapes the benchmark times (B 1, N 131072,
+    Hkv 8, G 8, D = Di = 128), on seeded sampled rows plus the sequence's
+    last row."""
+    w = Workload("dkl_n128k", 1, 131072, 8, 8, 128, 128)
+    log(f"{w.name}: drawing inputs on the device")
+    x = make_inputs(w, device=DEV, kinds=("q_idx", "k_idx", "q", "k", "v"))
+    _, lse = msa.dense_attn_fwd(x["q"], x["k"], x["v"])
+    kl, kl_sum = msa.dense_kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], lse)
+    torch.cuda.synchronize()
+    pos = np.concatenate([sample_rows(w, n=96, seed=1), np.array([[0, w.seqlen - 1]])])
+    _check_kl(w, x, kl, kl_sum, pos)

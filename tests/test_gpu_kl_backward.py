@@ -63,14 +63,21 @@ def compare(name, got, want):
 _JOB = None
 
 
-def _group_job(bg):
+def _group_job(job):
+    bg, rows = job
     q, k, qi, ki, bi, wr, w = _JOB
     b, g = divmod(bg, w.kv_heads)
     G = w.group_size
     hs = slice(g * G, (g + 1) * G)
     return O.kl_backward(q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], qi[b:b + 1, :, g:g + 1], ki[b:b + 1],
                          bi[b:b + 1, g:g + 1], w.block_size, dkl_rows=wr[b:b + 1, g:g + 1],
-                         scale=1 / np.sqrt(w.head_dim), index_scale=1 / np.sqrt(w.index_dim))
+                         scale=1 / np.sqrt(w.head_dim), index_scale=1 / np.sqrt(w.index_dim), row_range=rows)
+
+
+def row_chunks(N, parts):
+    """Contiguous row ranges covering [0, N): the oracle's results over them add up."""
+    step = -(-N // parts)
+    return [(i, min(N, i + step)) for i in range(0, N, step)]
 
 
 def _one_thread():
@@ -87,16 +94,18 @@ def oracle_by_group(host, wr, bi, w):
     _JOB = tuple(t.float().numpy() for t in (host["q"], host["k"], host["q_idx"], host["k_idx"])) + \
         (bi, wr.numpy(), w)
     n = w.batch * w.kv_heads
-    if n == 1 or WORKERS == 1:
-        parts = [_group_job(x) for x in range(n)]
+    chunks = max(1, WORKERS // n) if w.seqlen >= 16384 else 1
+    jobs = [(bg, rows) for bg in range(n) for rows in row_chunks(w.seqlen, chunks)]
+    if len(jobs) == 1 or WORKERS == 1:
+        parts = [_group_job(j) for j in jobs]
     else:
-        with mp.get_context("fork").Pool(min(WORKERS, n), initializer=_one_thread) as pool:
-            parts = pool.map(_group_job, range(n))
+        with mp.get_context("fork").Pool(min(WORKERS, len(jobs)), initializer=_one_thread) as pool:
+            parts = pool.map(_group_job, jobs)
     dqi = np.zeros((w.batch, w.seqlen, w.kv_heads, w.index_dim))
     dki = np.zeros((w.batch, w.seqlen, w.index_dim))
-    for x, (a, c) in enumerate(parts):
-        b, g = divmod(x, w.kv_heads)
-        dqi[b, :, g] = a[0, :, 0]
+    for (bg, _), (a, c) in zip(jobs, parts):
+        b, g = divmod(bg, w.kv_heads)
+        dqi[b, :, g] += a[0, :, 0]
         dki[b] += c[0]
     return dqi, dki
 
@@ -135,6 +144,12 @@ def test_kl_backward_every_element(w):
 
 def test_kl_backward_n8k_every_element():
     check_every_element(CONFIGS["n8k"], on_gpu_rng=True)
+
+
+def test_kl_backward_two_windows_every_element():
+    """Two windows of the inverted selection (N = 65,836): dk_idx of a key
+    block sums the items of both windows over every group."""
+    check_every_element(Workload("two_windows", 1, 65536 + 300, 2, 8, 128, 128, topk=8), on_gpu_rng=True)
 
 
 def test_kl_backward_n128k_sampled_rows_and_sum_rule():

@@ -99,6 +99,30 @@ def test_fp8_inputs_are_decoded_exactly():
         assert got[0, 0, i].tolist() == _brute_force_row(qf[0, i, 0], kf[0], i, Bk, k), i
 
 
+def test_fp4_inputs_are_decoded_exactly():
+    """OCP MX fp4 e2m1 (bias 1, one mantissa bit), the format's value table:
+    codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6 and codes 8..15 their negatives;
+    two codes per byte, the first in the low nibble (byte 0x72 = [1, 6])."""
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    packed = torch.tensor([(2 * c) | ((2 * c + 1) << 4) for c in range(8)], dtype=torch.uint8)
+    got = O._arr(packed.view(torch.float4_e2m1fn_x2))
+    assert got.dtype == np.float32 and got.tolist() == table
+    assert O._arr(torch.tensor([0x72], dtype=torch.uint8).view(torch.float4_e2m1fn_x2)).tolist() == [1.0, 6.0]
+    # the encoder used for test inputs holds the integers -4..4 and +-6 exactly
+    from synth import to_fp4_e2m1
+    ints = torch.tensor([[-6, -4, -3, -2, -1, 0, 1, 2, 3, 4, 6, 0]], dtype=torch.float32)
+    assert O._arr(to_fp4_e2m1(ints)).tolist() == ints.tolist()
+    # and the selection over fp4 tensors is the brute-force one on the decoded values
+    rng = np.random.default_rng(6)
+    N, Bk, k, Di = 30, 4, 4, 4
+    q4 = to_fp4_e2m1(torch.as_tensor(rng.integers(-4, 5, size=(1, N, 1, Di)), dtype=torch.float32))
+    k4 = to_fp4_e2m1(torch.as_tensor(rng.integers(-4, 5, size=(1, N, Di)), dtype=torch.float32))
+    got = O.index_topk(q4, k4, Bk, k)
+    qf, kf = O._arr(q4), O._arr(k4)
+    for i in range(N):
+        assert got[0, 0, i].tolist() == _brute_force_row(qf[0, i, 0], kf[0], i, Bk, k), i
+
+
 def test_selection_invariants_tiny_workload():
     from synth import get_workload, make_inputs
     w = get_workload("tiny")
@@ -617,3 +641,44 @@ def test_dense_rows_are_causal_sdpa():
     want_lse = torch.logsumexp(z, dim=-1)                                  # [B, Hq, N]
     np.testing.assert_allclose(o.reshape(B, N, Hkv * G, D), want.permute(0, 2, 1, 3).numpy(), atol=1e-12)
     np.testing.assert_allclose(lse.reshape(B, N, Hkv * G), want_lse.permute(0, 2, 1).numpy(), atol=1e-12)
+
+
+def test_backward_row_ranges():
+    """Keeping only the rows of a range in the backward is the gradient of the
+    loss with dO zero on every other row (then those rows' dS and P^T dO
+    vanish), checked against torch autograd; ranges covering [0, N) add up
+    to the whole."""
+    N, Bk, k, Hkv, G, D = 56, 8, 3, 2, 2, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(21, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    do = np.random.default_rng(22).standard_normal(q.shape)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    scale = 0.4
+    parts = [O.attention_backward(q, kk, vv, do, bi, Bk, scale, row_range=r) for r in ((0, 19), (19, 40), (40, N))]
+    masked = do.copy()
+    masked[:, :19] = 0.0
+    masked[:, 40:] = 0.0
+    want = _masked_dense_grads(q, kk, vv, masked, bi, Bk, scale)
+    for a, b in zip(parts[1], want):
+        np.testing.assert_allclose(a, b, atol=1e-12, rtol=0)
+    whole = O.attention_backward(q, kk, vv, do, bi, Bk, scale)
+    for x in range(3):
+        np.testing.assert_allclose(sum(p[x] for p in parts), whole[x], atol=1e-12, rtol=0)
+
+
+def test_kl_backward_row_ranges():
+    """The KL backward over a row range equals the whole backward with zero
+    row weights elsewhere; ranges covering [0, N) add up to the whole."""
+    N, Bk, k, Hkv, G, D = 56, 8, 3, 2, 2, 8
+    q_idx, k_idx, q, kk, vv = _rand_case(23, N=N, Hkv=Hkv, G=G, D=D, Bk=Bk)
+    bi = O.index_topk(q_idx, k_idx, Bk, k)
+    w = np.random.default_rng(24).uniform(0.5, 1.5, size=(1, Hkv, N))
+    a = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk, dkl_rows=w, row_range=(10, 33))
+    wm = np.zeros_like(w)
+    wm[..., 10:33] = w[..., 10:33]
+    b = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk, dkl_rows=wm)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, atol=1e-13, rtol=0)
+    rest = [O.kl_backward(q, kk, q_idx, k_idx, bi, Bk, dkl_rows=w, row_range=r) for r in ((0, 10), (33, N))]
+    whole = O.kl_backward(q, kk, q_idx, k_idx, bi, Bk, dkl_rows=w)
+    for x in range(2):
+        np.testing.assert_allclose(a[x] + rest[0][x] + rest[1][x], whole[x], atol=1e-12, rtol=0)
