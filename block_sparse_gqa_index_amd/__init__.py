@@ -34,7 +34,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
-MSA_BF16, MSA_F32, MSA_FP8_E4M3 = 0, 1, 2
+MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP4_E2M1 = 0, 1, 2, 3
+FP4 = torch.float4_e2m1fn_x2   # two OCP e2m1 values per byte, element 2c in the low nibble
 MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD, MSA_OP_KL_BWD = 0, 1, 2, 3, 4, 5
 MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE, MSA_OP_DENSE_ATTN, MSA_OP_DENSE_KL = 6, 7, 8, 9, 10
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
@@ -123,7 +124,7 @@ def make_dims(batch, seqlen, kv_heads, group_size, head_dim, index_dim, topk, dt
               block_size=128, causal=1) -> MsaDims:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.bfloat16: MSA_BF16, torch.float32: MSA_F32,
-                 torch.float8_e4m3fn: MSA_FP8_E4M3}.get(dtype, -1)
+                 torch.float8_e4m3fn: MSA_FP8_E4M3, FP4: MSA_FP4_E2M1}.get(dtype, -1)
     return MsaDims(batch, seqlen, kv_heads, group_size, head_dim, index_dim, block_size, topk,
                    dtype, causal)
 
@@ -179,13 +180,16 @@ def _req(t, name, dtype=None, ndim=None, shape=None, device=None):
 
 def index_topk(q_idx, k_idx, topk, block_idx=None, block_size=128):
     """Block selection. q_idx [B,N,Hkv,Di], k_idx [B,N,Di] (bf16, fp32 or
-    float8_e4m3fn) -> int32 [B,Hkv,N,topk]."""
+    float8_e4m3fn; or float4_e2m1fn_x2 with the last dimension Di/2, two values
+    per byte) -> int32 [B,Hkv,N,topk]."""
     lib = load_library()
     _req(q_idx, "q_idx", ndim=4)
     _req(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)
     B, N, Hkv, Di = q_idx.shape
-    if tuple(k_idx.shape) != (B, N, Di):
-        raise ValueError(f"k_idx shape {tuple(k_idx.shape)} != {(B, N, Di)}")
+    if q_idx.dtype == FP4:
+        Di *= 2
+    if tuple(k_idx.shape) != (B, N, q_idx.shape[3]):
+        raise ValueError(f"k_idx shape {tuple(k_idx.shape)} != {(B, N, q_idx.shape[3])}")
     _req(k_idx, "k_idx", device=q_idx.device)
     if block_idx is None:
         block_idx = torch.empty((B, Hkv, N, topk), dtype=torch.int32, device=q_idx.device)

@@ -66,6 +66,27 @@ template <> struct IdxMma<fp8_t> {    // v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 
     }
 };
 
+template <> struct IdxMma<fp4x2_t> {  // v_mfma_scale_f32_32x32x64_f8f6f4, e2m1 x e2m1, unit scales
+    struct Op {
+        i32x8 v;   // 32 values = 16 bytes; the fp4 form of the instruction reads the first four registers
+        __device__ __forceinline__ void load(const void* p) {
+            const uint4 x = *reinterpret_cast<const uint4*>(p);
+            v = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        }
+        __device__ __forceinline__ void zero() { v = i32x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    };
+    static constexpr int KD = 64;
+    static __device__ __forceinline__ void mma(floatx16& acc, const Op& a, const Op& b) {
+        // format codes 4 (fp4 e2m1) for both operands; scale exponents 127 = 2^0
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, acc, 4, 4, 0, 127, 0, 127);
+    }
+};
+
+// Bits per element of an index input, and the byte offset of element e of a row.
+template <typename T> struct IdxBits { static constexpr int v = 8 * (int)sizeof(T); };
+template <> struct IdxBits<fp4x2_t> { static constexpr int v = 4; };
+template <typename T> __device__ __host__ constexpr int elem_bytes(int e) { return e * IdxBits<T>::v / 8; }
+
 // Inserts (x, j) into the descending list; a no-op when x does not beat the
 // last entry (then no comparison below succeeds), so it runs without a branch
 // and can be scheduled under the matrix-core work of the next key block.
@@ -105,12 +126,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     int B, int N, int Hkv, int k, int qb_lo, int qb_cnt, int chunks) {
     constexpr int NTHR = 64 * WAVES;
-    constexpr int ES = sizeof(T);
-    constexpr int ROWB = DI * ES + 16;        // padded LDS row, bytes
+    constexpr int RB = elem_bytes<T>(DI);     // bytes of one index row
+    constexpr int ROWB = RB + 16;             // padded LDS row, bytes
     using MM = IdxMma<T>;
     constexpr int KD = MM::KD;
     constexpr int KS = DI / KD;               // KD-deep slices of the contraction
-    constexpr int CPR = DI * ES / 16;         // 16-byte chunks per key row
+    constexpr int CPR = RB / 16;              // 16-byte chunks per key row
     constexpr int CPT = kBlock * CPR / NTHR;  // chunks per thread per key block
     constexpr int NO = NT >= 2 ? NT / 2 : 1;  // rows each lane keeps a top-k list for
     static_assert(CPT * NTHR == kBlock * CPR, "staging must tile the block");
@@ -132,10 +153,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     for (int t = 0; t < NT; ++t) {
         const int R = r0 + 32 * t + col;
         const bool valid = qb * kBlock + R / Hkv < N;
-        const T* src = q_idx + (qrow0 + R) * DI + (KD / 2) * half;
+        const unsigned char* src =
+            reinterpret_cast<const unsigned char*>(q_idx) + (qrow0 + R) * RB + elem_bytes<T>((KD / 2) * half);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (valid) bq[t][s].load(src + KD * s);
+            if (valid) bq[t][s].load(src + elem_bytes<T>(KD * s));
             else bq[t][s].zero();
         }
     }
@@ -153,8 +175,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
         }
     }
 
-    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
-    const size_t kblock_bytes = (size_t)kBlock * DI * ES;
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx) + (size_t)b * N * RB;
+    const size_t kblock_bytes = (size_t)kBlock * RB;
     if (qb > 0) {   // a row of query block 0 has no candidate block (and block 0 may be short)
         u32x4 stage[BPB][CPT];
 #pragma unroll
@@ -205,11 +227,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
                 for (int kt = 0; kt < kBlock / 32; ++kt) {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
-                    const unsigned char* arow = &lds[cur][bb][(kt * 32 + col) * ROWB + (KD / 2) * half * ES];
+                    const unsigned char* arow = &lds[cur][bb][(kt * 32 + col) * ROWB + elem_bytes<T>((KD / 2) * half)];
 #pragma unroll
                     for (int s = 0; s < KS; ++s) {
                         typename MM::Op a;
-                        a.load(arow + KD * s * ES);
+                        a.load(arow + elem_bytes<T>(KD * s));
 #pragma unroll
                         for (int t = 0; t < NT; ++t) MM::mma(acc[kt & 1][t], a, bq[t][s]);
                     }
@@ -287,13 +309,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     int B, int N, int Hkv, int k, int qb_lo, int qb_cnt, int chunks) {
     constexpr int NTHR = 64 * WAVES;
-    constexpr int ES = sizeof(T);
-    constexpr int ROWB = DI * ES + 16;        // padded LDS row, bytes
+    constexpr int RB = elem_bytes<T>(DI);     // bytes of one index row
+    constexpr int ROWB = RB + 16;             // padded LDS row, bytes
     constexpr int BUF = kBlock * ROWB;        // one stage
     using MM = IdxMma<T>;
     constexpr int KD = MM::KD;
     constexpr int KS = DI / KD;               // KD-deep slices of the contraction
-    constexpr int CPR = DI * ES / 16;         // 16-byte chunks per key row
+    constexpr int CPR = RB / 16;              // 16-byte chunks per key row
     constexpr int CPT = kBlock * CPR / NTHR;  // chunks per thread per key block
     constexpr int NO = NT >= 2 ? NT / 2 : 1;  // rows each lane keeps a top-k list for
     constexpr int NOPS = (kBlock / 32) * KS;  // A operands per key block
@@ -317,10 +339,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     for (int t = 0; t < NT; ++t) {
         const int R = r0 + 32 * t + col;
         const bool valid = qb * kBlock + R / Hkv < N;
-        const T* src = q_idx + (qrow0 + R) * DI + (KD / 2) * half;
+        const unsigned char* src =
+            reinterpret_cast<const unsigned char*>(q_idx) + (qrow0 + R) * RB + elem_bytes<T>((KD / 2) * half);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (valid) bq[t][s].load(src + KD * s);
+            if (valid) bq[t][s].load(src + elem_bytes<T>(KD * s));
             else bq[t][s].zero();
         }
     }
@@ -339,9 +362,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     }
 
     // Stage offsets of this thread's chunks (global: linear; LDS: padded rows).
-    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx + (size_t)b * N * DI);
-    const size_t kblock_bytes = (size_t)kBlock * DI * ES;
-    const unsigned char* opbase = lds + col * ROWB + (KD / 2) * half * ES;   // + stage + operand offset
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx) + (size_t)b * N * RB;
+    const size_t kblock_bytes = (size_t)kBlock * RB;
+    const unsigned char* opbase = lds + col * ROWB + elem_bytes<T>((KD / 2) * half);   // + stage + operand offset
     u32x4 stage[CPT];
     typename MM::Op a[RING];
     if (qb > 0) {   // a row of query block 0 has no candidate block
@@ -363,7 +386,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     __syncthreads();
     if (qb > 0) {
 #pragma unroll
-        for (int m = 0; m < PF; ++m) a[m].load(opbase + ((m / KS) * 32) * ROWB + KD * (m % KS) * ES);
+        for (int m = 0; m < PF; ++m) a[m].load(opbase + ((m / KS) * 32) * ROWB + elem_bytes<T>(KD * (m % KS)));
     }
 
     float bm[NT], bm_prev[NT];
@@ -382,8 +405,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
         for (int n = 0; n < NOPS; ++n) {
             const int kt = n / KS, s = n % KS;
             const int m = n + PF;
-            if (m < NOPS) a[m % RING].load(opbase + sb * BUF + ((m / KS) * 32) * ROWB + KD * (m % KS) * ES);
-            else a[m % RING].load(opbase + nb1 * BUF + (((m - NOPS) / KS) * 32) * ROWB + KD * ((m - NOPS) % KS) * ES);
+            if (m < NOPS) a[m % RING].load(opbase + sb * BUF + ((m / KS) * 32) * ROWB + elem_bytes<T>(KD * (m % KS)));
+            else a[m % RING].load(opbase + nb1 * BUF + (((m - NOPS) / KS) * 32) * ROWB +
+                                  elem_bytes<T>(KD * ((m - NOPS) % KS)));
             if (s == 0) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[kt & 1][t] = zero16();
@@ -503,7 +527,8 @@ static hipError_t launch_di(const LaunchDims& d, int qb_lo, int qb_cnt, const vo
                             int32_t* out, hipStream_t st) {
     constexpr int NT = sizeof(T) <= 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
     const int rows = kBlock * d.Hkv;
-    if constexpr (sizeof(T) <= 2) {
+    // the pipelined kernel stages a key block with one 16-byte chunk per thread
+    if constexpr (sizeof(T) <= 2 && kBlock * elem_bytes<T>(DI) / 16 >= 512) {
         if (rows % (32 * 2 * 8) == 0) return launch_pipe<T, DI>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
     }
     if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
@@ -521,6 +546,10 @@ hipError_t launch_index_topk(const LaunchDims& d, int qb_lo, int qb_hi, const vo
     if (d.dtype == 2) {
         return d.Di == 128 ? launch_di<fp8_t, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
                            : launch_di<fp8_t, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);
+    }
+    if (d.dtype == 3) {
+        return d.Di == 128 ? launch_di<fp4x2_t, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
+                           : launch_di<fp4x2_t, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);
     }
     return d.Di == 128 ? launch_di<float, 128>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st)
                        : launch_di<float, 64>(d, qb_lo, cnt, q_idx, k_idx, block_idx, st);

@@ -34,10 +34,12 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (d->batch < 0 || d->seqlen < 0 || d->kv_heads < 1 || d->block_size < 1 || (uses_topk && d->topk < 1) ||
         (uses_heads && (d->group_size < 1 || d->head_dim < 1)) || (uses_index && d->index_dim < 1))
         return MSA_ERR_SHAPE;
-    // fp8 index inputs: selection only
+    // fp8 index inputs: selection only; fp4 (two values per byte): the forward selection only
     const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout || op == MSA_OP_DECODE_INDEX;
+    const bool fp4_ok = op == MSA_OP_INDEX || op == kOpLayout;
     if (d->block_size != 128 || (uses_topk && d->topk > 32) ||
-        (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3)) ||
+        (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3) &&
+         !(fp4_ok && d->dtype == MSA_FP4_E2M1)) ||
         ((op == MSA_OP_ATTN_BWD || op == MSA_OP_KL_BWD) && d->dtype != MSA_BF16) ||
         d->causal != 1 || (uses_heads && (!pow2_upto32(d->group_size) || (d->head_dim != 64 && d->head_dim != 128))) ||
         (uses_index && d->index_dim != 64 && d->index_dim != 128))
@@ -120,7 +122,7 @@ const char* msa_strerror(int status) {
         case MSA_ERR_SHAPE: return "invalid or too large problem sizes";
         case MSA_ERR_UNSUPPORTED: return "unsupported sizes or dtype (block_size 128, topk 1..32, group_size "
                                          "power of two <= 32, head/index dim 64 or 128, bf16/fp32 (fp8 e4m3 "
-                                         "for the selection only, bf16 for the backward), causal)";
+                                         "and fp4 e2m1 for the selection only, bf16 for the backward), causal)";
         case MSA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case MSA_ERR_WORKSPACE: return "workspace missing or smaller than msa_workspace_bytes";
         case MSA_ERR_HIP: return "HIP kernel launch failed";

@@ -18,6 +18,12 @@ namespace msa {
 
 typedef uint16_t bf16_t;
 typedef uint8_t fp8_t;   // OCP fp8 e4m3 bits (the variant without infinities)
+// Two OCP fp4 e2m1 values in one byte: element 2c in bits 0-3 of byte c,
+// element 2c + 1 in bits 4-7 (sign, two exponent bits with bias 1, one
+// mantissa bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}).
+struct fp4x2_t {
+    uint8_t bits;
+};
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));

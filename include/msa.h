@@ -47,12 +47,19 @@ extern "C" {
 #define MSA_API
 #endif
 
-/* Element type of every floating-point input (and of O). */
 /* Element type of the tensors. MSA_FP8_E4M3 (OCP fp8 e4m3, the variant with no
  * infinities, |x| <= 448) is accepted by msa_index_topk, msa_decode_index_topk
  * and msa_check_block_idx only: q_idx and k_idx in fp8 on the fp8 matrix cores, scores accumulated in
- * fp32 (exact, and the selection bit-exact, for integer-valued inputs). */
-enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2 };
+ * fp32 (exact, and the selection bit-exact, for integer-valued inputs).
+ * MSA_FP4_E2M1 (OCP fp4 e2m1: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}) is accepted by
+ * msa_index_topk and msa_check_block_idx only: q_idx and k_idx hold two values
+ * per byte (element 2c in bits 0-3 of byte c, element 2c+1 in bits 4-7), so a
+ * row of Di values is Di/2 bytes; the fp4 matrix cores multiply them exactly
+ * and accumulate in fp32, which is exact for any such inputs (every product
+ * is a multiple of 1/4 below 37, every score below 2^13 in magnitude), so the
+ * selection is exact for every fp4 input. The MSA article (7minutos.es, "El
+ * codiseño del kernel") names FP4 among the precisions of the open kernel. */
+enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2, MSA_FP4_E2M1 = 3 };
 
 /* Selector for msa_workspace_bytes. */
 enum msa_op {
@@ -100,8 +107,9 @@ typedef struct msa_dims {
  *
  *   Uses batch, seqlen, kv_heads, index_dim, block_size, topk, dtype and
  *   causal of `dims` (group_size and head_dim are not read).
- *   q_idx     [B, N, Hkv, Di]  index queries, dtype (bf16, fp32 or fp8 e4m3)
- *   k_idx     [B, N, Di]       shared index keys, dtype
+ *   q_idx     [B, N, Hkv, Di]  index queries, dtype (bf16, fp32, fp8 e4m3, or
+ *                              fp4 e2m1 packed as [B, N, Hkv, Di/2] bytes)
+ *   k_idx     [B, N, Di]       shared index keys, dtype (fp4: [B, N, Di/2] bytes)
  *   block_idx [B, Hkv, N, k]   int32 OUTPUT. For query i (local block L = i/Bk)
  *             and group g: the block ids j < L with the k-1 largest
  *             m_j = max_{t in block j} <q_idx[b,i,g], k_idx[b,t]> (ties: lower

@@ -150,3 +150,24 @@ def make_decode_inputs(w: Workload, device="cpu", seed=None, lengths=None):
         lengths = torch.randint(1, C + 1, (B,), generator=lgen)
     out["seqlens"] = torch.as_tensor(lengths, dtype=torch.int32).reshape(B).to(device)
     return out
+
+
+# OCP fp4 e2m1 magnitudes by code 0..7; the rounding boundaries between codes
+# c and c + 1 are the midpoints, a value on a midpoint goes to the even code.
+_FP4_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def to_fp4_e2m1(x: torch.Tensor) -> torch.Tensor:
+    """Round x to OCP fp4 e2m1 (nearest, ties to the even code, saturating at
+    +-6) and pack two values per byte, element 2c in bits 0-3 of byte c:
+    returns a float4_e2m1fn_x2 tensor with the last dimension halved (it must
+    be even). An input conversion for tests and the benchmark; the integers
+    -4..4 and +-6 are held exactly."""
+    a = x.detach().float().abs()
+    code = torch.zeros(a.shape, dtype=torch.uint8, device=x.device)
+    for c, t in enumerate(_FP4_MIDPOINTS):
+        up = (a > t) | ((a == t) & ((c + 1) % 2 == 0))
+        code += up.to(torch.uint8)
+    code |= ((x < 0) & (code != 0)).to(torch.uint8) << 3
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous().view(torch.float4_e2m1fn_x2)
