@@ -22,6 +22,7 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq]) (or [B,R,Hq,D], [B,Hq,R])
   decode(q_idx, k_idx, q, k, v, seqlens, topk)     -> (block_idx, o, lse): both decode steps
   decode_paged*(..., block_table, ...)             -> the decode calls on page pools [P, 128, ...] + a block table
+  decode_noalloc(q_idx, k_idx, q, k, v, seqlens, topk) -> decode() with the library's fixed scratch, no workspace
   dense_attn_fwd(q, k, v)                          -> (o, lse): causal attention over every visible key (warm-up)
   dense_kl_align_fwd(q, k, q_idx, k_idx, lse)      -> (kl_rows, kl_sum): the KL loss over every visible token
   workspace_bytes(dims, op)
@@ -40,12 +41,13 @@ MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD, MSA_OP_KL
 MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE, MSA_OP_DENSE_ATTN, MSA_OP_DENSE_KL = 6, 7, 8, 9, 10
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
-          4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP"}
+          4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP", 7: "MSA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MSA_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_sparse_attn_fwd_stages",
            "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
            "msa_decode_index_topk", "msa_decode_attn", "msa_decode", "msa_dense_attn_fwd",
            "msa_dense_kl_align_fwd", "msa_decode_paged_index_topk", "msa_decode_paged_attn", "msa_decode_paged",
-           "msa_decode_workspace_bytes",
+           "msa_decode_workspace_bytes", "msa_decode_noalloc",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -91,6 +93,7 @@ def load_library(path: str = LIB_PATH):
     lib.msa_decode_index_topk.argtypes = [dp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode_attn.argtypes = [dp, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode_noalloc.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
     lib.msa_decode_workspace_bytes.argtypes = [dp, ctypes.c_int, i32]
     lib.msa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_dense_attn_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
@@ -109,7 +112,7 @@ def load_library(path: str = LIB_PATH):
               lib.msa_kl_align_fwd, lib.msa_forward, lib.msa_kl_align_bwd, lib.msa_sparse_attn_bwd,
               lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode, lib.msa_dense_attn_fwd,
               lib.msa_dense_kl_align_fwd, lib.msa_decode_paged_index_topk, lib.msa_decode_paged_attn,
-              lib.msa_decode_paged):
+              lib.msa_decode_paged, lib.msa_decode_noalloc):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -528,6 +531,38 @@ def decode(q_idx, k_idx, q, k, v, seqlens, topk, softmax_scale=0.0, block_idx=No
     _check(lib.msa_decode(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
                           float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws,
                           _stream(q.device)))
+    return block_idx, o, lse
+
+
+def decode_noalloc(q_idx, k_idx, q, k, v, seqlens, topk, softmax_scale=0.0, block_idx=None, o=None, lse=None,
+                   block_size=128):
+    """decode() through msa_decode_noalloc: the library's fixed scratch array
+    (64 MiB per GPU) instead of a workspace; the library allocates nothing
+    (the outputs, if not given, are still allocated here by torch). Calls that
+    overlap on one GPU race on that array."""
+    lib = load_library()
+    R, multi = _rows(q_idx, "q_idx", 2)
+    R2, multi2 = _rows(q, "q", 2)
+    if (R2, multi2) != (R, multi) or q.dtype != q_idx.dtype:
+        raise ValueError("q and q_idx must have the same new-query axis and dtype")
+    _req(k_idx, "k_idx", dtype=q.dtype, ndim=3)
+    _req(k, "k", dtype=q.dtype, ndim=4)
+    _req(v, "v", dtype=q.dtype, ndim=4)
+    _req(seqlens, "seqlens", dtype=torch.int32, ndim=1)
+    B, C, Hkv, D = k.shape
+    Di, Hq = k_idx.shape[2], q.shape[-2]
+    if (tuple(k_idx.shape[:2]) != (B, C) or tuple(v.shape) != tuple(k.shape) or q_idx.shape[-2:] != (Hkv, Di)
+            or q.shape[-1] != D or Hq % Hkv or seqlens.shape[0] != B or q_idx.shape[0] != B or q.shape[0] != B):
+        raise ValueError("inconsistent shapes")
+    for name, t in (("q_idx", q_idx), ("k_idx", k_idx), ("k", k), ("v", v), ("seqlens", seqlens)):
+        _req(t, name, device=q.device)
+    block_idx, o, lse = _decode_outputs(B, R, multi, Hkv, Hq, D, topk, q, block_idx, o, lse)
+    _check_sel(block_idx, B, Hkv, R, multi, q.device, topk)
+    _check_decode_out(o, lse, B, R, multi, Hq, D, q.dtype, q.device)
+    dims = make_dims(B, C, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
+    _check(lib.msa_decode_noalloc(ctypes.byref(dims), R, _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(seqlens), float(softmax_scale), _ptr(block_idx), _ptr(o), _ptr(lse),
+                                  _stream(q.device)))
     return block_idx, o, lse
 
 

@@ -6,7 +6,9 @@
 
 #include <limits.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "msa_decode.h"
 #include "msa_internal.h"
@@ -87,7 +89,7 @@ size_t decode_ws(const LaunchDims& L, int op, int R) {
 // Decode calls share their argument checks: sizes, the per-op pointers, and
 // the workspace of `op`.
 int check_decode(const msa_dims* dims, int R, int op, LaunchDims* L, std::initializer_list<const void*> ptrs,
-                 const void* ws, size_t ws_bytes) {
+                 const void* ws, size_t ws_bytes, bool check_ws = true) {
     int st = check_dims(dims, op, L);
     if (st != MSA_OK) return st;
     // R new queries per sequence; the grids put sequences x queries (x group chunks of 32) on one axis.
@@ -103,11 +105,47 @@ int check_decode(const msa_dims* dims, int R, int op, LaunchDims* L, std::initia
     for (const void* p : ptrs)
         if (!aligned16(p)) return MSA_ERR_ALIGN;
     const size_t need = decode_ws(*L, op, R);
-    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
+    if (check_ws && need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MSA_ERR_WORKSPACE;
     return MSA_OK;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+}  // namespace
+
+// ------------------------------------------------- no-allocation decoding --
+// The scratch memory of msa_decode_noalloc: a file-scope device array, one copy
+// per GPU, in place of a caller-provided workspace (the decode's block scores,
+// then its per-block partial outputs and LSEs). Every call on a GPU uses that
+// GPU's copy, so calls that overlap on one GPU race on it. Host code never
+// passes the array's name to a kernel or a copy (on the host it is only a
+// stand-in): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current and kept.
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (MSA_ERR_HIP if HIP
+// cannot name the device or the symbol; nothing is enqueued either way).
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSA_ERR_HIP;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSA_ERR_HIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MSA_OK;
+}
 
 }  // namespace
 
@@ -126,6 +164,8 @@ const char* msa_strerror(int status) {
         case MSA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case MSA_ERR_WORKSPACE: return "workspace missing or smaller than msa_workspace_bytes";
         case MSA_ERR_HIP: return "HIP kernel launch failed";
+        case MSA_ERR_SCRATCH: return "the problem needs more than the no-allocation entry point's scratch memory "
+                                     "(MSA_NOALLOC_SCRATCH_BYTES = 64 MiB)";
         default: return "unknown status";
     }
 }
@@ -405,3 +445,22 @@ int msa_decode_paged(const msa_dims* dims, int32_t num_queries, const void* q_id
 }
 
 }  // extern "C"
+
+extern "C" int msa_decode_noalloc(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx,
+                                  const void* q, const void* k, const void* v, const int32_t* seqlens,
+                                  float softmax_scale, int32_t* block_idx, void* o, float* lse, void* stream) {
+    LaunchDims L;
+    int st = check_decode(dims, num_queries, MSA_OP_DECODE, &L, {q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse},
+                          nullptr, 0, /*check_ws=*/false);
+    if (st != MSA_OK || empty(L)) return st;
+    if (decode_ws(L, MSA_OP_DECODE, num_queries) > MSA_NOALLOC_SCRATCH_BYTES) return MSA_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != MSA_OK) return st;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const msa::DecodeDims d = decode_dims(L, num_queries);
+    if (msa::launch_decode_index(d, q_idx, k_idx, seqlens, nullptr, 0, block_idx, ws, s) != hipSuccess)
+        return MSA_ERR_HIP;
+    return hip_status(msa::launch_decode_attn(d, q, k, v, seqlens, block_idx, nullptr, 0, scale, o, lse, ws, s));
+}

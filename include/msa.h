@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 5
+#define MSA_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define MSA_API __attribute__((visibility("default")))
@@ -74,7 +74,8 @@ enum msa_status {
     MSA_ERR_UNSUPPORTED = 3, /* a size or dtype this build has no kernel for      */
     MSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned           */
     MSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than msa_workspace_bytes */
-    MSA_ERR_HIP = 6          /* a HIP launch failed                               */
+    MSA_ERR_HIP = 6,         /* a HIP launch failed                               */
+    MSA_ERR_SCRATCH = 7      /* msa_decode_noalloc: more than its scratch memory   */
 };
 
 /*
@@ -395,6 +396,28 @@ MSA_API int msa_decode_paged(const msa_dims* dims, int32_t num_queries, const vo
                              const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                              int32_t num_pages, const int32_t* seqlens, float softmax_scale, int32_t* block_idx,
                              void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decoding without any allocation: msa_decode with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Arguments, results
+ * and errors are those of msa_decode (every output bitwise the same); the
+ * scratch memory msa_decode takes from `ws` is instead a fixed array of
+ * MSA_NOALLOC_SCRATCH_BYTES bytes in the library's device memory, one per GPU,
+ * held until the process ends. A problem whose decode workspace
+ * (msa_decode_workspace_bytes(dims, MSA_OP_DECODE, num_queries)) is larger is
+ * refused with MSA_ERR_SCRATCH before any launch (64 MiB holds, e.g., 120
+ * sequences at k = 16, Hkv = 8, G = 8, D = 128). The call allocates and frees
+ * nothing. Every call on a GPU uses that GPU's one array: calls that overlap
+ * on one GPU (other streams, other threads) race and give unspecified
+ * results. The first call on each device (the calling thread's current
+ * device, which must be the stream's) looks the array's device address up
+ * once; MSA_ERR_HIP if that fails.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+MSA_API int msa_decode_noalloc(const msa_dims* dims, int32_t num_queries, const void* q_idx, const void* k_idx,
+                               const void* q, const void* k, const void* v, const int32_t* seqlens,
+                               float softmax_scale, int32_t* block_idx, void* o, float* lse, void* stream);
 
 /* Workspace bytes of a decode call with num_queries new queries per sequence
  * (op MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN or MSA_OP_DECODE); 0 if the sizes

@@ -42,8 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.msa_abi_version() == 5
-    for s in range(7):
+    assert lib.msa_abi_version() == 6
+    for s in range(8):
         assert lib.msa_strerror(s)
     assert lib.msa_strerror(99) == b"unknown status"
 
@@ -371,3 +371,24 @@ def test_multi_query_decode_arguments(lib):
     assert _dec(lib, _dims(batch=20000), dict(R=4)) == 2              # B * R > 65535
     assert _dec(lib, d, dict(R=4), ws=FAKE, nws=four - 1) == 5       # the R-query workspace is required
     assert _dec_attn(lib, d, dict(R=4, o=None), ws=FAKE, nws=four) == 1
+
+
+def test_noalloc_decode_arguments(lib):
+    """msa_decode_noalloc: the decode checks, then problems whose decode
+    workspace exceeds its 64 MiB scratch array are refused (MSA_ERR_SCRATCH)
+    before any device work; an empty batch needs nothing."""
+    def call(d, R=1, **ptrs):
+        p = dict(qi=FAKE, ki=FAKE, q=FAKE, k=FAKE, v=FAKE, sl=FAKE, bi=FAKE, o=FAKE, lse=FAKE)
+        p.update(ptrs)
+        return lib.msa_decode_noalloc(ctypes.byref(d), R, p["qi"], p["ki"], p["q"], p["k"], p["v"], p["sl"], 0.0,
+                                      p["bi"], p["o"], p["lse"], None)
+    big = _dims(batch=200, seqlen=131072, kv_heads=8, group_size=8, head_dim=128, index_dim=128, topk=16)
+    assert msa.decode_workspace_bytes(big, msa.MSA_OP_DECODE, 1) > msa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 7
+    assert call(big, R=2) == 7
+    assert call(big, q=None) == 1                      # pointer checks come first
+    assert call(big, o=MISALIGNED) == 4
+    assert call(_dims(block_size=64)) == 3
+    assert call(_dims(), R=0) == 2
+    assert call(_dims(batch=0)) == 0                   # empty: nothing to do, no device touched
+    assert b"scratch" in lib.msa_strerror(7)
