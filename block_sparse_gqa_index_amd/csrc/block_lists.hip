@@ -265,11 +265,11 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint32_t* __restrict
 // first min(k, L+1) entries strictly ascending in [0, L] ending with L, then
 // -1)? Broken rows are counted into *bad (cleared first by the caller).
 __global__ __launch_bounds__(256) void check_rows_kernel(const int32_t* __restrict__ block_idx, int32_t* bad,
-                                                         int64_t rows, int N, int k) {
+                                                         int64_t rows, int N, int k, int Bk) {
     const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (x >= rows) return;
     const int i = (int)(x % N);
-    const int L = i / kBlock;
+    const int L = i / Bk;
     const int nv = min(k, L + 1);
     const int32_t* row = block_idx + x * k;
     bool ok = true;
@@ -291,7 +291,7 @@ hipError_t launch_check_block_idx(const LaunchDims& d, const int32_t* block_idx,
     const int64_t rows = (int64_t)d.B * d.Hkv * d.N;
     if (rows > 0)
         hipLaunchKernelGGL(check_rows_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx, bad,
-                           rows, d.N, d.k);
+                           rows, d.N, d.k, d.Bk);
     return hipGetLastError();
 }
 

@@ -121,7 +121,24 @@ __device__ __forceinline__ void sort_ascending(int (&v)[SLOTS]) {
     }
 }
 
-template <typename T, int DI, int NT, int WAVES, int SLOTS, int BPB>
+// Rows, candidate blocks and staging shared by both index kernels for a block
+// size BK of 64, 128 or 256 keys. The kernels always scan 128-key blocks (one
+// LDS stage); a 256-key block's score is the larger of its two halves', and a
+// 128-key block holds two 64-key blocks (the max over its key tiles 0-1 and
+// 2-3). For BK = 64 the query block's own 128-key block is scanned too: its
+// first half competes for the rows in the second half of the query block.
+template <int BK>
+struct BlockPlan {
+    static_assert(BK == 64 || BK == 128 || BK == 256, "block size");
+    // 128-key blocks scanned for query block qb (whole pairs for BK = 256)
+    static __device__ __forceinline__ int scanned(int qb) { return BK == 128 ? qb : BK == 256 ? (qb & ~1) : qb + 1; }
+    // competing BK-blocks of the row at position p of query block qb (= its local block id)
+    static __device__ __forceinline__ int local(int qb, int p) {
+        return BK == 128 ? qb : BK == 256 ? qb / 2 : 2 * qb + (p >= 64 ? 1 : 0);
+    }
+};
+
+template <typename T, int DI, int NT, int WAVES, int SLOTS, int BPB, int BK>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     int B, int N, int Hkv, int k, int qb_lo, int qb_cnt, int chunks) {
@@ -176,15 +193,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
     }
 
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx) + (size_t)b * N * RB;
-    const size_t kblock_bytes = (size_t)kBlock * RB;
-    if (qb > 0) {   // a row of query block 0 has no candidate block (and block 0 may be short)
+    const int nj = BlockPlan<BK>::scanned(qb);
+    int lrow[NO];   // per owned row: its competing blocks (= its local block id)
+#pragma unroll
+    for (int o = 0; o < NO; ++o) lrow[o] = BlockPlan<BK>::local(qb, (r0 + 32 * (NT >= 2 ? 2 * o + half : 0) + col) / Hkv);
+    // 16-byte chunk ch of scanned block j (the query's own block, scanned for
+    // BK = 64, may end past N: its rows there repeat row N - 1, never used)
+    auto chunk_src = [&](int j, int ch) {
+        const int key = BK == 64 ? min(j * kBlock + ch / CPR, N - 1) : j * kBlock + ch / CPR;
+        return reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (ch % CPR) * 16);
+    };
+    if (nj > 0) {   // a row of query block 0 has no candidate block at BK >= 128
         u32x4 stage[BPB][CPT];
 #pragma unroll
         for (int bb = 0; bb < BPB; ++bb) {
-            const unsigned char* src = kbase + (size_t)min(bb, qb - 1) * kblock_bytes;
 #pragma unroll
-            for (int u = 0; u < CPT; ++u)
-                stage[bb][u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+            for (int u = 0; u < CPT; ++u) stage[bb][u] = *chunk_src(min(bb, nj - 1), tid + NTHR * u);
         }
         {
 #pragma unroll
@@ -201,24 +225,23 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
 
     // Block j's candidate (per owned row) is inserted while block j+1 is on the
     // matrix cores; each key tile's max overlaps the next tile's MFMAs.
-    float x_prev[NO];
+    float x_prev[NO], stash[NO];   // pending candidate; BK = 256: the first half's max
+    int id_prev = -1;
 #pragma unroll
-    for (int o = 0; o < NO; ++o) x_prev[o] = -__builtin_inff();
-    for (int jp = 0; jp < qb; jp += BPB) {
+    for (int o = 0; o < NO; ++o) x_prev[o] = stash[o] = -__builtin_inff();
+    for (int jp = 0; jp < nj; jp += BPB) {
         const int cur = (jp / BPB) & 1;
         // Next BPB key blocks: global -> VGPRs now, VGPRs -> LDS after this stage's math.
         u32x4 stage[BPB][CPT];
 #pragma unroll
         for (int bb = 0; bb < BPB; ++bb) {
-            const unsigned char* src = kbase + (size_t)min(jp + BPB + bb, qb - 1) * kblock_bytes;
 #pragma unroll
-            for (int u = 0; u < CPT; ++u)
-                stage[bb][u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+            for (int u = 0; u < CPT; ++u) stage[bb][u] = *chunk_src(min(jp + BPB + bb, nj - 1), tid + NTHR * u);
         }
 #pragma unroll
         for (int bb = 0; bb < BPB; ++bb) {
             const int j = jp + bb;
-            if (j < qb) {
+            if (j < nj) {
                 float bm[NT];
 #pragma unroll
                 for (int t = 0; t < NT; ++t) bm[t] = -__builtin_inff();
@@ -238,11 +261,24 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
                     if (kt == 0) {
                         if (j > 0) {
 #pragma unroll
-                            for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], j - 1);
+                            for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], id_prev);
                         }
                     } else {
 #pragma unroll
                         for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], max16(acc[(kt - 1) & 1][t]));
+                        if (BK == 64 && kt == 2) {
+                            // key tiles 0-1 done: the first 64-key block of j (for the
+                            // query's own block only the rows of the second half see it)
+#pragma unroll
+                            for (int t = 0; t < NT; ++t) bm[t] = fmaxf(bm[t], swap_halves(bm[t]));
+#pragma unroll
+                            for (int o = 0; o < NO; ++o) {
+                                const float x = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
+                                topk_insert<SLOTS>(sc[o], id[o], 2 * j < lrow[o] ? x : -__builtin_inff(), 2 * j);
+                            }
+#pragma unroll
+                            for (int t = 0; t < NT; ++t) bm[t] = -__builtin_inff();
+                        }
                     }
                 }
 #pragma unroll
@@ -251,7 +287,20 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
                     bm[t] = fmaxf(bm[t], swap_halves(bm[t]));
                 }
 #pragma unroll
-                for (int o = 0; o < NO; ++o) x_prev[o] = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
+                for (int o = 0; o < NO; ++o) {
+                    const float x = NT >= 2 ? (half ? bm[2 * o + 1] : bm[2 * o]) : bm[0];
+                    if (BK == 128) {
+                        x_prev[o] = x;
+                    } else if (BK == 64) {   // the second 64-key block of j (never a candidate in the query's block)
+                        x_prev[o] = 2 * j + 1 < lrow[o] ? x : -__builtin_inff();
+                    } else if (j & 1) {      // BK = 256: both halves seen
+                        x_prev[o] = fmaxf(stash[o], x);
+                    } else {
+                        stash[o] = x;
+                        x_prev[o] = -__builtin_inff();
+                    }
+                }
+                id_prev = BK == 128 ? j : BK == 64 ? 2 * j + 1 : j / 2;
             }
         }
         // Unconditional (the last iteration writes a copy of the last block that
@@ -269,12 +318,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
         }
         __syncthreads();
     }
-    if (qb > 0) {
+    if (nj > 0) {
 #pragma unroll
-        for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], qb - 1);
+        for (int o = 0; o < NO; ++o) topk_insert<SLOTS>(sc[o], id[o], x_prev[o], id_prev);
     }
 
-    const int nvalid = min(nslots, qb);
 #pragma unroll
     for (int o = 0; o < NO; ++o) {
         const int t = NT >= 2 ? 2 * o + half : 0;
@@ -282,6 +330,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
         const int pos = qb * kBlock + R / Hkv;
         const int g = R % Hkv;
         const bool writer = pos < N && (NT >= 2 || half == 0);
+        const int nvalid = min(nslots, lrow[o]);
         int v[SLOTS];
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) v[s] = id[o][s] < 0 ? 0x7fffffff : id[o][s];
@@ -290,7 +339,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
             int32_t* dst = block_idx + (((size_t)b * Hkv + g) * N + pos) * k;
 #pragma unroll
             for (int s = 0; s <= SLOTS; ++s) {
-                if (s < k) dst[s] = s < nvalid ? v[s < SLOTS ? s : SLOTS - 1] : (s == nvalid ? qb : -1);
+                if (s < k) dst[s] = s < nvalid ? v[s < SLOTS ? s : SLOTS - 1] : (s == nvalid ? lrow[o] : -1);
             }
         }
     }
@@ -304,7 +353,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
 // the MFMA that uses them, across block boundaries. The last key tile's max of
 // block j is taken under block j+1's first MFMAs, and its candidate inserted
 // right after.
-template <typename T, int DI, int NT, int WAVES, int SLOTS>
+template <typename T, int DI, int NT, int WAVES, int SLOTS, int BK>
 __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     int B, int N, int Hkv, int k, int qb_lo, int qb_cnt, int chunks) {
@@ -363,33 +412,41 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
 
     // Stage offsets of this thread's chunks (global: linear; LDS: padded rows).
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_idx) + (size_t)b * N * RB;
-    const size_t kblock_bytes = (size_t)kBlock * RB;
     const unsigned char* opbase = lds + col * ROWB + elem_bytes<T>((KD / 2) * half);   // + stage + operand offset
+    const int nj = BlockPlan<BK>::scanned(qb);
+    int lrow[NO];   // per owned row (t = 2o + half): its competing blocks (= its local block id)
+#pragma unroll
+    for (int o = 0; o < NO; ++o) lrow[o] = BlockPlan<BK>::local(qb, (r0 + 32 * (2 * o + half) + col) / Hkv);
+    // 16-byte chunk ch of scanned block j (the query's own block, scanned for
+    // BK = 64, may end past N: its rows there repeat row N - 1, never used)
+    auto chunk_src = [&](int j, int ch) {
+        const int key = BK == 64 ? min(j * kBlock + ch / CPR, N - 1) : j * kBlock + ch / CPR;
+        return reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (ch % CPR) * 16);
+    };
     u32x4 stage[CPT];
     typename MM::Op a[RING];
-    if (qb > 0) {   // a row of query block 0 has no candidate block
+    if (nj > 0) {   // a row of query block 0 has no candidate block at BK >= 128
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
-            const unsigned char* src = kbase + (size_t)min(bb, qb - 1) * kblock_bytes;
 #pragma unroll
-            for (int u = 0; u < CPT; ++u) stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+            for (int u = 0; u < CPT; ++u) stage[u] = *chunk_src(min(bb, nj - 1), tid + NTHR * u);
 #pragma unroll
             for (int u = 0; u < CPT; ++u) {
                 const int ch = tid + NTHR * u;
                 *reinterpret_cast<u32x4*>(lds + bb * BUF + (ch / CPR) * ROWB + (ch % CPR) * 16) = stage[u];
             }
         }
-        const unsigned char* src = kbase + (size_t)min(2, qb - 1) * kblock_bytes;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+        for (int u = 0; u < CPT; ++u) stage[u] = *chunk_src(min(2, nj - 1), tid + NTHR * u);
     }
     __syncthreads();
-    if (qb > 0) {
+    if (nj > 0) {
 #pragma unroll
         for (int m = 0; m < PF; ++m) a[m].load(opbase + ((m / KS) * 32) * ROWB + elem_bytes<T>(KD * (m % KS)));
     }
 
     float bm[NT], bm_prev[NT];
+    float stash[NO];   // BK = 256: the max of the pair's first block
     floatx16 acc[2][NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -397,8 +454,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[1][t][r] = -__builtin_inff();
     }
+#pragma unroll
+    for (int o = 0; o < NO; ++o) stash[o] = -__builtin_inff();
+    // Candidate of a finished block j (BK = 128: its max; 64: the max of its
+    // second half, never a candidate in the query's own block; 256: the pair's
+    // max once both halves are in).
+    auto finish_block = [&](int jb, float x, int o) {
+        if (BK == 128) {
+            if (__builtin_amdgcn_ballot_w64(x > sc[o][SLOTS - 1])) topk_insert<SLOTS>(sc[o], id[o], x, jb);
+        } else if (BK == 64) {
+            if (2 * jb + 1 < lrow[o]) topk_insert<SLOTS>(sc[o], id[o], x, 2 * jb + 1);
+        } else if (jb & 1) {
+            topk_insert<SLOTS>(sc[o], id[o], fmaxf(stash[o], x), jb / 2);
+        } else {
+            stash[o] = x;
+        }
+    };
     int sb = 0;   // stage of block j
-    for (int j = 0; j < qb; ++j) {
+    for (int j = 0; j < nj; ++j) {
         const int nb1 = sb == 2 ? 0 : sb + 1;    // stage of block j+1
         const int wb = nb1 == 2 ? 0 : nb1 + 1;   // stage of block j+2 (= that of block j-1)
 #pragma unroll
@@ -416,19 +489,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
             for (int t = 0; t < NT; ++t) MM::mma(acc[kt & 1][t], a[n % RING], bq[t][s]);
             if (s == KS - 1) {
                 if (kt == 0) {
-                    // block j-1: last tile's max, then its candidate
+                    // block j-1: last tile's max, then its candidate (at BK = 128 the
+                    // insert is skipped by the whole wave when no row's candidate beats
+                    // its current last entry, rare for late blocks of long rows)
+                    if (j > 0) {
 #pragma unroll
-                    for (int o = 0; o < NO; ++o) {
-                        const float x = pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
-                                                     fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1])));
-                        // skipped by the whole wave when no row's candidate beats its
-                        // current last entry (rare for late blocks of long rows)
-                        if (__builtin_amdgcn_ballot_w64(x > sc[o][SLOTS - 1]))
-                            topk_insert<SLOTS>(sc[o], id[o], x, j - 1);
+                        for (int o = 0; o < NO; ++o)
+                            finish_block(j - 1,
+                                         pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
+                                                      fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1]))),
+                                         o);
                     }
+                } else if (BK == 64 && kt == 3) {
+                    // the second half starts at key tile 2
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) bm[t] = max16(acc[0][t]);
                 } else {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) bm[t] = kt == 1 ? max16(acc[0][t]) : fmaxf(bm[t], max16(acc[(kt - 1) & 1][t]));
+                    if (BK == 64 && kt == 2) {
+                        // key tiles 0-1 done: the first 64-key block of j (for the
+                        // query's own block only the rows of the second half see it)
+#pragma unroll
+                        for (int o = 0; o < NO; ++o) {
+                            const float x = pair_max_own(bm[2 * o], bm[2 * o + 1]);
+                            if (2 * j < lrow[o]) topk_insert<SLOTS>(sc[o], id[o], x, 2 * j);
+                        }
+                    }
                 }
             }
         }
@@ -440,22 +527,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
             const int ch = tid + NTHR * u;
             *reinterpret_cast<u32x4*>(lds + wb * BUF + (ch / CPR) * ROWB + (ch % CPR) * 16) = stage[u];
         }
-        const unsigned char* src = kbase + (size_t)min(j + 3, qb - 1) * kblock_bytes;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) stage[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + NTHR * u) * 16);
+        for (int u = 0; u < CPT; ++u) stage[u] = *chunk_src(min(j + 3, nj - 1), tid + NTHR * u);
         __syncthreads();
         sb = nb1;
     }
-    if (qb > 0) {
+    if (nj > 0) {
 #pragma unroll
         for (int o = 0; o < NO; ++o)
-            topk_insert<SLOTS>(sc[o], id[o],
-                               pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
-                                            fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1]))),
-                               qb - 1);
+            finish_block(nj - 1,
+                         pair_max_own(fmaxf(bm_prev[2 * o], max16(acc[1][2 * o])),
+                                      fmaxf(bm_prev[2 * o + 1], max16(acc[1][2 * o + 1]))),
+                         o);
     }
 
-    const int nvalid = min(nslots, qb);
 #pragma unroll
     for (int o = 0; o < NO; ++o) {
         const int t = NT >= 2 ? 2 * o + half : 0;
@@ -463,6 +548,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
         const int pos = qb * kBlock + R / Hkv;
         const int g = R % Hkv;
         const bool writer = pos < N && (NT >= 2 || half == 0);
+        const int nvalid = min(nslots, lrow[o]);
         int v[SLOTS];
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) v[s] = id[o][s] < 0 ? 0x7fffffff : id[o][s];
@@ -471,13 +557,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
             int32_t* dst = block_idx + (((size_t)b * Hkv + g) * N + pos) * k;
 #pragma unroll
             for (int s = 0; s <= SLOTS; ++s) {
-                if (s < k) dst[s] = s < nvalid ? v[s < SLOTS ? s : SLOTS - 1] : (s == nvalid ? qb : -1);
+                if (s < k) dst[s] = s < nvalid ? v[s < SLOTS ? s : SLOTS - 1] : (s == nvalid ? lrow[o] : -1);
             }
         }
     }
 }
 
-template <typename T, int DI, int NT, int WAVES>
+template <typename T, int DI, int NT, int WAVES, int BK>
 static hipError_t launch_cfg(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                              int32_t* out, hipStream_t st) {
     // One key block per barrier: two such work-groups share a CU (two LDS
@@ -488,13 +574,13 @@ static hipError_t launch_cfg(const LaunchDims& d, int qb_lo, int qb_cnt, const v
     const T* q = static_cast<const T*>(q_idx);
     const T* kk = static_cast<const T*>(k_idx);
     if (d.k <= 8)
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 7, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 7, BPB, BK>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     else if (d.k <= 16)
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 15, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 15, BPB, BK>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     else
-        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 31, BPB>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_kernel<T, DI, NT, WAVES, 31, BPB, BK>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     return hipGetLastError();
 }
@@ -502,7 +588,7 @@ static hipError_t launch_cfg(const LaunchDims& d, int qb_lo, int qb_cnt, const v
 // Shapes: the pipelined 8-wave kernel when 512 rows tile a query block (128*Hkv
 // rows) in bf16; else 4-wave work-groups (one wave per SIMD, 64 rows per wave
 // for bf16, two work-groups per CU) when 256 rows do, else 2-wave ones.
-template <typename T, int DI>
+template <typename T, int DI, int BK>
 static hipError_t launch_pipe(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                               int32_t* out, hipStream_t st) {
     constexpr int NT = 2, WAVES = 8;
@@ -511,28 +597,39 @@ static hipError_t launch_pipe(const LaunchDims& d, int qb_lo, int qb_cnt, const 
     const T* q = static_cast<const T*>(q_idx);
     const T* kk = static_cast<const T*>(k_idx);
     if (d.k <= 8)
-        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 7>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 7, BK>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     else if (d.k <= 16)
-        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 15>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 15, BK>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     else
-        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 31>), grid, block, 0, st, q, kk, out, d.B, d.N,
+        hipLaunchKernelGGL((index_topk_pipe_kernel<T, DI, NT, WAVES, 31, BK>), grid, block, 0, st, q, kk, out, d.B, d.N,
                            d.Hkv, d.k, qb_lo, qb_cnt, chunks);
     return hipGetLastError();
 }
 
-template <typename T, int DI>
-static hipError_t launch_di(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
+template <typename T, int DI, int BK>
+static hipError_t launch_bk(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
                             int32_t* out, hipStream_t st) {
     constexpr int NT = sizeof(T) <= 2 ? 2 : 1;   // fp32 operands take twice the VGPRs
     const int rows = kBlock * d.Hkv;
     // the pipelined kernel stages a key block with one 16-byte chunk per thread
     if constexpr (sizeof(T) <= 2 && kBlock * elem_bytes<T>(DI) / 16 >= 512) {
-        if (rows % (32 * 2 * 8) == 0) return launch_pipe<T, DI>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+        if (rows % (32 * 2 * 8) == 0) return launch_pipe<T, DI, BK>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
     }
-    if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
-    return launch_cfg<T, DI, NT, 2>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+    if (rows % (32 * NT * 4) == 0) return launch_cfg<T, DI, NT, 4, BK>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+    return launch_cfg<T, DI, NT, 2, BK>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+}
+
+// Block sizes 64 and 256 for bf16 and fp32 index inputs; fp8 and fp4 at 128.
+template <typename T, int DI>
+static hipError_t launch_di(const LaunchDims& d, int qb_lo, int qb_cnt, const void* q_idx, const void* k_idx,
+                            int32_t* out, hipStream_t st) {
+    if constexpr (sizeof(T) == 2 || sizeof(T) == 4) {
+        if (d.Bk == 64) return launch_bk<T, DI, 64>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+        if (d.Bk == 256) return launch_bk<T, DI, 256>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
+    }
+    return launch_bk<T, DI, 128>(d, qb_lo, qb_cnt, q_idx, k_idx, out, st);
 }
 
 hipError_t launch_index_topk(const LaunchDims& d, int qb_lo, int qb_hi, const void* q_idx, const void* k_idx,

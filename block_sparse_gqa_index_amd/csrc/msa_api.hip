@@ -39,7 +39,14 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     // fp8 index inputs: selection only; fp4 (two values per byte): the forward selection only
     const bool fp8_ok = op == MSA_OP_INDEX || op == kOpLayout || op == MSA_OP_DECODE_INDEX;
     const bool fp4_ok = op == MSA_OP_INDEX || op == kOpLayout;
-    if (d->block_size != 128 || (uses_topk && d->topk > 32) ||
+    // Block sizes: 128 everywhere; 64 and 256 for the selection (bf16, fp32)
+    // and for the attention and KL forward, which take a 256-token block as two
+    // 128-token ones (so at most 16 of them fit the 32 slots).
+    const bool bk_ok = d->block_size == 128 ||
+                       ((d->block_size == 64 || d->block_size == 256) && (d->dtype == MSA_BF16 || d->dtype == MSA_F32) &&
+                        (op == MSA_OP_INDEX || op == kOpLayout) &&
+                        (d->block_size == 64 || op == MSA_OP_INDEX || op == kOpLayout || d->topk <= 16));
+    if (!bk_ok || (uses_topk && d->topk > 32) ||
         (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3) &&
          !(fp4_ok && d->dtype == MSA_FP4_E2M1)) ||
         ((op == MSA_OP_ATTN_BWD || op == MSA_OP_KL_BWD) && d->dtype != MSA_BF16) ||
@@ -70,6 +77,7 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     out->k = uses_topk ? d->topk : 1;
     out->nb = (int)((d->seqlen + 127) / 128);
     out->dtype = d->dtype;
+    out->Bk = d->block_size;
     return MSA_OK;
 }
 

@@ -13,7 +13,8 @@ constexpr int kWindow = 65536;   // query positions per window of the inverted s
 
 // Validated problem sizes (see msa.h for their meaning).
 struct LaunchDims {
-    int B, N, Hkv, G, D, Di, k, nb, dtype;   // dtype: 0 = bf16, 1 = fp32
+    int B, N, Hkv, G, D, Di, k, nb, dtype;   // dtype: 0 = bf16, 1 = fp32 (2 = fp8, 3 = fp4: selection only)
+    int Bk = 128;   // block size of the selection (nb counts 128-token blocks whatever Bk is)
     int Hq() const { return Hkv * G; }
 };
 

@@ -78,7 +78,8 @@ def _kl(lib, d, ptrs=None, ws=None, nws=0):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block_size=64), 3), (dict(topk=0), 2), (dict(topk=33), 3), (dict(dtype=7), 3),
+    (dict(block_size=96), 3), (dict(block_size=512), 3), (dict(block_size=64, dtype=msa.MSA_FP8_E4M3), 3),
+    (dict(block_size=256, dtype=msa.MSA_FP4_E2M1), 3), (dict(topk=0), 2), (dict(topk=33), 3), (dict(dtype=7), 3),
     (dict(causal=0), 3), (dict(index_dim=96), 3), (dict(kv_heads=0), 2), (dict(seqlen=-1), 2),
     (dict(batch=-2), 2), (dict(seqlen=1 << 26), 2),
 ])
@@ -180,7 +181,9 @@ def test_layout_check_arguments(lib):
     chk = lambda d, bi=FAKE, out=FAKE: lib.msa_check_block_idx(ctypes.byref(d), bi, out, None)
     assert chk(_dims(topk=0)) == 2
     assert chk(_dims(topk=33)) == 3
-    assert chk(_dims(block_size=64)) == 3
+    assert chk(_dims(block_size=96)) == 3
+    assert chk(_dims(block_size=64), out=None) == 1     # 64 and 256 are accepted: goes on to the pointers
+    assert chk(_dims(block_size=256), out=None) == 1
     # head and index dims are not read
     assert chk(_dims(head_dim=96, index_dim=96, group_size=3), out=None) == 1
     assert chk(_dims(), bi=None) == 1
