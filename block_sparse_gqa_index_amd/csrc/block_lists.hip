@@ -295,7 +295,108 @@ hipError_t launch_check_block_idx(const LaunchDims& d, const int32_t* block_idx,
     return hipGetLastError();
 }
 
+// ------------------------------------------ other block sizes as 128-blocks --
+
+// A selection at block size 64 or 256, rewritten over 128-token blocks for the
+// attention and KL kernels (which work on 128-token blocks). Per row (b, g, i)
+// with the layout msa_index_topk writes:
+//   Bk = 256: each kept non-local block j -> 128-blocks 2j and 2j + 1; the
+//     local block -> its first half 2L if that precedes the query's own
+//     128-block (fully visible), then the query's 128-block i / 128;
+//   Bk = 64: the kept blocks grouped by 128-block j >> 1, with a mask per
+//     entry (bit 0: first half kept, bit 1: second half kept); the last entry
+//     is the query's 128-block.
+// ids: ascending, -1 padded to ke entries; hmask (Bk = 64) per entry; info per
+// row: bits 0-5 the number of entries before the query's 128-block, bit 6 set
+// unless the first half of the query's 128-block is visible but not kept (a
+// query in the second half whose preceding 64-block was not selected). Rows
+// that break the layout give unspecified ids, but never more than ke of them.
+__global__ __launch_bounds__(256) void expand_blocks_kernel(const int32_t* __restrict__ block_idx,
+                                                            int32_t* __restrict__ ids, uint8_t* __restrict__ hmask,
+                                                            uint8_t* __restrict__ info, int64_t rows, int N, int k,
+                                                            int ke, int Bk) {
+    const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (x >= rows) return;
+    const int i = (int)(x % N);
+    const int L128 = i / kBlock;
+    const int32_t* in = block_idx + x * k;
+    int32_t* out = ids + x * ke;
+    int n = 0;
+    int low_kept = 1;
+    if (Bk == 256) {
+        const int L = i / 256;
+        for (int s = 0; s < k; ++s) {
+            const int j = in[s];
+            if (j >= 0 && j < L && n + 2 <= ke) {
+                out[n++] = 2 * j;
+                out[n++] = 2 * j + 1;
+            }
+        }
+        if (L128 > 2 * L && n < ke) out[n++] = 2 * L;
+        if (n < ke) out[n++] = L128;
+    } else {
+        uint8_t* hm = hmask + x * ke;
+        const int L = i / 64;
+        int cur = -1, m = 0;
+        for (int s = 0; s < k; ++s) {
+            const int j = in[s];
+            if (j < 0 || j > L) continue;
+            if ((j >> 1) != cur) {
+                if (cur >= 0 && n < ke) {
+                    out[n] = cur;
+                    hm[n++] = (uint8_t)m;
+                }
+                cur = j >> 1;
+                m = 0;
+            }
+            m |= 1 << (j & 1);
+        }
+        if (cur >= 0 && n < ke) {
+            out[n] = cur;
+            hm[n++] = (uint8_t)m;
+        }
+        low_kept = (L & 1) == 0 || (m & 1);
+        for (int s = n; s < ke; ++s) hm[s] = 0;
+    }
+    for (int s = n; s < ke; ++s) out[s] = -1;
+    info[x] = (uint8_t)((n > 0 ? n - 1 : 0) | (low_kept ? 64 : 0));
+}
+
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int expanded_topk(const LaunchDims& d) { return d.Bk == 256 ? 2 * d.k : d.k; }
+
+LaunchDims as_128(const LaunchDims& d) {
+    LaunchDims e = d;
+    e.k = expanded_topk(d);
+    e.Bk = 128;
+    return e;
+}
+
+ExpandLayout expand_layout(const LaunchDims& d, size_t base) {
+    ExpandLayout e{};
+    size_t off = align_up(base);
+    if (d.Bk == 128) {
+        e.end = off;
+        return e;
+    }
+    const size_t rows = (size_t)d.B * d.Hkv * d.N;
+    const size_t ke = (size_t)expanded_topk(d);
+    e.ids = off;    off = align_up(off + rows * ke * 4);
+    e.hmask = off;  off = align_up(off + (d.Bk == 64 ? rows * ke : 0));
+    e.info = off;   off = align_up(off + rows);
+    e.end = off;
+    return e;
+}
+
+void launch_expand(const LaunchDims& d, const int32_t* block_idx, unsigned char* ws, const ExpandLayout& E,
+                   hipStream_t st) {
+    const int64_t rows = (int64_t)d.B * d.Hkv * d.N;
+    if (rows == 0) return;
+    hipLaunchKernelGGL(expand_blocks_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, block_idx,
+                       reinterpret_cast<int32_t*>(ws + E.ids), reinterpret_cast<uint8_t*>(ws + E.hmask),
+                       reinterpret_cast<uint8_t*>(ws + E.info), rows, d.N, d.k, expanded_topk(d), d.Bk);
+}
 
 int windows(const LaunchDims& d) { return (d.N + kWindow - 1) / kWindow; }
 

@@ -93,9 +93,11 @@ __device__ __forceinline__ void combine_bit(KlAcc& a) {
 // tokens it holds, and the logarithms and exponentials below run once per
 // token instead of G times. The index scores u are equal in the G lanes (same
 // index query) and are only narrowed the same way.
+// MASK: only keys k_lo .. p_limit of the block are among the row's tokens
+// (the causal limit of the local block; the kept half of a 64-token selection).
 template <int G, bool MASK>
 __device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 (&u)[4], float scale_log2, float lse2,
-                                         float iscale, int p_limit, int half, int hh) {
+                                         float iscale, int p_limit, int half, int hh, int k_lo = 0) {
     constexpr float kLn2 = 0.69314718055994531f;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr int NV = 64 / G;   // tokens per lane after the reduce-scatter
@@ -110,7 +112,7 @@ __device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-            const bool vis = !MASK || key <= p_limit;
+            const bool vis = !MASK || (key <= p_limit && key >= k_lo);
             v[kt * 16 + r] = vis ? exp2_hw(fmaf(s[kt][r], scale_log2, -lse2)) : 0.f;
             uv[kt * 16 + r] = u[kt][r];
         }
@@ -129,7 +131,7 @@ __device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 
     for (int e = 0; e < NV; ++e) {
         const int t = base + e, kt = t >> 4, r = t & 15;
         const int key = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = !MASK || key <= p_limit;
+        const bool vis = !MASK || (key <= p_limit && key >= k_lo);
         const float p = v[e] * (1.0f / G);
         const float uu = uv[e] * iscale;
         uk[e] = vis ? uu : -__builtin_inff();
@@ -156,12 +158,14 @@ __device__ __forceinline__ KlAcc tile_kl(const floatx16 (&s)[4], const floatx16 
     return a;
 }
 
-template <typename T, int D, int DI, int G>
+// HM: each entry keeps only the halves of the block its mask byte names (a
+// selection made with 64-token blocks: bit 0 keys 0-63, bit 1 keys 64-127).
+template <typename T, int D, int DI, int G, bool HM>
 __global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const float* __restrict__ lse, const int32_t* __restrict__ list, const int4* __restrict__ items,
-    const int32_t* __restrict__ total_items, float* __restrict__ part, int N, int Hkv, int nb, int nwin, int KP,
-    float scale_log2, float iscale) {
+    const int32_t* __restrict__ total_items, float* __restrict__ part, const uint8_t* __restrict__ hmask, int N,
+    int Hkv, int nb, int nwin, int KP, float scale_log2, float iscale) {
     constexpr int PPT = 32 / G;
     __shared__ __align__(16) unsigned char lds[SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES];
     unsigned char* lds_i = lds + SwzTile<T, D>::BYTES;
@@ -212,7 +216,13 @@ __global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
         load_q_op<T, D>(bq, qrow(e_nxt), nvalid, half);
         tile_scores<T, DI>(u, bi, lds_i, col, half);
         load_q_op<T, DI>(bi, qirow(e_nxt), nvalid, half);
-        const KlAcc a = tile_kl<G, false>(s, u, scale_log2, lse2, iscale, 0, half, hh);
+        KlAcc a;
+        if constexpr (HM) {
+            const int m = hmask[(((size_t)b * Hkv + g) * N + i) * (KP + 1) + slot];
+            a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, (m & 2) ? 127 : 63, half, hh, (m & 1) ? 0 : 64);
+        } else {
+            a = tile_kl<G, false>(s, u, scale_log2, lse2, iscale, 0, half, hh);
+        }
         if (valid && hh == 0 && half == 0) {
             float* dst = part + ((((size_t)b * Hkv + g) * N + i) * KP + slot) * kKlPart;
             *reinterpret_cast<float4*>(dst) = make_float4(a.A, a.Bs, a.P, a.mu);
@@ -222,11 +232,15 @@ __global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
     }
 }
 
-template <typename T, int D, int DI, int G>
+// XP: the selection was made with another block size and rewritten over
+// 128-token blocks; info (per row) gives the row's number of non-local
+// entries and whether the first half of its own 128-key block is kept.
+template <typename T, int D, int DI, int G, bool XP>
 __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
-    const float* __restrict__ lse, const float* __restrict__ part, float* __restrict__ kl_rows,
-    float* __restrict__ index_lse, int B, int N, int Hkv, int nb, int topk, int KP, float scale_log2, float iscale) {
+    const float* __restrict__ lse, const float* __restrict__ part, const uint8_t* __restrict__ info,
+    float* __restrict__ kl_rows, float* __restrict__ index_lse, int B, int N, int Hkv, int nb, int topk, int KP,
+    float scale_log2, float iscale) {
     __shared__ __align__(16) unsigned char lds[SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES];
     unsigned char* lds_i = lds + SwzTile<T, D>::BYTES;
     const int g = blockIdx.x % Hkv;
@@ -243,13 +257,19 @@ __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, col = lane & 31;
     const int hh = col % G;
-    const int nnl = min(topk - 1, qb);
+    const int nnl_all = min(topk - 1, qb);
     constexpr float kLog2e = 1.4426950408889634f;
     for (int tile = w; tile < kBlock * G / 32; tile += 4) {
         const int p = (tile * 32 + col) / G;
         const int i = q0 + p;
         const bool valid = i < N;
         const int ii = valid ? i : q0;
+        int nnl = nnl_all, klo = 0;
+        if constexpr (XP) {
+            const int x = info[((size_t)b * Hkv + g) * N + ii];
+            nnl = min(x & 63, topk - 1);
+            klo = (x & 64) ? 0 : 64;
+        }
         Op8<T> bq[D / 16];
         load_q_op<T, D>(bq, q + ((size_t)b * N + ii) * Hq * D + (size_t)(g * G + hh) * D, valid, half);
         Op8<T> bi[DI / 16];
@@ -258,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void kl_local_combine_kernel(
         tile_scores<T, D>(s, bq, lds, col, half);
         tile_scores<T, DI>(u, bi, lds_i, col, half);
         const float lse2 = valid ? lse[((size_t)b * Hq + g * G + hh) * N + i] * kLog2e : 0.f;
-        KlAcc a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, p, half, hh);
+        KlAcc a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, p, half, hh, klo);
 
         const float* src = part + (((size_t)b * Hkv + g) * N + ii) * KP * kKlPart;
         for (int sl = 0; sl < nnl; ++sl) {
@@ -482,12 +502,14 @@ static int red_blocks_for(size_t rows) {
     return (int)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
 }
 
-KlWorkspace kl_workspace_layout(const LaunchDims& d) {
+KlWorkspace kl_workspace_layout(const LaunchDims& d0) {
     KlWorkspace w{};
-    w.lists = list_layout(d, 0);
+    w.ex = expand_layout(d0, 0);   // other block sizes: the selection over 128-token blocks first
+    const LaunchDims d = as_128(d0);
+    w.lists = list_layout(d, w.ex.end);
     const size_t rows = (size_t)d.B * d.Hkv * d.N;
     w.red_blocks = red_blocks_for(rows);
-    size_t off = w.lists.has_nonlocal ? w.lists.end : 0;
+    size_t off = w.lists.has_nonlocal ? w.lists.end : w.ex.end;
     w.part = off;  off = align_up(off + (w.lists.has_nonlocal ? w.lists.max_entries * kKlPart * 4 : 0));
     w.red = off;   off = align_up(off + (size_t)w.red_blocks * 8);
     w.bytes = off;
@@ -495,11 +517,19 @@ KlWorkspace kl_workspace_layout(const LaunchDims& d) {
 }
 
 template <typename T, int D, int DI, int G>
-static hipError_t launch_kl_t(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
-                              const void* k_idx, const int32_t* block_idx, const float* lse, float scale,
+static hipError_t launch_kl_t(const LaunchDims& d0, const void* q, const void* k, const void* q_idx,
+                              const void* k_idx, const int32_t* block_idx0, const float* lse, float scale,
                               float iscale, float* kl_rows, float* kl_sum, float* index_lse, unsigned char* ws,
                               hipStream_t st) {
-    const KlWorkspace L = kl_workspace_layout(d);
+    const KlWorkspace L = kl_workspace_layout(d0);
+    // Other block sizes: the rows' selections over 128-token blocks, with the
+    // half masks of 64-token selections.
+    const bool xp = d0.Bk != 128, hm = d0.Bk == 64;
+    const LaunchDims d = as_128(d0);
+    if (xp) launch_expand(d0, block_idx0, ws, L.ex, st);
+    const int32_t* block_idx = xp ? reinterpret_cast<const int32_t*>(ws + L.ex.ids) : block_idx0;
+    const uint8_t* hmask = reinterpret_cast<const uint8_t*>(ws + L.ex.hmask);
+    const uint8_t* info = reinterpret_cast<const uint8_t*>(ws + L.ex.info);
     const float scale_log2 = scale * 1.4426950408889634f;
     const int KP = d.k > 1 ? d.k - 1 : 1;
     const T* tq = static_cast<const T*>(q);
@@ -511,15 +541,26 @@ static hipError_t launch_kl_t(const LaunchDims& d, const void* q, const void* k,
         launch_build_lists(d, 0, d.N, block_idx, ws, L.lists, st);
         part = reinterpret_cast<float*>(ws + L.part);
         const size_t grid = (L.lists.max_items + 63) / 64 * 64;
-        hipLaunchKernelGGL((kl_nonlocal_kernel<T, D, DI, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tqi,
-                           tki, lse, reinterpret_cast<const int32_t*>(ws + L.lists.list),
-                           reinterpret_cast<const int4*>(ws + L.lists.items),
-                           reinterpret_cast<const int32_t*>(ws + L.lists.total), part, d.N, d.Hkv, d.nb,
-                           windows(d), KP, scale_log2, iscale);
+        const int32_t* list = reinterpret_cast<const int32_t*>(ws + L.lists.list);
+        const int4* items = reinterpret_cast<const int4*>(ws + L.lists.items);
+        const int32_t* total = reinterpret_cast<const int32_t*>(ws + L.lists.total);
+        if (hm)
+            hipLaunchKernelGGL((kl_nonlocal_kernel<T, D, DI, G, true>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
+                               tqi, tki, lse, list, items, total, part, hmask, d.N, d.Hkv, d.nb, windows(d), KP,
+                               scale_log2, iscale);
+        else
+            hipLaunchKernelGGL((kl_nonlocal_kernel<T, D, DI, G, false>), dim3((unsigned)grid), dim3(256), 0, st, tq,
+                               tk, tqi, tki, lse, list, items, total, part, hmask, d.N, d.Hkv, d.nb, windows(d), KP,
+                               scale_log2, iscale);
     }
-    hipLaunchKernelGGL((kl_local_combine_kernel<T, D, DI, G>), dim3((unsigned)(d.nb * d.B * d.Hkv)), dim3(256), 0,
-                       st, tq, tk, tqi, tki, lse, part, kl_rows, index_lse, d.B, d.N, d.Hkv, d.nb,
-                       L.lists.has_nonlocal ? d.k : 1, KP, scale_log2, iscale);
+    const dim3 cgrid((unsigned)(d.nb * d.B * d.Hkv));
+    const int kk = L.lists.has_nonlocal ? d.k : 1;
+    if (xp)
+        hipLaunchKernelGGL((kl_local_combine_kernel<T, D, DI, G, true>), cgrid, dim3(256), 0, st, tq, tk, tqi, tki, lse,
+                           part, info, kl_rows, index_lse, d.B, d.N, d.Hkv, d.nb, kk, KP, scale_log2, iscale);
+    else
+        hipLaunchKernelGGL((kl_local_combine_kernel<T, D, DI, G, false>), cgrid, dim3(256), 0, st, tq, tk, tqi, tki,
+                           lse, part, info, kl_rows, index_lse, d.B, d.N, d.Hkv, d.nb, kk, KP, scale_log2, iscale);
     double* red = reinterpret_cast<double*>(ws + L.red);
     const size_t rows = (size_t)d.B * d.Hkv * d.N;
     hipLaunchKernelGGL(kl_reduce_partial, dim3(L.red_blocks), dim3(kRedThreads), 0, st, kl_rows, rows, red);

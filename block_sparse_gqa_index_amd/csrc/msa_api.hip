@@ -44,7 +44,8 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     // 128-token ones (so at most 16 of them fit the 32 slots).
     const bool bk_ok = d->block_size == 128 ||
                        ((d->block_size == 64 || d->block_size == 256) && (d->dtype == MSA_BF16 || d->dtype == MSA_F32) &&
-                        (op == MSA_OP_INDEX || op == kOpLayout) &&
+                        (op == MSA_OP_INDEX || op == kOpLayout || op == MSA_OP_ATTN || op == MSA_OP_KL ||
+                         op == MSA_OP_FORWARD) &&
                         (d->block_size == 64 || op == MSA_OP_INDEX || op == kOpLayout || d->topk <= 16));
     if (!bk_ok || (uses_topk && d->topk > 32) ||
         (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3) &&

@@ -18,6 +18,13 @@ struct LaunchDims {
     int Hq() const { return Hkv * G; }
 };
 
+// A selection at block size 64 or 256 rewritten over 128-token blocks (entries,
+// per-entry half masks for Bk = 64, per-row counts and local-block flag) for
+// the attention and KL kernels; nothing for Bk = 128 (end == base).
+struct ExpandLayout {
+    size_t ids, hmask, info, end;
+};
+
 // Byte offsets (from the workspace base) of the selection-inversion buffers.
 struct ListLayout {
     size_t n_keys, max_entries, max_items;
@@ -28,6 +35,7 @@ struct ListLayout {
 };
 
 struct AttnWorkspace {
+    ExpandLayout ex;   // Bk != 128 only
     ListLayout lists;
     size_t vt, po, plse, bytes;
 };
@@ -39,12 +47,19 @@ struct BwdWorkspace {
 };
 
 struct KlWorkspace {
+    ExpandLayout ex;   // Bk != 128 only
     ListLayout lists;
     size_t part, red, bytes;
     int red_blocks;
 };
 
 ListLayout list_layout(const LaunchDims& d, size_t base, int seg = kSeg, bool sorted = false);
+
+int expanded_topk(const LaunchDims& d);    // entries per row after the rewrite
+LaunchDims as_128(const LaunchDims& d);    // the same problem over 128-token blocks, expanded_topk entries
+ExpandLayout expand_layout(const LaunchDims& d, size_t base);
+void launch_expand(const LaunchDims& d, const int32_t* block_idx, unsigned char* ws, const ExpandLayout& E,
+                   hipStream_t st);
 int windows(const LaunchDims& d);   // kWindow-position windows of the sequence
 
 // Work item handled by work-group x of a key-block-outer launch (grid a

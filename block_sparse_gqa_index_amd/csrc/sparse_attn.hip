@@ -142,16 +142,31 @@ __device__ __forceinline__ void store_partial(T* __restrict__ po, float* __restr
     if (half == 0) plse[pidx * G + hh] = (mz + __log2f(l)) * 0.69314718055994531f;
 }
 
+// Keys of the 128-key block a row keeps when its selection was made with
+// 64-token blocks: bit 0 of the entry's mask keeps keys 0-63 (key tiles 0-1),
+// bit 1 keys 64-127 (tiles 2-3).
+__device__ __forceinline__ void mask_halves(floatx16 (&s)[4], int m) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        const bool keep = (m >> (kt >> 1)) & 1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = keep ? s[kt][r] : -__builtin_inff();
+    }
+}
+
 // One 32-row tile of a non-local work item: the lane's row is list entry `e`
 // (position << 5 | slot); scores against the staged block, softmax, P V and
-// the partial store (skipped for the padding rows past the item's end).
-template <typename T, int D, int G>
+// the partial store (skipped for the padding rows past the item's end). HM:
+// the entry keeps only the halves its mask byte names (64-token selections).
+template <typename T, int D, int G, bool HM>
 __device__ __forceinline__ void nonlocal_tile(const Op8<T> (&qop)[D / 16], int e, bool valid,
                                               const unsigned char* lds, T* __restrict__ po,
                                               float* __restrict__ plse, int b, int g, int N, int Hkv, int KP,
-                                              float scale_log2, int hh, int col, int half) {
+                                              const uint8_t* __restrict__ hmask, float scale_log2, int hh, int col,
+                                              int half) {
     floatx16 s[4];
     tile_scores<T, D>(s, qop, lds, col, half);
+    if constexpr (HM) mask_halves(s, hmask[(((size_t)b * Hkv + g) * N + (e >> 5)) * (KP + 1) + (e & 31)]);
     float mz, l;
     tile_softmax(s, scale_log2, mz, l);
     floatx16 o[D / 32];
@@ -168,11 +183,11 @@ __device__ __forceinline__ void nonlocal_tile(const Op8<T> (&qop)[D / 16], int e
 // positions that kept j). K_j and V_j^T are staged in LDS once; each wave
 // streams 32-row tiles through them, loading the next tile's query rows while
 // the current tile is on the matrix cores.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool HM>
 __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ list, const int4* __restrict__ items, const int32_t* __restrict__ total_items,
-    const T* __restrict__ vt, T* __restrict__ po, float* __restrict__ plse, int N, int Hkv, int nb, int nwin,
-    int KP, float scale_log2) {
+    const T* __restrict__ vt, T* __restrict__ po, float* __restrict__ plse, const uint8_t* __restrict__ hmask, int N,
+    int Hkv, int nb, int nwin, int KP, float scale_log2) {
     using KV = KVTile<T, D>;
     constexpr int PPT = 32 / G;   // positions per 32-row tile
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
@@ -213,13 +228,13 @@ __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     for (; base < count; base += 2 * stride) {
         load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, base + stride + pp < count, half);
         const int e_2 = list[start + min(base + 2 * stride + pp, count - 1)];
-        nonlocal_tile<T, D, G>(q_cur, e_cur, base + pp < count, lds, po, plse, b, g, N, Hkv, KP, scale_log2, hh,
-                               col, half);
+        nonlocal_tile<T, D, G, HM>(q_cur, e_cur, base + pp < count, lds, po, plse, b, g, N, Hkv, KP, hmask,
+                                   scale_log2, hh, col, half);
         if (base + stride >= count) break;
         load_q_op<T, D>(q_cur, qbase + (size_t)(e_2 >> 5) * Hq * D, base + 2 * stride + pp < count, half);
         const int e_3 = list[start + min(base + 3 * stride + pp, count - 1)];
-        nonlocal_tile<T, D, G>(q_nxt, e_nxt, base + stride + pp < count, lds, po, plse, b, g, N, Hkv, KP,
-                               scale_log2, hh, col, half);
+        nonlocal_tile<T, D, G, HM>(q_nxt, e_nxt, base + stride + pp < count, lds, po, plse, b, g, N, Hkv, KP,
+                                   hmask, scale_log2, hh, col, half);
         e_cur = e_2;
         e_nxt = e_3;
     }
@@ -265,11 +280,14 @@ struct PartialRow {
 // possible slots are requested before the local block's math and kept in
 // registers (the loops over slots are unrolled, predicated on the row's slot
 // count); the partial outputs are fetched two slots at a time.
-template <typename T, int D, int G, int SL>
+// XP: the selection was made with another block size and rewritten over
+// 128-token blocks; info (per row) gives the row's number of non-local
+// entries and whether the first half of its own 128-key block is kept.
+template <typename T, int D, int G, int SL, bool XP>
 __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt, const T* __restrict__ po,
-    const float* __restrict__ plse, T* __restrict__ o, float* __restrict__ lse, int B, int N, int Hkv, int nb,
-    int qb_lo, int topk, int KP, float scale_log2) {
+    const float* __restrict__ plse, const uint8_t* __restrict__ info, T* __restrict__ o, float* __restrict__ lse,
+    int B, int N, int Hkv, int nb, int qb_lo, int topk, int KP, float scale_log2) {
     using KV = KVTile<T, D>;
     constexpr int BATCH = 2;
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
@@ -289,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
     const int half = lane >> 5, col = lane & 31;
     const int hh = col % G;
     const int h = g * G + hh;
-    const int nnl = min(topk - 1, qb);         // non-local slots of every row here
+    const int nnl_all = min(topk - 1, qb);     // non-local slots of every row here (Bk = 128)
     constexpr float kLog2e = 1.4426950408889634f;
 
     for (int tile = w; tile < kBlock * G / 32; tile += 4) {
@@ -297,6 +315,12 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
         const int i = q0 + p;
         const bool valid = i < N;
         const int ii = valid ? i : q0;
+        int nnl = nnl_all, klo = 0;
+        if constexpr (XP) {
+            const int x = info[((size_t)b * Hkv + g) * N + ii];
+            nnl = min(x & 63, topk - 1);
+            klo = (x & 64) ? 0 : 64;
+        }
         Op8<T> bq[D / 16];
         load_q_op<T, D>(bq, q + ((size_t)b * N + ii) * Hq * D + (size_t)h * D, valid, half);
         const size_t prow = (((size_t)b * Hkv + g) * N + ii) * KP;
@@ -312,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void attn_local_combine_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                if (key > p) s[kt][r] = -__builtin_inff();
+                if (key > p || key < klo) s[kt][r] = -__builtin_inff();
             }
         }
         float mz, l;
@@ -381,23 +405,33 @@ static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 AttnWorkspace attn_workspace_layout(const LaunchDims& d) {
     AttnWorkspace w{};
     const size_t es = d.dtype == 0 ? 2 : 4;
-    size_t off = 0;
-    w.vt = off;    off = align_up(off + (size_t)d.B * d.Hkv * d.nb * d.D * kBlock * es);
-    w.lists = list_layout(d, off);
+    w.ex = expand_layout(d, 0);   // other block sizes: the selection over 128-token blocks first
+    const LaunchDims e = as_128(d);
+    size_t off = w.ex.end;
+    w.vt = off;    off = align_up(off + (size_t)e.B * e.Hkv * e.nb * e.D * kBlock * es);
+    w.lists = list_layout(e, off);
     if (w.lists.has_nonlocal) {
         off = w.lists.end;
-        w.po = off;    off = align_up(off + w.lists.max_entries * d.G * d.D * es);
-        w.plse = off;  off = align_up(off + w.lists.max_entries * d.G * 4);
+        w.po = off;    off = align_up(off + w.lists.max_entries * e.G * e.D * es);
+        w.plse = off;  off = align_up(off + w.lists.max_entries * e.G * 4);
     }
     w.bytes = off;
     return w;
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_attn_t(const LaunchDims& d, int qb_lo, int qb_hi, const void* q, const void* k,
-                                const int32_t* block_idx, float scale, void* o, float* lse, unsigned char* ws,
+static hipError_t launch_attn_t(const LaunchDims& d0, int qb_lo, int qb_hi, const void* q, const void* k,
+                                const int32_t* block_idx0, float scale, void* o, float* lse, unsigned char* ws,
                                 int stages, hipStream_t st) {
-    const AttnWorkspace L = attn_workspace_layout(d);
+    const AttnWorkspace L = attn_workspace_layout(d0);
+    // Other block sizes: the rows' selections over 128-token blocks (rewritten
+    // by the first stage), with the half masks of 64-token selections.
+    const bool xp = d0.Bk != 128, hm = d0.Bk == 64;
+    const LaunchDims d = as_128(d0);
+    const int32_t* block_idx = xp ? reinterpret_cast<const int32_t*>(ws + L.ex.ids) : block_idx0;
+    const uint8_t* hmask = reinterpret_cast<const uint8_t*>(ws + L.ex.hmask);
+    const uint8_t* info = reinterpret_cast<const uint8_t*>(ws + L.ex.info);
+    if (xp && (stages & 1)) launch_expand(d0, block_idx0, ws, L.ex, st);
     const float scale_log2 = scale * 1.4426950408889634f;
     const int KP = d.k > 1 ? d.k - 1 : 1;
     const T* tq = static_cast<const T*>(q);
@@ -416,23 +450,36 @@ static hipError_t launch_attn_t(const LaunchDims& d, int qb_lo, int qb_hi, const
         po = reinterpret_cast<T*>(ws + L.po);
         plse = reinterpret_cast<float*>(ws + L.plse);
         const size_t grid = (list_items_bound(d, p_lo, p_hi, L.lists) + 63) / 64 * 64;
-        if (stages & 2)
-            hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
-                               list, items, total, vt, po, plse, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
+        if ((stages & 2) && hm)
+            hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G, true>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
+                               list, items, total, vt, po, plse, hmask, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
+        else if (stages & 2)
+            hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G, false>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
+                               list, items, total, vt, po, plse, hmask, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
     }
     if (stages & 4) {
         const dim3 grid((unsigned)((qb_hi - qb_lo) * d.B * d.Hkv));
         const int kk = nonlocal ? d.k : 1;
         T* to = static_cast<T*>(o);
-        if (kk <= 8)
-            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 7>), grid, dim3(256), 0, st, tq, tk, vt, po, plse,
-                               to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+        if (xp) {
+            if (kk <= 8)
+                hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 7, true>), grid, dim3(256), 0, st, tq, tk, vt,
+                                   po, plse, info, to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+            else if (kk <= 16)
+                hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 15, true>), grid, dim3(256), 0, st, tq, tk, vt,
+                                   po, plse, info, to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+            else
+                hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 31, true>), grid, dim3(256), 0, st, tq, tk, vt,
+                                   po, plse, info, to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+        } else if (kk <= 8)
+            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 7, false>), grid, dim3(256), 0, st, tq, tk, vt, po,
+                               plse, info, to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
         else if (kk <= 16)
-            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 15>), grid, dim3(256), 0, st, tq, tk, vt, po, plse,
-                               to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 15, false>), grid, dim3(256), 0, st, tq, tk, vt, po,
+                               plse, info, to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
         else
-            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 31>), grid, dim3(256), 0, st, tq, tk, vt, po, plse,
-                               to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
+            hipLaunchKernelGGL((attn_local_combine_kernel<T, D, G, 31, false>), grid, dim3(256), 0, st, tq, tk, vt, po,
+                               plse, info, to, lse, d.B, d.N, d.Hkv, d.nb, qb_lo, kk, KP, scale_log2);
     }
     return hipGetLastError();
 }

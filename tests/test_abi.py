@@ -89,7 +89,8 @@ def test_index_rejects_bad_dims(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), 3), (dict(group_size=3), 3), (dict(group_size=64), 3),
-    (dict(block_size=256), 3), (dict(topk=40), 3), (dict(group_size=0), 2),
+    (dict(block_size=256, topk=17), 3), (dict(block_size=96), 3), (dict(block_size=64, dtype=msa.MSA_FP8_E4M3), 3),
+    (dict(topk=40), 3), (dict(group_size=0), 2),
     # (batch, group, 64K-position window, key block) keys past 2^31 - 1
     (dict(kv_heads=16, seqlen=1 << 25, topk=2), 2),
 ])
