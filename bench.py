@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 import block_sparse_gqa_index_amd as msa  # noqa: E402
 from synth import (CONFIGS, DECODE_CONFIGS, make_decode_inputs, make_grad_output, make_inputs,  # noqa: E402
-                   sample_rows)
+                   make_row_weights, sample_rows)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and MFMA)
@@ -473,6 +473,8 @@ def main():
                          "(reported beside the bf16 headline, never as it)")
     ap.add_argument("--bwd", action="store_true",
                     help="also time the main-branch backward (msa_sparse_attn_bwd) on the step's outputs")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="with --bwd --kl: time only the fused backward (msa_fused_bwd), not the separate ones")
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step (64 sequences, 128K-token caches) instead of the forward")
     ap.add_argument("--decode-queries", type=int, default=1,
@@ -640,6 +642,39 @@ def main():
             "speedup_vs_bf16_index": stage_ms[index_kernel] / idx8,
             "ms_per_step": ms8, "tokens_per_s": tokens / (ms8 * 1e-3),
             "same_selection": bool(torch.equal(bi8, block_idx))}
+    if args.bwd and args.kl:
+        # Both branches' gradients from one pass (msa_fused_bwd), query window by query window.
+        log("[bench] fused backward of both branches")
+        dout_f = make_grad_output(w, device=dev)
+        wr_f = make_row_weights(w, device=dev)
+        ilse_f = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev)
+        kws_f = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_KL)), dtype=torch.uint8, device=dev)
+        msa.kl_align_fwd(x["q"], x["k"], x["q_idx"], x["k_idx"], block_idx, lse, index_lse=ilse_f, workspace=kws_f)
+        del kws_f
+        fws = torch.empty(max(1, msa.workspace_bytes(dims, msa.MSA_OP_FUSED_BWD)), dtype=torch.uint8, device=dev)
+        fouts = [torch.empty_like(t) for t in (x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"])]
+
+        def fused():
+            msa.fused_bwd(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], block_idx, o, lse, ilse_f, dout_f,
+                          dkl_rows=wr_f, dq=fouts[0], dk=fouts[1], dv=fouts[2], dq_idx=fouts[3], dk_idx=fouts[4],
+                          workspace=fws)
+        fused()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(1, args.steps))]
+        for e in fev:
+            e[0].record(stream)
+            fused()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        fms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+        fb = 2.5 * f_main + kl_backward_flops(w) - 2.0 * w.head_dim * B * Hkv * G * float(
+            ((np.minimum(w.topk, np.arange(N) // w.block_size + 1) - 1) * w.block_size + np.arange(N) % w.block_size
+             + 1).sum())   # the teacher's scores are the main branch's: counted once
+        out["fused_backward"] = {"ms": fms, "algorithmic_tflop": fb / 1e12, "tflops": fb / (fms * 1e-3) / 1e12,
+                                 "frac_of_peak": fb / (fms * 1e-3) / 1e12 / peak,
+                                 "workspace_gb": fws.numel() / 1e9, "tokens_per_s": tokens / (fms * 1e-3)}
+        del fws, fouts
+        if args.fused_only:
+            args.bwd = False
     if args.bwd:
         log("[bench] main-branch backward")
         dout = make_grad_output(w, device=dev)

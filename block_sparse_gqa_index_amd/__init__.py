@@ -17,6 +17,8 @@ Entry points (same names as the C ABI, without the ``msa_`` prefix):
   kl_align_bwd(q, k, q_idx, k_idx, block_idx, lse, index_lse) -> (dq_idx, dk_idx), bf16
   forward(q_idx, k_idx, q, k, v, topk)             -> (block_idx, o, lse): selection, then attention
   sparse_attn_bwd(q, k, v, block_idx, o, lse, dout) -> (dq, dk, dv), bf16
+  fused_bwd(q, k, v, q_idx, k_idx, block_idx, o, lse, index_lse, dout)
+                                                   -> (dq, dk, dv, dq_idx, dk_idx): both branches in one pass
   decode_index_topk(q_idx, k_idx, seqlens, topk)   -> block_idx int32 [B, Hkv, k] (one new query per sequence;
                                                       q_idx [B, R, Hkv, Di]: R new queries -> [B, Hkv, R, k])
   decode_attn(q, k, v, seqlens, block_idx)         -> (o [B,Hq,D], lse fp32 [B,Hq]) (or [B,R,Hq,D], [B,Hq,R])
@@ -39,6 +41,7 @@ MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP4_E2M1 = 0, 1, 2, 3
 FP4 = torch.float4_e2m1fn_x2   # two OCP e2m1 values per byte, element 2c in the low nibble
 MSA_OP_INDEX, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_FORWARD, MSA_OP_ATTN_BWD, MSA_OP_KL_BWD = 0, 1, 2, 3, 4, 5
 MSA_OP_DECODE_INDEX, MSA_OP_DECODE_ATTN, MSA_OP_DECODE, MSA_OP_DENSE_ATTN, MSA_OP_DENSE_KL = 6, 7, 8, 9, 10
+MSA_OP_FUSED_BWD = 11
 STAGE_PREPARE, STAGE_NONLOCAL, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_UNSUPPORTED",
           4: "MSA_ERR_ALIGN", 5: "MSA_ERR_WORKSPACE", 6: "MSA_ERR_HIP", 7: "MSA_ERR_SCRATCH"}
@@ -47,7 +50,7 @@ EXPORTS = ("msa_index_topk", "msa_check_block_idx", "msa_sparse_attn_fwd", "msa_
            "msa_forward", "msa_sparse_attn_bwd", "msa_kl_align_fwd", "msa_kl_align_bwd",
            "msa_decode_index_topk", "msa_decode_attn", "msa_decode", "msa_dense_attn_fwd",
            "msa_dense_kl_align_fwd", "msa_decode_paged_index_topk", "msa_decode_paged_attn", "msa_decode_paged",
-           "msa_decode_workspace_bytes", "msa_decode_noalloc",
+           "msa_decode_workspace_bytes", "msa_decode_noalloc", "msa_fused_bwd",
            "msa_workspace_bytes", "msa_strerror", "msa_abi_version")
 
 
@@ -94,6 +97,9 @@ def load_library(path: str = LIB_PATH):
     lib.msa_decode_attn.argtypes = [dp, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.msa_decode_noalloc.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
+    fl = ctypes.c_float
+    lib.msa_fused_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, fl, fl, vp, fl, vp, vp, vp, vp, vp, vp,
+                                  sz, vp]
     lib.msa_decode_workspace_bytes.argtypes = [dp, ctypes.c_int, i32]
     lib.msa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_dense_attn_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
@@ -112,7 +118,7 @@ def load_library(path: str = LIB_PATH):
               lib.msa_kl_align_fwd, lib.msa_forward, lib.msa_kl_align_bwd, lib.msa_sparse_attn_bwd,
               lib.msa_decode_index_topk, lib.msa_decode_attn, lib.msa_decode, lib.msa_dense_attn_fwd,
               lib.msa_dense_kl_align_fwd, lib.msa_decode_paged_index_topk, lib.msa_decode_paged_attn,
-              lib.msa_decode_paged, lib.msa_decode_noalloc):
+              lib.msa_decode_paged, lib.msa_decode_noalloc, lib.msa_fused_bwd):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -304,6 +310,43 @@ def _kl_input_shapes(q, k, q_idx, k_idx, lse, block_idx):
     _req(k_idx, "k_idx", shape=(B, N, Di), device=q.device)
     _req(lse, "lse", shape=(B, Hq, N), device=q.device)
     _req(block_idx, "block_idx", shape=(B, Hkv, N, block_idx.shape[3]), device=q.device)
+
+
+def fused_bwd(q, k, v, q_idx, k_idx, block_idx, o, lse, index_lse, dout, softmax_scale=0.0, index_scale=0.0,
+              dkl_rows=None, kl_weight=1.0, dq=None, dk=None, dv=None, dq_idx=None, dk_idx=None, workspace=None,
+              block_size=128):
+    """Both branches' gradients in one pass (msa_fused_bwd, bf16): the main
+    branch's (dq, dk, dv) for <dout, o> and the KL term's (dq_idx, dk_idx) for
+    sum_rows w_row KL_row -> (dq, dk, dv, dq_idx, dk_idx). o, lse come from
+    sparse_attn_fwd and index_lse from kl_align_fwd on the same inputs."""
+    lib = load_library()
+    _req(q, "q", ndim=4)
+    B, N, Hq, D = q.shape
+    Hkv, Di = q_idx.shape[2], q_idx.shape[3]
+    _kl_input_shapes(q, k, q_idx, k_idx, lse, block_idx)
+    topk = block_idx.shape[3]
+    for name, t in (("k", k), ("v", v), ("q_idx", q_idx), ("k_idx", k_idx), ("o", o), ("dout", dout)):
+        _req(t, name, dtype=q.dtype)
+    _req(v, "v", shape=k.shape, device=q.device)
+    _req(o, "o", shape=q.shape, device=q.device)
+    _req(dout, "dout", shape=q.shape, device=q.device)
+    _req(block_idx, "block_idx", dtype=torch.int32)
+    _req(lse, "lse", dtype=torch.float32)
+    _req(index_lse, "index_lse", dtype=torch.float32, shape=(B, Hkv, N), device=q.device)
+    if dkl_rows is not None:
+        _req(dkl_rows, "dkl_rows", dtype=torch.float32, shape=(B, Hkv, N), device=q.device)
+    dims = make_dims(B, N, Hkv, Hq // Hkv, D, Di, topk, q.dtype, block_size)
+    outs = []
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v), ("dq_idx", dq_idx, q_idx), ("dk_idx", dk_idx, k_idx)):
+        t = torch.empty_like(ref) if t is None else t
+        _req(t, name, dtype=q.dtype, shape=ref.shape, device=q.device)
+        outs.append(t)
+    ws, nws = _workspace(workspace_bytes(dims, MSA_OP_FUSED_BWD), q.device, workspace)
+    _check(lib.msa_fused_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                             _ptr(o), _ptr(lse), _ptr(index_lse), _ptr(dout), float(softmax_scale),
+                             float(index_scale), _ptr(dkl_rows), float(kl_weight), *[_ptr(t) for t in outs],
+                             _ptr(ws), nws, _stream(q.device)))
+    return tuple(outs)
 
 
 def kl_align_fwd(q, k, q_idx, k_idx, block_idx, lse, softmax_scale=0.0, index_scale=0.0,

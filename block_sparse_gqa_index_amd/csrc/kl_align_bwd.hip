@@ -117,26 +117,6 @@ __device__ __forceinline__ void kl_stage_store(const KlUnit& su, KlTile<D, DI>& 
     }
 }
 
-// Teacher of the row in accumulator r: the mean of P over the G rows of the
-// same position. Rows 8*(r/4) + 4h + r%4 of position m / G: the G rows of a
-// position are aligned groups of min(G, 16) accumulators (G <= 4 within one
-// half-wave's group of four), the other half-wave holding the rest for G >= 8.
-template <int G>
-__device__ __forceinline__ void head_mean(float (&p)[16]) {
-    constexpr int GS = G >= 32 ? 16 : (G >= 16 ? 8 : (G >= 4 ? 4 : G));
-    float t[16];
-#pragma unroll
-    for (int r0 = 0; r0 < 16; r0 += GS) {
-        float a = 0.f;
-#pragma unroll
-        for (int x = 0; x < GS; ++x) a += p[r0 + x];
-        if constexpr (G >= 8) a += swap_halves(a);
-#pragma unroll
-        for (int x = 0; x < GS; ++x) t[r0 + x] = a * (1.f / G);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = t[r];
-}
 
 template <int D, int DI, int G, bool LOCAL>
 __global__ __launch_bounds__(256, 1) void kl_bwd_kernel(
@@ -471,7 +451,7 @@ static hipError_t launch_kl_bwd_t(const LaunchDims& d, const void* q, const void
                        d.Hkv, d.nb, nwin, kSegBwd, local_base, nonlocal ? 1 : 0);
     const int64_t units = (int64_t)d.B * d.Hkv * d.N * (DI / 16);
     hipLaunchKernelGGL((dq_combine_kernel<DI, 1>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, dqi_part,
-                       static_cast<bf16_t*>(dq_idx), units, d.N, d.Hkv, d.k);
+                       static_cast<bf16_t*>(dq_idx), units, d.N, d.Hkv, d.k, 0, d.N, d.N);
     return hipGetLastError();
 }
 

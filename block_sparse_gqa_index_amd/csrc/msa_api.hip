@@ -50,7 +50,7 @@ int check_dims(const msa_dims* d, int op, LaunchDims* out) {
     if (!bk_ok || (uses_topk && d->topk > 32) ||
         (d->dtype != MSA_BF16 && d->dtype != MSA_F32 && !(fp8_ok && d->dtype == MSA_FP8_E4M3) &&
          !(fp4_ok && d->dtype == MSA_FP4_E2M1)) ||
-        ((op == MSA_OP_ATTN_BWD || op == MSA_OP_KL_BWD) && d->dtype != MSA_BF16) ||
+        ((op == MSA_OP_ATTN_BWD || op == MSA_OP_KL_BWD || op == MSA_OP_FUSED_BWD) && d->dtype != MSA_BF16) ||
         d->causal != 1 || (uses_heads && (!pow2_upto32(d->group_size) || (d->head_dim != 64 && d->head_dim != 128))) ||
         (uses_index && d->index_dim != 64 && d->index_dim != 128))
         return MSA_ERR_UNSUPPORTED;
@@ -181,7 +181,7 @@ const char* msa_strerror(int status) {
 
 size_t msa_workspace_bytes(const msa_dims* dims, int op) {
     LaunchDims L;
-    if (op < MSA_OP_INDEX || op > MSA_OP_DENSE_KL) return 0;
+    if (op < MSA_OP_INDEX || op > MSA_OP_FUSED_BWD) return 0;
     if (check_dims(dims, op, &L) != MSA_OK || empty(L)) return 0;
     switch (op) {
         case MSA_OP_INDEX: return 0;
@@ -195,6 +195,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, int op) {
         case MSA_OP_DENSE_ATTN: return msa::dense_workspace_bytes(L);
         case MSA_OP_DENSE_KL: return msa::dense_kl_workspace_bytes(L);
         case MSA_OP_DECODE: return decode_ws(L, op, 1);
+        case MSA_OP_FUSED_BWD: return msa::fused_bwd_workspace_layout(L).bytes;
         default: return 0;
     }
 }
@@ -329,6 +330,46 @@ int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k, const v
     return hip_status(msa::launch_kl_align_bwd(L, q, k, q_idx, k_idx, block_idx, lse, index_lse, scale, iscale,
                                                dkl_rows, kl_weight, dq_idx, dk_idx, ws,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int msa_fused_bwd(const msa_dims* dims, const void* q, const void* k, const void* v, const void* q_idx,
+                  const void* k_idx, const int32_t* block_idx, const void* o, const float* lse, const float* index_lse,
+                  const void* dout, float softmax_scale, float index_scale, const float* dkl_rows, float kl_weight,
+                  void* dq, void* dk, void* dv, void* dq_idx, void* dk_idx, void* ws, size_t ws_bytes, void* stream) {
+    LaunchDims L;
+    int st = check_dims(dims, MSA_OP_FUSED_BWD, &L);
+    if (st != MSA_OK) return st;
+    if (empty(L)) return MSA_OK;
+    if (!q || !k || !v || !q_idx || !k_idx || !block_idx || !o || !lse || !index_lse || !dout || !dq || !dk || !dv ||
+        !dq_idx || !dk_idx)
+        return MSA_ERR_NULL;
+    for (const void* p : {q, k, v, q_idx, k_idx, (const void*)block_idx, o, (const void*)lse, (const void*)index_lse,
+                          dout, (const void*)dkl_rows, (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)dq_idx, (const void*)dk_idx})
+        if (!aligned16(p)) return MSA_ERR_ALIGN;
+    const size_t need = msa::fused_bwd_workspace_layout(L).bytes;
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
+    msa::FusedBwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.o = o;
+    a.dout = dout;
+    a.block_idx = block_idx;
+    a.lse = lse;
+    a.index_lse = index_lse;
+    a.dkl_rows = dkl_rows;
+    a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    a.iscale = index_scale > 0.f ? index_scale : 1.0f / sqrtf((float)L.Di);
+    a.kl_weight = kl_weight;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dq_idx = dq_idx;
+    a.dk_idx = dk_idx;
+    return hip_status(msa::launch_fused_bwd(L, a, ws, static_cast<hipStream_t>(stream)));
 }
 
 int msa_dense_attn_fwd(const msa_dims* dims, const void* q, const void* k, const void* v, float softmax_scale,

@@ -43,6 +43,27 @@ struct BwdItem {
     }
 };
 
+// Teacher of the row in accumulator r: the mean of P over the G rows of the
+// same position. Rows 8*(r/4) + 4h + r%4 of position m / G: the G rows of a
+// position are aligned groups of min(G, 16) accumulators (G <= 4 within one
+// half-wave's group of four), the other half-wave holding the rest for G >= 8.
+template <int G>
+__device__ __forceinline__ void head_mean(float (&p)[16]) {
+    constexpr int GS = G >= 32 ? 16 : (G >= 16 ? 8 : (G >= 4 ? 4 : G));
+    float t[16];
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += GS) {
+        float a = 0.f;
+#pragma unroll
+        for (int x = 0; x < GS; ++x) a += p[r0 + x];
+        if constexpr (G >= 8) a += swap_halves(a);
+#pragma unroll
+        for (int x = 0; x < GS; ++x) t[r0 + x] = a * (1.f / G);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = t[r];
+}
+
 // Per row: the sum of its slots' bf16 partials in slot order (dQ, with G heads
 // of D dims per row; the KL term's dq_idx, with G = 1 and D = Di). A slot's
 // partial is G * D contiguous stored elements; thread t of a row sums the
@@ -51,23 +72,27 @@ struct BwdItem {
 // chunks or whole 128-byte halves of rows) and no line is split between them.
 // Stored element 16*qg + r of a head is dim 32*(qg/2) + 8*(r/4) + 4*(qg%2) + r%4
 // (the lane-major order of the partials).
+// The rows handled are positions p0 .. p0 + len - 1 of every (b, g), whose
+// partials sit at row (b * Hkv + g) * wrows + (i - p0) of dq_part (a window of
+// wrows positions; p0 = 0 and len = wrows = N for the whole sequence).
 template <int D, int G>
 __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restrict__ dq_part, bf16_t* __restrict__ dq,
-                                                         int64_t units, int N, int Hkv, int topk) {
+                                                         int64_t units, int N, int Hkv, int topk, int p0, int len,
+                                                         int wrows) {
     constexpr int SPAN = G * D;      // stored elements per (row, slot)
     constexpr int TPR = SPAN / 16;   // threads per row
     const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (x >= units) return;
     const int t = (int)(x % TPR);
-    const int64_t row = x / TPR;   // (b * Hkv + g) * N + i
-    const int i = (int)(row % N);
-    const int64_t bg = row / N;
+    const int64_t wr = x / TPR;   // (b * Hkv + g) * len + (i - p0)
+    const int i = p0 + (int)(wr % len);
+    const int64_t bg = wr / len;
     const int g = (int)(bg % Hkv), b = (int)(bg / Hkv);
     const int nv = min(topk, i / kBlock + 1);
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const bf16_t* src = dq_part + (size_t)row * topk * SPAN;
+    const bf16_t* src = dq_part + ((size_t)bg * wrows + (i - p0)) * topk * SPAN;
     for (int s = 0; s < nv; ++s) {
         const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)s * SPAN + 8 * t));
         const u32x4 c =

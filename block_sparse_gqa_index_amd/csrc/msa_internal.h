@@ -123,6 +123,28 @@ hipError_t launch_kl_align_bwd(const LaunchDims& d, const void* q, const void* k
                                const float* index_lse, float scale, float index_scale, const float* dkl_rows,
                                float kl_weight, void* dq_idx, void* dk_idx, void* ws, hipStream_t st);
 
+// Dl = <dO, O> per (b, h, i) row in fp32 ([B, Hq, N]).
+void launch_bwd_delta(const LaunchDims& d, const void* o, const void* dout, float* dl, hipStream_t st);
+
+// Fused backward of both branches (bf16): dq, dk, dv of the main branch for
+// <dO, O> and dq_idx, dk_idx of the KL term for sum_rows w_row KL_row, query
+// window by query window of kWindow positions.
+struct FusedBwdArgs {
+    const void *q, *k, *v, *q_idx, *k_idx, *o, *dout;
+    const int32_t* block_idx;
+    const float *lse, *index_lse, *dkl_rows;
+    float scale, iscale, kl_weight;
+    void *dq, *dk, *dv, *dq_idx, *dk_idx;
+};
+struct FusedBwdWorkspace {
+    ListLayout lists;   // position-sorted, kSegBwd entries per item, for the whole sequence
+    size_t kt, kit, dl, dq_part, dqi_part, dkv_part, dki_part, acc_dkv, acc_dki, bytes;
+    int bound;          // non-local work-item slots per (b, g) and window
+    size_t items;       // partial slots of one window: non-local, then local
+};
+FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d);
+hipError_t launch_fused_bwd(const LaunchDims& d, const FusedBwdArgs& a, void* ws, hipStream_t st);
+
 // Dense causal attention (every visible key kept): V^T copy into ws, then the
 // query-block-outer kernel. ws holds dense_workspace_bytes(d).
 size_t dense_workspace_bytes(const LaunchDims& d);

@@ -462,6 +462,16 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* __restrict
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+void launch_bwd_delta(const LaunchDims& d, const void* o, const void* dout, float* dl, hipStream_t st) {
+    const int64_t rows = (int64_t)d.B * d.N * d.Hq();
+    if (d.D == 128)
+        hipLaunchKernelGGL((bwd_delta_kernel<128>), dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), dl, rows, d.N, d.Hq());
+    else
+        hipLaunchKernelGGL((bwd_delta_kernel<64>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), dl, rows, d.N, d.Hq());
+}
+
 BwdWorkspace bwd_workspace_layout(const LaunchDims& d) {
     BwdWorkspace w{};
     size_t off = 0;
@@ -519,7 +529,7 @@ static hipError_t launch_bwd_t(const LaunchDims& d, const void* q, const void* k
                        nwin, kSegBwd, local_base, nonlocal ? 1 : 0);
     const int64_t units = (int64_t)d.B * d.Hkv * d.N * G * (D / 16);
     hipLaunchKernelGGL((dq_combine_kernel<D, G>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, dq_part,
-                       static_cast<bf16_t*>(dq), units, d.N, d.Hkv, d.k);
+                       static_cast<bf16_t*>(dq), units, d.N, d.Hkv, d.k, 0, d.N, d.N);
     return hipGetLastError();
 }
 

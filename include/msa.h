@@ -64,7 +64,8 @@ enum msa_dtype { MSA_BF16 = 0, MSA_F32 = 1, MSA_FP8_E4M3 = 2, MSA_FP4_E2M1 = 3 }
 /* Selector for msa_workspace_bytes. */
 enum msa_op {
     MSA_OP_INDEX = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_FORWARD = 3, MSA_OP_ATTN_BWD = 4, MSA_OP_KL_BWD = 5,
-    MSA_OP_DECODE_INDEX = 6, MSA_OP_DECODE_ATTN = 7, MSA_OP_DECODE = 8, MSA_OP_DENSE_ATTN = 9, MSA_OP_DENSE_KL = 10
+    MSA_OP_DECODE_INDEX = 6, MSA_OP_DECODE_ATTN = 7, MSA_OP_DECODE = 8, MSA_OP_DENSE_ATTN = 9, MSA_OP_DENSE_KL = 10,
+    MSA_OP_FUSED_BWD = 11
 };
 
 enum msa_status {
@@ -278,6 +279,40 @@ MSA_API int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k,
                              const float* index_lse, float softmax_scale, float index_scale,
                              const float* dkl_rows, float kl_weight, void* dq_idx, void* dk_idx, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * Fused backward of both branches: msa_sparse_attn_bwd's dq, dk, dv (main
+ * branch, loss <dO, O>) and msa_kl_align_bwd's dq_idx, dk_idx (KL term, loss
+ * sum_rows w_row KL_row, teacher held fixed) from one pass over the selected
+ * blocks, in which the main-branch scores and probabilities are computed once
+ * and serve both the main gradient and the teacher.
+ * Defined by the Flash-MSA article (tech.kuratif.com), paragraph on the
+ * backward (proxy and main attention gradients fused, over the cached block
+ * indices, linear in N) and "Accelerating Million-Token Training with Sparse
+ * Attention Kernels" (DeepHorus: the fused backward is what makes training at
+ * a million tokens possible); the functions differentiated are those of
+ * msa_sparse_attn_fwd and msa_kl_align_fwd (MSA article, 7minutos.es).
+ *
+ *   Uses every field of `dims`; dtype MSA_BF16 and block_size 128 only.
+ *   q, k, v, q_idx, k_idx, block_idx, softmax_scale, index_scale as for the
+ *             forward calls; o, lse: msa_sparse_attn_fwd's outputs; index_lse:
+ *             msa_kl_align_fwd's; dout [B, N, Hq, D] bf16; dkl_rows, kl_weight
+ *             as for msa_kl_align_bwd (row weights w_row = kl_weight *
+ *             (dkl_rows ? dkl_rows[row] : 1)).
+ *   dq [B, N, Hq, D], dk, dv [B, N, Hkv, D], dq_idx [B, N, Hkv, Di],
+ *   dk_idx [B, N, Di]  OUTPUTS bf16 (every element written; keys no row
+ *             selects get 0).
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_FUSED_BWD) bytes. The
+ *             query rows are processed 65,536 positions at a time, so the
+ *             per-(row, slot) partials never exceed one such window: about
+ *             28 GB for N = 1,048,576, Hkv = 4, G = 8, D = Di = 128, k = 16.
+ * Deterministic: every sum runs in a fixed order.
+ */
+MSA_API int msa_fused_bwd(const msa_dims* dims, const void* q, const void* k, const void* v, const void* q_idx,
+                          const void* k_idx, const int32_t* block_idx, const void* o, const float* lse,
+                          const float* index_lse, const void* dout, float softmax_scale, float index_scale,
+                          const float* dkl_rows, float kl_weight, void* dq, void* dk, void* dv, void* dq_idx,
+                          void* dk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense causal GQA attention forward: the main branch with every causally

@@ -231,7 +231,8 @@ def test_workspace_sizes(lib):
     assert msa.workspace_bytes(_dims(seqlen=128), msa.MSA_OP_ATTN) == 2 * 128 * 128 * 2
     assert msa.workspace_bytes(_dims(topk=1), msa.MSA_OP_ATTN) == 2 * 8 * 128 * 128 * 2
     assert msa.workspace_bytes(_dims(), msa.MSA_OP_INDEX) == 0
-    assert msa.workspace_bytes(_dims(), 11) == 0
+    assert msa.workspace_bytes(_dims(), 12) == 0
+    assert msa.workspace_bytes(_dims(), msa.MSA_OP_FUSED_BWD) > msa.workspace_bytes(_dims(), msa.MSA_OP_ATTN_BWD) > 0
     # the partial outputs dominate: rows * (k-1) * G * D * 2 bytes for bf16
     d = _dims(seqlen=131072, kv_heads=8, group_size=8, topk=16)
     need = msa.workspace_bytes(d, msa.MSA_OP_ATTN)
