@@ -45,8 +45,22 @@
 
 namespace msa {
 
-// One staged 32-row tile: query, output-gradient and index-query rows, each
-// natural and transposed, and the rows' scalars.
+// v_mfma_f32_16x16x32_bf16: A (16 x 32) lane l supplies row l % 16 and
+// contraction elements 8*(l/16) .. +7, B (32 x 16) column l % 16 and the same
+// elements, C (16 x 16) lane l holds column l % 16, rows 4*(l/16) + r, r < 4.
+__device__ __forceinline__ void mma1632(floatx4& c, const Op8<bf16_t>& a, const Op8<bf16_t>& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+// Row order of the transposed tiles (the contraction over a tile's 32 rows):
+// lane group q = l / 16 holds rows 4q .. 4q+3 (first row half) and 16 + 4q ..
+// 16 + 4q + 3 (second) in its accumulators, so chunk q of a transposed row
+// (8 positions, 16 bytes) holds exactly those rows: row m sits at position
+// 8 * ((m % 16) / 4) + 4 * (m / 16) + m % 4.
+__device__ __forceinline__ int fused_tpos(int m) { return 8 * ((m & 15) >> 2) + 4 * (m >> 4) + (m & 3); }
+
+// One staged 32-row tile: query, output-gradient and index-query rows, natural
+// and transposed (chunk-major, in the row order above), and the rows' scalars.
 template <int D, int DI>
 struct FusedTile {
     using QT = SwzTile<bf16_t, D>;    // [32 rows][D]
@@ -59,85 +73,107 @@ struct FusedTile {
     int pos[32], slot[32];
 };
 
-// LDS of one work-group: the staged tile, the dS and dU tiles, the key
-// block's K^T and K_idx^T (A operands of dQ and dq_idx, read from here rather
-// than held in registers, which the other operands and the dK, dV, dk_idx sums
-// already fill), the item's list entries.
+// LDS of one work-group: two tile buffers (tile t is computed from one while
+// tile t + 1 is written into the other), the dS and dU tiles, the key block's
+// K_idx^T (A operand of dq_idx; K^T, that of dQ, stays in registers), the
+// item's list entries.
 template <int D, int DI>
 struct FusedLds {
-    using DsT = SwzTile<bf16_t, kBlock>;   // [rows][128 keys, permuted]: dS, dU, K^T, K_idx^T
-    FusedTile<D, DI> tile;
+    using DsT = SwzTile<bf16_t, kBlock>;   // [rows][128 keys, permuted]: dS, dU, K_idx^T
+    FusedTile<D, DI> tile[2];
     unsigned char ds[32 * DsT::ROWB], du[32 * DsT::ROWB];
-    unsigned char kt[D * DsT::ROWB], kit[DI * DsT::ROWB];
+    unsigned char kit[DI * DsT::ROWB];
     int entries[kSegBwd];
 };
 
-struct FusedUnit {
-    u32x4 x[8];
-};
-
-// Staging units of one tile: 4*(D/8) units of Q rows, 4*(D/8) of dO rows, then
-// 4*(DI/8) of index-query rows (the position's one index query on each of its
-// G rows). Unit v of a tensor: row group v % 4 (rows 16c + {4h..4h+3,
-// 8+4h..8+4h+3}), dims 8*(v/4) .. +7; every unit is stored natural and
+// Staging of one tile in quarter units: 4 rows x 16 bytes (dims 8*dc .. +7) of
+// one tensor (Q, dO, Q_idx, in that order), every quarter stored natural and
 // transposed.
 template <int D, int DI>
 struct FusedUnits {
-    static constexpr int NQ = 4 * (D / 8), NI = 4 * (DI / 8), N = 2 * NQ + NI;
+    static constexpr int NQ = 8 * (D / 8), NI = 8 * (DI / 8), N = 2 * NQ + NI;
+};
+struct FusedQuarter {
+    u32x4 x[4];
 };
 
 template <int D, int DI, int G, bool LOCAL>
-__device__ __forceinline__ void fused_stage_load(FusedUnit& su, const BwdItem<LOCAL>& it, int t, int u,
+__device__ __forceinline__ void fused_stage_load(FusedQuarter& su, const BwdItem<LOCAL>& it, int t, int u,
                                                  const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
                                                  const bf16_t* __restrict__ q_idx, int N, int Hkv) {
     constexpr int NQ = FusedUnits<D, DI>::NQ, PPT = 32 / G;
     const int tensor = u < NQ ? 0 : (u < 2 * NQ ? 1 : 2);
     const int v = u - tensor * NQ;
-    const int grp = v & 3, dc = v >> 2;   // the row group varies fastest across lanes
-    const int c = grp >> 1, h = grp & 1;
+    const int rq = v & 7, dc = v >> 3;   // the row quarter varies fastest across lanes
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int m = 16 * c + 8 * (e / 4) + 4 * h + e % 4;
+    for (int e = 0; e < 4; ++e) {
+        const int m = 4 * rq + e;
         const int pe = t * PPT + m / G;
         su.x[e] = u32x4{0u, 0u, 0u, 0u};
         if (pe < it.count) {
             int i, s;
             it.entry(pe, i, s);
-            const size_t hrow = ((size_t)it.b * N + i) * Hkv * G + it.g * G + m % G;
             const bf16_t* src = tensor == 2 ? q_idx + (((size_t)it.b * N + i) * Hkv + it.g) * DI + dc * 8
-                                            : (tensor ? dout : q) + hrow * D + dc * 8;
+                                            : (tensor ? dout : q) + (((size_t)it.b * N + i) * Hkv * G + it.g * G + m % G) * D +
+                                                  dc * 8;
             su.x[e] = *reinterpret_cast<const u32x4*>(src);
         }
     }
 }
 
 template <int D, int DI>
-__device__ __forceinline__ void fused_stage_store(const FusedUnit& su, FusedTile<D, DI>& sh, int u) {
+__device__ __forceinline__ void fused_stage_store(const FusedQuarter& su, FusedTile<D, DI>& sh, int u) {
     constexpr int NQ = FusedUnits<D, DI>::NQ;
     using F = FusedTile<D, DI>;
     const int tensor = u < NQ ? 0 : (u < 2 * NQ ? 1 : 2);
     const int v = u - tensor * NQ;
-    const int grp = v & 3, dc = v >> 2;
-    const int c = grp >> 1, h = grp & 1;
+    const int rq = v & 7, dc = v >> 3;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int m = 16 * c + 8 * (e / 4) + 4 * h + e % 4;
+    for (int e = 0; e < 4; ++e) {
+        const int m = 4 * rq + e;
         unsigned char* dst = tensor == 2 ? sh.qi + F::IT::offset(m, dc * 16)
                                          : (tensor ? sh.dout : sh.q) + F::QT::offset(m, dc * 16);
         *reinterpret_cast<u32x4*>(dst) = su.x[e];
     }
+    // rows 4rq .. 4rq+3 are 4 consecutive positions of chunk rq % 4 (first or second half of it)
+    const int chunk = rq & 3, sub = (rq >> 2) * 8;
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-        u32x4 y;
+        uint2 y;
+        const uint32_t sel = dd % 2 ? 0x07060302u : 0x05040100u;   // the 16-bit element dd of two rows
+        y.x = __builtin_amdgcn_perm(su.x[1][dd / 2], su.x[0][dd / 2], sel);
+        y.y = __builtin_amdgcn_perm(su.x[3][dd / 2], su.x[2][dd / 2], sel);
+        unsigned char* dst = tensor == 2 ? sh.qit + F::ICT::offset(dc * 8 + dd, chunk)
+                                         : (tensor ? sh.dot : sh.qt) + F::QCT::offset(dc * 8 + dd, chunk);
+        *reinterpret_cast<uint2*>(dst + sub) = y;
+    }
+}
+
+// Teacher of each of the lane's 8 rows (rh*4 + r: row 16*rh + 4*(l/16) + r):
+// the mean of P over the G rows of the row's position (G consecutive rows).
+template <int G>
+__device__ __forceinline__ void head_mean8(float (&p)[8]) {
+    if constexpr (G == 1) return;
+    float a[2][4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // the 16-bit element dd of rows 2w and 2w + 1 (low and high half of the word)
-            y[w] = __builtin_amdgcn_perm(su.x[2 * w + 1][dd / 2], su.x[2 * w][dd / 2],
-                                         dd % 2 ? 0x07060302u : 0x05040100u);
+    for (int rh = 0; rh < 2; ++rh) {
+        if constexpr (G == 2) {
+            a[rh][0] = a[rh][1] = p[4 * rh] + p[4 * rh + 1];
+            a[rh][2] = a[rh][3] = p[4 * rh + 2] + p[4 * rh + 3];
+        } else {
+            float s = p[4 * rh] + p[4 * rh + 1] + p[4 * rh + 2] + p[4 * rh + 3];
+            if constexpr (G >= 8) s += __shfl_xor(s, 16);
+            if constexpr (G >= 16) s += __shfl_xor(s, 32);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[rh][r] = s;
         }
-        unsigned char* dst = tensor == 2 ? sh.qit + F::ICT::offset(dc * 8 + dd, 2 * c + h)
-                                         : (tensor ? sh.dot : sh.qt) + F::QCT::offset(dc * 8 + dd, 2 * c + h);
-        *reinterpret_cast<u32x4*>(dst) = y;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float lo = a[0][r], hi = a[1][r];
+        if constexpr (G == 32) lo = hi = lo + hi;
+        p[r] = lo * (1.f / G);
+        p[4 + r] = hi * (1.f / G);
     }
 }
 
@@ -148,13 +184,15 @@ struct FusedWindow {
     int bound;             // work-item slots per (b, g)
 };
 
-// One work-group (4 waves) per work item: the window's non-local rows of key
-// block j (LOCAL = false), or the rows of query block j against their own
-// block under the causal mask (LOCAL = true). Wave w owns keys 32w .. 32w+31
-// of the block for S, dP, U and the dK, dV, dk_idx sums, and dims 32w ..
-// 32w+31 of the dQ and dq_idx tiles.
+constexpr int kFusedWaves = 8;
+
+// One 8-wave work-group (two waves per SIMD) per work item: the window's
+// non-local rows of key block j (LOCAL = false), or the rows of query block j
+// against their own block under the causal mask (LOCAL = true). Wave w owns
+// keys 16w .. 16w+15 of the block for S, dP, U and the dK, dV, dk_idx sums,
+// and dims 16w .. 16w+15 of the dQ and dq_idx tiles.
 template <int D, int DI, int G, bool LOCAL>
-__global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
+__global__ __launch_bounds__(64 * kFusedWaves, 1) void fused_bwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ q_idx, const bf16_t* __restrict__ k_idx, const bf16_t* __restrict__ kt,
     const bf16_t* __restrict__ kit, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
@@ -164,9 +202,11 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
     bf16_t* __restrict__ dq_part, bf16_t* __restrict__ dqi_part, float* __restrict__ dkv_part,
     float* __restrict__ dki_part, int B, int N, int Hkv, int nb, int nwin, int topk, FusedWindow win,
     float scale_log2, float scale, float iscale) {
-    constexpr int PPT = 32 / G, DT = D / 32, DIT = DI / 32, KS = D / 16, KSI = DI / 16;
+    constexpr int PPT = 32 / G, DT = D / 16, DIT = DI / 16, KS = D / 32, KSI = DI / 32;
     constexpr int NST = FusedUnits<D, DI>::N;
-    static_assert(NST <= 224, "staging threads and the 32 row-scalar threads share the work-group");
+    constexpr int NTHR = 64 * kFusedWaves;
+    static_assert(NST <= NTHR - 32, "staging threads and the 32 row-scalar threads share the work-group");
+    static_assert(DT <= kFusedWaves && DIT <= kFusedWaves, "a wave per 16 dims of dQ and dq_idx");
     __shared__ __align__(16) FusedLds<D, DI> sh;
     using F = FusedTile<D, DI>;
     using L = FusedLds<D, DI>;
@@ -208,21 +248,21 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
         __syncthreads();
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int half = lane >> 5, col = lane & 31;
+    const int ql = lane >> 4, cl = lane & 15;   // lane group (row quarter / contraction octet), column
     const int ntiles = (it.count + PPT - 1) / PPT;
 
-    // The wave's keys as B operands (S, dP, U), its dims of K^T and K_idx^T as A operands (dQ, dq_idx).
-    const int key = 32 * w + col;
+    // The wave's 16 keys as B operands (S, dP, U) and its 16 dims of K^T as the A operand of dQ.
+    const int key = 16 * w + cl;
     const int kabs = it.j * kBlock + key;
-    Op8<bf16_t> kop[KS], vop[KS], kiop[KSI];
+    Op8<bf16_t> kop[KS], vop[KS], kiop[KSI], ktop[4];
     {
-        const size_t roff = (((size_t)it.b * N + kabs) * Hkv + it.g) * D + 8 * half;
-        const size_t ioff = ((size_t)it.b * N + kabs) * DI + 8 * half;
+        const size_t roff = (((size_t)it.b * N + kabs) * Hkv + it.g) * D + 8 * ql;
+        const size_t ioff = ((size_t)it.b * N + kabs) * DI + 8 * ql;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if (kabs < N) {
-                kop[s].load(k + roff + 16 * s);
-                vop[s].load(v + roff + 16 * s);
+                kop[s].load(k + roff + 32 * s);
+                vop[s].load(v + roff + 32 * s);
             } else {
                 kop[s].zero();
                 vop[s].zero();
@@ -230,40 +270,41 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
         }
 #pragma unroll
         for (int s = 0; s < KSI; ++s) {
-            if (kabs < N) kiop[s].load(k_idx + ioff + 16 * s);
+            if (kabs < N) kiop[s].load(k_idx + ioff + 32 * s);
             else kiop[s].zero();
         }
+        if (w < DT) {
+            const bf16_t* src = kt + ((((size_t)it.b * Hkv + it.g) * nb + it.j) * D + 16 * w + cl) * kBlock + 8 * ql;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ktop[c].load(src + 32 * c);
+        }
     }
-    // The block's K^T and K_idx^T rows (dims) into LDS, 16 bytes per thread per step.
+    // The block's K_idx^T rows (dims) into LDS, 16 bytes per thread per step.
     {
         using KT = typename L::DsT;
-        const bf16_t* src = kt + (((size_t)it.b * Hkv + it.g) * nb + it.j) * D * kBlock;
-        for (int ch = threadIdx.x; ch < D * KT::CPR; ch += blockDim.x)
-            *reinterpret_cast<u32x4*>(sh.kt + KT::offset(ch / KT::CPR, (ch % KT::CPR) * 16)) =
-                *reinterpret_cast<const u32x4*>(src + (size_t)ch * 8);
         const bf16_t* srci = kit + ((size_t)it.b * nb + it.j) * DI * kBlock;
         for (int ch = threadIdx.x; ch < DI * KT::CPR; ch += blockDim.x)
             *reinterpret_cast<u32x4*>(sh.kit + KT::offset(ch / KT::CPR, (ch % KT::CPR) * 16)) =
                 *reinterpret_cast<const u32x4*>(srci + (size_t)ch * 8);
     }
 
-    floatx16 dkt[DT], dvt[DT], dkit[DIT];
+    floatx4 dkt[DT], dvt[DT], dkit[DIT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        dkt[dt] = zero16();
-        dvt[dt] = zero16();
+        dkt[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dvt[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int dt = 0; dt < DIT; ++dt) dkit[dt] = zero16();
+    for (int dt = 0; dt < DIT; ++dt) dkit[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     constexpr float kLog2e = 1.4426950408889634f;
     const float iscale_log2 = iscale * kLog2e;
-    // Threads 0 .. NST-1 stage one unit of every tile (tile t + 1 requested when
-    // tile t is stored, so its loads are in flight while tile t is on the
-    // matrix cores); threads 224 .. 255 load the per-row scalars.
-    FusedUnit su;
+    // Threads 0 .. NST-1 stage one quarter of every tile: tile t + 2 is
+    // requested when tile t + 1 is stored, while tile t is on the matrix cores;
+    // the last 32 threads load the per-row scalars.
+    FusedQuarter su;
     const int u = threadIdx.x;
-    const int m_row = (int)threadIdx.x - 224;
+    const int m_row = (int)threadIdx.x - (NTHR - 32);
     float r_lse = 0.f, r_dl = 0.f, r_lseu = 0.f, r_w = 0.f;
     int r_pos = -1, r_slot = 0;
     auto row_load = [&](int t) {
@@ -289,8 +330,8 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
             }
         }
     };
-    auto store_tile = [&]() {
-        F& tb = sh.tile;
+    auto store_tile = [&](int t) {
+        F& tb = sh.tile[t & 1];
         if (u < NST) fused_stage_store<D, DI>(su, tb, u);
         if (m_row >= 0) {
             tb.lse2[m_row] = r_lse * kLog2e;
@@ -309,77 +350,88 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
     // Every load issued so far (the key block's operands, tile 0) completes here,
     // so the loop below only ever waits for its own prefetches.
     __builtin_amdgcn_s_waitcnt(0);
+    if (ntiles > 0) {
+        store_tile(0);
+        if (ntiles > 1) load_tile(1);
+    }
 
     for (int t = 0; t < ntiles; ++t) {
-        // The readers of tile t - 1 and of the dS / dU tiles are done.
+        // Tile t is complete in its buffer; the other buffer's readers (tile
+        // t - 1) and the dS / dU readers are done.
         __syncthreads();
-        store_tile();
-        if (t + 1 < ntiles) load_tile(t + 1);   // in flight during tile t's math
-        __syncthreads();
-        const F& sh_t = sh.tile;
+        if (t + 1 < ntiles) {   // overlaps tile t's math
+            store_tile(t + 1);
+            if (t + 2 < ntiles) load_tile(t + 2);
+        }
+        const F& sh_t = sh.tile[t & 1];
 
-        // S = Q K_w^T, dP = dO V_w^T, U = Q_idx K_idx,w^T: lane = key, accumulators = rows.
-        floatx16 s = zero16(), dp = zero16(), uu = zero16();
+        // S = Q K_w^T, dP = dO V_w^T, U = Q_idx K_idx,w^T for both 16-row halves:
+        // lane = key 16w + l % 16, accumulators = rows 16 rh + 4 (l / 16) + r.
+        floatx4 s[2], dp[2], uu[2];
 #pragma unroll
-        for (int sl = 0; sl < KS; ++sl) {
-            Op8<bf16_t> a, b;
-            a.load(sh_t.q + F::QT::offset(col, (16 * sl + 8 * half) * 2));
-            b.load(sh_t.dout + F::QT::offset(col, (16 * sl + 8 * half) * 2));
-            mma16(s, a, kop[sl]);
-            mma16(dp, b, vop[sl]);
+        for (int rh = 0; rh < 2; ++rh) {
+            s[rh] = dp[rh] = uu[rh] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Op8<bf16_t> a, b;
+                a.load(sh_t.q + F::QT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
+                b.load(sh_t.dout + F::QT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
+                mma1632(s[rh], a, kop[ks]);
+                mma1632(dp[rh], b, vop[ks]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSI; ++ks) {
+                Op8<bf16_t> a;
+                a.load(sh_t.qi + F::IT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
+                mma1632(uu[rh], a, kiop[ks]);
+            }
         }
+        float p[8], ds[8], du[8];
 #pragma unroll
-        for (int sl = 0; sl < KSI; ++sl) {
-            Op8<bf16_t> a;
-            a.load(sh_t.qi + F::IT::offset(col, (16 * sl + 8 * half) * 2));
-            mma16(uu, a, kiop[sl]);
-        }
-        float p[16], ds[16], du[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 8 * (r / 4) + 4 * half + r % 4;
-            float pr = exp2_hw(fmaf(s[r], scale_log2, -sh_t.lse2[m]));
+        for (int e = 0; e < 8; ++e) {
+            const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
+            float pr = exp2_hw(fmaf(s[e >> 2][e & 3], scale_log2, -sh_t.lse2[m]));
             if constexpr (LOCAL) {
                 if (it.q0 + key > sh_t.pos[m]) pr = 0.f;   // also the rows past the item (pos = -1)
             }
-            p[r] = pr;
-            ds[r] = pr * (dp[r] - sh_t.dl[m]);
-            du[r] = pr;
+            p[e] = pr;
+            ds[e] = pr * (dp[e >> 2][e & 3] - sh_t.dl[m]);
+            du[e] = pr;
         }
-        head_mean<G>(du);   // the teacher of each row's position
+        head_mean8<G>(du);   // the teacher of each row's position
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 8 * (r / 4) + 4 * half + r % 4;
-            float st = exp2_hw(fmaf(uu[r], iscale_log2, -sh_t.lseu2[m]));
+        for (int e = 0; e < 8; ++e) {
+            const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
+            float st = exp2_hw(fmaf(uu[e >> 2][e & 3], iscale_log2, -sh_t.lseu2[m]));
             if constexpr (LOCAL) {
                 if (it.q0 + key > sh_t.pos[m]) st = 0.f;
             }
-            du[r] = sh_t.wkl[m] * (st - du[r]);
+            du[e] = sh_t.wkl[m] * (st - du[e]);
         }
         // dV^T += dO^T P, dK^T += Q^T dS and dk_idx^T += Q_idx^T (dU / G) (every
-        // position's G replicated rows count once) over the tile's two 16-row slices.
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
+        // position's G replicated rows count once): the lane's 8 values are the
+        // contraction elements of its key column, in the transposed tiles' row order.
+        {
             Op8<bf16_t> bp, bds, bdu;
-            PType<bf16_t>::pack(bp, p + 8 * sl);
-            PType<bf16_t>::pack(bds, ds + 8 * sl);
+            PType<bf16_t>::pack(bp, p);
+            PType<bf16_t>::pack(bds, ds);
             float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = du[8 * sl + e] * (1.f / G);
+            for (int e = 0; e < 8; ++e) x[e] = du[e] * (1.f / G);
             PType<bf16_t>::pack(bdu, x);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 Op8<bf16_t> a, b;
-                a.load(sh_t.dot + F::QCT::offset(32 * dt + col, 2 * sl + half));
-                b.load(sh_t.qt + F::QCT::offset(32 * dt + col, 2 * sl + half));
-                mma16(dvt[dt], a, bp);
-                mma16(dkt[dt], b, bds);
+                a.load(sh_t.dot + F::QCT::offset(16 * dt + cl, ql));
+                b.load(sh_t.qt + F::QCT::offset(16 * dt + cl, ql));
+                mma1632(dvt[dt], a, bp);
+                mma1632(dkt[dt], b, bds);
             }
 #pragma unroll
             for (int dt = 0; dt < DIT; ++dt) {
                 Op8<bf16_t> a;
-                a.load(sh_t.qit + F::ICT::offset(32 * dt + col, 2 * sl + half));
-                mma16(dkit[dt], a, bdu);
+                a.load(sh_t.qit + F::ICT::offset(16 * dt + cl, ql));
+                mma1632(dkit[dt], a, bdu);
             }
         }
         // dS and dU -> LDS as [row][permuted key] for the dQ and dq_idx products.
@@ -388,10 +440,10 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
             uint16_t* dul = reinterpret_cast<uint16_t*>(sh.du);
             const int pk = perm16(key);
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {   // rows m and m + 1: one conversion, two 16-bit stores
-                const int m = 8 * (r / 4) + 4 * half + r % 4;
-                const uint32_t a2 = pack_bf16x2(ds[r], ds[r + 1]);
-                const uint32_t b2 = pack_bf16x2(du[r], du[r + 1]);
+            for (int e = 0; e < 8; e += 2) {   // rows m and m + 1: one conversion, two 16-bit stores
+                const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
+                const uint32_t a2 = pack_bf16x2(ds[e], ds[e + 1]);
+                const uint32_t b2 = pack_bf16x2(du[e], du[e + 1]);
                 dsl[L::DsT::offset(m, pk * 2) / 2] = (uint16_t)(a2 & 0xffffu);
                 dsl[L::DsT::offset(m + 1, pk * 2) / 2] = (uint16_t)(a2 >> 16);
                 dul[L::DsT::offset(m, pk * 2) / 2] = (uint16_t)(b2 & 0xffffu);
@@ -399,51 +451,43 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
             }
         }
         __syncthreads();
-        // dQ^T (dims 32w.., rows) = K^T dS^T and dq_idx^T = K_idx^T dU^T over the block's 128 keys.
-        const int i = sh_t.pos[col];
-        const size_t prow = i >= 0 ? (((size_t)it.b * Hkv + it.g) * win.len + (i - win.p0)) * topk + sh_t.slot[col]
-                                   : 0;
-        if (w < DT) {
-            floatx16 acc = zero16();
+        // dQ^T (dims 16w.., rows) = K^T dS^T and dq_idx^T = K_idx^T dU^T over the
+        // block's 128 keys: lane = row 16 rh + l % 16, accumulators = dims 16w + 4 (l / 16) + r.
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                Op8<bf16_t> a, b;
-                a.load(sh.kt + L::DsT::offset(32 * w + col, (16 * c + 8 * half) * 2));
-                b.load(sh.ds + L::DsT::offset(col, (16 * c + 8 * half) * 2));
-                mma16(acc, a, b);
-            }
-            if (i >= 0) {
-                // partial of (row, slot), head col % G: [G][D] bf16, each 32-dim slice lane-major
-                bf16_t* dst = dq_part + prow * G * D + (size_t)(col % G) * D + 32 * w + 16 * half;
-                u32x4 w0, w1;
+        for (int rh = 0; rh < 2; ++rh) {
+            const int row = 16 * rh + cl;
+            const int i = sh_t.pos[row];
+            const size_t prow =
+                i >= 0 ? (((size_t)it.b * Hkv + it.g) * win.len + (i - win.p0)) * topk + sh_t.slot[row] : 0;
+            if (w < DT) {
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w0[e] = pack_bf16x2(acc[2 * e] * scale, acc[2 * e + 1] * scale);
-                    w1[e] = pack_bf16x2(acc[8 + 2 * e] * scale, acc[8 + 2 * e + 1] * scale);
+                for (int c = 0; c < 4; ++c) {
+                    Op8<bf16_t> b;
+                    b.load(sh.ds + L::DsT::offset(row, (32 * c + 8 * ql) * 2));
+                    mma1632(acc, ktop[c], b);
                 }
-                *reinterpret_cast<u32x4*>(dst) = w0;
-                *reinterpret_cast<u32x4*>(dst + 8) = w1;
-            }
-        }
-        if (w < DIT) {
-            floatx16 acc = zero16();
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                Op8<bf16_t> a, b;
-                a.load(sh.kit + L::DsT::offset(32 * w + col, (16 * c + 8 * half) * 2));
-                b.load(sh.du + L::DsT::offset(col, (16 * c + 8 * half) * 2));
-                mma16(acc, a, b);
-            }
-            if (i >= 0 && col % G == 0) {   // the position's first head row writes it
-                bf16_t* dst = dqi_part + prow * DI + 32 * w + 16 * half;
-                u32x4 w0, w1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w0[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
-                    w1[e] = pack_bf16x2(acc[8 + 2 * e], acc[8 + 2 * e + 1]);
+                if (i >= 0) {
+                    // partial of (row, slot), head row % G: [G][D] bf16 in natural dim order
+                    bf16_t* dst = dq_part + prow * G * D + (size_t)(row % G) * D + 16 * w + 4 * ql;
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0] * scale, acc[1] * scale),
+                                                                pack_bf16x2(acc[2] * scale, acc[3] * scale));
                 }
-                *reinterpret_cast<u32x4*>(dst) = w0;
-                *reinterpret_cast<u32x4*>(dst + 8) = w1;
+            }
+            if (w < DIT) {
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    Op8<bf16_t> a, b;
+                    a.load(sh.kit + L::DsT::offset(16 * w + cl, (32 * c + 8 * ql) * 2));
+                    b.load(sh.du + L::DsT::offset(row, (32 * c + 8 * ql) * 2));
+                    mma1632(acc, a, b);
+                }
+                if (i >= 0 && row % G == 0) {   // the position's first head row writes it
+                    bf16_t* dst = dqi_part + prow * DI + 16 * w + 4 * ql;
+                    *reinterpret_cast<uint2*>(dst) =
+                        make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+                }
             }
         }
     }
@@ -453,30 +497,15 @@ __global__ __launch_bounds__(256, 1) void fused_bwd_kernel(
     float* pv = pk + (size_t)kBlock * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+        floatx4 xk;
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            floatx4 xk, xv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xk[e] = dkt[dt][4 * rq + e] * scale;
-                xv[e] = dvt[dt][4 * rq + e];
-            }
-            const int d0 = 32 * dt + 8 * rq + 4 * half;
-            *reinterpret_cast<floatx4*>(pk + d0) = xk;
-            *reinterpret_cast<floatx4*>(pv + d0) = xv;
-        }
+        for (int e = 0; e < 4; ++e) xk[e] = dkt[dt][e] * scale;
+        *reinterpret_cast<floatx4*>(pk + 16 * dt + 4 * ql) = xk;
+        *reinterpret_cast<floatx4*>(pv + 16 * dt + 4 * ql) = dvt[dt];
     }
     float* pki = dki_part + pidx * kBlock * DI + (size_t)key * DI;
 #pragma unroll
-    for (int dt = 0; dt < DIT; ++dt) {
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            floatx4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = dkit[dt][4 * rq + e];
-            *reinterpret_cast<floatx4*>(pki + 32 * dt + 8 * rq + 4 * half) = x;
-        }
-    }
+    for (int dt = 0; dt < DIT; ++dt) *reinterpret_cast<floatx4*>(pki + 16 * dt + 4 * ql) = dkit[dt];
 }
 
 // One work-group per (b, g, key block j < the window's last query block): the
@@ -667,11 +696,13 @@ static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, uns
         const int nbw = win.qb0 + nqb;   // key blocks the window's rows can keep
         const int last = w == nwin - 1;
         if (nonlocal)
-            hipLaunchKernelGGL((fused_bwd_kernel<D, DI, G, false>), dim3((unsigned)(bg * L.bound)), dim3(256), 0, st,
+            hipLaunchKernelGGL((fused_bwd_kernel<D, DI, G, false>), dim3((unsigned)(bg * L.bound)),
+                               dim3(64 * kFusedWaves), 0, st,
                                tq, tk, tv, tqi, tki, kt, kit, tdo, a.lse, dl, a.index_lse, a.dkl_rows, a.kl_weight,
                                list, items, item_offsets, total, (int)L.lists.n_keys, dq_part, dqi_part, dkv_part,
                                dki_part, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win, scale_log2, a.scale, a.iscale);
-        hipLaunchKernelGGL((fused_bwd_kernel<D, DI, G, true>), dim3((unsigned)(bg * nqb)), dim3(256), 0, st, tq, tk,
+        hipLaunchKernelGGL((fused_bwd_kernel<D, DI, G, true>), dim3((unsigned)(bg * nqb)), dim3(64 * kFusedWaves), 0,
+                           st, tq, tk,
                            tv, tqi, tki, kt, kit, tdo, a.lse, dl, a.index_lse, a.dkl_rows, a.kl_weight, nullptr,
                            nullptr, nullptr, nullptr, 0, dq_part, dqi_part, dkv_part, dki_part, d.B, d.N, d.Hkv, d.nb,
                            nwin, d.k, win, scale_log2, a.scale, a.iscale);
@@ -682,10 +713,11 @@ static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, uns
                            counts, item_offsets, acc_dki, static_cast<bf16_t*>(a.dk_idx), d.B, d.N, d.Hkv, d.nb, nwin,
                            kSegBwd, win, nbw, last, nonlocal ? 1 : 0);
         const int64_t units = (int64_t)bg * win.len * G * (D / 16);
-        hipLaunchKernelGGL((dq_combine_kernel<D, G>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, dq_part,
+        hipLaunchKernelGGL((dq_combine_kernel<D, G, true>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st,
+                           dq_part,
                            static_cast<bf16_t*>(a.dq), units, d.N, d.Hkv, d.k, win.p0, win.len, win.len);
         const int64_t iunits = (int64_t)bg * win.len * (DI / 16);
-        hipLaunchKernelGGL((dq_combine_kernel<DI, 1>), dim3((unsigned)((iunits + 255) / 256)), dim3(256), 0, st,
+        hipLaunchKernelGGL((dq_combine_kernel<DI, 1, true>), dim3((unsigned)((iunits + 255) / 256)), dim3(256), 0, st,
                            dqi_part, static_cast<bf16_t*>(a.dq_idx), iunits, d.N, d.Hkv, d.k, win.p0, win.len,
                            win.len);
     }
