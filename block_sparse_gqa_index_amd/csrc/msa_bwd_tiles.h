@@ -4,6 +4,7 @@
 #pragma once
 
 #include "msa_common.h"
+#include "msa_internal.h"
 
 namespace msa {
 
@@ -43,6 +44,51 @@ struct BwdItem {
     }
 };
 
+// Sets up the work item of this work-group in window `win` (LOCAL: the causal
+// block of query block qb0 + blockIdx.x / (B * Hkv)) and its partial slot;
+// false when the slot is empty (the whole work-group returns). Non-local items
+// copy their list entries into `entries` (LDS), then synchronise.
+template <bool LOCAL>
+__device__ __forceinline__ bool fused_item(BwdItem<LOCAL>& it, size_t& pidx, int* entries,
+                                           const int32_t* __restrict__ list, const int4* __restrict__ items,
+                                           const int32_t* __restrict__ item_offsets,
+                                           const int32_t* __restrict__ total_items, int n_keys, int B, int N, int Hkv,
+                                           int nb, int nwin, int topk, const FusedWindow& win) {
+    if constexpr (LOCAL) {
+        const int nqb = (win.len + kBlock - 1) / kBlock;
+        const int x = blockIdx.x;
+        it.g = x % Hkv;
+        it.b = (x / Hkv) % B;
+        it.j = win.qb0 + x / (Hkv * B);
+        it.q0 = it.j * kBlock;
+        it.count = min(kBlock, N - it.q0);
+        it.lslot = min(topk, it.j + 1) - 1;
+        it.start = 0;
+        it.entries = nullptr;
+        pidx = (size_t)B * Hkv * win.bound + ((size_t)it.b * Hkv + it.g) * nqb + (it.j - win.qb0);
+        return true;
+    } else {
+        const int bgi = blockIdx.x / win.bound, x = blockIdx.x % win.bound;
+        const int kf = (bgi * nwin + win.w) * nb;
+        const int first = item_offsets[kf];
+        const int end = kf + nb < n_keys ? item_offsets[kf + nb] : total_items[0];
+        if (first + x >= end) return false;
+        const int4 e = items[first + x];
+        it.j = e.x % nb;
+        it.g = bgi % Hkv;
+        it.b = bgi / Hkv;
+        it.start = e.y;
+        it.count = e.z;
+        it.q0 = 0;
+        it.lslot = 0;
+        it.entries = entries;
+        pidx = blockIdx.x;
+        for (int y = threadIdx.x; y < it.count; y += blockDim.x) entries[y] = list[it.start + y];
+        __syncthreads();
+        return true;
+    }
+}
+
 // Teacher of the row in accumulator r: the mean of P over the G rows of the
 // same position. Rows 8*(r/4) + 4h + r%4 of position m / G: the G rows of a
 // position are aligned groups of min(G, 16) accumulators (G <= 4 within one
@@ -71,12 +117,11 @@ __device__ __forceinline__ void head_mean(float (&p)[16]) {
 // instructions per slot reads whole cache lines (64 consecutive 16-byte
 // chunks or whole 128-byte halves of rows) and no line is split between them.
 // Stored element 16*qg + r of a head is dim 32*(qg/2) + 8*(r/4) + 4*(qg%2) + r%4
-// (the lane-major order of the partials), or dim 16*qg + r when NAT is set
-// (partials in natural dim order).
+// (the lane-major order of the partials).
 // The rows handled are positions p0 .. p0 + len - 1 of every (b, g), whose
 // partials sit at row (b * Hkv + g) * wrows + (i - p0) of dq_part (a window of
 // wrows positions; p0 = 0 and len = wrows = N for the whole sequence).
-template <int D, int G, bool NAT = false>
+template <int D, int G>
 __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restrict__ dq_part, bf16_t* __restrict__ dq,
                                                          int64_t units, int N, int Hkv, int topk, int p0, int len,
                                                          int wrows) {
@@ -107,17 +152,6 @@ __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restric
         }
     }
     const int Hq = Hkv * G;
-    if constexpr (NAT) {
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-            const int e0 = 8 * (t + part * TPR);
-            const float* v = acc + 8 * part;
-            *reinterpret_cast<u32x4*>(dq + (((size_t)b * N + i) * Hq + g * G) * D + e0) =
-                u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7])};
-        }
-        return;
-    }
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
         const int e0 = 8 * (t + part * TPR);   // first stored element of the group in the slot's partial

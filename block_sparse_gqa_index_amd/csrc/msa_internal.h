@@ -138,12 +138,38 @@ struct FusedBwdArgs {
 };
 struct FusedBwdWorkspace {
     ListLayout lists;   // position-sorted, kSegBwd entries per item, for the whole sequence
-    size_t kt, kit, dl, dq_part, dqi_part, dkv_part, dki_part, acc_dkv, acc_dki, bytes;
+    size_t kt, kit, dl, teacher, dq_part, dqi_part, dkv_part, dki_part, acc_dkv, acc_dki, bytes;
     int bound;          // non-local work-item slots per (b, g) and window
     size_t items;       // partial slots of one window: non-local, then local
 };
 FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d);
 hipError_t launch_fused_bwd(const LaunchDims& d, const FusedBwdArgs& a, void* ws, hipStream_t st);
+
+// Window of the fused backward: query positions [p0, p0 + len) of every
+// (b, g) and the work-item slots of their lists. Non-local slot x of (b, g)
+// (work-group (b * Hkv + g) * bound + x) is the x-th item of the keys
+// (b, g, w, 0 .. nb-1), which the position-sorted lists keep contiguous; the
+// local items of the window's query blocks follow all non-local slots.
+struct FusedWindow {
+    int w, p0, len, qb0;   // window index, first position, positions, first query block
+    int bound;             // non-local work-item slots per (b, g)
+};
+// What the main-branch backward kernel needs to run as the first half of the
+// fused backward: the window, the lists' item offsets, and the teacher output
+// [B * Hkv * len][k][128] fp32 (the head mean of P per (row, slot, key)).
+struct BwdFusedCtx {
+    const int32_t* item_offsets;
+    float* teacher;
+    int n_keys;   // (b, g, window, key block) list keys
+    FusedWindow win;
+};
+// Main-branch kernels of one window (non-local items when `nonlocal`, then the
+// window's causal local blocks): dQ partials per (window row, slot), dK/dV
+// partials per work-item slot, and the teacher.
+hipError_t launch_attn_bwd_window(const LaunchDims& d, const void* q, const void* k, const void* v, const void* kt,
+                                  const void* dout, const float* lse, const float* dl, const int32_t* list,
+                                  const int4* items, const int32_t* total, bool nonlocal, void* dq_part,
+                                  float* dkv_part, const BwdFusedCtx& fx, float scale, hipStream_t st);
 
 // Dense causal attention (every visible key kept): V^T copy into ws, then the
 // query-block-outer kernel. ws holds dense_workspace_bytes(d).

@@ -159,13 +159,13 @@ __device__ __forceinline__ void stage_store(const StageUnit& su, BwdTile<D>& sh,
 // (LOCAL = false), or the rows of query block j against their own block
 // under the causal mask (LOCAL = true). Wave w owns keys 32w .. 32w+31 of the
 // block for S, dP, dK, dV, and dims 32w .. 32w+31 of the dQ tile.
-template <int D, int G, bool LOCAL>
+template <int D, int G, bool LOCAL, bool FUSED>
 __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ kt, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ dl, const int32_t* __restrict__ list, const int4* __restrict__ items,
     const int32_t* __restrict__ total_items, bf16_t* __restrict__ dq_part, float* __restrict__ dkv_part, int B, int N,
-    int Hkv, int nb, int nwin, int topk, size_t local_base, float scale_log2, float scale) {
+    int Hkv, int nb, int nwin, int topk, size_t local_base, float scale_log2, float scale, BwdFusedCtx fx) {
     constexpr int PPT = 32 / G, DT = D / 32, KS = D / 16;
     constexpr int NSTAGE = 2 * 4 * (D / 8);   // staging threads
     __shared__ __align__(16) BwdLds<D> sh;
@@ -173,7 +173,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
 
     BwdItem<LOCAL> it;
     size_t pidx;
-    if constexpr (LOCAL) {
+    if constexpr (FUSED) {
+        if (!fused_item<LOCAL>(it, pidx, sh.entries, list, items, fx.item_offsets, total_items, fx.n_keys, B, N, Hkv,
+                               nb, nwin, topk, fx.win))
+            return;
+    } else if constexpr (LOCAL) {
         const int x = blockIdx.x;
         it.g = x % Hkv;
         it.b = (x / Hkv) % B;
@@ -330,6 +334,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             p[r] = pr;
             ds[r] = pr * (dp[r] - rd[r]);
         }
+        if constexpr (FUSED) {
+            // The KL term's teacher of (position, key): the mean of P over the
+            // position's G head rows, written by the lane holding its first row.
+            float tp[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tp[r] = p[r];
+            head_mean<G>(tp);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 8 * (r / 4) + 4 * half + r % 4;
+                if (m % G == 0) {
+                    const int i = sh_t.pos[m];
+                    if (i >= 0)
+                        fx.teacher[((((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)) * topk +
+                                    sh_t.slot[m]) * kBlock + key] = tp[r];
+                }
+            }
+        }
         // dV^T += dO^T P and dK^T += Q^T dS over the tile's two 16-row slices.
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
@@ -379,8 +401,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             if (i >= 0) {
                 // partial of (row (b, g, i), slot), head col % G: [G][D] bf16, each 32-dim slice lane-major
                 // (element 32w + 16h + r holds dim 32w + 8*(r/4) + 4h + r%4)
-                bf16_t* dst = dq_part + ((((size_t)it.b * Hkv + it.g) * N + i) * topk + sh_t.slot[col]) * G * D +
-                              (size_t)(col % G) * D + 32 * w + 16 * half;
+                // (rows of the window's positions [p0, p0 + len) in the fused backward, of all N otherwise)
+                const size_t drow = FUSED ? ((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)
+                                          : ((size_t)it.b * Hkv + it.g) * N + i;
+                bf16_t* dst = dq_part + (drow * topk + sh_t.slot[col]) * G * D + (size_t)(col % G) * D + 32 * w +
+                              16 * half;
                 u32x4 w0, w1;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -515,21 +540,71 @@ static hipError_t launch_bwd_t(const LaunchDims& d, const void* q, const void* k
     if (nonlocal) {
         launch_build_lists(d, 0, d.N, block_idx, ws, L.lists, st);
         const size_t grid = (list_items_bound(d, 0, d.N, L.lists) + 63) / 64 * 64;
-        hipLaunchKernelGGL((attn_bwd_kernel<D, G, false>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tv, kt,
+        hipLaunchKernelGGL((attn_bwd_kernel<D, G, false, false>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tv, kt,
                            tdo, lse, dl, reinterpret_cast<const int32_t*>(ws + L.lists.list),
                            reinterpret_cast<const int4*>(ws + L.lists.items),
                            reinterpret_cast<const int32_t*>(ws + L.lists.total), dq_part, dkv_part, d.B, d.N, d.Hkv,
-                           d.nb, nwin, d.k, local_base, scale_log2, scale);
+                           d.nb, nwin, d.k, local_base, scale_log2, scale, BwdFusedCtx{});
     }
-    hipLaunchKernelGGL((attn_bwd_kernel<D, G, true>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st, tq, tk,
-                       tv, kt, tdo, lse, dl, nullptr, nullptr, nullptr, dq_part, dkv_part, d.B, d.N, d.Hkv, d.nb, nwin,
-                       d.k, local_base, scale_log2, scale);
+    hipLaunchKernelGGL((attn_bwd_kernel<D, G, true, false>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st,
+                       tq, tk, tv, kt, tdo, lse, dl, nullptr, nullptr, nullptr, dq_part, dkv_part, d.B, d.N, d.Hkv,
+                       d.nb, nwin, d.k, local_base, scale_log2, scale, BwdFusedCtx{});
     hipLaunchKernelGGL((dkv_reduce_kernel<D>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st, dkv_part,
                        counts, item_offsets, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), d.B, d.N, d.Hkv, d.nb,
                        nwin, kSegBwd, local_base, nonlocal ? 1 : 0);
     const int64_t units = (int64_t)d.B * d.Hkv * d.N * G * (D / 16);
     hipLaunchKernelGGL((dq_combine_kernel<D, G>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, dq_part,
                        static_cast<bf16_t*>(dq), units, d.N, d.Hkv, d.k, 0, d.N, d.N);
+    return hipGetLastError();
+}
+
+template <int D, int G>
+static void launch_bwd_window_t(const LaunchDims& d, const void* q, const void* k, const void* v, const void* kt,
+                                const void* dout, const float* lse, const float* dl, const int32_t* list,
+                                const int4* items, const int32_t* total, bool nonlocal, void* dq_part,
+                                float* dkv_part, const BwdFusedCtx& fx, float scale, hipStream_t st) {
+    const bf16_t* tq = static_cast<const bf16_t*>(q);
+    const bf16_t* tk = static_cast<const bf16_t*>(k);
+    const bf16_t* tv = static_cast<const bf16_t*>(v);
+    const bf16_t* tkt = static_cast<const bf16_t*>(kt);
+    const bf16_t* tdo = static_cast<const bf16_t*>(dout);
+    bf16_t* dqp = static_cast<bf16_t*>(dq_part);
+    const float scale_log2 = scale * 1.4426950408889634f;
+    const int nwin = windows(d);
+    const int bg = d.B * d.Hkv;
+    const int nqb = (fx.win.len + kBlock - 1) / kBlock;
+    if (nonlocal)
+        hipLaunchKernelGGL((attn_bwd_kernel<D, G, false, true>), dim3((unsigned)(bg * fx.win.bound)), dim3(256), 0,
+                           st, tq, tk, tv, tkt, tdo, lse, dl, list, items, total, dqp, dkv_part, d.B, d.N, d.Hkv,
+                           d.nb, nwin, d.k, (size_t)0, scale_log2, scale, fx);
+    hipLaunchKernelGGL((attn_bwd_kernel<D, G, true, true>), dim3((unsigned)(bg * nqb)), dim3(256), 0, st, tq, tk, tv,
+                       tkt, tdo, lse, dl, nullptr, nullptr, nullptr, dqp, dkv_part, d.B, d.N, d.Hkv, d.nb, nwin, d.k,
+                       (size_t)0, scale_log2, scale, fx);
+}
+
+hipError_t launch_attn_bwd_window(const LaunchDims& d, const void* q, const void* k, const void* v, const void* kt,
+                                  const void* dout, const float* lse, const float* dl, const int32_t* list,
+                                  const int4* items, const int32_t* total, bool nonlocal, void* dq_part,
+                                  float* dkv_part, const BwdFusedCtx& fx, float scale, hipStream_t st) {
+#define MSA_BWD_WIN(DD, GG)                                                                                           \
+    launch_bwd_window_t<DD, GG>(d, q, k, v, kt, dout, lse, dl, list, items, total, nonlocal, dq_part, dkv_part, fx,   \
+                                scale, st)
+#define MSA_BWD_WIN_G(DD)                                                                                             \
+    switch (d.G) {                                                                                                    \
+        case 1: MSA_BWD_WIN(DD, 1); break;                                                                            \
+        case 2: MSA_BWD_WIN(DD, 2); break;                                                                            \
+        case 4: MSA_BWD_WIN(DD, 4); break;                                                                            \
+        case 8: MSA_BWD_WIN(DD, 8); break;                                                                            \
+        case 16: MSA_BWD_WIN(DD, 16); break;                                                                          \
+        default: MSA_BWD_WIN(DD, 32); break;                                                                          \
+    }
+    if (d.D == 128) {
+        MSA_BWD_WIN_G(128)
+    } else {
+        MSA_BWD_WIN_G(64)
+    }
+#undef MSA_BWD_WIN_G
+#undef MSA_BWD_WIN
     return hipGetLastError();
 }
 
