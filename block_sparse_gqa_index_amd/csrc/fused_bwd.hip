@@ -446,9 +446,9 @@ FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d) {
     w.lists = list_layout(d, off, kSegBwd, true);
     off = w.lists.end;
     w.bound = w.lists.has_nonlocal ? fused_bound(d) : 0;
-    w.teacher = off;   off = align_up(off + bg * W * d.k * kBlock * 4);
+    w.teacher = off;   off = align_up(off + (bg * W * d.k + 1) * kBlock * 4);   // + spare row
     w.items = bg * w.bound + bg * ((W + kBlock - 1) / kBlock);   // non-local slots, then local ones
-    w.dq_part = off;   off = align_up(off + bg * W * d.k * d.G * d.D * 2);
+    w.dq_part = off;   off = align_up(off + (bg * W * d.k + 1) * d.G * d.D * 2);   // + spare
     w.dqi_part = off;  off = align_up(off + bg * W * d.k * d.Di * 2);
     w.dkv_part = off;  off = align_up(off + w.items * 2 * kBlock * d.D * 4);
     w.dki_part = off;  off = align_up(off + w.items * kBlock * d.Di * 4);

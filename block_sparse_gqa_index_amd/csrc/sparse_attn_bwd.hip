@@ -241,6 +241,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
     }
 
     constexpr float kLog2e = 1.4426950408889634f;
+    // Spare (row, slot) of the dQ partials and the teacher, for rows past the item.
+    const size_t spare = FUSED ? (size_t)B * Hkv * fx.win.len * topk : (size_t)B * Hkv * N * topk;
     // Tiles are staged two ahead: the threads of half `par` (threadIdx.x / 128)
     // stage the tiles t with t % 2 == par, the global loads of tile t + 2
     // being issued while tiles t and t + 1 are on the matrix cores.
@@ -296,7 +298,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
         // Tile t is complete in its buffer; the other buffer's readers (tile
         // t - 1) and the dS readers are done.
         __syncthreads();
-        if (t + 1 < ntiles && ((t + 1) & 1) == par) commit(t + 1);   // overlaps tile t's math
         const BwdTile<D>& sh_t = sh.tile[t & 1];
 
         // S = Q K_w^T and dP = dO V_w^T: lane = key, accumulators = rows. The
@@ -334,6 +335,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             p[r] = pr;
             ds[r] = pr * (dp[r] - rd[r]);
         }
+        // Staging of tile t + 1 (overlaps tile t's math). It waits for every memory
+        // operation before it, so it comes after S and dP (the previous tile's dQ
+        // stores have landed by then) and before this tile's stores.
+        if (t + 1 < ntiles && ((t + 1) & 1) == par) commit(t + 1);
         if constexpr (FUSED) {
             // The KL term's teacher of (position, key): the mean of P over the
             // position's G head rows, written by the lane holding its first row.
@@ -343,12 +348,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             head_mean<G>(tp);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = 8 * (r / 4) + 4 * half + r % 4;
-                if (m % G == 0) {
+                // the lanes holding a position's first row write its mean (for G >= 8 the
+                // same row of both half-waves: they hold the same mean); rows past the item
+                // write the spare row, so the stores are issued on every tile
+                if ((8 * (r / 4) + r % 4) % G == 0) {
+                    const int m = 8 * (r / 4) + 4 * half + r % 4;
                     const int i = sh_t.pos[m];
-                    if (i >= 0)
-                        fx.teacher[((((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)) * topk +
-                                    sh_t.slot[m]) * kBlock + key] = tp[r];
+                    const size_t row = i >= 0 ? (((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)) * topk +
+                                                    sh_t.slot[m]
+                                              : spare;
+                    fx.teacher[row * kBlock + key] = tp[r];
                 }
             }
         }
@@ -398,23 +407,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
             const int i = sh_t.pos[col];
-            if (i >= 0) {
-                // partial of (row (b, g, i), slot), head col % G: [G][D] bf16, each 32-dim slice lane-major
-                // (element 32w + 16h + r holds dim 32w + 8*(r/4) + 4h + r%4)
-                // (rows of the window's positions [p0, p0 + len) in the fused backward, of all N otherwise)
-                const size_t drow = FUSED ? ((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)
-                                          : ((size_t)it.b * Hkv + it.g) * N + i;
-                bf16_t* dst = dq_part + (drow * topk + sh_t.slot[col]) * G * D + (size_t)(col % G) * D + 32 * w +
-                              16 * half;
-                u32x4 w0, w1;
+            // partial of (row (b, g, i), slot), head col % G: [G][D] bf16, each 32-dim slice lane-major
+            // (element 32w + 16h + r holds dim 32w + 8*(r/4) + 4h + r%4); rows of the window's
+            // positions [p0, p0 + len) in the fused backward, of all N otherwise; rows past the
+            // item write the spare partial, so the stores are issued on every tile
+            const size_t drow = FUSED ? ((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)
+                                      : ((size_t)it.b * Hkv + it.g) * N + i;
+            const size_t prow = i >= 0 ? drow * topk + sh_t.slot[col] : spare;
+            bf16_t* dst = dq_part + prow * G * D + (size_t)(col % G) * D + 32 * w + 16 * half;
+            u32x4 w0, w1;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w0[e] = pack_bf16x2(acc[2 * e] * scale, acc[2 * e + 1] * scale);
-                    w1[e] = pack_bf16x2(acc[8 + 2 * e] * scale, acc[8 + 2 * e + 1] * scale);
-                }
-                *reinterpret_cast<u32x4*>(dst) = w0;
-                *reinterpret_cast<u32x4*>(dst + 8) = w1;
+            for (int e = 0; e < 4; ++e) {
+                w0[e] = pack_bf16x2(acc[2 * e] * scale, acc[2 * e + 1] * scale);
+                w1[e] = pack_bf16x2(acc[8 + 2 * e] * scale, acc[8 + 2 * e + 1] * scale);
             }
+            *reinterpret_cast<u32x4*>(dst) = w0;
+            *reinterpret_cast<u32x4*>(dst + 8) = w1;
         }
     }
 
@@ -504,7 +512,7 @@ BwdWorkspace bwd_workspace_layout(const LaunchDims& d) {
     w.dl = off;   off = align_up(off + (size_t)d.B * d.Hq() * d.N * 4);
     w.lists = list_layout(d, off, kSegBwd, true);
     off = w.lists.end;
-    w.dq_part = off;   off = align_up(off + (size_t)d.B * d.Hkv * d.N * d.k * d.G * d.D * 2);
+    w.dq_part = off;   off = align_up(off + ((size_t)d.B * d.Hkv * d.N * d.k + 1) * d.G * d.D * 2);   // + spare
     w.local_items = (size_t)d.B * d.Hkv * d.nb;
     w.dkv_items = w.local_items + (w.lists.has_nonlocal ? w.lists.max_items : 0);
     w.dkv_part = off;  off = align_up(off + w.dkv_items * 2 * kBlock * d.D * 4);
