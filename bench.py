@@ -35,11 +35,12 @@ sys.path.insert(0, ROOT)
 
 import block_sparse_gqa_index_amd as msa  # noqa: E402
 from synth import (CONFIGS, DECODE_CONFIGS, make_decode_inputs, make_grad_output, make_inputs,  # noqa: E402
-                   make_row_weights, sample_rows)
+                   make_row_weights, sample_rows, to_fp4_e2m1)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and MFMA)
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CSRC = os.path.join(ROOT, "block_sparse_gqa_index_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_n128k.json")
@@ -471,6 +472,9 @@ def main():
     ap.add_argument("--index-fp8", action="store_true",
                     help="also time the step with the selection on fp8 e4m3 copies of the index inputs "
                          "(reported beside the bf16 headline, never as it)")
+    ap.add_argument("--index-fp4", action="store_true",
+                    help="also time the step with the selection on fp4 e2m1 copies of the index inputs "
+                         "(reported beside the bf16 headline, never as it)")
     ap.add_argument("--bwd", action="store_true",
                     help="also time the main-branch backward (msa_sparse_attn_bwd) on the step's outputs")
     ap.add_argument("--fused-only", action="store_true",
@@ -483,6 +487,8 @@ def main():
                     help="with --decode: also time the step on paged caches (block table, random page order)")
     ap.add_argument("--dense", action="store_true",
                     help="time the warm-up's dense causal attention (msa_dense_attn_fwd) on the 128K shapes instead")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only time plain read/write/copy kernels on cache-resident and HBM-sized buffers")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -493,6 +499,31 @@ def main():
         sys.exit(2)
 
     dev = torch.device("cuda:0")
+    if args.stream_probe:
+        # Streaming rates of plain torch kernels on buffers that fit the 256 MB infinity
+        # cache (repeated passes stay resident) and on buffers far larger than it.
+        res = []
+        for mib in (64, 128, 192, 4096):
+            n = mib << 18
+            a = torch.ones(n, dtype=torch.float32, device=dev)
+            b = torch.empty_like(a)
+            for name, fn, nbytes in (("read", lambda: a.sum(), n * 4), ("write", lambda: b.fill_(1.0), n * 4),
+                                     ("copy", lambda: b.copy_(a), 2 * n * 4)):
+                for _ in range(3):
+                    fn()
+                reps = max(8, (8 << 30) // nbytes)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                res.append({"mib": mib, "op": name, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9})
+                log(f"[bench] stream {name} {mib} MiB: {res[-1]['gbs']:.0f} GB/s")
+            del a, b
+        print(json.dumps({"stream_probe": res}), flush=True)
+        return
     if args.copy_mib:
         # Reference for HBM byte counters: one launch reads and writes exactly this many bytes.
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
@@ -642,6 +673,31 @@ def main():
             "speedup_vs_bf16_index": stage_ms[index_kernel] / idx8,
             "ms_per_step": ms8, "tokens_per_s": tokens / (ms8 * 1e-3),
             "same_selection": bool(torch.equal(bi8, block_idx))}
+    if args.index_fp4:
+        # The index inputs as OCP fp4 e2m1 (two per byte): the integers -4..4 are exact, so
+        # the selection equals the bf16 one wherever the inputs fit; the 128K stripes' +3
+        # bias takes some components to 5..7, which round to 4 or 6.
+        log("[bench] step with the fp4 selection")
+        qi4, ki4 = to_fp4_e2m1(x["q_idx"]), to_fp4_e2m1(x["k_idx"])
+        bi4 = torch.empty_like(block_idx)
+        for _ in range(args.warmup):
+            step(events(), qi4, ki4, bi4)
+        evs4 = [events() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for ev in evs4:
+            step(ev, qi4, ki4, bi4)
+        torch.cuda.synchronize()
+        ms4 = (time.perf_counter() - t0) * 1e3 / args.steps
+        idx4 = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs4]))
+        a4 = f_idx / (idx4 * 1e-3) / 1e12
+        out["index_fp4"] = {
+            "kernel": index_kernel, "dtype": "fp4 e2m1 index inputs (unit scales), fp32 accumulation", "ms": idx4,
+            "achieved": a4, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": a4 / PEAK_FP4_TFLOPS,
+            "speedup_vs_bf16_index": stage_ms[index_kernel] / idx4,
+            "ms_per_step": ms4, "tokens_per_s": tokens / (ms4 * 1e-3),
+            "same_selection": bool(torch.equal(bi4, block_idx)),
+            "rows_with_same_selection": float((bi4 == block_idx).all(dim=-1).float().mean())}
     if args.bwd and args.kl:
         # Both branches' gradients from one pass (msa_fused_bwd), query window by query window.
         log("[bench] fused backward of both branches")

@@ -167,7 +167,8 @@ const char* msa_strerror(int status) {
         case MSA_OK: return "ok";
         case MSA_ERR_NULL: return "a required pointer is NULL";
         case MSA_ERR_SHAPE: return "invalid or too large problem sizes";
-        case MSA_ERR_UNSUPPORTED: return "unsupported sizes or dtype (block_size 128, topk 1..32, group_size "
+        case MSA_ERR_UNSUPPORTED: return "unsupported sizes or dtype (block_size 128, or 64/256 for the selection, "
+                                         "attention and KL forward (256: topk <= 16 there), topk 1..32, group_size "
                                          "power of two <= 32, head/index dim 64 or 128, bf16/fp32 (fp8 e4m3 "
                                          "and fp4 e2m1 for the selection only, bf16 for the backward), causal)";
         case MSA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";

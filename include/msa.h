@@ -82,9 +82,14 @@ enum msa_status {
 /*
  * Problem sizes. Supported: batch >= 0, seqlen >= 0 (any value; the last block
  * may be partial), kv_heads >= 1, group_size in {1,2,4,8,16,32}, head_dim and
- * index_dim in {64,128}, block_size == 128, topk in [1,32], dtype MSA_BF16 or
- * MSA_F32 (MSA_FP8_E4M3 for the selection only), causal == 1. batch == 0 or
- * seqlen == 0 is a valid empty problem.
+ * index_dim in {64,128}, block_size 128 (also 64 and 256 for the selection,
+ * msa_check_block_idx, the attention and KL forward and msa_forward, in bf16
+ * or fp32, with topk <= 16 at 256 outside the selection: a 256-token block
+ * takes two of the 128-token slots those kernels work in), topk in [1,32],
+ * dtype MSA_BF16 or MSA_F32 (MSA_FP8_E4M3 and MSA_FP4_E2M1 for the selection
+ * only), causal == 1. batch == 0 or seqlen == 0 is a valid empty problem.
+ * The MSA article (7minutos.es, "¿Qué es MSA?") gives 128 as the default block
+ * size, not the only one.
  */
 typedef struct msa_dims {
     int64_t batch;
@@ -305,7 +310,7 @@ MSA_API int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k,
  *   ws        at least msa_workspace_bytes(dims, MSA_OP_FUSED_BWD) bytes. The
  *             query rows are processed 65,536 positions at a time, so the
  *             per-(row, slot) partials never exceed one such window: about
- *             28 GB for N = 1,048,576, Hkv = 4, G = 8, D = Di = 128, k = 16.
+ *             30 GB for N = 1,048,576, Hkv = 4, G = 8, D = Di = 128, k = 16.
  * Deterministic: every sum runs in a fixed order.
  */
 MSA_API int msa_fused_bwd(const msa_dims* dims, const void* q, const void* k, const void* v, const void* q_idx,
