@@ -45,6 +45,334 @@
 
 namespace msa {
 
+// ----------------------------------------------- main branch, two waves/SIMD --
+
+// v_mfma_f32_16x16x32_bf16: A (16 x 32) lane l supplies row l % 16 and
+// contraction elements 8*(l/16) .. +7, B (32 x 16) column l % 16 and the same
+// elements, C (16 x 16) lane l holds column l % 16, rows 4*(l/16) + r, r < 4.
+__device__ __forceinline__ void mma1632(floatx4& c, const Op8<bf16_t>& a, const Op8<bf16_t>& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+// One staged 32-row tile of the eight-wave main-branch kernel: Q and dO rows,
+// natural and transposed, and the rows' scalars. In the transposed copies the
+// contraction over the tile's rows follows the 16 x 16 accumulator layout:
+// lane group q = l / 16 holds rows 4q .. 4q+3 and 16 + 4q .. 16 + 4q + 3, so
+// chunk q of a transposed row (8 positions) holds exactly those rows, row m at
+// position 4 * (m / 16) + m % 4.
+template <int D>
+struct Main8Tile {
+    using QT = SwzTile<bf16_t, D>;   // [32 rows][D]
+    using QCT = ColTile<D>;          // [D][32 rows, permuted]
+    unsigned char q[32 * QT::ROWB], dout[32 * QT::ROWB];
+    unsigned char qt[QCT::BYTES], dot[QCT::BYTES];
+    float lse2[32], dl[32];
+    int pos[32], slot[32];
+};
+
+template <int D>
+struct Main8Lds {
+    using DsT = SwzTile<bf16_t, kBlock>;   // [32 rows][128 keys, permuted]
+    Main8Tile<D> tile[2];
+    unsigned char ds[32 * DsT::ROWB];
+    int entries[kSegBwd];
+};
+
+// Staging in quarter units: 4 rows x 16 bytes (dims 8*dc .. +7) of Q (units
+// 0 .. D-1) or dO (units D .. 2D-1), the row quarter varying fastest across
+// lanes; rows past the item read its last entry (their P is zero).
+struct Main8Quarter {
+    u32x4 x[4];
+};
+
+template <int D, int G, bool LOCAL>
+__device__ __forceinline__ void main8_stage_load(Main8Quarter& su, const BwdItem<LOCAL>& it, int t, int u,
+                                                 const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
+                                                 int N, int Hq) {
+    constexpr int PPT = 32 / G;
+    const int tensor = u >= D, v = tensor ? u - D : u;
+    const int rq = v & 7, dc = v >> 3;
+    const bf16_t* src = tensor ? dout : q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int m = 4 * rq + e;
+        int i, s;
+        it.entry(min(t * PPT + m / G, it.count - 1), i, s);
+        su.x[e] = *reinterpret_cast<const u32x4*>(src + (((size_t)it.b * N + i) * Hq + it.g * G + m % G) * D + dc * 8);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void main8_stage_store(const Main8Quarter& su, Main8Tile<D>& tb, int u) {
+    using T = Main8Tile<D>;
+    const int tensor = u >= D, v = tensor ? u - D : u;
+    const int rq = v & 7, dc = v >> 3;
+    unsigned char* nat = tensor ? tb.dout : tb.q;
+    unsigned char* tr = tensor ? tb.dot : tb.qt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(nat + T::QT::offset(4 * rq + e, dc * 16)) = su.x[e];
+    // rows 4rq .. 4rq+3 are four consecutive positions of chunk rq % 4
+    const int chunk = rq & 3, sub = (rq >> 2) * 8;
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+        const uint32_t sel = dd % 2 ? 0x07060302u : 0x05040100u;   // the 16-bit element dd of two rows
+        *reinterpret_cast<uint2*>(tr + T::QCT::offset(dc * 8 + dd, chunk) + sub) =
+            make_uint2(__builtin_amdgcn_perm(su.x[1][dd / 2], su.x[0][dd / 2], sel),
+                       __builtin_amdgcn_perm(su.x[3][dd / 2], su.x[2][dd / 2], sel));
+    }
+}
+
+// Teacher of each of the lane's 8 rows (rh*4 + r: row 16*rh + 4*(l/16) + r):
+// the mean of P over the G rows of the row's position (G consecutive rows).
+template <int G>
+__device__ __forceinline__ void head_mean8(float (&p)[8]) {
+    if constexpr (G == 1) return;
+    float a[2][4];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+        if constexpr (G == 2) {
+            a[rh][0] = a[rh][1] = p[4 * rh] + p[4 * rh + 1];
+            a[rh][2] = a[rh][3] = p[4 * rh + 2] + p[4 * rh + 3];
+        } else {
+            float s = p[4 * rh] + p[4 * rh + 1] + p[4 * rh + 2] + p[4 * rh + 3];
+            if constexpr (G >= 8) s += __shfl_xor(s, 16);
+            if constexpr (G >= 16) s += __shfl_xor(s, 32);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[rh][r] = s;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float lo = a[0][r], hi = a[1][r];
+        if constexpr (G == 32) lo = hi = lo + hi;
+        p[r] = lo * (1.f / G);
+        p[4 + r] = hi * (1.f / G);
+    }
+}
+
+constexpr int kMain8Waves = 8;
+
+// The main branch of the fused backward with two waves per SIMD: one 8-wave
+// work-group per work item of a window (as attn_bwd_kernel's fused mode), wave
+// w owning keys 16w .. 16w+15 of the block for S, dP, dK, dV (K and V as B
+// operands in VGPRs) and dims 16w .. 16w+15 of the dQ tile (its K^T rows as A
+// operands); 16 x 16 x 32 products throughout. Writes the dQ partials in
+// natural dim order, the dK/dV partial of the item and the teacher.
+template <int D, int G, bool LOCAL>
+__global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ kt, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ dl, const int32_t* __restrict__ list, const int4* __restrict__ items,
+    const int32_t* __restrict__ item_offsets, const int32_t* __restrict__ total_items, int n_keys,
+    bf16_t* __restrict__ dq_part, float* __restrict__ dkv_part, float* __restrict__ teacher, int B, int N, int Hkv,
+    int nb, int nwin, int topk, FusedWindow win, float scale_log2, float scale) {
+    constexpr int PPT = 32 / G, DT = D / 16, KS = D / 32;
+    constexpr int NTHR = 64 * kMain8Waves;
+    static_assert(2 * D <= NTHR - 32, "staging threads and the 32 row-scalar threads share the work-group");
+    __shared__ __align__(16) Main8Lds<D> sh;
+    using T = Main8Tile<D>;
+    using L = Main8Lds<D>;
+    const int Hq = Hkv * G;
+
+    BwdItem<LOCAL> it;
+    size_t pidx;
+    if (!fused_item<LOCAL>(it, pidx, sh.entries, list, items, item_offsets, total_items, n_keys, B, N, Hkv, nb, nwin,
+                           topk, win))
+        return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ql = lane >> 4, cl = lane & 15;
+    const int ntiles = (it.count + PPT - 1) / PPT;
+    const size_t rbase = ((size_t)it.b * Hkv + it.g) * win.len - win.p0;   // window row of position i: rbase + i
+    const size_t spare = (size_t)B * Hkv * win.len * topk;                 // (row, slot) of rows past the item
+
+    const int key = 16 * w + cl;
+    const int kabs = it.j * kBlock + key;
+    Op8<bf16_t> kop[KS], vop[KS], ktop[4];
+    {
+        const size_t roff = (((size_t)it.b * N + kabs) * Hkv + it.g) * D + 8 * ql;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (kabs < N) {
+                kop[s].load(k + roff + 32 * s);
+                vop[s].load(v + roff + 32 * s);
+            } else {
+                kop[s].zero();
+                vop[s].zero();
+            }
+        }
+        if (w < DT) {
+            const bf16_t* src = kt + ((((size_t)it.b * Hkv + it.g) * nb + it.j) * D + 16 * w + cl) * kBlock + 8 * ql;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ktop[c].load(src + 32 * c);
+        }
+    }
+    floatx4 dkt[DT], dvt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        dkt[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dvt[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    constexpr float kLog2e = 1.4426950408889634f;
+    // Threads 0 .. 2D-1 stage a quarter of every tile, the last 32 threads the
+    // rows' scalars: tile t + 1 is written to LDS and tile t + 2 requested while
+    // tile t is on the matrix cores.
+    Main8Quarter su;
+    const int u = threadIdx.x;
+    const int m_row = (int)threadIdx.x - (NTHR - 32);
+    float r_lse = 0.f, r_dl = 0.f;
+    int r_pos = -1, r_slot = 0;
+    auto load_tile = [&](int t) {
+        if (u < 2 * D) main8_stage_load<D, G, LOCAL>(su, it, t, u, q, dout, N, Hq);
+        if (m_row >= 0) {
+            const int pe = t * PPT + m_row / G;
+            int i, s;
+            it.entry(min(pe, it.count - 1), i, s);
+            const size_t r = ((size_t)it.b * Hq + it.g * G + m_row % G) * N + i;
+            r_pos = pe < it.count ? i : -1;
+            r_slot = s;
+            r_lse = lse[r];
+            r_dl = dl[r];
+        }
+    };
+    auto store_tile = [&](int t) {
+        T& tb = sh.tile[t & 1];
+        if (u < 2 * D) main8_stage_store<D>(su, tb, u);
+        if (m_row >= 0) {
+            const bool ok = r_pos >= 0;
+            tb.lse2[m_row] = ok ? r_lse * kLog2e : __builtin_inff();
+            tb.dl[m_row] = ok ? r_dl : 0.f;
+            tb.pos[m_row] = r_pos;
+            tb.slot[m_row] = r_slot;
+        }
+    };
+    load_tile(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    store_tile(0);
+    if (ntiles > 1) load_tile(1);
+
+    for (int t = 0; t < ntiles; ++t) {
+        // Tile t is complete in its buffer; the other buffer's readers (tile
+        // t - 1) and the dS readers are done.
+        __syncthreads();
+        const T& sh_t = sh.tile[t & 1];
+
+        // S = Q K_w^T and dP = dO V_w^T for both 16-row halves: lane = key
+        // 16w + l % 16, accumulators = rows 16 rh + 4 (l / 16) + r.
+        floatx4 s[2], dp[2];
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+            s[rh] = dp[rh] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Op8<bf16_t> a, b;
+                a.load(sh_t.q + T::QT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
+                b.load(sh_t.dout + T::QT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
+                mma1632(s[rh], a, kop[ks]);
+                mma1632(dp[rh], b, vop[ks]);
+            }
+        }
+        // Staging of tile t + 1 and request of tile t + 2. It waits for every memory
+        // operation before it, so it comes after S and dP (the previous tile's dQ
+        // stores have landed by then) and before this tile's stores.
+        if (t + 1 < ntiles) {
+            store_tile(t + 1);
+            if (t + 2 < ntiles) load_tile(t + 2);
+        }
+        float p[8], ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
+            float pr = exp2_hw(fmaf(s[e >> 2][e & 3], scale_log2, -sh_t.lse2[m]));
+            if constexpr (LOCAL) {
+                if (it.q0 + key > sh_t.pos[m]) pr = 0.f;   // also the rows past the item (pos = -1)
+            }
+            p[e] = pr;
+            ds[e] = pr * (dp[e >> 2][e & 3] - sh_t.dl[m]);
+        }
+        // The KL term's teacher of (position, key): the mean of P over the position's
+        // G head rows. The lanes holding a position's first row write it (for G >= 8
+        // also the other lane groups of the position, which hold the same mean); rows
+        // past the item write the spare row, so every tile issues the same stores.
+        {
+            float tp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tp[e] = p[e];
+            head_mean8<G>(tp);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if ((e & 3) % (G < 4 ? G : 4) == 0) {
+                    const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
+                    const int i = sh_t.pos[m];
+                    const size_t row = i >= 0 ? (rbase + i) * topk + sh_t.slot[m] : spare;
+                    teacher[row * kBlock + key] = tp[e];
+                }
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: the lane's 8 values are the contraction
+        // elements of its key column, in the transposed tiles' row order.
+        {
+            Op8<bf16_t> bp, bds;
+            PType<bf16_t>::pack(bp, p);
+            PType<bf16_t>::pack(bds, ds);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                Op8<bf16_t> a, b;
+                a.load(sh_t.dot + T::QCT::offset(16 * dt + cl, ql));
+                b.load(sh_t.qt + T::QCT::offset(16 * dt + cl, ql));
+                mma1632(dvt[dt], a, bp);
+                mma1632(dkt[dt], b, bds);
+            }
+        }
+        // dS -> LDS as [row][permuted key] for the dQ product.
+        {
+            uint16_t* dsl = reinterpret_cast<uint16_t*>(sh.ds);
+            const int pk = perm16(key);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {   // rows m and m + 1: one conversion, two 16-bit stores
+                const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
+                const uint32_t a2 = pack_bf16x2(ds[e], ds[e + 1]);
+                dsl[L::DsT::offset(m, pk * 2) / 2] = (uint16_t)(a2 & 0xffffu);
+                dsl[L::DsT::offset(m + 1, pk * 2) / 2] = (uint16_t)(a2 >> 16);
+            }
+        }
+        __syncthreads();
+        // dQ^T (dims 16w.., rows) = K^T dS^T over the block's 128 keys: lane = row
+        // 16 rh + l % 16, accumulators = dims 16w + 4 (l / 16) + r.
+        if (w < DT) {
+#pragma unroll
+            for (int rh = 0; rh < 2; ++rh) {
+                const int row = 16 * rh + cl;
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    Op8<bf16_t> b;
+                    b.load(sh.ds + L::DsT::offset(row, (32 * c + 8 * ql) * 2));
+                    mma1632(acc, ktop[c], b);
+                }
+                const int i = sh_t.pos[row];
+                const size_t prow = i >= 0 ? (rbase + i) * topk + sh_t.slot[row] : spare;
+                // partial of (window row, slot), head row % G: [G][D] bf16 in natural dim order
+                bf16_t* dst = dq_part + prow * G * D + (size_t)(row % G) * D + 16 * w + 4 * ql;
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0] * scale, acc[1] * scale),
+                                                            pack_bf16x2(acc[2] * scale, acc[3] * scale));
+            }
+        }
+    }
+
+    // The item's dK, dV partial: [2][128 keys][D] fp32 (dK scaled by sigma).
+    float* pk = dkv_part + pidx * 2 * kBlock * D + (size_t)key * D;
+    float* pv = pk + (size_t)kBlock * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        floatx4 xk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xk[e] = dkt[dt][e] * scale;
+        *reinterpret_cast<floatx4*>(pk + 16 * dt + 4 * ql) = xk;
+        *reinterpret_cast<floatx4*>(pv + 16 * dt + 4 * ql) = dvt[dt];
+    }
+}
+
 // ------------------------------------------------------------ index branch --
 
 // One staged tile of the index branch: the index-query rows of 32 (position,
@@ -462,6 +790,11 @@ FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d) {
 template <int D, int DI, int G>
 static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, unsigned char* ws, hipStream_t st) {
     const FusedBwdWorkspace L = fused_bwd_workspace_layout(d);
+    const bf16_t* tq = static_cast<const bf16_t*>(a.q);
+    const bf16_t* tk = static_cast<const bf16_t*>(a.k);
+    const bf16_t* tv = static_cast<const bf16_t*>(a.v);
+    const bf16_t* tdo = static_cast<const bf16_t*>(a.dout);
+    const float scale_log2 = a.scale * 1.4426950408889634f;
     const bf16_t* tqi = static_cast<const bf16_t*>(a.q_idx);
     const bf16_t* tki = static_cast<const bf16_t*>(a.k_idx);
     bf16_t* kt = reinterpret_cast<bf16_t*>(ws + L.kt);
@@ -504,9 +837,15 @@ static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, uns
         const int nbw = win.qb0 + nqb;   // key blocks the window's rows can keep
         const int last = w == nwin - 1;
         const BwdFusedCtx fx{item_offsets, teacher, (int)L.lists.n_keys, win};
-        e = launch_attn_bwd_window(d, a.q, a.k, a.v, kt, a.dout, a.lse, dl, list, items, total, nonlocal, dq_part,
-                                   dkv_part, fx, a.scale, st);
-        if (e != hipSuccess) return e;
+        (void)fx;
+        if (nonlocal)
+            hipLaunchKernelGGL((main8_bwd_kernel<D, G, false>), dim3((unsigned)(bg * L.bound)), dim3(64 * kMain8Waves),
+                               0, st, tq, tk, tv, kt, tdo, a.lse, dl, list, items, item_offsets, total,
+                               (int)L.lists.n_keys, dq_part, dkv_part, teacher, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win,
+                               scale_log2, a.scale);
+        hipLaunchKernelGGL((main8_bwd_kernel<D, G, true>), dim3((unsigned)(bg * nqb)), dim3(64 * kMain8Waves), 0, st,
+                           tq, tk, tv, kt, tdo, a.lse, dl, nullptr, nullptr, nullptr, nullptr, 0, dq_part, dkv_part,
+                           teacher, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win, scale_log2, a.scale);
         if (nonlocal)
             hipLaunchKernelGGL((fused_index_kernel<DI, false>), dim3((unsigned)(bg * L.bound)), dim3(256), 0, st, tqi,
                                tki, kit, a.index_lse, a.dkl_rows, a.kl_weight, teacher, list, items, item_offsets,
@@ -522,7 +861,8 @@ static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, uns
                            counts, item_offsets, acc_dki, static_cast<bf16_t*>(a.dk_idx), d.B, d.N, d.Hkv, d.nb, nwin,
                            kSegBwd, win, nbw, last, nonlocal ? 1 : 0);
         const int64_t units = (int64_t)bg * win.len * G * (D / 16);
-        hipLaunchKernelGGL((dq_combine_kernel<D, G>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, dq_part,
+        hipLaunchKernelGGL((dq_combine_kernel<D, G, true>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st,
+                           dq_part,
                            static_cast<bf16_t*>(a.dq), units, d.N, d.Hkv, d.k, win.p0, win.len, win.len);
         const int64_t iunits = (int64_t)bg * win.len * (DI / 16);
         hipLaunchKernelGGL((dq_combine_kernel<DI, 1>), dim3((unsigned)((iunits + 255) / 256)), dim3(256), 0, st,

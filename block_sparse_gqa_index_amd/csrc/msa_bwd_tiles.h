@@ -117,11 +117,12 @@ __device__ __forceinline__ void head_mean(float (&p)[16]) {
 // instructions per slot reads whole cache lines (64 consecutive 16-byte
 // chunks or whole 128-byte halves of rows) and no line is split between them.
 // Stored element 16*qg + r of a head is dim 32*(qg/2) + 8*(r/4) + 4*(qg%2) + r%4
-// (the lane-major order of the partials).
+// (the lane-major order of the partials), or dim 16*qg + r when NAT is set
+// (partials in natural dim order).
 // The rows handled are positions p0 .. p0 + len - 1 of every (b, g), whose
 // partials sit at row (b * Hkv + g) * wrows + (i - p0) of dq_part (a window of
 // wrows positions; p0 = 0 and len = wrows = N for the whole sequence).
-template <int D, int G>
+template <int D, int G, bool NAT = false>
 __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restrict__ dq_part, bf16_t* __restrict__ dq,
                                                          int64_t units, int N, int Hkv, int topk, int p0, int len,
                                                          int wrows) {
@@ -152,6 +153,17 @@ __global__ __launch_bounds__(256) void dq_combine_kernel(const bf16_t* __restric
         }
     }
     const int Hq = Hkv * G;
+    if constexpr (NAT) {
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            const int e0 = 8 * (t + part * TPR);
+            const float* v = acc + 8 * part;
+            *reinterpret_cast<u32x4*>(dq + (((size_t)b * N + i) * Hq + g * G) * D + e0) =
+                u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
+        }
+        return;
+    }
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
         const int e0 = 8 * (t + part * TPR);   // first stored element of the group in the slot's partial
