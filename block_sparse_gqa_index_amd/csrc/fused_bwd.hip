@@ -389,27 +389,27 @@ struct IdxBwdTile {
 // Two tile buffers, the dU tile, the item's entries.
 template <int DI>
 struct IdxBwdLds {
-    using DuT = SwzTile<bf16_t, kBlock>;   // [32 rows][128 keys, permuted]
+    using DuT = SwzTile<bf16_t, kBlock>;   // [32 rows][128 keys, permuted]; also K_idx^T [DI][128 keys]
     IdxBwdTile<DI> tile[2];
     unsigned char du[32 * DuT::ROWB];
+    unsigned char kit[DI * DuT::ROWB];
     int entries[kSegBwd];
 };
 
-// One 8-row x 16-byte unit of the staging: rows 16c + {4h..4h+3, 8+4h..8+4h+3}
-// (the rows of one transposed 16-byte chunk), dims 8*dc .. 8*dc+7; unit u of
-// the 4*(DI/8) units of a tile has the row group u % 4 and dc = u / 4.
+// One 4-row x 16-byte unit of the staging: rows 4rq .. 4rq+3 at dims 8*dc .. +7
+// (unit u of the 8 * (DI/8) units of a tile: rq = u % 8, dc = u / 8). Rows
+// 4rq .. 4rq+3 are four consecutive positions of one transposed chunk.
 struct IdxUnit {
-    u32x4 x[8];
+    u32x4 x[4];
 };
 
 template <int DI, bool LOCAL>
 __device__ __forceinline__ void idx_stage_load(IdxUnit& su, const BwdItem<LOCAL>& it, int t, int u,
                                                const bf16_t* __restrict__ q_idx, int N, int Hkv) {
-    const int grp = u & 3, dc = u >> 2;
-    const int c = grp >> 1, h = grp & 1;
+    const int rq = u & 7, dc = u >> 3;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int pe = 32 * t + 16 * c + 8 * (e / 4) + 4 * h + e % 4;
+    for (int e = 0; e < 4; ++e) {
+        const int pe = 32 * t + 4 * rq + e;
         su.x[e] = u32x4{0u, 0u, 0u, 0u};
         if (pe < it.count) {
             int i, s;
@@ -422,23 +422,18 @@ __device__ __forceinline__ void idx_stage_load(IdxUnit& su, const BwdItem<LOCAL>
 template <int DI>
 __device__ __forceinline__ void idx_stage_store(const IdxUnit& su, IdxBwdTile<DI>& tb, int u) {
     using T = IdxBwdTile<DI>;
-    const int grp = u & 3, dc = u >> 2;
-    const int c = grp >> 1, h = grp & 1;
+    const int rq = u & 7, dc = u >> 3;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int m = 16 * c + 8 * (e / 4) + 4 * h + e % 4;
-        *reinterpret_cast<u32x4*>(tb.qi + T::IT::offset(m, dc * 16)) = su.x[e];
-    }
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(tb.qi + T::IT::offset(4 * rq + e, dc * 16)) = su.x[e];
+    // row m sits in chunk 2 * (m / 16) + (m / 4) % 2 at position 4 * ((m / 8) % 2) + m % 4
+    const int chunk = 2 * (rq >> 2) + (rq & 1), sub = 8 * ((rq >> 1) & 1);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-        u32x4 y;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // the 16-bit element dd of rows 2w and 2w + 1 (low and high half of the word)
-            y[w] = __builtin_amdgcn_perm(su.x[2 * w + 1][dd / 2], su.x[2 * w][dd / 2],
-                                         dd % 2 ? 0x07060302u : 0x05040100u);
-        }
-        *reinterpret_cast<u32x4*>(tb.qit + T::ICT::offset(dc * 8 + dd, 2 * c + h)) = y;
+        // the 16-bit element dd of rows 2w and 2w + 1 (low and high half of the word)
+        const uint32_t sel = dd % 2 ? 0x07060302u : 0x05040100u;
+        *reinterpret_cast<uint2*>(tb.qit + T::ICT::offset(dc * 8 + dd, chunk) + sub) =
+            make_uint2(__builtin_amdgcn_perm(su.x[1][dd / 2], su.x[0][dd / 2], sel),
+                       __builtin_amdgcn_perm(su.x[3][dd / 2], su.x[2][dd / 2], sel));
     }
 }
 
@@ -451,14 +446,14 @@ __device__ __forceinline__ void idx_stage_store(const IdxUnit& su, IdxBwdTile<DI
 //   U = Q_idx K_idx^T,  s = exp(c U - LSE_u),  dU = w c (s - teacher),
 //   dk_idx^T += Q_idx^T dU (over the item),  dq_idx^T = K_idx^T dU^T (per tile).
 template <int DI, bool LOCAL>
-__global__ __launch_bounds__(256, 1) void fused_index_kernel(
+__global__ __launch_bounds__(256, 2) void fused_index_kernel(
     const bf16_t* __restrict__ q_idx, const bf16_t* __restrict__ k_idx, const bf16_t* __restrict__ kit,
     const float* __restrict__ index_lse, const float* __restrict__ dkl_rows, float kl_weight,
     const float* __restrict__ teacher, const int32_t* __restrict__ list, const int4* __restrict__ items,
     const int32_t* __restrict__ item_offsets, const int32_t* __restrict__ total_items, int n_keys,
     bf16_t* __restrict__ dqi_part, float* __restrict__ dki_part, int B, int N, int Hkv, int nb, int nwin, int topk,
     FusedWindow win, float iscale) {
-    constexpr int DIT = DI / 32, NST = 4 * (DI / 8);
+    constexpr int DIT = DI / 32, NST = 8 * (DI / 8);
     __shared__ __align__(16) IdxBwdLds<DI> sh;
     using L = IdxBwdLds<DI>;
     using T = IdxBwdTile<DI>;
@@ -481,11 +476,12 @@ __global__ __launch_bounds__(256, 1) void fused_index_kernel(
         if (kabs < N) kiop[s].load(k_idx + ((size_t)it.b * N + kabs) * DI + 8 * half + 16 * s);
         else kiop[s].zero();
     }
-    Op8<bf16_t> kitop[8];
-    if (w < DIT) {
-        const bf16_t* src = kit + (((size_t)it.b * nb + it.j) * DI + 32 * w + col) * kBlock + 8 * half;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) kitop[c].load(src + 16 * c);
+    // The block's K_idx^T (A operand of dq_idx) into LDS, 16 bytes per thread and step.
+    {
+        const bf16_t* src = kit + ((size_t)it.b * nb + it.j) * DI * kBlock;
+        for (int ch = threadIdx.x; ch < DI * L::DuT::CPR; ch += blockDim.x)
+            *reinterpret_cast<u32x4*>(sh.kit + L::DuT::offset(ch / L::DuT::CPR, (ch % L::DuT::CPR) * 16)) =
+                *reinterpret_cast<const u32x4*>(src + (size_t)ch * 8);
     }
     floatx16 dkit[DIT];
 #pragma unroll
@@ -615,7 +611,9 @@ __global__ __launch_bounds__(256, 1) void fused_index_kernel(
             for (int c = 0; c < 8; ++c) {
                 Op8<bf16_t> b;
                 b.load(sh.du + L::DuT::offset(col, (16 * c + 8 * half) * 2));
-                mma16(acc, kitop[c], b);
+                Op8<bf16_t> a;
+                a.load(sh.kit + L::DuT::offset(32 * w + col, (16 * c + 8 * half) * 2));
+                mma16(acc, a, b);
             }
             const int i = sh_t.pos[col];
             if (i >= 0) {
