@@ -20,22 +20,31 @@
 //   dU_t = w c (s_t - p_t),  dq_idx = sum_t dU_t k_idx_t,  dk_idx_t = sum dU_t q_idx.
 //
 // Work is key-block-outer over the position-sorted lists, one 64K-position
-// window of query rows at a time, so the per-(row, slot) dQ and dq_idx partials
-// only ever hold one window (the workspace stays bounded at a million tokens):
-//   per window: fused_bwd_kernel on the window's non-local items, then on the
-//   causal local blocks of its query blocks; fused_dkv_reduce and
-//   fused_dki_reduce add the window's per-item partials, in item order, to fp32
-//   running sums per key block (written as bf16 after the last window);
-//   dq_combine_kernel sums the window's rows' slot partials.
-// Every sum runs in a fixed order, so the gradients are deterministic.
+// window of query rows at a time, so the per-(row, slot) partials only ever
+// hold one window (the workspace stays bounded at a million tokens). Per
+// window:
+//   main8_bwd_kernel: the main branch over the window's non-local items, then
+//     the causal local blocks of its query blocks (eight waves, two per SIMD):
+//     S and P once per (row, kept block), dQ partials per (row, slot), dK/dV
+//     partials per item, and the teacher p (head mean of P) per (row, slot,
+//     key) for the index branch;
+//   fused_index_kernel: the index branch over the same items, one row per
+//     position, from the teacher: dq_idx partials, dk_idx partials per item;
+//   fused_dkv_reduce / fused_dki_reduce: the window's per-item partials, in
+//     item order, added to fp32 running sums per key block (bf16 after the
+//     last window); dq_combine_kernel: each row's slot partials in slot order.
+// Every sum runs in a fixed order, so the gradients are deterministic. The
+// teacher goes through memory (512 bytes per (row, slot)) because the index
+// branch has one row per position and the main branch G: inside one tile its
+// products would be repeated G times and its operands would take registers
+// the main branch needs.
 //
-// Matrix-core orientation as in the separate backward kernels: S = Q K^T,
-// dP = dO V^T and U = Q_idx K_idx^T with A = tile rows (LDS) and B = the wave's
-// 32 keys (VGPRs) leave one key per lane and 16 rows in its accumulators; P, dS
-// and dU in that layout are the B operands of dV^T = dO^T P, dK^T = Q^T dS and
-// dk_idx^T = Q_idx^T (dU / G) against transposed tiles staged with the matching
-// row permutation; dQ and dq_idx contract over keys, so dS and dU go through
-// LDS and the A operands are the per-block K^T and K_idx^T copies.
+// Matrix-core orientation: products with A = tile rows (LDS) and B = the
+// wave's keys (VGPRs) leave one key per lane and the rows in its accumulators;
+// P, dS and dU in that layout are the B operands of dV^T = dO^T P,
+// dK^T = Q^T dS and dk_idx^T = Q_idx^T dU against transposed tiles staged with
+// the matching row order; dQ and dq_idx contract over keys, so dS and dU go
+// through LDS and the A operands are the per-block K^T and K_idx^T copies.
 #include "msa_common.h"
 #include "msa_internal.h"
 #include "msa_tiles.h"
@@ -834,8 +843,6 @@ static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, uns
         const int nqb = (win.len + kBlock - 1) / kBlock;
         const int nbw = win.qb0 + nqb;   // key blocks the window's rows can keep
         const int last = w == nwin - 1;
-        const BwdFusedCtx fx{item_offsets, teacher, (int)L.lists.n_keys, win};
-        (void)fx;
         if (nonlocal)
             hipLaunchKernelGGL((main8_bwd_kernel<D, G, false>), dim3((unsigned)(bg * L.bound)), dim3(64 * kMain8Waves),
                                0, st, tq, tk, tv, kt, tdo, a.lse, dl, list, items, item_offsets, total,

@@ -154,22 +154,6 @@ struct FusedWindow {
     int w, p0, len, qb0;   // window index, first position, positions, first query block
     int bound;             // non-local work-item slots per (b, g)
 };
-// What the main-branch backward kernel needs to run as the first half of the
-// fused backward: the window, the lists' item offsets, and the teacher output
-// [B * Hkv * len][k][128] fp32 (the head mean of P per (row, slot, key)).
-struct BwdFusedCtx {
-    const int32_t* item_offsets;
-    float* teacher;
-    int n_keys;   // (b, g, window, key block) list keys
-    FusedWindow win;
-};
-// Main-branch kernels of one window (non-local items when `nonlocal`, then the
-// window's causal local blocks): dQ partials per (window row, slot), dK/dV
-// partials per work-item slot, and the teacher.
-hipError_t launch_attn_bwd_window(const LaunchDims& d, const void* q, const void* k, const void* v, const void* kt,
-                                  const void* dout, const float* lse, const float* dl, const int32_t* list,
-                                  const int4* items, const int32_t* total, bool nonlocal, void* dq_part,
-                                  float* dkv_part, const BwdFusedCtx& fx, float scale, hipStream_t st);
 
 // Dense causal attention (every visible key kept): V^T copy into ws, then the
 // query-block-outer kernel. ws holds dense_workspace_bytes(d).

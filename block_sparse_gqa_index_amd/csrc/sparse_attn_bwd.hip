@@ -159,13 +159,13 @@ __device__ __forceinline__ void stage_store(const StageUnit& su, BwdTile<D>& sh,
 // (LOCAL = false), or the rows of query block j against their own block
 // under the causal mask (LOCAL = true). Wave w owns keys 32w .. 32w+31 of the
 // block for S, dP, dK, dV, and dims 32w .. 32w+31 of the dQ tile.
-template <int D, int G, bool LOCAL, bool FUSED>
+template <int D, int G, bool LOCAL>
 __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ kt, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ dl, const int32_t* __restrict__ list, const int4* __restrict__ items,
     const int32_t* __restrict__ total_items, bf16_t* __restrict__ dq_part, float* __restrict__ dkv_part, int B, int N,
-    int Hkv, int nb, int nwin, int topk, size_t local_base, float scale_log2, float scale, BwdFusedCtx fx) {
+    int Hkv, int nb, int nwin, int topk, size_t local_base, float scale_log2, float scale) {
     constexpr int PPT = 32 / G, DT = D / 32, KS = D / 16;
     constexpr int NSTAGE = 2 * 4 * (D / 8);   // staging threads
     __shared__ __align__(16) BwdLds<D> sh;
@@ -173,11 +173,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
 
     BwdItem<LOCAL> it;
     size_t pidx;
-    if constexpr (FUSED) {
-        if (!fused_item<LOCAL>(it, pidx, sh.entries, list, items, fx.item_offsets, total_items, fx.n_keys, B, N, Hkv,
-                               nb, nwin, topk, fx.win))
-            return;
-    } else if constexpr (LOCAL) {
+    if constexpr (LOCAL) {
         const int x = blockIdx.x;
         it.g = x % Hkv;
         it.b = (x / Hkv) % B;
@@ -241,8 +237,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
     }
 
     constexpr float kLog2e = 1.4426950408889634f;
-    // Spare (row, slot) of the dQ partials and the teacher, for rows past the item.
-    const size_t spare = FUSED ? (size_t)B * Hkv * fx.win.len * topk : (size_t)B * Hkv * N * topk;
+    // Spare (row, slot) of the dQ partials, for rows past the item.
+    const size_t spare = (size_t)B * Hkv * N * topk;
     // Tiles are staged two ahead: the threads of half `par` (threadIdx.x / 128)
     // stage the tiles t with t % 2 == par, the global loads of tile t + 2
     // being issued while tiles t and t + 1 are on the matrix cores.
@@ -339,28 +335,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
         // operation before it, so it comes after S and dP (the previous tile's dQ
         // stores have landed by then) and before this tile's stores.
         if (t + 1 < ntiles && ((t + 1) & 1) == par) commit(t + 1);
-        if constexpr (FUSED) {
-            // The KL term's teacher of (position, key): the mean of P over the
-            // position's G head rows, written by the lane holding its first row.
-            float tp[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tp[r] = p[r];
-            head_mean<G>(tp);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                // the lanes holding a position's first row write its mean (for G >= 8 the
-                // same row of both half-waves: they hold the same mean); rows past the item
-                // write the spare row, so the stores are issued on every tile
-                if ((8 * (r / 4) + r % 4) % G == 0) {
-                    const int m = 8 * (r / 4) + 4 * half + r % 4;
-                    const int i = sh_t.pos[m];
-                    const size_t row = i >= 0 ? (((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)) * topk +
-                                                    sh_t.slot[m]
-                                              : spare;
-                    fx.teacher[row * kBlock + key] = tp[r];
-                }
-            }
-        }
         // dV^T += dO^T P and dK^T += Q^T dS over the tile's two 16-row slices.
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
@@ -408,12 +382,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(
             for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
             const int i = sh_t.pos[col];
             // partial of (row (b, g, i), slot), head col % G: [G][D] bf16, each 32-dim slice lane-major
-            // (element 32w + 16h + r holds dim 32w + 8*(r/4) + 4h + r%4); rows of the window's
-            // positions [p0, p0 + len) in the fused backward, of all N otherwise; rows past the
-            // item write the spare partial, so the stores are issued on every tile
-            const size_t drow = FUSED ? ((size_t)it.b * Hkv + it.g) * fx.win.len + (i - fx.win.p0)
-                                      : ((size_t)it.b * Hkv + it.g) * N + i;
-            const size_t prow = i >= 0 ? drow * topk + sh_t.slot[col] : spare;
+            // (element 32w + 16h + r holds dim 32w + 8*(r/4) + 4h + r%4); rows past the item write
+            // the spare partial, so the stores are issued on every tile
+            const size_t prow = i >= 0 ? (((size_t)it.b * Hkv + it.g) * N + i) * topk + sh_t.slot[col] : spare;
             bf16_t* dst = dq_part + prow * G * D + (size_t)(col % G) * D + 32 * w + 16 * half;
             u32x4 w0, w1;
 #pragma unroll
@@ -548,71 +519,21 @@ static hipError_t launch_bwd_t(const LaunchDims& d, const void* q, const void* k
     if (nonlocal) {
         launch_build_lists(d, 0, d.N, block_idx, ws, L.lists, st);
         const size_t grid = (list_items_bound(d, 0, d.N, L.lists) + 63) / 64 * 64;
-        hipLaunchKernelGGL((attn_bwd_kernel<D, G, false, false>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tv, kt,
+        hipLaunchKernelGGL((attn_bwd_kernel<D, G, false>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk, tv, kt,
                            tdo, lse, dl, reinterpret_cast<const int32_t*>(ws + L.lists.list),
                            reinterpret_cast<const int4*>(ws + L.lists.items),
                            reinterpret_cast<const int32_t*>(ws + L.lists.total), dq_part, dkv_part, d.B, d.N, d.Hkv,
-                           d.nb, nwin, d.k, local_base, scale_log2, scale, BwdFusedCtx{});
+                           d.nb, nwin, d.k, local_base, scale_log2, scale);
     }
-    hipLaunchKernelGGL((attn_bwd_kernel<D, G, true, false>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_bwd_kernel<D, G, true>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st,
                        tq, tk, tv, kt, tdo, lse, dl, nullptr, nullptr, nullptr, dq_part, dkv_part, d.B, d.N, d.Hkv,
-                       d.nb, nwin, d.k, local_base, scale_log2, scale, BwdFusedCtx{});
+                       d.nb, nwin, d.k, local_base, scale_log2, scale);
     hipLaunchKernelGGL((dkv_reduce_kernel<D>), dim3((unsigned)(d.B * d.Hkv * d.nb)), dim3(256), 0, st, dkv_part,
                        counts, item_offsets, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), d.B, d.N, d.Hkv, d.nb,
                        nwin, kSegBwd, local_base, nonlocal ? 1 : 0);
     const int64_t units = (int64_t)d.B * d.Hkv * d.N * G * (D / 16);
     hipLaunchKernelGGL((dq_combine_kernel<D, G>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, dq_part,
                        static_cast<bf16_t*>(dq), units, d.N, d.Hkv, d.k, 0, d.N, d.N);
-    return hipGetLastError();
-}
-
-template <int D, int G>
-static void launch_bwd_window_t(const LaunchDims& d, const void* q, const void* k, const void* v, const void* kt,
-                                const void* dout, const float* lse, const float* dl, const int32_t* list,
-                                const int4* items, const int32_t* total, bool nonlocal, void* dq_part,
-                                float* dkv_part, const BwdFusedCtx& fx, float scale, hipStream_t st) {
-    const bf16_t* tq = static_cast<const bf16_t*>(q);
-    const bf16_t* tk = static_cast<const bf16_t*>(k);
-    const bf16_t* tv = static_cast<const bf16_t*>(v);
-    const bf16_t* tkt = static_cast<const bf16_t*>(kt);
-    const bf16_t* tdo = static_cast<const bf16_t*>(dout);
-    bf16_t* dqp = static_cast<bf16_t*>(dq_part);
-    const float scale_log2 = scale * 1.4426950408889634f;
-    const int nwin = windows(d);
-    const int bg = d.B * d.Hkv;
-    const int nqb = (fx.win.len + kBlock - 1) / kBlock;
-    if (nonlocal)
-        hipLaunchKernelGGL((attn_bwd_kernel<D, G, false, true>), dim3((unsigned)(bg * fx.win.bound)), dim3(256), 0,
-                           st, tq, tk, tv, tkt, tdo, lse, dl, list, items, total, dqp, dkv_part, d.B, d.N, d.Hkv,
-                           d.nb, nwin, d.k, (size_t)0, scale_log2, scale, fx);
-    hipLaunchKernelGGL((attn_bwd_kernel<D, G, true, true>), dim3((unsigned)(bg * nqb)), dim3(256), 0, st, tq, tk, tv,
-                       tkt, tdo, lse, dl, nullptr, nullptr, nullptr, dqp, dkv_part, d.B, d.N, d.Hkv, d.nb, nwin, d.k,
-                       (size_t)0, scale_log2, scale, fx);
-}
-
-hipError_t launch_attn_bwd_window(const LaunchDims& d, const void* q, const void* k, const void* v, const void* kt,
-                                  const void* dout, const float* lse, const float* dl, const int32_t* list,
-                                  const int4* items, const int32_t* total, bool nonlocal, void* dq_part,
-                                  float* dkv_part, const BwdFusedCtx& fx, float scale, hipStream_t st) {
-#define MSA_BWD_WIN(DD, GG)                                                                                           \
-    launch_bwd_window_t<DD, GG>(d, q, k, v, kt, dout, lse, dl, list, items, total, nonlocal, dq_part, dkv_part, fx,   \
-                                scale, st)
-#define MSA_BWD_WIN_G(DD)                                                                                             \
-    switch (d.G) {                                                                                                    \
-        case 1: MSA_BWD_WIN(DD, 1); break;                                                                            \
-        case 2: MSA_BWD_WIN(DD, 2); break;                                                                            \
-        case 4: MSA_BWD_WIN(DD, 4); break;                                                                            \
-        case 8: MSA_BWD_WIN(DD, 8); break;                                                                            \
-        case 16: MSA_BWD_WIN(DD, 16); break;                                                                          \
-        default: MSA_BWD_WIN(DD, 32); break;                                                                          \
-    }
-    if (d.D == 128) {
-        MSA_BWD_WIN_G(128)
-    } else {
-        MSA_BWD_WIN_G(64)
-    }
-#undef MSA_BWD_WIN_G
-#undef MSA_BWD_WIN
     return hipGetLastError();
 }
 
