@@ -88,11 +88,28 @@ struct Main8Lds {
 };
 
 // Staging in quarter units: 4 rows x 16 bytes (dims 8*dc .. +7) of Q (units
-// 0 .. D-1) or dO (units D .. 2D-1), the row quarter varying fastest across
-// lanes; rows past the item read its last entry (their P is zero).
+// 0 .. D-1) or dO (units D .. 2D-1); rows past the item read its last entry
+// (their P is zero).
 struct Main8Quarter {
     u32x4 x[4];
 };
+
+// Row quarter rq and 16-byte chunk dc of unit v of a tensor. Eight consecutive
+// lanes read eight consecutive chunks of a row (whole 128-byte lines); the next
+// lane bit picks the row quarter 4 apart (the other half of the same transposed
+// chunk), so that the natural rows (16 lanes: 16 different swizzled chunks) and
+// the transposed 8-byte writes (16 lanes: both halves of 8 chunk slots) of one
+// store instruction fall in different banks.
+template <int D>
+__device__ __forceinline__ void main8_unit(int v, int& rq, int& dc) {
+    if constexpr (D == 128) {
+        dc = (v & 7) | (((v >> 4) & 1) << 3);
+        rq = (((v >> 3) & 1) << 2) | ((v >> 5) & 3);
+    } else {
+        dc = v & 7;
+        rq = (((v >> 3) & 1) << 2) | ((v >> 4) & 3);
+    }
+}
 
 template <int D, int G, bool LOCAL>
 __device__ __forceinline__ void main8_stage_load(Main8Quarter& su, const BwdItem<LOCAL>& it, int t, int u,
@@ -100,7 +117,8 @@ __device__ __forceinline__ void main8_stage_load(Main8Quarter& su, const BwdItem
                                                  int N, int Hq) {
     constexpr int PPT = 32 / G;
     const int tensor = u >= D, v = tensor ? u - D : u;
-    const int rq = v & 7, dc = v >> 3;
+    int rq, dc;
+    main8_unit<D>(v, rq, dc);
     const bf16_t* src = tensor ? dout : q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -115,7 +133,8 @@ template <int D>
 __device__ __forceinline__ void main8_stage_store(const Main8Quarter& su, Main8Tile<D>& tb, int u) {
     using T = Main8Tile<D>;
     const int tensor = u >= D, v = tensor ? u - D : u;
-    const int rq = v & 7, dc = v >> 3;
+    int rq, dc;
+    main8_unit<D>(v, rq, dc);
     unsigned char* nat = tensor ? tb.dout : tb.q;
     unsigned char* tr = tensor ? tb.dot : tb.qt;
 #pragma unroll

@@ -14,16 +14,16 @@ __device__ __forceinline__ int perm16(int x) { return (x & ~12) | ((x & 4) << 1)
 
 // Transposed 32-row tile [D][32 rows, permuted], stored chunk-major: the
 // 16-byte chunk q (rows 8q .. 8q+7 of the permuted order) of dim d sits at
-// q * (16 D + 16) + 16 (d ^ ((d / 8) % 8)). The 16 lanes of a read phase
-// (consecutive d, one q) cover all banks once; the XOR sends the staging
-// writes of one dim offset d % 8 from eight 8-dim groups to eight different
-// 16-byte slots (without it they all hit the same banks), and the 16-byte pad
-// between chunk columns spreads those of different q.
+// q * (16 D + 16) + 16 (d ^ ((d / 8) % 16)). The 16 lanes of a read phase
+// (consecutive d, one q) still cover 16 different 16-byte slots; the XOR sends
+// the staging writes of one dim offset d % 8 from sixteen 8-dim groups to
+// sixteen different slots (without it they all hit the same banks), and the
+// 16-byte pad between chunk columns spreads those of different q.
 template <int D>
 struct ColTile {
     static constexpr int QSTRIDE = 16 * D + 16;
     static constexpr int BYTES = 4 * QSTRIDE;
-    __device__ static __forceinline__ int offset(int d, int q) { return q * QSTRIDE + 16 * (d ^ ((d >> 3) & 7)); }
+    __device__ static __forceinline__ int offset(int d, int q) { return q * QSTRIDE + 16 * (d ^ ((d >> 3) & 15)); }
 };
 
 // Work item of a backward kernel: the rows of one (b, g, key block j) item of
