@@ -16,8 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.hip", "index_topk.hip", "block_lists.hip", "sparse_attn.hip", "sparse_attn_bwd.hip",
-           "kl_align.hip", "kl_align_bwd.hip", "fused_bwd.hip", "decode.hip",
+SOURCES = ["msa_api.hip", "index_topk.hip", "block_lists.hip", "sparse_attn.hip", "kl_align.hip", "fused_bwd.hip", "decode.hip",
            "dense_attn.hip"]
 ARCH = "gfx950"
 FLAGS = [

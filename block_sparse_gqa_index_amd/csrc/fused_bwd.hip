@@ -51,8 +51,38 @@
 #include "msa_bwd_tiles.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace msa {
+
+// ------------------------------------------------------------- row deltas --
+
+// Dl[b, h, i] = <dO[b, i, h], O[b, i, h]> in fp32; D/8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                                                        float* __restrict__ dl, int64_t rows, int N, int Hq) {
+    constexpr int LPR = D / 8;
+    const int64_t row = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / LPR;
+    const int c = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + c * 8);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(dout + row * D + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(x[e] << 16), acc);
+            acc = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(x[e] & 0xffff0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && c == 0) {
+        const int h = (int)(row % Hq);
+        const int64_t bi = row / Hq;   // b * N + i
+        const int64_t b = bi / N, i = bi % N;
+        dl[(b * Hq + h) * N + i] = acc;
+    }
+}
 
 // ----------------------------------------------- main branch, two waves/SIMD --
 
@@ -111,7 +141,7 @@ __device__ __forceinline__ void main8_unit(int v, int& rq, int& dc) {
     }
 }
 
-template <int D, int G, bool LOCAL>
+template <int D, int G, bool LOCAL, bool MAIN>
 __device__ __forceinline__ void main8_stage_load(Main8Quarter& su, const BwdItem<LOCAL>& it, int t, int u,
                                                  const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
                                                  int N, int Hq) {
@@ -129,7 +159,7 @@ __device__ __forceinline__ void main8_stage_load(Main8Quarter& su, const BwdItem
     }
 }
 
-template <int D>
+template <int D, bool MAIN>
 __device__ __forceinline__ void main8_stage_store(const Main8Quarter& su, Main8Tile<D>& tb, int u) {
     using T = Main8Tile<D>;
     const int tensor = u >= D, v = tensor ? u - D : u;
@@ -139,6 +169,7 @@ __device__ __forceinline__ void main8_stage_store(const Main8Quarter& su, Main8T
     unsigned char* tr = tensor ? tb.dot : tb.qt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(nat + T::QT::offset(4 * rq + e, dc * 16)) = su.x[e];
+    if constexpr (!MAIN) return;   // the transposed copies only feed dV and dK
     // rows 4rq .. 4rq+3 are four consecutive positions of chunk rq % 4
     const int chunk = rq & 3, sub = (rq >> 2) * 8;
 #pragma unroll
@@ -180,13 +211,20 @@ __device__ __forceinline__ void head_mean8(float (&p)[8]) {
 
 constexpr int kMain8Waves = 8;
 
-// The main branch of the fused backward with two waves per SIMD: one 8-wave
-// work-group per work item of a window (as attn_bwd_kernel's fused mode), wave
-// w owning keys 16w .. 16w+15 of the block for S, dP, dK, dV (K and V as B
-// operands in VGPRs) and dims 16w .. 16w+15 of the dQ tile (its K^T rows as A
-// operands); 16 x 16 x 32 products throughout. Writes the dQ partials in
-// natural dim order, the dK/dV partial of the item and the teacher.
-template <int D, int G, bool LOCAL>
+// What one pass of the main-branch kernel produces: dQ, dK, dV and the KL
+// term's teacher (the fused backward), the gradients only (the main-branch
+// backward alone), or the teacher only (the KL term's backward alone: S and P,
+// no dP and no gradient products).
+enum Main8Mode { kMainAndTeacher = 0, kMainOnly = 1, kTeacherOnly = 2 };
+
+// The main branch of the backward with two waves per SIMD: one 8-wave
+// work-group per work item of a window, wave w owning keys 16w .. 16w+15 of
+// the block for S, dP, dK, dV (K and V as B operands in VGPRs) and dims
+// 16w .. 16w+15 of the dQ tile (its K^T rows as A operands); 16 x 16 x 32
+// products throughout. Writes the dQ partials in
+// natural dim order, the dK/dV partial of the item and/or the teacher (MODE).
+// With MODE = kTeacherOnly, v, kt, dout, dl, dq_part and dkv_part are unused.
+template <int D, int G, bool LOCAL, int MODE>
 __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ kt, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
@@ -196,6 +234,8 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
     int nb, int nwin, int topk, FusedWindow win, float scale_log2, float scale) {
     constexpr int PPT = 32 / G, DT = D / 16, KS = D / 32;
     constexpr int NTHR = 64 * kMain8Waves;
+    constexpr bool MAIN = MODE != kTeacherOnly, TEACH = MODE != kMainOnly;
+    constexpr int NST = MAIN ? 2 * D : D;   // staging units: Q and dO, or Q only
     static_assert(2 * D <= NTHR - 32, "staging threads and the 32 row-scalar threads share the work-group");
     __shared__ __align__(16) Main8Lds<D> sh;
     using T = Main8Tile<D>;
@@ -220,15 +260,14 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
         const size_t roff = (((size_t)it.b * N + kabs) * Hkv + it.g) * D + 8 * ql;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (kabs < N) {
-                kop[s].load(k + roff + 32 * s);
-                vop[s].load(v + roff + 32 * s);
-            } else {
-                kop[s].zero();
-                vop[s].zero();
+            if (kabs < N) kop[s].load(k + roff + 32 * s);
+            else kop[s].zero();
+            if constexpr (MAIN) {
+                if (kabs < N) vop[s].load(v + roff + 32 * s);
+                else vop[s].zero();
             }
         }
-        if (w < DT) {
+        if (MAIN && w < DT) {
             const bf16_t* src = kt + ((((size_t)it.b * Hkv + it.g) * nb + it.j) * D + 16 * w + cl) * kBlock + 8 * ql;
 #pragma unroll
             for (int c = 0; c < 4; ++c) ktop[c].load(src + 32 * c);
@@ -251,7 +290,7 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
     float r_lse = 0.f, r_dl = 0.f;
     int r_pos = -1, r_slot = 0;
     auto load_tile = [&](int t) {
-        if (u < 2 * D) main8_stage_load<D, G, LOCAL>(su, it, t, u, q, dout, N, Hq);
+        if (u < NST) main8_stage_load<D, G, LOCAL, MAIN>(su, it, t, u, q, dout, N, Hq);
         if (m_row >= 0) {
             const int pe = t * PPT + m_row / G;
             int i, s;
@@ -260,12 +299,12 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
             r_pos = pe < it.count ? i : -1;
             r_slot = s;
             r_lse = lse[r];
-            r_dl = dl[r];
+            if constexpr (MAIN) r_dl = dl[r];
         }
     };
     auto store_tile = [&](int t) {
         T& tb = sh.tile[t & 1];
-        if (u < 2 * D) main8_stage_store<D>(su, tb, u);
+        if (u < NST) main8_stage_store<D, MAIN>(su, tb, u);
         if (m_row >= 0) {
             const bool ok = r_pos >= 0;
             tb.lse2[m_row] = ok ? r_lse * kLog2e : __builtin_inff();
@@ -293,11 +332,14 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
             s[rh] = dp[rh] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                Op8<bf16_t> a, b;
+                Op8<bf16_t> a;
                 a.load(sh_t.q + T::QT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
-                b.load(sh_t.dout + T::QT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
                 mma1632(s[rh], a, kop[ks]);
-                mma1632(dp[rh], b, vop[ks]);
+                if constexpr (MAIN) {
+                    Op8<bf16_t> b;
+                    b.load(sh_t.dout + T::QT::offset(16 * rh + cl, (32 * ks + 8 * ql) * 2));
+                    mma1632(dp[rh], b, vop[ks]);
+                }
             }
         }
         // Staging of tile t + 1 and request of tile t + 2. It waits for every memory
@@ -316,88 +358,94 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
                 if (it.q0 + key > sh_t.pos[m]) pr = 0.f;   // also the rows past the item (pos = -1)
             }
             p[e] = pr;
-            ds[e] = pr * (dp[e >> 2][e & 3] - sh_t.dl[m]);
+            if constexpr (MAIN) ds[e] = pr * (dp[e >> 2][e & 3] - sh_t.dl[m]);
         }
-        // The KL term's teacher of (position, key): the mean of P over the position's
-        // G head rows. The lanes holding a position's first row write it (for G >= 8
-        // also the other lane groups of the position, which hold the same mean); rows
-        // past the item write the spare row, so every tile issues the same stores.
-        {
-            float tp[8];
+        if constexpr (TEACH) {
+            // The KL term's teacher of (position, key): the mean of P over the position's
+            // G head rows. The lanes holding a position's first row write it (for G >= 8
+            // also the other lane groups of the position, which hold the same mean); rows
+            // past the item write the spare row, so every tile issues the same stores.
+            {
+                float tp[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tp[e] = p[e];
-            head_mean8<G>(tp);
+                for (int e = 0; e < 8; ++e) tp[e] = p[e];
+                head_mean8<G>(tp);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if ((e & 3) % (G < 4 ? G : 4) == 0) {
+                for (int e = 0; e < 8; ++e) {
+                    if ((e & 3) % (G < 4 ? G : 4) == 0) {
+                        const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
+                        const int i = sh_t.pos[m];
+                        const size_t row = i >= 0 ? (rbase + i) * topk + sh_t.slot[m] : spare;
+                        teacher[row * kBlock + key] = tp[e];
+                    }
+                }
+            }
+        }
+        if constexpr (MAIN) {
+            // dV^T += dO^T P and dK^T += Q^T dS: the lane's 8 values are the contraction
+            // elements of its key column, in the transposed tiles' row order.
+            {
+                Op8<bf16_t> bp, bds;
+                PType<bf16_t>::pack(bp, p);
+                PType<bf16_t>::pack(bds, ds);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    Op8<bf16_t> a, b;
+                    a.load(sh_t.dot + T::QCT::offset(16 * dt + cl, ql));
+                    b.load(sh_t.qt + T::QCT::offset(16 * dt + cl, ql));
+                    mma1632(dvt[dt], a, bp);
+                    mma1632(dkt[dt], b, bds);
+                }
+            }
+            // dS -> LDS as [row][permuted key] for the dQ product.
+            {
+                uint16_t* dsl = reinterpret_cast<uint16_t*>(sh.ds);
+                const int pk = perm16(key);
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {   // rows m and m + 1: one conversion, two 16-bit stores
                     const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
-                    const int i = sh_t.pos[m];
-                    const size_t row = i >= 0 ? (rbase + i) * topk + sh_t.slot[m] : spare;
-                    teacher[row * kBlock + key] = tp[e];
+                    const uint32_t a2 = pack_bf16x2(ds[e], ds[e + 1]);
+                    dsl[L::DsT::offset(m, pk * 2) / 2] = (uint16_t)(a2 & 0xffffu);
+                    dsl[L::DsT::offset(m + 1, pk * 2) / 2] = (uint16_t)(a2 >> 16);
                 }
             }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS: the lane's 8 values are the contraction
-        // elements of its key column, in the transposed tiles' row order.
-        {
-            Op8<bf16_t> bp, bds;
-            PType<bf16_t>::pack(bp, p);
-            PType<bf16_t>::pack(bds, ds);
+            __syncthreads();
+            // dQ^T (dims 16w.., rows) = K^T dS^T over the block's 128 keys: lane = row
+            // 16 rh + l % 16, accumulators = dims 16w + 4 (l / 16) + r.
+            if (w < DT) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                Op8<bf16_t> a, b;
-                a.load(sh_t.dot + T::QCT::offset(16 * dt + cl, ql));
-                b.load(sh_t.qt + T::QCT::offset(16 * dt + cl, ql));
-                mma1632(dvt[dt], a, bp);
-                mma1632(dkt[dt], b, bds);
-            }
-        }
-        // dS -> LDS as [row][permuted key] for the dQ product.
-        {
-            uint16_t* dsl = reinterpret_cast<uint16_t*>(sh.ds);
-            const int pk = perm16(key);
+                for (int rh = 0; rh < 2; ++rh) {
+                    const int row = 16 * rh + cl;
+                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {   // rows m and m + 1: one conversion, two 16-bit stores
-                const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
-                const uint32_t a2 = pack_bf16x2(ds[e], ds[e + 1]);
-                dsl[L::DsT::offset(m, pk * 2) / 2] = (uint16_t)(a2 & 0xffffu);
-                dsl[L::DsT::offset(m + 1, pk * 2) / 2] = (uint16_t)(a2 >> 16);
-            }
-        }
-        __syncthreads();
-        // dQ^T (dims 16w.., rows) = K^T dS^T over the block's 128 keys: lane = row
-        // 16 rh + l % 16, accumulators = dims 16w + 4 (l / 16) + r.
-        if (w < DT) {
-#pragma unroll
-            for (int rh = 0; rh < 2; ++rh) {
-                const int row = 16 * rh + cl;
-                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    Op8<bf16_t> b;
-                    b.load(sh.ds + L::DsT::offset(row, (32 * c + 8 * ql) * 2));
-                    mma1632(acc, ktop[c], b);
+                    for (int c = 0; c < 4; ++c) {
+                        Op8<bf16_t> b;
+                        b.load(sh.ds + L::DsT::offset(row, (32 * c + 8 * ql) * 2));
+                        mma1632(acc, ktop[c], b);
+                    }
+                    const int i = sh_t.pos[row];
+                    const size_t prow = i >= 0 ? (rbase + i) * topk + sh_t.slot[row] : spare;
+                    // partial of (window row, slot), head row % G: [G][D] bf16 in natural dim order
+                    bf16_t* dst = dq_part + prow * G * D + (size_t)(row % G) * D + 16 * w + 4 * ql;
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0] * scale, acc[1] * scale),
+                                                                pack_bf16x2(acc[2] * scale, acc[3] * scale));
                 }
-                const int i = sh_t.pos[row];
-                const size_t prow = i >= 0 ? (rbase + i) * topk + sh_t.slot[row] : spare;
-                // partial of (window row, slot), head row % G: [G][D] bf16 in natural dim order
-                bf16_t* dst = dq_part + prow * G * D + (size_t)(row % G) * D + 16 * w + 4 * ql;
-                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0] * scale, acc[1] * scale),
-                                                            pack_bf16x2(acc[2] * scale, acc[3] * scale));
             }
         }
     }
 
-    // The item's dK, dV partial: [2][128 keys][D] fp32 (dK scaled by sigma).
-    float* pk = dkv_part + pidx * 2 * kBlock * D + (size_t)key * D;
-    float* pv = pk + (size_t)kBlock * D;
+    if constexpr (MAIN) {
+        // The item's dK, dV partial: [2][128 keys][D] fp32 (dK scaled by sigma).
+        float* pk = dkv_part + pidx * 2 * kBlock * D + (size_t)key * D;
+        float* pv = pk + (size_t)kBlock * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        floatx4 xk;
+        for (int dt = 0; dt < DT; ++dt) {
+            floatx4 xk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xk[e] = dkt[dt][e] * scale;
-        *reinterpret_cast<floatx4*>(pk + 16 * dt + 4 * ql) = xk;
-        *reinterpret_cast<floatx4*>(pv + 16 * dt + 4 * ql) = dvt[dt];
+            for (int e = 0; e < 4; ++e) xk[e] = dkt[dt][e] * scale;
+            *reinterpret_cast<floatx4*>(pk + 16 * dt + 4 * ql) = xk;
+            *reinterpret_cast<floatx4*>(pv + 16 * dt + 4 * ql) = dvt[dt];
+        }
     }
 }
 
@@ -780,6 +828,16 @@ __global__ __launch_bounds__(256) void fused_dki_reduce_kernel(
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+void launch_bwd_delta(const LaunchDims& d, const void* o, const void* dout, float* dl, hipStream_t st) {
+    const int64_t rows = (int64_t)d.B * d.N * d.Hq();
+    if (d.D == 128)
+        hipLaunchKernelGGL((bwd_delta_kernel<128>), dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), dl, rows, d.N, d.Hq());
+    else
+        hipLaunchKernelGGL((bwd_delta_kernel<64>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), dl, rows, d.N, d.Hq());
+}
+
 // Work-item slots per (b, g) in one window: every key's items (a list entry per
 // kept non-local block of the window's rows, cut every kSegBwd) fit in
 // ceil(W (k-1) / kSegBwd) + nb.
@@ -789,33 +847,35 @@ static int fused_bound(const LaunchDims& d) {
     return (int)((W * kp + kSegBwd - 1) / kSegBwd + (size_t)d.nb);
 }
 
-FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d) {
+FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d, BwdParts parts) {
     FusedBwdWorkspace w{};
     const size_t W = (size_t)std::min(d.N, kWindow);
     const size_t bg = (size_t)d.B * d.Hkv;
+    const bool mn = parts.main, kl = parts.kl;
+    const bool multi = windows(d) > 1;   // running sums across windows
     size_t off = 0;
-    w.kt = off;    off = align_up(off + bg * d.nb * d.D * kBlock * 2);
-    w.kit = off;   off = align_up(off + (size_t)d.B * d.nb * d.Di * kBlock * 2);
-    w.dl = off;    off = align_up(off + (size_t)d.B * d.Hq() * d.N * 4);
+    w.kt = off;    off = align_up(off + (mn ? bg * d.nb * d.D * kBlock * 2 : 0));
+    w.kit = off;   off = align_up(off + (kl ? (size_t)d.B * d.nb * d.Di * kBlock * 2 : 0));
+    w.dl = off;    off = align_up(off + (mn ? (size_t)d.B * d.Hq() * d.N * 4 : 0));
     w.lists = list_layout(d, off, kSegBwd, true);
     off = w.lists.end;
     w.bound = w.lists.has_nonlocal ? fused_bound(d) : 0;
-    w.teacher = off;   off = align_up(off + (bg * W * d.k + 1) * kBlock * 4);   // + spare row
     w.items = bg * w.bound + bg * ((W + kBlock - 1) / kBlock);   // non-local slots, then local ones
-    w.dq_part = off;   off = align_up(off + (bg * W * d.k + 1) * d.G * d.D * 2);   // + spare
-    w.dqi_part = off;  off = align_up(off + bg * W * d.k * d.Di * 2);
-    w.dkv_part = off;  off = align_up(off + w.items * 2 * kBlock * d.D * 4);
-    w.dki_part = off;  off = align_up(off + w.items * kBlock * d.Di * 4);
-    const bool multi = windows(d) > 1;   // running sums across windows
-    w.acc_dkv = off;   off = align_up(off + (multi ? bg * d.nb * 2 * kBlock * d.D * 4 : 0));
-    w.acc_dki = off;   off = align_up(off + (multi ? (size_t)d.B * d.nb * kBlock * d.Di * 4 : 0));
+    w.teacher = off;   off = align_up(off + (kl ? (bg * W * d.k + 1) * kBlock * 4 : 0));   // + spare row
+    w.dq_part = off;   off = align_up(off + (mn ? (bg * W * d.k + 1) * d.G * d.D * 2 : 0));   // + spare
+    w.dqi_part = off;  off = align_up(off + (kl ? bg * W * d.k * d.Di * 2 : 0));
+    w.dkv_part = off;  off = align_up(off + (mn ? w.items * 2 * kBlock * d.D * 4 : 0));
+    w.dki_part = off;  off = align_up(off + (kl ? w.items * kBlock * d.Di * 4 : 0));
+    w.acc_dkv = off;   off = align_up(off + (mn && multi ? bg * d.nb * 2 * kBlock * d.D * 4 : 0));
+    w.acc_dki = off;   off = align_up(off + (kl && multi ? (size_t)d.B * d.nb * kBlock * d.Di * 4 : 0));
     w.bytes = off;
     return w;
 }
 
 template <int D, int DI, int G>
 static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, unsigned char* ws, hipStream_t st) {
-    const FusedBwdWorkspace L = fused_bwd_workspace_layout(d);
+    const FusedBwdWorkspace L = fused_bwd_workspace_layout(d, a.parts);
+    const bool mn = a.parts.main, kl = a.parts.kl;
     const bf16_t* tq = static_cast<const bf16_t*>(a.q);
     const bf16_t* tk = static_cast<const bf16_t*>(a.k);
     const bf16_t* tv = static_cast<const bf16_t*>(a.v);
@@ -834,15 +894,20 @@ static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, uns
     float* acc_dki = reinterpret_cast<float*>(ws + L.acc_dki);
     const int nwin = windows(d);
 
-    hipError_t e = launch_transpose_kv(d, a.k, kt, st);
-    if (e != hipSuccess) return e;
-    LaunchDims di = d;   // k_idx as a one-head [B, N, 1, Di] tensor
-    di.Hkv = 1;
-    di.G = 1;
-    di.D = d.Di;
-    e = launch_transpose_kv(di, a.k_idx, kit, st);
-    if (e != hipSuccess) return e;
-    launch_bwd_delta(d, a.o, a.dout, dl, st);
+    hipError_t e = hipSuccess;
+    if (mn) {
+        e = launch_transpose_kv(d, a.k, kt, st);
+        if (e != hipSuccess) return e;
+        launch_bwd_delta(d, a.o, a.dout, dl, st);
+    }
+    if (kl) {
+        LaunchDims di = d;   // k_idx as a one-head [B, N, 1, Di] tensor
+        di.Hkv = 1;
+        di.G = 1;
+        di.D = d.Di;
+        e = launch_transpose_kv(di, a.k_idx, kit, st);
+        if (e != hipSuccess) return e;
+    }
     const bool nonlocal = L.lists.has_nonlocal;
     if (nonlocal) launch_build_lists(d, 0, d.N, a.block_idx, ws, L.lists, st);
     const int32_t* list = reinterpret_cast<const int32_t*>(ws + L.lists.list);
@@ -862,36 +927,49 @@ static hipError_t launch_fused_t(const LaunchDims& d, const FusedBwdArgs& a, uns
         const int nqb = (win.len + kBlock - 1) / kBlock;
         const int nbw = win.qb0 + nqb;   // key blocks the window's rows can keep
         const int last = w == nwin - 1;
-        if (nonlocal)
-            hipLaunchKernelGGL((main8_bwd_kernel<D, G, false>), dim3((unsigned)(bg * L.bound)), dim3(64 * kMain8Waves),
-                               0, st, tq, tk, tv, kt, tdo, a.lse, dl, list, items, item_offsets, total,
-                               (int)L.lists.n_keys, dq_part, dkv_part, teacher, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win,
-                               scale_log2, a.scale);
-        hipLaunchKernelGGL((main8_bwd_kernel<D, G, true>), dim3((unsigned)(bg * nqb)), dim3(64 * kMain8Waves), 0, st,
-                           tq, tk, tv, kt, tdo, a.lse, dl, nullptr, nullptr, nullptr, nullptr, 0, dq_part, dkv_part,
-                           teacher, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win, scale_log2, a.scale);
-        if (nonlocal)
-            hipLaunchKernelGGL((fused_index_kernel<DI, false>), dim3((unsigned)(bg * L.bound)), dim3(256), 0, st, tqi,
-                               tki, kit, a.index_lse, a.dkl_rows, a.kl_weight, teacher, list, items, item_offsets,
-                               total, (int)L.lists.n_keys, dqi_part, dki_part, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win,
-                               a.iscale);
-        hipLaunchKernelGGL((fused_index_kernel<DI, true>), dim3((unsigned)(bg * nqb)), dim3(256), 0, st, tqi, tki, kit,
-                           a.index_lse, a.dkl_rows, a.kl_weight, teacher, nullptr, nullptr, nullptr, nullptr, 0,
-                           dqi_part, dki_part, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win, a.iscale);
-        hipLaunchKernelGGL((fused_dkv_reduce_kernel<D>), dim3((unsigned)(bg * nbw)), dim3(256), 0, st, dkv_part,
-                           counts, item_offsets, acc_dkv, static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv), d.B,
-                           d.N, d.Hkv, d.nb, nwin, kSegBwd, win, nbw, last, nonlocal ? 1 : 0);
-        hipLaunchKernelGGL((fused_dki_reduce_kernel<DI>), dim3((unsigned)(d.B * nbw)), dim3(256), 0, st, dki_part,
-                           counts, item_offsets, acc_dki, static_cast<bf16_t*>(a.dk_idx), d.B, d.N, d.Hkv, d.nb, nwin,
-                           kSegBwd, win, nbw, last, nonlocal ? 1 : 0);
-        const int64_t units = (int64_t)bg * win.len * G * (D / 16);
-        hipLaunchKernelGGL((dq_combine_kernel<D, G, true>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st,
-                           dq_part,
-                           static_cast<bf16_t*>(a.dq), units, d.N, d.Hkv, d.k, win.p0, win.len, win.len);
-        const int64_t iunits = (int64_t)bg * win.len * (DI / 16);
-        hipLaunchKernelGGL((dq_combine_kernel<DI, 1>), dim3((unsigned)((iunits + 255) / 256)), dim3(256), 0, st,
-                           dqi_part, static_cast<bf16_t*>(a.dq_idx), iunits, d.N, d.Hkv, d.k, win.p0, win.len,
-                           win.len);
+        // the main-branch kernel of the parts asked for
+        auto main_pass = [&](auto mode) {
+            constexpr int M = decltype(mode)::value;
+            if (nonlocal)
+                hipLaunchKernelGGL((main8_bwd_kernel<D, G, false, M>), dim3((unsigned)(bg * L.bound)),
+                                   dim3(64 * kMain8Waves), 0, st, tq, tk, tv, kt, tdo, a.lse, dl, list, items,
+                                   item_offsets, total, (int)L.lists.n_keys, dq_part, dkv_part, teacher, d.B, d.N,
+                                   d.Hkv, d.nb, nwin, d.k, win, scale_log2, a.scale);
+            hipLaunchKernelGGL((main8_bwd_kernel<D, G, true, M>), dim3((unsigned)(bg * nqb)), dim3(64 * kMain8Waves),
+                               0, st, tq, tk, tv, kt, tdo, a.lse, dl, nullptr, nullptr, nullptr, nullptr, 0, dq_part,
+                               dkv_part, teacher, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win, scale_log2, a.scale);
+        };
+        if (mn && kl) main_pass(std::integral_constant<int, kMainAndTeacher>{});
+        else if (mn) main_pass(std::integral_constant<int, kMainOnly>{});
+        else main_pass(std::integral_constant<int, kTeacherOnly>{});
+        if (kl) {
+            if (nonlocal)
+                hipLaunchKernelGGL((fused_index_kernel<DI, false>), dim3((unsigned)(bg * L.bound)), dim3(256), 0, st,
+                                   tqi, tki, kit, a.index_lse, a.dkl_rows, a.kl_weight, teacher, list, items,
+                                   item_offsets, total, (int)L.lists.n_keys, dqi_part, dki_part, d.B, d.N, d.Hkv, d.nb,
+                                   nwin, d.k, win, a.iscale);
+            hipLaunchKernelGGL((fused_index_kernel<DI, true>), dim3((unsigned)(bg * nqb)), dim3(256), 0, st, tqi, tki,
+                               kit, a.index_lse, a.dkl_rows, a.kl_weight, teacher, nullptr, nullptr, nullptr, nullptr,
+                               0, dqi_part, dki_part, d.B, d.N, d.Hkv, d.nb, nwin, d.k, win, a.iscale);
+        }
+        if (mn) {
+            hipLaunchKernelGGL((fused_dkv_reduce_kernel<D>), dim3((unsigned)(bg * nbw)), dim3(256), 0, st, dkv_part,
+                               counts, item_offsets, acc_dkv, static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv),
+                               d.B, d.N, d.Hkv, d.nb, nwin, kSegBwd, win, nbw, last, nonlocal ? 1 : 0);
+            const int64_t units = (int64_t)bg * win.len * G * (D / 16);
+            hipLaunchKernelGGL((dq_combine_kernel<D, G, true>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
+                               st, dq_part, static_cast<bf16_t*>(a.dq), units, d.N, d.Hkv, d.k, win.p0, win.len,
+                               win.len);
+        }
+        if (kl) {
+            hipLaunchKernelGGL((fused_dki_reduce_kernel<DI>), dim3((unsigned)(d.B * nbw)), dim3(256), 0, st, dki_part,
+                               counts, item_offsets, acc_dki, static_cast<bf16_t*>(a.dk_idx), d.B, d.N, d.Hkv, d.nb,
+                               nwin, kSegBwd, win, nbw, last, nonlocal ? 1 : 0);
+            const int64_t iunits = (int64_t)bg * win.len * (DI / 16);
+            hipLaunchKernelGGL((dq_combine_kernel<DI, 1>), dim3((unsigned)((iunits + 255) / 256)), dim3(256), 0, st,
+                               dqi_part, static_cast<bf16_t*>(a.dq_idx), iunits, d.N, d.Hkv, d.k, win.p0, win.len,
+                               win.len);
+        }
     }
     return hipGetLastError();
 }

@@ -188,15 +188,15 @@ size_t msa_workspace_bytes(const msa_dims* dims, int op) {
         case MSA_OP_INDEX: return 0;
         case MSA_OP_ATTN:
         case MSA_OP_FORWARD: return msa::attn_workspace_layout(L).bytes;
-        case MSA_OP_ATTN_BWD: return msa::bwd_workspace_layout(L).bytes;
+        case MSA_OP_ATTN_BWD: return msa::fused_bwd_workspace_layout(L, msa::BwdParts{true, false}).bytes;
         case MSA_OP_KL: return msa::kl_workspace_layout(L).bytes;
-        case MSA_OP_KL_BWD: return msa::kl_bwd_workspace_layout(L).bytes;
+        case MSA_OP_KL_BWD: return msa::fused_bwd_workspace_layout(L, msa::BwdParts{false, true}).bytes;
         case MSA_OP_DECODE_INDEX:
         case MSA_OP_DECODE_ATTN: return decode_ws(L, op, 1);
         case MSA_OP_DENSE_ATTN: return msa::dense_workspace_bytes(L);
         case MSA_OP_DENSE_KL: return msa::dense_kl_workspace_bytes(L);
         case MSA_OP_DECODE: return decode_ws(L, op, 1);
-        case MSA_OP_FUSED_BWD: return msa::fused_bwd_workspace_layout(L).bytes;
+        case MSA_OP_FUSED_BWD: return msa::fused_bwd_workspace_layout(L, msa::BwdParts{true, true}).bytes;
         default: return 0;
     }
 }
@@ -281,11 +281,22 @@ int msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* k, cons
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(o) ||
         !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return MSA_ERR_ALIGN;
-    const size_t need = msa::bwd_workspace_layout(L).bytes;
+    const size_t need = msa::fused_bwd_workspace_layout(L, msa::BwdParts{true, false}).bytes;
     if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
-    return hip_status(msa::launch_sparse_attn_bwd(L, q, k, v, block_idx, o, lse, dout, scale, dq, dk, dv, ws,
-                                                  static_cast<hipStream_t>(stream)));
+    msa::FusedBwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.block_idx = block_idx;
+    a.lse = lse;
+    a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.parts = msa::BwdParts{true, false};
+    return hip_status(msa::launch_fused_bwd(L, a, ws, static_cast<hipStream_t>(stream)));
 }
 
 int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
@@ -324,13 +335,24 @@ int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k, const v
         !aligned16(lse) || !aligned16(index_lse) || !aligned16(dkl_rows) || !aligned16(dq_idx) ||
         !aligned16(dk_idx))
         return MSA_ERR_ALIGN;
-    const size_t need = msa::kl_bwd_workspace_layout(L).bytes;
+    const size_t need = msa::fused_bwd_workspace_layout(L, msa::BwdParts{false, true}).bytes;
     if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
-    const float iscale = index_scale > 0.f ? index_scale : 1.0f / sqrtf((float)L.Di);
-    return hip_status(msa::launch_kl_align_bwd(L, q, k, q_idx, k_idx, block_idx, lse, index_lse, scale, iscale,
-                                               dkl_rows, kl_weight, dq_idx, dk_idx, ws,
-                                               static_cast<hipStream_t>(stream)));
+    msa::FusedBwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.block_idx = block_idx;
+    a.lse = lse;
+    a.index_lse = index_lse;
+    a.dkl_rows = dkl_rows;
+    a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)L.D);
+    a.iscale = index_scale > 0.f ? index_scale : 1.0f / sqrtf((float)L.Di);
+    a.kl_weight = kl_weight;
+    a.dq_idx = dq_idx;
+    a.dk_idx = dk_idx;
+    a.parts = msa::BwdParts{false, true};
+    return hip_status(msa::launch_fused_bwd(L, a, ws, static_cast<hipStream_t>(stream)));
 }
 
 int msa_fused_bwd(const msa_dims* dims, const void* q, const void* k, const void* v, const void* q_idx,
@@ -348,9 +370,9 @@ int msa_fused_bwd(const msa_dims* dims, const void* q, const void* k, const void
                           dout, (const void*)dkl_rows, (const void*)dq, (const void*)dk, (const void*)dv,
                           (const void*)dq_idx, (const void*)dk_idx})
         if (!aligned16(p)) return MSA_ERR_ALIGN;
-    const size_t need = msa::fused_bwd_workspace_layout(L).bytes;
+    const size_t need = msa::fused_bwd_workspace_layout(L, msa::BwdParts{true, true}).bytes;
     if (!ws || ws_bytes < need || !aligned16(ws)) return MSA_ERR_WORKSPACE;
-    msa::FusedBwdArgs a;
+    msa::FusedBwdArgs a{};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -370,6 +392,7 @@ int msa_fused_bwd(const msa_dims* dims, const void* q, const void* k, const void
     a.dv = dv;
     a.dq_idx = dq_idx;
     a.dk_idx = dk_idx;
+    a.parts = msa::BwdParts{true, true};
     return hip_status(msa::launch_fused_bwd(L, a, ws, static_cast<hipStream_t>(stream)));
 }
 

@@ -1,5 +1,5 @@
-// Pieces shared by the two backward kernels (main branch and KL term): both
-// visit the rows of one key block in 32-row tiles, key-block-outer, over the
+// Pieces shared by the backward kernels (main branch and KL term): both visit
+// the rows of one key block in 32-row tiles, key-block-outer, over the
 // position-sorted selection lists.
 #pragma once
 
@@ -89,27 +89,6 @@ __device__ __forceinline__ bool fused_item(BwdItem<LOCAL>& it, size_t& pidx, int
         __syncthreads();
         return true;
     }
-}
-
-// Teacher of the row in accumulator r: the mean of P over the G rows of the
-// same position. Rows 8*(r/4) + 4h + r%4 of position m / G: the G rows of a
-// position are aligned groups of min(G, 16) accumulators (G <= 4 within one
-// half-wave's group of four), the other half-wave holding the rest for G >= 8.
-template <int G>
-__device__ __forceinline__ void head_mean(float (&p)[16]) {
-    constexpr int GS = G >= 32 ? 16 : (G >= 16 ? 8 : (G >= 4 ? 4 : G));
-    float t[16];
-#pragma unroll
-    for (int r0 = 0; r0 < 16; r0 += GS) {
-        float a = 0.f;
-#pragma unroll
-        for (int x = 0; x < GS; ++x) a += p[r0 + x];
-        if constexpr (G >= 8) a += swap_halves(a);
-#pragma unroll
-        for (int x = 0; x < GS; ++x) t[r0 + x] = a * (1.f / G);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = t[r];
 }
 
 // Per row: the sum of its slots' bf16 partials in slot order (dQ, with G heads

@@ -40,11 +40,6 @@ struct AttnWorkspace {
     size_t vt, po, plse, bytes;
 };
 
-struct BwdWorkspace {
-    ListLayout lists;   // position-sorted, kSegBwd entries per item
-    size_t kt, dl, dq_part, dkv_part, bytes;
-    size_t local_items, dkv_items;   // dK/dV partials: list items first, then one per (b, g, block)
-};
 
 struct KlWorkspace {
     ExpandLayout ex;   // Bk != 128 only
@@ -78,7 +73,6 @@ size_t list_items_bound(const LaunchDims& d, int p_lo, int p_hi, const ListLayou
 hipError_t launch_check_block_idx(const LaunchDims& d, const int32_t* block_idx, int32_t* bad, hipStream_t st);
 
 AttnWorkspace attn_workspace_layout(const LaunchDims& d);
-BwdWorkspace bwd_workspace_layout(const LaunchDims& d);
 KlWorkspace kl_workspace_layout(const LaunchDims& d);
 
 // Selection for the query blocks [qb_lo, qb_hi).
@@ -98,10 +92,6 @@ hipError_t launch_sparse_attn(const LaunchDims& d, int qb_lo, int qb_hi, const v
                               const int32_t* block_idx, float scale, void* o, float* lse, void* ws, int stages,
                               hipStream_t st);
 
-// Main-branch backward (bf16): dq [B,N,Hq,D], dk, dv [B,N,Hkv,D].
-hipError_t launch_sparse_attn_bwd(const LaunchDims& d, const void* q, const void* k, const void* v,
-                                  const int32_t* block_idx, const void* o, const float* lse, const void* dout,
-                                  float scale, void* dq, void* dk, void* dv, void* ws, hipStream_t st);
 
 // KL forward; index_lse (nullable) receives the student's natural-log LSE per row.
 hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
@@ -109,32 +99,24 @@ hipError_t launch_kl_align(const LaunchDims& d, const void* q, const void* k, co
                            float index_scale, float* kl_rows, float* kl_sum, float* index_lse, void* ws,
                            hipStream_t st);
 
-struct KlBwdWorkspace {
-    ListLayout lists;   // position-sorted, kSegBwd entries per item
-    size_t kit, dqi_part, dki_part, bytes;
-    size_t local_items, dki_items;
-};
-KlBwdWorkspace kl_bwd_workspace_layout(const LaunchDims& d);
-
-// KL backward (bf16): dq_idx [B,N,Hkv,Di], dk_idx [B,N,Di] for the loss
-// sum_rows w_row KL_row, w_row = kl_weight * (dkl_rows ? dkl_rows[row] : 1).
-hipError_t launch_kl_align_bwd(const LaunchDims& d, const void* q, const void* k, const void* q_idx,
-                               const void* k_idx, const int32_t* block_idx, const float* lse,
-                               const float* index_lse, float scale, float index_scale, const float* dkl_rows,
-                               float kl_weight, void* dq_idx, void* dk_idx, void* ws, hipStream_t st);
-
 // Dl = <dO, O> per (b, h, i) row in fp32 ([B, Hq, N]).
 void launch_bwd_delta(const LaunchDims& d, const void* o, const void* dout, float* dl, hipStream_t st);
 
-// Fused backward of both branches (bf16): dq, dk, dv of the main branch for
-// <dO, O> and dq_idx, dk_idx of the KL term for sum_rows w_row KL_row, query
-// window by query window of kWindow positions.
+// Backward over the cached block ids (bf16), query window by query window of
+// kWindow positions: dq, dk, dv of the main branch for <dO, O> and/or dq_idx,
+// dk_idx of the KL term for sum_rows w_row KL_row (both from one pass in which
+// the main-branch probabilities are computed once). BwdParts: the parts one
+// call computes (the pointers of a part not computed are unused).
+struct BwdParts {
+    bool main, kl;
+};
 struct FusedBwdArgs {
     const void *q, *k, *v, *q_idx, *k_idx, *o, *dout;
     const int32_t* block_idx;
     const float *lse, *index_lse, *dkl_rows;
     float scale, iscale, kl_weight;
     void *dq, *dk, *dv, *dq_idx, *dk_idx;
+    BwdParts parts;
 };
 struct FusedBwdWorkspace {
     ListLayout lists;   // position-sorted, kSegBwd entries per item, for the whole sequence
@@ -142,7 +124,7 @@ struct FusedBwdWorkspace {
     int bound;          // non-local work-item slots per (b, g) and window
     size_t items;       // partial slots of one window: non-local, then local
 };
-FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d);
+FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d, BwdParts parts);
 hipError_t launch_fused_bwd(const LaunchDims& d, const FusedBwdArgs& a, void* ws, hipStream_t st);
 
 // Window of the fused backward: query positions [p0, p0 + len) of every
