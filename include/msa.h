@@ -219,9 +219,12 @@ MSA_API int msa_forward(const msa_dims* dims, const void* q_idx, const void* k_i
  *   dk, dv    [B, N, Hkv, D]  OUTPUT bf16 (every key is written; keys no row
  *             selects get 0)
  *   ws        at least msa_workspace_bytes(dims, MSA_OP_ATTN_BWD) bytes
- *             (per-(row, slot) dQ partials and per-work-item dK/dV partials;
- *             about 37 GB for N = 128K, Hkv = 8, G = 8, D = 128, k = 16).
- * Deterministic: every sum runs in a fixed order.
+ *             (the query rows are processed 65,536 positions at a time: the
+ *             window's per-(row, slot) dQ partials and per-work-item dK/dV
+ *             partials, fp32 running sums across windows; about 21 GB for
+ *             N = 128K, Hkv = 8, G = 8, D = 128, k = 16, 24 GB at N = 1M, Hkv 4).
+ * Deterministic: every sum runs in a fixed order. This is msa_fused_bwd's
+ * pass without the KL term.
  */
 MSA_API int msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* k, const void* v,
                                 const int32_t* block_idx, const void* o, const float* lse, const void* dout,
@@ -276,8 +279,12 @@ MSA_API int msa_kl_align_fwd(const msa_dims* dims, const void* q, const void* k,
  *   dkl_rows  [B, Hkv, N] fp32 row weights, or NULL for all ones
  *   dq_idx    [B, N, Hkv, Di] OUTPUT bf16
  *   dk_idx    [B, N, Di]      OUTPUT bf16 (every key written; 0 if unseen)
- *   ws        at least msa_workspace_bytes(dims, MSA_OP_KL_BWD) bytes.
- * Deterministic: every sum runs in a fixed order.
+ *   ws        at least msa_workspace_bytes(dims, MSA_OP_KL_BWD) bytes (65,536
+ *             query positions at a time: the teacher p per (row, slot, key),
+ *             dq_idx and dk_idx partials; about 8 GB at N = 128K, Hkv = 8,
+ *             11 GB at N = 1M, Hkv = 4).
+ * Deterministic: every sum runs in a fixed order. This is msa_fused_bwd's
+ * pass without the main-branch gradients (S and P only, for the teacher).
  */
 MSA_API int msa_kl_align_bwd(const msa_dims* dims, const void* q, const void* k, const void* q_idx,
                              const void* k_idx, const int32_t* block_idx, const float* lse,
