@@ -632,13 +632,7 @@ __global__ __launch_bounds__(256, 2) void fused_index_kernel(
         // Tile t is complete in its buffer; the other buffer's readers (tile
         // t - 1) and the dU readers are done.
         __syncthreads();
-        if (t + 1 < ntiles && ((t + 1) & 1) == par) commit(t + 1);   // overlaps tile t's math
         const T& sh_t = sh.tile[t & 1];
-        float tc[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tc[r] = tn[r];
-        if (t + 1 < ntiles) teacher_load(t + 1);
-
         floatx16 uu = zero16();
 #pragma unroll
         for (int sl = 0; sl < DI / 16; ++sl) {
@@ -646,6 +640,15 @@ __global__ __launch_bounds__(256, 2) void fused_index_kernel(
             a.load(sh_t.qi + T::IT::offset(col, (16 * sl + 8 * half) * 2));
             mma16(uu, a, kiop[sl]);
         }
+        // Staging of tile t + 1 (overlaps tile t's math) and the teacher of tile
+        // t + 1. The staging waits for every memory operation before it, so it
+        // comes after U (the previous tile's stores and this tile's teacher have
+        // landed by then) and before this tile's stores and the next teacher loads.
+        if (t + 1 < ntiles && ((t + 1) & 1) == par) commit(t + 1);
+        float tc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tc[r] = tn[r];
+        if (t + 1 < ntiles) teacher_load(t + 1);
         float du[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
