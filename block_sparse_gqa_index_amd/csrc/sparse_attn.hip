@@ -156,14 +156,15 @@ __device__ __forceinline__ void mask_halves(floatx16 (&s)[4], int m) {
 
 // One 32-row tile of a non-local work item: the lane's row is list entry `e`
 // (position << 5 | slot); scores against the staged block, softmax, P V and
-// the partial store (skipped for the padding rows past the item's end). HM:
+// the partial store (to the spare partial for the padding rows past the
+// item's end). HM:
 // the entry keeps only the halves its mask byte names (64-token selections).
 template <typename T, int D, int G, bool HM>
 __device__ __forceinline__ void nonlocal_tile(const Op8<T> (&qop)[D / 16], int e, bool valid,
                                               const unsigned char* lds, T* __restrict__ po,
                                               float* __restrict__ plse, int b, int g, int N, int Hkv, int KP,
                                               const uint8_t* __restrict__ hmask, float scale_log2, int hh, int col,
-                                              int half) {
+                                              int half, size_t spare) {
     floatx16 s[4];
     tile_scores<T, D>(s, qop, lds, col, half);
     if constexpr (HM) mask_halves(s, hmask[(((size_t)b * Hkv + g) * N + (e >> 5)) * (KP + 1) + (e & 31)]);
@@ -173,10 +174,10 @@ __device__ __forceinline__ void nonlocal_tile(const Op8<T> (&qop)[D / 16], int e
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
     tile_pv<T, D>(o, s, lds, col, half);
-    if (valid) {
-        const int i = e >> 5, slot = e & 31;
-        store_partial<T, D, G>(po, plse, (((size_t)b * Hkv + g) * N + i) * KP + slot, hh, half, o, mz, l);
-    }
+    // Padding rows store to the spare partial so the store is unconditional
+    // (the next tile's waits then count it in order with the loads).
+    const size_t pidx = valid ? (((size_t)b * Hkv + g) * N + (e >> 5)) * KP + (e & 31) : spare;
+    store_partial<T, D, G>(po, plse, pidx, hh, half, o, mz, l);
 }
 
 // One work-group per work item (batch, group, key block j, <= kSeg query
@@ -187,7 +188,7 @@ template <typename T, int D, int G, bool HM>
 __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ list, const int4* __restrict__ items, const int32_t* __restrict__ total_items,
     const T* __restrict__ vt, T* __restrict__ po, float* __restrict__ plse, const uint8_t* __restrict__ hmask, int N,
-    int Hkv, int nb, int nwin, int KP, float scale_log2) {
+    int Hkv, int nb, int nwin, int KP, float scale_log2, size_t spare) {
     using KV = KVTile<T, D>;
     constexpr int PPT = 32 / G;   // positions per 32-row tile
     __shared__ __align__(16) unsigned char lds[KV::BYTES];
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     int base = w * PPT;
     int e_cur = list[start + min(base + pp, count - 1)];
     Op8<T> q_cur[D / 16];
-    load_q_op<T, D>(q_cur, qbase + (size_t)(e_cur >> 5) * Hq * D, base + pp < count, half);
+    load_q_op<T, D>(q_cur, qbase + (size_t)(e_cur >> 5) * Hq * D, true, half);
     int e_nxt = list[start + min(base + stride + pp, count - 1)];
 
     const size_t kv_row = (size_t)Hkv * D;
@@ -226,15 +227,15 @@ __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     // the next tile's rows load into the other.
     Op8<T> q_nxt[D / 16];
     for (; base < count; base += 2 * stride) {
-        load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, base + stride + pp < count, half);
+        load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, true, half);
         const int e_2 = list[start + min(base + 2 * stride + pp, count - 1)];
         nonlocal_tile<T, D, G, HM>(q_cur, e_cur, base + pp < count, lds, po, plse, b, g, N, Hkv, KP, hmask,
-                                   scale_log2, hh, col, half);
+                                   scale_log2, hh, col, half, spare);
         if (base + stride >= count) break;
-        load_q_op<T, D>(q_cur, qbase + (size_t)(e_2 >> 5) * Hq * D, base + 2 * stride + pp < count, half);
+        load_q_op<T, D>(q_cur, qbase + (size_t)(e_2 >> 5) * Hq * D, true, half);
         const int e_3 = list[start + min(base + 3 * stride + pp, count - 1)];
         nonlocal_tile<T, D, G, HM>(q_nxt, e_nxt, base + stride + pp < count, lds, po, plse, b, g, N, Hkv, KP,
-                                   hmask, scale_log2, hh, col, half);
+                                   hmask, scale_log2, hh, col, half, spare);
         e_cur = e_2;
         e_nxt = e_3;
     }
@@ -412,8 +413,9 @@ AttnWorkspace attn_workspace_layout(const LaunchDims& d) {
     w.lists = list_layout(e, off);
     if (w.lists.has_nonlocal) {
         off = w.lists.end;
-        w.po = off;    off = align_up(off + w.lists.max_entries * e.G * e.D * es);
-        w.plse = off;  off = align_up(off + w.lists.max_entries * e.G * 4);
+        // One spare (row, slot) past the last: the padding rows' partials.
+        w.po = off;    off = align_up(off + (w.lists.max_entries + 1) * e.G * e.D * es);
+        w.plse = off;  off = align_up(off + (w.lists.max_entries + 1) * e.G * 4);
     }
     w.bytes = off;
     return w;
@@ -452,10 +454,12 @@ static hipError_t launch_attn_t(const LaunchDims& d0, int qb_lo, int qb_hi, cons
         const size_t grid = (list_items_bound(d, p_lo, p_hi, L.lists) + 63) / 64 * 64;
         if ((stages & 2) && hm)
             hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G, true>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
-                               list, items, total, vt, po, plse, hmask, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
+                               list, items, total, vt, po, plse, hmask, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2,
+                               L.lists.max_entries);
         else if (stages & 2)
             hipLaunchKernelGGL((attn_nonlocal_kernel<T, D, G, false>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
-                               list, items, total, vt, po, plse, hmask, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2);
+                               list, items, total, vt, po, plse, hmask, d.N, d.Hkv, d.nb, windows(d), KP, scale_log2,
+                               L.lists.max_entries);
     }
     if (stages & 4) {
         const dim3 grid((unsigned)((qb_hi - qb_lo) * d.B * d.Hkv));
