@@ -472,17 +472,33 @@ struct IdxBwdLds {
     int entries[kSegBwd];
 };
 
-// One 4-row x 16-byte unit of the staging: rows 4rq .. 4rq+3 at dims 8*dc .. +7
-// (unit u of the 8 * (DI/8) units of a tile: rq = u % 8, dc = u / 8). Rows
-// 4rq .. 4rq+3 are four consecutive positions of one transposed chunk.
+// One 4-row x 16-byte unit of the staging: rows 4rq .. 4rq+3 at dims 8*dc .. +7.
+// Rows 4rq .. 4rq+3 are four consecutive positions of one transposed chunk.
 struct IdxUnit {
     u32x4 x[4];
 };
 
+// Row quarter rq and 16-byte chunk dc of unit u (of the 8 * (DI/8) units of a
+// tile): eight consecutive lanes read eight consecutive chunks of a row (whole
+// 128-byte lines), and the lane bits above are spread over the row quarters so
+// that the natural and the transposed writes of one store instruction fall in
+// different banks.
+template <int DI>
+__device__ __forceinline__ void idx_unit(int u, int& rq, int& dc) {
+    if constexpr (DI == 128) {
+        dc = (u & 7) | (((u >> 4) & 1) << 3);
+        rq = ((u >> 5) & 1) | (((u >> 3) & 1) << 1) | (((u >> 6) & 1) << 2);
+    } else {
+        dc = u & 7;
+        rq = ((u >> 4) & 1) | (((u >> 3) & 1) << 1) | (((u >> 5) & 1) << 2);
+    }
+}
+
 template <int DI, bool LOCAL>
 __device__ __forceinline__ void idx_stage_load(IdxUnit& su, const BwdItem<LOCAL>& it, int t, int u,
                                                const bf16_t* __restrict__ q_idx, int N, int Hkv) {
-    const int rq = u & 7, dc = u >> 3;
+    int rq, dc;
+    idx_unit<DI>(u, rq, dc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int pe = 32 * t + 4 * rq + e;
@@ -498,7 +514,8 @@ __device__ __forceinline__ void idx_stage_load(IdxUnit& su, const BwdItem<LOCAL>
 template <int DI>
 __device__ __forceinline__ void idx_stage_store(const IdxUnit& su, IdxBwdTile<DI>& tb, int u) {
     using T = IdxBwdTile<DI>;
-    const int rq = u & 7, dc = u >> 3;
+    int rq, dc;
+    idx_unit<DI>(u, rq, dc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(tb.qi + T::IT::offset(4 * rq + e, dc * 16)) = su.x[e];
     // row m sits in chunk 2 * (m / 16) + (m / 4) % 2 at position 4 * ((m / 8) % 2) + m % 4
