@@ -180,6 +180,88 @@ __device__ __forceinline__ void nonlocal_tile(const Op8<T> (&qop)[D / 16], int e
     store_partial<T, D, G>(po, plse, pidx, hh, half, o, mz, l);
 }
 
+// Pipelined form of a bf16 tile. A tile reads its A operands from the
+// LDS-resident block in one fixed order: the K operands of S^T (D/16 slices x
+// 4 key tiles), then the V^T operands of O^T (D/32 dim tiles x 8 key slices).
+// Every tile of a work item repeats that order, so the operands go through an
+// 8-register ring loaded 6 products ahead, across the softmax and across tiles.
+template <int D>
+struct TileOps {
+    static constexpr int NS = (D / 16) * 4, NP = 8 * (D / 32), N = NS + NP;
+    static constexpr int RING = 8, PF = 6;
+    static_assert(N % RING == 0, "the ring must tile the operand sequence");
+};
+
+template <int D>
+__device__ __forceinline__ void tile_op(Op8<bf16_t>& a, const unsigned char* lds, int n, int col, int half) {
+    using O = TileOps<D>;
+    using KS = SwzTile<bf16_t, D>;
+    if (n < O::NS) {
+        KS::load8(a, lds, (n % 4) * 32 + col, 16 * (n / 4) + 8 * half);
+    } else {
+        const int m = n - O::NS;
+        load_vt_op<bf16_t>(a, lds + kBlock * KS::ROWB, (m / 8) * 32 + col, m % 8, half);
+    }
+}
+
+// One 32-row bf16 tile: S^T, softmax, then O^T one 32-dim tile at a time over
+// the 8 key slices (the probabilities packed once as the B operands), each dim
+// tile's normalised partial stored while the next one is on the matrix cores.
+// Rows past the item's end store to the spare partial, so every tile issues the
+// same stores; both half-waves hold the row's LSE and write it (same value).
+template <int D, int G, bool HM>
+__device__ __forceinline__ void nonlocal_tile_pipe(Op8<bf16_t> (&ring)[TileOps<D>::RING],
+                                                   const Op8<bf16_t> (&qop)[D / 16], int e, bool valid,
+                                                   const unsigned char* lds, bf16_t* __restrict__ po,
+                                                   float* __restrict__ plse, int b, int g, int N, int Hkv, int KP,
+                                                   const uint8_t* __restrict__ hmask, float scale_log2, int hh,
+                                                   int col, int half, size_t spare) {
+    using O = TileOps<D>;
+    floatx16 s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s[kt] = zero16();
+#pragma unroll
+    for (int n = 0; n < O::NS; ++n) {
+        tile_op<D>(ring[(n + O::PF) % O::RING], lds, (n + O::PF) % O::N, col, half);
+        mma16(s[n % 4], ring[n % O::RING], qop[n / 4]);
+        __builtin_amdgcn_sched_barrier(0);   // keep each load PF products ahead, no further
+    }
+    if constexpr (HM) mask_halves(s, hmask[(((size_t)b * Hkv + g) * N + (e >> 5)) * (KP + 1) + (e & 31)]);
+    float mz, l;
+    tile_softmax(s, scale_log2, mz, l);
+    Op8<bf16_t> bp[8];   // key slice c: the lane's 8 probabilities of keys 16c ..
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float pe[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) pe[x] = s[c / 2][8 * (c % 2) + x];
+        PType<bf16_t>::pack(bp[c], pe);
+    }
+    const size_t pidx = valid ? (((size_t)b * Hkv + g) * N + (e >> 5)) * KP + (e & 31) : spare;
+    bf16_t* region = po + pidx * G * D;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        floatx16 o = zero16();
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int n = O::NS + 8 * dt + c;
+            tile_op<D>(ring[(n + O::PF) % O::RING], lds, (n + O::PF) % O::N, col, half);
+            mma16(o, ring[n % O::RING], bp[c]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        u32x4 w0, w1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            w0[r] = pack_bf16x2(o[2 * r] * inv, o[2 * r + 1] * inv);
+            w1[r] = pack_bf16x2(o[8 + 2 * r] * inv, o[8 + 2 * r + 1] * inv);
+        }
+        __builtin_nontemporal_store(w0, partial_piece<bf16_t, D, G>(region, 2 * dt, hh, half));
+        __builtin_nontemporal_store(w1, partial_piece<bf16_t, D, G>(region, 2 * dt + 1, hh, half));
+    }
+    plse[pidx * G + hh] = (mz + __log2f(l)) * 0.69314718055994531f;
+}
+
 // One work-group per work item (batch, group, key block j, <= kSeg query
 // positions that kept j). K_j and V_j^T are staged in LDS once; each wave
 // streams 32-row tiles through them, loading the next tile's query rows while
@@ -226,6 +308,26 @@ __global__ __launch_bounds__(256, 2) void attn_nonlocal_kernel(
     // neither is copied into the other): the tile at `base` runs from one while
     // the next tile's rows load into the other.
     Op8<T> q_nxt[D / 16];
+    if constexpr (sizeof(T) == 2) {
+        using O = TileOps<D>;
+        Op8<bf16_t> ring[O::RING];
+#pragma unroll
+        for (int n = 0; n < O::PF; ++n) tile_op<D>(ring[n], lds, n, col, half);
+        for (; base < count; base += 2 * stride) {
+            load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, true, half);
+            const int e_2 = list[start + min(base + 2 * stride + pp, count - 1)];
+            nonlocal_tile_pipe<D, G, HM>(ring, q_cur, e_cur, base + pp < count, lds, po, plse, b, g, N, Hkv, KP,
+                                         hmask, scale_log2, hh, col, half, spare);
+            if (base + stride >= count) break;
+            load_q_op<T, D>(q_cur, qbase + (size_t)(e_2 >> 5) * Hq * D, true, half);
+            const int e_3 = list[start + min(base + 3 * stride + pp, count - 1)];
+            nonlocal_tile_pipe<D, G, HM>(ring, q_nxt, e_nxt, base + stride + pp < count, lds, po, plse, b, g, N,
+                                         Hkv, KP, hmask, scale_log2, hh, col, half, spare);
+            e_cur = e_2;
+            e_nxt = e_3;
+        }
+        return;
+    }
     for (; base < count; base += 2 * stride) {
         load_q_op<T, D>(q_nxt, qbase + (size_t)(e_nxt >> 5) * Hq * D, true, half);
         const int e_2 = list[start + min(base + 2 * stride + pp, count - 1)];
