@@ -99,6 +99,16 @@ __device__ __forceinline__ void mma1632(floatx4& c, const Op8<bf16_t>& a, const 
 // lane group q = l / 16 holds rows 4q .. 4q+3 and 16 + 4q .. 16 + 4q + 3, so
 // chunk q of a transposed row (8 positions) holds exactly those rows, row m at
 // position 4 * (m / 16) + m % 4.
+// Position (within the tile) and head of tile row m. The 16 x 16 accumulator
+// rows of lane group q are m = 16 h4 + 4 q + r (h4 < 2, r < 4): for G = 8 they
+// hold position q, head 4 h4 + r, so each lane group has all G rows of one
+// position and the KL teacher (the mean over them) stays in the lane; for the
+// other G, G consecutive rows per position.
+template <int G>
+__device__ __forceinline__ int tile_pos(int m) { return G == 8 ? (m >> 2) & 3 : m / G; }
+template <int G>
+__device__ __forceinline__ int tile_head(int m) { return G == 8 ? ((m >> 4) << 2) | (m & 3) : m % G; }
+
 template <int D>
 struct Main8Tile {
     using QT = SwzTile<bf16_t, D>;   // [32 rows][D]
@@ -154,8 +164,9 @@ __device__ __forceinline__ void main8_stage_load(Main8Quarter& su, const BwdItem
     for (int e = 0; e < 4; ++e) {
         const int m = 4 * rq + e;
         int i, s;
-        it.entry(min(t * PPT + m / G, it.count - 1), i, s);
-        su.x[e] = *reinterpret_cast<const u32x4*>(src + (((size_t)it.b * N + i) * Hq + it.g * G + m % G) * D + dc * 8);
+        it.entry(min(t * PPT + tile_pos<G>(m), it.count - 1), i, s);
+        su.x[e] = *reinterpret_cast<const u32x4*>(src + (((size_t)it.b * N + i) * Hq + it.g * G + tile_head<G>(m)) * D +
+                                                  dc * 8);
     }
 }
 
@@ -182,10 +193,18 @@ __device__ __forceinline__ void main8_stage_store(const Main8Quarter& su, Main8T
 }
 
 // Teacher of each of the lane's 8 rows (rh*4 + r: row 16*rh + 4*(l/16) + r):
-// the mean of P over the G rows of the row's position (G consecutive rows).
+// the mean of P over the G rows of the row's position (tile_pos, tile_head).
 template <int G>
 __device__ __forceinline__ void head_mean8(float (&p)[8]) {
     if constexpr (G == 1) return;
+    if constexpr (G == 8) {   // the lane's 8 rows are the 8 heads of one position
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += p[e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = s * (1.f / G);
+        return;
+    }
     float a[2][4];
 #pragma unroll
     for (int rh = 0; rh < 2; ++rh) {
@@ -194,8 +213,10 @@ __device__ __forceinline__ void head_mean8(float (&p)[8]) {
             a[rh][2] = a[rh][3] = p[4 * rh + 2] + p[4 * rh + 3];
         } else {
             float s = p[4 * rh] + p[4 * rh + 1] + p[4 * rh + 2] + p[4 * rh + 3];
-            if constexpr (G >= 8) s += __shfl_xor(s, 16);
-            if constexpr (G >= 16) s += __shfl_xor(s, 32);
+            if constexpr (G >= 16) {
+                s += __shfl_xor(s, 16);
+                s += __shfl_xor(s, 32);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) a[rh][r] = s;
         }
@@ -292,10 +313,10 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
     auto load_tile = [&](int t) {
         if (u < NST) main8_stage_load<D, G, LOCAL, MAIN>(su, it, t, u, q, dout, N, Hq);
         if (m_row >= 0) {
-            const int pe = t * PPT + m_row / G;
+            const int pe = t * PPT + tile_pos<G>(m_row);
             int i, s;
             it.entry(min(pe, it.count - 1), i, s);
-            const size_t r = ((size_t)it.b * Hq + it.g * G + m_row % G) * N + i;
+            const size_t r = ((size_t)it.b * Hq + it.g * G + tile_head<G>(m_row)) * N + i;
             r_pos = pe < it.count ? i : -1;
             r_slot = s;
             r_lse = lse[r];
@@ -362,9 +383,10 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
         }
         if constexpr (TEACH) {
             // The KL term's teacher of (position, key): the mean of P over the position's
-            // G head rows. The lanes holding a position's first row write it (for G >= 8
-            // also the other lane groups of the position, which hold the same mean); rows
-            // past the item write the spare row, so every tile issues the same stores.
+            // G head rows. The lanes holding a position's first row write it (G = 8: one
+            // store per lane; G >= 16: also the other lane groups of the position, which
+            // hold the same mean); rows past the item write the spare row, so every tile
+            // issues the same stores.
             {
                 float tp[8];
 #pragma unroll
@@ -372,7 +394,7 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
                 head_mean8<G>(tp);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    if ((e & 3) % (G < 4 ? G : 4) == 0) {
+                    if (G == 8 ? e == 0 : (e & 3) % (G < 4 ? G : 4) == 0) {
                         const int m = 16 * (e >> 2) + 4 * ql + (e & 3);
                         const int i = sh_t.pos[m];
                         const size_t row = i >= 0 ? (rbase + i) * topk + sh_t.slot[m] : spare;
@@ -425,8 +447,8 @@ __global__ __launch_bounds__(64 * kMain8Waves, 1) void main8_bwd_kernel(
                     }
                     const int i = sh_t.pos[row];
                     const size_t prow = i >= 0 ? (rbase + i) * topk + sh_t.slot[row] : spare;
-                    // partial of (window row, slot), head row % G: [G][D] bf16 in natural dim order
-                    bf16_t* dst = dq_part + prow * G * D + (size_t)(row % G) * D + 16 * w + 4 * ql;
+                    // partial of (window row, slot), the row's head: [G][D] bf16 in natural dim order
+                    bf16_t* dst = dq_part + prow * G * D + (size_t)tile_head<G>(row) * D + 16 * w + 4 * ql;
                     *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0] * scale, acc[1] * scale),
                                                                 pack_bf16x2(acc[2] * scale, acc[3] * scale));
                 }
