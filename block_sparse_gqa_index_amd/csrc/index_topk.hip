@@ -31,6 +31,7 @@
 // CU; index_topk_kernel (2- or 4-wave work-groups, two LDS stages) serves the
 // other shapes and fp32.
 #include "msa_common.h"
+#include <type_traits>
 #include "msa_internal.h"
 
 namespace msa {
@@ -372,7 +373,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     static_assert(CPT * NTHR == kBlock * CPR, "staging must tile the block");
     static_assert(NOPS % RING == 0 && PF < RING, "operand ring must tile the block");
     static_assert(NT % 2 == 0, "lanes of both half-waves own rows");
-    __shared__ __align__(16) unsigned char lds[3 * BUF];
+    // bf16: blocks are copied global -> LDS directly (no registers), through
+    // four stages. Each 64-lane copy fills 1 KiB of consecutive LDS, i.e. 64
+    // chunks of the padded rows (a row's pad chunk takes a copy of its first
+    // chunk), so a stage is exactly DMA_N copies; every wave issues DMA_W of
+    // them per block (the ones past DMA_N into a scratch area), so that the
+    // wait at the end of a block can leave exactly the next block's copies in
+    // flight. Other element types stage through registers, three stages.
+    constexpr bool kDma = std::is_same<T, bf16_t>::value;
+    constexpr int DMA_N = kBlock * (CPR + 1) / 64, DMA_W = (DMA_N + WAVES - 1) / WAVES;
+    constexpr int DMA_X = DMA_W * WAVES - DMA_N;   // scratch copies
+    static_assert(!kDma || (ROWB == 16 * (CPR + 1) && DMA_W <= 15), "copies fill padded rows; vmcnt field");
+    __shared__ __align__(16) unsigned char lds[kDma ? 4 * BUF + 1024 * (DMA_X > 0 ? DMA_X : 1) : 3 * BUF];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -423,9 +435,43 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
         const int key = BK == 64 ? min(j * kBlock + ch / CPR, N - 1) : j * kBlock + ch / CPR;
         return reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (ch % CPR) * 16);
     };
-    u32x4 stage[CPT];
+    int dch[kDma ? DMA_W : 1];   // source chunk (row * CPR + column) of each of this wave's copies
+#pragma unroll
+    for (int u = 0; u < (kDma ? DMA_W : 1); ++u) {
+        const int c = 64 * (w + WAVES * u) + lane;
+        const int row = c / (CPR + 1), cc = c % (CPR + 1);
+        dch[u] = c < 64 * DMA_N ? row * CPR + (cc < CPR ? cc : 0) : 0;
+    }
+    auto dma_block = [&](int jb, int st) {
+#pragma unroll
+        for (int u = 0; u < DMA_W; ++u) {
+            const int i = w + WAVES * u;
+            unsigned char* dst = i < DMA_N ? lds + st * BUF + 1024 * i : lds + 4 * BUF + 1024 * (i - DMA_N);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)chunk_src(jb, dch[u]),
+                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+    };
+    // End of a block on the copy path: this wave's copies of the block after
+    // next have landed (only the DMA_W copies requested since may be in flight)
+    // and its LDS reads are done; then the barrier. The wavefront-scope fences
+    // emit no wait of their own but keep the compiler from moving LDS accesses
+    // across the barrier.
+    auto dma_barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x70 | DMA_W);   // vmcnt(DMA_W) lgkmcnt(0)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    u32x4 stage[kDma ? 1 : CPT];
     typename MM::Op a[RING];
-    if (nj > 0) {   // a row of query block 0 has no candidate block at BK >= 128
+    if (kDma) {
+        if (nj > 0) {
+            dma_block(0, 0);
+            dma_block(min(1, nj - 1), 1);
+            dma_block(min(2, nj - 1), 2);
+            dma_barrier();   // blocks 0 and 1 in LDS
+        }
+    } else if (nj > 0) {   // a row of query block 0 has no candidate block at BK >= 128
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
@@ -439,7 +485,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
 #pragma unroll
         for (int u = 0; u < CPT; ++u) stage[u] = *chunk_src(min(2, nj - 1), tid + NTHR * u);
     }
-    __syncthreads();
+    if constexpr (!kDma) __syncthreads();
     if (nj > 0) {
 #pragma unroll
         for (int m = 0; m < PF; ++m) a[m].load(opbase + ((m / KS) * 32) * ROWB + elem_bytes<T>(KD * (m % KS)));
@@ -472,8 +518,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     };
     int sb = 0;   // stage of block j
     for (int j = 0; j < nj; ++j) {
-        const int nb1 = sb == 2 ? 0 : sb + 1;    // stage of block j+1
-        const int wb = nb1 == 2 ? 0 : nb1 + 1;   // stage of block j+2 (= that of block j-1)
+        // stages of blocks j+1 and j+2 (three stages: that of block j-1; four: block j+3 goes there)
+        const int nb1 = kDma ? (sb + 1) & 3 : (sb == 2 ? 0 : sb + 1);
+        const int wb = kDma ? (sb + 2) & 3 : (nb1 == 2 ? 0 : nb1 + 1);
+        if constexpr (kDma) dma_block(min(j + 3, nj - 1), (sb + 3) & 3);
 #pragma unroll
         for (int n = 0; n < NOPS; ++n) {
             const int kt = n / KS, s = n % KS;
@@ -521,17 +569,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) bm_prev[t] = bm[t];
-        // Block j+2 into the stage block j-1 used; block j+3 into VGPRs.
+        if constexpr (kDma) {
+            dma_barrier();
+        } else {
+            // Block j+2 into the stage block j-1 used; block j+3 into VGPRs.
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ch = tid + NTHR * u;
-            *reinterpret_cast<u32x4*>(lds + wb * BUF + (ch / CPR) * ROWB + (ch % CPR) * 16) = stage[u];
+            for (int u = 0; u < CPT; ++u) {
+                const int ch = tid + NTHR * u;
+                *reinterpret_cast<u32x4*>(lds + wb * BUF + (ch / CPR) * ROWB + (ch % CPR) * 16) = stage[u];
+            }
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) stage[u] = *chunk_src(min(j + 3, nj - 1), tid + NTHR * u);
+            __syncthreads();
         }
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) stage[u] = *chunk_src(min(j + 3, nj - 1), tid + NTHR * u);
-        __syncthreads();
         sb = nb1;
     }
+    // no copy may still be writing this work-group's LDS when its waves end
+    if constexpr (kDma) __builtin_amdgcn_s_waitcnt(0);
     if (nj > 0) {
 #pragma unroll
         for (int o = 0; o < NO; ++o)
