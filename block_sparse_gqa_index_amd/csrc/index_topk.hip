@@ -373,13 +373,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_topk_pipe_kernel(
     static_assert(CPT * NTHR == kBlock * CPR, "staging must tile the block");
     static_assert(NOPS % RING == 0 && PF < RING, "operand ring must tile the block");
     static_assert(NT % 2 == 0, "lanes of both half-waves own rows");
-    // bf16: blocks are copied global -> LDS directly (no registers), through
-    // four stages. Each 64-lane copy fills 1 KiB of consecutive LDS, i.e. 64
-    // chunks of the padded rows (a row's pad chunk takes a copy of its first
-    // chunk), so a stage is exactly DMA_N copies; every wave issues DMA_W of
-    // them per block (the ones past DMA_N into a scratch area), so that the
-    // wait at the end of a block can leave exactly the next block's copies in
-    // flight. Other element types stage through registers, three stages.
+    // bf16 blocks are copied global -> LDS directly (no registers), through
+    // four stages. Each 64-lane copy fills 1 KiB of consecutive LDS, i.e. 64 chunks
+    // of the padded rows (a row's pad chunk takes a copy of its first chunk),
+    // so a stage is exactly DMA_N copies; every wave issues DMA_W of them per
+    // block (the ones past DMA_N into a scratch area), so that the wait at the
+    // end of a block can leave exactly the next block's copies in flight. The
+    // 8-bit and 4-bit inputs keep the register-staged three-stage form: their
+    // blocks take a quarter or an eighth of the matrix-core time, too little to
+    // hide the copies (fp8 7.6 ms with them against 6.2-6.5, fp4 5.5 against 4.6).
     constexpr bool kDma = std::is_same<T, bf16_t>::value;
     constexpr int DMA_N = kBlock * (CPR + 1) / 64, DMA_W = (DMA_N + WAVES - 1) / WAVES;
     constexpr int DMA_X = DMA_W * WAVES - DMA_N;   // scratch copies
