@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const float* __restrict__ lse, const int32_t* __restrict__ list, const int4* __restrict__ items,
     const int32_t* __restrict__ total_items, float* __restrict__ part, const uint8_t* __restrict__ hmask, int N,
-    int Hkv, int nb, int nwin, int KP, float scale_log2, float iscale) {
+    int Hkv, int nb, int nwin, int KP, float scale_log2, float iscale, size_t spare) {
     constexpr int PPT = 32 / G;
     __shared__ __align__(16) unsigned char lds[SwzTile<T, D>::BYTES + SwzTile<T, DI>::BYTES];
     unsigned char* lds_i = lds + SwzTile<T, D>::BYTES;
@@ -197,13 +197,68 @@ __global__ __launch_bounds__(256, 2) void kl_nonlocal_kernel(
     int e_cur = entry(base);
     Op8<T> bq[D / 16];
     Op8<T> bi[DI / 16];
-    load_q_op<T, D>(bq, qrow(e_cur), base + pp < count, half);
-    load_q_op<T, DI>(bi, qirow(e_cur), base + pp < count, half);
+    load_q_op<T, D>(bq, qrow(e_cur), sizeof(T) == 2 || base + pp < count, half);
+    load_q_op<T, DI>(bi, qirow(e_cur), sizeof(T) == 2 || base + pp < count, half);
 
     stage_rows<T, D>(lds, k + ((size_t)b * N + (size_t)j * kBlock) * Hkv * D + (size_t)g * D, (size_t)Hkv * D,
                      kBlock);
     stage_rows<T, DI>(lds_i, k_idx + ((size_t)b * N + (size_t)j * kBlock) * DI, DI, kBlock);
     __syncthreads();
+
+    if constexpr (sizeof(T) == 2) {
+        // bf16: the A operands of a tile (the K slices of S^T, then the K_idx
+        // slices of U^T) repeat every tile, so they go through an 8-register ring
+        // loaded 6 products ahead across tiles; the rows' loads (clamped to the
+        // item's last entry) and the partial stores (the other lanes and the
+        // padding rows to the spare record) are unconditional, so each tile's
+        // wait covers only the next rows' loads.
+        constexpr int NS = (D / 16) * 4, N_OPS = NS + (DI / 16) * 4, RING = 8, PF = 6;
+        static_assert(N_OPS % RING == 0, "the ring must tile the operand sequence");
+        auto op = [&](Op8<bf16_t>& a, int n) {
+            if (n < NS) SwzTile<bf16_t, D>::load8(a, lds, (n % 4) * 32 + col, 16 * (n / 4) + 8 * half);
+            else SwzTile<bf16_t, DI>::load8(a, lds_i, ((n - NS) % 4) * 32 + col, 16 * ((n - NS) / 4) + 8 * half);
+        };
+        Op8<bf16_t> ring[RING];
+#pragma unroll
+        for (int n = 0; n < PF; ++n) op(ring[n], n);
+        for (; base < count; base += stride) {
+            const bool valid = base + pp < count;
+            const int i = e_cur >> 5, slot = e_cur & 31;
+            const float lse_row = lse[((size_t)b * Hq + g * G + hh) * N + i];
+            const int e_nxt = entry(base + stride);
+            floatx16 s[4], u[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) s[kt] = u[kt] = zero16();
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+                op(ring[(n + PF) % RING], (n + PF) % N_OPS);
+                mma16(s[n % 4], ring[n % RING], bq[n / 4]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            load_q_op<T, D>(bq, qrow(e_nxt), true, half);
+#pragma unroll
+            for (int n = NS; n < N_OPS; ++n) {
+                op(ring[(n + PF) % RING], (n + PF) % N_OPS);
+                mma16(u[(n - NS) % 4], ring[n % RING], bi[(n - NS) / 4]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            load_q_op<T, DI>(bi, qirow(e_nxt), true, half);
+            const float lse2 = valid ? lse_row * kLog2e : 0.f;
+            KlAcc a;
+            if constexpr (HM) {
+                const int m = hmask[(((size_t)b * Hkv + g) * N + i) * (KP + 1) + slot];
+                a = tile_kl<G, true>(s, u, scale_log2, lse2, iscale, (m & 2) ? 127 : 63, half, hh, (m & 1) ? 0 : 64);
+            } else {
+                a = tile_kl<G, false>(s, u, scale_log2, lse2, iscale, 0, half, hh);
+            }
+            const size_t rec = valid && hh == 0 && half == 0 ? (((size_t)b * Hkv + g) * N + i) * KP + slot : spare;
+            float* dst = part + rec * kKlPart;
+            *reinterpret_cast<float4*>(dst) = make_float4(a.A, a.Bs, a.P, a.mu);
+            dst[4] = a.lu;
+            e_cur = e_nxt;
+        }
+        return;
+    }
 
     for (; base < count; base += stride) {
         const bool valid = base + pp < count;
@@ -510,7 +565,8 @@ KlWorkspace kl_workspace_layout(const LaunchDims& d0) {
     const size_t rows = (size_t)d.B * d.Hkv * d.N;
     w.red_blocks = red_blocks_for(rows);
     size_t off = w.lists.has_nonlocal ? w.lists.end : w.ex.end;
-    w.part = off;  off = align_up(off + (w.lists.has_nonlocal ? w.lists.max_entries * kKlPart * 4 : 0));
+    // one spare record past the last (row, slot): the stores of padding rows and non-writer lanes
+    w.part = off;  off = align_up(off + (w.lists.has_nonlocal ? (w.lists.max_entries + 1) * kKlPart * 4 : 0));
     w.red = off;   off = align_up(off + (size_t)w.red_blocks * 8);
     w.bytes = off;
     return w;
@@ -547,11 +603,11 @@ static hipError_t launch_kl_t(const LaunchDims& d0, const void* q, const void* k
         if (hm)
             hipLaunchKernelGGL((kl_nonlocal_kernel<T, D, DI, G, true>), dim3((unsigned)grid), dim3(256), 0, st, tq, tk,
                                tqi, tki, lse, list, items, total, part, hmask, d.N, d.Hkv, d.nb, windows(d), KP,
-                               scale_log2, iscale);
+                               scale_log2, iscale, L.lists.max_entries);
         else
             hipLaunchKernelGGL((kl_nonlocal_kernel<T, D, DI, G, false>), dim3((unsigned)grid), dim3(256), 0, st, tq,
                                tk, tqi, tki, lse, list, items, total, part, hmask, d.N, d.Hkv, d.nb, windows(d), KP,
-                               scale_log2, iscale);
+                               scale_log2, iscale, L.lists.max_entries);
     }
     const dim3 cgrid((unsigned)(d.nb * d.B * d.Hkv));
     const int kk = L.lists.has_nonlocal ? d.k : 1;
