@@ -157,8 +157,8 @@ __device__ __forceinline__ void mask_halves(floatx16 (&s)[4], int m) {
 // One 32-row tile of a non-local work item: the lane's row is list entry `e`
 // (position << 5 | slot); scores against the staged block, softmax, P V and
 // the partial store (to the spare partial for the padding rows past the
-// item's end). HM:
-// the entry keeps only the halves its mask byte names (64-token selections).
+// item's end). HM: the entry keeps only the halves its mask byte names
+// (64-token selections).
 template <typename T, int D, int G, bool HM>
 __device__ __forceinline__ void nonlocal_tile(const Op8<T> (&qop)[D / 16], int e, bool valid,
                                               const unsigned char* lds, T* __restrict__ po,
