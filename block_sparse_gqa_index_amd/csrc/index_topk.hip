@@ -89,24 +89,25 @@ template <> struct IdxBits<fp4x2_t> { static constexpr int v = 4; };
 template <typename T> __device__ __host__ constexpr int elem_bytes(int e) { return e * IdxBits<T>::v / 8; }
 
 // Inserts (x, j) into the descending list; a no-op when x does not beat the
-// last entry (then no comparison below succeeds), so it runs without a branch
-// and can be scheduled under the matrix-core work of the next key block.
+// last entry, so it runs without a branch and can be scheduled under the
+// matrix-core work of the next key block. Every slot is computed from the old
+// list and x alone (no chain through the slots): slot s takes the entry above
+// it when x beats that entry, x when x beats only its own entry, else keeps
+// its entry; the score is then the median of (entry above, x, own entry),
+// which is the same value in all three cases. "Beats" is strictly greater, so
+// an equal score never displaces a lower id.
 template <int SLOTS>
 __device__ __forceinline__ void topk_insert(float (&sc)[SLOTS], int (&id)[SLOTS], float x, int j) {
-    float cs = x;
-    int ci = j;
-    bool ins = false;
+    bool gt[SLOTS];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-        const bool take = ins | (cs > sc[s]);
-        const float ts = sc[s];
-        const int ti = id[s];
-        sc[s] = take ? cs : ts;
-        id[s] = take ? ci : ti;
-        cs = take ? ts : cs;
-        ci = take ? ti : ci;
-        ins = take;
+    for (int s = 0; s < SLOTS; ++s) gt[s] = x > sc[s];
+#pragma unroll
+    for (int s = SLOTS - 1; s > 0; --s) {   // bottom up: slot s still reads the old slot s - 1
+        id[s] = gt[s - 1] ? id[s - 1] : (gt[s] ? j : id[s]);
+        sc[s] = __builtin_amdgcn_fmed3f(sc[s - 1], x, sc[s]);
     }
+    id[0] = gt[0] ? j : id[0];
+    sc[0] = gt[0] ? x : sc[0];
 }
 
 template <int SLOTS>
