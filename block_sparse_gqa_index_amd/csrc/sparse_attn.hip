@@ -259,7 +259,9 @@ __device__ __forceinline__ void nonlocal_tile_pipe(Op8<bf16_t> (&ring)[TileOps<D
         __builtin_nontemporal_store(w0, partial_piece<bf16_t, D, G>(region, 2 * dt, hh, half));
         __builtin_nontemporal_store(w1, partial_piece<bf16_t, D, G>(region, 2 * dt + 1, hh, half));
     }
-    plse[pidx * G + hh] = (mz + __log2f(l)) * 0.69314718055994531f;
+    // Streamed past the caches like the pieces: the 32-byte LSE records of one
+    // tile land in different lines, which no later store of this kernel fills.
+    __builtin_nontemporal_store((mz + __log2f(l)) * 0.69314718055994531f, plse + pidx * G + hh);
 }
 
 // One work-group per work item (batch, group, key block j, <= kSeg query
