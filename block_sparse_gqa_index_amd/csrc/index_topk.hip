@@ -26,10 +26,11 @@
 //  * Work-groups are numbered heaviest query block first (longest-processing-
 //    time order over the triangular load).
 //
-// index_topk_pipe_kernel (bf16 when 512 rows tile a query block) is the
-// software-pipelined form with three LDS stages and one 8-wave work-group per
-// CU; index_topk_kernel (2- or 4-wave work-groups, two LDS stages) serves the
-// other shapes and fp32.
+// index_topk_pipe_kernel (bf16, fp8, fp4 when 512 rows tile a query block) is
+// the software-pipelined form with one 8-wave work-group per CU (bf16: four LDS
+// stages filled by direct global -> LDS copies; fp8/fp4: three stages staged
+// through registers); index_topk_kernel (2- or 4-wave work-groups, two LDS
+// stages) serves the other shapes and fp32.
 #include "msa_common.h"
 #include <type_traits>
 #include "msa_internal.h"
@@ -348,11 +349,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void index_topk_kernel(
 }
 
 // Software-pipelined variant for 8-wave work-groups (one per CU, two waves
-// per SIMD): three LDS stages so that the first operands of key block j+1 can
-// be requested while block j is still on the matrix cores (block j+2 is
-// written to the third stage meanwhile, block j+3 is in flight in VGPRs, one
-// barrier per block), and the A operands of a block are requested PF ahead of
-// the MFMA that uses them, across block boundaries. The last key tile's max of
+// per SIMD): several LDS stages so that the first operands of key block j+1
+// can be requested while block j is still on the matrix cores (fp8/fp4: three
+// stages, block j+2 written to the third one meanwhile and block j+3 in flight
+// in VGPRs; bf16: four stages, block j+3 copied straight into the stage block
+// j-1 freed; one barrier per block either way), and the A operands of a block
+// are requested PF ahead of the MFMA that uses them, across block boundaries. The last key tile's max of
 // block j is taken under block j+1's first MFMAs, and its candidate inserted
 // right after.
 template <typename T, int DI, int NT, int WAVES, int SLOTS, int BK>
