@@ -22,9 +22,9 @@ torch.Generator on the target device):
 """
 from .configs import CONFIGS, DECODE_CONFIGS, Workload, get_workload
 from .inputs import (make_inputs, make_decode_inputs, make_grad_output, make_row_weights, sample_rows,
-                     edge_positions, to_fp4_e2m1)
+                     uniform_rows, edge_positions, to_fp4_e2m1)
 
 __all__ = ["CONFIGS", "DECODE_CONFIGS", "Workload", "get_workload", "make_inputs", "make_decode_inputs",
            "make_grad_output", "make_row_weights",
-           "sample_rows",
+           "sample_rows", "uniform_rows",
            "edge_positions", "to_fp4_e2m1"]

@@ -79,17 +79,22 @@ def edge_positions(w: Workload):
     return sorted({p for p in cand if 0 <= p < N})
 
 
+def uniform_rows(w: Workload, n=None, seed=1):
+    """The uniformly drawn part of ``sample_rows``: ``n`` flat positions
+    b * N + i drawn without replacement over all B*N (all of them when n
+    covers the workload), unsorted int64."""
+    n = w.sampled_rows if n is None else n
+    total = w.batch * w.seqlen
+    if n <= 0 or n >= total:
+        return np.arange(total, dtype=np.int64)
+    return np.random.default_rng(seed).choice(total, size=n, replace=False).astype(np.int64)
+
+
 def sample_rows(w: Workload, n=None, seed=1):
     """(b, i) query positions checked on large workloads: ``n`` drawn without
     replacement over all B*N positions plus the edge positions in every batch.
     Returns an int64 array of shape [M, 2], sorted."""
-    n = w.sampled_rows if n is None else n
-    total = w.batch * w.seqlen
-    rng = np.random.default_rng(seed)
-    if n <= 0 or n >= total:
-        flat = np.arange(total, dtype=np.int64)
-    else:
-        flat = rng.choice(total, size=n, replace=False).astype(np.int64)
+    flat = uniform_rows(w, n, seed)
     edges = [b * w.seqlen + p for b in range(w.batch) for p in edge_positions(w)]
     flat = np.unique(np.concatenate([flat, np.asarray(edges, dtype=np.int64)]))
     return np.stack([flat // w.seqlen, flat % w.seqlen], axis=1)

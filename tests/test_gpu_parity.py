@@ -15,7 +15,7 @@ import torch
 
 import block_sparse_gqa_index_amd as msa
 from oracle import msa_oracle as O
-from synth import CONFIGS, Workload, make_inputs, sample_rows
+from synth import CONFIGS, Workload, make_inputs, sample_rows, uniform_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -138,6 +138,17 @@ def run_and_check(w: Workload, positions=None, on_gpu_rng=False, check_kl=False)
         else:
             # kl_sum is the fixed-order sum of the GPU rows
             assert abs(kl_sum.item() - kl.double().sum().item()) <= 1e-4 * abs(kl.double().sum().item()) + 1e-3
+            # and, independently of the GPU rows, agrees with the oracle's estimate
+            # of the total from the uniformly drawn positions (B*N times their mean
+            # row total over the groups) within five standard errors of that mean
+            flat = pos[:, 0] * w.seqlen + pos[:, 1]
+            per_pos = np.asarray(want_kl, dtype=np.float64).reshape(len(pos), -1).sum(axis=1)
+            t = per_pos[np.isin(flat, uniform_rows(w))]
+            total = w.batch * w.seqlen
+            est = total * t.mean()
+            se = total * t.std(ddof=1) / np.sqrt(len(t))
+            log(f"  kl_sum {kl_sum.item():.6e} vs oracle estimate {est:.6e} +- {se:.2e} ({len(t)} uniform rows)")
+            assert abs(kl_sum.item() - est) <= 5 * se
     return x, bi, o, lse
 
 
