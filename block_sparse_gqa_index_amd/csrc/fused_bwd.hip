@@ -523,13 +523,11 @@ __device__ __forceinline__ void idx_stage_load(IdxUnit& su, const BwdItem<LOCAL>
     idx_unit<DI>(u, rq, dc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int pe = 32 * t + 4 * rq + e;
-        su.x[e] = u32x4{0u, 0u, 0u, 0u};
-        if (pe < it.count) {
-            int i, s;
-            it.entry(pe, i, s);
-            su.x[e] = *reinterpret_cast<const u32x4*>(q_idx + (((size_t)it.b * N + i) * Hkv + it.g) * DI + dc * 8);
-        }
+        // rows past the item read its last entry (their dU is zero), so every
+        // load is issued unconditionally
+        int i, s;
+        it.entry(min(32 * t + 4 * rq + e, it.count - 1), i, s);
+        su.x[e] = *reinterpret_cast<const u32x4*>(q_idx + (((size_t)it.b * N + i) * Hkv + it.g) * DI + dc * 8);
     }
 }
 
@@ -582,6 +580,7 @@ __global__ __launch_bounds__(256, 2) void fused_index_kernel(
     const int half = lane >> 5, col = lane & 31;
     const int ntiles = (it.count + 31) / 32;
     const size_t rbase = ((size_t)it.b * Hkv + it.g) * win.len - win.p0;   // window row of position i: rbase + i
+    const size_t spare = (size_t)B * Hkv * win.len * topk;                 // (row, slot) of rows past the item
 
     const int key = 32 * w + col;
     const int kabs = it.j * kBlock + key;
@@ -602,18 +601,15 @@ __global__ __launch_bounds__(256, 2) void fused_index_kernel(
 #pragma unroll
     for (int dt = 0; dt < DIT; ++dt) dkit[dt] = zero16();
 
-    // The teacher of the lane's 16 rows (rows 8*(r/4) + 4*half + r%4) at its key, one tile ahead.
+    // The teacher of the lane's 16 rows (rows 8*(r/4) + 4*half + r%4) at its key, one tile ahead;
+    // rows past the item read its last entry's (finite; their weight is zero).
     float tn[16];
     auto teacher_load = [&](int t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int pe = 32 * t + 8 * (r / 4) + 4 * half + r % 4;
-            tn[r] = 0.f;
-            if (pe < it.count) {
-                int i, s;
-                it.entry(pe, i, s);
-                tn[r] = teacher[((rbase + i) * topk + s) * kBlock + key];
-            }
+            int i, s;
+            it.entry(min(32 * t + 8 * (r / 4) + 4 * half + r % 4, it.count - 1), i, s);
+            tn[r] = teacher[((rbase + i) * topk + s) * kBlock + key];
         }
     };
 
@@ -733,19 +729,19 @@ __global__ __launch_bounds__(256, 2) void fused_index_kernel(
                 a.load(sh.kit + L::DuT::offset(32 * w + col, (16 * c + 8 * half) * 2));
                 mma16(acc, a, b);
             }
+            // partial of (window row, slot): [DI] bf16, each 32-dim slice lane-major; rows
+            // past the item write the spare row, so every tile issues the same stores
             const int i = sh_t.pos[col];
-            if (i >= 0) {
-                // partial of (window row, slot): [DI] bf16, each 32-dim slice lane-major
-                bf16_t* dst = dqi_part + ((rbase + i) * topk + sh_t.slot[col]) * DI + 32 * w + 16 * half;
-                u32x4 w0, w1;
+            const size_t prow = i >= 0 ? (rbase + i) * topk + sh_t.slot[col] : spare;
+            bf16_t* dst = dqi_part + prow * DI + 32 * w + 16 * half;
+            u32x4 w0, w1;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w0[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
-                    w1[e] = pack_bf16x2(acc[8 + 2 * e], acc[8 + 2 * e + 1]);
-                }
-                *reinterpret_cast<u32x4*>(dst) = w0;
-                *reinterpret_cast<u32x4*>(dst + 8) = w1;
+            for (int e = 0; e < 4; ++e) {
+                w0[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+                w1[e] = pack_bf16x2(acc[8 + 2 * e], acc[8 + 2 * e + 1]);
             }
+            *reinterpret_cast<u32x4*>(dst) = w0;
+            *reinterpret_cast<u32x4*>(dst + 8) = w1;
         }
     }
 
@@ -905,7 +901,7 @@ FusedBwdWorkspace fused_bwd_workspace_layout(const LaunchDims& d, BwdParts parts
     w.items = bg * w.bound + bg * ((W + kBlock - 1) / kBlock);   // non-local slots, then local ones
     w.teacher = off;   off = align_up(off + (kl ? (bg * W * d.k + 1) * kBlock * 4 : 0));   // + spare row
     w.dq_part = off;   off = align_up(off + (mn ? (bg * W * d.k + 1) * d.G * d.D * 2 : 0));   // + spare
-    w.dqi_part = off;  off = align_up(off + (kl ? bg * W * d.k * d.Di * 2 : 0));
+    w.dqi_part = off;  off = align_up(off + (kl ? (bg * W * d.k + 1) * d.Di * 2 : 0));   // + spare
     w.dkv_part = off;  off = align_up(off + (mn ? w.items * 2 * kBlock * d.D * 4 : 0));
     w.dki_part = off;  off = align_up(off + (kl ? w.items * kBlock * d.Di * 4 : 0));
     w.acc_dkv = off;   off = align_up(off + (mn && multi ? bg * d.nb * 2 * kBlock * d.D * 4 : 0));
