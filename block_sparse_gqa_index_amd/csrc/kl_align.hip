@@ -45,20 +45,21 @@ __device__ __forceinline__ float lane_pair(float x) {
 
 // One reduce-scatter step over bit BIT of the head index (see tile_kl): keeps
 // the upper or lower half of the first N tokens, adding the partner's half.
-// The u values (equal in all lanes of the group) are narrowed with an exact
-// 0/1 blend rather than a select: selects of plain copies of accumulator
-// elements are folded by the compiler, across the unrolled steps, into one
-// lane-dependent element index that it expands as a compare chain per value.
+// The u values (equal in all lanes of the group) are narrowed with a bitwise
+// select under a lane mask rather than a select of floats: selects of plain
+// copies of accumulator elements are folded by the compiler, across the
+// unrolled steps, into one lane-dependent element index that it expands as a
+// compare chain per value; the integer form stays one instruction per value.
 template <int BIT, int N>
 __device__ __forceinline__ void scatter_step(float (&v)[64], float (&uv)[64], int hh, int& base) {
     const bool hi = (hh >> BIT) & 1;
-    const float fh = hi ? 1.f : 0.f, fl = 1.f - fh;
+    const uint32_t msk = hi ? 0xffffffffu : 0u;
 #pragma unroll
     for (int t = 0; t < N / 2; ++t) {
         const float send = hi ? v[t] : v[t + N / 2];
         const float keep = hi ? v[t + N / 2] : v[t];
         v[t] = keep + lane_pair<BIT>(send);
-        uv[t] = fmaf(uv[t + N / 2], fh, uv[t] * fl);   // finite values: exact
+        uv[t] = __uint_as_float((__float_as_uint(uv[t + N / 2]) & msk) | (__float_as_uint(uv[t]) & ~msk));
     }
     base += hi ? N / 2 : 0;
 }
