@@ -250,8 +250,19 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint32_t* __restrict
             word &= word - 1;
             const int i = win * kWindow + (w0 + lane) * 32 + bit;
             const int32_t* row = block_idx + (bg * N + i) * k;
+            // j's slot = the row's entries before it (ascending, -1 padded): read
+            // with independent loads (indexes clamped into the row) instead of a
+            // scan that waits for each load before the next
             int slot = 0;
-            while (slot + 2 < k && row[slot] != j) ++slot;
+            if (k <= 16) {
+                int e[15];
+#pragma unroll
+                for (int s = 0; s < 15; ++s) e[s] = row[min(s, k - 2)];
+#pragma unroll
+                for (int s = 0; s < 15; ++s) slot += (s < k - 1 && e[s] >= 0 && e[s] < j) ? 1 : 0;
+            } else {
+                while (slot + 2 < k && row[slot] != j) ++slot;
+            }
             list[pos++] = (i << 5) | slot;
         }
         at += __shfl(incl, 63);
